@@ -1,0 +1,456 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU implementation of what the quantized
+ * GEMV / MoE path computes, in IEEE double precision.  Only the test suite,
+ * the smoke check and the bench's CPU-baseline leg load this library; the HIP
+ * library never links, includes or calls it, and the two share no code,
+ * headers, tables or constants.
+ *
+ * Method: every GGUF block is dequantized to exact f64 values by the block
+ * formulas, then the dot product is taken in f64 (the pages state that their
+ * in-shader products equal llama.cpp's "up to summation order", so the plain
+ * definition dequantize-then-dot is the result to reproduce).  No factorisation
+ * used by the kernels (block-scale-once, x-sums for the K-quant mins) appears
+ * here.
+ *
+ * Sources (the five diskformer package-diff pages; each function names its own):
+ *   [bonsai]  diskformer 0.5.4 -> 0.6.6, engines/ternary_bonsai_2_dflash.js
+ *   [gemma4]  diskformer 0.0.1 -> 0.2.0, engines/gemma4_moe_ssd.js
+ *   [qwen3]   diskformer 0.0.1 -> 0.3.0, engines/qwen3_moe_ssd.js
+ *   [qwen35]  diskformer 0.0.1 -> 0.3.0, engines/qwen35_moe_ssd.js
+ *   [dense]   diskformer 0.5.4 -> 0.6.6, engines/qwen35_dense.js
+ *
+ * Parity status: every function here is pinned by tests/test_oracle_*.py
+ * against closed forms, second decoders written from the pages' other
+ * renderings, brute force and library routines.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* GGML type ids (the GGUF on-disk enum; [bonsai] header section prints
+ * Q4_K = 12 and Q6_K = 14; Q4_0 = 2 and Q8_0 = 8 complete the same enum). */
+#define OR_Q4_0 2
+#define OR_Q8_0 8
+#define OR_Q4_K 12
+#define OR_Q6_K 14
+
+#define OR_ACT_SILU 0
+#define OR_ACT_GELU_TANH 1
+
+/* ---------------------------------------------------------------- f16 ---- */
+/* IEEE binary16 -> double, exact for every pattern (subnormals, inf, NaN).
+ * [bonsai] "f16 codecs" section, f16ToF32: sign bit 15, 5-bit exponent
+ * (bias 15), 10-bit fraction; exponent 0 is subnormal, 31 is inf/NaN. */
+double or_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ------------------------------------------------------- block formats ---- */
+int or_block_values(int type)  /* values per block */
+{
+    switch (type) {
+    case OR_Q8_0: case OR_Q4_0: return 32;
+    case OR_Q4_K: case OR_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int or_block_bytes(int type)
+{
+    switch (type) {
+    case OR_Q8_0: return 2 + 32;                   /* f16 d, int8 q[32] */
+    case OR_Q4_0: return 2 + 16;                   /* f16 d, 16 bytes of nibbles */
+    case OR_Q4_K: return 2 + 2 + 12 + 128;         /* d, dmin, scales[12], qs[128] */
+    case OR_Q6_K: return 128 + 64 + 16 + 2;        /* ql, qh, scales[16], d */
+    default: return 0;
+    }
+}
+
+/* Q8_0: value i = d * int8(q[i]).
+ * [qwen3] header comment (a block is an f16 scale and 32 int8 values, copied
+ * bit-exact) and the WGSL i8at / matmulQ8 kernels (int8 times the f16 scale of
+ * its 32-value group). Reading: d occupies bytes 0-1, codes bytes 2..33. */
+static void deq_q8_0(const uint8_t *b, double *out)
+{
+    double d = or_f16(rd16(b));
+    for (int i = 0; i < 32; i++)
+        out[i] = d * (double)(int8_t)b[2 + i];
+}
+
+/* Q4_0: byte j of the 16 nibble bytes holds value j in its low nibble and value
+ * j+16 in its high nibble; value = (nibble - 8) * d.
+ * [gemma4] WGSL section, the Q4_0 plane comment and q4dot. Reading: d first. */
+static void deq_q4_0(const uint8_t *b, double *out)
+{
+    double d = or_f16(rd16(b));
+    for (int j = 0; j < 16; j++) {
+        out[j] = d * (double)((b[2 + j] & 15) - 8);
+        out[j + 16] = d * (double)((b[2 + j] >> 4) - 8);
+    }
+}
+
+/* The 12 scale bytes of a Q4_K block hold eight 6-bit scales and eight 6-bit
+ * mins.  Sub-blocks 0..3 use the low 6 bits of bytes s and s+4; sub-blocks
+ * 4..7 take their low 4 bits from byte s+4 (low / high nibble) and their top 2
+ * bits from the top 2 bits of bytes s-4 (scale) and s (min).
+ * [bonsai] "dequantizers" section, scaleMinK4. */
+static void q4k_scale_min(const uint8_t *S, int s, int *sc, int *mn)
+{
+    if (s < 4) {
+        *sc = S[s] & 63;
+        *mn = S[s + 4] & 63;
+    } else {
+        *sc = (S[s + 4] & 15) | ((S[s - 4] >> 6) << 4);
+        *mn = (S[s + 4] >> 4) | ((S[s] >> 6) << 4);
+    }
+}
+
+/* Q4_K (144 B, 256 values): d, dmin (f16), scales[12], qs[128].  Chunk c of 32
+ * qs bytes feeds sub-block 2c with its low nibbles and sub-block 2c+1 with its
+ * high nibbles; value = d*sc*q - dmin*m.
+ * [bonsai] "dequantizers" section, dequantQ4K. */
+static void deq_q4_k(const uint8_t *b, double *out)
+{
+    double d = or_f16(rd16(b)), dmin = or_f16(rd16(b + 2));
+    const uint8_t *S = b + 4, *Q = b + 16;
+    for (int c = 0; c < 4; c++) {
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(S, 2 * c, &sc0, &m0);
+        q4k_scale_min(S, 2 * c + 1, &sc1, &m1);
+        for (int l = 0; l < 32; l++) {
+            out[64 * c + l] = d * sc0 * (double)(Q[32 * c + l] & 15) - dmin * m0;
+            out[64 * c + 32 + l] = d * sc1 * (double)(Q[32 * c + l] >> 4) - dmin * m1;
+        }
+    }
+}
+
+/* Q6_K (210 B, 256 values): ql[128], qh[64], int8 scales[16], f16 d at byte
+ * 208.  Each half n of 128 values uses ql[64n..], qh[32n..], scales[8n..]; for
+ * l in 0..31 the four values at offsets l, l+32, l+64, l+96 take the low nibble
+ * of ql[l], low nibble of ql[l+32], high nibble of ql[l], high nibble of
+ * ql[l+32] as their low 4 bits and bit pairs 0-1, 2-3, 4-5, 6-7 of qh[l] as
+ * their top 2 bits; value = d * scale[l/16 + 2p] * (q - 32) for p = 0..3.
+ * [bonsai] "dequantizers" section, dequantQ6K. */
+static void deq_q6_k(const uint8_t *b, double *out)
+{
+    double d = or_f16(rd16(b + 208));
+    for (int n = 0; n < 2; n++) {
+        const uint8_t *ql = b + 64 * n, *qh = b + 128 + 32 * n;
+        const int8_t *sc = (const int8_t *)(b + 192 + 8 * n);
+        double *o = out + 128 * n;
+        for (int l = 0; l < 32; l++) {
+            int i = l / 16;
+            int q1 = ((ql[l] & 15) | (((qh[l] >> 0) & 3) << 4)) - 32;
+            int q2 = ((ql[l + 32] & 15) | (((qh[l] >> 2) & 3) << 4)) - 32;
+            int q3 = ((ql[l] >> 4) | (((qh[l] >> 4) & 3) << 4)) - 32;
+            int q4 = ((ql[l + 32] >> 4) | (((qh[l] >> 6) & 3) << 4)) - 32;
+            o[l] = d * sc[i + 0] * (double)q1;
+            o[l + 32] = d * sc[i + 2] * (double)q2;
+            o[l + 64] = d * sc[i + 4] * (double)q3;
+            o[l + 96] = d * sc[i + 6] * (double)q4;
+        }
+    }
+}
+
+static int deq_block(int type, const uint8_t *b, double *out)
+{
+    switch (type) {
+    case OR_Q8_0: deq_q8_0(b, out); return 0;
+    case OR_Q4_0: deq_q4_0(b, out); return 0;
+    case OR_Q4_K: deq_q4_k(b, out); return 0;
+    case OR_Q6_K: deq_q6_k(b, out); return 0;
+    default: return -1;
+    }
+}
+
+/* Dequantize n consecutive values (n a multiple of the block size). */
+int or_dequant(int type, const uint8_t *blocks, int64_t n, double *out)
+{
+    int qk = or_block_values(type), bb = or_block_bytes(type);
+    if (!qk || n % qk) return -1;
+    for (int64_t b = 0; b < n / qk; b++)
+        if (deq_block(type, blocks + b * bb, out + b * qk)) return -1;
+    return 0;
+}
+
+/* ------------------------------------------------------------ GEMV ---- */
+/* y[t][r] = sum_c W[r][c] * x[t][c] and A[t][r] = sum_c |W[r][c] * x[t][c]|,
+ * for the rows listed in row_idx (all rows when row_idx is NULL).  W is
+ * row-major in whole blocks: row r starts at byte r * (cols/QK) * block_bytes.
+ * The pages' GEMV kernels ([qwen3] WGSL matmulQ8, [gemma4] matmulQ4 and
+ * matmulQ6K, [bonsai] packed-weight GEMMs) all compute this sum. */
+static int gemv_impl(int type, const uint8_t *W, const float *x, int64_t rows,
+                     int64_t cols, int ntok, const int64_t *row_idx, int64_t n_idx,
+                     double *y, double *A)
+{
+    int qk = or_block_values(type), bb = or_block_bytes(type);
+    if (!qk || cols <= 0 || cols % qk || ntok <= 0) return -1;
+    int64_t row_bytes = (cols / qk) * bb;
+    int64_t nout = row_idx ? n_idx : rows;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)cols);
+        if (!w) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < nout; i++) {
+            if (!w) continue;
+            int64_t r = row_idx ? row_idx[i] : i;
+            if (r < 0 || r >= rows) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            or_dequant(type, W + r * row_bytes, cols, w);
+            for (int t = 0; t < ntok; t++) {
+                const float *xt = x + (int64_t)t * cols;
+                double s = 0.0, a = 0.0;
+                for (int64_t c = 0; c < cols; c++) {
+                    double p = w[c] * (double)xt[c];
+                    s += p;
+                    a += fabs(p);
+                }
+                y[(int64_t)t * nout + i] = s;
+                if (A) A[(int64_t)t * nout + i] = a;
+            }
+        }
+        free(w);
+    }
+    return bad ? -1 : 0;
+}
+
+int or_gemv(int type, const uint8_t *W, const float *x, int64_t rows, int64_t cols,
+            int ntok, double *y, double *A)
+{
+    return gemv_impl(type, W, x, rows, cols, ntok, NULL, 0, y, A);
+}
+
+/* Same sum for a sample of rows; y and A are [ntok][n_idx]. */
+int or_gemv_rows(int type, const uint8_t *W, const float *x, int64_t rows, int64_t cols,
+                 int ntok, const int64_t *row_idx, int64_t n_idx, double *y, double *A)
+{
+    if (!row_idx) return -1;
+    return gemv_impl(type, W, x, rows, cols, ntok, row_idx, n_idx, y, A);
+}
+
+/* Same sum with an f64 input vector (used for chained stages fed from the
+ * oracle's own f64 intermediates). */
+int or_gemv_f64(int type, const uint8_t *W, const double *x, int64_t rows, int64_t cols,
+                double *y, double *A)
+{
+    int qk = or_block_values(type), bb = or_block_bytes(type);
+    if (!qk || cols <= 0 || cols % qk) return -1;
+    int64_t row_bytes = (cols / qk) * bb;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)cols);
+#pragma omp for schedule(static)
+        for (int64_t r = 0; r < rows; r++) {
+            if (!w) continue;
+            or_dequant(type, W + r * row_bytes, cols, w);
+            double s = 0.0, a = 0.0;
+            for (int64_t c = 0; c < cols; c++) {
+                double p = w[c] * x[c];
+                s += p;
+                a += fabs(p);
+            }
+            y[r] = s;
+            if (A) A[r] = a;
+        }
+        free(w);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------ activations ---- */
+/* SiLU(g) = g / (1 + e^-g).  [qwen3] WGSL siluMulMoe; [dense] siluMul. */
+double or_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* GELU, tanh form, with the tanh argument clamped to [-10, 10]:
+ * 0.5 g (1 + tanh(clamp(0.7978845608 g (1 + 0.044715 g^2), -10, 10))).
+ * [gemma4] WGSL section, the GELU / tanhc helpers and geglu. */
+double or_gelu_tanh(double g)
+{
+    double u = 0.7978845608 * g * (1.0 + 0.044715 * g * g);
+    if (u < -10.0) u = -10.0;
+    if (u > 10.0) u = 10.0;
+    return 0.5 * g * (1.0 + tanh(u));
+}
+
+static double act_fn(int act, double g)
+{
+    return act == OR_ACT_GELU_TANH ? or_gelu_tanh(g) : or_silu(g);
+}
+
+/* act[f] = act_fn(gu[f]) * gu[F + f] for one [gate F | up F] vector.
+ * [dense] siluMul, [qwen3] siluMulMoe, [gemma4] geglu. */
+void or_glu(int act, const double *gu, int64_t F, double *out)
+{
+    for (int64_t f = 0; f < F; f++) out[f] = act_fn(act, gu[f]) * gu[F + f];
+}
+
+/* Same from f32 inputs (a stage fed with a GPU intermediate). */
+void or_glu_f32(int act, const float *gu, int64_t F, double *out)
+{
+    for (int64_t f = 0; f < F; f++)
+        out[f] = act_fn(act, (double)gu[f]) * (double)gu[F + f];
+}
+
+/* ------------------------------------------------------------ router ---- */
+/* Per token: the k experts with the largest logits, ties to the lower index,
+ * in pick order; weights renormalised over the picks:
+ * w_j = exp(l_j - lmax) / sum_{i in picks} exp(l_i - lmax).
+ * [qwen3] WGSL topk (softmax over the logits, k rounds of argmax with ties to
+ * the lowest index, division by the sum of the picked probabilities).  Ranking
+ * the logits is the same order as ranking exact probabilities, and the full
+ * softmax denominator cancels in the renormalised weights. */
+int or_router_topk(const float *logits, int E, int k, int ntok, int32_t *ids, double *w)
+{
+    if (E <= 0 || k <= 0 || k > E || ntok <= 0) return -1;
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    if (!taken) return -1;
+    for (int t = 0; t < ntok; t++) {
+        const float *l = logits + (int64_t)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep lower index */
+            }
+            taken[best] = 1;
+            ids[t * k + j] = best;
+        }
+        double lmax = (double)l[ids[t * k]];
+        double s = 0.0;
+        for (int j = 0; j < k; j++) s += exp((double)l[ids[t * k + j]] - lmax);
+        for (int j = 0; j < k; j++) w[t * k + j] = exp((double)l[ids[t * k + j]] - lmax) / s;
+    }
+    free(taken);
+    return 0;
+}
+
+/* --------------------------------------------------------------- MoE ---- */
+/* One routed-expert FFN over ntok tokens.
+ *   ids, c  = router(logits[t])                          (or_router_topk)
+ *   slot_j  = slots[ids_j]; a token with an absent pick (slot < 0) is skipped
+ *   gu_j    = W_gu[slot_j] . x[t]          (2F rows, gate rows first)
+ *   a_j     = act(gu_j[0:F]) * gu_j[F:2F]
+ *   dn_j    = W_d[slot_j] . a_j            (H rows)
+ *   y[t]    = sum_j (dn_j * s[ids_j]) * c_j   (s = 1 when down_scale is NULL)
+ * [qwen3] WGSL expertQ8 / siluMulMoe / moeAccum and engine encodeExperts;
+ * [gemma4] expertQ4 / geglu / moeSum (the per-expert down scale).
+ * Outputs: y and its bound A_y[t][h] = sum_j |c_j s_j| sum_f |W_d[h,f] a_j[f]|
+ * ([ntok][H] each), gu ([ntok][k][2F], may be NULL), ids/c ([ntok][k]).
+ * Returns the number of tokens skipped for an absent expert, or -1. */
+int or_moe_ffn(int type, int act, int64_t H, int64_t F, int E,
+               const uint8_t *gate_up, int64_t gu_stride,
+               const uint8_t *down, int64_t d_stride, const float *down_scale,
+               const float *logits, int k, const int32_t *slots,
+               const float *x, int ntok,
+               double *y, double *Ay, double *gu_out, int32_t *ids, double *c)
+{
+    if (or_router_topk(logits, E, k, ntok, ids, c)) return -1;
+    double *gu = (double *)malloc(sizeof(double) * (size_t)(2 * F));
+    double *a = (double *)malloc(sizeof(double) * (size_t)F);
+    double *dn = (double *)malloc(sizeof(double) * (size_t)H);
+    double *dA = (double *)malloc(sizeof(double) * (size_t)H);
+    double *xd = (double *)malloc(sizeof(double) * (size_t)H);
+    if (!gu || !a || !dn || !dA || !xd) return -1;
+    int skipped = 0;
+    for (int t = 0; t < ntok; t++) {
+        int absent = 0;
+        for (int j = 0; j < k; j++)
+            if (slots[ids[t * k + j]] < 0) absent = 1;
+        if (absent) { skipped++; continue; }
+        double *yt = y + (int64_t)t * H, *At = Ay + (int64_t)t * H;
+        for (int64_t h = 0; h < H; h++) { yt[h] = 0.0; At[h] = 0.0; }
+        for (int64_t h = 0; h < H; h++) xd[h] = (double)x[(int64_t)t * H + h];
+        for (int j = 0; j < k; j++) {
+            int e = ids[t * k + j];
+            int64_t slot = slots[e];
+            double s = down_scale ? (double)down_scale[e] : 1.0;
+            or_gemv_f64(type, gate_up + slot * gu_stride, xd, 2 * F, H, gu, NULL);
+            if (gu_out)
+                memcpy(gu_out + ((int64_t)t * k + j) * 2 * F, gu, sizeof(double) * (size_t)(2 * F));
+            or_glu(act, gu, F, a);
+            or_gemv_f64(type, down + slot * d_stride, a, H, F, dn, dA);
+            double cj = c[t * k + j];
+            for (int64_t h = 0; h < H; h++) {
+                yt[h] += (dn[h] * s) * cj;
+                At[h] += fabs(cj * s) * dA[h];
+            }
+        }
+    }
+    free(gu); free(a); free(dn); free(dA); free(xd);
+    return skipped;
+}
+
+/* The down half of the same FFN fed with a given gate||up stage (an f32
+ * intermediate read back from another implementation): per token and pick,
+ * a = act(gu[0:F]) * gu[F:2F], dn = W_d[slot] . a, y = sum_j (dn * s) * c_j.
+ * gu is [ntok][k][2F]; ids and c come from the caller.  Writes y, A_y and the
+ * weighted absolute row sums R[t][h] = sum_j |c_j s_j| sum_f |W_d[h,f]| * eps_f
+ * where eps_f = |g_f| * |u_f| (the scale of the activation's rounding error). */
+int or_moe_down(int type, int act, int64_t H, int64_t F,
+                const uint8_t *down, int64_t d_stride, const float *down_scale,
+                const int32_t *slots, const int32_t *ids, const double *c, int k,
+                const float *gu, int ntok, double *y, double *Ay, double *R)
+{
+    double *a = (double *)malloc(sizeof(double) * (size_t)F);
+    double *ga = (double *)malloc(sizeof(double) * (size_t)F);
+    double *dn = (double *)malloc(sizeof(double) * (size_t)H);
+    double *dA = (double *)malloc(sizeof(double) * (size_t)H);
+    double *dR = (double *)malloc(sizeof(double) * (size_t)H);
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)F);
+    if (!a || !ga || !dn || !dA || !dR || !wrow) return -1;
+    int qk = or_block_values(type), bb = or_block_bytes(type);
+    int64_t row_bytes = (F / qk) * bb;
+    for (int t = 0; t < ntok; t++) {
+        double *yt = y + (int64_t)t * H, *At = Ay + (int64_t)t * H, *Rt = R + (int64_t)t * H;
+        for (int64_t h = 0; h < H; h++) { yt[h] = 0.0; At[h] = 0.0; Rt[h] = 0.0; }
+        for (int j = 0; j < k; j++) {
+            int e = ids[t * k + j];
+            int64_t slot = slots[e];
+            double s = down_scale ? (double)down_scale[e] : 1.0;
+            const float *g = gu + ((int64_t)t * k + j) * 2 * F;
+            or_glu_f32(act, g, F, a);
+            for (int64_t f = 0; f < F; f++) ga[f] = fabs((double)g[f] * (double)g[F + f]);
+            or_gemv_f64(type, down + slot * d_stride, a, H, F, dn, dA);
+            for (int64_t h = 0; h < H; h++) {
+                or_dequant(type, down + slot * d_stride + h * row_bytes, F, wrow);
+                double r = 0.0;
+                for (int64_t f = 0; f < F; f++) r += fabs(wrow[f]) * ga[f];
+                dR[h] = r;
+            }
+            double cj = c[t * k + j];
+            for (int64_t h = 0; h < H; h++) {
+                yt[h] += (dn[h] * s) * cj;
+                At[h] += fabs(cj * s) * dA[h];
+                Rt[h] += fabs(cj * s) * dR[h];
+            }
+        }
+    }
+    free(a); free(ga); free(dn); free(dA); free(dR); free(wrow);
+    return 0;
+}
