@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Effective weight-HBM bandwidth of the quantized GEMV / MoE path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 1] [--all] [--no-cpu]
+
+A step is one pass of the named workload over one batch of synthetic inputs
+already resident in HBM.  The default workload is the Q8_0 dense Qwen3-style
+MLP decode (hidden 2560, ff 9728: gate||up -> SwiGLU -> down) followed by the
+tied-head GEMV [151936 x 2560], one token: 492,646,400 weight bytes per step.
+Two full copies of the weights alternate between steps so that no step finds
+its weights in the 256 MB last-level cache.
+
+Printed: one JSON line with the throughput (algorithmic weight bytes / time),
+the roofline of the dominant kernel (the head GEMV, timed with HIP events on
+the stream it runs on) and the oracle timed on the host cores.  --all adds one
+JSON line per other workload (parity-test shapes timed the same way) to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILE_FACTORS = {}           # filled from profiles/ when counter runs exist
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="1", help="0, 1, 2, 3a, 3b, 4, 4t16")
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------- workloads --
+class Workload:
+    name = ""
+    bytes_per_step = 0
+    dominant = ""            # kernel whose duration the roofline reports
+    dominant_bytes = 0
+
+    def step(self, i, ev=None):
+        raise NotImplementedError
+
+
+def _gen(seed):
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return g
+
+
+class DenseMlpHead(Workload):
+    """gate||up -> SwiGLU -> down (qg_mlp) then head GEMV (qg_gemv), Q8_0, T = 1."""
+
+    def __init__(self, copies=2, H=2560, F=9728, V=151936):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        self.qg = qg
+        self.H, self.F, self.V = H, F, V
+        self.sets = []
+        for c in range(copies):
+            g = _gen(100 + c)
+            self.sets.append(dict(
+                Wg=gs.device_weights(gs.Q8_0, F, H, g), Wu=gs.device_weights(gs.Q8_0, F, H, g),
+                Wd=gs.device_weights(gs.Q8_0, H, F, g), Wh=gs.device_weights(gs.Q8_0, V, H, g)))
+        self.x = gs.device_activations(1, H, _gen(7))
+        self.h = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        self.logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+        rb = gs.row_bytes(gs.Q8_0, H)
+        self.mlp_bytes = 2 * F * rb + H * gs.row_bytes(gs.Q8_0, F)
+        self.dominant_bytes = V * rb
+        self.bytes_per_step = self.mlp_bytes + self.dominant_bytes
+        self.name = "q8_0 dense MLP decode 2560x9728 (gate||up, SwiGLU, down) + tied head 151936x2560, 1 token"
+        self.dominant = "head GEMV Q8_0 151936x2560"
+
+    def step(self, i, ev=None):
+        qg = self.qg
+        s = self.sets[i % len(self.sets)]
+        qg.qg_mlp(qg.QG_Q8_0, qg.QG_ACT_SILU, s["Wg"], s["Wu"], s["Wd"], self.H, self.F, self.x, self.h, 1,
+                  self.ws)
+        if ev is not None:
+            ev[0].record()
+        qg.qg_gemv(qg.QG_Q8_0, s["Wh"], self.h, self.logits, self.V, self.H, 1)
+        if ev is not None:
+            ev[1].record()
+
+    def cpu_baseline(self, min_seconds=10.0):
+        """The oracle over the whole step (same shapes, numpy-drawn weights),
+        repeated until at least min_seconds of CPU time have passed."""
+        import oracle
+        import gguf_synth as gs
+        c = gs.config1(seed=0)
+        oracle.lib()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            yg, _ = oracle.gemv(gs.Q8_0, c["Wg"], c["x"], self.F, self.H)
+            yu, _ = oracle.gemv(gs.Q8_0, c["Wu"], c["x"], self.F, self.H)
+            import numpy as np
+            a = oracle.glu(oracle.ACT_SILU, np.concatenate([yg[0], yu[0]]), self.F)
+            h, _ = oracle.gemv_f64(gs.Q8_0, c["Wd"], a, self.H, self.F)
+            oracle.gemv(gs.Q8_0, c["Wh"], h.astype(np.float32), self.V, self.H)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds and reps >= 2:
+                break
+        return dict(value=round(self.bytes_per_step * reps / dt / 1e9, 3), unit="GB/s",
+                    cores=_oracle_threads(), kind="oracle",
+                    sample="the whole step (gate||up, SwiGLU, down, head 151936x2560), %d repetitions in %.1f s"
+                           % (reps, dt))
+
+
+def _oracle_threads():
+    n = os.environ.get("OMP_NUM_THREADS")
+    try:
+        return int(n) if n else os.cpu_count()
+    except ValueError:
+        return os.cpu_count()
+
+
+class GemvRot(Workload):
+    """One quantized GEMV, T tokens, rotating through distinct weight copies."""
+
+    def __init__(self, t, rows, cols, ntok, total_bytes, label):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        self.qg, self.t, self.rows, self.cols, self.ntok = qg, t, rows, cols, ntok
+        wb = rows * gs.row_bytes(t, cols)
+        copies = max(2, int(total_bytes // wb))
+        g = _gen(300 + t)
+        self.W = [gs.device_weights(t, rows, cols, g) for _ in range(copies)]
+        self.x = gs.device_activations(ntok, cols, g)
+        self.y = torch.empty((ntok, rows), dtype=torch.float32, device="cuda")
+        self.bytes_per_step = wb
+        self.dominant_bytes = wb
+        self.name = label
+        self.dominant = label
+
+    def step(self, i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        self.qg.qg_gemv(self.t, self.W[i % len(self.W)], self.x, self.y, self.rows, self.cols, self.ntok)
+        if ev is not None:
+            ev[1].record()
+
+
+class MoeLayers(Workload):
+    """qg_moe_ffn over L independent layers (pools, logits, x), T tokens."""
+
+    def __init__(self, t, act, H, F, E, k, ntok, layers, scale, label):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        self.qg, self.ntok, self.k = qg, ntok, k
+        rb_gu, rb_d = gs.row_bytes(t, H), gs.row_bytes(t, F)
+        rec = 2 * F * rb_gu + H * rb_d
+        self.layers = []
+        g = _gen(500 + t)
+        for _ in range(layers):
+            gu = gs.device_weights(t, E * 2 * F, H, g)        # E records of gate||up
+            dn = gs.device_weights(t, E * H, F, g)            # E records of down
+            lg = torch.randn((ntok, E), generator=g, device="cuda")
+            x = gs.device_activations(ntok, H, g)
+            ds = (torch.rand(E, generator=g, device="cuda") * 1.5 + 0.5) if scale else None
+            m = qg.make_moe(t, act, H, F, E, gu, 2 * F * rb_gu, dn, H * rb_d, ds)
+            self.layers.append(dict(m=m, gu=gu, dn=dn, lg=lg, x=x, ds=ds))
+        self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
+        self.y = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
+        self.ids = torch.empty((ntok, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((ntok, k), dtype=torch.float32, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.ws = torch.empty(qg.qg_moe_workspace_size(self.layers[0]["m"], k, ntok) // 4, dtype=torch.float32,
+                              device="cuda")
+        # algorithmic bytes: each distinct picked expert's record once
+        uniq = []
+        for L in self.layers:
+            lg = L["lg"].cpu()
+            ids = torch.topk(lg, k, dim=1).indices
+            uniq.append(len(set(ids.flatten().tolist())))
+        self.uniq = uniq
+        self.rec = rec
+        self.bytes_per_step = int(sum(uniq) / len(uniq) * rec)
+        self.dominant_bytes = self.bytes_per_step
+        self.name = label
+        self.dominant = label
+
+    def step(self, i, ev=None):
+        L = self.layers[i % len(self.layers)]
+        if ev is not None:
+            ev[0].record()
+        self.qg.qg_moe_ffn(L["m"], L["lg"], self.k, self.slots, L["x"], self.y, self.ntok, self.ids, self.w,
+                           self.status, self.ws)
+        if ev is not None:
+            ev[1].record()
+
+
+def make_workload(name, copies):
+    import gguf_synth as gs
+    big = 1.2e9   # bytes of distinct weight copies to rotate through (> 2x the 256 MB cache)
+    if name == "1":
+        return DenseMlpHead(copies=copies or 2)
+    if name == "0":
+        return GemvRot(gs.Q8_0, 1024, 2048, 1, big, "q8_0 GEMV 1024x2048, 1 token")
+    if name == "3a":
+        return GemvRot(gs.Q4_K, 17408, 5120, 1, big, "q4_k GEMV 17408x5120, 1 token")
+    if name == "3b":
+        return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token")
+    if name == "2":
+        return MoeLayers(gs.Q8_0, 0, 2048, 768, 128, 8, 1, 8, False,
+                         "q8_0 MoE layer 2048, 128 experts ff 768, top-8, 1 token")
+    if name in ("4", "4t16"):
+        T = 16 if name == "4t16" else 1
+        return MoeLayers(gs.Q4_0, 1, 2816, 704, 128, 8, T, 4, True,
+                         "q4_0 MoE layer 2816, 128 experts ff 704 (GELU, down scale), top-8, %d token(s)" % T)
+    raise SystemExit("unknown config " + name)
+
+
+def time_workload(wl, steps, warmup):
+    import torch
+    for i in range(warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        wl.step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return dt * 1e3 / steps, dom_ms
+
+
+def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
+    gbs = wl.bytes_per_step / (ms * 1e-3) / 1e9
+    dom_gbs = wl.dominant_bytes / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": "effective weight HBM GB/s (and % of peak) per quantized GEMV / MoE layer, 1 tok",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 accumulate over GGUF-quantized weights (q8_0/q4_0/q4_k/q6_k)",
+        "data": "synthetic (seeded), inputs resident in HBM",
+        "config": {"workload": wl.name, "bytes_per_step": wl.bytes_per_step, "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": wl.dominant, "bytes_per_launch": wl.dominant_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 3)},
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path has no multi-GPU leg); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import gguf_dequant_gemv_amd as qg
+    qg.lib()   # fails loudly if the HIP library is not built
+    log("[bench] workload", args.config)
+    wl = make_workload(args.config, args.copies)
+    ms, dom_ms = time_workload(wl, args.steps, args.warmup)
+    log("[bench] %.4f ms/step, dominant %.4f ms" % (ms, dom_ms))
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the oracle on the host cores")
+        cpu = wl.cpu_baseline() if hasattr(wl, "cpu_baseline") else None
+    print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu)), flush=True)
+    if args.all:
+        for name in ("0", "3a", "3b", "2", "4", "4t16"):
+            if name == args.config:
+                continue
+            log("[bench] workload", name)
+            w2 = make_workload(name, 0)
+            ms2, dom2 = time_workload(w2, args.steps, args.warmup)
+            log(json.dumps(result_line(w2, ms2, dom2, args.steps, args.warmup)))
+            del w2
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+"""Python binding of libqgemv (include/qgemv.h): argument marshalling only.
+
+Every function has the C entry point's name and argument order.  Device
+buffers are torch tensors on the GPU (or raw integer device addresses);
+`stream` defaults to torch's current stream.  Every step of the path runs in
+the HIP library; this module never computes anything itself and raises if the
+library is missing or a call fails.
+"""
+import ctypes
+import os
+
+QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 2, 8, 12, 14
+QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
+QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
+QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK = 16, 256, 32
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqgemv.so")
+
+# Every symbol include/qgemv.h declares.
+EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_dequant",
+           "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
+           "qg_moe_ffn")
+
+_lib = None
+
+
+class QgError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__("%s failed: %d (%s)" % (fn, code, strerror(code)))
+        self.code = code
+
+
+class qg_moe(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int), ("act", ctypes.c_int),
+                ("hidden", ctypes.c_int64), ("ff", ctypes.c_int64), ("n_experts", ctypes.c_int),
+                ("gate_up", ctypes.c_void_p), ("gate_up_stride", ctypes.c_int64),
+                ("down", ctypes.c_void_p), ("down_stride", ctypes.c_int64),
+                ("down_scale", ctypes.c_void_p), ("n_slots", ctypes.c_int)]
+
+
+def lib():
+    """The loaded libqgemv.so; raises FileNotFoundError if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError("libqgemv.so is not built: run python -m gguf_dequant_gemv_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.qg_block_values.argtypes = [i32]
+        L.qg_block_bytes.argtypes = [i32]
+        L.qg_strerror.argtypes = [i32]
+        L.qg_strerror.restype = ctypes.c_char_p
+        L.qg_gemv.argtypes = [i32, P, P, P, i64, i64, i32, P]
+        L.qg_dequant.argtypes = [i32, P, P, i64, i64, P]
+        L.qg_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
+        L.qg_mlp_workspace_size.argtypes = [i64, i32]
+        L.qg_mlp_workspace_size.restype = sz
+        L.qg_mlp.argtypes = [i32, i32, P, P, P, i64, i64, P, P, i32, P, sz, P]
+        L.qg_moe_workspace_size.argtypes = [ctypes.POINTER(qg_moe), i32, i32]
+        L.qg_moe_workspace_size.restype = sz
+        L.qg_moe_ffn.argtypes = [ctypes.POINTER(qg_moe), P, i32, P, P, P, i32, P, P, P, P, sz, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, rc):
+    if rc != QG_OK:
+        raise QgError(fn, rc)
+
+
+def strerror(code):
+    return lib().qg_strerror(code).decode()
+
+
+def qg_block_values(t):
+    return lib().qg_block_values(t)
+
+
+def qg_block_bytes(t):
+    return lib().qg_block_bytes(t)
+
+
+def qg_gemv(type, W, x, y, rows, cols, ntok=1, stream=None):
+    _check("qg_gemv", lib().qg_gemv(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _stream(stream)))
+
+
+def qg_dequant(type, W, out, rows, cols, stream=None):
+    _check("qg_dequant", lib().qg_dequant(type, _ptr(W), _ptr(out), rows, cols, _stream(stream)))
+
+
+def qg_router_topk(logits, n_experts, k, ntok, ids, weights, stream=None):
+    _check("qg_router_topk", lib().qg_router_topk(_ptr(logits), n_experts, k, ntok, _ptr(ids),
+                                                  _ptr(weights), _stream(stream)))
+
+
+def qg_mlp_workspace_size(ff, ntok):
+    return lib().qg_mlp_workspace_size(ff, ntok)
+
+
+def qg_mlp(type, act, W_gate, W_up, W_down, hidden, ff, x, y, ntok, workspace, workspace_bytes=None,
+           stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("qg_mlp", lib().qg_mlp(type, act, _ptr(W_gate), _ptr(W_up), _ptr(W_down), hidden, ff, _ptr(x),
+                                  _ptr(y), ntok, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def make_moe(type, act, hidden, ff, n_experts, gate_up, gate_up_stride, down, down_stride,
+             down_scale=None, n_slots=0):
+    return qg_moe(type, act, hidden, ff, n_experts, _ptr(gate_up), gate_up_stride, _ptr(down),
+                  down_stride, _ptr(down_scale), n_slots)
+
+
+def qg_moe_workspace_size(m, topk, ntok):
+    return lib().qg_moe_workspace_size(ctypes.byref(m), topk, ntok)
+
+
+def qg_moe_ffn(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace,
+               workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("qg_moe_ffn", lib().qg_moe_ffn(ctypes.byref(m), _ptr(router_logits), topk, _ptr(expert_slots),
+                                          _ptr(x), _ptr(y), ntok, _ptr(ids_out), _ptr(w_out), _ptr(status),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -1,0 +1,371 @@
+// qg_abi.hip -- the extern "C" entry points of libqgemv (see include/qgemv.h):
+// synchronous argument validation, launch planning and kernel dispatch.
+// Nothing here allocates memory or synchronises a stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/qgemv.h"
+#include "qg_kernels.h"
+
+using namespace qg;
+
+namespace {
+
+struct TypeInfo {
+    int qk, bytes;        // values / bytes per GGUF block
+    int unit_vals;        // values per lane unit (pair of blocks or one block)
+    int unit_bytes;
+    int max_unr;          // units a lane keeps in flight
+};
+
+bool type_info(int t, TypeInfo &ti) {
+    switch (t) {
+    case QG_Q8_0: ti = {32, 34, 64, 68, 4}; return true;
+    case QG_Q4_0: ti = {32, 18, 64, 36, 4}; return true;
+    case QG_Q4_K: ti = {256, 144, 256, 144, 2}; return true;
+    case QG_Q6_K: ti = {256, 210, 256, 210, 1}; return true;
+    default: return false;
+    }
+}
+
+constexpr int NUM_CU = 256;
+constexpr size_t LDS_MAX = 160 * 1024;
+
+struct Shape {
+    int type;
+    TypeInfo ti;
+    int64_t rows, row_bytes;
+    int cols, nb, upr;
+};
+
+int make_shape(int type, int64_t rows, int64_t cols, Shape &s) {
+    if (!type_info(type, s.ti)) return QG_EINVAL;
+    if (rows <= 0 || cols <= 0 || cols % s.ti.qk) return QG_EINVAL;
+    if (cols > (1 << 20) || rows > ((int64_t)1 << 40)) return QG_ELIMIT;
+    s.type = type;
+    s.rows = rows;
+    s.cols = (int)cols;
+    s.nb = (int)(cols / s.ti.qk);
+    s.row_bytes = (int64_t)s.nb * s.ti.bytes;
+    s.upr = (int)((cols + s.ti.unit_vals - 1) / s.ti.unit_vals);
+    return QG_OK;
+}
+
+size_t lds_bytes(const Shape &s, int nt) {
+    const int sums = s.type == QG_Q6_K ? 16 : (s.type == QG_Q8_0 ? 0 : 32);
+    const int cpad = s.upr * s.ti.unit_vals;   // x staged zero-padded to whole units
+    const size_t per = (size_t)xstride_of(cpad) + (sums ? cpad / sums : 0);
+    return (size_t)nt * per * sizeof(float);
+}
+
+struct Plan {
+    int lpr, unr, nt;
+    int ntiles, gx;
+    size_t lds;
+};
+
+// rows_align: a row index (the W0/W1 split) no wave may straddle; 0 = none.
+Plan make_plan(const Shape &s, int ntok_chunk_max, int64_t rows_align, int64_t parallel_copies) {
+    Plan p;
+    // tokens per workgroup: all of them up to 8, fewer if x would not fit
+    int nt = 1;
+    while (nt < ntok_chunk_max && nt < 8) nt <<= 1;
+    while (nt > 1 && lds_bytes(s, nt) > 64 * 1024) nt >>= 1;
+    p.nt = nt;
+    p.lds = lds_bytes(s, nt);
+    // lanes per row: best lane utilisation, then enough waves, then wider
+    const bool any_phase = (s.row_bytes & 3) != 0;   // rows alternate 0 / 2 mod 4
+    double best = -1.0;
+    int best_lpr = 64;
+    const int cands[5] = {64, 32, 16, 8, 4};
+    for (int ci = 0; ci < 5; ci++) {
+        const int lpr = cands[ci], rpw = 64 / lpr;
+        if (any_phase && rpw != 1) continue;
+        if (rows_align > 0 && rows_align % rpw) continue;
+        const int per_lane = (s.upr + lpr - 1) / lpr;
+        const double util = (double)s.upr / ((double)lpr * per_lane);
+        const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)parallel_copies;
+        const double fill = waves >= 4.0 * NUM_CU ? 1.0 : waves / (4.0 * NUM_CU);
+        const double score = util * (0.5 + 0.5 * fill);
+        if (score > best + 1e-9) { best = score; best_lpr = lpr; }
+    }
+    p.lpr = best_lpr;
+    const int per_lane = (s.upr + p.lpr - 1) / p.lpr;
+    p.unr = s.ti.max_unr;
+    while (p.unr > 1 && p.unr / 2 >= per_lane) p.unr >>= 1;
+    const int rpw = 64 / p.lpr;
+    const int64_t tile_rows = 4LL * rpw;
+    p.ntiles = (int)((s.rows + tile_rows - 1) / tile_rows);
+    // resident workgroups per CU, limited by LDS; spread tiles evenly
+    int per_cu = (int)(LDS_MAX / (p.lds + 512));
+    if (per_cu > 8) per_cu = 8;
+    if (per_cu < 1) per_cu = 1;
+    int64_t cap = (int64_t)NUM_CU * per_cu / (parallel_copies > 0 ? parallel_copies : 1);
+    if (cap < 1) cap = 1;
+    const int64_t tpw = (p.ntiles + cap - 1) / cap;
+    p.gx = (int)((p.ntiles + tpw - 1) / tpw);
+    return p;
+}
+
+#define QG_PICK_NT(NAME) \
+    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.lpr, p.unr) : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.lpr, p.unr) \
+     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.lpr, p.unr) : gemv_kernel_##NAME##_t8(p.lpr, p.unr))
+
+gemv_fn pick(int type, const Plan &p) {
+    switch (type) {
+    case QG_Q8_0: return QG_PICK_NT(q8_0);
+    case QG_Q4_0: return QG_PICK_NT(q4_0);
+    case QG_Q4_K: return QG_PICK_NT(q4_k);
+    default: return QG_PICK_NT(q6_k);
+    }
+}
+#undef QG_PICK_NT
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
+    a.row_bytes = s.row_bytes;
+    a.cols = s.cols;
+    a.upr = s.upr;
+    a.nb = s.nb;
+    a.rows = s.rows;
+    a.ntiles = p.ntiles;
+    gemv_fn f = pick(s.type, p);
+    if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
+        return QG_EHIP;
+    hipLaunchKernelGGL(f, grid, dim3(256), p.lds, st, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int qg_block_values(int type) {
+    TypeInfo ti;
+    return type_info(type, ti) ? ti.qk : 0;
+}
+
+int qg_block_bytes(int type) {
+    TypeInfo ti;
+    return type_info(type, ti) ? ti.bytes : 0;
+}
+
+const char *qg_strerror(int code) {
+    switch (code) {
+    case QG_OK: return "ok";
+    case QG_EINVAL: return "invalid argument (type, size, pointer or alignment)";
+    case QG_EABSENT: return "a picked expert has no pool slot";
+    case QG_EHIP: return "HIP launch or query failed";
+    case QG_ELIMIT: return "size limit exceeded (ntok <= 16, experts <= 256, topk <= 32)";
+    default: return "unknown error";
+    }
+}
+
+int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
+    Shape s;
+    int rc = make_shape(type, rows, cols, s);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+    if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
+    Plan p = make_plan(s, ntok, 0, 1);
+    GemvArgs a = {};
+    a.W0 = a.W1 = (const uint8_t *)W;
+    a.rows0 = rows;
+    a.x = x;
+    a.x_stride = cols;
+    a.xmode = XM_PLAIN;
+    a.y = y;
+    a.y_stride = rows;
+    a.ntok = ntok;
+    dim3 grid(p.gx, (ntok + p.nt - 1) / p.nt, 1);
+    return launch_gemv(s, p, a, grid, (hipStream_t)stream);
+}
+
+int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
+    Shape s;
+    int rc = make_shape(type, rows, cols, s);
+    if (rc) return rc;
+    if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;
+    const int64_t units = rows * s.upr;
+    dim3 grid((unsigned)((units + 255) / 256));
+    hipStream_t st = (hipStream_t)stream;
+    dequant_fn f = dequant_kernel(type);
+    hipLaunchKernelGGL(f, grid, dim3(256), 0, st, (const uint8_t *)W, out, rows, s.cols, s.row_bytes, s.upr, s.nb);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t *ids, float *weights, void *stream) {
+    if (n_experts < 1 || n_experts > QG_MAX_EXPERTS || k < 1 || k > QG_MAX_TOPK || k > n_experts ||
+        ntok < 1 || ntok > QG_MAX_TOKENS)
+        return QG_ELIMIT;
+    if (!logits || !ids || !weights || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
+        return QG_EINVAL;
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * ntok), 0, (hipStream_t)stream, logits, n_experts, k, ntok,
+                       (const int32_t *)nullptr, 1, ids, weights, (int32_t *)nullptr, ids, weights,
+                       (int32_t *)nullptr, (int32_t *)nullptr);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+size_t qg_mlp_workspace_size(int64_t ff, int ntok) {
+    if (ff <= 0 || ntok < 1 || ntok > QG_MAX_TOKENS) return 0;
+    return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float));
+}
+
+int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
+           const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
+    Shape s_gu, s_dn;
+    int rc = make_shape(type, 2 * ff, hidden, s_gu);
+    if (rc) return rc;
+    rc = make_shape(type, hidden, ff, s_dn);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+    if (act != QG_ACT_SILU && act != QG_ACT_GELU_TANH) return QG_EINVAL;
+    if (!W_gate || !W_up || !W_down || !x || !y || !workspace) return QG_EINVAL;
+    if (!aligned(W_gate, 2) || !aligned(W_up, 2) || !aligned(W_down, 2) || !aligned(x, 4) || !aligned(y, 4) ||
+        !aligned(workspace, 256))
+        return QG_EINVAL;
+    if (workspace_bytes < qg_mlp_workspace_size(ff, ntok)) return QG_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    float *gu = (float *)workspace;
+    // gate || up in one launch: rows [0, ff) from W_gate, [ff, 2ff) from W_up
+    Plan p1 = make_plan(s_gu, ntok, ff, 1);
+    GemvArgs a = {};
+    a.W0 = (const uint8_t *)W_gate;
+    a.W1 = (const uint8_t *)W_up;
+    a.rows0 = ff;
+    a.x = x;
+    a.x_stride = hidden;
+    a.xmode = XM_PLAIN;
+    a.y = gu;
+    a.y_stride = 2 * ff;
+    a.ntok = ntok;
+    rc = launch_gemv(s_gu, p1, a, dim3(p1.gx, (ntok + p1.nt - 1) / p1.nt, 1), st);
+    if (rc) return rc;
+    // down, with act(gate) * up formed while x is staged
+    Plan p2 = make_plan(s_dn, ntok, 0, 1);
+    GemvArgs b = {};
+    b.W0 = b.W1 = (const uint8_t *)W_down;
+    b.rows0 = hidden;
+    b.x = gu;
+    b.x_stride = 2 * ff;
+    b.xmode = act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    b.y = y;
+    b.y_stride = hidden;
+    b.ntok = ntok;
+    return launch_gemv(s_dn, p2, b, dim3(p2.gx, (ntok + p2.nt - 1) / p2.nt, 1), st);
+}
+
+// Workspace layout for qg_moe_ffn (each part 256-byte aligned, in order):
+//   gu [T*k][2F] f32 | dn [T*k][H] f32 | ids [T*k] i32 | w [T*k] f32 |
+//   valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32
+namespace {
+struct MoeWs {
+    size_t gu, dn, ids, w, valid, grp, total;
+};
+MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
+    MoeWs o;
+    size_t off = 0;
+    const size_t pairs = (size_t)T * k;
+    const size_t groups = pairs < (size_t)E ? pairs : (size_t)E;
+    o.gu = off; off += align256(pairs * 2 * (size_t)F * 4);
+    o.dn = off; off += align256(pairs * (size_t)H * 4);
+    o.ids = off; off += align256(pairs * 4);
+    o.w = off; off += align256(pairs * 4);
+    o.valid = off; off += align256((size_t)T * 4);
+    o.grp = off; off += align256((1 + groups * GREC) * 4);
+    o.total = off;
+    return o;
+}
+}  // namespace
+
+size_t qg_moe_workspace_size(const qg_moe *m, int topk, int ntok) {
+    if (!m || m->hidden <= 0 || m->ff <= 0 || m->n_experts < 1 || topk < 1 || ntok < 1 || ntok > QG_MAX_TOKENS)
+        return 0;
+    return moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok).total;
+}
+
+int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
+               float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    if (!m) return QG_EINVAL;
+    const int E = m->n_experts;
+    if (E < 1 || E > QG_MAX_EXPERTS || topk < 1 || topk > QG_MAX_TOPK || topk > E || ntok < 1 ||
+        ntok > QG_MAX_TOKENS)
+        return QG_ELIMIT;
+    if (m->act != QG_ACT_SILU && m->act != QG_ACT_GELU_TANH) return QG_EINVAL;
+    Shape s_gu, s_dn;
+    int rc = make_shape(m->type, 2 * m->ff, m->hidden, s_gu);
+    if (rc) return rc;
+    rc = make_shape(m->type, m->hidden, m->ff, s_dn);
+    if (rc) return rc;
+    if (!m->gate_up || !m->down || !router_logits || !expert_slots || !x || !y || !status || !workspace)
+        return QG_EINVAL;
+    if (m->gate_up_stride < s_gu.rows * s_gu.row_bytes || m->down_stride < s_dn.rows * s_dn.row_bytes)
+        return QG_EINVAL;
+    if (!aligned(m->gate_up, 2) || !aligned(m->down, 2) || (m->gate_up_stride & 1) || (m->down_stride & 1) ||
+        !aligned(router_logits, 4) || !aligned(expert_slots, 4) || !aligned(x, 4) || !aligned(y, 4) ||
+        !aligned(status, 4) || !aligned(workspace, 256) || (m->down_scale && !aligned(m->down_scale, 4)))
+        return QG_EINVAL;
+    const int64_t H = m->hidden, F = m->ff;
+    const MoeWs L = moe_ws(H, F, E, topk, ntok);
+    if (workspace_bytes < L.total) return QG_EINVAL;
+    uint8_t *ws = (uint8_t *)workspace;
+    float *gu = (float *)(ws + L.gu);
+    float *dn = (float *)(ws + L.dn);
+    int32_t *rt_ids = (int32_t *)(ws + L.ids);
+    float *rt_w = (float *)(ws + L.w);
+    int32_t *rt_valid = (int32_t *)(ws + L.valid);
+    int32_t *grp = (int32_t *)(ws + L.grp);
+    hipStream_t st = (hipStream_t)stream;
+
+    // 1. route: top-k, weights, slot lookup, grouping by expert
+    const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
+    const int n_slots = m->n_slots > 0 ? m->n_slots : E;
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots, n_slots, ids_out,
+                       w_out, status, rt_ids, rt_w, rt_valid, grp);
+    if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    const int pairs = ntok * topk;
+    const int gmax = pairs < E ? pairs : E;
+
+    // 2. gate || up for every group of pairs that picked the same expert
+    Plan p1 = make_plan(s_gu, ntok, 0, gmax);
+    GemvArgs a = {};
+    a.W0 = a.W1 = (const uint8_t *)m->gate_up;
+    a.rows0 = s_gu.rows;
+    a.slot_stride = m->gate_up_stride;
+    a.x = x;
+    a.x_stride = H;
+    a.xmode = XM_PLAIN;
+    a.y = gu;
+    a.y_stride = 2 * F;
+    a.grp = grp;
+    a.in_by_pair = 0;
+    rc = launch_gemv(s_gu, p1, a, dim3(p1.gx, gmax, (ntok + p1.nt - 1) / p1.nt), st);
+    if (rc) return rc;
+
+    // 3. down on act(gate) * up, per pair
+    Plan p2 = make_plan(s_dn, ntok, 0, gmax);
+    GemvArgs b = {};
+    b.W0 = b.W1 = (const uint8_t *)m->down;
+    b.rows0 = s_dn.rows;
+    b.slot_stride = m->down_stride;
+    b.x = gu;
+    b.x_stride = 2 * F;
+    b.xmode = m->act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    b.y = dn;
+    b.y_stride = H;
+    b.grp = grp;
+    b.in_by_pair = 1;
+    rc = launch_gemv(s_dn, p2, b, dim3(p2.gx, gmax, (ntok + p2.nt - 1) / p2.nt), st);
+    if (rc) return rc;
+
+    // 4. weighted combine in pick order
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), ntok), dim3(256), 0, st, dn, rt_ids, rt_w,
+                       rt_valid, m->down_scale, y, H, topk);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+}  // extern "C"

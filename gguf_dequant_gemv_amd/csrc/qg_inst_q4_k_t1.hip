@@ -1,0 +1,3 @@
+// Q4_K GEMV instances with 1 token(s) per workgroup.
+#include "qg_inst.h"
+QG_GEMV_INSTANCES(q4_k, qg::T_Q4_K, 1)

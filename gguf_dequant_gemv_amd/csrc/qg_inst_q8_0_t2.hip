@@ -1,0 +1,3 @@
+// Q8_0 GEMV instances with 2 token(s) per workgroup.
+#include "qg_inst.h"
+QG_GEMV_INSTANCES(q8_0, qg::T_Q8_0, 2)

@@ -1,0 +1,143 @@
+// qg_route.hip -- router top-k / expert grouping and the MoE combine (gfx950).
+#include "qg_kernels.h"
+
+namespace qg {
+
+// -------------------------------------------------------------- router ----
+// One wave per token: the k largest logits (ties to the lower index) in pick
+// order, and exp(l_j - l_0) / sum over the picks.  The qwen3_moe_ssd.js topk
+// kernel's selection and renormalisation; ranking logits orders as ranking
+// the probabilities does.  With `grp` set it also groups the (token, pick)
+// pairs by expert for the expert GEMVs (slot lookup, absent-expert status).
+QG_DEV u32 order_key(float f) {  // monotone map f32 -> u32 (-0 folded onto +0)
+    u32 u = __builtin_bit_cast(u32, f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+QG_DEV unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const unsigned long long o = __shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+QG_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+__global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int k, int T,
+                                                const int32_t *slots, int n_slots, int32_t *ids_out, float *w_out,
+                                                int32_t *status, int32_t *rt_ids, float *rt_w,
+                                                int32_t *rt_valid, int32_t *grp) {
+    __shared__ int s_ids[MAXT * 32];
+    __shared__ int s_valid[MAXT];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave < T) {
+        const float *l = logits + (int64_t)wave * E;
+        u32 key[4];
+        u32 taken = 0u;  // bit i: value lane + 64 i is picked or absent
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? order_key(l[e]) : 0u;
+            if (e >= E) taken |= 1u << i;
+        }
+        for (int j = 0; j < k; j++) {
+            u32 bk = 0u;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || key[i] > bk)) { bk = key[i]; bi = lane + 64 * i; }
+            unsigned long long kk = bi == 0x7FFFFFFF ? 0ull : (((unsigned long long)bk << 32) | (u32)(~(u32)bi));
+            kk = wave_max_u64(kk);
+            const int e = (int)(~(u32)(kk & 0xFFFFFFFFull));
+            if ((e & 63) == lane) taken |= 1u << (e >> 6);
+            if (lane == 0) s_ids[wave * k + j] = e;
+        }
+        __builtin_amdgcn_wave_barrier();
+        // weights over the picks, relative to the top pick
+        float ex = 0.0f;
+        const float l0 = l[s_ids[wave * k]];
+        if (lane < k) ex = expf(l[s_ids[wave * k + lane]] - l0);
+        const float sum = wave_sum(ex);
+        if (lane < k) {
+            const float wj = ex / sum;
+            const int z = wave * k + lane;
+            if (rt_ids) rt_ids[z] = s_ids[z];
+            if (rt_w) rt_w[z] = wj;
+            if (ids_out) ids_out[z] = s_ids[z];
+            if (w_out) w_out[z] = wj;
+        }
+        if (lane == 0) {
+            int ok = 1;
+            for (int j = 0; j < k; j++) {
+                const int sl = slots ? slots[s_ids[wave * k + j]] : 0;
+                ok &= (sl >= 0 && sl < n_slots);
+            }
+            s_valid[wave] = ok;
+            if (rt_valid) rt_valid[wave] = ok;
+        }
+    }
+    __syncthreads();
+    if (!grp) return;
+    // Group pairs by expert: ascending expert id, pairs in (t, j) order.
+    // Thread e (< E) counts its expert's pairs; the group index is the number
+    // of lower experts with pairs (ballot per wave, wave totals through LDS).
+    __shared__ int s_wcnt[16];
+    int cnt = 0;
+    if (tid < E)
+        for (int z = 0; z < T * k; z++) cnt += (s_valid[z / k] && s_ids[z] == tid);
+    const unsigned long long mask = __ballot(tid < E && cnt > 0);
+    if (lane == 0) s_wcnt[wave] = __popcll(mask);
+    __syncthreads();
+    int base = 0;
+    for (int w2 = 0; w2 < wave; w2++) base += s_wcnt[w2];
+    const int gi = base + __popcll(mask & ((1ull << lane) - 1ull));
+    if (tid == 0) {
+        int ok = 1, G = 0;
+        for (int t = 0; t < T; t++) ok &= s_valid[t];
+        for (int w2 = 0; w2 < (int)(blockDim.x >> 6); w2++) G += s_wcnt[w2];
+        if (status) *status = ok ? 0 : -2;  // QG_OK / QG_EABSENT
+        grp[0] = G;
+    }
+    if (tid < E && cnt > 0) {
+        int *rec = grp + 1 + gi * GREC;
+        int n = 0;
+        for (int z = 0; z < T * k; z++) {
+            if (s_valid[z / k] && s_ids[z] == tid) {
+                rec[3 + n] = z / k;
+                rec[19 + n] = z;
+                n++;
+            }
+        }
+        rec[0] = tid;
+        rec[1] = slots[tid];
+        rec[2] = n;
+    }
+}
+
+// ------------------------------------------------------------- combine ----
+// y[t][h] = sum_j (dn[t*k + j][h] * s[id]) * w_j, added in pick order (the
+// gemma4_moe_ssd.js moeSum / qwen3_moe_ssd.js moeAccum combine); tokens with
+// an absent pick are left untouched.
+__global__ __launch_bounds__(256) void k_combine(const float *dn, const int32_t *rt_ids, const float *rt_w,
+                                                 const int32_t *rt_valid, const float *dscale, float *y,
+                                                 int64_t H, int k) {
+    const int t = blockIdx.y;
+    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (h >= H || !rt_valid[t]) return;
+    float acc = 0.0f;
+    for (int j = 0; j < k; j++) {
+        const int z = t * k + j;
+        const float s = dscale ? dscale[rt_ids[z]] : 1.0f;
+        acc += (dn[(int64_t)z * H + h] * s) * rt_w[z];
+    }
+    y[(int64_t)t * H + h] = acc;
+}
+
+}  // namespace qg

@@ -42,7 +42,7 @@ def q8_0(g, rows, cols, sigma=0.02):
     """d = f16(|N(0, sigma)|); codes uniform int8 on [-127, 127]."""
     nb = rows * (cols // 32)
     d = _abs_normal_f16(g, nb, sigma)
-    q = g.integers(-127, 128, size=(nb, 32), dtype=np.int64).astype(np.int8).view(np.uint8)
+    q = g.integers(-127, 128, size=(nb, 32), dtype=np.int8).view(np.uint8)
     return np.concatenate([d, q], axis=1).reshape(rows, -1)
 
 
@@ -50,7 +50,7 @@ def q4_0(g, rows, cols, sigma=0.02):
     """d = f16(|N(0, sigma)|); nibble bytes uniform on 0..255 (nibbles uniform 0..15)."""
     nb = rows * (cols // 32)
     d = _abs_normal_f16(g, nb, sigma)
-    q = g.integers(0, 256, size=(nb, 16), dtype=np.int64).astype(np.uint8)
+    q = g.integers(0, 256, size=(nb, 16), dtype=np.uint8)
     return np.concatenate([d, q], axis=1).reshape(rows, -1)
 
 
@@ -59,17 +59,17 @@ def q4_k(g, rows, cols, sigma=0.01):
     nb = rows * (cols // 256)
     d = _abs_normal_f16(g, nb, sigma)
     dmin = _abs_normal_f16(g, nb, sigma)
-    sc = g.integers(0, 256, size=(nb, 12), dtype=np.int64).astype(np.uint8)
-    qs = g.integers(0, 256, size=(nb, 128), dtype=np.int64).astype(np.uint8)
+    sc = g.integers(0, 256, size=(nb, 12), dtype=np.uint8)
+    qs = g.integers(0, 256, size=(nb, 128), dtype=np.uint8)
     return np.concatenate([d, dmin, sc, qs], axis=1).reshape(rows, -1)
 
 
 def q6_k(g, rows, cols, sigma=0.01):
     """ql, qh bytes uniform; int8 scales uniform over all 256 values; d = f16(|N(0, sigma)|)."""
     nb = rows * (cols // 256)
-    ql = g.integers(0, 256, size=(nb, 128), dtype=np.int64).astype(np.uint8)
-    qh = g.integers(0, 256, size=(nb, 64), dtype=np.int64).astype(np.uint8)
-    sc = g.integers(0, 256, size=(nb, 16), dtype=np.int64).astype(np.uint8)
+    ql = g.integers(0, 256, size=(nb, 128), dtype=np.uint8)
+    qh = g.integers(0, 256, size=(nb, 64), dtype=np.uint8)
+    sc = g.integers(0, 256, size=(nb, 16), dtype=np.uint8)
     d = _abs_normal_f16(g, nb, sigma)
     return np.concatenate([ql, qh, sc, d], axis=1).reshape(rows, -1)
 
@@ -173,3 +173,36 @@ def config4(seed=0, ntok=1, E=128):
                 Fd=Fd, F=F, E=E, k=k, Wg=Wg, Wu=Wu, Wd=Wd, pool=pool, record=rec,
                 gu_off=gu_off, d_off=d_off, down_scale=ds, logits=lg, x=x, ntok=ntok,
                 slots=np.arange(E, dtype=np.int32))
+
+
+# ---- the same recipes drawn on the GPU (timing-size inputs) ------------------
+# Seeded torch generator on the device; same distributions and byte layout as
+# the numpy generators above (a different random stream).  Used where only
+# the shapes and distributions matter (bandwidth timing), never for parity.
+
+def device_weights(t, rows, cols, gen, device="cuda", sigma=None):
+    import torch
+    sigma = DEFAULT_SIGMA[t] if sigma is None else sigma
+    nb = rows * (cols // QK[t])
+
+    def f16(n):
+        return (torch.randn(n, generator=gen, device=device) * sigma).abs().half().view(torch.uint8).view(n, 2)
+
+    def u8(n, k):
+        return torch.randint(0, 256, (n, k), generator=gen, device=device, dtype=torch.uint8)
+
+    if t == Q8_0:
+        q = torch.randint(-127, 128, (nb, 32), generator=gen, device=device, dtype=torch.int8).view(torch.uint8)
+        parts = [f16(nb), q]
+    elif t == Q4_0:
+        parts = [f16(nb), u8(nb, 16)]
+    elif t == Q4_K:
+        parts = [f16(nb), f16(nb), u8(nb, 12), u8(nb, 128)]
+    else:
+        parts = [u8(nb, 128), u8(nb, 64), u8(nb, 16), f16(nb)]
+    return torch.cat(parts, dim=1).view(rows, -1)
+
+
+def device_activations(ntok, n, gen, device="cuda"):
+    import torch
+    return torch.randn((ntok, n), generator=gen, device=device, dtype=torch.float32)

@@ -1,0 +1,177 @@
+/*
+ * qgemv.h -- C ABI of libqgemv: decode-time matrix-vector products over GGUF
+ * block-quantized weights, dequantized inside HIP kernels for gfx950 (MI355X)
+ * with f32 accumulation, and the routed mixture-of-experts step built on them.
+ *
+ * Sources (the diskformer package-diff pages this library follows):
+ *   [bonsai]  diskformer 0.5.4 -> 0.6.6, engines/ternary_bonsai_2_dflash.js
+ *   [gemma4]  diskformer 0.0.1 -> 0.2.0, engines/gemma4_moe_ssd.js
+ *   [qwen3]   diskformer 0.0.1 -> 0.3.0, engines/qwen3_moe_ssd.js
+ *   [qwen35]  diskformer 0.0.1 -> 0.3.0, engines/qwen35_moe_ssd.js
+ *   [dense]   diskformer 0.5.4 -> 0.6.6, engines/qwen35_dense.js
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *     caller owns all memory (the library allocates nothing on any call).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return without synchronising; results are valid once the
+ *     stream has reached that point.
+ *   - Return value: QG_OK, or a negative qg_err code from synchronous argument
+ *     validation (nothing is enqueued then), or QG_EHIP when a launch fails.
+ *     No C++ exception crosses the ABI.
+ *   - Weights are GGUF block streams: row-major, rows contiguous, row r at byte
+ *     r * (cols / QK) * block_bytes, blocks exactly as GGUF stores them (no
+ *     padding, no plane split).  W needs only 2-byte alignment.  The GGUF dims
+ *     order is (cols, rows): dims[0] is the contiguous, quantized axis.
+ *   - Activations are f32, token-major: x is [ntok][cols], y is [ntok][rows].
+ *     Outputs are overwritten (no residual add).
+ *   - 1 <= ntok <= QG_MAX_TOKENS; cols must be a multiple of the block's QK.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block types, numbered as GGML/GGUF number them ([bonsai] GGUF reader prints
+ * Q4_K = 12 and Q6_K = 14; Q4_0 = 2 and Q8_0 = 8 are the same enum).
+ *   Q8_0  34 B / 32 values : f16 d | int8 q[32]            value = d*q
+ *         ([qwen3] header comment and WGSL i8at / matmulQ8)
+ *   Q4_0  18 B / 32 values : f16 d | 16 B nibbles           value = (nib-8)*d,
+ *         byte j holds value j (low nibble) and j+16 (high) ([gemma4] q4dot)
+ *   Q4_K 144 B / 256 values: f16 d | f16 dmin | scales[12] | qs[128]
+ *         value = d*sc*q - dmin*m per 32-value sub-block ([bonsai] dequantQ4K)
+ *   Q6_K 210 B / 256 values: ql[128] | qh[64] | int8 scales[16] | f16 d
+ *         value = d*sc*(q-32) per 16 values ([bonsai] dequantQ6K)            */
+enum qg_type { QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14 };
+
+/* Gated activations: act(gate) * up.
+ *   QG_ACT_SILU       gate / (1 + exp(-gate))           ([qwen3] siluMulMoe)
+ *   QG_ACT_GELU_TANH  0.5 g (1 + tanh(clamp(0.7978845608 g (1 + 0.044715 g^2),
+ *                     -10, 10)))                         ([gemma4] GELU, geglu) */
+enum qg_act { QG_ACT_SILU = 0, QG_ACT_GELU_TANH = 1 };
+
+enum qg_err {
+    QG_OK = 0,
+    QG_EINVAL = -1,   /* bad type, size, pointer or alignment                  */
+    QG_EABSENT = -2,  /* (status word only) a picked expert has no slot        */
+    QG_EHIP = -3,     /* a HIP launch or query failed                           */
+    QG_ELIMIT = -4    /* a size limit below is exceeded                         */
+};
+
+#define QG_MAX_TOKENS 16    /* small-batch (speculative verify) limit          */
+#define QG_MAX_EXPERTS 256  /* router width limit ([qwen3] engine: n <= 256)    */
+#define QG_MAX_TOPK 32      /* picks per token limit ([qwen3] engine: k <= 32)  */
+
+/* Values and bytes per block of `type`; 0 for an unknown type.  Host only. */
+int qg_block_values(int type);
+int qg_block_bytes(int type);
+
+/* Human-readable name of a qg_err code (static string).  Host only. */
+const char *qg_strerror(int code);
+
+/* Quantized GEMV / small-batch GEMV.
+ *   y[t][r] = sum_c W[r][c] * x[t][c]   for t < ntok, r < rows
+ * with W dequantized in registers and f32 accumulation.  Each weight byte is
+ * read once per call for ntok <= 8 (twice at most for ntok <= 16 when the
+ * tokens do not fit in local memory together).
+ * The sum the pages' GEMV kernels compute: [qwen3] WGSL matmulQ8, [gemma4]
+ * matmulQ4 / matmulQ6K, [bonsai] packed-weight GEMMs, [qwen35] matmulQ8T.
+ * W: rows x cols GGUF blocks; x: [ntok][cols] f32; y: [ntok][rows] f32.
+ * Errors: QG_EINVAL (type, rows<=0, cols<=0 or cols % QK, null pointer, W not
+ * 2-byte aligned, x/y not 4-byte aligned), QG_ELIMIT (ntok outside 1..16). */
+int qg_gemv(int type, const void *W, const float *x, float *y,
+            int64_t rows, int64_t cols, int ntok, void *stream);
+
+/* Dequantize a whole tensor: out[r][c] = W[r][c] as f32, bit-exact (each
+ * value is the f32 nearest to its exact value; for Q8_0, Q4_0 and Q6_K the
+ * exact value is always an f32).  The block-unpack layer's test hook.
+ * Formulas: [bonsai] dequantQ4K / dequantQ6K, [gemma4] q4dot, [qwen3] i8at.
+ * Errors: as qg_gemv (no ntok). */
+int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream);
+
+/* Router: per token, the k experts with the largest logits (ties go to the
+ * lower expert index), in pick order, and their weights renormalised over the
+ * picks: w_j = exp(l_j - l_max) / sum_{i picked} exp(l_i - l_max).  This is the
+ * [qwen3] WGSL topk kernel (softmax, k argmax rounds with ties to the lowest
+ * index, renormalisation); the selection ranks logits, which orders exactly as
+ * the probabilities do.
+ * logits: [ntok][n_experts] f32; ids: [ntok][k] int32; weights: [ntok][k] f32.
+ * Errors: QG_EINVAL (null pointer), QG_ELIMIT (n_experts outside 1..256, k
+ * outside 1..min(32, n_experts), ntok outside 1..16). */
+int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
+                   int32_t *ids, float *weights, void *stream);
+
+/* Dense gated MLP (one FFN without norms or residual):
+ *   gu   = [W_gate x | W_up x]               (one launch, gate rows first)
+ *   a    = act(gu[0:ff]) * gu[ff:2ff]          (fused into the down launch)
+ *   y    = W_down a
+ * [dense] encodeLayer (gate and up into the two halves of one buffer, siluMul,
+ * down); [gemma4] dense GELU MLP (geglu).
+ * W_gate, W_up: ff x hidden; W_down: hidden x ff (same block type).
+ * x: [ntok][hidden], y: [ntok][hidden].
+ * workspace: device scratch of at least qg_mlp_workspace_size(ff, ntok) bytes,
+ * 256-byte aligned.  After the call it holds gu as [ntok][2*ff] f32 at offset 0
+ * (a documented intermediate, useful for staged checking).
+ * Errors: as qg_gemv for both shapes, QG_EINVAL for a short workspace or an
+ * unknown act. */
+size_t qg_mlp_workspace_size(int64_t ff, int ntok);
+int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down,
+           int64_t hidden, int64_t ff, const float *x, float *y, int ntok,
+           void *workspace, size_t workspace_bytes, void *stream);
+
+/* A pool of routed experts (a HOST struct; its pointers are device pointers).
+ * Expert e lives in pool slot expert_slots[e] (0 <= slot < n_slots); the
+ * weights of slot s are
+ *   gate_up + s * gate_up_stride : (2 ff) x hidden blocks, gate rows first
+ *   down    + s * down_stride    : hidden x ff blocks
+ * (strides in bytes; [qwen3] expert record guQ then dQ, [gemma4] fused
+ * ffn_gate_up_exps).  down_scale: [n_experts] f32 per-expert factor applied to
+ * the down output ([gemma4] moeSum), or NULL for 1. */
+typedef struct qg_moe {
+    int type;            /* qg_type of both projections                        */
+    int act;             /* qg_act                                             */
+    int64_t hidden;      /* H: x and y width                                   */
+    int64_t ff;          /* F: expert feed-forward width                       */
+    int n_experts;       /* E: router width                                    */
+    const void *gate_up; int64_t gate_up_stride;
+    const void *down;    int64_t down_stride;
+    const float *down_scale;
+    int n_slots;         /* slots in the pool; a slot outside [0, n_slots) is
+                            treated as absent.  0 means n_experts.          */
+} qg_moe;
+
+/* Routed-expert FFN for ntok tokens ([qwen3] encodeExperts: topk, expertQ8 on
+ * gate||up, siluMulMoe, expertQ8 on down, moeAccum; [gemma4] encodeExpertsB:
+ * topkB, expertQ4B, geglu, expertQ4B, moeSumB):
+ *   ids, c = router(router_logits[t])       (as qg_router_topk)
+ *   gu_j   = W_gate_up[slot(ids_j)] x[t]
+ *   a_j    = act(gu_j[0:F]) * gu_j[F:2F]
+ *   dn_j   = W_down[slot(ids_j)] a_j
+ *   y[t]   = sum_j (dn_j * s[ids_j]) * c_j   (pick order)
+ * Pairs that pick the same expert are grouped so each picked expert's weights
+ * are read once per call for all the tokens that picked it.
+ * m: host pointer to the pool description.
+ * router_logits: [ntok][E]; expert_slots: [E] int32 (-1 = not resident);
+ * x, y: [ntok][H]; ids_out: [ntok][topk] int32; w_out: [ntok][topk] f32
+ * (both may be NULL); status: one device int32, set to QG_OK or QG_EABSENT.
+ * A token with an absent pick gets no output (its y row is left as it was)
+ * and the status word reads QG_EABSENT.
+ * workspace: at least qg_moe_workspace_size(m, topk, ntok) bytes, 256-byte
+ * aligned.  After the call it holds, at offset 0, gu as [ntok][topk][2F] f32.
+ * Errors: as qg_gemv for both shapes; QG_ELIMIT (n_experts > 256, topk > 32 or
+ * > n_experts, ntok > 16); QG_EINVAL (short workspace, null pointer, bad act). */
+size_t qg_moe_workspace_size(const qg_moe *m, int topk, int ntok);
+int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk,
+               const int32_t *expert_slots, const float *x, float *y, int ntok,
+               int32_t *ids_out, float *w_out, int32_t *status,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QGEMV_H */

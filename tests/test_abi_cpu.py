@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, reports block sizes, and rejects bad arguments synchronously
+(these calls return before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_dequant_gemv_amd as qg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+# a fake, never-dereferenced device address (validation fails before any use)
+FAKE = 0x7F0000000000
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(qg_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_lists_the_binding_exports():
+    assert sorted(qg.EXPORTS) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    L = qg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_block_sizes():
+    assert [qg.qg_block_values(t) for t in (2, 8, 12, 14)] == [32, 32, 256, 256]
+    assert [qg.qg_block_bytes(t) for t in (2, 8, 12, 14)] == [18, 34, 144, 210]
+    assert qg.qg_block_values(3) == 0 and qg.qg_block_bytes(99) == 0
+
+
+def test_strerror():
+    for c in (0, -1, -2, -3, -4, 7):
+        assert isinstance(qg.strerror(c), str) and qg.strerror(c)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((99, FAKE, FAKE, FAKE, 16, 64, 1), qg.QG_EINVAL),          # unknown type
+    ((8, FAKE, FAKE, FAKE, 16, 48, 1), qg.QG_EINVAL),           # cols % 32
+    ((12, FAKE, FAKE, FAKE, 16, 512 + 32, 1), qg.QG_EINVAL),    # cols % 256
+    ((8, FAKE, FAKE, FAKE, 0, 64, 1), qg.QG_EINVAL),            # rows
+    ((8, FAKE, FAKE, FAKE, 16, 64, 0), qg.QG_ELIMIT),           # ntok
+    ((8, FAKE, FAKE, FAKE, 16, 64, 17), qg.QG_ELIMIT),
+    ((8, None, FAKE, FAKE, 16, 64, 1), qg.QG_EINVAL),           # null W
+    ((8, FAKE + 1, FAKE, FAKE, 16, 64, 1), qg.QG_EINVAL),       # W odd address
+    ((8, FAKE, FAKE + 2, FAKE, 16, 64, 1), qg.QG_EINVAL),       # x misaligned
+])
+def test_gemv_rejects(args, code):
+    assert qg.lib().qg_gemv(*args, None) == code
+
+
+def test_dequant_rejects():
+    L = qg.lib()
+    assert L.qg_dequant(14, FAKE, FAKE, 4, 100, None) == qg.QG_EINVAL
+    assert L.qg_dequant(2, None, FAKE, 4, 64, None) == qg.QG_EINVAL
+
+
+def test_router_rejects():
+    L = qg.lib()
+    assert L.qg_router_topk(FAKE, 257, 8, 1, FAKE, FAKE, None) == qg.QG_ELIMIT
+    assert L.qg_router_topk(FAKE, 128, 33, 1, FAKE, FAKE, None) == qg.QG_ELIMIT
+    assert L.qg_router_topk(FAKE, 4, 5, 1, FAKE, FAKE, None) == qg.QG_ELIMIT
+    assert L.qg_router_topk(FAKE, 128, 8, 17, FAKE, FAKE, None) == qg.QG_ELIMIT
+    assert L.qg_router_topk(None, 128, 8, 1, FAKE, FAKE, None) == qg.QG_EINVAL
+
+
+def test_mlp_rejects_and_sizes():
+    L = qg.lib()
+    assert qg.qg_mlp_workspace_size(9728, 1) == 2 * 9728 * 4
+    assert qg.qg_mlp_workspace_size(100, 3) % 256 == 0
+    assert qg.qg_mlp_workspace_size(9728, 0) == 0
+    ws = qg.qg_mlp_workspace_size(64, 1)
+    assert L.qg_mlp(8, 0, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 1, FAKE, ws - 4, None) == qg.QG_EINVAL
+    assert L.qg_mlp(8, 5, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_mlp(8, 0, FAKE, FAKE, FAKE, 64, 48, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_mlp(8, 0, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 1, FAKE + 16, ws, None) == qg.QG_EINVAL
+
+
+def _moe(**kw):
+    d = dict(type=8, act=0, hidden=2048, ff=768, n_experts=128, gate_up=FAKE, gate_up_stride=5013504,
+             down=FAKE + 3342336, down_stride=5013504, down_scale=None)
+    d.update(kw)
+    return qg.qg_moe(d["type"], d["act"], d["hidden"], d["ff"], d["n_experts"], d["gate_up"],
+                     d["gate_up_stride"], d["down"], d["down_stride"], d["down_scale"])
+
+
+def test_moe_rejects_and_sizes():
+    L = qg.lib()
+    m = _moe()
+    ws = qg.qg_moe_workspace_size(m, 8, 1)
+    assert ws >= 8 * 2 * 768 * 4 + 8 * 2048 * 4
+    assert ws % 256 == 0
+    call = lambda mm, k=8, T=1, w=ws, st=FAKE: L.qg_moe_ffn(ctypes.byref(mm), FAKE, k, FAKE, FAKE, FAKE, T,
+                                                           None, None, st, FAKE, w, None)
+    assert call(_moe(n_experts=257)) == qg.QG_ELIMIT
+    assert call(m, k=33) == qg.QG_ELIMIT
+    assert call(m, T=17) == qg.QG_ELIMIT
+    assert call(m, w=ws - 256) == qg.QG_EINVAL
+    assert call(m, st=None) == qg.QG_EINVAL
+    assert call(_moe(act=9)) == qg.QG_EINVAL
+    assert call(_moe(ff=100)) == qg.QG_EINVAL                     # ff % 32
+    assert call(_moe(gate_up_stride=1000)) == qg.QG_EINVAL        # stride shorter than a record
+    assert L.qg_moe_ffn(None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, FAKE, ws, None) == qg.QG_EINVAL
