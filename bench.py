@@ -47,8 +47,16 @@ class Workload:
     bytes_per_step = 0
     dominant = ""            # kernel whose duration the roofline reports
     dominant_bytes = 0
+    period = 1               # distinct weight copies the steps rotate through
+    dominant_period = 1
 
-    def step(self, i, ev=None):
+    def step(self, i):
+        raise NotImplementedError
+
+    def dominant_step(self, i):
+        self.step(i)
+
+    def output(self):
         raise NotImplementedError
 
 
@@ -84,17 +92,21 @@ class DenseMlpHead(Workload):
         self.bytes_per_step = self.mlp_bytes + self.dominant_bytes
         self.name = "q8_0 dense MLP decode 2560x9728 (gate||up, SwiGLU, down) + tied head 151936x2560, 1 token"
         self.dominant = "head GEMV Q8_0 151936x2560"
+        self.period = self.dominant_period = copies
 
-    def step(self, i, ev=None):
+    def step(self, i):
         qg = self.qg
         s = self.sets[i % len(self.sets)]
         qg.qg_mlp(qg.QG_Q8_0, qg.QG_ACT_SILU, s["Wg"], s["Wu"], s["Wd"], self.H, self.F, self.x, self.h, 1,
                   self.ws)
-        if ev is not None:
-            ev[0].record()
         qg.qg_gemv(qg.QG_Q8_0, s["Wh"], self.h, self.logits, self.V, self.H, 1)
-        if ev is not None:
-            ev[1].record()
+
+    def dominant_step(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.qg.qg_gemv(self.qg.QG_Q8_0, s["Wh"], self.h, self.logits, self.V, self.H, 1)
+
+    def output(self):
+        return self.logits
 
     def cpu_baseline(self, min_seconds=10.0):
         """The oracle over the whole step (same shapes, numpy-drawn weights),
@@ -147,23 +159,24 @@ class GemvRot(Workload):
         self.dominant_bytes = wb
         self.name = label
         self.dominant = label
+        self.period = self.dominant_period = copies
 
-    def step(self, i, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(self, i):
         self.qg.qg_gemv(self.t, self.W[i % len(self.W)], self.x, self.y, self.rows, self.cols, self.ntok)
-        if ev is not None:
-            ev[1].record()
+
+    def output(self):
+        return self.y
 
 
 class MoeLayers(Workload):
     """qg_moe_ffn over L independent layers (pools, logits, x), T tokens."""
 
-    def __init__(self, t, act, H, F, E, k, ntok, layers, scale, label):
+    def __init__(self, t, act, H, F, E, k, ntok, layers, scale, label, dense_ff=0):
         import torch
         import gguf_synth as gs
         import gguf_dequant_gemv_amd as qg
         self.qg, self.ntok, self.k = qg, ntok, k
+        self.t, self.act, self.H, self.dense_ff = t, act, H, dense_ff
         rb_gu, rb_d = gs.row_bytes(t, H), gs.row_bytes(t, F)
         rec = 2 * F * rb_gu + H * rb_d
         self.layers = []
@@ -175,7 +188,11 @@ class MoeLayers(Workload):
             x = gs.device_activations(ntok, H, g)
             ds = (torch.rand(E, generator=g, device="cuda") * 1.5 + 0.5) if scale else None
             m = qg.make_moe(t, act, H, F, E, gu, 2 * F * rb_gu, dn, H * rb_d, ds)
-            self.layers.append(dict(m=m, gu=gu, dn=dn, lg=lg, x=x, ds=ds))
+            L = dict(m=m, gu=gu, dn=dn, lg=lg, x=x, ds=ds)
+            if dense_ff:   # the dense MLP that runs beside the experts
+                L.update(Wg=gs.device_weights(t, dense_ff, H, g), Wu=gs.device_weights(t, dense_ff, H, g),
+                         Wd=gs.device_weights(t, H, dense_ff, g))
+            self.layers.append(L)
         self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
         self.y = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
         self.ids = torch.empty((ntok, k), dtype=torch.int32, device="cuda")
@@ -191,19 +208,27 @@ class MoeLayers(Workload):
             uniq.append(len(set(ids.flatten().tolist())))
         self.uniq = uniq
         self.rec = rec
-        self.bytes_per_step = int(sum(uniq) / len(uniq) * rec)
+        self.dense_bytes = (2 * dense_ff * rb_gu + H * gs.row_bytes(t, dense_ff)) if dense_ff else 0
+        if dense_ff:
+            self.ym = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
+            self.wsm = torch.empty(qg.qg_mlp_workspace_size(dense_ff, ntok) // 4, dtype=torch.float32,
+                                   device="cuda")
+        self.bytes_per_step = int(sum(uniq) / len(uniq) * rec) + self.dense_bytes
         self.dominant_bytes = self.bytes_per_step
         self.name = label
         self.dominant = label
+        self.period = self.dominant_period = layers
 
-    def step(self, i, ev=None):
+    def step(self, i):
         L = self.layers[i % len(self.layers)]
-        if ev is not None:
-            ev[0].record()
+        if self.dense_ff:
+            self.qg.qg_mlp(self.t, self.act, L["Wg"], L["Wu"], L["Wd"], self.H, self.dense_ff, L["x"], self.ym,
+                           self.ntok, self.wsm)
         self.qg.qg_moe_ffn(L["m"], L["lg"], self.k, self.slots, L["x"], self.y, self.ntok, self.ids, self.w,
                            self.status, self.ws)
-        if ev is not None:
-            ev[1].record()
+
+    def output(self):
+        return self.y
 
 
 def make_workload(name, copies):
@@ -223,25 +248,70 @@ def make_workload(name, copies):
     if name in ("4", "4t16"):
         T = 16 if name == "4t16" else 1
         return MoeLayers(gs.Q4_0, 1, 2816, 704, 128, 8, T, 4, True,
-                         "q4_0 MoE layer 2816, 128 experts ff 704 (GELU, down scale), top-8, %d token(s)" % T)
+                         "q4_0 dense GELU MLP 2816x2112 + MoE layer 2816, 128 experts ff 704 (GELU, down scale), "
+                         "top-8, %d token(s)" % T, dense_ff=2112)
     raise SystemExit("unknown config " + name)
 
 
+def _capture(fn, idxs):
+    """One HIP graph holding fn(i) for every i in idxs (captured on torch's
+    capture stream, which the binding picks up as the current stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in idxs:
+            fn(i)
+    return g
+
+
 def time_workload(wl, steps, warmup):
+    """(ms per step, ms per dominant-kernel launch).  Steps run as replays of
+    captured graphs (period consecutive steps per graph, so exactly `steps`
+    steps are timed); the dominant kernel is timed the same way on its own."""
     import torch
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    per = max(1, min(wl.period, steps))
+    full = _capture(wl.step, range(per))
+    rem = steps % per
+    tail = _capture(wl.step, range(rem)) if rem else None
+    # a replay must reproduce the eager result bit for bit
+    wl.step(per - 1)
     torch.cuda.synchronize()
+    ref = wl.output().clone()
+    full.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(ref, wl.output()):
+        raise SystemExit("bench: graph replay differs from the eager run")
+    for _ in range(2):
+        full.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        wl.step(warmup + i, evs[i])
+    e0.record()
+    for _ in range(steps // per):
+        full.replay()
+    if tail is not None:
+        tail.replay()
+    e1.record()
     torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    return dt * 1e3 / steps, dom_ms
-
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    log("[bench] %d steps: %.4f ms/step by events, %.4f ms/step by the host clock" % (steps, ms, wall * 1e3 / steps))
+    # dominant kernel alone, same rotation
+    dper = max(1, min(wl.dominant_period, 64))
+    dg = _capture(wl.dominant_step, range(dper))
+    dg.replay()
+    torch.cuda.synchronize()
+    reps = max(1, (steps + dper - 1) // dper)
+    e0.record()
+    for _ in range(reps):
+        dg.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    dom_ms = e0.elapsed_time(e1) / (reps * dper)
+    return ms, dom_ms
 
 def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
     gbs = wl.bytes_per_step / (ms * 1e-3) / 1e9

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/qgemv.h"
 #include "qg_kernels.h"
 
@@ -29,7 +31,6 @@ bool type_info(int t, TypeInfo &ti) {
 }
 
 constexpr int NUM_CU = 256;
-constexpr size_t LDS_MAX = 160 * 1024;
 
 struct Shape {
     int type;
@@ -61,6 +62,7 @@ size_t lds_bytes(const Shape &s, int nt) {
 struct Plan {
     int lpr, unr, nt;
     int ntiles, gx;
+    int64_t copies;     // independent problems sharing the GPU in one launch
     size_t lds;
 };
 
@@ -96,15 +98,36 @@ Plan make_plan(const Shape &s, int ntok_chunk_max, int64_t rows_align, int64_t p
     const int rpw = 64 / p.lpr;
     const int64_t tile_rows = 4LL * rpw;
     p.ntiles = (int)((s.rows + tile_rows - 1) / tile_rows);
-    // resident workgroups per CU, limited by LDS; spread tiles evenly
-    int per_cu = (int)(LDS_MAX / (p.lds + 512));
-    if (per_cu > 8) per_cu = 8;
-    if (per_cu < 1) per_cu = 1;
-    int64_t cap = (int64_t)NUM_CU * per_cu / (parallel_copies > 0 ? parallel_copies : 1);
+    p.copies = parallel_copies > 0 ? parallel_copies : 1;
+    p.gx = p.ntiles;   // refined by grid_for() once the kernel is known
+    return p;
+}
+
+// Workgroups that stay resident at once (all CUs), from the kernel's actual
+// register and LDS use; cached per kernel and LDS size.
+int resident_wgs(gemv_fn f, size_t lds) {
+    struct Entry { gemv_fn f; size_t lds; int n; };
+    static std::mutex mu;
+    static Entry cache[256];
+    static int used = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; i++)
+        if (cache[i].f == f && cache[i].lds == lds) return cache[i].n;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 256, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const int n = per_cu * NUM_CU;
+    if (used < 256) cache[used++] = {f, lds, n};
+    return n;
+}
+
+// Grid-stride width: every tile once, in as few resident waves of workgroups
+// as possible, with the tiles spread evenly over the workgroups.
+int grid_for(const Plan &p, gemv_fn f) {
+    int64_t cap = resident_wgs(f, p.lds) / p.copies;
     if (cap < 1) cap = 1;
     const int64_t tpw = (p.ntiles + cap - 1) / cap;
-    p.gx = (int)((p.ntiles + tpw - 1) / tpw);
-    return p;
+    return (int)((p.ntiles + tpw - 1) / tpw);
 }
 
 #define QG_PICK_NT(NAME) \
@@ -125,6 +148,7 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.row_bytes = s.row_bytes;
+    a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
     a.upr = s.upr;
     a.nb = s.nb;
@@ -133,6 +157,7 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     gemv_fn f = pick(s.type, p);
     if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
         return QG_EHIP;
+    grid.x = grid_for(p, f);
     hipLaunchKernelGGL(f, grid, dim3(256), p.lds, st, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }

@@ -53,6 +53,7 @@ struct GemvArgs {
     const float *x;
     int64_t x_stride;
     int xmode;
+    int x_vec;         // x rows are 16-byte aligned (x and x_stride * 4)
     // outputs: vector i goes to y + idx_i * y_stride
     float *y;
     int64_t y_stride;
@@ -63,12 +64,13 @@ struct GemvArgs {
 };
 
 // -------------------------------------------------------- unit dot product --
-// acc[t] += sum over the unit of value(i) * x_t[i], for tokens t < nt.
+// acc[t] += sum over the unit of value(i) * x_t[i], for all NT token slots
+// (slots past the chunk's last token hold a copy of it; their sums are dropped).
 // Per scale group: s = sum(code * x) with f32 FMAs, then fold(s, sum(x)); the
 // unit's groups are summed before joining the lane accumulator.
 template <class U, int NT>
 QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *__restrict__ xs, int xstride,
-                     const float *__restrict__ ss, int sstride, int nt, float (&acc)[NT]) {
+                     const float *__restrict__ ss, int sstride, float (&acc)[NT]) {
     float us[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) us[t] = 0.0f;
@@ -84,43 +86,51 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *__restrict__ xs, int xs
             const float q2 = U::code(w, i + 2), q3 = U::code(w, i + 3);
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                if (t < nt) {
-                    const f32x4 xv = *(const f32x4 *)(xs + t * xstride + i + ((i >> 6) << 2));
-                    float &s = (k & 1) ? s1[t] : s0[t];
-                    s = fmaf(q0, xv.x, s);
-                    s = fmaf(q1, xv.y, s);
-                    s = fmaf(q2, xv.z, s);
-                    s = fmaf(q3, xv.w, s);
-                }
+                const f32x4 xv = *(const f32x4 *)(xs + t * xstride + i + ((i >> 6) << 2));
+                float &s = (k & 1) ? s1[t] : s0[t];
+                s = fmaf(q0, xv.x, s);
+                s = fmaf(q1, xv.y, s);
+                s = fmaf(q2, xv.z, s);
+                s = fmaf(q3, xv.w, s);
             }
         }
 #pragma unroll
         for (int t = 0; t < NT; t++)
-            if (t < nt) us[t] += U::fold(w, g, s0[t] + s1[t], U::SUMS ? ss[t * sstride + g] : 0.0f);
+            us[t] += U::fold(w, g, s0[t] + s1[t], U::SUMS ? ss[t * sstride + g] : 0.0f);
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] += us[t];
 }
 
 // One wave's pass over its rows: lane (grp, sub) accumulates row grp's units
-// sub, sub+LPR, ...; UNR units are loaded before any is decoded.
+// sub, sub+LPR, ...; UNR units are loaded before any is decoded.  Pair units
+// are whole pairs in the main loop; with an odd number of blocks per row the
+// last, single block is a separate step taken by one lane per row.
 template <class U, int LPR, int NT, int UNR>
 QG_DEV void lane_rows(rsrc_t rs, u32 row_off, int upr, int nb, int sub, const float *xs, int xstride,
-                      const float *ss, int sstride, int nt, float (&acc)[NT]) {
+                      const float *ss, int sstride, float (&acc)[NT]) {
     constexpr int UV = U::VALUES;
     constexpr int SPU = UV / (U::SUMS ? U::SUMS : UV) * (U::SUMS ? 1 : 0);  // x-sums per unit
-    for (int u0 = sub; u0 < upr; u0 += LPR * UNR) {
+    const int nfull = (UV == 64) ? (nb >> 1) : upr;
+    for (int u0 = sub; u0 < nfull; u0 += LPR * UNR) {
+        // every lane loads UNR units (a lane past the row's end re-loads the
+        // row's last unit, a cache hit) so the loads are straight-line code
         u32 w[UNR][U::ND];
 #pragma unroll
         for (int i = 0; i < UNR; i++) {
-            const int u = u0 + i * LPR;
-            if (u < upr) U::load(rs, row_off + (u32)u * U::BYTES, w[i], (UV == 64) ? (2 * u + 1 < nb) : true);
+            const int u = min(u0 + i * LPR, nfull - 1);
+            U::load(rs, row_off + (u32)u * U::BYTES, w[i], true);
         }
 #pragma unroll
         for (int i = 0; i < UNR; i++) {
             const int u = u0 + i * LPR;
-            if (u < upr) unit_dot<U, NT>(w[i], xs + xpad(u * UV), xstride, ss + u * SPU, sstride, nt, acc);
+            if (u < nfull) unit_dot<U, NT>(w[i], xs + xpad(u * UV), xstride, ss + u * SPU, sstride, acc);
         }
+    }
+    if (UV == 64 && (nb & 1) && sub == nfull % LPR) {
+        u32 w[U::ND];
+        U::load(rs, row_off + (u32)nfull * U::BYTES, w, false);
+        unit_dot<U, NT>(w, xs + xpad(nfull * UV), xstride, ss + nfull * SPU, sstride, acc);
     }
 }
 
@@ -130,6 +140,57 @@ template <int PH> struct UnitOf<T_Q8_0, PH> { typedef UQ8_0<PH> U; };
 template <int PH> struct UnitOf<T_Q4_0, PH> { typedef UQ4_0<PH> U; };
 template <int PH> struct UnitOf<T_Q4_K, PH> { typedef UQ4_K<PH> U; };
 template <int PH> struct UnitOf<T_Q6_K, PH> { typedef UQ6_K U; };
+
+// x[t] (or act(gate) * up from a [gate | up] row) into LDS, zero-padded from
+// cols to cpad.  a.x_vec: every source row is 16-byte aligned, so whole
+// float4s are loaded (cols is a multiple of 32).
+template <int NT>
+QG_DEV void stage_x(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride) {
+    constexpr int B = 8;  // float4 loads in flight per thread
+    const int tid = threadIdx.x;
+    if (a.x_vec) {
+        const int n4 = cpad >> 2, c4 = cols >> 2;
+        for (int t = 0; t < NT; t++) {
+            const f32x4 *src = (const f32x4 *)(a.x + (int64_t)in_idx[t] * a.x_stride);
+            for (int base = tid; base < n4; base += 256 * B) {
+                f32x4 v[B], u[B];
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const int i = min(base + 256 * b, c4 - 1);
+                    v[b] = src[i];
+                    if (a.xmode != XM_PLAIN) u[b] = src[c4 + i];
+                }
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const int i = base + 256 * b;
+                    if (i < n4) {
+                        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+                        if (i < c4) {
+                            if (a.xmode == XM_PLAIN) {
+                                o = v[b];
+                            } else {
+                                o.x = glu(a.xmode, v[b].x, u[b].x);
+                                o.y = glu(a.xmode, v[b].y, u[b].y);
+                                o.z = glu(a.xmode, v[b].z, u[b].z);
+                                o.w = glu(a.xmode, v[b].w, u[b].w);
+                            }
+                        }
+                        *(f32x4 *)(xs + t * xstride + xpad(4 * i)) = o;
+                    }
+                }
+            }
+        }
+    } else {
+        for (int t = 0; t < NT; t++) {
+            const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
+            for (int c = tid; c < cpad; c += 256) {
+                float v = 0.0f;
+                if (c < cols) v = a.xmode == XM_PLAIN ? src[c] : glu(a.xmode, src[c], src[cols + c]);
+                xs[t * xstride + xpad(c)] = v;
+            }
+        }
+    }
+}
 
 // ------------------------------------------------------------ GEMV kernel --
 // grid.x: row tiles (grid-stride); grid.y: dense token chunk, or group;
@@ -170,24 +231,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 
     // ---- stage x (and the GLU transform) into LDS ----
     // x is zero-padded to whole units (cpad values), so a row's last, half
-    // pair reads zeros rather than whatever follows the vector.
+    // pair reads zeros rather than whatever follows the vector.  Loads are
+    // 16-byte vectors, all issued before any is stored, so staging costs about
+    // one L2 round trip rather than one per element.
     const int cols = a.cols;
     const int cpad = a.upr * U0::VALUES;
     const int xstride = xstride_of(cpad);
     const int nsum = SUMS ? cpad / SUMS : 0;
     float *xs = lds;
     float *ss = lds + NT * xstride;
-    for (int t = 0; t < nt; t++) {
-        const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
-        for (int c = threadIdx.x; c < cpad; c += 256) {
-            float v = 0.0f;
-            if (c < cols) v = a.xmode == XM_PLAIN ? src[c] : glu(a.xmode, src[c], src[cols + c]);
-            xs[t * xstride + xpad(c)] = v;
-        }
-    }
+    stage_x<NT>(a, in_idx, cols, cpad, xs, xstride);
     __syncthreads();
     if constexpr (SUMS != 0) {
-        for (int i = threadIdx.x; i < nt * nsum; i += 256) {
+        for (int i = threadIdx.x; i < NT * nsum; i += 256) {
             const int t = i / nsum, gi = i - t * nsum;
             const float *p = xs + t * xstride + xpad(gi * SUMS);  // SUMS divides 64: no pad inside
             float s0 = 0.0f, s1 = 0.0f;
@@ -199,7 +255,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
 
     // ---- rows ----
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform; saying so keeps the buffer descriptors in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = lane / LPR, sub = lane % LPR;
     for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
         const int64_t r0 = ((int64_t)tile * 4 + wave) * RPW;
@@ -217,13 +274,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         if (grp < nrows) {
             const u32 roff = (u32)grp * (u32)a.row_bytes;
             if constexpr (TYPE == T_Q6_K) {
-                lane_rows<UQ6_K, LPR, NT, UNR>(rs, roff + ph, a.upr, a.nb, sub, xs, xstride, ss, nsum, nt, acc);
+                lane_rows<UQ6_K, LPR, NT, UNR>(rs, roff + ph, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
             } else {
                 // rows of one wave share a phase (host guarantees row_bytes % 4 == 0 or RPW == 1)
                 if (ph == 0)
-                    lane_rows<typename UnitOf<TYPE, 0>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, nt, acc);
+                    lane_rows<typename UnitOf<TYPE, 0>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
                 else
-                    lane_rows<typename UnitOf<TYPE, 2>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, nt, acc);
+                    lane_rows<typename UnitOf<TYPE, 2>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
             }
         }
 #pragma unroll
