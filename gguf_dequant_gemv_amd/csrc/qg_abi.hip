@@ -15,28 +15,28 @@ namespace {
 
 struct TypeInfo {
     int qk, bytes;        // values / bytes per GGUF block
-    int unit_vals;        // values per lane unit (pair of blocks or one block)
-    int unit_bytes;
-    int max_unr;          // units a lane keeps in flight
+    int block_vals;       // values per block unit
+    int pairs;            // 1: Q8_0 / Q4_0 can use pair units
 };
 
 bool type_info(int t, TypeInfo &ti) {
     switch (t) {
-    case QG_Q8_0: ti = {32, 34, 64, 68, 4}; return true;
-    case QG_Q4_0: ti = {32, 18, 64, 36, 4}; return true;
-    case QG_Q4_K: ti = {256, 144, 256, 144, 2}; return true;
-    case QG_Q6_K: ti = {256, 210, 256, 210, 1}; return true;
+    case QG_Q8_0: ti = {32, 34, 32, 1}; return true;
+    case QG_Q4_0: ti = {32, 18, 32, 1}; return true;
+    case QG_Q4_K: ti = {256, 144, 256, 0}; return true;
+    case QG_Q6_K: ti = {256, 210, 256, 0}; return true;
     default: return false;
     }
 }
 
 constexpr int NUM_CU = 256;
+constexpr int64_t MAX_RANGE = (int64_t)1 << 31;   // bytes one buffer descriptor addresses per launch
 
 struct Shape {
     int type;
     TypeInfo ti;
     int64_t rows, row_bytes;
-    int cols, nb, upr;
+    int cols, nb;
 };
 
 int make_shape(int type, int64_t rows, int64_t cols, Shape &s) {
@@ -48,58 +48,62 @@ int make_shape(int type, int64_t rows, int64_t cols, Shape &s) {
     s.cols = (int)cols;
     s.nb = (int)(cols / s.ti.qk);
     s.row_bytes = (int64_t)s.nb * s.ti.bytes;
-    s.upr = (int)((cols + s.ti.unit_vals - 1) / s.ti.unit_vals);
     return QG_OK;
 }
 
-size_t lds_bytes(const Shape &s, int nt) {
-    const int sums = s.type == QG_Q6_K ? 16 : (s.type == QG_Q8_0 ? 0 : 32);
-    const int cpad = s.upr * s.ti.unit_vals;   // x staged zero-padded to whole units
+int sums_of(int type) { return type == QG_Q6_K ? 16 : (type == QG_Q8_0 ? 0 : 32); }
+
+size_t lds_bytes(int type, int cpad, int nt) {
+    const int sums = sums_of(type);
     const size_t per = (size_t)xstride_of(cpad) + (sums ? cpad / sums : 0);
     return (size_t)nt * per * sizeof(float);
 }
 
 struct Plan {
-    int lpr, unr, nt;
-    int ntiles, gx;
-    int64_t copies;     // independent problems sharing the GPU in one launch
+    int kind, lpr, nt;
+    int nunits;          // units per row
+    int ntiles;          // row tiles of 4 * 64/lpr rows
+    int64_t copies;      // independent problems sharing the GPU in one launch
     size_t lds;
 };
 
-// rows_align: a row index (the W0/W1 split) no wave may straddle; 0 = none.
-Plan make_plan(const Shape &s, int ntok_chunk_max, int64_t rows_align, int64_t parallel_copies) {
+// Unit kind and lanes per row: best lane utilisation (units per row spread
+// evenly over the row's lanes), then enough waves to fill the GPU.
+//   ntok_max:   most tokens one workgroup must serve
+//   rows_align: a row index (the W0/W1 split) no wave may straddle; 0 = none
+//   pair_ok:    every weight range starts 4-byte aligned (pairs stay aligned)
+Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok) {
     Plan p;
-    // tokens per workgroup: all of them up to 8, fewer if x would not fit
     int nt = 1;
-    while (nt < ntok_chunk_max && nt < 8) nt <<= 1;
-    while (nt > 1 && lds_bytes(s, nt) > 64 * 1024) nt >>= 1;
-    p.nt = nt;
-    p.lds = lds_bytes(s, nt);
-    // lanes per row: best lane utilisation, then enough waves, then wider
-    const bool any_phase = (s.row_bytes & 3) != 0;   // rows alternate 0 / 2 mod 4
+    while (nt < ntok_max && nt < 8) nt <<= 1;
+    p.copies = copies > 0 ? copies : 1;
+    const bool pairs = s.ti.pairs && pair_ok && (s.nb % 2) == 0;
     double best = -1.0;
-    int best_lpr = 64;
-    const int cands[5] = {64, 32, 16, 8, 4};
-    for (int ci = 0; ci < 5; ci++) {
-        const int lpr = cands[ci], rpw = 64 / lpr;
-        if (any_phase && rpw != 1) continue;
-        if (rows_align > 0 && rows_align % rpw) continue;
-        const int per_lane = (s.upr + lpr - 1) / lpr;
-        const double util = (double)s.upr / ((double)lpr * per_lane);
-        const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)parallel_copies;
-        const double fill = waves >= 4.0 * NUM_CU ? 1.0 : waves / (4.0 * NUM_CU);
-        const double score = util * (0.5 + 0.5 * fill);
-        if (score > best + 1e-9) { best = score; best_lpr = lpr; }
+    p.kind = UK_BLOCK;
+    p.lpr = 64;
+    for (int kind = 0; kind <= (pairs ? 1 : 0); kind++) {
+        const int nunits = kind == UK_PAIR ? s.nb / 2 : s.cols / s.ti.block_vals;
+        const int cands[5] = {64, 32, 16, 8, 4};
+        for (int ci = 0; ci < 5; ci++) {
+            const int lpr = cands[ci], rpw = 64 / lpr;
+            if (rows_align > 0 && rows_align % rpw) continue;
+            const int per_lane = (nunits + lpr - 1) / lpr;
+            const double util = (double)nunits / ((double)lpr * per_lane);
+            const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)p.copies;
+            const double fill = waves >= 8.0 * NUM_CU ? 1.0 : waves / (8.0 * NUM_CU);
+            // pairs: half the load instructions and no re-alignment
+            const double score = util * (0.55 + 0.45 * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
+            if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
+        }
     }
-    p.lpr = best_lpr;
-    const int per_lane = (s.upr + p.lpr - 1) / p.lpr;
-    p.unr = s.ti.max_unr;
-    while (p.unr > 1 && p.unr / 2 >= per_lane) p.unr >>= 1;
-    const int rpw = 64 / p.lpr;
-    const int64_t tile_rows = 4LL * rpw;
+    p.nunits = p.kind == UK_PAIR ? s.nb / 2 : s.cols / s.ti.block_vals;
+    const int uv = p.kind == UK_PAIR ? 2 * s.ti.qk : s.ti.block_vals;
+    const int cpad = p.nunits * uv;
+    while (nt > 1 && lds_bytes(s.type, cpad, nt) > 64 * 1024) nt >>= 1;
+    p.nt = nt;
+    p.lds = lds_bytes(s.type, cpad, nt);
+    const int64_t tile_rows = 4LL * (64 / p.lpr);
     p.ntiles = (int)((s.rows + tile_rows - 1) / tile_rows);
-    p.copies = parallel_copies > 0 ? parallel_copies : 1;
-    p.gx = p.ntiles;   // refined by grid_for() once the kernel is known
     return p;
 }
 
@@ -108,7 +112,7 @@ Plan make_plan(const Shape &s, int ntok_chunk_max, int64_t rows_align, int64_t p
 int resident_wgs(gemv_fn f, size_t lds) {
     struct Entry { gemv_fn f; size_t lds; int n; };
     static std::mutex mu;
-    static Entry cache[256];
+    static Entry cache[512];
     static int used = 0;
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < used; i++)
@@ -117,22 +121,34 @@ int resident_wgs(gemv_fn f, size_t lds) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 256, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const int n = per_cu * NUM_CU;
-    if (used < 256) cache[used++] = {f, lds, n};
+    if (used < 512) cache[used++] = {f, lds, n};
     return n;
 }
 
-// Grid-stride width: every tile once, in as few resident waves of workgroups
-// as possible, with the tiles spread evenly over the workgroups.
+// Grid-stride width.  Workgroups that cannot be resident at once run in
+// later rounds, and fewer workgroups than resident slots leave memory
+// parallelism unused; pick the tiles per workgroup that minimises
+//   rounds * tiles per workgroup * (slots / workgroups, if fewer) + a start
+// cost per round (staging x and filling the pipeline).
 int grid_for(const Plan &p, gemv_fn f) {
     int64_t cap = resident_wgs(f, p.lds) / p.copies;
     if (cap < 1) cap = 1;
-    const int64_t tpw = (p.ntiles + cap - 1) / cap;
-    return (int)((p.ntiles + tpw - 1) / tpw);
+    double best = 1e300;
+    int64_t best_gx = p.ntiles;
+    for (int64_t tpw = 1; tpw <= 16; tpw++) {
+        const int64_t gx = (p.ntiles + tpw - 1) / tpw;
+        const int64_t rounds = (gx + cap - 1) / cap;
+        const double under = gx < cap ? (double)cap / (double)gx : 1.0;
+        const double cost = (double)rounds * (double)tpw * under + 0.3 * (double)rounds;
+        if (cost < best - 1e-9) { best = cost; best_gx = gx; }
+        if (gx == 1) break;
+    }
+    return (int)best_gx;
 }
 
 #define QG_PICK_NT(NAME) \
-    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.lpr, p.unr) : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.lpr, p.unr) \
-     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.lpr, p.unr) : gemv_kernel_##NAME##_t8(p.lpr, p.unr))
+    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.kind, p.lpr) : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.kind, p.lpr) \
+     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.kind, p.lpr) : gemv_kernel_##NAME##_t8(p.kind, p.lpr))
 
 gemv_fn pick(int type, const Plan &p) {
     switch (type) {
@@ -146,13 +162,20 @@ gemv_fn pick(int type, const Plan &p) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// a: weights, x/y, tokens or groups set by the caller; rows0 and rows set.
 int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.row_bytes = s.row_bytes;
+    if (a.glu) {           // gate rows in W0, the same rows of the up matrix in W1
+        a.rows0 = a.rows;
+        a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
+    } else {
+        a.bytes0 = a.rows0 * s.row_bytes;
+        a.bytes1 = (a.rows - a.rows0) * s.row_bytes;
+    }
+    if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
-    a.upr = s.upr;
-    a.nb = s.nb;
-    a.rows = s.rows;
+    a.nunits = p.nunits;
     a.ntiles = p.ntiles;
     gemv_fn f = pick(s.type, p);
     if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
@@ -195,18 +218,25 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
     if (rc) return rc;
     if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
-    Plan p = make_plan(s, ntok, 0, 1);
-    GemvArgs a = {};
-    a.W0 = a.W1 = (const uint8_t *)W;
-    a.rows0 = rows;
-    a.x = x;
-    a.x_stride = cols;
-    a.xmode = XM_PLAIN;
-    a.y = y;
-    a.y_stride = rows;
-    a.ntok = ntok;
-    dim3 grid(p.gx, (ntok + p.nt - 1) / p.nt, 1);
-    return launch_gemv(s, p, a, grid, (hipStream_t)stream);
+    // rows in launches of at most MAX_RANGE weight bytes each
+    const int64_t chunk = MAX_RANGE / s.row_bytes;
+    for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+        Shape sc = s;
+        sc.rows = rows - r0 < chunk ? rows - r0 : chunk;
+        const uint8_t *Wc = (const uint8_t *)W + r0 * s.row_bytes;
+        Plan p = make_plan(sc, ntok, 0, 1, aligned(Wc, 4));
+        GemvArgs a = {};
+        a.W0 = a.W1 = Wc;
+        a.rows0 = a.rows = sc.rows;
+        a.x = x;
+        a.x_stride = cols;
+        a.y = y + r0;
+        a.y_stride = rows;
+        a.ntok = ntok;
+        rc = launch_gemv(sc, p, a, dim3(1, (ntok + p.nt - 1) / p.nt, 1), (hipStream_t)stream);
+        if (rc) return rc;
+    }
+    return QG_OK;
 }
 
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
@@ -214,11 +244,10 @@ int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, 
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
     if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;
-    const int64_t units = rows * s.upr;
-    dim3 grid((unsigned)((units + 255) / 256));
-    hipStream_t st = (hipStream_t)stream;
-    dequant_fn f = dequant_kernel(type);
-    hipLaunchKernelGGL(f, grid, dim3(256), 0, st, (const uint8_t *)W, out, rows, s.cols, s.row_bytes, s.upr, s.nb);
+    const int64_t blocks = rows * s.nb;
+    dim3 grid((unsigned)((blocks + 255) / 256));
+    hipLaunchKernelGGL(dequant_kernel(type), grid, dim3(256), 0, (hipStream_t)stream, (const uint8_t *)W, out, rows,
+                       s.cols, s.row_bytes);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
@@ -234,15 +263,16 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
+// Workspace of qg_mlp: gu [ntok][2ff] f32 at offset 0, then act [ntok][ff].
 size_t qg_mlp_workspace_size(int64_t ff, int ntok) {
     if (ff <= 0 || ntok < 1 || ntok > QG_MAX_TOKENS) return 0;
-    return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float));
+    return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float));
 }
 
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
            const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
-    Shape s_gu, s_dn;
-    int rc = make_shape(type, 2 * ff, hidden, s_gu);
+    Shape s_g, s_dn;
+    int rc = make_shape(type, ff, hidden, s_g);
     if (rc) return rc;
     rc = make_shape(type, hidden, ff, s_dn);
     if (rc) return rc;
@@ -255,40 +285,42 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     if (workspace_bytes < qg_mlp_workspace_size(ff, ntok)) return QG_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     float *gu = (float *)workspace;
-    // gate || up in one launch: rows [0, ff) from W_gate, [ff, 2ff) from W_up
-    Plan p1 = make_plan(s_gu, ntok, ff, 1);
+    float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
+    // gate and up rows together: act(gate) * up per row, raw gate / up kept in gu
+    Plan p1 = make_plan(s_g, ntok, 0, 1, aligned(W_gate, 4) && aligned(W_up, 4));
     GemvArgs a = {};
     a.W0 = (const uint8_t *)W_gate;
     a.W1 = (const uint8_t *)W_up;
-    a.rows0 = ff;
+    a.rows0 = a.rows = ff;
     a.x = x;
     a.x_stride = hidden;
-    a.xmode = XM_PLAIN;
-    a.y = gu;
-    a.y_stride = 2 * ff;
+    a.y = av;
+    a.y_stride = ff;
+    a.glu = act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    a.y2 = gu;
+    a.y2_stride = 2 * ff;
     a.ntok = ntok;
-    rc = launch_gemv(s_gu, p1, a, dim3(p1.gx, (ntok + p1.nt - 1) / p1.nt, 1), st);
+    rc = launch_gemv(s_g, p1, a, dim3(1, (ntok + p1.nt - 1) / p1.nt, 1), st);
     if (rc) return rc;
-    // down, with act(gate) * up formed while x is staged
-    Plan p2 = make_plan(s_dn, ntok, 0, 1);
+    // down on the activations
+    Plan p2 = make_plan(s_dn, ntok, 0, 1, aligned(W_down, 4));
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)W_down;
-    b.rows0 = hidden;
-    b.x = gu;
-    b.x_stride = 2 * ff;
-    b.xmode = act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    b.rows0 = b.rows = hidden;
+    b.x = av;
+    b.x_stride = ff;
     b.y = y;
     b.y_stride = hidden;
     b.ntok = ntok;
-    return launch_gemv(s_dn, p2, b, dim3(p2.gx, (ntok + p2.nt - 1) / p2.nt, 1), st);
+    return launch_gemv(s_dn, p2, b, dim3(1, (ntok + p2.nt - 1) / p2.nt, 1), st);
 }
 
 // Workspace layout for qg_moe_ffn (each part 256-byte aligned, in order):
-//   gu [T*k][2F] f32 | dn [T*k][H] f32 | ids [T*k] i32 | w [T*k] f32 |
-//   valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32
+//   gu [T*k][2F] f32 | act [T*k][F] f32 | dn [T*k][H] f32 | ids [T*k] i32 |
+//   w [T*k] f32 | valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32
 namespace {
 struct MoeWs {
-    size_t gu, dn, ids, w, valid, grp, total;
+    size_t gu, act, dn, ids, w, valid, grp, total;
 };
 MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     MoeWs o;
@@ -296,6 +328,7 @@ MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     const size_t pairs = (size_t)T * k;
     const size_t groups = pairs < (size_t)E ? pairs : (size_t)E;
     o.gu = off; off += align256(pairs * 2 * (size_t)F * 4);
+    o.act = off; off += align256(pairs * (size_t)F * 4);
     o.dn = off; off += align256(pairs * (size_t)H * 4);
     o.ids = off; off += align256(pairs * 4);
     o.w = off; off += align256(pairs * 4);
@@ -321,14 +354,14 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
         ntok > QG_MAX_TOKENS)
         return QG_ELIMIT;
     if (m->act != QG_ACT_SILU && m->act != QG_ACT_GELU_TANH) return QG_EINVAL;
-    Shape s_gu, s_dn;
-    int rc = make_shape(m->type, 2 * m->ff, m->hidden, s_gu);
+    Shape s_g, s_dn;
+    int rc = make_shape(m->type, m->ff, m->hidden, s_g);
     if (rc) return rc;
     rc = make_shape(m->type, m->hidden, m->ff, s_dn);
     if (rc) return rc;
     if (!m->gate_up || !m->down || !router_logits || !expert_slots || !x || !y || !status || !workspace)
         return QG_EINVAL;
-    if (m->gate_up_stride < s_gu.rows * s_gu.row_bytes || m->down_stride < s_dn.rows * s_dn.row_bytes)
+    if (m->gate_up_stride < 2 * s_g.rows * s_g.row_bytes || m->down_stride < s_dn.rows * s_dn.row_bytes)
         return QG_EINVAL;
     if (!aligned(m->gate_up, 2) || !aligned(m->down, 2) || (m->gate_up_stride & 1) || (m->down_stride & 1) ||
         !aligned(router_logits, 4) || !aligned(expert_slots, 4) || !aligned(x, 4) || !aligned(y, 4) ||
@@ -339,6 +372,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     if (workspace_bytes < L.total) return QG_EINVAL;
     uint8_t *ws = (uint8_t *)workspace;
     float *gu = (float *)(ws + L.gu);
+    float *av = (float *)(ws + L.act);
     float *dn = (float *)(ws + L.dn);
     int32_t *rt_ids = (int32_t *)(ws + L.ids);
     float *rt_w = (float *)(ws + L.w);
@@ -355,36 +389,38 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     const int pairs = ntok * topk;
     const int gmax = pairs < E ? pairs : E;
 
-    // 2. gate || up for every group of pairs that picked the same expert
-    Plan p1 = make_plan(s_gu, ntok, 0, gmax);
+    // 2. gate and up rows of every group's expert together: act(gate) * up per
+    //    pair into act, raw gate / up into gu
+    Plan p1 = make_plan(s_g, ntok, 0, gmax, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0);
     GemvArgs a = {};
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
-    a.rows0 = s_gu.rows;
+    a.rows0 = a.rows = F;
     a.slot_stride = m->gate_up_stride;
     a.x = x;
     a.x_stride = H;
-    a.xmode = XM_PLAIN;
-    a.y = gu;
-    a.y_stride = 2 * F;
+    a.y = av;
+    a.y_stride = F;
+    a.glu = m->act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    a.y2 = gu;
+    a.y2_stride = 2 * F;
     a.grp = grp;
     a.in_by_pair = 0;
-    rc = launch_gemv(s_gu, p1, a, dim3(p1.gx, gmax, (ntok + p1.nt - 1) / p1.nt), st);
+    rc = launch_gemv(s_g, p1, a, dim3(1, gmax, (ntok + p1.nt - 1) / p1.nt), st);
     if (rc) return rc;
 
-    // 3. down on act(gate) * up, per pair
-    Plan p2 = make_plan(s_dn, ntok, 0, gmax);
+    // 3. down on each pair's activations
+    Plan p2 = make_plan(s_dn, ntok, 0, gmax, aligned(m->down, 4) && (m->down_stride % 4) == 0);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;
-    b.rows0 = s_dn.rows;
+    b.rows0 = b.rows = s_dn.rows;
     b.slot_stride = m->down_stride;
-    b.x = gu;
-    b.x_stride = 2 * F;
-    b.xmode = m->act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    b.x = av;
+    b.x_stride = F;
     b.y = dn;
     b.y_stride = H;
     b.grp = grp;
     b.in_by_pair = 1;
-    rc = launch_gemv(s_dn, p2, b, dim3(p2.gx, gmax, (ntok + p2.nt - 1) / p2.nt), st);
+    rc = launch_gemv(s_dn, p2, b, dim3(1, gmax, (ntok + p2.nt - 1) / p2.nt), st);
     if (rc) return rc;
 
     // 4. weighted combine in pick order

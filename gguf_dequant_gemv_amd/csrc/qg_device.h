@@ -1,22 +1,18 @@
 // qg_device.h -- device helpers and the per-type block-unpack layer (gfx950).
 //
 // A "unit" is the piece of a weight row one lane loads and decodes at a time:
-//   Q8_0  a pair of blocks  (64 values,  68 B)
-//   Q4_0  a pair of blocks  (64 values,  36 B)
-//   Q4_K  one block         (256 values, 144 B)
-//   Q6_K  one block         (256 values, 210 B)
-// Pairs make every unit start on a 4-byte boundary when the row does (34*2 and
-// 18*2 are multiples of 4), so the lane's loads are plain dword-aligned buffer
-// loads and every byte position inside the unit is a compile-time constant.
-// Q6_K blocks alternate between 0 and 2 mod 4; they are loaded from the
-// aligned-down address and re-aligned in registers with v_alignbyte.
+//   Q8_0  one block (32 values, 34 B) or a pair of blocks (64 values, 68 B)
+//   Q4_0  one block (32 values, 18 B) or a pair of blocks (64 values, 36 B)
+//   Q4_K  one block (256 values, 144 B)
+//   Q6_K  one block (256 values, 210 B)
+// GGUF blocks sit at 2-byte alignment.  A pair of Q8_0 or Q4_0 blocks is a
+// multiple of 4 bytes, so in a tensor that starts 4-byte aligned with an even
+// number of blocks per row every pair starts on a dword and every field in it
+// sits at a compile-time byte position.  Single blocks and the K-quant blocks
+// are loaded from the aligned-down address and shifted into place with
+// v_alignbyte (one op per dword).
 //
-// Each unit type exposes
-//   code(w, i)   the integer code of value i as f32 (exact)
-//   GROUPS/GSIZE the scale groups (values sharing one scale) in value order
-//   fold(...)    a group's contribution from  sum(code * x)  and  sum(x)
-//   value(w, i)  the dequantized f32 value (one rounding of the exact value)
-// so the GEMV dot products and the dequantization kernel share one decoder.
+// The GEMV dot products and the dequantization kernel share these decoders.
 // Block formulas: the ternary_bonsai_2_dflash.js page (dequantQ4K,
 // dequantQ6K, scaleMinK4), the gemma4_moe_ssd.js page (Q4_0 plane comment,
 // q4dot) and the qwen3_moe_ssd.js page (i8at, matmulQ8).
@@ -103,74 +99,123 @@ QG_DEV int xpad(int c) { return c + ((c >> 6) << 2); }
 __host__ __device__ inline int xstride_of(int cols) { return cols + ((cols >> 6) << 2) + 4; }
 
 // ================================================================ units ====
+// Every unit type exposes
+//   VALUES, BYTES        values and bytes per unit
+//   NR, ND               dwords a lane holds for one unit as loaded / decoded
+//   GROUPS, GSIZE, SUMS  scale groups (GSIZE values each) and the span of the
+//                        x-sums fold() needs (0 = none)
+//   issue(r, off, raw)   start the loads of the unit at byte `off`
+//   prep(raw, off, w)    the loaded dwords in decode order (after they arrive)
+//   load(r, off, w)      issue + prep
+//   code(w, i)           integer code of value i as f32 (exact)
+//   fold(w, g, s, xs)    group g's contribution from s = sum(code*x), xs = sum(x)
+//   value(w, i)          the dequantized value as f32 (one rounding)
 
-// ---- Q8_0: pair of blocks; block A at byte PH, block B at byte PH+34 ------
-template <int PH>
-struct UQ8_0 {
-    static constexpr int TYPE = T_Q8_0, VALUES = 64, BYTES = 68, ND = PH ? 18 : 17;
-    static constexpr int GROUPS = 2, GSIZE = 32, SUMS = 0;  // no x-sums needed
-    // has_b == false: the row ends after block A (odd blocks per row).
-    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND], bool has_b) {
-        ldn<9>(r, off, w);
-        if (has_b) {
-            ldn<ND - 9, 9>(r, off + 36, w);
-        } else {
+// Realigned units: the N dwords that start at byte `off` (2-byte aligned) are
+// issued as N+1 aligned dwords from off & ~3 (raw_load, kept as they arrive)
+// and shifted into place with v_alignbyte only when the unit is consumed
+// (realign), so a lane can keep several units' loads in flight.
+template <int N, int M>
+QG_DEV void raw_load(rsrc_t r, u32 off, u32 (&t)[M]) {
+    static_assert(N + 1 <= M, "raw_load: out of range");
+    ldn<N>(r, off & ~3u, t);
+    // the extra dword is a load of its own: past the tensor's last dword it
+    // is out of the descriptor's range and reads 0 without touching memory
+    t[N] = __builtin_amdgcn_raw_buffer_load_b32(r, (off & ~3u) + 4 * N, 0, 0);
+}
+template <int N, int M, int K>
+QG_DEV void realign(const u32 (&t)[M], u32 off, u32 (&w)[K]) {
+    static_assert(N + 1 <= M && N <= K, "realign: out of range");
+    const u32 s = off & 3u;
 #pragma unroll
-            for (int i = 9; i < ND; i++) w[i] = 0;
-        }
+    for (int i = 0; i < N; i++) w[i] = __builtin_amdgcn_alignbyte(t[i + 1], t[i], s);
+}
+
+// ---- Q8_0, one block (32 values, 34 B), any 2-byte phase -------------------
+struct UQ8_0B {
+    static constexpr int TYPE = T_Q8_0, VALUES = 32, BYTES = 34, NR = 10, ND = 9;
+    static constexpr int GROUPS = 1, GSIZE = 32, SUMS = 0;
+    // 9 dwords from off & ~3 cover the 34 bytes for either phase; the 10th
+    // (a separate load) only keeps the shift uniform
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { raw_load<9>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32 off, u32 (&w)[ND]) { realign<9>(t, off, w); }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { u32 t[NR]; issue(r, off, t); prep(t, off, w); }
+    QG_DEV static float scale(const u32 (&w)[ND]) { return h2f(w[0]); }
+    QG_DEV static float code(const u32 (&w)[ND], int i) { return s8_at(w, 2 + i); }
+    QG_DEV static float fold(const u32 (&w)[ND], int, float s, float) { return scale(w) * s; }
+    QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w) * code(w, i); }
+};
+
+// ---- Q8_0, a pair of blocks (64 values, 68 B) starting 4-byte aligned ------
+// Block A at byte 0, block B at byte 34: every field sits at a fixed byte.
+struct UQ8_0P {
+    static constexpr int TYPE = T_Q8_0, VALUES = 64, BYTES = 68, NR = 17, ND = 17;
+    static constexpr int GROUPS = 2, GSIZE = 32, SUMS = 0;
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { ldn<17>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32, u32 (&w)[ND]) {
+#pragma unroll
+        for (int i = 0; i < ND; i++) w[i] = t[i];
     }
-    QG_DEV static float scale(const u32 (&w)[ND], int g) { return h2f(half_at(w, PH + 34 * g)); }
-    QG_DEV static float code(const u32 (&w)[ND], int i) { return s8_at(w, PH + 34 * (i >> 5) + 2 + (i & 31)); }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { ldn<17>(r, off, w); }
+    QG_DEV static float scale(const u32 (&w)[ND], int g) { return h2f(half_at(w, 34 * g)); }
+    QG_DEV static float code(const u32 (&w)[ND], int i) { return s8_at(w, 34 * (i >> 5) + 2 + (i & 31)); }
     QG_DEV static float fold(const u32 (&w)[ND], int g, float s, float) { return scale(w, g) * s; }
     QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w, i >> 5) * code(w, i); }
 };
 
-// ---- Q4_0: pair of blocks; block A at byte PH, block B at byte PH+18 ------
-// Byte j of a block's 16 nibble bytes: low nibble = value j, high = value j+16.
-template <int PH>
-struct UQ4_0 {
-    static constexpr int TYPE = T_Q4_0, VALUES = 64, BYTES = 36, ND = PH ? 10 : 9;
-    static constexpr int GROUPS = 2, GSIZE = 32, SUMS = 32;  // x-sums over 32 values
-    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND], bool has_b) {
-        ldn<5>(r, off, w);
-        if (has_b) {
-            ldn<ND - 5, 5>(r, off + 20, w);
-        } else {
-#pragma unroll
-            for (int i = 5; i < ND; i++) w[i] = 0;
-        }
-    }
-    QG_DEV static float scale(const u32 (&w)[ND], int g) { return h2f(half_at(w, PH + 18 * g)); }
+// ---- Q4_0, one block (32 values, 18 B), any 2-byte phase -------------------
+// Byte j of the 16 nibble bytes: low nibble = value j, high = value j+16.
+struct UQ4_0B {
+    static constexpr int TYPE = T_Q4_0, VALUES = 32, BYTES = 18, NR = 6, ND = 5;
+    static constexpr int GROUPS = 1, GSIZE = 32, SUMS = 32;
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { raw_load<5>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32 off, u32 (&w)[ND]) { realign<5>(t, off, w); }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { u32 t[NR]; issue(r, off, t); prep(t, off, w); }
+    QG_DEV static float scale(const u32 (&w)[ND]) { return h2f(w[0]); }
     QG_DEV static float code(const u32 (&w)[ND], int i) {  // nibble 0..15
-        const int pos = PH + 18 * (i >> 5) + 2 + (i & 15);
+        const int pos = 2 + (i & 15);
         const u32 word = w[pos >> 2];
         const u32 m = (i & 16) ? ((word >> 4) & 0x0F0F0F0Fu) : (word & 0x0F0F0F0Fu);
         return u8_of(m, pos & 3);
     }
     // d * sum((q - 8) x) = d * (sum(q x) - 8 sum(x))
+    QG_DEV static float fold(const u32 (&w)[ND], int, float s, float xs) { return scale(w) * fmaf(-8.0f, xs, s); }
+    QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w) * (code(w, i) - 8.0f); }
+};
+
+// ---- Q4_0, a pair of blocks (64 values, 36 B) starting 4-byte aligned ------
+struct UQ4_0P {
+    static constexpr int TYPE = T_Q4_0, VALUES = 64, BYTES = 36, NR = 9, ND = 9;
+    static constexpr int GROUPS = 2, GSIZE = 32, SUMS = 32;
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { ldn<9>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32, u32 (&w)[ND]) {
+#pragma unroll
+        for (int i = 0; i < ND; i++) w[i] = t[i];
+    }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { ldn<9>(r, off, w); }
+    QG_DEV static float scale(const u32 (&w)[ND], int g) { return h2f(half_at(w, 18 * g)); }
+    QG_DEV static float code(const u32 (&w)[ND], int i) {
+        const int pos = 18 * (i >> 5) + 2 + (i & 15);
+        const u32 word = w[pos >> 2];
+        const u32 m = (i & 16) ? ((word >> 4) & 0x0F0F0F0Fu) : (word & 0x0F0F0F0Fu);
+        return u8_of(m, pos & 3);
+    }
     QG_DEV static float fold(const u32 (&w)[ND], int g, float s, float xs) { return scale(w, g) * fmaf(-8.0f, xs, s); }
     QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w, i >> 5) * (code(w, i) - 8.0f); }
 };
 
-// ---- Q4_K: one block, 36 dwords: [d|dmin] [scales x3] [qs x32] -----------
-// qs chunk c (dwords 4+8c .. 4+8c+7): low nibbles are sub-block 2c, high
-// nibbles sub-block 2c+1.  The 12 scale bytes hold 6-bit (scale, min) pairs:
-// sub-blocks 0..3 use bytes j and j+4; 4..7 take the low/high nibble of byte
-// j+4 and the top two bits of bytes j-4 (scale) and j (min).
-template <int PH>
+// ---- Q4_K: one block (256 values, 144 B), realigned to 36 dwords ----------
+// [d|dmin] [scales x3] [qs x32].  qs chunk c (dwords 4+8c .. 4+8c+7): low
+// nibbles are sub-block 2c, high nibbles sub-block 2c+1.  The 12 scale bytes
+// hold 6-bit (scale, min) pairs: sub-blocks 0..3 use bytes j and j+4; 4..7
+// take the low/high nibble of byte j+4 and the top two bits of bytes j-4
+// (scale) and j (min).
 struct UQ4_K {
-    static constexpr int TYPE = T_Q4_K, VALUES = 256, BYTES = 144, ND = 36;
+    static constexpr int TYPE = T_Q4_K, VALUES = 256, BYTES = 144, NR = 37, ND = 36;
     static constexpr int GROUPS = 8, GSIZE = 32, SUMS = 32;
-    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND], bool) {
-        if constexpr (PH == 0) {
-            ldn<36>(r, off, w);
-        } else {  // block at 2 mod 4: 37 dwords from 2 bytes earlier, re-aligned
-            u32 t[37];
-            ldn<37>(r, off, t);
-#pragma unroll
-            for (int i = 0; i < 36; i++) w[i] = __builtin_amdgcn_alignbyte(t[i + 1], t[i], 2);
-        }
-    }
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { raw_load<36>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32 off, u32 (&w)[ND]) { realign<36>(t, off, w); }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { u32 t[NR]; issue(r, off, t); prep(t, off, w); }
     // scale / min bytes for sub-blocks 4h..4h+3 (one per byte)
     QG_DEV static u32 sc4(const u32 (&w)[ND], int h) {
         return h == 0 ? (w[1] & 0x3F3F3F3Fu) : ((w[3] & 0x0F0F0F0Fu) | ((w[1] >> 2) & 0x30303030u));
@@ -192,22 +237,17 @@ struct UQ4_K {
     QG_DEV static float value(const u32 (&w)[ND], int i) { return fmaf(dsc(w, i >> 5), code(w, i), -dmn(w, i >> 5)); }
 };
 
-// ---- Q6_K: one block, re-aligned to 53 dwords: ql[0..31] qh[32..47] sc[48..51] d[52]
-// Half n of the block (values 128n..): value 128n + 32p + l (l < 32) takes the
-// low (p = 0, 1) or high (p = 2, 3) nibble of ql[64n + l + 32(p & 1)] and bits
-// 2p, 2p+1 of qh[32n + l]; its scale is int8 scales[(value >> 4)].
+// ---- Q6_K: one block (256 values, 210 B), realigned to 53 dwords ----------
+// ql[0..31] qh[32..47] sc[48..51] d[52].  Half n of the block (values 128n..):
+// value 128n + 32p + l (l < 32) takes the low (p = 0, 1) or high (p = 2, 3)
+// nibble of ql[64n + l + 32(p & 1)] and bits 2p, 2p+1 of qh[32n + l]; its
+// scale is int8 scales[value >> 4].
 struct UQ6_K {
-    static constexpr int TYPE = T_Q6_K, VALUES = 256, BYTES = 210, ND = 53;
+    static constexpr int TYPE = T_Q6_K, VALUES = 256, BYTES = 210, NR = 54, ND = 53;
     static constexpr int GROUPS = 16, GSIZE = 16, SUMS = 16;
-    // off: the block's byte offset; loads 53 dwords from off & ~3 and shifts.
-    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND], bool) {
-        u32 t[54];
-        const u32 s = off & 3u;
-        ldn<53>(r, off & ~3u, t);
-        t[53] = 0;
-#pragma unroll
-        for (int i = 0; i < 53; i++) w[i] = __builtin_amdgcn_alignbyte(t[i + 1], t[i], s);
-    }
+    QG_DEV static void issue(rsrc_t r, u32 off, u32 (&t)[NR]) { raw_load<53>(r, off, t); }
+    QG_DEV static void prep(const u32 (&t)[NR], u32 off, u32 (&w)[ND]) { realign<53>(t, off, w); }
+    QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { u32 t[NR]; issue(r, off, t); prep(t, off, w); }
     // four 6-bit codes (one per byte) for values 128n + 32p + 4k .. +3
     QG_DEV static u32 code4(const u32 (&w)[ND], int n, int p, int k) {
         const u32 ql = w[16 * n + 8 * (p & 1) + k], qh = w[32 + 8 * n + k];

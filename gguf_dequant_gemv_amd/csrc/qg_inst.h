@@ -7,25 +7,29 @@
 namespace qg {
 namespace inst {
 
-template <int TY, int LPR, int NT>
-gemv_fn pick_unr(int unr) {
-    constexpr int MAXU = TY == T_Q6_K ? 1 : TY == T_Q4_K ? 2 : 4;
-    if constexpr (MAXU >= 4)
-        if (unr >= 4) return k_gemv<TY, LPR, NT, 4>;
-    if constexpr (MAXU >= 2)
-        if (unr >= 2) return k_gemv<TY, LPR, NT, 2>;
-    return k_gemv<TY, LPR, NT, 1>;
+template <class U, int NT>
+gemv_fn pick_lpr(int lpr) {
+    switch (lpr) {
+    case 4: return k_gemv<U, 4, NT>;
+    case 8: return k_gemv<U, 8, NT>;
+    case 16: return k_gemv<U, 16, NT>;
+    case 32: return k_gemv<U, 32, NT>;
+    default: return k_gemv<U, 64, NT>;
+    }
 }
 
+template <int TY> struct Units;
+template <> struct Units<T_Q8_0> { typedef UQ8_0B B; typedef UQ8_0P P; };
+template <> struct Units<T_Q4_0> { typedef UQ4_0B B; typedef UQ4_0P P; };
+template <> struct Units<T_Q4_K> { typedef UQ4_K B; typedef UQ4_K P; };
+template <> struct Units<T_Q6_K> { typedef UQ6_K B; typedef UQ6_K P; };
+
 template <int TY, int NT>
-gemv_fn pick_lpr(int lpr, int unr) {
-    switch (lpr) {
-    case 4: return pick_unr<TY, 4, NT>(unr);
-    case 8: return pick_unr<TY, 8, NT>(unr);
-    case 16: return pick_unr<TY, 16, NT>(unr);
-    case 32: return pick_unr<TY, 32, NT>(unr);
-    default: return pick_unr<TY, 64, NT>(unr);
+gemv_fn pick(int kind, int lpr) {
+    if constexpr (TY == T_Q8_0 || TY == T_Q4_0) {
+        if (kind == UK_PAIR) return pick_lpr<typename Units<TY>::P, NT>(lpr);
     }
+    return pick_lpr<typename Units<TY>::B, NT>(lpr);
 }
 
 }  // namespace inst
@@ -33,5 +37,5 @@ gemv_fn pick_lpr(int lpr, int unr) {
 
 #define QG_GEMV_INSTANCES(NAME, TY, NT) \
     namespace qg { \
-    gemv_fn gemv_kernel_##NAME##_t##NT(int lpr, int unr) { return inst::pick_lpr<TY, NT>(lpr, unr); } \
+    gemv_fn gemv_kernel_##NAME##_t##NT(int kind, int lpr) { return inst::pick<TY, NT>(kind, lpr); } \
     }

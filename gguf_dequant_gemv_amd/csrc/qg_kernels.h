@@ -45,18 +45,26 @@ constexpr int MAXT = 16;
 
 struct GemvArgs {
     // weights: dense rows [0, rows0) come from W0, rows [rows0, rows) from W1;
-    // grouped: W0 + slot * slot_stride for the group's slot.
+    // grouped: W0 + slot * slot_stride for the group's slot.  Gated pairs:
+    // gate rows [0, rows) from W0, up rows [0, rows) from W1 (grouped: the up
+    // rows follow the gate rows in the slot).
     const uint8_t *W0, *W1;
     int64_t rows0, rows, row_bytes, slot_stride;
-    int cols, upr, nb;
-    // inputs: vector i of the chunk is x + idx_i * x_stride (+ GLU transform)
+    int64_t bytes0, bytes1;   // bytes of the W0 / W1 ranges
+    int cols, nunits;         // values per row; units per row
+    // inputs: vector i of the chunk is x + idx_i * x_stride
     const float *x;
     int64_t x_stride;
-    int xmode;
     int x_vec;         // x rows are 16-byte aligned (x and x_stride * 4)
     // outputs: vector i goes to y + idx_i * y_stride
     float *y;
     int64_t y_stride;
+    // gated pairs (XM_SILU / XM_GELU): row r of the output is act(g_r) * u_r
+    // where g_r is row r of W0 and u_r row r of W1 (rows = the gate rows);
+    // the raw g_r, u_r also go to y2 + idx_i * y2_stride + r (+ rows), if set
+    int glu;
+    float *y2;
+    int64_t y2_stride;
     int ntok;          // dense: tokens 0..ntok-1
     const int *grp;    // grouped: the routing table, or nullptr for dense
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
@@ -69,8 +77,8 @@ struct GemvArgs {
 // Per scale group: s = sum(code * x) with f32 FMAs, then fold(s, sum(x)); the
 // unit's groups are summed before joining the lane accumulator.
 template <class U, int NT>
-QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *__restrict__ xs, int xstride,
-                     const float *__restrict__ ss, int sstride, float (&acc)[NT]) {
+QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
+                     const float *ss, int sstride, float (&acc)[NT]) {
     float us[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) us[t] = 0.0f;
@@ -97,53 +105,21 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *__restrict__ xs, int xs
 #pragma unroll
         for (int t = 0; t < NT; t++)
             us[t] += U::fold(w, g, s0[t] + s1[t], U::SUMS ? ss[t * sstride + g] : 0.0f);
+        // decode group by group: keeps a block's codes from all being live at once
+        if constexpr (U::GROUPS > 2) {
+            // finish this group's sums before the next group's x reads start
+#pragma unroll
+            for (int t = 0; t < NT; t++) asm volatile("" : "+v"(us[t])::"memory");
+        }
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] += us[t];
 }
 
-// One wave's pass over its rows: lane (grp, sub) accumulates row grp's units
-// sub, sub+LPR, ...; UNR units are loaded before any is decoded.  Pair units
-// are whole pairs in the main loop; with an odd number of blocks per row the
-// last, single block is a separate step taken by one lane per row.
-template <class U, int LPR, int NT, int UNR>
-QG_DEV void lane_rows(rsrc_t rs, u32 row_off, int upr, int nb, int sub, const float *xs, int xstride,
-                      const float *ss, int sstride, float (&acc)[NT]) {
-    constexpr int UV = U::VALUES;
-    constexpr int SPU = UV / (U::SUMS ? U::SUMS : UV) * (U::SUMS ? 1 : 0);  // x-sums per unit
-    const int nfull = (UV == 64) ? (nb >> 1) : upr;
-    for (int u0 = sub; u0 < nfull; u0 += LPR * UNR) {
-        // every lane loads UNR units (a lane past the row's end re-loads the
-        // row's last unit, a cache hit) so the loads are straight-line code
-        u32 w[UNR][U::ND];
-#pragma unroll
-        for (int i = 0; i < UNR; i++) {
-            const int u = min(u0 + i * LPR, nfull - 1);
-            U::load(rs, row_off + (u32)u * U::BYTES, w[i], true);
-        }
-#pragma unroll
-        for (int i = 0; i < UNR; i++) {
-            const int u = u0 + i * LPR;
-            if (u < nfull) unit_dot<U, NT>(w[i], xs + xpad(u * UV), xstride, ss + u * SPU, sstride, acc);
-        }
-    }
-    if (UV == 64 && (nb & 1) && sub == nfull % LPR) {
-        u32 w[U::ND];
-        U::load(rs, row_off + (u32)nfull * U::BYTES, w, false);
-        unit_dot<U, NT>(w, xs + xpad(nfull * UV), xstride, ss + nfull * SPU, sstride, acc);
-    }
-}
-
-// Pairs of Q8_0/Q4_0 blocks are templated on the pair's phase (start mod 4).
-template <int TYPE, int PH> struct UnitOf;
-template <int PH> struct UnitOf<T_Q8_0, PH> { typedef UQ8_0<PH> U; };
-template <int PH> struct UnitOf<T_Q4_0, PH> { typedef UQ4_0<PH> U; };
-template <int PH> struct UnitOf<T_Q4_K, PH> { typedef UQ4_K<PH> U; };
-template <int PH> struct UnitOf<T_Q6_K, PH> { typedef UQ6_K U; };
-
-// x[t] (or act(gate) * up from a [gate | up] row) into LDS, zero-padded from
-// cols to cpad.  a.x_vec: every source row is 16-byte aligned, so whole
-// float4s are loaded (cols is a multiple of 32).
+// x[t] into LDS, zero-padded from cols to cpad.  a.x_vec: every source row is
+// 16-byte aligned, so whole float4s are loaded (cols is a multiple of 32).
+// All of a thread's loads are issued before any is stored, so staging costs
+// about one L2 round trip.
 template <int NT>
 QG_DEV void stage_x(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride) {
     constexpr int B = 8;  // float4 loads in flight per thread
@@ -153,29 +129,15 @@ QG_DEV void stage_x(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cp
         for (int t = 0; t < NT; t++) {
             const f32x4 *src = (const f32x4 *)(a.x + (int64_t)in_idx[t] * a.x_stride);
             for (int base = tid; base < n4; base += 256 * B) {
-                f32x4 v[B], u[B];
+                f32x4 v[B];
 #pragma unroll
-                for (int b = 0; b < B; b++) {
-                    const int i = min(base + 256 * b, c4 - 1);
-                    v[b] = src[i];
-                    if (a.xmode != XM_PLAIN) u[b] = src[c4 + i];
-                }
+                for (int b = 0; b < B; b++) v[b] = src[min(base + 256 * b, c4 - 1)];
 #pragma unroll
                 for (int b = 0; b < B; b++) {
                     const int i = base + 256 * b;
                     if (i < n4) {
-                        f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-                        if (i < c4) {
-                            if (a.xmode == XM_PLAIN) {
-                                o = v[b];
-                            } else {
-                                o.x = glu(a.xmode, v[b].x, u[b].x);
-                                o.y = glu(a.xmode, v[b].y, u[b].y);
-                                o.z = glu(a.xmode, v[b].z, u[b].z);
-                                o.w = glu(a.xmode, v[b].w, u[b].w);
-                            }
-                        }
-                        *(f32x4 *)(xs + t * xstride + xpad(4 * i)) = o;
+                        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+                        *(f32x4 *)(xs + t * xstride + xpad(4 * i)) = i < c4 ? v[b] : z;
                     }
                 }
             }
@@ -183,24 +145,39 @@ QG_DEV void stage_x(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cp
     } else {
         for (int t = 0; t < NT; t++) {
             const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
-            for (int c = tid; c < cpad; c += 256) {
-                float v = 0.0f;
-                if (c < cols) v = a.xmode == XM_PLAIN ? src[c] : glu(a.xmode, src[c], src[cols + c]);
-                xs[t * xstride + xpad(c)] = v;
-            }
+            for (int c = tid; c < cpad; c += 256) xs[t * xstride + xpad(c)] = c < cols ? src[c] : 0.0f;
         }
     }
 }
 
+// Units in flight per lane: about 72 dwords of loads (the decode and the
+// accumulators need the rest of the register file).
+template <class U, int NT>
+constexpr int pipe_depth() {
+    return (U::NR >= 36) ? 2 : (72 / U::NR > 8 ? 8 : 72 / U::NR) / (NT >= 4 ? 2 : 1);
+}
+
 // ------------------------------------------------------------ GEMV kernel --
-// grid.x: row tiles (grid-stride); grid.y: dense token chunk, or group;
-// grid.z: grouped token chunk.  LDS: x for NT vectors + their x-sums.
-template <int TYPE, int LPR, int NT, int UNR>
+// One kernel for every block type, dense or expert-grouped, T = 1..16 tokens.
+//   grid.x: row tiles, grid-stride (tile = 4 waves x RPW rows, RPW = 64/L);
+//   grid.y: dense token chunk, or expert group;  grid.z: grouped token chunk.
+// Each lane runs one stream of elements (row tile p, unit slot j): unit
+// u = sub + j*L of row (tile's rows) + grp, across all the wave's tiles, with
+// D elements' loads always in flight.  Lanes past the row's last unit, and
+// rows past the matrix's last row, re-load a valid unit (a cache hit) and do
+// not compute, so every load is unconditional and in bounds.  The first D
+// elements' loads are issued before x is staged, so weight latency overlaps
+// the staging.  In gated mode a tile's slots run over its gate rows' units
+// and then over the same rows of the up matrix, and the row outputs are
+// act(gate) * up.
+template <class U, int L, int NT>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     extern __shared__ float lds[];
-    typedef typename UnitOf<TYPE, 0>::U U0;
-    constexpr int RPW = 64 / LPR;
-    constexpr int SUMS = U0::SUMS;
+    constexpr int RPW = 64 / L;
+    constexpr int UV = U::VALUES;
+    constexpr int SUMS = U::SUMS;
+    constexpr int SPU = SUMS ? UV / SUMS : 0;
+    constexpr int D = pipe_depth<U, NT>();
 
     // ---- which vectors this workgroup serves, and which weights ----
     const uint8_t *Wg0 = a.W0, *Wg1 = a.W1;
@@ -215,7 +192,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         const int c0 = blockIdx.z * NT;
         if (c0 >= n) return;
         nt = min(NT, n - c0);
-        Wg0 = Wg1 = a.W0 + (int64_t)rec[1] * a.slot_stride;
+        Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
+        Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const int i = c0 + min(t, nt - 1);
@@ -229,13 +207,62 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         for (int t = 0; t < NT; t++) in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
     }
 
-    // ---- stage x (and the GLU transform) into LDS ----
-    // x is zero-padded to whole units (cpad values), so a row's last, half
-    // pair reads zeros rather than whatever follows the vector.  Loads are
-    // 16-byte vectors, all issued before any is stored, so staging costs about
-    // one L2 round trip rather than one per element.
+    // ---- descriptors over the two weight ranges (tensor start aligned down) ----
+    const u32 ph0 = (u32)((uintptr_t)Wg0 & 3u), ph1 = (u32)((uintptr_t)Wg1 & 3u);
+    const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 3) & ~(int64_t)3));
+    const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 3) & ~(int64_t)3));
+
+    // ---- the lane's element stream ----
+    // the wave index is uniform; saying so keeps the descriptors in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = lane / L, sub = lane % L;
+    const int K = (a.nunits + L - 1) / L;     // unit slots per lane per row and matrix
+    const int KT = a.glu ? 2 * K : K;         // slots per row tile
+    const int P = ((int)a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int S = P * KT;
+    const int64_t rows = a.rows, rows0 = a.rows0;
+    const int64_t rb = a.row_bytes;
+
+    // element (p, j) -> descriptor + byte offset of the unit to load
+    auto locate = [&](int p, int j, u32 &off) -> bool {  // returns: from range 1
+        const int64_t tile = (int64_t)blockIdx.x + (int64_t)p * gridDim.x;
+        const int64_t r0 = (tile * 4 + wave) * RPW;
+        const int64_t r = min(r0 + grp, rows - 1);
+        bool hi;
+        int64_t rl;
+        int jj = j;
+        if (a.glu) {             // slots [0, K): gate row r; [K, 2K): up row r
+            hi = j >= K;
+            jj = hi ? j - K : j;
+            rl = r;
+        } else {                 // waves never straddle rows0
+            hi = rows0 < rows && r0 >= rows0;
+            rl = hi ? r - rows0 : r;
+        }
+        const int u = min(sub + jj * L, a.nunits - 1);
+        off = (hi ? ph1 : ph0) + (u32)(rl * rb) + (u32)u * U::BYTES;
+        return hi;
+    };
+
+    u32 w[D][U::NR];     // raw dwords of the units in flight
+    u32 woff[D];         // and their byte offsets (the re-alignment shift)
+    // issue pointer (element s + D), compute pointer (element s)
+    int ip = 0, ij = 0, cp = 0, cj = 0;
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+        u32 off;
+        const int sp = min(ip, P - 1), sj = ip < P ? ij : KT - 1;   // past the end: re-load the last element
+        const bool hi = locate(sp, sj, off);
+        U::issue(hi ? rs1 : rs0, off, w[d]);
+        woff[d] = off;
+        if (++ij == KT) { ij = 0; ++ip; }
+        // keep the issue order: slot d's loads go out before slot d+1's
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- stage x (zero-padded to whole units) and its group sums ----
     const int cols = a.cols;
-    const int cpad = a.upr * U0::VALUES;
+    const int cpad = a.nunits * UV;
     const int xstride = xstride_of(cpad);
     const int nsum = SUMS ? cpad / SUMS : 0;
     float *xs = lds;
@@ -254,86 +281,115 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         __syncthreads();
     }
 
-    // ---- rows ----
-    // the wave index is uniform; saying so keeps the buffer descriptors in SGPRs
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int grp = lane / LPR, sub = lane % LPR;
-    for (int tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        const int64_t r0 = ((int64_t)tile * 4 + wave) * RPW;
-        if (r0 >= a.rows) break;
-        const bool lo = r0 < a.rows0;
-        const int64_t end = lo ? a.rows0 : a.rows;
-        const int nrows = (int)min((int64_t)RPW, end - r0);
-        const uint8_t *rowp = lo ? Wg0 + r0 * a.row_bytes : Wg1 + (r0 - a.rows0) * a.row_bytes;
-        const u32 ph = (u32)((uintptr_t)rowp & 3u);
-        const u32 span = (u32)(ph + (u32)nrows * (u32)a.row_bytes + 3u) & ~3u;
-        const rsrc_t rs = make_rsrc(rowp - ph, span);
-        float acc[NT];
+    float acc[NT], gate[NT];
 #pragma unroll
-        for (int t = 0; t < NT; t++) acc[t] = 0.0f;
-        if (grp < nrows) {
-            const u32 roff = (u32)grp * (u32)a.row_bytes;
-            if constexpr (TYPE == T_Q6_K) {
-                lane_rows<UQ6_K, LPR, NT, UNR>(rs, roff + ph, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
-            } else {
-                // rows of one wave share a phase (host guarantees row_bytes % 4 == 0 or RPW == 1)
-                if (ph == 0)
-                    lane_rows<typename UnitOf<TYPE, 0>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
-                else
-                    lane_rows<typename UnitOf<TYPE, 2>::U, LPR, NT, UNR>(rs, roff, a.upr, a.nb, sub, xs, xstride, ss, nsum, acc);
+    for (int t = 0; t < NT; t++) { acc[t] = 0.0f; gate[t] = 0.0f; }
+    // one element: consume slot d, refill it with element s + D, and close the
+    // row (or its gate half) when its last unit slot has been consumed
+    auto element = [&](u32 (&ws)[U::NR], u32 &wo) {
+        const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
+        const int64_t r0 = (tile * 4 + wave) * RPW;
+        const int u = sub + (cj >= K ? cj - K : cj) * L;
+        if (u < a.nunits) {
+            u32 wd[U::ND];
+            U::prep(ws, wo, wd);
+            unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
+        }
+        // this element's arithmetic is done before the next element's decode
+#pragma unroll
+        for (int t = 0; t < NT; t++) asm volatile("" : "+v"(acc[t])::"memory");
+        // the slot is consumed before it is refilled, and the refill is issued
+        // before the next slot is consumed
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            u32 off;
+            const int sp = min(ip, P - 1), sj = ip < P ? ij : KT - 1;  // past the end: re-load the last element
+            const bool hi = locate(sp, sj, off);
+            U::issue(hi ? rs1 : rs0, off, ws);
+            wo = off;
+            if (++ij == KT) { ij = 0; ++ip; }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        ++cj;
+        if (a.glu && cj == K) {   // gate half done: keep its row sums
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                gate[t] = group_sum<L>(acc[t]);
+                acc[t] = 0.0f;
             }
         }
+        if (cj == KT) {  // end of this tile's row: reduce over the row's L lanes and store
+            cj = 0;
+            ++cp;
 #pragma unroll
-        for (int t = 0; t < NT; t++) acc[t] = group_sum<LPR>(acc[t]);
-        if (sub == 0 && grp < nrows) {
+            for (int t = 0; t < NT; t++) acc[t] = group_sum<L>(acc[t]);
             const int64_t r = r0 + grp;
+            if (sub == 0 && r < rows) {
 #pragma unroll
-            for (int t = 0; t < NT; t++)
-                if (t < nt) a.y[(int64_t)out_idx[t] * a.y_stride + r] = acc[t];
+                for (int t = 0; t < NT; t++) {
+                    if (t < nt) {
+                        if (a.glu) {
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
+                            if (a.y2) {
+                                a.y2[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
+                                a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
+                            }
+                        } else {
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = acc[t];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; t++) acc[t] = 0.0f;
         }
+    };
+    // full rounds of D elements (no per-slot conditions), then the tail
+    int s0 = 0;
+    for (; s0 + D <= S; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) element(w[d], woff[d]);
     }
+#pragma unroll
+    for (int d = 0; d < D; d++)
+        if (s0 + d < S) element(w[d], woff[d]);
 }
 
 // ------------------------------------------------------- dequantization ---
-// One thread per unit: out[r][c] = value of W[r][c] as f32, through the same
-// loads and decoders as the GEMV.
-template <int TYPE>
+// One thread per block: out[r][c] = value of W[r][c] as f32, through the same
+// loads and decoders as the GEMV (block units: any 2-byte phase).
+template <class U>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *W, float *out, int64_t rows, int cols,
-                                                 int64_t row_bytes, int upr, int nb) {
-    typedef typename UnitOf<TYPE, 0>::U U0;
+                                                 int64_t row_bytes) {
+    const int nbr = cols / U::VALUES;
     const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (id >= rows * upr) return;
-    const int64_t r = id / upr;
-    const int u = (int)(id - r * upr);
-    const uint8_t *p = W + r * row_bytes + (int64_t)u * U0::BYTES;
+    if (id >= rows * nbr) return;
+    const int64_t r = id / nbr;
+    const int b = (int)(id - r * nbr);
+    const uint8_t *p = W + r * row_bytes + (int64_t)b * U::BYTES;
     const u32 ph = (u32)((uintptr_t)p & 3u);
-    const int vals = min(U0::VALUES, cols - u * U0::VALUES);
-    const rsrc_t rs = make_rsrc(p - ph, (u32)(ph + U0::BYTES + 3) & ~3u);
-    float *o = out + r * cols + (int64_t)u * U0::VALUES;
-    auto emit = [&](auto unit) {
-        typedef decltype(unit) U;
-        u32 w[U::ND];
-        U::load(rs, TYPE == T_Q6_K ? ph : 0u, w, vals > 32);
+    // descriptor over this block's dwords only
+    const rsrc_t rs = make_rsrc(p - ph, (u32)(ph + U::BYTES + 3) & ~3u);
+    u32 w[U::ND];
+    U::load(rs, ph, w);
+    float *o = out + r * cols + (int64_t)b * U::VALUES;
 #pragma unroll
-        for (int i = 0; i < U::VALUES; i++)
-            if (i < vals) o[i] = U::value(w, i);
-    };
-    if (TYPE == T_Q6_K || ph == 0)
-        emit(typename UnitOf<TYPE, 0>::U());
-    else
-        emit(typename UnitOf<TYPE, 2>::U());
+    for (int i = 0; i < U::VALUES; i++) o[i] = U::value(w, i);
 }
 
 // ------------------------------------------------------ instance tables ---
 typedef void (*gemv_fn)(GemvArgs);
-typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t, int, int);
-// One per (block type, tokens per workgroup), each in its own translation
-// unit (qg_inst_<type>_t<NT>.hip); qg_inst_dequant.hip holds the dequantizers.
+typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
+// Unit kinds: block units for every type; pair units for Q8_0 / Q4_0.
+enum { UK_BLOCK = 0, UK_PAIR = 1 };
+// One function per (block type, tokens per workgroup), each instantiated in
+// its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
+// (unit kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
 #define QG_DECL_GEMV(NAME) \
-    gemv_fn gemv_kernel_##NAME##_t1(int lpr, int unr); \
-    gemv_fn gemv_kernel_##NAME##_t2(int lpr, int unr); \
-    gemv_fn gemv_kernel_##NAME##_t4(int lpr, int unr); \
-    gemv_fn gemv_kernel_##NAME##_t8(int lpr, int unr);
+    gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr); \
+    gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr); \
+    gemv_fn gemv_kernel_##NAME##_t4(int kind, int lpr); \
+    gemv_fn gemv_kernel_##NAME##_t8(int kind, int lpr);
 QG_DECL_GEMV(q8_0)
 QG_DECL_GEMV(q4_0)
 QG_DECL_GEMV(q4_k)

@@ -107,8 +107,10 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
                    int32_t *ids, float *weights, void *stream);
 
 /* Dense gated MLP (one FFN without norms or residual):
- *   gu   = [W_gate x | W_up x]               (one launch, gate rows first)
- *   a    = act(gu[0:ff]) * gu[ff:2ff]          (fused into the down launch)
+ *   gu   = [W_gate x | W_up x]
+ *   a    = act(gu[0:ff]) * gu[ff:2ff]          (same launch as gu: each row
+ *                                              tile reads its gate rows, then
+ *                                              the same rows of W_up)
  *   y    = W_down a
  * [dense] encodeLayer (gate and up into the two halves of one buffer, siluMul,
  * down); [gemma4] dense GELU MLP (geglu).
@@ -116,7 +118,8 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
  * x: [ntok][hidden], y: [ntok][hidden].
  * workspace: device scratch of at least qg_mlp_workspace_size(ff, ntok) bytes,
  * 256-byte aligned.  After the call it holds gu as [ntok][2*ff] f32 at offset 0
- * (a documented intermediate, useful for staged checking).
+ * and a as [ntok][ff] f32 after it (at the next 256-byte boundary):
+ * documented intermediates, useful for staged checking.
  * Errors: as qg_gemv for both shapes, QG_EINVAL for a short workspace or an
  * unknown act. */
 size_t qg_mlp_workspace_size(int64_t ff, int ntok);
@@ -162,7 +165,8 @@ typedef struct qg_moe {
  * A token with an absent pick gets no output (its y row is left as it was)
  * and the status word reads QG_EABSENT.
  * workspace: at least qg_moe_workspace_size(m, topk, ntok) bytes, 256-byte
- * aligned.  After the call it holds, at offset 0, gu as [ntok][topk][2F] f32.
+ * aligned.  After the call it holds, at offset 0, gu as [ntok][topk][2F] f32,
+ * and a as [ntok][topk][F] f32 after it (at the next 256-byte boundary).
  * Errors: as qg_gemv for both shapes; QG_ELIMIT (n_experts > 256, topk > 32 or
  * > n_experts, ntok > 16); QG_EINVAL (short workspace, null pointer, bad act). */
 size_t qg_moe_workspace_size(const qg_moe *m, int topk, int ntok);

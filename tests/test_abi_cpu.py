@@ -76,7 +76,7 @@ def test_router_rejects():
 
 def test_mlp_rejects_and_sizes():
     L = qg.lib()
-    assert qg.qg_mlp_workspace_size(9728, 1) == 2 * 9728 * 4
+    assert qg.qg_mlp_workspace_size(9728, 1) == 2 * 9728 * 4 + 9728 * 4   # gu, then act
     assert qg.qg_mlp_workspace_size(100, 3) % 256 == 0
     assert qg.qg_mlp_workspace_size(9728, 0) == 0
     ws = qg.qg_mlp_workspace_size(64, 1)
@@ -98,7 +98,7 @@ def test_moe_rejects_and_sizes():
     L = qg.lib()
     m = _moe()
     ws = qg.qg_moe_workspace_size(m, 8, 1)
-    assert ws >= 8 * 2 * 768 * 4 + 8 * 2048 * 4
+    assert ws >= 8 * 2 * 768 * 4 + 8 * 768 * 4 + 8 * 2048 * 4   # gu, act, down outputs
     assert ws % 256 == 0
     call = lambda mm, k=8, T=1, w=ws, st=FAKE: L.qg_moe_ffn(ctypes.byref(mm), FAKE, k, FAKE, FAKE, FAKE, T,
                                                            None, None, st, FAKE, w, None)

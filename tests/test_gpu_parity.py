@@ -57,6 +57,20 @@ def check_rows(y, y_ref, A, what):
     return ratio
 
 
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+def check_act(orc, act, gu, a, F, what):
+    """The activation the gated launch wrote against the oracle's f64 act(g)*u
+    of the same f32 gate and up sums: f32 evaluation error, a few ulp of |g*u|."""
+    for i in range(gu.shape[0]):
+        ref = orc.glu(act, gu[i], F)
+        bound = 1e-6 * np.abs(gu[i, :F].astype(np.float64) * gu[i, F:].astype(np.float64)) + 1e-30
+        err = np.abs(a[i].astype(np.float64) - ref)
+        assert np.all(err <= bound), "%s vector %d: worst err/|gu| %.3g" % (what, i, (err / bound).max() * 1e-6)
+
+
 def gpu_gemv(t, W, x, rows, cols, ntok, w_offset=0):
     import gguf_dequant_gemv_amd as qg
     torch = _torch()
@@ -160,7 +174,10 @@ def test_mlp_stagewise(orc, t, act, H, F, T):
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(qg.qg_mlp_workspace_size(F, T) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, act, tg, tu, td, H, F, xt, y, T, ws)
-    gu = host(ws)[:T * 2 * F].reshape(T, 2 * F)
+    wsh = host(ws)
+    gu = wsh[:T * 2 * F].reshape(T, 2 * F)
+    a0 = _align256(T * 2 * F * 4) // 4
+    check_act(orc, act, gu, wsh[a0:a0 + T * F].reshape(T, F), F, "mlp act")
     # stage 1: gate || up
     yg, Ag = orc.gemv(t, Wg, x, F, H, T)
     yu, Au = orc.gemv(t, Wu, x, F, H, T)
@@ -208,8 +225,11 @@ def run_moe_gpu(c, slots=None, perm_pool=None):
     status = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
     ws = torch.empty(qg.qg_moe_workspace_size(m, k, T) // 4, dtype=torch.float32, device="cuda")
     qg.qg_moe_ffn(m, lt, k, st, xt, y, T, ids, w, status, ws)
+    wsh = host(ws)
+    F = c["F"]
+    a0 = _align256(T * k * 2 * F * 4) // 4
     out = dict(y=host(y), ids=host(ids), w=host(w), status=int(host(status)[0]),
-               gu=host(ws)[:T * k * 2 * c["F"]].reshape(T, k, 2 * c["F"]))
+               gu=wsh[:T * k * 2 * F].reshape(T, k, 2 * F), act=wsh[a0:a0 + T * k * F].reshape(T, k, F))
     del pt
     return out
 
@@ -242,6 +262,7 @@ def test_moe_stagewise(orc, t, act, H, F, E, k, T, scale):
             base = e * c["rec"]
             yy, AA = orc.gemv(t, c["pool"][base:base + c["d_off"]], c["x"][tt:tt + 1], 2 * F, H, 1)
             check_rows(r["gu"][tt, j][None], yy, AA, "moe gate||up t%d j%d" % (tt, j))
+    check_act(orc, act, r["gu"].reshape(T * k, 2 * F), r["act"].reshape(T * k, F), F, "moe act")
     # stage 2: down + combine fed the GPU's gate || up
     yd, Ad, R = orc.moe_down(t, act, H, F, c["pool"][c["d_off"]:], c["rec"], c["ds"],
                              np.arange(E, dtype=np.int32), ref["ids"], r["w"].astype(np.float64), r["gu"], T)
