@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (calibrates the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -350,6 +352,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = args.copy_probe << 18          # float32 elements
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copied %d MiB five times" % args.copy_probe)
+        return
     import gguf_dequant_gemv_amd as qg
     qg.lib()   # fails loudly if the HIP library is not built
     log("[bench] workload", args.config)

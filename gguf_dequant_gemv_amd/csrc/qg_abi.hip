@@ -64,29 +64,51 @@ struct Plan {
     int nunits;          // units per row
     int ntiles;          // row tiles of 4 * 64/lpr rows
     int64_t copies;      // independent problems sharing the GPU in one launch
+    int depth;           // UK_LDS: stages in flight per wave
+    int ring_off;        // UK_LDS: byte offset of the stage rings in LDS
     size_t lds;
 };
+
+// Bytes of one UK_LDS stage: 64 units in whole KiB (16-byte pieces, 64 per load).
+int stage_bytes(const TypeInfo &ti) {
+    const int ub = ti.pairs ? 2 * ti.bytes : ti.bytes;
+    return (4 * ub + 63) / 64 * 1024;
+}
+
+int unit_count(const Shape &s, int kind) {
+    if (kind == UK_PAIR || (kind == UK_LDS && s.ti.pairs)) return s.nb / 2;
+    return s.cols / s.ti.block_vals;
+}
 
 // Unit kind and lanes per row: best lane utilisation (units per row spread
 // evenly over the row's lanes), then enough waves to fill the GPU.
 //   ntok_max:   most tokens one workgroup must serve
 //   rows_align: a row index (the W0/W1 split) no wave may straddle; 0 = none
 //   pair_ok:    every weight range starts 4-byte aligned (pairs stay aligned)
-Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok) {
+//   lds_ok:     every weight range starts 16-byte aligned; with rows a whole
+//               number of 16-byte pieces the weights can be staged in LDS
+Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok, bool lds_ok) {
     Plan p;
     int nt = 1;
     while (nt < ntok_max && nt < 8) nt <<= 1;
     p.copies = copies > 0 ? copies : 1;
     const bool pairs = s.ti.pairs && pair_ok && (s.nb % 2) == 0;
+    const bool staged = lds_ok && (s.row_bytes % 16) == 0 && (!s.ti.pairs || (s.nb % 2) == 0);
     double best = -1.0;
     p.kind = UK_BLOCK;
     p.lpr = 64;
-    for (int kind = 0; kind <= (pairs ? 1 : 0); kind++) {
-        const int nunits = kind == UK_PAIR ? s.nb / 2 : s.cols / s.ti.block_vals;
+    const int kinds[3] = {UK_BLOCK, UK_PAIR, UK_LDS};
+    for (int ki = 0; ki < 3; ki++) {
+        const int kind = kinds[ki];
+        if (kind == UK_PAIR && !pairs) continue;
+        if (kind == UK_LDS && !staged) continue;
+        if (staged && kind != UK_LDS) continue;   // staging through LDS wins whenever it applies
+        const int nunits = unit_count(s, kind);
         const int cands[5] = {64, 32, 16, 8, 4};
         for (int ci = 0; ci < 5; ci++) {
             const int lpr = cands[ci], rpw = 64 / lpr;
             if (rows_align > 0 && rows_align % rpw) continue;
+            if (kind == UK_LDS && s.type == QG_Q6_K && lpr < 8) continue;   // 210-byte units: 16-byte segments need 8
             const int per_lane = (nunits + lpr - 1) / lpr;
             const double util = (double)nunits / ((double)lpr * per_lane);
             const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)p.copies;
@@ -96,12 +118,26 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
             if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
         }
     }
-    p.nunits = p.kind == UK_PAIR ? s.nb / 2 : s.cols / s.ti.block_vals;
-    const int uv = p.kind == UK_PAIR ? 2 * s.ti.qk : s.ti.block_vals;
+    p.nunits = unit_count(s, p.kind);
+    const int uv = (p.kind == UK_PAIR || (p.kind == UK_LDS && s.ti.pairs)) ? 2 * s.ti.qk : s.ti.block_vals;
     const int cpad = p.nunits * uv;
-    while (nt > 1 && lds_bytes(s.type, cpad, nt) > 64 * 1024) nt >>= 1;
+    const size_t xcap = p.kind == UK_LDS ? 96 * 1024 : 64 * 1024;
+    while (nt > 1 && lds_bytes(s.type, cpad, nt) > xcap) nt >>= 1;
     p.nt = nt;
     p.lds = lds_bytes(s.type, cpad, nt);
+    p.depth = 0;
+    p.ring_off = 0;
+    if (p.kind == UK_LDS) {
+        // stage rings after x: two stages per wave when two workgroups still
+        // fit a CU's 160 KiB, else one (a stage is refilled as soon as it has
+        // been read, so even one keeps a stage per wave in flight)
+        p.ring_off = (int)((p.lds + 255) & ~(size_t)255);
+        const size_t per_depth = 4 * (size_t)stage_bytes(s.ti);
+        p.depth = 1;
+        for (int d = 2; d >= 1; d--)
+            if (p.ring_off + d * per_depth <= 80 * 1024) { p.depth = d; break; }
+        p.lds = p.ring_off + p.depth * per_depth;
+    }
     const int64_t tile_rows = 4LL * (64 / p.lpr);
     p.ntiles = (int)((s.rows + tile_rows - 1) / tile_rows);
     return p;
@@ -177,6 +213,8 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     a.cols = s.cols;
     a.nunits = p.nunits;
     a.ntiles = p.ntiles;
+    a.depth = p.depth;
+    a.ring_off = p.ring_off;
     gemv_fn f = pick(s.type, p);
     if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
         return QG_EHIP;
@@ -224,7 +262,7 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
         Shape sc = s;
         sc.rows = rows - r0 < chunk ? rows - r0 : chunk;
         const uint8_t *Wc = (const uint8_t *)W + r0 * s.row_bytes;
-        Plan p = make_plan(sc, ntok, 0, 1, aligned(Wc, 4));
+        Plan p = make_plan(sc, ntok, 0, 1, aligned(Wc, 4), aligned(Wc, 16));
         GemvArgs a = {};
         a.W0 = a.W1 = Wc;
         a.rows0 = a.rows = sc.rows;
@@ -287,7 +325,7 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     float *gu = (float *)workspace;
     float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
     // gate and up rows together: act(gate) * up per row, raw gate / up kept in gu
-    Plan p1 = make_plan(s_g, ntok, 0, 1, aligned(W_gate, 4) && aligned(W_up, 4));
+    Plan p1 = make_plan(s_g, ntok, 0, 1, aligned(W_gate, 4) && aligned(W_up, 4), aligned(W_gate, 16) && aligned(W_up, 16));
     GemvArgs a = {};
     a.W0 = (const uint8_t *)W_gate;
     a.W1 = (const uint8_t *)W_up;
@@ -303,7 +341,7 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     rc = launch_gemv(s_g, p1, a, dim3(1, (ntok + p1.nt - 1) / p1.nt, 1), st);
     if (rc) return rc;
     // down on the activations
-    Plan p2 = make_plan(s_dn, ntok, 0, 1, aligned(W_down, 4));
+    Plan p2 = make_plan(s_dn, ntok, 0, 1, aligned(W_down, 4), aligned(W_down, 16));
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)W_down;
     b.rows0 = b.rows = hidden;
@@ -391,7 +429,8 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
 
     // 2. gate and up rows of every group's expert together: act(gate) * up per
     //    pair into act, raw gate / up into gu
-    Plan p1 = make_plan(s_g, ntok, 0, gmax, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0);
+    Plan p1 = make_plan(s_g, ntok, 0, gmax, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0,
+                        aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0);
     GemvArgs a = {};
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
     a.rows0 = a.rows = F;
@@ -409,7 +448,8 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     if (rc) return rc;
 
     // 3. down on each pair's activations
-    Plan p2 = make_plan(s_dn, ntok, 0, gmax, aligned(m->down, 4) && (m->down_stride % 4) == 0);
+    Plan p2 = make_plan(s_dn, ntok, 0, gmax, aligned(m->down, 4) && (m->down_stride % 4) == 0,
+                        aligned(m->down, 16) && (m->down_stride % 16) == 0);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;
     b.rows0 = b.rows = s_dn.rows;

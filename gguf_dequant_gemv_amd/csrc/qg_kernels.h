@@ -68,6 +68,10 @@ struct GemvArgs {
     int ntok;          // dense: tokens 0..ntok-1
     const int *grp;    // grouped: the routing table, or nullptr for dense
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
+    // LDS-staged variant (k_gemv_lds): stages in flight per wave and the byte
+    // offset of the stage rings in LDS
+    int depth;
+    int ring_off;
     int ntiles;        // row tiles of 4*RPW rows
 };
 
@@ -116,36 +120,52 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
     for (int t = 0; t < NT; t++) acc[t] += us[t];
 }
 
-// x[t] into LDS, zero-padded from cols to cpad.  a.x_vec: every source row is
-// 16-byte aligned, so whole float4s are loaded (cols is a multiple of 32).
-// All of a thread's loads are issued before any is stored, so staging costs
-// about one L2 round trip.
-template <int NT>
-QG_DEV void stage_x(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride) {
-    constexpr int B = 8;  // float4 loads in flight per thread
-    const int tid = threadIdx.x;
-    if (a.x_vec) {
-        const int n4 = cpad >> 2, c4 = cols >> 2;
-        for (int t = 0; t < NT; t++) {
-            const f32x4 *src = (const f32x4 *)(a.x + (int64_t)in_idx[t] * a.x_stride);
-            for (int base = tid; base < n4; base += 256 * B) {
-                f32x4 v[B];
+// ---- staging x[t] into LDS, zero-padded from cols to cpad ----
+// Vector path (a.x_vec: every source row 16-byte aligned, cols a multiple of
+// 32): batches of XB float4 per thread; the group sums the folding formats
+// need (SUMS consecutive values) are reduced across the SUMS/4 lanes holding
+// them while the batch is in registers.
+constexpr int XB = 8;
+
+QG_DEV void x_load(const float *src, int base0, int c4, f32x4 (&v)[XB]) {
 #pragma unroll
-                for (int b = 0; b < B; b++) v[b] = src[min(base + 256 * b, c4 - 1)];
+    for (int b = 0; b < XB; b++) v[b] = ((const f32x4 *)src)[min(base0 + (int)threadIdx.x + 256 * b, c4 - 1)];
+}
+
+template <int SUMS>
+QG_DEV void x_put(const f32x4 (&v)[XB], int base0, int n4, int c4, float *xt, float *st) {
 #pragma unroll
-                for (int b = 0; b < B; b++) {
-                    const int i = base + 256 * b;
-                    if (i < n4) {
-                        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                        *(f32x4 *)(xs + t * xstride + xpad(4 * i)) = i < c4 ? v[b] : z;
-                    }
-                }
-            }
+    for (int b = 0; b < XB; b++) {
+        const int i = base0 + (int)threadIdx.x + 256 * b;
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x4 val = i < c4 ? v[b] : z;
+        if constexpr (SUMS != 0) {
+            // every lane takes part; n4 is a multiple of SUMS/4, so a lane
+            // group is wholly inside or wholly past the row
+            const float g = group_sum<SUMS / 4>((val.x + val.y) + (val.z + val.w));
+            if (i < n4 && (i & (SUMS / 4 - 1)) == 0) st[(4 * i) / SUMS] = g;
         }
-    } else {
-        for (int t = 0; t < NT; t++) {
-            const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
-            for (int c = tid; c < cpad; c += 256) xs[t * xstride + xpad(c)] = c < cols ? src[c] : 0.0f;
+        if (i < n4) *(f32x4 *)(xt + xpad(4 * i)) = val;
+    }
+}
+
+// Scalar path (unaligned x): element by element, then the sums from LDS.
+template <int NT, int SUMS>
+QG_DEV void stage_x_scalar(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride,
+                           float *ss, int nsum) {
+    for (int t = 0; t < NT; t++) {
+        const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
+        for (int c = threadIdx.x; c < cpad; c += 256) xs[t * xstride + xpad(c)] = c < cols ? src[c] : 0.0f;
+    }
+    if constexpr (SUMS != 0) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < NT * nsum; i += 256) {
+            const int t = i / nsum, gi = i - t * nsum;
+            const float *p = xs + t * xstride + xpad(gi * SUMS);  // SUMS divides 64: no pad inside
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < SUMS; j += 2) { s0 += p[j]; s1 += p[j + 1]; }
+            ss[t * nsum + gi] = s0 + s1;
         }
     }
 }
@@ -244,6 +264,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         return hi;
     };
 
+    // ---- x: the first batch of the first vector goes out before the
+    //      weights, so that waiting for it does not wait for them ----
+    const int cols = a.cols;
+    const int cpad = a.nunits * UV;
+    const int xstride = xstride_of(cpad);
+    const int nsum = SUMS ? cpad / SUMS : 0;
+    const int n4 = cpad >> 2, c4 = cols >> 2;
+    float *xs = lds;
+    float *ss = lds + NT * xstride;
+    f32x4 xv[XB];
+    if (a.x_vec) x_load(a.x + (int64_t)in_idx[0] * a.x_stride, 0, c4, xv);
+    __builtin_amdgcn_sched_barrier(0);
+
     u32 w[D][U::NR];     // raw dwords of the units in flight
     u32 woff[D];         // and their byte offsets (the re-alignment shift)
     // issue pointer (element s + D), compute pointer (element s)
@@ -260,26 +293,20 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- stage x (zero-padded to whole units) and its group sums ----
-    const int cols = a.cols;
-    const int cpad = a.nunits * UV;
-    const int xstride = xstride_of(cpad);
-    const int nsum = SUMS ? cpad / SUMS : 0;
-    float *xs = lds;
-    float *ss = lds + NT * xstride;
-    stage_x<NT>(a, in_idx, cols, cpad, xs, xstride);
-    __syncthreads();
-    if constexpr (SUMS != 0) {
-        for (int i = threadIdx.x; i < NT * nsum; i += 256) {
-            const int t = i / nsum, gi = i - t * nsum;
-            const float *p = xs + t * xstride + xpad(gi * SUMS);  // SUMS divides 64: no pad inside
-            float s0 = 0.0f, s1 = 0.0f;
+    // ---- the rest of x, and the group sums ----
+    if (a.x_vec) {
 #pragma unroll
-            for (int j = 0; j < SUMS; j += 2) { s0 += p[j]; s1 += p[j + 1]; }
-            ss[t * nsum + gi] = s0 + s1;
+        for (int t = 0; t < NT; t++) {
+            const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
+            for (int base0 = 0; base0 < n4; base0 += 256 * XB) {
+                if (t != 0 || base0 != 0) x_load(src, base0, c4, xv);
+                x_put<SUMS>(xv, base0, n4, c4, xs + t * xstride, ss + t * nsum);
+            }
         }
-        __syncthreads();
+    } else {
+        stage_x_scalar<NT, SUMS>(a, in_idx, cols, cpad, xs, xstride, ss, nsum);
     }
+    __syncthreads();
 
     float acc[NT], gate[NT];
 #pragma unroll
@@ -355,6 +382,253 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         if (s0 + d < S) element(w[d], woff[d]);
 }
 
+// ------------------------------------------- GEMV, weights staged in LDS ---
+// The same element stream as k_gemv, but a wave's weights reach it through
+// LDS: for element (tile p, slot j) the wave needs, for each of its RPW rows,
+// the L consecutive units [jL, jL+L) -- one contiguous segment of L*BYTES
+// bytes per row, 16-byte aligned when rows and the tensor are.  Those
+// segments are copied HBM -> LDS with 16-byte buffer-to-LDS loads whose lanes
+// take consecutive 16-byte pieces of each segment, so every load instruction
+// reads whole cache lines; lane (grp, sub) then finds its unit at byte
+// lane*BYTES of the stage.  Each wave owns a ring of `depth` stages; a stage
+// is refilled as soon as its unit has been read into registers, so `depth`
+// stages stay in flight while the unit is decoded.  The waits on the
+// buffer-to-LDS loads are explicit vmcnt waits (the compiler does not track
+// them); y stores in between only make those waits stricter.
+template <class U>
+QG_DEV void lds_unit(const uint8_t *stage, u32 off, u32 (&wd)[U::ND]) {
+    if constexpr (U::BYTES % 16 == 0) {
+        const u32x4 *p = (const u32x4 *)(stage + off);
+#pragma unroll
+        for (int i = 0; i < U::ND / 4; i++) {
+            const u32x4 v = p[i];
+            wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
+        }
+    } else if constexpr (U::BYTES % 4 == 0) {
+        const u32 *p = (const u32 *)(stage + off);
+#pragma unroll
+        for (int i = 0; i < U::ND; i++) wd[i] = p[i];
+    } else {
+        const u32 *p = (const u32 *)(stage + (off & ~3u));
+        u32 t[U::NR];
+#pragma unroll
+        for (int i = 0; i < U::NR; i++) t[i] = p[i];
+        U::prep(t, off, wd);
+    }
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on)
+#define QG_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+#define QG_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
+template <int NI>
+QG_DEV void wait_stages(int k) {   // at most k stages (NI loads each) still in flight
+    switch (k) {
+    case 0: QG_WAIT_VM(0); break;
+    case 1: QG_WAIT_VM(NI); break;
+    case 2: QG_WAIT_VM(2 * NI); break;
+    default: QG_WAIT_VM(3 * NI); break;
+    }
+}
+
+template <class U>
+struct StageGeom {
+    static constexpr int BYTES = U::BYTES;
+    static constexpr int PIECES = 4 * BYTES;            // 64 units of BYTES bytes, 16 B each
+    static constexpr int NI = (PIECES + 63) / 64;        // load instructions per stage
+    static constexpr int LAST = PIECES - 64 * (NI - 1);  // lanes active in the last one
+    static constexpr int STAGE = NI * 1024;              // stage bytes in LDS
+};
+
+template <class U, int L, int NT>
+__global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
+    extern __shared__ float lds[];
+    constexpr int RPW = 64 / L;
+    constexpr int UV = U::VALUES;
+    constexpr int SUMS = U::SUMS;
+    constexpr int SPU = SUMS ? UV / SUMS : 0;
+    typedef StageGeom<U> G;
+    constexpr int SEG = L * U::BYTES / 16;               // pieces per row segment
+    static_assert((L * U::BYTES) % 16 == 0, "row segments must be whole 16-byte pieces");
+    static_assert(3 * G::NI <= 63, "vmcnt range");
+
+    // ---- which vectors this workgroup serves, and which weights ----
+    const uint8_t *Wg0 = a.W0, *Wg1 = a.W1;
+    int nt;
+    int in_idx[NT], out_idx[NT];
+    if (a.grp) {
+        const int Gn = a.grp[0];
+        const int g = blockIdx.y;
+        if (g >= Gn) return;
+        const int *rec = a.grp + 1 + g * GREC;
+        const int n = rec[2];
+        const int c0 = blockIdx.z * NT;
+        if (c0 >= n) return;
+        nt = min(NT, n - c0);
+        Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
+        Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const int i = c0 + min(t, nt - 1);
+            in_idx[t] = a.in_by_pair ? rec[19 + i] : rec[3 + i];
+            out_idx[t] = rec[19 + i];
+        }
+    } else {
+        const int c0 = blockIdx.y * NT;
+        nt = min(NT, a.ntok - c0);
+#pragma unroll
+        for (int t = 0; t < NT; t++) in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
+    }
+    // both ranges start 16-byte aligned here (the host checks)
+    const rsrc_t rs0 = make_rsrc(Wg0, (u32)a.bytes0);
+    const rsrc_t rs1 = make_rsrc(Wg1, (u32)a.bytes1);
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = lane / L, sub = lane % L;
+    const int K = (a.nunits + L - 1) / L;
+    const int KT = a.glu ? 2 * K : K;
+    const int P = ((int)a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int S = P * KT;
+    const int D = a.depth;
+    const int64_t rows = a.rows, rows0 = a.rows0;
+    const u32 rb = (u32)a.row_bytes;
+    uint8_t *ring = (uint8_t *)lds + a.ring_off + wave * D * G::STAGE;
+
+    // this lane's pieces: row within the wave's rows, byte within the segment
+    int prow[G::NI];
+    u32 poff[G::NI];
+#pragma unroll
+    for (int c = 0; c < G::NI; c++) {
+        const int pc = min(c * 64 + lane, G::PIECES - 1);
+        prow[c] = pc / SEG;
+        poff[c] = (u32)(pc % SEG) * 16u;
+    }
+    // copy element (p, j)'s segments into stage `slot`
+    auto issue = [&](int p, int j, int slot) {
+        const int64_t tile = (int64_t)blockIdx.x + (int64_t)p * gridDim.x;
+        const int64_t r0 = (tile * 4 + wave) * RPW;
+        bool hi;
+        int jj = j;
+        int64_t shift = 0;
+        if (a.glu) {
+            hi = j >= K;
+            jj = hi ? j - K : j;
+        } else {                 // waves never straddle rows0
+            hi = rows0 < rows && r0 >= rows0;
+            shift = hi ? rows0 : 0;
+        }
+        const rsrc_t rs = hi ? rs1 : rs0;
+        const u32 seg = (u32)jj * (u32)(L * U::BYTES);
+        __attribute__((address_space(3))) void *dst =
+            (__attribute__((address_space(3))) void *)(ring + slot * G::STAGE);
+#pragma unroll
+        for (int c = 0; c < G::NI; c++) {
+            const int64_t r = min(r0 + prow[c], rows - 1) - shift;
+            const u32 off = (u32)r * rb + seg + poff[c];
+            if (c < G::NI - 1 || lane < G::LAST)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)
+                                                         ((__attribute__((address_space(3))) uint8_t *)dst + c * 1024),
+                                                         16, off, 0, 0, 0);
+        }
+    };
+
+    // ---- x: the first batch goes out before the weights ----
+    const int cols = a.cols;
+    const int cpad = a.nunits * UV;
+    const int xstride = xstride_of(cpad);
+    const int nsum = SUMS ? cpad / SUMS : 0;
+    const int n4 = cpad >> 2, c4 = cols >> 2;
+    float *xs = lds;
+    float *ss = lds + NT * xstride;
+    f32x4 xv[XB];
+    if (a.x_vec) x_load(a.x + (int64_t)in_idx[0] * a.x_stride, 0, c4, xv);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the first `depth` stages ----
+    int ip = 0, ij = 0;          // next element to issue
+    for (int d = 0; d < D; d++) {
+        if (ip < P) {
+            issue(ip, ij, d);
+            if (++ij == KT) { ij = 0; ++ip; }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the rest of x, and the group sums ----
+    if (a.x_vec) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
+            for (int base0 = 0; base0 < n4; base0 += 256 * XB) {
+                if (t != 0 || base0 != 0) x_load(src, base0, c4, xv);
+                x_put<SUMS>(xv, base0, n4, c4, xs + t * xstride, ss + t * nsum);
+            }
+        }
+    } else {
+        stage_x_scalar<NT, SUMS>(a, in_idx, cols, cpad, xs, xstride, ss, nsum);
+    }
+    __syncthreads();
+
+    float acc[NT], gate[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) { acc[t] = 0.0f; gate[t] = 0.0f; }
+    int cp = 0, cj = 0;          // element being consumed
+    for (int s = 0; s < S; s++) {
+        const int slot = s % D;
+        // stage s has landed once no more than the later issued ones are in flight
+        wait_stages<G::NI>(min(D - 1, S - 1 - s));
+        u32 wd[U::ND];
+        lds_unit<U>(ring + slot * G::STAGE, (u32)lane * U::BYTES, wd);
+        QG_WAIT_LGKM0();   // the unit is in registers: the stage can be refilled
+        __builtin_amdgcn_sched_barrier(0);
+        if (ip < P) {
+            issue(ip, ij, slot);
+            if (++ij == KT) { ij = 0; ++ip; }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
+        const int64_t r0 = (tile * 4 + wave) * RPW;
+        const int u = sub + (cj >= K ? cj - K : cj) * L;
+        if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
+        ++cj;
+        if (a.glu && cj == K) {   // gate half done: keep its row sums
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                gate[t] = group_sum<L>(acc[t]);
+                acc[t] = 0.0f;
+            }
+        }
+        if (cj == KT) {  // end of this tile's row: reduce over the row's L lanes and store
+            cj = 0;
+            ++cp;
+#pragma unroll
+            for (int t = 0; t < NT; t++) acc[t] = group_sum<L>(acc[t]);
+            const int64_t r = r0 + grp;
+            if (sub == 0 && r < rows) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    if (t < nt) {
+                        if (a.glu) {
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
+                            if (a.y2) {
+                                a.y2[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
+                                a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
+                            }
+                        } else {
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = acc[t];
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; t++) acc[t] = 0.0f;
+        }
+    }
+    // no buffer-to-LDS load may still be in flight when the wave ends
+    QG_WAIT_VM(0);
+}
+
 // ------------------------------------------------------- dequantization ---
 // One thread per block: out[r][c] = value of W[r][c] as f32, through the same
 // loads and decoders as the GEMV (block units: any 2-byte phase).
@@ -381,7 +655,8 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *W, float *out, i
 typedef void (*gemv_fn)(GemvArgs);
 typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
 // Unit kinds: block units for every type; pair units for Q8_0 / Q4_0.
-enum { UK_BLOCK = 0, UK_PAIR = 1 };
+// UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or the K-quant blocks.
+enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2 };
 // One function per (block type, tokens per workgroup), each instantiated in
 // its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
 // (unit kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.

@@ -15,13 +15,20 @@ QG_DEV u32 order_key(float f) {  // monotone map f32 -> u32 (-0 folded onto +0)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-QG_DEV unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const unsigned long long o = __shfl_xor(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+// Maximum over the wave, uniform: DPP within each row of 16 lanes, then the
+// four row results through scalar registers.
+template <int CTRL>
+QG_DEV u32 dpp_u(u32 v) {
+    return (u32)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+QG_DEV u32 wave_max_u32(u32 v) {
+    v = max(v, dpp_u<0xB1>(v));    // lane ^ 1
+    v = max(v, dpp_u<0x4E>(v));    // lane ^ 2
+    v = max(v, dpp_u<0x141>(v));   // row_half_mirror
+    v = max(v, dpp_u<0x140>(v));   // row_mirror
+    const u32 a = (u32)__builtin_amdgcn_readlane((int)v, 0), b = (u32)__builtin_amdgcn_readlane((int)v, 16);
+    const u32 c = (u32)__builtin_amdgcn_readlane((int)v, 32), d = (u32)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
 }
 
 QG_DEV float wave_sum(float v) {
@@ -36,7 +43,11 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
                                                 int32_t *rt_valid, int32_t *grp) {
     __shared__ int s_ids[MAXT * 32];
     __shared__ int s_valid[MAXT];
+    __shared__ u32 s_tmask[256];    // expert e: bit t set when valid token t picked e
+    __shared__ int s_gidx[256];     // expert e: its group index
+    __shared__ int s_wcnt[16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int e = tid; e < E; e += blockDim.x) s_tmask[e] = 0u;
     if (wave < T) {
         const float *l = logits + (int64_t)wave * E;
         u32 key[4];
@@ -48,14 +59,18 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
             if (e >= E) taken |= 1u << i;
         }
         for (int j = 0; j < k; j++) {
-            u32 bk = 0u;
-            int bi = 0x7FFFFFFF;
+            // the largest key still free; among equal keys the lowest index
+            u32 lm = 0u;
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                if (!((taken >> i) & 1u) && (bi == 0x7FFFFFFF || key[i] > bk)) { bk = key[i]; bi = lane + 64 * i; }
-            unsigned long long kk = bi == 0x7FFFFFFF ? 0ull : (((unsigned long long)bk << 32) | (u32)(~(u32)bi));
-            kk = wave_max_u64(kk);
-            const int e = (int)(~(u32)(kk & 0xFFFFFFFFull));
+                if (!((taken >> i) & 1u)) lm = max(lm, key[i]);
+            const u32 M = wave_max_u32(lm);
+            int e = -1;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
+                if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
+            }
             if ((e & 63) == lane) taken |= 1u << (e >> 6);
             if (lane == 0) s_ids[wave * k + j] = e;
         }
@@ -63,8 +78,15 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
         // weights over the picks, relative to the top pick
         float ex = 0.0f;
         const float l0 = l[s_ids[wave * k]];
-        if (lane < k) ex = expf(l[s_ids[wave * k + lane]] - l0);
+        int ok = 1;
+        if (lane < k) {
+            const int id = s_ids[wave * k + lane];
+            ex = expf(l[id] - l0);
+            const int sl = slots ? slots[id] : 0;
+            ok = sl >= 0 && sl < n_slots;
+        }
         const float sum = wave_sum(ex);
+        const int all_ok = __ballot(!ok) == 0ull;
         if (lane < k) {
             const float wj = ex / sum;
             const int z = wave * k + lane;
@@ -74,25 +96,22 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
             if (w_out) w_out[z] = wj;
         }
         if (lane == 0) {
-            int ok = 1;
-            for (int j = 0; j < k; j++) {
-                const int sl = slots ? slots[s_ids[wave * k + j]] : 0;
-                ok &= (sl >= 0 && sl < n_slots);
-            }
-            s_valid[wave] = ok;
-            if (rt_valid) rt_valid[wave] = ok;
+            s_valid[wave] = all_ok;
+            if (rt_valid) rt_valid[wave] = all_ok;
         }
     }
     __syncthreads();
     if (!grp) return;
-    // Group pairs by expert: ascending expert id, pairs in (t, j) order.
-    // Thread e (< E) counts its expert's pairs; the group index is the number
-    // of lower experts with pairs (ballot per wave, wave totals through LDS).
-    __shared__ int s_wcnt[16];
-    int cnt = 0;
-    if (tid < E)
-        for (int z = 0; z < T * k; z++) cnt += (s_valid[z / k] && s_ids[z] == tid);
-    const unsigned long long mask = __ballot(tid < E && cnt > 0);
+    // Group pairs by expert: ascending expert id, pairs in (t, j) order.  A
+    // token picks an expert at most once, so a pair's place in its group is
+    // the number of lower tokens that picked the same expert.
+    for (int z = tid; z < T * k; z += blockDim.x) {
+        const int t = z / k;
+        if (s_valid[t]) atomicOr(&s_tmask[s_ids[z]], 1u << t);
+    }
+    __syncthreads();
+    const bool has = tid < E && s_tmask[tid] != 0u;
+    const unsigned long long mask = __ballot(has);
     if (lane == 0) s_wcnt[wave] = __popcll(mask);
     __syncthreads();
     int base = 0;
@@ -105,19 +124,22 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
         if (status) *status = ok ? 0 : -2;  // QG_OK / QG_EABSENT
         grp[0] = G;
     }
-    if (tid < E && cnt > 0) {
+    if (has) {
         int *rec = grp + 1 + gi * GREC;
-        int n = 0;
-        for (int z = 0; z < T * k; z++) {
-            if (s_valid[z / k] && s_ids[z] == tid) {
-                rec[3 + n] = z / k;
-                rec[19 + n] = z;
-                n++;
-            }
-        }
         rec[0] = tid;
         rec[1] = slots[tid];
-        rec[2] = n;
+        rec[2] = __popc(s_tmask[tid]);
+        s_gidx[tid] = gi;
+    }
+    __syncthreads();
+    for (int z = tid; z < T * k; z += blockDim.x) {
+        const int t = z / k;
+        if (!s_valid[t]) continue;
+        const int e = s_ids[z];
+        const int r = __popc(s_tmask[e] & ((1u << t) - 1u));
+        int *rec = grp + 1 + s_gidx[e] * GREC;
+        rec[3 + r] = t;
+        rec[19 + r] = z;
     }
 }
 
