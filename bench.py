@@ -22,7 +22,9 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-PROFILE_FACTORS = {}           # filled from profiles/ when counter runs exist
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+CSRC = os.path.join(HERE, "gguf_dequant_gemv_amd", "csrc")
 
 
 def log(*a):
@@ -40,6 +42,15 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (calibrates the HBM byte counters)")
+    ap.add_argument("--dominant-only", action="store_true",
+                    help="only launch the dominant kernel, eagerly, --steps times (for counter runs)")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="no GPU: summarise four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a "
+                         "--dominant-only run and of a --copy-probe run) into the text kept under profiles/")
+    ap.add_argument("--copy-mib", type=int, default=512, help="size of the --copy-probe run summarised")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "COMMAND"),
+                    help="no GPU: summarise the kernel statistics of a rocprofv3 --kernel-trace --stats run "
+                         "(output folder DIR, made by COMMAND) into the text kept under profiles/")
     return ap.parse_args()
 
 
@@ -94,6 +105,7 @@ class DenseMlpHead(Workload):
         self.bytes_per_step = self.mlp_bytes + self.dominant_bytes
         self.name = "q8_0 dense MLP decode 2560x9728 (gate||up, SwiGLU, down) + tied head 151936x2560, 1 token"
         self.dominant = "head GEMV Q8_0 151936x2560"
+        self.key = "head_q8_0_151936x2560"
         self.period = self.dominant_period = copies
 
     def step(self, i):
@@ -161,6 +173,7 @@ class GemvRot(Workload):
         self.dominant_bytes = wb
         self.name = label
         self.dominant = label
+        self.key = "gemv_%s_%dx%d_t%d" % (gs.NAMES[t].lower(), rows, cols, ntok)
         self.period = self.dominant_period = copies
 
     def step(self, i):
@@ -219,6 +232,7 @@ class MoeLayers(Workload):
         self.dominant_bytes = self.bytes_per_step
         self.name = label
         self.dominant = label
+        self.key = "moe_%s_%d_e%d_t%d" % (gs.NAMES[t].lower(), H, E, ntok)
         self.period = self.dominant_period = layers
 
     def step(self, i):
@@ -315,6 +329,114 @@ def time_workload(wl, steps, warmup):
     dom_ms = e0.elapsed_time(e1) / (reps * dper)
     return ms, dom_ms
 
+# ------------------------------------------------------ counter summaries --
+def source_hash():
+    """sha256 over the HIP sources: a counter summary holds only for the
+    kernels it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_rows(folder, counter):
+    import csv
+    out = []
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    for r in csv.DictReader(fh):
+                        if r["Counter_Name"] == counter:
+                            out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, wl_key, bytes_per_launch):
+    """Text summary: HBM bytes per launch of the dominant kernel from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
+    reads for a plain device copy of known size."""
+    def kavg(folder, counter, pick):
+        rows = [r for r in _counter_rows(folder, counter) if pick(r[0])]
+        if not rows:
+            raise SystemExit("no %s rows in %s" % (counter, folder))
+        names = sorted(set(r[0] for r in rows))
+        return sum(r[2] for r in rows) / len(rows), len(rows), names
+    gem = lambda n: "k_gemv" in n
+    cpy = lambda n: "copyBuffer" in n or "copy" in n.lower()
+    f, nf, names = kavg(fetch_dir, "FETCH_SIZE", gem)
+    w, nw, _ = kavg(write_dir, "WRITE_SIZE", gem)
+    cf, ncf, _ = kavg(cfetch_dir, "FETCH_SIZE", cpy)
+    cw, ncw, _ = kavg(cwrite_dir, "WRITE_SIZE", cpy)
+    kib = copy_mib * 1024.0
+    ff, fw = kib / cf, kib / cw
+    traffic = (f * ff + w * fw) * 1024.0
+    lines = [
+        "workload: %s" % wl_key,
+        "kernel: %s" % "; ".join(n.replace("void qg::", "").split("(")[0] for n in names),
+        "fetch_kib_per_dispatch: %.1f (mean of %d dispatches)" % (f, nf),
+        "write_kib_per_dispatch: %.1f (mean of %d dispatches)" % (w, nw),
+        "copy_probe_mib: %d (read %d MiB, write %d MiB per copy)" % (copy_mib, copy_mib, copy_mib),
+        "copy_fetch_kib: %.1f (%d dispatches) -> fetch factor %.4f" % (cf, ncf, ff),
+        "copy_write_kib: %.1f (%d dispatches) -> write factor %.4f" % (cw, ncw, fw),
+        "traffic_bytes_per_launch: %.0f" % traffic,
+        "algorithmic_bytes_per_launch: %d" % bytes_per_launch,
+        "traffic_over_algorithmic: %.4f" % (traffic / bytes_per_launch),
+        "source_sha256: %s" % source_hash(),
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def stats_summary(folder, command):
+    """Per-kernel table from rocprofv3's kernel_stats.csv: this library's
+    kernels one by one, everything else (input generation, copies) summed."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("kernel_stats.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no kernel_stats.csv under " + folder)
+    ours = [r for r in rows if "qg::" in r["Name"]]
+    rest = [r for r in rows if "qg::" not in r["Name"]]
+    out = ["command: " + command, "source_sha256: " + source_hash(), "",
+           "%-48s %7s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].replace("void qg::", "").split("(qg::")[0].split("(float")[0]
+        out.append("%-48s %7s %12.3f %12.3f %12.3f" % (name[:48], r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                       float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    tot = sum(float(r["TotalDurationNs"]) for r in rest)
+    calls = sum(int(r["Calls"]) for r in rest)
+    out.append("%-48s %7d %12s (total %.1f us)" % ("(other kernels: inputs, copies)", calls, "", tot / 1e3))
+    return "\n".join(out) + "\n"
+
+
+def load_traffic(wl_key):
+    """Measured HBM bytes per launch for this workload's dominant kernel, or
+    None when no summary exists or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic_%s.txt" % wl_key)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
     gbs = wl.bytes_per_step / (ms * 1e-3) / 1e9
     dom_gbs = wl.dominant_bytes / (dom_ms * 1e-3) / 1e9
@@ -333,7 +455,7 @@ def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
         "data": "synthetic (seeded), inputs resident in HBM",
         "config": {"workload": wl.name, "bytes_per_step": wl.bytes_per_step, "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(wl.key),
                      "kernel": wl.dominant, "bytes_per_launch": wl.dominant_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
     }
@@ -348,6 +470,16 @@ def main():
         print("bench.py: this build measures one GPU only (the path has no multi-GPU leg); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.stats_summary:
+        sys.stdout.write(stats_summary(*args.stats_summary))
+        return
+    if args.traffic_summary:
+        wl_cls = {"1": ("head_q8_0_151936x2560", 151936 * 80 * 34)}
+        key, nbytes = wl_cls.get(args.config, (None, None))
+        if key is None:
+            raise SystemExit("--traffic-summary: counter summaries are kept for config 1's head GEMV")
+        sys.stdout.write(traffic_summary(*args.traffic_summary, args.copy_mib, key, nbytes))
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -365,6 +497,12 @@ def main():
     qg.lib()   # fails loudly if the HIP library is not built
     log("[bench] workload", args.config)
     wl = make_workload(args.config, args.copies)
+    if args.dominant_only:
+        for i in range(args.steps):
+            wl.dominant_step(i)
+        torch.cuda.synchronize()
+        log("[bench] %d dominant launches: %s" % (args.steps, wl.dominant))
+        return
     ms, dom_ms = time_workload(wl, args.steps, args.warmup)
     log("[bench] %.4f ms/step, dominant %.4f ms" % (ms, dom_ms))
     cpu = None
