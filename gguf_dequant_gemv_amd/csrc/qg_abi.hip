@@ -65,6 +65,7 @@ struct Plan {
     int ntiles;          // row tiles of 4 * 64/lpr rows
     int64_t copies;      // independent problems sharing the GPU in one launch
     int depth;           // UK_LDS: stages in flight per wave
+    bool valu_heavy;     // K-quant units: decode-bound rather than HBM-bound
     int ring_off;        // UK_LDS: byte offset of the stage rings in LDS
     size_t lds;
 };
@@ -113,8 +114,16 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
             const double util = (double)nunits / ((double)lpr * per_lane);
             const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)p.copies;
             const double fill = waves >= 8.0 * NUM_CU ? 1.0 : waves / (8.0 * NUM_CU);
-            // pairs: half the load instructions and no re-alignment
-            const double score = util * (0.55 + 0.45 * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
+            // pairs: half the load instructions and no re-alignment.  Staged
+            // through LDS, each wave streams 64/lpr row segments of lpr units:
+            // segments of 1 KiB or more keep HBM reads in long runs (measured
+            // worth more than the idle lanes of a ragged last slot).
+            double seg = 1.0;
+            if (kind == UK_LDS) {
+                const double sb = (double)lpr * (s.ti.pairs ? 2 * s.ti.bytes : s.ti.bytes);
+                seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
+            }
+            const double score = util * seg * (0.55 + 0.45 * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
             if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
         }
     }
@@ -127,6 +136,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
     p.lds = lds_bytes(s.type, cpad, nt);
     p.depth = 0;
     p.ring_off = 0;
+    p.valu_heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
     if (p.kind == UK_LDS) {
         // stage rings after x: two stages per wave when two workgroups still
         // fit a CU's 160 KiB, else one (a stage is refilled as soon as it has
@@ -169,6 +179,18 @@ int resident_wgs(gemv_fn f, size_t lds) {
 int grid_for(const Plan &p, gemv_fn f) {
     int64_t cap = resident_wgs(f, p.lds) / p.copies;
     if (cap < 1) cap = 1;
+    if (p.kind == UK_LDS) {
+        // every tile its own workgroup while they all fit at once; past that,
+        // about two workgroups per CU, each streaming many tiles (fewer,
+        // longer HBM streams measured faster than filling every slot)
+        if (p.ntiles <= cap) return p.ntiles;
+        // the K-quant decode is VALU-heavy: there every resident slot helps
+        int64_t target = p.valu_heavy ? cap : 2 * NUM_CU / p.copies;
+        if (target < 1) target = 1;
+        if (target > cap) target = cap;
+        const int64_t tpw = (p.ntiles + target - 1) / target;
+        return (int)((p.ntiles + tpw - 1) / tpw);
+    }
     double best = 1e300;
     int64_t best_gx = p.ntiles;
     for (int64_t tpw = 1; tpw <= 16; tpw++) {
@@ -460,12 +482,14 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     b.y_stride = H;
     b.grp = grp;
     b.in_by_pair = 1;
+    b.escale = m->down_scale;   // (dn * s[e]) * c_z, the combine's terms
+    b.pscale = rt_w;
     rc = launch_gemv(s_dn, p2, b, dim3(1, gmax, (ntok + p2.nt - 1) / p2.nt), st);
     if (rc) return rc;
 
     // 4. weighted combine in pick order
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), ntok), dim3(256), 0, st, dn, rt_ids, rt_w,
-                       rt_valid, m->down_scale, y, H, topk);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), ntok), dim3(256), 0, st, dn, rt_valid, y, H,
+                       topk);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 

@@ -68,6 +68,10 @@ struct GemvArgs {
     int ntok;          // dense: tokens 0..ntok-1
     const int *grp;    // grouped: the routing table, or nullptr for dense
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
+    // grouped outputs scaled as (y * escale[expert]) * pscale[pair] when set
+    // (the MoE combine's per-expert down scale and routing weight)
+    const float *escale;
+    const float *pscale;
     // LDS-staged variant (k_gemv_lds): stages in flight per wave and the byte
     // offset of the stage rings in LDS
     int depth;
@@ -118,6 +122,30 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] += us[t];
+}
+
+// The same sums for one token with the unit's x values already in registers
+// (xr[k] = x[4k .. 4k+3] of the unit), so all of a unit's LDS reads can be in
+// flight together before the arithmetic starts.
+template <class U>
+QG_DEV void unit_dot_x(const u32 (&w)[U::ND], const f32x4 (&xr)[U::VALUES / 4], const float *ss, float &acc) {
+    float us = 0.0f;
+#pragma unroll
+    for (int g = 0; g < U::GROUPS; g++) {
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < U::GSIZE / 4; k++) {
+            const int i = g * U::GSIZE + 4 * k;
+            const f32x4 xv = xr[i >> 2];
+            float &s = (k & 1) ? s1 : s0;
+            s = fmaf(U::code(w, i), xv.x, s);
+            s = fmaf(U::code(w, i + 1), xv.y, s);
+            s = fmaf(U::code(w, i + 2), xv.z, s);
+            s = fmaf(U::code(w, i + 3), xv.w, s);
+        }
+        us += U::fold(w, g, s0 + s1, U::SUMS ? ss[g] : 0.0f);
+    }
+    acc += us;
 }
 
 // ---- staging x[t] into LDS, zero-padded from cols to cpad ----
@@ -203,6 +231,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     const uint8_t *Wg0 = a.W0, *Wg1 = a.W1;
     int nt;
     int in_idx[NT], out_idx[NT];
+    float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
     if (a.grp) {
         const int G = a.grp[0];
         const int g = blockIdx.y;
@@ -214,17 +243,23 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         nt = min(NT, n - c0);
         Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
         Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
+        const float es = a.escale ? a.escale[rec[0]] : 1.0f;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const int i = c0 + min(t, nt - 1);
             in_idx[t] = a.in_by_pair ? rec[19 + i] : rec[3 + i];
             out_idx[t] = rec[19 + i];
+            osc_e[t] = es;
+            osc_p[t] = a.pscale ? a.pscale[out_idx[t]] : 1.0f;
         }
     } else {
         const int c0 = blockIdx.y * NT;
         nt = min(NT, a.ntok - c0);
 #pragma unroll
-        for (int t = 0; t < NT; t++) in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
+        for (int t = 0; t < NT; t++) {
+            in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
+            osc_e[t] = osc_p[t] = 1.0f;
+        }
     }
 
     // ---- descriptors over the two weight ranges (tensor start aligned down) ----
@@ -362,7 +397,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
                                 a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
                             }
                         } else {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = acc[t];
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
                         }
                     }
                 }
@@ -457,6 +492,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     const uint8_t *Wg0 = a.W0, *Wg1 = a.W1;
     int nt;
     int in_idx[NT], out_idx[NT];
+    float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
     if (a.grp) {
         const int Gn = a.grp[0];
         const int g = blockIdx.y;
@@ -468,17 +504,23 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         nt = min(NT, n - c0);
         Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
         Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
+        const float es = a.escale ? a.escale[rec[0]] : 1.0f;
 #pragma unroll
         for (int t = 0; t < NT; t++) {
             const int i = c0 + min(t, nt - 1);
             in_idx[t] = a.in_by_pair ? rec[19 + i] : rec[3 + i];
             out_idx[t] = rec[19 + i];
+            osc_e[t] = es;
+            osc_p[t] = a.pscale ? a.pscale[out_idx[t]] : 1.0f;
         }
     } else {
         const int c0 = blockIdx.y * NT;
         nt = min(NT, a.ntok - c0);
 #pragma unroll
-        for (int t = 0; t < NT; t++) in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
+        for (int t = 0; t < NT; t++) {
+            in_idx[t] = out_idx[t] = c0 + min(t, nt - 1);
+            osc_e[t] = osc_p[t] = 1.0f;
+        }
     }
     // both ranges start 16-byte aligned here (the host checks)
     const rsrc_t rs0 = make_rsrc(Wg0, (u32)a.bytes0);
@@ -590,7 +632,16 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
         const int64_t r0 = (tile * 4 + wave) * RPW;
         const int u = sub + (cj >= K ? cj - K : cj) * L;
-        if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
+        if constexpr (NT == 1 && UV <= 64) {
+            // one token, 64-value units: all the unit's x reads go out at once
+            const float *xp = xs + xpad(min(u, a.nunits - 1) * UV);
+            f32x4 xr[UV / 4];
+#pragma unroll
+            for (int q = 0; q < UV / 4; q++) xr[q] = *(const f32x4 *)(xp + 4 * q);
+            if (u < a.nunits) unit_dot_x<U>(wd, xr, ss + u * SPU, acc[0]);
+        } else {
+            if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
+        }
         ++cj;
         if (a.glu && cj == K) {   // gate half done: keep its row sums
 #pragma unroll
@@ -616,7 +667,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
                                 a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
                             }
                         } else {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = acc[t];
+                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
                         }
                     }
                 }
@@ -676,7 +727,6 @@ dequant_fn dequant_kernel(int type);
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,
                         float *w_out, int32_t *status, int32_t *rt_ids, float *rt_w, int32_t *rt_valid,
                         int32_t *grp);
-__global__ void k_combine(const float *dn, const int32_t *rt_ids, const float *rt_w, const int32_t *rt_valid,
-                          const float *dscale, float *y, int64_t H, int k);
+__global__ void k_combine(const float *dn, const int32_t *rt_valid, float *y, int64_t H, int k);
 
 }  // namespace qg

@@ -31,10 +31,13 @@ QG_DEV u32 wave_max_u32(u32 v) {
     return max(max(a, b), max(c, d));
 }
 
-QG_DEV float wave_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-    return v;
+QG_DEV float wave_sum(float v) {   // every lane gets the same sum
+    v = group_sum<16>(v);
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (a + b) + (c + d);
 }
 
 __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int k, int T,
@@ -46,16 +49,23 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
     __shared__ u32 s_tmask[256];    // expert e: bit t set when valid token t picked e
     __shared__ int s_gidx[256];     // expert e: its group index
     __shared__ int s_wcnt[16];
+    __shared__ int s_slot[256];     // expert e: its pool slot
+    __shared__ float s_val[MAXT * 32];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int e = tid; e < E; e += blockDim.x) s_tmask[e] = 0u;
+    for (int e = tid; e < E; e += blockDim.x) {
+        s_tmask[e] = 0u;
+        s_slot[e] = slots ? slots[e] : 0;
+    }
     if (wave < T) {
         const float *l = logits + (int64_t)wave * E;
+        float lv[4];
         u32 key[4];
         u32 taken = 0u;  // bit i: value lane + 64 i is picked or absent
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int e = lane + 64 * i;
-            key[i] = e < E ? order_key(l[e]) : 0u;
+            lv[i] = e < E ? l[e] : 0.0f;
+            key[i] = order_key(lv[i]);
             if (e >= E) taken |= 1u << i;
         }
         for (int j = 0; j < k; j++) {
@@ -71,18 +81,26 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
                 const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
                 if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
             }
-            if ((e & 63) == lane) taken |= 1u << (e >> 6);
-            if (lane == 0) s_ids[wave * k + j] = e;
+            if ((e & 63) == lane) {
+                taken |= 1u << (e >> 6);
+                float v = lv[0];
+#pragma unroll
+                for (int i = 1; i < 4; i++) v = (e >> 6) == i ? lv[i] : v;
+                s_ids[wave * k + j] = e;
+                s_val[wave * k + j] = v;
+            }
         }
-        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();   // picks, logit values and slots visible to every wave
+    if (wave < T) {
         // weights over the picks, relative to the top pick
         float ex = 0.0f;
-        const float l0 = l[s_ids[wave * k]];
+        const float l0 = s_val[wave * k];
         int ok = 1;
         if (lane < k) {
             const int id = s_ids[wave * k + lane];
-            ex = expf(l[id] - l0);
-            const int sl = slots ? slots[id] : 0;
+            ex = expf(s_val[wave * k + lane] - l0);
+            const int sl = s_slot[id];
             ok = sl >= 0 && sl < n_slots;
         }
         const float sum = wave_sum(ex);
@@ -127,7 +145,7 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
     if (has) {
         int *rec = grp + 1 + gi * GREC;
         rec[0] = tid;
-        rec[1] = slots[tid];
+        rec[1] = s_slot[tid];
         rec[2] = __popc(s_tmask[tid]);
         s_gidx[tid] = gi;
     }
@@ -144,22 +162,28 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
 }
 
 // ------------------------------------------------------------- combine ----
-// y[t][h] = sum_j (dn[t*k + j][h] * s[id]) * w_j, added in pick order (the
-// gemma4_moe_ssd.js moeSum / qwen3_moe_ssd.js moeAccum combine); tokens with
-// an absent pick are left untouched.
-__global__ __launch_bounds__(256) void k_combine(const float *dn, const int32_t *rt_ids, const float *rt_w,
-                                                 const int32_t *rt_valid, const float *dscale, float *y,
-                                                 int64_t H, int k) {
+// y[t][h] = sum_j dn'[t*k + j][h], added in pick order, where the down launch
+// already stored dn' = (dn * s[id]) * w_j (the gemma4_moe_ssd.js moeSum /
+// qwen3_moe_ssd.js moeAccum combine, same operations in the same order);
+// tokens with an absent pick are left untouched.
+__global__ __launch_bounds__(256) void k_combine(const float *dn, const int32_t *rt_valid, float *y, int64_t H,
+                                                 int k) {
     const int t = blockIdx.y;
     const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (h >= H || !rt_valid[t]) return;
+    if (h >= H) return;
+    const int ok = rt_valid[t];
+    const float *p = dn + (int64_t)t * k * H + h;
     float acc = 0.0f;
-    for (int j = 0; j < k; j++) {
-        const int z = t * k + j;
-        const float s = dscale ? dscale[rt_ids[z]] : 1.0f;
-        acc += (dn[(int64_t)z * H + h] * s) * rt_w[z];
+    // eight picks' loads in flight at a time, added in pick order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = j0 + j < k ? p[(int64_t)(j0 + j) * H] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (j0 + j < k) acc += v[j];
     }
-    y[(int64_t)t * H + h] = acc;
+    if (ok) y[(int64_t)t * H + h] = acc;
 }
 
 }  // namespace qg
