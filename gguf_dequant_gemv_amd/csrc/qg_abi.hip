@@ -70,14 +70,18 @@ struct Plan {
     size_t lds;
 };
 
-// Bytes of one UK_LDS stage: 64 units in whole KiB (16-byte pieces, 64 per load).
-int stage_bytes(const TypeInfo &ti) {
+bool lds_kind(int kind) { return kind == UK_LDS || kind == UK_LDS2; }
+
+// Bytes of one LDS stage in whole KiB: 64/lpr rows of lpr units in 16-byte
+// pieces (UK_LDS2 fetches one more piece per row), 64 pieces per load.
+int stage_bytes(const TypeInfo &ti, int lpr, int kind) {
     const int ub = ti.pairs ? 2 * ti.bytes : ti.bytes;
-    return (4 * ub + 63) / 64 * 1024;
+    const int pieces = (64 / lpr) * (lpr * ub / 16 + (kind == UK_LDS2 ? 1 : 0));
+    return (pieces + 63) / 64 * 1024;
 }
 
 int unit_count(const Shape &s, int kind) {
-    if (kind == UK_PAIR || (kind == UK_LDS && s.ti.pairs)) return s.nb / 2;
+    if (kind == UK_PAIR || (lds_kind(kind) && s.ti.pairs)) return s.nb / 2;
     return s.cols / s.ti.block_vals;
 }
 
@@ -94,22 +98,25 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
     while (nt < ntok_max && nt < 8) nt <<= 1;
     p.copies = copies > 0 ? copies : 1;
     const bool pairs = s.ti.pairs && pair_ok && (s.nb % 2) == 0;
-    const bool staged = lds_ok && (s.row_bytes % 16) == 0 && (!s.ti.pairs || (s.nb % 2) == 0);
+    // staged through LDS: 16-byte aligned (UK_LDS) or any 2-byte phase
+    // (UK_LDS2); pair units need an even number of blocks per row
+    const bool units_ok = !s.ti.pairs || (s.nb % 2) == 0;
+    const int staged = !units_ok ? -1 : (lds_ok && (s.row_bytes % 16) == 0) ? UK_LDS : UK_LDS2;
     double best = -1.0;
     p.kind = UK_BLOCK;
     p.lpr = 64;
-    const int kinds[3] = {UK_BLOCK, UK_PAIR, UK_LDS};
-    for (int ki = 0; ki < 3; ki++) {
+    const int kinds[4] = {UK_BLOCK, UK_PAIR, UK_LDS, UK_LDS2};
+    for (int ki = 0; ki < 4; ki++) {
         const int kind = kinds[ki];
         if (kind == UK_PAIR && !pairs) continue;
-        if (kind == UK_LDS && !staged) continue;
-        if (staged && kind != UK_LDS) continue;   // staging through LDS wins whenever it applies
+        if (staged >= 0 && kind != staged) continue;   // staging through LDS wins whenever it applies
+        if (staged < 0 && lds_kind(kind)) continue;
         const int nunits = unit_count(s, kind);
         const int cands[5] = {64, 32, 16, 8, 4};
         for (int ci = 0; ci < 5; ci++) {
             const int lpr = cands[ci], rpw = 64 / lpr;
             if (rows_align > 0 && rows_align % rpw) continue;
-            if (kind == UK_LDS && s.type == QG_Q6_K && lpr < 8) continue;   // 210-byte units: 16-byte segments need 8
+            if (lds_kind(kind) && s.type == QG_Q6_K && lpr < 8) continue;   // 210-byte units: 16-byte segments need 8
             const int per_lane = (nunits + lpr - 1) / lpr;
             const double util = (double)nunits / ((double)lpr * per_lane);
             const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)p.copies;
@@ -119,7 +126,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
             // segments of 1 KiB or more keep HBM reads in long runs (measured
             // worth more than the idle lanes of a ragged last slot).
             double seg = 1.0;
-            if (kind == UK_LDS) {
+            if (lds_kind(kind)) {
                 const double sb = (double)lpr * (s.ti.pairs ? 2 * s.ti.bytes : s.ti.bytes);
                 seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
             }
@@ -128,21 +135,21 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
         }
     }
     p.nunits = unit_count(s, p.kind);
-    const int uv = (p.kind == UK_PAIR || (p.kind == UK_LDS && s.ti.pairs)) ? 2 * s.ti.qk : s.ti.block_vals;
+    const int uv = (p.kind == UK_PAIR || (lds_kind(p.kind) && s.ti.pairs)) ? 2 * s.ti.qk : s.ti.block_vals;
     const int cpad = p.nunits * uv;
-    const size_t xcap = p.kind == UK_LDS ? 96 * 1024 : 64 * 1024;
+    const size_t xcap = lds_kind(p.kind) ? 96 * 1024 : 64 * 1024;
     while (nt > 1 && lds_bytes(s.type, cpad, nt) > xcap) nt >>= 1;
     p.nt = nt;
     p.lds = lds_bytes(s.type, cpad, nt);
     p.depth = 0;
     p.ring_off = 0;
     p.valu_heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
-    if (p.kind == UK_LDS) {
+    if (lds_kind(p.kind)) {
         // stage rings after x: two stages per wave when two workgroups still
         // fit a CU's 160 KiB, else one (a stage is refilled as soon as it has
         // been read, so even one keeps a stage per wave in flight)
         p.ring_off = (int)((p.lds + 255) & ~(size_t)255);
-        const size_t per_depth = 4 * (size_t)stage_bytes(s.ti);
+        const size_t per_depth = 4 * (size_t)stage_bytes(s.ti, p.lpr, p.kind);
         p.depth = 1;
         for (int d = 2; d >= 1; d--)
             if (p.ring_off + d * per_depth <= 80 * 1024) { p.depth = d; break; }
@@ -179,7 +186,7 @@ int resident_wgs(gemv_fn f, size_t lds) {
 int grid_for(const Plan &p, gemv_fn f) {
     int64_t cap = resident_wgs(f, p.lds) / p.copies;
     if (cap < 1) cap = 1;
-    if (p.kind == UK_LDS) {
+    if (lds_kind(p.kind)) {
         // every tile its own workgroup while they all fit at once; past that,
         // about two workgroups per CU, each streaming many tiles (fewer,
         // longer HBM streams measured faster than filling every slot)

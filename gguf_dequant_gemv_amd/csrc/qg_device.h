@@ -45,6 +45,13 @@ QG_DEV u32 half_at(const u32 *w, int pos) { return (w[pos >> 2] >> (8 * (pos & 3
 QG_DEV float s8_at(const u32 *w, int pos) { return (float)(int8_t)(w[pos >> 2] >> (8 * (pos & 3))); }
 QG_DEV float u8_of(u32 word, int b) { return (float)((word >> (8 * b)) & 0xFFu); }
 
+// The value unchanged, but opaque to the optimiser: a masked word then feeds
+// four byte-select converts instead of being re-extracted field by field.
+QG_DEV u32 opaque(u32 v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // ------------------------------------------------------- buffer loads -----
 // Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
 QG_DEV rsrc_t make_rsrc(const void *base, u32 bytes) {
@@ -108,6 +115,11 @@ __host__ __device__ inline int xstride_of(int cols) { return cols + ((cols >> 6)
 //   prep(raw, off, w)    the loaded dwords in decode order (after they arrive)
 //   load(r, off, w)      issue + prep
 //   code(w, i)           integer code of value i as f32 (exact)
+//   dcode(w, i)          the code as the dot products use it: times dfix(g, h)^-1
+//                        for half h of group g (a high nibble left in place is
+//                        16 times the code; the factor is a power of two, so
+//                        dcode*x sums scale back exactly)
+//   dfix(g, h)           that factor (1 or 1/16)
 //   fold(w, g, s, xs)    group g's contribution from s = sum(code*x), xs = sum(x)
 //   value(w, i)          the dequantized value as f32 (one rounding)
 
@@ -141,6 +153,8 @@ struct UQ8_0B {
     QG_DEV static void prep(const u32 (&t)[NR], u32 off, u32 (&w)[ND]) { realign<9>(t, off, w); }
     QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { u32 t[NR]; issue(r, off, t); prep(t, off, w); }
     QG_DEV static float scale(const u32 (&w)[ND]) { return h2f(w[0]); }
+    QG_DEV static float dfix(int, int) { return 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) { return code(w, i); }
     QG_DEV static float code(const u32 (&w)[ND], int i) { return s8_at(w, 2 + i); }
     QG_DEV static float fold(const u32 (&w)[ND], int, float s, float) { return scale(w) * s; }
     QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w) * code(w, i); }
@@ -158,6 +172,8 @@ struct UQ8_0P {
     }
     QG_DEV static void load(rsrc_t r, u32 off, u32 (&w)[ND]) { ldn<17>(r, off, w); }
     QG_DEV static float scale(const u32 (&w)[ND], int g) { return h2f(half_at(w, 34 * g)); }
+    QG_DEV static float dfix(int, int) { return 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) { return code(w, i); }
     QG_DEV static float code(const u32 (&w)[ND], int i) { return s8_at(w, 34 * (i >> 5) + 2 + (i & 31)); }
     QG_DEV static float fold(const u32 (&w)[ND], int g, float s, float) { return scale(w, g) * s; }
     QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w, i >> 5) * code(w, i); }
@@ -177,6 +193,12 @@ struct UQ4_0B {
         const u32 word = w[pos >> 2];
         const u32 m = (i & 16) ? ((word >> 4) & 0x0F0F0F0Fu) : (word & 0x0F0F0F0Fu);
         return u8_of(m, pos & 3);
+    }
+    // values 16..31 are the high nibbles: 16 * code in place
+    QG_DEV static float dfix(int, int h) { return h ? 0.0625f : 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) {
+        const int pos = 2 + (i & 15);
+        return u8_of(opaque(w[pos >> 2] & ((i & 16) ? 0xF0F0F0F0u : 0x0F0F0F0Fu)), pos & 3);
     }
     // d * sum((q - 8) x) = d * (sum(q x) - 8 sum(x))
     QG_DEV static float fold(const u32 (&w)[ND], int, float s, float xs) { return scale(w) * fmaf(-8.0f, xs, s); }
@@ -199,6 +221,11 @@ struct UQ4_0P {
         const u32 word = w[pos >> 2];
         const u32 m = (i & 16) ? ((word >> 4) & 0x0F0F0F0Fu) : (word & 0x0F0F0F0Fu);
         return u8_of(m, pos & 3);
+    }
+    QG_DEV static float dfix(int, int h) { return h ? 0.0625f : 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) {
+        const int pos = 18 * (i >> 5) + 2 + (i & 15);
+        return u8_of(opaque(w[pos >> 2] & ((i & 16) ? 0xF0F0F0F0u : 0x0F0F0F0Fu)), pos & 3);
     }
     QG_DEV static float fold(const u32 (&w)[ND], int g, float s, float xs) { return scale(w, g) * fmaf(-8.0f, xs, s); }
     QG_DEV static float value(const u32 (&w)[ND], int i) { return scale(w, i >> 5) * (code(w, i) - 8.0f); }
@@ -231,6 +258,12 @@ struct UQ4_K {
         const u32 m = hi ? ((word >> 4) & 0x0F0F0F0Fu) : (word & 0x0F0F0F0Fu);
         return u8_of(m, i & 3);
     }
+    // odd sub-blocks are the high nibbles: 16 * code in place
+    QG_DEV static float dfix(int g, int) { return (g & 1) ? 0.0625f : 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) {
+        const int c = i >> 6, hi = (i >> 5) & 1, k = (i & 31) >> 2;
+        return u8_of(opaque(w[4 + 8 * c + k] & (hi ? 0xF0F0F0F0u : 0x0F0F0F0Fu)), i & 3);
+    }
     // d*sc*sum(q x) - dmin*m*sum(x)
     QG_DEV static float fold(const u32 (&w)[ND], int g, float s, float xs) { return fmaf(dsc(w, g), s, -(dmn(w, g) * xs)); }
     // (d*sc)*q - dmin*m with one rounding: both products are exact in f32
@@ -254,6 +287,10 @@ struct UQ6_K {
         const u32 lo = (p >> 1) ? ((ql >> 4) & 0x0F0F0F0Fu) : (ql & 0x0F0F0F0Fu);
         const u32 hb = (p == 0) ? (qh << 4) : (p == 1) ? (qh << 2) : (p == 2) ? qh : (qh >> 2);
         return lo | (hb & 0x30303030u);
+    }
+    QG_DEV static float dfix(int, int) { return 1.0f; }
+    QG_DEV static float dcode(const u32 (&w)[ND], int i) {  // one code word per 4 values
+        return u8_of(opaque(code4(w, i >> 7, (i >> 5) & 3, (i & 31) >> 2)), i & 3);
     }
     QG_DEV static float code(const u32 (&w)[ND], int i) {  // 0..63
         return u8_of(code4(w, i >> 7, (i >> 5) & 3, (i & 31) >> 2), i & 3);

@@ -18,22 +18,22 @@ gemv_fn pick_lpr(int lpr) {
     }
 }
 
-template <class U, int NT>
+template <class U, int NT, bool ALN>
 gemv_fn pick_lpr_lds(int lpr) {
     if constexpr (U::BYTES % 4 != 0) {   // 8 lanes or more make whole 16-byte segments
         switch (lpr) {
-        case 16: return k_gemv_lds<U, 16, NT>;
-        case 32: return k_gemv_lds<U, 32, NT>;
-        case 64: return k_gemv_lds<U, 64, NT>;
-        default: return k_gemv_lds<U, 8, NT>;
+        case 16: return k_gemv_lds<U, 16, NT, ALN>;
+        case 32: return k_gemv_lds<U, 32, NT, ALN>;
+        case 64: return k_gemv_lds<U, 64, NT, ALN>;
+        default: return k_gemv_lds<U, 8, NT, ALN>;
         }
     } else {
         switch (lpr) {
-        case 4: return k_gemv_lds<U, 4, NT>;
-        case 8: return k_gemv_lds<U, 8, NT>;
-        case 16: return k_gemv_lds<U, 16, NT>;
-        case 32: return k_gemv_lds<U, 32, NT>;
-        default: return k_gemv_lds<U, 64, NT>;
+        case 4: return k_gemv_lds<U, 4, NT, ALN>;
+        case 8: return k_gemv_lds<U, 8, NT, ALN>;
+        case 16: return k_gemv_lds<U, 16, NT, ALN>;
+        case 32: return k_gemv_lds<U, 32, NT, ALN>;
+        default: return k_gemv_lds<U, 64, NT, ALN>;
         }
     }
 }
@@ -46,7 +46,8 @@ template <> struct Units<T_Q6_K> { typedef UQ6_K B; typedef UQ6_K P; };
 
 template <int TY, int NT>
 gemv_fn pick(int kind, int lpr) {
-    if (kind == UK_LDS) return pick_lpr_lds<typename Units<TY>::P, NT>(lpr);
+    if (kind == UK_LDS) return pick_lpr_lds<typename Units<TY>::P, NT, true>(lpr);
+    if (kind == UK_LDS2) return pick_lpr_lds<typename Units<TY>::P, NT, false>(lpr);
     if constexpr (TY == T_Q8_0 || TY == T_Q4_0) {
         if (kind == UK_PAIR) return pick_lpr<typename Units<TY>::P, NT>(lpr);
     }

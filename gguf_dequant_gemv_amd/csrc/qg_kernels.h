@@ -95,15 +95,16 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
         float s0[NT], s1[NT];
 #pragma unroll
         for (int t = 0; t < NT; t++) { s0[t] = 0.0f; s1[t] = 0.0f; }
+        // s0 sums the group's first half, s1 its second (dcode scale dfix)
 #pragma unroll
         for (int k = 0; k < U::GSIZE / 4; k++) {
             const int i = g * U::GSIZE + 4 * k;
-            const float q0 = U::code(w, i), q1 = U::code(w, i + 1);
-            const float q2 = U::code(w, i + 2), q3 = U::code(w, i + 3);
+            const float q0 = U::dcode(w, i), q1 = U::dcode(w, i + 1);
+            const float q2 = U::dcode(w, i + 2), q3 = U::dcode(w, i + 3);
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 const f32x4 xv = *(const f32x4 *)(xs + t * xstride + i + ((i >> 6) << 2));
-                float &s = (k & 1) ? s1[t] : s0[t];
+                float &s = (k >= U::GSIZE / 8) ? s1[t] : s0[t];
                 s = fmaf(q0, xv.x, s);
                 s = fmaf(q1, xv.y, s);
                 s = fmaf(q2, xv.z, s);
@@ -112,7 +113,8 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
         }
 #pragma unroll
         for (int t = 0; t < NT; t++)
-            us[t] += U::fold(w, g, s0[t] + s1[t], U::SUMS ? ss[t * sstride + g] : 0.0f);
+            us[t] += U::fold(w, g, fmaf(s1[t], U::dfix(g, 1), s0[t] * U::dfix(g, 0)),
+                             U::SUMS ? ss[t * sstride + g] : 0.0f);
         // decode group by group: keeps a block's codes from all being live at once
         if constexpr (U::GROUPS > 2) {
             // finish this group's sums before the next group's x reads start
@@ -137,13 +139,13 @@ QG_DEV void unit_dot_x(const u32 (&w)[U::ND], const f32x4 (&xr)[U::VALUES / 4], 
         for (int k = 0; k < U::GSIZE / 4; k++) {
             const int i = g * U::GSIZE + 4 * k;
             const f32x4 xv = xr[i >> 2];
-            float &s = (k & 1) ? s1 : s0;
-            s = fmaf(U::code(w, i), xv.x, s);
-            s = fmaf(U::code(w, i + 1), xv.y, s);
-            s = fmaf(U::code(w, i + 2), xv.z, s);
-            s = fmaf(U::code(w, i + 3), xv.w, s);
+            float &s = (k >= U::GSIZE / 8) ? s1 : s0;
+            s = fmaf(U::dcode(w, i), xv.x, s);
+            s = fmaf(U::dcode(w, i + 1), xv.y, s);
+            s = fmaf(U::dcode(w, i + 2), xv.z, s);
+            s = fmaf(U::dcode(w, i + 3), xv.w, s);
         }
-        us += U::fold(w, g, s0 + s1, U::SUMS ? ss[g] : 0.0f);
+        us += U::fold(w, g, fmaf(s1, U::dfix(g, 1), s0 * U::dfix(g, 0)), U::SUMS ? ss[g] : 0.0f);
     }
     acc += us;
 }
@@ -430,9 +432,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 // stages stay in flight while the unit is decoded.  The waits on the
 // buffer-to-LDS loads are explicit vmcnt waits (the compiler does not track
 // them); y stores in between only make those waits stricter.
-template <class U>
+template <class U, bool ALN>
 QG_DEV void lds_unit(const uint8_t *stage, u32 off, u32 (&wd)[U::ND]) {
-    if constexpr (U::BYTES % 16 == 0) {
+    if constexpr (!ALN) {   // any 2-byte phase: aligned dwords, shifted into place
+        const u32 *p = (const u32 *)(stage + (off & ~3u));
+        u32 t[U::ND + 1];
+#pragma unroll
+        for (int i = 0; i <= U::ND; i++) t[i] = p[i];
+        realign<U::ND>(t, off, wd);
+    } else if constexpr (U::BYTES % 16 == 0) {
         const u32x4 *p = (const u32x4 *)(stage + off);
 #pragma unroll
         for (int i = 0; i < U::ND / 4; i++) {
@@ -467,24 +475,29 @@ QG_DEV void wait_stages(int k) {   // at most k stages (NI loads each) still in 
     }
 }
 
-template <class U>
+// A stage: for each of the wave's RPW rows, SEGP 16-byte pieces from the
+// segment's 16-byte-aligned start (one more than the segment's own when the
+// segment may start mid-piece).
+template <class U, int L, bool ALN>
 struct StageGeom {
-    static constexpr int BYTES = U::BYTES;
-    static constexpr int PIECES = 4 * BYTES;            // 64 units of BYTES bytes, 16 B each
-    static constexpr int NI = (PIECES + 63) / 64;        // load instructions per stage
-    static constexpr int LAST = PIECES - 64 * (NI - 1);  // lanes active in the last one
-    static constexpr int STAGE = NI * 1024;              // stage bytes in LDS
+    static constexpr int RPW = 64 / L;
+    static constexpr int SEG = L * U::BYTES / 16;         // pieces per row segment
+    static constexpr int SEGP = SEG + (ALN ? 0 : 1);      // pieces fetched per row
+    static constexpr int PIECES = RPW * SEGP;
+    static constexpr int NI = (PIECES + 63) / 64;         // load instructions per stage
+    static constexpr int LAST = PIECES - 64 * (NI - 1);   // lanes active in the last one
+    static constexpr int STAGE = NI * 1024;               // stage bytes in LDS
 };
 
-template <class U, int L, int NT>
+template <class U, int L, int NT, bool ALN>
 __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     extern __shared__ float lds[];
     constexpr int RPW = 64 / L;
     constexpr int UV = U::VALUES;
     constexpr int SUMS = U::SUMS;
     constexpr int SPU = SUMS ? UV / SUMS : 0;
-    typedef StageGeom<U> G;
-    constexpr int SEG = L * U::BYTES / 16;               // pieces per row segment
+    typedef StageGeom<U, L, ALN> G;
+    constexpr int SEGP = G::SEGP;
     static_assert((L * U::BYTES) % 16 == 0, "row segments must be whole 16-byte pieces");
     static_assert(3 * G::NI <= 63, "vmcnt range");
 
@@ -522,9 +535,15 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
             osc_e[t] = osc_p[t] = 1.0f;
         }
     }
-    // both ranges start 16-byte aligned here (the host checks)
-    const rsrc_t rs0 = make_rsrc(Wg0, (u32)a.bytes0);
-    const rsrc_t rs1 = make_rsrc(Wg1, (u32)a.bytes1);
+    // descriptors from the ranges' 16-byte-aligned starts (ALN: the ranges,
+    // their rows and segments all start 16-byte aligned; the host checks).
+    // The range check works on whole loads, so each range is rounded up to
+    // the 16-byte piece holding its last byte (that piece lies in the same
+    // page as the byte, so reading it is safe; the bytes past the end are
+    // never decoded).
+    const u32 ph0 = ALN ? 0u : (u32)((uintptr_t)Wg0 & 15u), ph1 = ALN ? 0u : (u32)((uintptr_t)Wg1 & 15u);
+    const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
+    const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = lane / L, sub = lane % L;
@@ -543,8 +562,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < G::NI; c++) {
         const int pc = min(c * 64 + lane, G::PIECES - 1);
-        prow[c] = pc / SEG;
-        poff[c] = (u32)(pc % SEG) * 16u;
+        prow[c] = pc / SEGP;
+        poff[c] = (u32)(pc % SEGP) * 16u;
     }
     // copy element (p, j)'s segments into stage `slot`
     auto issue = [&](int p, int j, int slot) {
@@ -561,13 +580,13 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
             shift = hi ? rows0 : 0;
         }
         const rsrc_t rs = hi ? rs1 : rs0;
-        const u32 seg = (u32)jj * (u32)(L * U::BYTES);
+        const u32 seg = (u32)jj * (u32)(L * U::BYTES) + (hi ? ph1 : ph0);
         __attribute__((address_space(3))) void *dst =
             (__attribute__((address_space(3))) void *)(ring + slot * G::STAGE);
 #pragma unroll
         for (int c = 0; c < G::NI; c++) {
             const int64_t r = min(r0 + prow[c], rows - 1) - shift;
-            const u32 off = (u32)r * rb + seg + poff[c];
+            const u32 off = (((u32)r * rb + seg) & ~15u) + poff[c];
             if (c < G::NI - 1 || lane < G::LAST)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)
                                                          ((__attribute__((address_space(3))) uint8_t *)dst + c * 1024),
@@ -621,7 +640,17 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         // stage s has landed once no more than the later issued ones are in flight
         wait_stages<G::NI>(min(D - 1, S - 1 - s));
         u32 wd[U::ND];
-        lds_unit<U>(ring + slot * G::STAGE, (u32)lane * U::BYTES, wd);
+        u32 uoff = (u32)lane * U::BYTES;   // where this lane's unit sits in the stage
+        if constexpr (!ALN) {
+            const int64_t tl = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
+            const int64_t rw0 = (tl * 4 + wave) * RPW;
+            const bool hi = a.glu ? cj >= K : (rows0 < rows && rw0 >= rows0);
+            const int64_t rr = min(rw0 + grp, rows - 1) - (!a.glu && hi ? rows0 : 0);
+            const u32 jj = (u32)(a.glu && hi ? cj - K : cj);
+            const u32 phase = ((u32)rr * rb + jj * (u32)(L * U::BYTES) + (hi ? ph1 : ph0)) & 15u;
+            uoff = (u32)grp * (SEGP * 16) + phase + (u32)sub * U::BYTES;
+        }
+        lds_unit<U, ALN>(ring + slot * G::STAGE, uoff, wd);
         QG_WAIT_LGKM0();   // the unit is in registers: the stage can be refilled
         __builtin_amdgcn_sched_barrier(0);
         if (ip < P) {
@@ -706,8 +735,9 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *W, float *out, i
 typedef void (*gemv_fn)(GemvArgs);
 typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
 // Unit kinds: block units for every type; pair units for Q8_0 / Q4_0.
-// UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or the K-quant blocks.
-enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2 };
+// UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or the K-quant blocks,
+// 16-byte aligned ranges and rows; UK_LDS2: the same for 2-byte alignment.
+enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2, UK_LDS2 = 3 };
 // One function per (block type, tokens per workgroup), each instantiated in
 // its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
 // (unit kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
