@@ -125,12 +125,16 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
             // through LDS, each wave streams 64/lpr row segments of lpr units:
             // segments of 1 KiB or more keep HBM reads in long runs (measured
             // worth more than the idle lanes of a ragged last slot).
+            // The K-quant decode is VALU-bound: there idle lanes cost most and
+            // fewer lanes per row (more units each) measured fastest.
+            const bool heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
             double seg = 1.0;
-            if (lds_kind(kind)) {
+            if (lds_kind(kind) && !heavy) {
                 const double sb = (double)lpr * (s.ti.pairs ? 2 * s.ti.bytes : s.ti.bytes);
                 seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
             }
-            const double score = util * seg * (0.55 + 0.45 * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
+            const double fw = heavy ? 0.1 : 0.45;
+            const double score = util * seg * (1.0 - fw + fw * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
             if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
         }
     }
@@ -458,7 +462,13 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
 
     // 2. gate and up rows of every group's expert together: act(gate) * up per
     //    pair into act, raw gate / up into gu
-    Plan p1 = make_plan(s_g, ntok, 0, gmax, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0,
+    // tokens per workgroup for a group: a group holds the pairs that picked one
+    // expert, on average about ntok*topk/E of them, so chunks sized for the
+    // typical group (a few tokens) keep workgroups from computing copies
+    int gtok = (2 * ntok * topk + E - 1) / E;
+    gtok = gtok < 1 ? 1 : (gtok > ntok ? ntok : gtok);
+    const int busy = (pairs + gtok - 1) / gtok;   // about this many (group, chunk) sets carry work
+    Plan p1 = make_plan(s_g, gtok, 0, busy, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0,
                         aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0);
     GemvArgs a = {};
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
@@ -477,7 +487,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     if (rc) return rc;
 
     // 3. down on each pair's activations
-    Plan p2 = make_plan(s_dn, ntok, 0, gmax, aligned(m->down, 4) && (m->down_stride % 4) == 0,
+    Plan p2 = make_plan(s_dn, gtok, 0, busy, aligned(m->down, 4) && (m->down_stride % 4) == 0,
                         aligned(m->down, 16) && (m->down_stride % 16) == 0);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;

@@ -1,0 +1,99 @@
+"""GPU parity at the workloads' full sizes, through the same entry points and
+with the same device allocations the bench times.  The oracle computes sampled
+rows one by one (plus every row where that is cheap); the bar is the same as
+in test_gpu_parity: |y - y_ref| <= 1e-5 * sum|W x| per row, stage by stage,
+each stage fed the GPU's own input.
+"""
+import numpy as np
+import pytest
+
+import gguf_synth as gs
+from test_gpu_parity import TOL, _torch, check_act, check_rows, dev, host, say, _align256
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(g, rows, n):
+    """n seeded rows, always including the first and the last (the ragged tile)."""
+    idx = set(g.choice(rows, size=min(n, rows), replace=False).tolist())
+    idx.update({0, rows - 1})
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+def gemv_gpu(t, Wt, xt, rows, cols, T):
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    y = torch.full((T, rows), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qg_gemv(t, Wt, xt, y, rows, cols, T)
+    return host(y)
+
+
+def test_q8_0_gemv_1024x2048_every_row(orc):
+    t, rows, cols = gs.Q8_0, 1024, 2048
+    c = gs.config0(seed=0)
+    say("full q8_0 gemv", rows, cols)
+    Wt, _ = dev(c["W"])
+    xt, _ = dev(c["x"])
+    y = gemv_gpu(t, Wt, xt, rows, cols, 1)
+    yr, A = orc.gemv(t, c["W"], c["x"], rows, cols, 1)
+    check_rows(y, yr, A, "q8_0 1024x2048")
+
+
+def test_dense_mlp_2560x9728_and_head_151936(orc):
+    """The dense Qwen3-style chain at Q8_0, one token: gate||up -> SwiGLU ->
+    down (qg_mlp), then the tied head on the GPU's down output (qg_gemv)."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    c = gs.config1(seed=0)
+    t, H, F, V = gs.Q8_0, c["H"], c["F"], c["head_rows"]
+    say("full dense mlp", H, F, "head", V)
+    tg, _ = dev(c["Wg"])
+    tu, _ = dev(c["Wu"])
+    td, _ = dev(c["Wd"])
+    xt, _ = dev(c["x"])
+    h = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+    qg.qg_mlp(t, qg.QG_ACT_SILU, tg, tu, td, H, F, xt, h, 1, ws)
+    wsh = host(ws)
+    gu = wsh[:2 * F].reshape(1, 2 * F)
+    a0 = _align256(2 * F * 4) // 4
+    act = wsh[a0:a0 + F].reshape(1, F)
+    g = gs.rng(11)
+    # gate and up rows, sampled
+    ri = sample_rows(g, F, 384)
+    yg, Ag = orc.gemv(t, c["Wg"], c["x"], F, H, 1, row_idx=ri)
+    yu, Au = orc.gemv(t, c["Wu"], c["x"], F, H, 1, row_idx=ri)
+    check_rows(gu[:, ri], yg, Ag, "gate rows")
+    check_rows(gu[:, F + ri], yu, Au, "up rows")
+    # activation, every element
+    check_act(orc, 0, gu, act, F, "silu(g)*u")
+    # down on the GPU's activation, every row
+    hh = host(h)
+    yd, Ad = orc.gemv(t, c["Wd"], act, H, F, 1)
+    check_rows(hh, yd, Ad, "down")
+    # head on the GPU's h, sampled rows
+    Wh = c["Wh"]
+    th, _ = dev(Wh)
+    ht, _ = dev(hh)
+    logits = gemv_gpu(t, th, ht, V, H, 1)
+    rh = sample_rows(g, V, 1024)
+    yh, Ah = orc.gemv(t, Wh, hh, V, H, 1, row_idx=rh)
+    check_rows(logits[:, rh], yh, Ah, "head")
+    assert np.isfinite(logits).all()
+
+
+@pytest.mark.parametrize("which", ["q4_k", "q6_k"])
+def test_kquant_gemv_full(orc, which):
+    c = gs.config3(seed=0)
+    if which == "q4_k":
+        t, W, x, rows, cols = gs.Q4_K, c["W4"], c["x4"], 17408, 5120
+    else:
+        t, W, x, rows, cols = gs.Q6_K, c["W6"], c["x6"], 5120, 17408
+    say("full", which, rows, cols)
+    Wt, _ = dev(W)
+    xt, _ = dev(x)
+    y = gemv_gpu(t, Wt, xt, rows, cols, 1)
+    ri = sample_rows(gs.rng(12), rows, 768)
+    yr, A = orc.gemv(t, W, x, rows, cols, 1, row_idx=ri)
+    check_rows(y[:, ri], yr, A, which)
+    assert np.isfinite(y).all()

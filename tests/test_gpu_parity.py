@@ -159,7 +159,7 @@ def test_router_parity(orc, E, k, T):
 # --------------------------------------------------------------- dense MLP --
 @pytest.mark.parametrize("t,act,H,F,T", [(gs.Q8_0, 0, 256, 320, 1), (gs.Q4_0, 1, 320, 224, 3),
                                          (gs.Q4_K, 0, 512, 768, 2), (gs.Q6_K, 1, 768, 512, 16),
-                                         (gs.Q4_0, 1, 2816, 2112, 16)])
+                                         (gs.Q4_0, 1, 2816, 2112, 16), (gs.Q4_0, 1, 2816, 2112, 1)])
 def test_mlp_stagewise(orc, t, act, H, F, T):
     import gguf_dequant_gemv_amd as qg
     torch = _torch()
@@ -242,6 +242,7 @@ MOE_CASES = [
     (gs.Q6_K, 1, 256, 512, 6, 6, 2, True),
     (gs.Q8_0, 0, 2048, 768, 128, 8, 1, False),      # Qwen3-30B-A3B layer shape
     (gs.Q4_0, 1, 2816, 704, 128, 8, 16, True),      # Gemma-4 26B-A4B expert shape, T = 16
+    (gs.Q4_0, 1, 2816, 704, 128, 8, 1, True),       # the same, one token
 ]
 
 
