@@ -92,8 +92,26 @@ int unit_count(const Shape &s, int kind) {
 //   pair_ok:    every weight range starts 4-byte aligned (pairs stay aligned)
 //   lds_ok:     every weight range starts 16-byte aligned; with rows a whole
 //               number of 16-byte pieces the weights can be staged in LDS
-Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok, bool lds_ok) {
+// T = 4..16 tokens of Q8_0 / Q4_0 go to the MFMA kernel (one 16-token chunk).
+constexpr int MFMA_MIN_TOK = 4;
+
+Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok, bool lds_ok,
+               int mfma_ntok = -1) {
     Plan p;
+    if (mfma_ntok < 0) mfma_ntok = ntok_max;
+    if ((s.type == QG_Q8_0 || s.type == QG_Q4_0) && mfma_ntok >= MFMA_MIN_TOK) {
+        p.kind = UK_MFMA;
+        p.lpr = 0;
+        p.nt = 16;
+        p.nunits = s.nb;
+        p.copies = copies > 0 ? copies : 1;
+        p.depth = 0;
+        p.ring_off = 0;
+        p.valu_heavy = false;
+        p.lds = 0;
+        p.ntiles = 0;     // set at launch (gated tiles hold half the rows)
+        return p;
+    }
     int nt = 1;
     while (nt < ntok_max && nt < 8) nt <<= 1;
     p.copies = copies > 0 ? copies : 1;
@@ -232,6 +250,24 @@ gemv_fn pick(int type, const Plan &p) {
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // a: weights, x/y, tokens or groups set by the caller; rows0 and rows set.
+int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
+    a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
+    a.cols = s.cols;
+    a.nunits = p.nunits;
+    // four groups of 16 rows per tile, or two when that leaves too few tiles
+    // to spread over the CUs
+    int groups = 4;
+    if ((a.rows + 16 * (a.glu ? 2 : 4) - 1) / (16 * (a.glu ? 2 : 4)) * p.copies < 2 * NUM_CU) groups = 2;
+    const int tile_rows = 16 * (a.glu ? groups / 2 : groups);
+    a.ntiles = (int)((a.rows + tile_rows - 1) / tile_rows);
+    gemv_fn f = gemv_kernel_mfma(s.type, groups);
+    int64_t cap = resident_wgs(f, 0) / p.copies;
+    if (cap < 1) cap = 1;
+    grid.x = (unsigned)(a.ntiles < cap ? a.ntiles : cap);
+    hipLaunchKernelGGL(f, grid, dim3(256), 0, st, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
 int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.row_bytes = s.row_bytes;
     if (a.glu) {           // gate rows in W0, the same rows of the up matrix in W1
@@ -242,6 +278,7 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
         a.bytes1 = (a.rows - a.rows0) * s.row_bytes;
     }
     if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
+    if (p.kind == UK_MFMA) return launch_mfma(s, p, a, grid, st);
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
     a.nunits = p.nunits;
@@ -468,8 +505,10 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     int gtok = (2 * ntok * topk + E - 1) / E;
     gtok = gtok < 1 ? 1 : (gtok > ntok ? ntok : gtok);
     const int busy = (pairs + gtok - 1) / gtok;   // about this many (group, chunk) sets carry work
+    // (a group takes the MFMA kernel only when groups typically hold 4+ tokens:
+    // smaller groups would leave most of its 16 token columns empty)
     Plan p1 = make_plan(s_g, gtok, 0, busy, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0,
-                        aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0);
+                        aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
     GemvArgs a = {};
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
     a.rows0 = a.rows = F;
@@ -488,7 +527,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
 
     // 3. down on each pair's activations
     Plan p2 = make_plan(s_dn, gtok, 0, busy, aligned(m->down, 4) && (m->down_stride % 4) == 0,
-                        aligned(m->down, 16) && (m->down_stride % 16) == 0);
+                        aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;
     b.rows0 = b.rows = s_dn.rows;

@@ -709,6 +709,256 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     QG_WAIT_VM(0);
 }
 
+// ------------------------------------------- small batch on the MFMA units ---
+// T tokens (up to 16) against Q8_0 / Q4_0 rows with v_mfma_f32_16x16x32_bf16:
+// per 32-value block, A (16 x 32) holds the tokens' x, B (32 x 16) sixteen
+// rows' codes, and D[token][row] is accumulated as d_row * D into f32.  The
+// products are exact: codes (int8, or nibble - 8) are small integers in bf16,
+// and x enters as three bf16 parts whose sum is x exactly (truncation splits
+// leave at most 16, then 8 significant bits), each part taking one MFMA.
+// Lane l holds token l%16 / row l%16 of its fragments for k = 8(l/16)..+7
+// (values 8q..8q+7 of the block: Q8_0 code bytes 2+8q.., Q4_0 low nibbles of
+// code bytes 8(q&1).. for q < 2, high nibbles for q >= 2), and D rows (tokens)
+// 4(l/16)..+3 of column (row) l%16.  A wave owns RG groups of 16 rows (gated:
+// RG/2 gate groups and the same up groups); a workgroup is 4 waves.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// x = h + m + l exactly, each part a bf16 (truncation splits)
+QG_DEV void split3(const f32x4 &x0, const f32x4 &x1, u32 (&h)[4], u32 (&m)[4], u32 (&l)[4]) {
+    float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    u32 hb[8], mb[8], lb[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        hb[j] = __builtin_bit_cast(u32, x[j]) & 0xFFFF0000u;
+        const float r = x[j] - __builtin_bit_cast(float, hb[j]);
+        mb[j] = __builtin_bit_cast(u32, r) & 0xFFFF0000u;
+        lb[j] = __builtin_bit_cast(u32, r - __builtin_bit_cast(float, mb[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {   // element 2j in the low half, 2j+1 in the high half
+        h[j] = __builtin_amdgcn_perm(hb[2 * j + 1], hb[2 * j], 0x07060302u);
+        m[j] = __builtin_amdgcn_perm(mb[2 * j + 1], mb[2 * j], 0x07060302u);
+        l[j] = __builtin_amdgcn_perm(lb[2 * j + 1], lb[2 * j], 0x07060302u);
+    }
+}
+
+QG_DEV bf16x8 as_bf16x8(const u32 (&v)[4]) {
+    u32x4 t = {v[0], v[1], v[2], v[3]};
+    return __builtin_bit_cast(bf16x8, t);
+}
+
+// 8 codes (as f32-exact integers) -> packed bf16 pairs
+template <int TY>
+QG_DEV void codes_bf16(u32 c0, u32 c1, int q, u32 (&o)[4]) {
+    float f[8];
+    if constexpr (TY == T_Q8_0) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            f[j] = (float)(int8_t)(c0 >> (8 * j));
+            f[4 + j] = (float)(int8_t)(c1 >> (8 * j));
+        }
+    } else {
+        const u32 m0 = opaque(q >= 2 ? (c0 >> 4) & 0x0F0F0F0Fu : c0 & 0x0F0F0F0Fu);
+        const u32 m1 = opaque(q >= 2 ? (c1 >> 4) & 0x0F0F0F0Fu : c1 & 0x0F0F0F0Fu);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            f[j] = u8_of(m0, j) - 8.0f;
+            f[4 + j] = u8_of(m1, j) - 8.0f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        o[j] = __builtin_amdgcn_perm(__builtin_bit_cast(u32, f[2 * j + 1]), __builtin_bit_cast(u32, f[2 * j]), 0x07060302u);
+}
+
+template <int TY, int RG>
+__global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
+    constexpr int BYTES = TY == T_Q8_0 ? 34 : 18;
+    constexpr int GR = RG;                 // row groups of 16 rows per tile
+    constexpr int PF = 2;                  // blocks in flight ahead of the one in use
+    __shared__ int s_in[16], s_out[16];
+    __shared__ float s_osc[16];
+    __shared__ float s_red[4][GR * 4][64];   // per-wave partial sums
+
+    // ---- which vectors this workgroup serves, and which weights ----
+    const uint8_t *Wg0 = a.W0, *Wg1 = a.W1;
+    int nt;
+    float es = 1.0f;
+    const int *rec = nullptr;
+    int c0 = 0;
+    if (a.grp) {
+        const int Gn = a.grp[0];
+        const int g = blockIdx.y;
+        if (g >= Gn) return;
+        rec = a.grp + 1 + g * GREC;
+        const int n = rec[2];
+        c0 = blockIdx.z * 16;
+        if (c0 >= n) return;
+        nt = min(16, n - c0);
+        Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
+        Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;
+        es = a.escale ? a.escale[rec[0]] : 1.0f;
+    } else {
+        c0 = blockIdx.y * 16;
+        nt = min(16, a.ntok - c0);
+    }
+    if (threadIdx.x < 16) {
+        const int t = threadIdx.x, i = c0 + min(t, nt - 1);
+        if (rec) {
+            s_in[t] = a.in_by_pair ? rec[19 + i] : rec[3 + i];
+            s_out[t] = rec[19 + i];
+            s_osc[t] = a.pscale ? a.pscale[rec[19 + i]] : 1.0f;
+        } else {
+            s_in[t] = s_out[t] = i;
+            s_osc[t] = 1.0f;
+        }
+    }
+    __syncthreads();
+
+    const u32 ph0 = (u32)((uintptr_t)Wg0 & 3u), ph1 = (u32)((uintptr_t)Wg1 & 3u);
+    const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
+    const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
+
+    // the four waves split each row's blocks (wave w takes blocks w, w+4, ...)
+    // and their partial sums are added in wave order at the tile's end
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n16 = lane & 15, q = lane >> 4;
+    const int nb = a.cols / 32;
+    const int64_t rows = a.rows;
+    const u32 rb = (u32)a.row_bytes;
+    const u32 cpos = 2u + 8u * (u32)(TY == T_Q8_0 ? q : (q & 1));
+    const float *xrow = a.x + (int64_t)s_in[n16] * a.x_stride + 8 * q;
+    const int tile_rows = a.glu ? 16 * (GR / 2) : 16 * GR;
+
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        u32 rbase[GR];
+        bool hi[GR];
+#pragma unroll
+        for (int gi = 0; gi < GR; gi++) {
+            // gated: groups [0, GR/2) gate rows, [GR/2, GR) the same up rows
+            hi[gi] = a.glu && gi >= GR / 2;
+            const int64_t r0 = tile * tile_rows + 16 * (a.glu ? gi % (GR / 2) : gi);
+            const int64_t r = min(r0 + n16, rows - 1);
+            rbase[gi] = (u32)r * rb + (hi[gi] ? ph1 : ph0);
+        }
+        float acc[GR][4];
+#pragma unroll
+        for (int gi = 0; gi < GR; gi++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[gi][i] = 0.0f;
+
+        // block b's raw data: a 12-byte window holding the lane's 8 code bytes,
+        // the dword holding its row's scale, and its token's 8 x values
+        u32 win[PF + 1][GR][3], sd[PF + 1][GR];
+        f32x4 xa[PF + 1], xb[PF + 1];
+        auto fetch = [&](int b, int k) {
+            b = min(b, nb - 1);   // past the row's end: re-load its last block
+#pragma unroll
+            for (int gi = 0; gi < GR; gi++) {
+                const u32 o = rbase[gi] + (u32)b * BYTES + cpos;
+                const rsrc_t rs = hi[gi] ? rs1 : rs0;
+                const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, o & ~3u, 0, 0);
+                win[k][gi][0] = v.x; win[k][gi][1] = v.y; win[k][gi][2] = v.z;
+                sd[k][gi] = __builtin_amdgcn_raw_buffer_load_b32(rs, (rbase[gi] + (u32)b * BYTES) & ~3u, 0, 0);
+            }
+            if (a.x_vec) {
+                xa[k] = *(const f32x4 *)(xrow + 32 * b);
+                xb[k] = *(const f32x4 *)(xrow + 32 * b + 4);
+            } else {
+                const float *p = xrow + 32 * b;
+                xa[k] = f32x4{p[0], p[1], p[2], p[3]};
+                xb[k] = f32x4{p[4], p[5], p[6], p[7]};
+            }
+        };
+        auto consume = [&](int b, int k) {
+            u32 ph[4], pm[4], pl[4];
+            split3(xa[k], xb[k], ph, pm, pl);
+            const bf16x8 xh = as_bf16x8(ph), xm = as_bf16x8(pm), xl = as_bf16x8(pl);
+#pragma unroll
+            for (int gi = 0; gi < GR; gi++) {
+                const u32 o = rbase[gi] + (u32)b * BYTES + cpos;
+                const u32 sh = o & 3u;
+                const u32 cw0 = __builtin_amdgcn_alignbyte(win[k][gi][1], win[k][gi][0], sh);
+                const u32 cw1 = __builtin_amdgcn_alignbyte(win[k][gi][2], win[k][gi][1], sh);
+                u32 cb[4];
+                codes_bf16<TY>(cw0, cw1, q, cb);
+                const u32 so = rbase[gi] + (u32)b * BYTES;
+                const float d = h2f(sd[k][gi] >> (8 * (so & 3u)));
+                const bf16x8 wv = as_bf16x8(cb);
+                f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, wv, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xm, wv, c, 0, 0, 0);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, wv, c, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[gi][i] = fmaf(d, c[i], acc[gi][i]);
+            }
+        };
+        // blocks wave, wave+4, ...: PF of them in flight ahead of the one in use
+        const int nmine = nb > wave ? (nb - wave + 3) / 4 : 0;
+#pragma unroll
+        for (int k = 0; k < PF; k++) fetch(wave + 4 * k, k);
+        int j = 0;
+        for (; j + PF + 1 <= nmine; j += PF + 1) {
+#pragma unroll
+            for (int k = 0; k <= PF; k++) {
+                fetch(wave + 4 * (j + k + PF), (k + PF) % (PF + 1));
+                consume(wave + 4 * (j + k), k);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k <= PF; k++) {
+            if (j + k < nmine) {
+                fetch(wave + 4 * (j + k + PF), (k + PF) % (PF + 1));
+                consume(wave + 4 * (j + k), k);
+            }
+        }
+        // the four waves' partial sums, added in wave order
+#pragma unroll
+        for (int gi = 0; gi < GR; gi++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) s_red[wave][gi * 4 + i][lane] = acc[gi][i];
+        __syncthreads();
+        // every wave finishes one quarter of the (group, token) outputs
+#pragma unroll
+        for (int gi = 0; gi < GR; gi++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int e = gi * 4 + i;
+                acc[gi][i] = ((s_red[0][e][lane] + s_red[1][e][lane]) + s_red[2][e][lane]) + s_red[3][e][lane];
+            }
+        __syncthreads();   // s_red is free for the next tile
+        // lane holds tokens 4q..4q+3 of row n16 of each group; wave w stores token 4q+w
+        {
+            const int i = wave;
+            const int t = 4 * q + i;
+            if (t < nt) {
+                const int64_t oi = s_out[t];
+                const float osc = s_osc[t];
+                if (a.glu) {
+#pragma unroll
+                    for (int gi = 0; gi < GR / 2; gi++) {
+                        const int64_t r = tile * tile_rows + 16 * gi + n16;
+                        if (r < rows) {
+                            const float gv = acc[gi][i], uv = acc[gi + GR / 2][i];
+                            a.y[oi * a.y_stride + r] = glu(a.glu, gv, uv);
+                            if (a.y2) {
+                                a.y2[oi * a.y2_stride + r] = gv;
+                                a.y2[oi * a.y2_stride + rows + r] = uv;
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int gi = 0; gi < GR; gi++) {
+                        const int64_t r = tile * tile_rows + 16 * gi + n16;
+                        if (r < rows) a.y[oi * a.y_stride + r] = (acc[gi][i] * es) * osc;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------- dequantization ---
 // One thread per block: out[r][c] = value of W[r][c] as f32, through the same
 // loads and decoders as the GEMV (block units: any 2-byte phase).
@@ -737,7 +987,8 @@ typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
 // Unit kinds: block units for every type; pair units for Q8_0 / Q4_0.
 // UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or the K-quant blocks,
 // 16-byte aligned ranges and rows; UK_LDS2: the same for 2-byte alignment.
-enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2, UK_LDS2 = 3 };
+// UK_MFMA: k_gemv_mfma (Q8_0 / Q4_0, 4..16 tokens).
+enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2, UK_LDS2 = 3, UK_MFMA = 4 };
 // One function per (block type, tokens per workgroup), each instantiated in
 // its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
 // (unit kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
@@ -752,6 +1003,8 @@ QG_DECL_GEMV(q4_k)
 QG_DECL_GEMV(q6_k)
 #undef QG_DECL_GEMV
 dequant_fn dequant_kernel(int type);
+// MFMA small-batch kernels (Q8_0 / Q4_0), qg_inst_mfma.hip
+gemv_fn gemv_kernel_mfma(int type, int groups);
 
 // Router / grouping and combine kernels (qg_route.hip).
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,
