@@ -151,7 +151,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
                 const double sb = (double)lpr * (s.ti.pairs ? 2 * s.ti.bytes : s.ti.bytes);
                 seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
             }
-            const double fw = heavy ? 0.1 : 0.45;
+            const double fw = heavy ? 0.1 : 0.35;
             const double score = util * seg * (1.0 - fw + fw * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
             if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
         }
@@ -170,11 +170,14 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
         // stage rings after x: two stages per wave when two workgroups still
         // fit a CU's 160 KiB, else one (a stage is refilled as soon as it has
         // been read, so even one keeps a stage per wave in flight)
+        // A launch whose workgroups take a tile or two each runs best with one
+        // stage per wave (smaller rings, more workgroups resident); long
+        // streams keep two in flight.
         p.ring_off = (int)((p.lds + 255) & ~(size_t)255);
         const size_t per_depth = 4 * (size_t)stage_bytes(s.ti, p.lpr, p.kind);
+        const int64_t tiles_all = (s.rows + 4LL * (64 / p.lpr) - 1) / (4LL * (64 / p.lpr)) * p.copies;
         p.depth = 1;
-        for (int d = 2; d >= 1; d--)
-            if (p.ring_off + d * per_depth <= 80 * 1024) { p.depth = d; break; }
+        if (tiles_all > 4 * NUM_CU && p.ring_off + 2 * per_depth <= 80 * 1024) p.depth = 2;
         p.lds = p.ring_off + p.depth * per_depth;
     }
     const int64_t tile_rows = 4LL * (64 / p.lpr);
