@@ -288,7 +288,10 @@ def time_workload(wl, steps, warmup):
     for i in range(warmup):
         wl.step(i)
     torch.cuda.synchronize()
-    per = max(1, min(wl.period, steps))
+    # several steps per graph, a whole number of weight-copy rotations, so the
+    # graph launch itself is amortised
+    per = wl.period * max(1, 16 // wl.period)
+    per = max(1, min(per, steps))
     full = _capture(wl.step, range(per))
     rem = steps % per
     tail = _capture(wl.step, range(rem)) if rem else None
@@ -300,9 +303,13 @@ def time_workload(wl, steps, warmup):
     torch.cuda.synchronize()
     if not torch.equal(ref, wl.output()):
         raise SystemExit("bench: graph replay differs from the eager run")
-    for _ in range(2):
+    # untimed replays until the clocks have settled (at least 0.3 s of work)
+    t_w = time.perf_counter()
+    nrep = 0
+    while nrep < 3 or time.perf_counter() - t_w < 0.3:
         full.replay()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        nrep += 1
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
@@ -316,10 +323,13 @@ def time_workload(wl, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     log("[bench] %d steps: %.4f ms/step by events, %.4f ms/step by the host clock" % (steps, ms, wall * 1e3 / steps))
     # dominant kernel alone, same rotation
-    dper = max(1, min(wl.dominant_period, 64))
+    dper = wl.dominant_period * max(1, 32 // wl.dominant_period)
+    dper = max(1, min(dper, 64))
     dg = _capture(wl.dominant_step, range(dper))
-    dg.replay()
-    torch.cuda.synchronize()
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.1:
+        dg.replay()
+        torch.cuda.synchronize()
     reps = max(1, (steps + dper - 1) // dper)
     e0.record()
     for _ in range(reps):
@@ -392,28 +402,35 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, wl_k
 
 
 def stats_summary(folder, command):
-    """Per-kernel table from rocprofv3's kernel_stats.csv: this library's
-    kernels one by one, everything else (input generation, copies) summed."""
+    """Per-kernel table from a rocprofv3 --kernel-trace run: this library's
+    kernels by name and grid (one template can serve several shapes), everything
+    else (input generation, copies) summed."""
     import csv
     rows = []
     for root, _, files in os.walk(folder):
         for f in files:
-            if f.endswith("kernel_stats.csv"):
+            if f.endswith("kernel_trace.csv"):
                 with open(os.path.join(root, f)) as fh:
                     rows += list(csv.DictReader(fh))
     if not rows:
-        raise SystemExit("no kernel_stats.csv under " + folder)
-    ours = [r for r in rows if "qg::" in r["Name"]]
-    rest = [r for r in rows if "qg::" not in r["Name"]]
+        raise SystemExit("no kernel_trace.csv under " + folder)
+    groups, other, n_other = {}, 0.0, 0
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if "qg::" not in r["Kernel_Name"]:
+            other += dur
+            n_other += 1
+            continue
+        name = r["Kernel_Name"].replace("void qg::", "").split("(qg::")[0].split("(float")[0]
+        key = (name, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]), int(r["Grid_Size_Y"]),
+               int(r["Grid_Size_Z"]))
+        groups.setdefault(key, []).append(dur)
     out = ["command: " + command, "source_sha256: " + source_hash(), "",
-           "%-48s %7s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
-    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
-        name = r["Name"].replace("void qg::", "").split("(qg::")[0].split("(float")[0]
-        out.append("%-48s %7s %12.3f %12.3f %12.3f" % (name[:48], r["Calls"], float(r["AverageNs"]) / 1e3,
-                                                       float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-    tot = sum(float(r["TotalDurationNs"]) for r in rest)
-    calls = sum(int(r["Calls"]) for r in rest)
-    out.append("%-48s %7d %12s (total %.1f us)" % ("(other kernels: inputs, copies)", calls, "", tot / 1e3))
+           "%-44s %-16s %6s %10s %10s %10s" % ("kernel", "grid (wg)", "calls", "avg_us", "min_us", "max_us")]
+    for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append("%-44s %-16s %6d %10.3f %10.3f %10.3f" % (key[0][:44], "%dx%dx%d" % key[1:], len(d),
+                                                            sum(d) / len(d), min(d), max(d)))
+    out.append("%-44s %-16s %6d %10s (total %.1f us)" % ("(other kernels: inputs, copies)", "", n_other, "", other))
     return "\n".join(out) + "\n"
 
 
