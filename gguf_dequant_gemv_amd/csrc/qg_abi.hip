@@ -130,7 +130,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
         if (staged >= 0 && kind != staged) continue;   // staging through LDS wins whenever it applies
         if (staged < 0 && lds_kind(kind)) continue;
         const int nunits = unit_count(s, kind);
-        const int cands[5] = {64, 32, 16, 8, 4};
+        const int cands[5] = {4, 8, 16, 32, 64};   // ties go to fewer lanes per row
         for (int ci = 0; ci < 5; ci++) {
             const int lpr = cands[ci], rpw = 64 / lpr;
             if (rows_align > 0 && rows_align % rpw) continue;

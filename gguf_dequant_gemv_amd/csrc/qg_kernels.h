@@ -126,6 +126,44 @@ QG_DEV void unit_dot(const u32 (&w)[U::ND], const float *xs, int xstride,
     for (int t = 0; t < NT; t++) acc[t] += us[t];
 }
 
+// One token, many scale groups (the K-quant blocks): the next group's x reads
+// are issued before this group's arithmetic, so LDS latency hides behind it.
+template <class U>
+QG_DEV void unit_dot_pf(const u32 (&w)[U::ND], const float *xs, const float *ss, float &acc) {
+    constexpr int Q = U::GSIZE / 4;          // float4 reads per group
+    float us = 0.0f;
+    f32x4 xn[Q];
+#pragma unroll
+    for (int k = 0; k < Q; k++) xn[k] = *(const f32x4 *)(xs + 4 * k);
+#pragma unroll
+    for (int g = 0; g < U::GROUPS; g++) {
+        f32x4 xc[Q];
+#pragma unroll
+        for (int k = 0; k < Q; k++) xc[k] = xn[k];
+        if (g + 1 < U::GROUPS) {
+#pragma unroll
+            for (int k = 0; k < Q; k++) {
+                const int i = (g + 1) * U::GSIZE + 4 * k;
+                xn[k] = *(const f32x4 *)(xs + i + ((i >> 6) << 2));
+            }
+        }
+        float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < Q; k++) {
+            const int i = g * U::GSIZE + 4 * k;
+            float &s = (k >= Q / 2) ? s1 : s0;
+            s = fmaf(U::dcode(w, i), xc[k].x, s);
+            s = fmaf(U::dcode(w, i + 1), xc[k].y, s);
+            s = fmaf(U::dcode(w, i + 2), xc[k].z, s);
+            s = fmaf(U::dcode(w, i + 3), xc[k].w, s);
+        }
+        us += U::fold(w, g, fmaf(s1, U::dfix(g, 1), s0 * U::dfix(g, 0)), U::SUMS ? ss[g] : 0.0f);
+        // this group's sums close before the group after next is read
+        asm volatile("" : "+v"(us)::"memory");
+    }
+    acc += us;
+}
+
 // The same sums for one token with the unit's x values already in registers
 // (xr[k] = x[4k .. 4k+3] of the unit), so all of a unit's LDS reads can be in
 // flight together before the arithmetic starts.
@@ -668,6 +706,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
 #pragma unroll
             for (int q = 0; q < UV / 4; q++) xr[q] = *(const f32x4 *)(xp + 4 * q);
             if (u < a.nunits) unit_dot_x<U>(wd, xr, ss + u * SPU, acc[0]);
+        } else if constexpr (NT == 1 && U::GROUPS > 2) {
+            if (u < a.nunits) unit_dot_pf<U>(wd, xs + xpad(u * UV), ss + u * SPU, acc[0]);
         } else {
             if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
         }
