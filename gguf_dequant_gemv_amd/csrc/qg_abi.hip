@@ -81,22 +81,21 @@ int stage_bytes(const TypeInfo &ti, int lpr, int kind) {
 }
 
 int unit_count(const Shape &s, int kind) {
-    if (kind == UK_PAIR || (lds_kind(kind) && s.ti.pairs)) return s.nb / 2;
+    if (lds_kind(kind) && s.ti.pairs) return s.nb / 2;
     return s.cols / s.ti.block_vals;
 }
 
-// Unit kind and lanes per row: best lane utilisation (units per row spread
-// evenly over the row's lanes), then enough waves to fill the GPU.
+// Kernel kind and lanes per row: best lane utilisation (units per row spread
+// evenly over the row's lanes), then segment length and wave fill.
 //   ntok_max:   most tokens one workgroup must serve
-//   rows_align: a row index (the W0/W1 split) no wave may straddle; 0 = none
-//   pair_ok:    every weight range starts 4-byte aligned (pairs stay aligned)
-//   lds_ok:     every weight range starts 16-byte aligned; with rows a whole
-//               number of 16-byte pieces the weights can be staged in LDS
+//   copies:     independent problems sharing the GPU in one launch
+//   lds_ok:     every weight range starts 16-byte aligned (with rows a whole
+//               number of 16-byte pieces, the aligned LDS variant applies)
+//   mfma_ntok:  tokens a workgroup's chunk may hold (MFMA from 4 on)
 // T = 4..16 tokens of Q8_0 / Q4_0 go to the MFMA kernel (one 16-token chunk).
 constexpr int MFMA_MIN_TOK = 4;
 
-Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies, bool pair_ok, bool lds_ok,
-               int mfma_ntok = -1) {
+Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mfma_ntok = -1) {
     Plan p;
     if (mfma_ntok < 0) mfma_ntok = ntok_max;
     if ((s.type == QG_Q8_0 || s.type == QG_Q4_0) && mfma_ntok >= MFMA_MIN_TOK) {
@@ -115,34 +114,26 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
     int nt = 1;
     while (nt < ntok_max && nt < 8) nt <<= 1;
     p.copies = copies > 0 ? copies : 1;
-    const bool pairs = s.ti.pairs && pair_ok && (s.nb % 2) == 0;
-    // staged through LDS: 16-byte aligned (UK_LDS) or any 2-byte phase
-    // (UK_LDS2); pair units need an even number of blocks per row
+    // staged through LDS (16-byte aligned, or any 2-byte phase) unless a
+    // Q8_0 / Q4_0 row has an odd block count (pair units need whole pairs)
     const bool units_ok = !s.ti.pairs || (s.nb % 2) == 0;
-    const int staged = !units_ok ? -1 : (lds_ok && (s.row_bytes % 16) == 0) ? UK_LDS : UK_LDS2;
-    double best = -1.0;
-    p.kind = UK_BLOCK;
+    p.kind = !units_ok ? UK_BLOCK : (lds_ok && (s.row_bytes % 16) == 0) ? UK_LDS : UK_LDS2;
     p.lpr = 64;
-    const int kinds[4] = {UK_BLOCK, UK_PAIR, UK_LDS, UK_LDS2};
-    for (int ki = 0; ki < 4; ki++) {
-        const int kind = kinds[ki];
-        if (kind == UK_PAIR && !pairs) continue;
-        if (staged >= 0 && kind != staged) continue;   // staging through LDS wins whenever it applies
-        if (staged < 0 && lds_kind(kind)) continue;
+    double best = -1.0;
+    {
+        const int kind = p.kind;
         const int nunits = unit_count(s, kind);
         const int cands[5] = {4, 8, 16, 32, 64};   // ties go to fewer lanes per row
         for (int ci = 0; ci < 5; ci++) {
             const int lpr = cands[ci], rpw = 64 / lpr;
-            if (rows_align > 0 && rows_align % rpw) continue;
             if (lds_kind(kind) && s.type == QG_Q6_K && lpr < 8) continue;   // 210-byte units: 16-byte segments need 8
             const int per_lane = (nunits + lpr - 1) / lpr;
             const double util = (double)nunits / ((double)lpr * per_lane);
             const double waves = (double)((s.rows + rpw - 1) / rpw) * (double)p.copies;
             const double fill = waves >= 8.0 * NUM_CU ? 1.0 : waves / (8.0 * NUM_CU);
-            // pairs: half the load instructions and no re-alignment.  Staged
-            // through LDS, each wave streams 64/lpr row segments of lpr units:
-            // segments of 1 KiB or more keep HBM reads in long runs (measured
-            // worth more than the idle lanes of a ragged last slot).
+            // Staged through LDS, each wave streams 64/lpr row segments of lpr
+            // units: segments of 1 KiB or more keep HBM reads in long runs
+            // (measured worth more than the idle lanes of a ragged last slot).
             // The K-quant decode is VALU-bound: there idle lanes cost most and
             // fewer lanes per row (more units each) measured fastest.
             const bool heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
@@ -152,12 +143,12 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t rows_align, int64_t copies,
                 seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
             }
             const double fw = heavy ? 0.1 : 0.35;
-            const double score = util * seg * (1.0 - fw + fw * fill) * (kind == UK_PAIR ? 1.03 : 1.0);
-            if (score > best + 1e-9) { best = score; p.kind = kind; p.lpr = lpr; }
+            const double score = util * seg * (1.0 - fw + fw * fill);
+            if (score > best + 1e-9) { best = score; p.lpr = lpr; }
         }
     }
     p.nunits = unit_count(s, p.kind);
-    const int uv = (p.kind == UK_PAIR || (lds_kind(p.kind) && s.ti.pairs)) ? 2 * s.ti.qk : s.ti.block_vals;
+    const int uv = (lds_kind(p.kind) && s.ti.pairs) ? 2 * s.ti.qk : s.ti.block_vals;
     const int cpad = p.nunits * uv;
     const size_t xcap = lds_kind(p.kind) ? 96 * 1024 : 64 * 1024;
     while (nt > 1 && lds_bytes(s.type, cpad, nt) > xcap) nt >>= 1;
@@ -252,7 +243,7 @@ gemv_fn pick(int type, const Plan &p) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// a: weights, x/y, tokens or groups set by the caller; rows0 and rows set.
+// a: weights, x/y, tokens or groups and rows set by the caller.
 int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
@@ -273,13 +264,9 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
 
 int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.row_bytes = s.row_bytes;
-    if (a.glu) {           // gate rows in W0, the same rows of the up matrix in W1
-        a.rows0 = a.rows;
-        a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
-    } else {
-        a.bytes0 = a.rows0 * s.row_bytes;
-        a.bytes1 = (a.rows - a.rows0) * s.row_bytes;
-    }
+    // gated: gate rows in W0, the same rows of the up matrix in W1
+    a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
+    if (!a.glu) a.W1 = a.W0;
     if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
     if (p.kind == UK_MFMA) return launch_mfma(s, p, a, grid, st);
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
@@ -335,10 +322,10 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
         Shape sc = s;
         sc.rows = rows - r0 < chunk ? rows - r0 : chunk;
         const uint8_t *Wc = (const uint8_t *)W + r0 * s.row_bytes;
-        Plan p = make_plan(sc, ntok, 0, 1, aligned(Wc, 4), aligned(Wc, 16));
+        Plan p = make_plan(sc, ntok, 1, aligned(Wc, 16));
         GemvArgs a = {};
         a.W0 = a.W1 = Wc;
-        a.rows0 = a.rows = sc.rows;
+        a.rows = sc.rows;
         a.x = x;
         a.x_stride = cols;
         a.y = y + r0;
@@ -398,11 +385,11 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     float *gu = (float *)workspace;
     float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
     // gate and up rows together: act(gate) * up per row, raw gate / up kept in gu
-    Plan p1 = make_plan(s_g, ntok, 0, 1, aligned(W_gate, 4) && aligned(W_up, 4), aligned(W_gate, 16) && aligned(W_up, 16));
+    Plan p1 = make_plan(s_g, ntok, 1, aligned(W_gate, 16) && aligned(W_up, 16));
     GemvArgs a = {};
     a.W0 = (const uint8_t *)W_gate;
     a.W1 = (const uint8_t *)W_up;
-    a.rows0 = a.rows = ff;
+    a.rows = ff;
     a.x = x;
     a.x_stride = hidden;
     a.y = av;
@@ -414,10 +401,10 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     rc = launch_gemv(s_g, p1, a, dim3(1, (ntok + p1.nt - 1) / p1.nt, 1), st);
     if (rc) return rc;
     // down on the activations
-    Plan p2 = make_plan(s_dn, ntok, 0, 1, aligned(W_down, 4), aligned(W_down, 16));
+    Plan p2 = make_plan(s_dn, ntok, 1, aligned(W_down, 16));
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)W_down;
-    b.rows0 = b.rows = hidden;
+    b.rows = hidden;
     b.x = av;
     b.x_stride = ff;
     b.y = y;
@@ -510,11 +497,10 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     const int busy = (pairs + gtok - 1) / gtok;   // about this many (group, chunk) sets carry work
     // (a group takes the MFMA kernel only when groups typically hold 4+ tokens:
     // smaller groups would leave most of its 16 token columns empty)
-    Plan p1 = make_plan(s_g, gtok, 0, busy, aligned(m->gate_up, 4) && (m->gate_up_stride % 4) == 0,
-                        aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
+    Plan p1 = make_plan(s_g, gtok, busy, aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
     GemvArgs a = {};
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
-    a.rows0 = a.rows = F;
+    a.rows = F;
     a.slot_stride = m->gate_up_stride;
     a.x = x;
     a.x_stride = H;
@@ -529,11 +515,10 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     if (rc) return rc;
 
     // 3. down on each pair's activations
-    Plan p2 = make_plan(s_dn, gtok, 0, busy, aligned(m->down, 4) && (m->down_stride % 4) == 0,
-                        aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
+    Plan p2 = make_plan(s_dn, gtok, busy, aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;
-    b.rows0 = b.rows = s_dn.rows;
+    b.rows = s_dn.rows;
     b.slot_stride = m->down_stride;
     b.x = av;
     b.x_stride = F;

@@ -44,14 +44,14 @@ template <> struct Units<T_Q4_0> { typedef UQ4_0B B; typedef UQ4_0P P; };
 template <> struct Units<T_Q4_K> { typedef UQ4_K B; typedef UQ4_K P; };
 template <> struct Units<T_Q6_K> { typedef UQ6_K B; typedef UQ6_K P; };
 
+// UK_BLOCK exists for Q8_0 / Q4_0 only (the K-quants always stage in LDS)
 template <int TY, int NT>
 gemv_fn pick(int kind, int lpr) {
-    if (kind == UK_LDS) return pick_lpr_lds<typename Units<TY>::P, NT, true>(lpr);
-    if (kind == UK_LDS2) return pick_lpr_lds<typename Units<TY>::P, NT, false>(lpr);
     if constexpr (TY == T_Q8_0 || TY == T_Q4_0) {
-        if (kind == UK_PAIR) return pick_lpr<typename Units<TY>::P, NT>(lpr);
+        if (kind == UK_BLOCK) return pick_lpr<typename Units<TY>::B, NT>(lpr);
     }
-    return pick_lpr<typename Units<TY>::B, NT>(lpr);
+    if (kind == UK_LDS) return pick_lpr_lds<typename Units<TY>::P, NT, true>(lpr);
+    return pick_lpr_lds<typename Units<TY>::P, NT, false>(lpr);
 }
 
 }  // namespace inst

@@ -44,12 +44,11 @@ constexpr int GREC = 35;
 constexpr int MAXT = 16;
 
 struct GemvArgs {
-    // weights: dense rows [0, rows0) come from W0, rows [rows0, rows) from W1;
-    // grouped: W0 + slot * slot_stride for the group's slot.  Gated pairs:
-    // gate rows [0, rows) from W0, up rows [0, rows) from W1 (grouped: the up
-    // rows follow the gate rows in the slot).
+    // weights: rows [0, rows) of W0 (grouped: W0 + slot * slot_stride for the
+    // group's slot).  Gated pairs: gate rows from W0, the same up rows from W1
+    // (grouped: the up rows follow the gate rows in the slot).
     const uint8_t *W0, *W1;
-    int64_t rows0, rows, row_bytes, slot_stride;
+    int64_t rows, row_bytes, slot_stride;
     int64_t bytes0, bytes1;   // bytes of the W0 / W1 ranges
     int cols, nunits;         // values per row; units per row
     // inputs: vector i of the chunk is x + idx_i * x_stride
@@ -315,27 +314,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     const int KT = a.glu ? 2 * K : K;         // slots per row tile
     const int P = ((int)a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int S = P * KT;
-    const int64_t rows = a.rows, rows0 = a.rows0;
+    const int64_t rows = a.rows;
     const int64_t rb = a.row_bytes;
 
     // element (p, j) -> descriptor + byte offset of the unit to load
-    auto locate = [&](int p, int j, u32 &off) -> bool {  // returns: from range 1
+    auto locate = [&](int p, int j, u32 &off) -> bool {  // returns: from W1
         const int64_t tile = (int64_t)blockIdx.x + (int64_t)p * gridDim.x;
         const int64_t r0 = (tile * 4 + wave) * RPW;
         const int64_t r = min(r0 + grp, rows - 1);
-        bool hi;
-        int64_t rl;
-        int jj = j;
-        if (a.glu) {             // slots [0, K): gate row r; [K, 2K): up row r
-            hi = j >= K;
-            jj = hi ? j - K : j;
-            rl = r;
-        } else {                 // waves never straddle rows0
-            hi = rows0 < rows && r0 >= rows0;
-            rl = hi ? r - rows0 : r;
-        }
+        // gated: slots [0, K) are gate row r, [K, 2K) up row r (uniform)
+        const bool hi = __builtin_amdgcn_readfirstlane((int)(a.glu && j >= K)) != 0;
+        const int jj = hi ? j - K : j;
         const int u = min(sub + jj * L, a.nunits - 1);
-        off = (hi ? ph1 : ph0) + (u32)(rl * rb) + (u32)u * U::BYTES;
+        off = (hi ? ph1 : ph0) + (u32)(r * rb) + (u32)u * U::BYTES;
         return hi;
     };
 
@@ -590,7 +581,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     const int P = ((int)a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int S = P * KT;
     const int D = a.depth;
-    const int64_t rows = a.rows, rows0 = a.rows0;
+    const int64_t rows = a.rows;
     const u32 rb = (u32)a.row_bytes;
     uint8_t *ring = (uint8_t *)lds + a.ring_off + wave * D * G::STAGE;
 
@@ -607,23 +598,17 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     auto issue = [&](int p, int j, int slot) {
         const int64_t tile = (int64_t)blockIdx.x + (int64_t)p * gridDim.x;
         const int64_t r0 = (tile * 4 + wave) * RPW;
-        bool hi;
-        int jj = j;
-        int64_t shift = 0;
-        if (a.glu) {
-            hi = j >= K;
-            jj = hi ? j - K : j;
-        } else {                 // waves never straddle rows0
-            hi = rows0 < rows && r0 >= rows0;
-            shift = hi ? rows0 : 0;
-        }
+        // gated: [K, 2K) are the up rows (uniform; saying so keeps the
+        // descriptor choice in scalar registers)
+        const bool hi = __builtin_amdgcn_readfirstlane((int)(a.glu && j >= K)) != 0;
+        const int jj = hi ? j - K : j;
         const rsrc_t rs = hi ? rs1 : rs0;
         const u32 seg = (u32)jj * (u32)(L * U::BYTES) + (hi ? ph1 : ph0);
         __attribute__((address_space(3))) void *dst =
             (__attribute__((address_space(3))) void *)(ring + slot * G::STAGE);
 #pragma unroll
         for (int c = 0; c < G::NI; c++) {
-            const int64_t r = min(r0 + prow[c], rows - 1) - shift;
+            const int64_t r = min(r0 + prow[c], rows - 1);
             const u32 off = (((u32)r * rb + seg) & ~15u) + poff[c];
             if (c < G::NI - 1 || lane < G::LAST)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)
@@ -682,9 +667,9 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         if constexpr (!ALN) {
             const int64_t tl = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
             const int64_t rw0 = (tl * 4 + wave) * RPW;
-            const bool hi = a.glu ? cj >= K : (rows0 < rows && rw0 >= rows0);
-            const int64_t rr = min(rw0 + grp, rows - 1) - (!a.glu && hi ? rows0 : 0);
-            const u32 jj = (u32)(a.glu && hi ? cj - K : cj);
+            const bool hi = a.glu && cj >= K;
+            const int64_t rr = min(rw0 + grp, rows - 1);
+            const u32 jj = (u32)(hi ? cj - K : cj);
             const u32 phase = ((u32)rr * rb + jj * (u32)(L * U::BYTES) + (hi ? ph1 : ph0)) & 15u;
             uoff = (u32)grp * (SEGP * 16) + phase + (u32)sub * U::BYTES;
         }
@@ -1024,14 +1009,15 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *W, float *out, i
 // ------------------------------------------------------ instance tables ---
 typedef void (*gemv_fn)(GemvArgs);
 typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
-// Unit kinds: block units for every type; pair units for Q8_0 / Q4_0.
-// UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or the K-quant blocks,
-// 16-byte aligned ranges and rows; UK_LDS2: the same for 2-byte alignment.
+// Kernel kinds.  UK_BLOCK: k_gemv over single Q8_0 / Q4_0 blocks (rows with
+// an odd block count).  UK_LDS: k_gemv_lds over pair units (Q8_0 / Q4_0) or
+// the K-quant blocks, 16-byte aligned ranges and rows; UK_LDS2: the same for
+// any 2-byte phase.
 // UK_MFMA: k_gemv_mfma (Q8_0 / Q4_0, 4..16 tokens).
-enum { UK_BLOCK = 0, UK_PAIR = 1, UK_LDS = 2, UK_LDS2 = 3, UK_MFMA = 4 };
+enum { UK_BLOCK = 0, UK_LDS = 1, UK_LDS2 = 2, UK_MFMA = 3 };
 // One function per (block type, tokens per workgroup), each instantiated in
 // its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
-// (unit kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
+// (kernel kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
 #define QG_DECL_GEMV(NAME) \
     gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr); \
     gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr); \
