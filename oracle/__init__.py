@@ -12,7 +12,7 @@ import numpy as np
 
 from . import build as _build
 
-Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
+F32, Q4_0, Q8_0, Q4_K, Q6_K = 0, 2, 8, 12, 14
 ACT_SILU, ACT_GELU_TANH = 0, 1
 
 _lib = None
@@ -48,6 +48,15 @@ def lib():
         L.or_moe_ffn.argtypes = [i32, i32, i64, i64, i32, P, i64, P, i64, P, P, i32, P, P, i32,
                                  P, P, P, P, P]
         L.or_moe_down.argtypes = [i32, i32, i64, i64, P, i64, P, P, P, P, i32, P, i32, P, P, P]
+        d = ctypes.c_double
+        L.or_rmsnorm.argtypes = [P, P, i64, i32, d, d, P]
+        L.or_sigmoid.restype = d
+        L.or_sigmoid.argtypes = [d]
+        L.or_moe_shared_combine.argtypes = [P, i32, P, P, P, P, i64, i32, P, P, P]
+        L.or_post_ffn.argtypes = [P, P, P, P, P, d, P, i64, i32, d, P, P]
+        L.or_embed.argtypes = [i32, P, i64, i64, P, i32, ctypes.c_float, P]
+        L.or_softcap.argtypes = [P, i64, ctypes.c_float, P]
+        L.or_argmax.argtypes = [P, i64, i32, P]
         _lib = L
     return _lib
 
@@ -179,3 +188,79 @@ def moe_down(t, act, H, F, down, d_stride, down_scale, slots, ids, c, gu_f32, nt
     if rc:
         raise ValueError("or_moe_down: bad arguments")
     return y, A, R
+
+
+# ------------------------------------------------------ around the MoE step
+
+
+def rmsnorm(x, w, n, ntok, eps, k=1.0):
+    """((x * r) * k) * w per token, r = 1/sqrt(mean x^2 + eps); f64 [ntok][n]."""
+    xf = _c(x, np.float32)
+    wf = _c(w, np.float32)
+    assert xf.size == n * ntok and wf.size == n
+    y = np.empty((ntok, n), np.float64)
+    if lib().or_rmsnorm(_p(xf), _p(wf), n, ntok, float(eps), float(k), _p(y)):
+        raise ValueError("or_rmsnorm: bad arguments")
+    return y
+
+
+def sigmoid(g):
+    return lib().or_sigmoid(float(g))
+
+
+def moe_shared_combine(terms, sh, gate_inp, x, resid, H, ntok):
+    """(y, A, sg): y = (sum_j terms_j + sh * sigmoid(gate_inp . x)) + resid, f64 [ntok][H]."""
+    tf = _c(terms, np.float32)
+    k = tf.size // (ntok * H)
+    assert tf.size == ntok * k * H
+    shf = _c(sh, np.float32)
+    gf = _c(gate_inp, np.float32)
+    xf = _c(x, np.float32)
+    rf = _c(resid, np.float32)
+    y = np.empty((ntok, H), np.float64)
+    A = np.empty((ntok, H), np.float64)
+    sg = np.empty(ntok, np.float64)
+    if lib().or_moe_shared_combine(_p(tf), k, _p(shf), _p(gf), _p(xf), _p(rf), H, ntok, _p(y), _p(A), _p(sg)):
+        raise ValueError("or_moe_shared_combine: bad arguments")
+    return y, A, sg
+
+
+def post_ffn(mlp, moe, w1, w2, w, os_, x, n, ntok, eps):
+    """Gemma's FFN tail: (y, A), f64 [ntok][n]."""
+    a = [_c(v, np.float32) for v in (mlp, moe, w1, w2, w, x)]
+    y = np.empty((ntok, n), np.float64)
+    A = np.empty((ntok, n), np.float64)
+    if lib().or_post_ffn(_p(a[0]), _p(a[1]), _p(a[2]), _p(a[3]), _p(a[4]), float(os_), _p(a[5]), n, ntok,
+                         float(eps), _p(y), _p(A)):
+        raise ValueError("or_post_ffn: bad arguments")
+    return y, A
+
+
+# ---------------------------------------------------- embedding and head
+
+
+def embed(t, W, rows, cols, tokens, scale=1.0):
+    """f32 [ntok][cols]: each row's values rounded to f32, times scale in f32."""
+    Wb = _c(W, np.uint8)
+    tk = _c(tokens, np.int32).ravel()
+    out = np.empty((tk.size, cols), np.float32)
+    if lib().or_embed(t, _p(Wb), rows, cols, _p(tk), tk.size, float(scale), _p(out)):
+        raise ValueError("or_embed: bad arguments")
+    return out
+
+
+def softcap(l, cap):
+    lf = _c(l, np.float32)
+    out = np.empty(lf.shape, np.float64)
+    if lib().or_softcap(_p(lf), lf.size, float(cap), _p(out)):
+        raise ValueError("or_softcap: bad arguments")
+    return out
+
+
+def argmax(l, n, ntok):
+    lf = _c(l, np.float32)
+    assert lf.size == n * ntok
+    idx = np.empty(ntok, np.int32)
+    if lib().or_argmax(_p(lf), n, ntok, _p(idx)):
+        raise ValueError("or_argmax: bad arguments")
+    return idx

@@ -32,7 +32,10 @@
 #include <string.h>
 
 /* GGML type ids (the GGUF on-disk enum; [bonsai] header section prints
- * Q4_K = 12 and Q6_K = 14; Q4_0 = 2 and Q8_0 = 8 complete the same enum). */
+ * Q4_K = 12 and Q6_K = 14; Q4_0 = 2 and Q8_0 = 8 complete the same enum, where
+ * plain f32 is 0: the router and shared-gate weights stay f32 on the pages,
+ * [qwen3] WGSL matmulF32). */
+#define OR_F32 0
 #define OR_Q4_0 2
 #define OR_Q8_0 8
 #define OR_Q4_K 12
@@ -66,6 +69,7 @@ static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); 
 int or_block_values(int type)  /* values per block */
 {
     switch (type) {
+    case OR_F32: return 1;
     case OR_Q8_0: case OR_Q4_0: return 32;
     case OR_Q4_K: case OR_Q6_K: return 256;
     default: return 0;
@@ -75,6 +79,7 @@ int or_block_values(int type)  /* values per block */
 int or_block_bytes(int type)
 {
     switch (type) {
+    case OR_F32: return 4;                         /* one IEEE binary32, little-endian */
     case OR_Q8_0: return 2 + 32;                   /* f16 d, int8 q[32] */
     case OR_Q4_0: return 2 + 16;                   /* f16 d, 16 bytes of nibbles */
     case OR_Q4_K: return 2 + 2 + 12 + 128;         /* d, dmin, scales[12], qs[128] */
@@ -169,9 +174,18 @@ static void deq_q6_k(const uint8_t *b, double *out)
     }
 }
 
+/* F32: the 4 bytes are the value's IEEE binary32 pattern, low byte first. */
+static void deq_f32(const uint8_t *b, double *out)
+{
+    float f;
+    memcpy(&f, b, 4);
+    out[0] = (double)f;
+}
+
 static int deq_block(int type, const uint8_t *b, double *out)
 {
     switch (type) {
+    case OR_F32: deq_f32(b, out); return 0;
     case OR_Q8_0: deq_q8_0(b, out); return 0;
     case OR_Q4_0: deq_q4_0(b, out); return 0;
     case OR_Q4_K: deq_q4_k(b, out); return 0;
@@ -452,5 +466,165 @@ int or_moe_down(int type, int act, int64_t H, int64_t F,
         }
     }
     free(a); free(ga); free(dn); free(dA); free(dR); free(wrow);
+    return 0;
+}
+
+/* ------------------------------------------------ around the MoE step ---- */
+/* RMS norm with a scalar factor, per token of n values:
+ *   r = 1 / sqrt(sum_i x_i^2 / n + eps),   y_i = ((x_i * r) * k) * w_i.
+ * [qwen3] WGSL rmsnorm (k = 1) and [gemma4] rmsnormK (k = 1/sqrt(H) and the
+ * router's scale vector as w: the router's input).  In f64 from f32 inputs. */
+int or_rmsnorm(const float *x, const float *w, int64_t n, int ntok, double eps, double k, double *y)
+{
+    if (n <= 0 || ntok <= 0) return -1;
+    for (int t = 0; t < ntok; t++) {
+        const float *xt = x + (int64_t)t * n;
+        double ss = 0.0;
+        for (int64_t i = 0; i < n; i++) ss += (double)xt[i] * (double)xt[i];
+        double r = 1.0 / sqrt(ss / (double)n + eps);
+        for (int64_t i = 0; i < n; i++) y[(int64_t)t * n + i] = (((double)xt[i] * r) * k) * (double)w[i];
+    }
+    return 0;
+}
+
+/* The logistic function 1 / (1 + e^-g).  [qwen35] SIGMOID helper, used on the
+ * shared expert's scalar gate logit. */
+double or_sigmoid(double g) { return 1.0 / (1.0 + exp(-g)); }
+
+/* The last step of a MoE block with a shared expert, per token:
+ *   sg    = sum_c gate_inp[c] * x[c]                 (the scalar gate logit)
+ *   y[h]  = (sum_j terms_j[h] + sh[h] * sigmoid(sg)) + resid[h]
+ * where terms_j = (dn_j * s_j) * c_j are the routed picks' weighted down
+ * outputs, added in pick order, and resid is the residual stream.
+ * [qwen35] WGSL moeAccumShared / moeAccumSharedB (routed experts, then the
+ * gated shared expert, then the residual) and the engine's shgate binding (an
+ * f32 GEMV of one row on the normed input).
+ * Inputs f32: terms [ntok][k][H], sh [ntok][H], gate_inp [H], x [ntok][H],
+ * resid [ntok][H].  Outputs f64 [ntok][H]: y, and the error scale
+ *   A[h] = sum_j |terms_j[h]| + |sh[h]| sigmoid(sg) + |resid[h]|
+ *          + |sh[h]| / 4 * sum_c |gate_inp[c] x[c]|
+ * (the last term: the logistic slope is at most 1/4, times the scale of the
+ * gate logit's own rounding).  sg_out [ntok] may be NULL. */
+int or_moe_shared_combine(const float *terms, int k, const float *sh, const float *gate_inp,
+                          const float *x, const float *resid, int64_t H, int ntok,
+                          double *y, double *A, double *sg_out)
+{
+    if (H <= 0 || ntok <= 0 || k <= 0) return -1;
+    for (int t = 0; t < ntok; t++) {
+        const float *xt = x + (int64_t)t * H;
+        double sg = 0.0, sa = 0.0;
+        for (int64_t c = 0; c < H; c++) {
+            double p = (double)gate_inp[c] * (double)xt[c];
+            sg += p;
+            sa += fabs(p);
+        }
+        if (sg_out) sg_out[t] = sg;
+        double gs = or_sigmoid(sg);
+        for (int64_t h = 0; h < H; h++) {
+            double acc = 0.0, aa = 0.0;
+            for (int j = 0; j < k; j++) {
+                double v = (double)terms[((int64_t)t * k + j) * H + h];
+                acc += v;
+                aa += fabs(v);
+            }
+            double s = (double)sh[(int64_t)t * H + h], r = (double)resid[(int64_t)t * H + h];
+            y[(int64_t)t * H + h] = (acc + s * gs) + r;
+            A[(int64_t)t * H + h] = aa + fabs(s) * gs + fabs(r) + fabs(s) * 0.25 * sa;
+        }
+    }
+    return 0;
+}
+
+/* Gemma's FFN tail, per token of n values:
+ *   m  = rmsnorm(mlp, w1)   (the dense MLP's output, post_ffw_norm_1)
+ *   e  = rmsnorm(moe, w2)   (the MoE sum, post_ffw_norm_2)
+ *   v  = m + e
+ *   x  = ((v * r_v) * w + x) * os          r_v = 1 / sqrt(sum v^2 / n + eps)
+ * [gemma4] engine encodeExperts (mpost, mpost2) and WGSL postFfn (the last
+ * norm, the residual add and the layer's output scalar os).  x is updated in
+ * place (f32 in, f64 out as y).  A[i] = |os| ((|m_i| + |e_i|) r_v |w_i| + |x_i|)
+ * is the scale of the rounding error of an f32 evaluation. */
+int or_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2,
+                const float *w, double os, const float *x, int64_t n, int ntok, double eps,
+                double *y, double *A)
+{
+    if (n <= 0 || ntok <= 0) return -1;
+    double *m = (double *)malloc(sizeof(double) * (size_t)n);
+    double *e = (double *)malloc(sizeof(double) * (size_t)n);
+    if (!m || !e) { free(m); free(e); return -1; }
+    for (int t = 0; t < ntok; t++) {
+        int64_t o = (int64_t)t * n;
+        or_rmsnorm(mlp + o, w1, n, 1, eps, 1.0, m);
+        or_rmsnorm(moe + o, w2, n, 1, eps, 1.0, e);
+        double ss = 0.0;
+        for (int64_t i = 0; i < n; i++) ss += (m[i] + e[i]) * (m[i] + e[i]);
+        double r = 1.0 / sqrt(ss / (double)n + eps);
+        for (int64_t i = 0; i < n; i++) {
+            y[o + i] = (((m[i] + e[i]) * r) * (double)w[i] + (double)x[o + i]) * os;
+            A[o + i] = fabs(os) * ((fabs(m[i]) + fabs(e[i])) * r * fabs((double)w[i]) + fabs((double)x[o + i]));
+        }
+    }
+    free(m); free(e);
+    return 0;
+}
+
+/* --------------------------------------------------- embedding and head ---- */
+/* Embedding rows of a quantized table, scaled:
+ *   out[t][c] = f32(f32(W[tok_t][c]) * scale)
+ * each value first rounded to the f32 nearest its exact value (exact for
+ * Q8_0, Q4_0, Q6_K and F32), then multiplied by scale in f32.
+ * [qwen3] WGSL embedQ8 (scale 1) and [gemma4] embedQ6K (its scale uniform).
+ * Returns -1 for a token outside [0, rows). */
+int or_embed(int type, const uint8_t *W, int64_t rows, int64_t cols, const int32_t *tok, int ntok,
+             float scale, float *out)
+{
+    int qk = or_block_values(type), bb = or_block_bytes(type);
+    if (!qk || cols <= 0 || cols % qk || ntok <= 0) return -1;
+    int64_t row_bytes = (cols / qk) * bb;
+    double *w = (double *)malloc(sizeof(double) * (size_t)cols);
+    if (!w) return -1;
+    for (int t = 0; t < ntok; t++) {
+        if (tok[t] < 0 || tok[t] >= rows) { free(w); return -1; }
+        or_dequant(type, W + (int64_t)tok[t] * row_bytes, cols, w);
+        for (int64_t c = 0; c < cols; c++) {
+            float v = (float)w[c];
+            out[(int64_t)t * cols + c] = (float)((double)v * (double)scale);
+        }
+    }
+    free(w);
+    return 0;
+}
+
+/* Final logit soft cap: l = tanh(clamp(l * inv, -10, 10)) * cap, inv the f32
+ * nearest 1/cap.  [gemma4] WGSL softcap with the tanhc clamp.  f64 out. */
+int or_softcap(const float *l, int64_t n, float cap, double *out)
+{
+    if (n < 0 || !(cap > 0.0f)) return -1;
+    float inv = (float)(1.0 / (double)cap);
+    for (int64_t i = 0; i < n; i++) {
+        double a = (double)l[i] * (double)inv;
+        if (a < -10.0) a = -10.0;
+        if (a > 10.0) a = 10.0;
+        out[i] = tanh(a) * (double)cap;
+    }
+    return 0;
+}
+
+/* Greedy pick per token: the index of the largest value, ties to the lowest
+ * index; NaN entries never win; a row with no number gives 0.
+ * [qwen3] WGSL argmax (strict greater-than while scanning, the lower index on
+ * equal values while reducing). */
+int or_argmax(const float *l, int64_t n, int ntok, int32_t *idx)
+{
+    if (n <= 0 || ntok <= 0) return -1;
+    for (int t = 0; t < ntok; t++) {
+        const float *lt = l + (int64_t)t * n;
+        int64_t best = -1;
+        for (int64_t i = 0; i < n; i++) {
+            if (lt[i] != lt[i]) continue;   /* NaN */
+            if (best < 0 || lt[i] > lt[best]) best = i;
+        }
+        idx[t] = (int32_t)(best < 0 ? 0 : best);
+    }
     return 0;
 }
