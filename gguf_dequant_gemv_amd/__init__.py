@@ -9,7 +9,7 @@ library is missing or a call fails.
 import ctypes
 import os
 
-QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 2, 8, 12, 14
+QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
 QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK = 16, 256, 32
@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 # Every symbol include/qgemv.h declares.
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
-           "qg_moe_ffn")
+           "qg_moe_ffn", "qg_rmsnorm", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
+           "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
 
 _lib = None
 
@@ -37,6 +38,11 @@ class qg_moe(ctypes.Structure):
                 ("gate_up", ctypes.c_void_p), ("gate_up_stride", ctypes.c_int64),
                 ("down", ctypes.c_void_p), ("down_stride", ctypes.c_int64),
                 ("down_scale", ctypes.c_void_p), ("n_slots", ctypes.c_int)]
+
+
+class qg_shared_expert(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int), ("ff", ctypes.c_int64), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("gate_inp", ctypes.c_void_p)]
 
 
 def lib():
@@ -60,6 +66,18 @@ def lib():
         L.qg_moe_workspace_size.argtypes = [ctypes.POINTER(qg_moe), i32, i32]
         L.qg_moe_workspace_size.restype = sz
         L.qg_moe_ffn.argtypes = [ctypes.POINTER(qg_moe), P, i32, P, P, P, i32, P, P, P, P, sz, P]
+        f = ctypes.c_float
+        L.qg_rmsnorm.argtypes = [P, P, P, i64, i32, f, f, P]
+        L.qg_moe_shared_workspace_size.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_shared_expert), i32,
+                                                   i32]
+        L.qg_moe_shared_workspace_size.restype = sz
+        L.qg_moe_ffn_shared.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_shared_expert), P, i32, P, P,
+                                        P, i32, P, P, P, P, sz, P]
+        L.qg_post_ffn.argtypes = [P, P, P, P, P, P, P, i64, i32, f, P]
+        L.qg_embed.argtypes = [i32, P, i64, i64, P, i32, f, P, P]
+        L.qg_argmax_workspace_size.argtypes = [i64, i32]
+        L.qg_argmax_workspace_size.restype = sz
+        L.qg_argmax.argtypes = [P, i64, i32, f, P, P, sz, P]
         _lib = L
     return _lib
 
@@ -140,3 +158,46 @@ def qg_moe_ffn(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out,
     _check("qg_moe_ffn", lib().qg_moe_ffn(ctypes.byref(m), _ptr(router_logits), topk, _ptr(expert_slots),
                                           _ptr(x), _ptr(y), ntok, _ptr(ids_out), _ptr(w_out), _ptr(status),
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def _nbytes(t, given):
+    return given if given is not None else t.numel() * t.element_size()
+
+
+def qg_rmsnorm(x, w, y, n, ntok, eps, k=1.0, stream=None):
+    _check("qg_rmsnorm", lib().qg_rmsnorm(_ptr(x), _ptr(w), _ptr(y), n, ntok, eps, k, _stream(stream)))
+
+
+def make_shared_expert(type, ff, gate, up, down, gate_inp):
+    return qg_shared_expert(type, ff, _ptr(gate), _ptr(up), _ptr(down), _ptr(gate_inp))
+
+
+def qg_moe_shared_workspace_size(m, sh, topk, ntok):
+    return lib().qg_moe_shared_workspace_size(ctypes.byref(m), ctypes.byref(sh), topk, ntok)
+
+
+def qg_moe_ffn_shared(m, sh, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status,
+                      workspace, workspace_bytes=None, stream=None):
+    _check("qg_moe_ffn_shared",
+           lib().qg_moe_ffn_shared(ctypes.byref(m), ctypes.byref(sh), _ptr(router_logits), topk, _ptr(expert_slots),
+                                   _ptr(x), _ptr(resid), ntok, _ptr(ids_out), _ptr(w_out), _ptr(status),
+                                   _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def qg_post_ffn(mlp, moe, w1, w2, w, out_scale, x, n, ntok, eps, stream=None):
+    _check("qg_post_ffn", lib().qg_post_ffn(_ptr(mlp), _ptr(moe), _ptr(w1), _ptr(w2), _ptr(w), _ptr(out_scale),
+                                            _ptr(x), n, ntok, eps, _stream(stream)))
+
+
+def qg_embed(type, W, rows, cols, tokens, ntok, scale, out, stream=None):
+    _check("qg_embed", lib().qg_embed(type, _ptr(W), rows, cols, _ptr(tokens), ntok, scale, _ptr(out),
+                                      _stream(stream)))
+
+
+def qg_argmax_workspace_size(n, ntok):
+    return lib().qg_argmax_workspace_size(n, ntok)
+
+
+def qg_argmax(logits, n, ntok, softcap, idx, workspace, workspace_bytes=None, stream=None):
+    _check("qg_argmax", lib().qg_argmax(_ptr(logits), n, ntok, softcap, _ptr(idx), _ptr(workspace),
+                                        _nbytes(workspace, workspace_bytes), _stream(stream)))

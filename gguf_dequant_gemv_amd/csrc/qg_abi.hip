@@ -8,6 +8,7 @@
 
 #include "../../include/qgemv.h"
 #include "qg_kernels.h"
+#include "qg_block.h"
 
 using namespace qg;
 
@@ -290,11 +291,13 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 extern "C" {
 
 int qg_block_values(int type) {
+    if (type == QG_F32) return 1;
     TypeInfo ti;
     return type_info(type, ti) ? ti.qk : 0;
 }
 
 int qg_block_bytes(int type) {
+    if (type == QG_F32) return 4;
     TypeInfo ti;
     return type_info(type, ti) ? ti.bytes : 0;
 }
@@ -311,6 +314,12 @@ const char *qg_strerror(int code) {
 }
 
 int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
+    if (type == QG_F32) {   // plain f32 weights (router, shared-expert gate)
+        if (rows <= 0 || cols <= 0) return QG_EINVAL;
+        if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+        if (!W || !x || !y || !aligned(W, 4) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
+        return launch_gemv_f32((const float *)W, x, y, rows, cols, ntok, (hipStream_t)stream);
+    }
     Shape s;
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
@@ -443,9 +452,15 @@ size_t qg_moe_workspace_size(const qg_moe *m, int topk, int ntok) {
     return moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok).total;
 }
 
-int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
-               float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
-               size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// Validation, routing, and the two grouped expert launches of a MoE step.  On
+// success dn holds the weighted terms (dn_j s_j) c_j as [ntok][topk][H] and
+// valid the per-token validity, both inside the workspace.
+int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
+               const float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
+               size_t workspace_bytes, size_t ws_extra, hipStream_t st, float **dn_out, int32_t **valid_out) {
     if (!m) return QG_EINVAL;
     const int E = m->n_experts;
     if (E < 1 || E > QG_MAX_EXPERTS || topk < 1 || topk > QG_MAX_TOPK || topk > E || ntok < 1 ||
@@ -467,7 +482,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
         return QG_EINVAL;
     const int64_t H = m->hidden, F = m->ff;
     const MoeWs L = moe_ws(H, F, E, topk, ntok);
-    if (workspace_bytes < L.total) return QG_EINVAL;
+    if (workspace_bytes < L.total + ws_extra) return QG_EINVAL;
     uint8_t *ws = (uint8_t *)workspace;
     float *gu = (float *)(ws + L.gu);
     float *av = (float *)(ws + L.act);
@@ -476,7 +491,6 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     float *rt_w = (float *)(ws + L.w);
     int32_t *rt_valid = (int32_t *)(ws + L.valid);
     int32_t *grp = (int32_t *)(ws + L.grp);
-    hipStream_t st = (hipStream_t)stream;
 
     // 1. route: top-k, weights, slot lookup, grouping by expert
     const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
@@ -530,11 +544,127 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     b.pscale = rt_w;
     rc = launch_gemv(s_dn, p2, b, dim3(1, gmax, (ntok + p2.nt - 1) / p2.nt), st);
     if (rc) return rc;
+    *dn_out = dn;
+    *valid_out = rt_valid;
+    return QG_OK;
+}
 
-    // 4. weighted combine in pick order
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((H + 255) / 256), ntok), dim3(256), 0, st, dn, rt_valid, y, H,
-                       topk);
+// Workspace of a shared expert after the routed part's: gu [ntok][2 SF],
+// act [ntok][SF], sh [ntok][H], each 256-byte aligned.
+struct SharedWs {
+    size_t gu, act, sh, total;
+};
+SharedWs shared_ws(int64_t H, int64_t SF, int ntok) {
+    SharedWs o;
+    o.gu = 0;
+    o.act = align256((size_t)ntok * 2 * (size_t)SF * 4);
+    o.sh = o.act + align256((size_t)ntok * (size_t)SF * 4);
+    o.total = o.sh + align256((size_t)ntok * (size_t)H * 4);
+    return o;
+}
+}  // namespace
+
+extern "C" {
+
+int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
+               float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    hipStream_t st = (hipStream_t)stream;
+    float *dn = nullptr;
+    int32_t *valid = nullptr;
+    int rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace,
+                        workspace_bytes, 0, st, &dn, &valid);
+    if (rc) return rc;
+    // weighted combine in pick order
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((m->hidden + 255) / 256), ntok), dim3(256), 0, st, dn, valid, y,
+                       m->hidden, topk);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+size_t qg_moe_shared_workspace_size(const qg_moe *m, const qg_shared_expert *sh, int topk, int ntok) {
+    const size_t a = qg_moe_workspace_size(m, topk, ntok);
+    if (!a || !sh || sh->ff <= 0) return 0;
+    return a + shared_ws(m->hidden, sh->ff, ntok).total;
+}
+
+int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *router_logits, int topk,
+                      const int32_t *expert_slots, const float *x, float *resid, int ntok, int32_t *ids_out,
+                      float *w_out, int32_t *status, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!m || !sh) return QG_EINVAL;
+    if (!sh->gate || !sh->up || !sh->down || !sh->gate_inp || !aligned(sh->gate_inp, 4) || sh->ff <= 0)
+        return QG_EINVAL;
+    {   // the shared expert's shapes, checked before anything is enqueued
+        Shape a, b;
+        int rc = make_shape(sh->type, sh->ff, m->hidden, a);
+        if (!rc) rc = make_shape(sh->type, m->hidden, sh->ff, b);
+        if (rc) return rc;
+        if (!aligned(sh->gate, 2) || !aligned(sh->up, 2) || !aligned(sh->down, 2)) return QG_EINVAL;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const size_t base = qg_moe_workspace_size(m, topk, ntok);
+    if (!base) return ntok < 1 || ntok > QG_MAX_TOKENS ? QG_ELIMIT : QG_EINVAL;
+    const SharedWs S = shared_ws(m->hidden, sh->ff, ntok);
+    float *dn = nullptr;
+    int32_t *valid = nullptr;
+    int rc = moe_routed(m, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status, workspace,
+                        workspace_bytes, S.total, st, &dn, &valid);
+    if (rc) return rc;
+    // the shared expert: a dense gated MLP on the same input, into the workspace
+    uint8_t *ws = (uint8_t *)workspace + base;
+    rc = qg_mlp(sh->type, m->act, sh->gate, sh->up, sh->down, m->hidden, sh->ff, x, (float *)(ws + S.sh), ntok,
+                ws + S.gu, S.sh - S.gu, stream);
+    if (rc) return rc;
+    // routed terms + gated shared output + residual
+    return launch_combine_shared(dn, valid, (const float *)(ws + S.sh), sh->gate_inp, x, resid, m->hidden, topk,
+                                 ntok, st);
+}
+
+int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k, void *stream) {
+    if (n <= 0 || ntok < 1 || !x || !w || !y || !aligned(x, 4) || !aligned(w, 4) || !aligned(y, 4))
+        return QG_EINVAL;
+    if (!(eps >= 0.0f)) return QG_EINVAL;
+    return launch_rmsnorm(x, w, y, n, ntok, eps, k, (hipStream_t)stream);
+}
+
+int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2, const float *w,
+                const float *out_scale, float *x, int64_t n, int ntok, float eps, void *stream) {
+    if (n <= 0 || ntok < 1 || !(eps >= 0.0f)) return QG_EINVAL;
+    const float *ps[] = {mlp, moe, w1, w2, w, out_scale, x};
+    for (const float *p : ps)
+        if (!p || !aligned(p, 4)) return QG_EINVAL;
+    return launch_post_ffn(mlp, moe, w1, w2, w, out_scale, x, n, ntok, eps, (hipStream_t)stream);
+}
+
+int qg_embed(int type, const void *W, int64_t rows, int64_t cols, const int32_t *tokens, int ntok, float scale,
+             float *out, void *stream) {
+    Shape s;
+    int rc = make_shape(type, rows, cols, s);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > 65535) return QG_ELIMIT;
+    if (!W || !tokens || !out || !aligned(W, 2) || !aligned(tokens, 4) || !aligned(out, 4)) return QG_EINVAL;
+    dim3 grid((unsigned)((s.nb + 255) / 256), ntok);
+    hipLaunchKernelGGL(embed_kernel(type), grid, dim3(256), 0, (hipStream_t)stream, (const uint8_t *)W, rows, s.cols,
+                       s.row_bytes, tokens, scale, out);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+size_t qg_argmax_workspace_size(int64_t n, int ntok) {
+    if (n <= 0 || ntok < 1) return 0;
+    const size_t parts = (size_t)ntok * argmax_parts(n);
+    return align256(parts * 4) * 2;
+}
+
+int qg_argmax(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, void *workspace,
+              size_t workspace_bytes, void *stream) {
+    if (n <= 0 || ntok < 1 || !(softcap >= 0.0f)) return QG_EINVAL;
+    if (n > INT32_MAX || ntok > 65535) return QG_ELIMIT;
+    if (!logits || !idx || !workspace || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(workspace, 256))
+        return QG_EINVAL;
+    const size_t need = qg_argmax_workspace_size(n, ntok);
+    if (workspace_bytes < need) return QG_EINVAL;
+    float *pv = (float *)workspace;
+    int32_t *pi = (int32_t *)((uint8_t *)workspace + need / 2);
+    return launch_argmax(logits, n, ntok, softcap, pv, pi, idx, (hipStream_t)stream);
 }
 
 }  // extern "C"

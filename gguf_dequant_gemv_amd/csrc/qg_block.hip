@@ -1,0 +1,316 @@
+// qg_block.hip -- the steps on either side of the routed experts (gfx950):
+// RMS norm, the f32 GEMV of the router and shared-expert gate weights, the
+// shared-expert combine with the residual, Gemma's FFN tail, embedding rows,
+// and the logit soft cap with the greedy pick.
+#include "../../include/qgemv.h"
+#include "qg_kernels.h"
+#include "qg_block.h"
+
+namespace qg {
+
+// Sum over a workgroup of NW waves, returned to every thread.  The additions
+// run in a fixed order (DPP inside each wave, then the wave sums in wave
+// order), so every workgroup that reduces the same data gets the same bits.
+template <int NW>
+QG_DEV float block_sum(float v, float *s_red) {
+    v = wave_sum(v);
+    __syncthreads();   // s_red may still be read by an earlier call
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float s = s_red[0];
+#pragma unroll
+    for (int i = 1; i < NW; i++) s += s_red[i];
+    return s;
+}
+
+QG_DEV float rms_factor(float ss, int64_t n, float eps) { return 1.0f / sqrtf(ss / (float)n + eps); }
+
+// ------------------------------------------------------------- RMS norm ----
+// One workgroup per token: r = 1/sqrt(mean x^2 + eps), y = ((x r) k) w.  The
+// qwen3_moe_ssd.js rmsnorm kernel (k = 1) and gemma4_moe_ssd.js rmsnormK (the
+// router input: k = 1/sqrt(H), w the router's scale vector).  Every x is read
+// for the sum before any y is written, so y may be x.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w, float *y, int64_t n, float eps,
+                                                 float k) {
+    __shared__ float s_red[4];
+    const float *xt = x + (int64_t)blockIdx.x * n;
+    float *yt = y + (int64_t)blockIdx.x * n;
+    float ss = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) ss = fmaf(xt[i], xt[i], ss);
+    const float r = rms_factor(block_sum<4>(ss, s_red), n, eps);
+    for (int64_t i = threadIdx.x; i < n; i += 256) yt[i] = ((xt[i] * r) * k) * w[i];
+}
+
+// ------------------------------------------------------------ f32 GEMV ----
+// y[t][r] = sum_c W[r][c] x[t][c] for f32 weights (the router's logits and the
+// shared expert's gate: qwen3_moe_ssd.js matmulF32).  One wave per row; each
+// lane takes 4 consecutive columns per step (V4: 16-byte loads), the row's
+// values are loaded once and used for all NT tokens, and the lane partials are
+// summed across the wave.
+template <int NT, bool V4>
+__global__ __launch_bounds__(256) void k_gemv_f32(const float *W, const float *x, float *y, int64_t rows,
+                                                  int64_t cols, int ntok) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= rows) return;   // the whole wave leaves; nothing below waits on it
+    const float *wr = W + r * cols;
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.0f;
+    if constexpr (V4) {
+#pragma unroll 4
+        for (int64_t c = 4 * lane; c < cols; c += 256) {
+            const float4 wv = *(const float4 *)(wr + c);
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                if (t < ntok) {
+                    const float4 xv = *(const float4 *)(x + t * cols + c);
+                    acc[t] = fmaf(wv.x, xv.x, acc[t]);
+                    acc[t] = fmaf(wv.y, xv.y, acc[t]);
+                    acc[t] = fmaf(wv.z, xv.z, acc[t]);
+                    acc[t] = fmaf(wv.w, xv.w, acc[t]);
+                }
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int64_t c = lane; c < cols; c += 64) {
+            const float wv = wr[c];
+#pragma unroll
+            for (int t = 0; t < NT; t++)
+                if (t < ntok) acc[t] = fmaf(wv, x[t * cols + c], acc[t]);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        if (t < ntok) {
+            const float s = wave_sum(acc[t]);
+            if (lane == 0) y[t * rows + r] = s;
+        }
+    }
+}
+
+// ----------------------------------------------- shared-expert combine ----
+// Per token t and hidden index h:
+//   sg   = gate_inp . x[t]                    (the shared expert's gate logit)
+//   y[h] = (sum_j terms_j[h] + sh[h] sigmoid(sg)) + resid[h]      -> resid[h]
+// terms_j = (dn_j s_j) c_j come from the expert down launch; added in pick
+// order.  qwen35_moe_ssd.js moeAccumShared: routed experts, the gated shared
+// expert, then the residual.  Each workgroup of token t reduces the same gate
+// products in the same order, so all of them use the same sg.
+__global__ __launch_bounds__(256) void k_combine_shared(const float *dn, const int32_t *rt_valid, const float *sh,
+                                                        const float *gate_inp, const float *x, float *resid,
+                                                        int64_t H, int k) {
+    __shared__ float s_red[4];
+    const int t = blockIdx.y;
+    const float *xt = x + (int64_t)t * H;
+    float p = 0.0f;
+    for (int64_t c = threadIdx.x; c < H; c += 256) p = fmaf(gate_inp[c], xt[c], p);
+    const float sg = block_sum<4>(p, s_red);
+    const float gs = 1.0f / (1.0f + expf(-sg));
+    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    const float *q = dn + (int64_t)t * k * H + h;
+    float acc = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = j0 + j < k ? q[(int64_t)(j0 + j) * H] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            if (j0 + j < k) acc += v[j];
+    }
+    const int64_t o = (int64_t)t * H + h;
+    if (rt_valid[t]) resid[o] = (acc + sh[o] * gs) + resid[o];
+}
+
+// ----------------------------------------------------- Gemma's FFN tail ----
+// One workgroup per token:
+//   m = rmsnorm(mlp) w1,  e = rmsnorm(moe) w2,  v = m + e,
+//   x = ((v r_v) w + x) os
+// gemma4_moe_ssd.js encodeExperts (post_ffw_norm_1 / _2) and postFfn, in one
+// launch: the sums of squares of mlp and moe first, then that of v, then the
+// update (v recomputed from the same f32 operations each time).
+__global__ __launch_bounds__(256) void k_post_ffn(const float *mlp, const float *moe, const float *w1,
+                                                  const float *w2, const float *w, const float *os, float *x,
+                                                  int64_t n, float eps) {
+    __shared__ float s_red[4];
+    const int64_t o = (int64_t)blockIdx.x * n;
+    const float *a = mlp + o, *b = moe + o;
+    float *xt = x + o;
+    float s1 = 0.0f, s2 = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        s1 = fmaf(a[i], a[i], s1);
+        s2 = fmaf(b[i], b[i], s2);
+    }
+    const float r1 = rms_factor(block_sum<4>(s1, s_red), n, eps);
+    const float r2 = rms_factor(block_sum<4>(s2, s_red), n, eps);
+    float s3 = 0.0f;
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        const float v = (a[i] * r1) * w1[i] + (b[i] * r2) * w2[i];
+        s3 = fmaf(v, v, s3);
+    }
+    const float r3 = rms_factor(block_sum<4>(s3, s_red), n, eps);
+    const float ko = os[0];
+    for (int64_t i = threadIdx.x; i < n; i += 256) {
+        const float v = (a[i] * r1) * w1[i] + (b[i] * r2) * w2[i];
+        xt[i] = ((v * r3) * w[i] + xt[i]) * ko;
+    }
+}
+
+// ------------------------------------------------------ embedding rows ----
+// out[t][c] = value(W[tok[t]][c]) * scale: one thread per block of the row,
+// decoded by the same block units as the GEMV (qwen3_moe_ssd.js embedQ8,
+// gemma4_moe_ssd.js embedQ6K with its scale).  A token outside [0, rows)
+// reads nothing and gets a row of NaN.
+template <class U>
+__global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
+                                               const int32_t *tok, float scale, float *out) {
+    const int nbr = cols / U::VALUES;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b >= nbr) return;
+    const int32_t id = tok[blockIdx.y];
+    float *o = out + (int64_t)blockIdx.y * cols + (int64_t)b * U::VALUES;
+    if (id < 0 || id >= rows) {
+        for (int i = 0; i < U::VALUES; i++) o[i] = __builtin_nanf("");
+        return;
+    }
+    const uint8_t *p = W + (int64_t)id * row_bytes + (int64_t)b * U::BYTES;
+    const u32 ph = (u32)((uintptr_t)p & 3u);
+    const rsrc_t rs = make_rsrc(p - ph, (u32)(ph + U::BYTES + 3) & ~3u);
+    u32 w[U::ND];
+    U::load(rs, ph, w);
+#pragma unroll
+    for (int i = 0; i < U::VALUES; i++) o[i] = U::value(w, i) * scale;
+}
+
+embed_fn embed_kernel(int type) {
+    switch (type) {
+    case T_Q8_0: return k_embed<UQ8_0B>;
+    case T_Q4_0: return k_embed<UQ4_0B>;
+    case T_Q4_K: return k_embed<UQ4_K>;
+    default: return k_embed<UQ6_K>;
+    }
+}
+
+// ---------------------------------------------------- soft cap, argmax ----
+// (value, index) candidates: the larger value wins, equal values go to the
+// lower index, an empty candidate (index < 0) always loses.  The winner over
+// any set is unique, so the order of the merges does not matter.
+QG_DEV void am_merge(float &bv, int &bi, float ov, int oi) {
+    if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+QG_DEV void am_wave(float &bv, int &bi) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m);
+        const int oi = __shfl_xor(bi, m);
+        am_merge(bv, bi, ov, oi);
+    }
+}
+
+// Phase 1, workgroup (g, t): the span [g span, (g+1) span) of token t's
+// logits.  With cap > 0 each logit is first capped in place,
+// l = tanh(clamp(l inv, -10, 10)) cap (gemma4_moe_ssd.js softcap); NaN stays
+// NaN.  Then the first index of the largest value, NaN skipped
+// (qwen3_moe_ssd.js argmax: strict greater-than, lower index on ties).
+__global__ __launch_bounds__(256) void k_argmax_part(float *l, int64_t n, int64_t span, float cap, float inv,
+                                                     float *pv, int32_t *pi) {
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    float *lt = l + (int64_t)blockIdx.y * n;
+    const int64_t lo = (int64_t)blockIdx.x * span;
+    const int64_t hi = min(n, lo + span);
+    float bv = 0.0f;
+    int bi = -1;
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+        float v = lt[i];
+        if (cap > 0.0f) {
+            float a = v * inv;
+            a = a < -10.0f ? -10.0f : (a > 10.0f ? 10.0f : a);
+            v = tanhf(a) * cap;
+            lt[i] = v;
+        }
+        if (v == v && (bi < 0 || v > bv)) {
+            bv = v;
+            bi = (int)i;
+        }
+    }
+    am_wave(bv, bi);
+    if ((threadIdx.x & 63) == 0) {
+        s_v[threadIdx.x >> 6] = bv;
+        s_i[threadIdx.x >> 6] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < 4; w++) am_merge(bv, bi, s_v[w], s_i[w]);
+        pv[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = bv;
+        pi[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = bi;
+    }
+}
+
+// Phase 2, one wave per token: the winner over the G partials; 0 when the
+// token's logits hold no number at all.
+__global__ __launch_bounds__(64) void k_argmax_final(const float *pv, const int32_t *pi, int G, int32_t *idx) {
+    const int t = blockIdx.x, lane = threadIdx.x;
+    float bv = 0.0f;
+    int bi = -1;
+    for (int g = lane; g < G; g += 64) am_merge(bv, bi, pv[(int64_t)t * G + g], pi[(int64_t)t * G + g]);
+    am_wave(bv, bi);
+    if (lane == 0) idx[t] = bi < 0 ? 0 : bi;
+}
+
+// ------------------------------------------------------------ launches ----
+int launch_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k,
+                   hipStream_t st) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(ntok), dim3(256), 0, st, x, w, y, n, eps, k);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_gemv_f32(const float *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok,
+                    hipStream_t st) {
+    const bool v4 = (cols % 4) == 0 && ((uintptr_t)W % 16) == 0 && ((uintptr_t)x % 16) == 0;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    void (*f)(const float *, const float *, float *, int64_t, int64_t, int);
+    if (ntok == 1) f = v4 ? k_gemv_f32<1, true> : k_gemv_f32<1, false>;
+    else if (ntok <= 4) f = v4 ? k_gemv_f32<4, true> : k_gemv_f32<4, false>;
+    else f = v4 ? k_gemv_f32<16, true> : k_gemv_f32<16, false>;
+    hipLaunchKernelGGL(f, grid, dim3(256), 0, st, W, x, y, rows, cols, ntok);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_combine_shared(const float *dn, const int32_t *rt_valid, const float *sh, const float *gate_inp,
+                          const float *x, float *resid, int64_t H, int k, int ntok, hipStream_t st) {
+    hipLaunchKernelGGL(k_combine_shared, dim3((unsigned)((H + 255) / 256), ntok), dim3(256), 0, st, dn, rt_valid,
+                       sh, gate_inp, x, resid, H, k);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2, const float *w,
+                    const float *os, float *x, int64_t n, int ntok, float eps, hipStream_t st) {
+    hipLaunchKernelGGL(k_post_ffn, dim3(ntok), dim3(256), 0, st, mlp, moe, w1, w2, w, os, x, n, eps);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int argmax_parts(int64_t n) {
+    int64_t g = (n + ARGMAX_SPAN - 1) / ARGMAX_SPAN;
+    return (int)(g < ARGMAX_MAX_PARTS ? g : ARGMAX_MAX_PARTS);
+}
+
+int launch_argmax(float *l, int64_t n, int ntok, float cap, float *pv, int32_t *pi, int32_t *idx,
+                  hipStream_t st) {
+    const int G = argmax_parts(n);
+    const int64_t span = (n + G - 1) / G;
+    // the f32 nearest 1/cap, as the soft cap's uniform holds it
+    const float inv = cap > 0.0f ? (float)(1.0 / (double)cap) : 0.0f;
+    hipLaunchKernelGGL(k_argmax_part, dim3(G, ntok), dim3(256), 0, st, l, n, span, cap, inv, pv, pi);
+    if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    hipLaunchKernelGGL(k_argmax_final, dim3(ntok), dim3(64), 0, st, pv, pi, G, idx);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+}  // namespace qg

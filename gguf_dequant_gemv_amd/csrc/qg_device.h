@@ -99,6 +99,17 @@ QG_DEV float group_sum(float v) {
     return v;
 }
 
+// Sum over the whole wave, every lane getting the same value: DPP within each
+// row of 16 lanes, then the four row sums through scalar registers.
+QG_DEV float wave_sum(float v) {
+    v = group_sum<16>(v);
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (a + b) + (c + d);
+}
+
 // ------------------------------------------------ x staging layout (LDS) ----
 // x values are stored with 4 floats of padding after every 64, so that lanes
 // reading the 64- or 256-value spans of different units hit different banks.

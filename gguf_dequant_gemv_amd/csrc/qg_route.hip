@@ -31,15 +31,6 @@ QG_DEV u32 wave_max_u32(u32 v) {
     return max(max(a, b), max(c, d));
 }
 
-QG_DEV float wave_sum(float v) {   // every lane gets the same sum
-    v = group_sum<16>(v);
-    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return (a + b) + (c + d);
-}
-
 __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int k, int T,
                                                 const int32_t *slots, int n_slots, int32_t *ids_out, float *w_out,
                                                 int32_t *status, int32_t *rt_ids, float *rt_w,

@@ -206,3 +206,50 @@ def device_weights(t, rows, cols, gen, device="cuda", sigma=None):
 def device_activations(ntok, n, gen, device="cuda"):
     import torch
     return torch.randn((ntok, n), generator=gen, device=device, dtype=torch.float32)
+
+
+# ---- whole FFN blocks (the steps around the MoE) -------------------------------
+
+def norm_weights(g, n):
+    """a norm's gain vector ~ U(0.5, 1.5) f32 [n] (stand-in for trained gains near 1)."""
+    return g.uniform(0.5, 1.5, n).astype(np.float32)
+
+
+def f32_matrix(g, rows, cols, sigma):
+    """plain f32 weights ~ N(0, sigma) [rows][cols] (router, shared-expert gate)."""
+    return (g.standard_normal((rows, cols), dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+
+
+def qwen35_block(seed=0, ntok=1, t=Q8_0, H=2048, E=256, F=512, SF=512, k=8):
+    """Qwen3.5/3.6-MoE-style FFN block: post-attention RMS norm, f32 router
+    [E x H] (sigma 1/sqrt(H), so logits are about N(0, 1)), E routed experts of
+    ff F, top-k, and a shared expert of ff SF with an f32 gate row; residual
+    stream x ~ N(0, 1)."""
+    g = rng(seed)
+    pool, rec, gu_off, d_off = expert_pool(t, g, E, H, F)
+    sg = weights(t, g, SF, H)
+    su = weights(t, g, SF, H)
+    sd = weights(t, g, H, SF)
+    return dict(name="qwen35_moe_block_h%d_e%d_ff%d_shared%d_top%d_t%d" % (H, E, F, SF, k, ntok), type=t, H=H,
+                F=F, SF=SF, E=E, k=k, pool=pool, record=rec, gu_off=gu_off, d_off=d_off,
+                sh_gate=sg, sh_up=su, sh_down=sd,
+                sh_gate_inp=f32_matrix(g, 1, H, 1.0 / np.sqrt(H))[0],
+                router=f32_matrix(g, E, H, 1.0 / np.sqrt(H)), norm=norm_weights(g, H),
+                x=activations(g, ntok, H), ntok=ntok, slots=np.arange(E, dtype=np.int32))
+
+
+def gemma_block(seed=0, ntok=1, E=128):
+    """Gemma4-26B-A4B-style FFN block at Q4_0: the dense GELU MLP (ff 2112) and
+    the MoE (E experts of ff 704, top-8, per-expert down scale) with their
+    norms: ffn_norm, pre_ffw_norm_2, the router's scale (router input
+    rmsnorm * 1/sqrt(H) * scale; f32 router [E x H] ~ N(0, 1), so logits are
+    about N(0, 1)), post_ffw_norm_1 / _2, post_ffw_norm and the layer's output
+    scalar ~ U(0.5, 1); residual stream x ~ N(0, 1)."""
+    c = config4(seed, ntok, E)
+    g = rng(seed + 7919)
+    H = c["H"]
+    c.update(name="gemma_ffn_block_2816_e%d_t%d" % (E, ntok), router=f32_matrix(g, E, H, 1.0),
+             w_ffn=norm_weights(g, H), w_pre2=norm_weights(g, H), w_rscale=norm_weights(g, H),
+             w_post1=norm_weights(g, H), w_post2=norm_weights(g, H), w_post=norm_weights(g, H),
+             out_scale=np.array([g.uniform(0.5, 1.0)], np.float32))
+    return c

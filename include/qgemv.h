@@ -24,8 +24,10 @@
  *     padding, no plane split).  W needs only 2-byte alignment.  The GGUF dims
  *     order is (cols, rows): dims[0] is the contiguous, quantized axis.
  *   - Activations are f32, token-major: x is [ntok][cols], y is [ntok][rows].
- *     Outputs are overwritten (no residual add).
- *   - 1 <= ntok <= QG_MAX_TOKENS; cols must be a multiple of the block's QK.
+ *     Outputs are overwritten, except where an entry point states that it
+ *     updates the residual stream in place.
+ *   - 1 <= ntok <= QG_MAX_TOKENS unless an entry point states its own limit;
+ *     cols must be a multiple of the block's QK.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -46,8 +48,10 @@ extern "C" {
  *   Q4_K 144 B / 256 values: f16 d | f16 dmin | scales[12] | qs[128]
  *         value = d*sc*q - dmin*m per 32-value sub-block ([bonsai] dequantQ4K)
  *   Q6_K 210 B / 256 values: ql[128] | qh[64] | int8 scales[16] | f16 d
- *         value = d*sc*(q-32) per 16 values ([bonsai] dequantQ6K)            */
-enum qg_type { QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14 };
+ *         value = d*sc*(q-32) per 16 values ([bonsai] dequantQ6K)
+ *   F32     4 B / 1 value  : IEEE binary32 (GGML's 0), accepted by qg_gemv only:
+ *         the router and shared-expert gate weights ([qwen3] matmulF32)     */
+enum qg_type { QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14 };
 
 /* Gated activations: act(gate) * up.
  *   QG_ACT_SILU       gate / (1 + exp(-gate))           ([qwen3] siluMulMoe)
@@ -67,7 +71,8 @@ enum qg_err {
 #define QG_MAX_EXPERTS 256  /* router width limit ([qwen3] engine: n <= 256)    */
 #define QG_MAX_TOPK 32      /* picks per token limit ([qwen3] engine: k <= 32)  */
 
-/* Values and bytes per block of `type`; 0 for an unknown type.  Host only. */
+/* Values and bytes per block of `type` (1 and 4 for QG_F32); 0 for an unknown
+ * type.  Host only. */
 int qg_block_values(int type);
 int qg_block_bytes(int type);
 
@@ -82,6 +87,9 @@ const char *qg_strerror(int code);
  * The sum the pages' GEMV kernels compute: [qwen3] WGSL matmulQ8, [gemma4]
  * matmulQ4 / matmulQ6K, [bonsai] packed-weight GEMMs, [qwen35] matmulQ8T.
  * W: rows x cols GGUF blocks; x: [ntok][cols] f32; y: [ntok][rows] f32.
+ * type QG_F32: W is a plain row-major f32 matrix (4-byte aligned), the
+ * router's logits and the shared expert's gate logit ([qwen3] matmulF32,
+ * [qwen35] shgate binding).
  * Errors: QG_EINVAL (type, rows<=0, cols<=0 or cols % QK, null pointer, W not
  * 2-byte aligned, x/y not 4-byte aligned), QG_ELIMIT (ntok outside 1..16). */
 int qg_gemv(int type, const void *W, const float *x, float *y,
@@ -174,6 +182,86 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk,
                const int32_t *expert_slots, const float *x, float *y, int ntok,
                int32_t *ids_out, float *w_out, int32_t *status,
                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------ around the routed experts */
+
+/* RMS norm with a scalar factor, per token of n values:
+ *   r = 1 / sqrt(sum_i x_i^2 / n + eps),   y_i = ((x_i * r) * k) * w_i
+ * [qwen3] WGSL rmsnorm (k = 1: the FFN input xn) and [gemma4] rmsnormK (the
+ * router's input: k = 1/sqrt(H), w = ffn_gate_inp.scale).
+ * x, y: [ntok][n] f32 (y may equal x); w: [n] f32.  One workgroup per token.
+ * Errors: QG_EINVAL (n <= 0, ntok < 1, eps < 0 or NaN, null or misaligned
+ * pointer). */
+int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k,
+               void *stream);
+
+/* The shared expert of a MoE block (a HOST struct; its pointers are device
+ * pointers): a dense gated MLP with ff SF beside the routed experts, scaled
+ * by the logistic of a scalar gate logit ([qwen35] ffn_gate_shexp,
+ * ffn_up_shexp, ffn_down_shexp, ffn_gate_inp_shexp). */
+typedef struct qg_shared_expert {
+    int type;               /* qg_type of gate, up and down (not QG_F32)       */
+    int64_t ff;             /* SF                                              */
+    const void *gate;       /* SF x H blocks                                   */
+    const void *up;         /* SF x H blocks                                   */
+    const void *down;       /* H x SF blocks                                   */
+    const float *gate_inp;  /* [H] f32: the scalar gate's weight row           */
+} qg_shared_expert;
+
+/* MoE block with a shared expert and the residual ([qwen35] encodeAttention's
+ * shared-expert dispatches and encodeExperts; WGSL moeAccumShared /
+ * moeAccumSharedB), per token t:
+ *   terms_j = (dn_j * s[ids_j]) * c_j          (the routed part, as qg_moe_ffn)
+ *   sh      = W_sd (act(W_sg x) * (W_su x))    (act = m->act)
+ *   sg      = gate_inp . x
+ *   resid   = (sum_j terms_j + sh * sigmoid(sg)) + resid      (in place)
+ * x is the block's (normed) input, resid the residual stream [ntok][H],
+ * updated in place.  A token with an absent pick keeps its resid row and the
+ * status word reads QG_EABSENT.
+ * workspace: at least qg_moe_shared_workspace_size(m, sh, topk, ntok) bytes,
+ * 256-byte aligned: qg_moe_ffn's workspace (same layout), then the shared
+ * expert's gu [ntok][2 SF] and act [ntok][SF] (qg_mlp's layout) and its
+ * output sh [ntok][H], each at a 256-byte boundary.
+ * Errors: as qg_moe_ffn, and as qg_mlp for the shared expert's shapes (all
+ * checked before anything is enqueued). */
+size_t qg_moe_shared_workspace_size(const qg_moe *m, const qg_shared_expert *sh, int topk, int ntok);
+int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *router_logits, int topk,
+                      const int32_t *expert_slots, const float *x, float *resid, int ntok, int32_t *ids_out,
+                      float *w_out, int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Gemma's FFN tail, per token of n values ([gemma4] encodeExperts: the
+ * post_ffw_norm_1 / post_ffw_norm_2 rmsnorms, then WGSL postFfn):
+ *   m = rmsnorm(mlp) * w1,  e = rmsnorm(moe) * w2,  v = m + e
+ *   x = ((v * r_v) * w + x) * out_scale[0],   r_v = 1/sqrt(sum v^2 / n + eps)
+ * mlp: the dense MLP's output, moe: the MoE sum, x: the residual stream
+ * (updated in place), all [ntok][n]; w1, w2, w: [n]; out_scale: one f32 (the
+ * layer's output scalar).  One launch, one workgroup per token.
+ * Errors: QG_EINVAL (n <= 0, ntok < 1, eps < 0, null or misaligned pointer). */
+int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2, const float *w,
+                const float *out_scale, float *x, int64_t n, int ntok, float eps, void *stream);
+
+/* Embedding rows of a quantized table: out[t][c] = W[tokens[t]][c] * scale,
+ * each value the f32 nearest its exact value (as qg_dequant), multiplied by
+ * scale in f32 ([qwen3] WGSL embedQ8 with scale 1, [gemma4] embedQ6K with its
+ * scale).  tokens: [ntok] int32 on the device; a token outside [0, rows) reads
+ * nothing and gets a row of NaN.  out: [ntok][cols].
+ * Errors: as qg_dequant; QG_ELIMIT for ntok outside 1..65535. */
+int qg_embed(int type, const void *W, int64_t rows, int64_t cols, const int32_t *tokens, int ntok, float scale,
+             float *out, void *stream);
+
+/* Greedy pick over logits, per token: with softcap > 0 each logit is first
+ * replaced in place by tanh(clamp(l * inv, -10, 10)) * softcap, inv the f32
+ * nearest 1/softcap ([gemma4] WGSL softcap); then idx[t] = the index of the
+ * largest value, ties to the lowest index, NaN never picked, 0 for a row with
+ * no number ([qwen3] WGSL argmax).  Two launches: partial winners of spans of
+ * the row, then the winner of those.
+ * logits: [ntok][n] f32; idx: [ntok] int32.  workspace: at least
+ * qg_argmax_workspace_size(n, ntok) bytes, 256-byte aligned.
+ * Errors: QG_EINVAL (n <= 0, ntok < 1, softcap < 0 or NaN, null or misaligned
+ * pointer, short workspace), QG_ELIMIT (n > 2^31 - 1, ntok > 65535). */
+size_t qg_argmax_workspace_size(int64_t n, int ntok);
+int qg_argmax(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, void *workspace,
+              size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -111,3 +111,58 @@ def test_moe_rejects_and_sizes():
     assert call(_moe(ff=100)) == qg.QG_EINVAL                     # ff % 32
     assert call(_moe(gate_up_stride=1000)) == qg.QG_EINVAL        # stride shorter than a record
     assert L.qg_moe_ffn(None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, FAKE, ws, None) == qg.QG_EINVAL
+
+
+def test_f32_block_and_gemv_rejects():
+    L = qg.lib()
+    assert qg.qg_block_values(qg.QG_F32) == 1 and qg.qg_block_bytes(qg.QG_F32) == 4
+    assert L.qg_gemv(0, FAKE, FAKE, FAKE, 128, 2048, 17, None) == qg.QG_ELIMIT
+    assert L.qg_gemv(0, FAKE + 2, FAKE, FAKE, 128, 2048, 1, None) == qg.QG_EINVAL   # W not 4-byte aligned
+    assert L.qg_gemv(0, FAKE, FAKE, FAKE, 0, 2048, 1, None) == qg.QG_EINVAL
+    # f32 is a GEMV weight type only
+    assert L.qg_dequant(0, FAKE, FAKE, 4, 64, None) == qg.QG_EINVAL
+    assert L.qg_embed(0, FAKE, 4, 64, FAKE, 1, 1.0, FAKE, None) == qg.QG_EINVAL
+
+
+def test_rmsnorm_post_ffn_rejects():
+    L = qg.lib()
+    assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 0, 1, 1e-6, 1.0, None) == qg.QG_EINVAL
+    assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 64, 0, 1e-6, 1.0, None) == qg.QG_EINVAL
+    assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 64, 1, -1.0, 1.0, None) == qg.QG_EINVAL
+    assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 64, 1, float("nan"), 1.0, None) == qg.QG_EINVAL
+    assert L.qg_rmsnorm(FAKE + 2, FAKE, FAKE, 64, 1, 1e-6, 1.0, None) == qg.QG_EINVAL
+    assert L.qg_post_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 1, 1e-6, None) == qg.QG_EINVAL
+    assert L.qg_post_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1e-6, None) == qg.QG_EINVAL
+
+
+def test_embed_argmax_rejects_and_sizes():
+    L = qg.lib()
+    assert L.qg_embed(14, FAKE, 10, 300, FAKE, 1, 1.0, FAKE, None) == qg.QG_EINVAL    # cols % 256
+    assert L.qg_embed(8, FAKE, 10, 64, FAKE, 0, 1.0, FAKE, None) == qg.QG_ELIMIT
+    assert L.qg_embed(8, FAKE, 10, 64, None, 1, 1.0, FAKE, None) == qg.QG_EINVAL
+    n = 151936
+    ws = qg.qg_argmax_workspace_size(n, 2)
+    assert ws % 256 == 0 and ws >= 2 * 2 * ((n + 2047) // 2048) * 4
+    assert qg.qg_argmax_workspace_size(0, 1) == 0
+    assert L.qg_argmax(FAKE, n, 2, 0.0, FAKE, FAKE, ws - 4, None) == qg.QG_EINVAL
+    assert L.qg_argmax(FAKE, n, 2, -1.0, FAKE, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_argmax(FAKE, n, 2, 0.0, FAKE, FAKE + 16, ws, None) == qg.QG_EINVAL
+    assert L.qg_argmax(FAKE, 1 << 31, 1, 0.0, FAKE, FAKE, 1 << 20, None) == qg.QG_ELIMIT
+
+
+def test_moe_shared_rejects_and_sizes():
+    L = qg.lib()
+    m = _moe(n_experts=256, ff=512, gate_up_stride=2 * 512 * 64 * 34, down_stride=2048 * 16 * 34)
+    sh = qg.qg_shared_expert(8, 512, FAKE, FAKE, FAKE, FAKE)
+    base = qg.qg_moe_workspace_size(m, 8, 1)
+    ws = qg.qg_moe_shared_workspace_size(m, sh, 8, 1)
+    assert ws == base + 2 * 512 * 4 + 512 * 4 + 2048 * 4     # gu, act, sh after the routed part
+    call = lambda s, w=ws, T=1: L.qg_moe_ffn_shared(ctypes.byref(m), ctypes.byref(s), FAKE, 8, FAKE, FAKE, FAKE, T,
+                                                   None, None, FAKE, FAKE, w, None)
+    assert call(sh, w=ws - 256) == qg.QG_EINVAL
+    assert call(sh, T=17) == qg.QG_ELIMIT
+    assert call(qg.qg_shared_expert(8, 100, FAKE, FAKE, FAKE, FAKE)) == qg.QG_EINVAL   # SF % 32
+    assert call(qg.qg_shared_expert(0, 512, FAKE, FAKE, FAKE, FAKE)) == qg.QG_EINVAL   # f32 shared expert
+    assert call(qg.qg_shared_expert(8, 512, FAKE, FAKE, FAKE, None)) == qg.QG_EINVAL   # no gate row
+    assert L.qg_moe_ffn_shared(ctypes.byref(m), None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, FAKE, ws,
+                               None) == qg.QG_EINVAL
