@@ -36,7 +36,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="1", help="0, 1, 2, 3a, 3b, 4, 4t16")
+    ap.add_argument("--config", default="1",
+                    help="0, 1, 2, 3a, 3b, 4, 4t16; whole FFN blocks q35, q35t16, gblk, gblkt16; heads head8, head6")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
@@ -68,6 +69,9 @@ class Workload:
 
     def dominant_step(self, i):
         self.step(i)
+
+    def reset(self):
+        """Restore state that steps update in place (a residual stream)."""
 
     def output(self):
         raise NotImplementedError
@@ -247,6 +251,199 @@ class MoeLayers(Workload):
         return self.y
 
 
+class Qwen35Block(Workload):
+    """A Qwen3.5/3.6-MoE-style FFN block, T tokens, over L independent layers:
+    RMS norm of the residual stream, f32 router GEMV, routed experts plus the
+    gated shared expert added into the residual (qg_rmsnorm, qg_gemv QG_F32,
+    qg_moe_ffn_shared)."""
+
+    def __init__(self, ntok, layers=16, H=2048, E=256, F=512, SF=512, k=8):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        t = gs.Q8_0
+        self.qg, self.ntok, self.k, self.H, self.E = qg, ntok, k, H, E
+        rb_h, rb_f, rb_s = gs.row_bytes(t, H), gs.row_bytes(t, F), gs.row_bytes(t, SF)
+        rec = 2 * F * rb_h + H * rb_f
+        g = _gen(800 + ntok)
+        self.layers = []
+        uniq = []
+        for _ in range(layers):
+            gu = gs.device_weights(t, E * 2 * F, H, g)
+            dn = gs.device_weights(t, E * H, F, g)
+            L = dict(gu=gu, dn=dn, sg=gs.device_weights(t, SF, H, g), su=gs.device_weights(t, SF, H, g),
+                     sd=gs.device_weights(t, H, SF, g),
+                     gi=torch.randn(H, generator=g, device="cuda") / H ** 0.5,
+                     router=torch.randn((E, H), generator=g, device="cuda") / H ** 0.5,
+                     norm=torch.rand(H, generator=g, device="cuda") + 0.5,
+                     x0=gs.device_activations(ntok, H, g))
+            L["x"] = L["x0"].clone()
+            L["m"] = qg.make_moe(t, qg.QG_ACT_SILU, H, F, E, gu, 2 * F * rb_h, dn, H * rb_f)
+            L["sh"] = qg.make_shared_expert(t, SF, L["sg"], L["su"], L["sd"], L["gi"])
+            self.layers.append(L)
+        self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
+        self.xn = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
+        self.lg = torch.empty((ntok, E), dtype=torch.float32, device="cuda")
+        self.ids = torch.empty((ntok, k), dtype=torch.int32, device="cuda")
+        self.w = torch.empty((ntok, k), dtype=torch.float32, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L0 = self.layers[0]
+        self.ws = torch.empty(qg.qg_moe_shared_workspace_size(L0["m"], L0["sh"], k, ntok) // 4,
+                              dtype=torch.float32, device="cuda")
+        # algorithmic bytes: each distinct picked expert's record once, the
+        # shared expert, the router and the norm / gate vectors
+        for L in self.layers:
+            self.step_layer(L)
+            uniq.append(len(set(self.ids.cpu().flatten().tolist())))
+        self.reset()
+        fixed = 2 * SF * rb_h + H * rb_s + E * H * 4 + 2 * H * 4
+        self.bytes_per_step = int(sum(uniq) / len(uniq) * rec) + fixed
+        self.dominant_bytes = self.bytes_per_step
+        self.name = ("q8_0 Qwen3.5-MoE-style FFN block: rmsnorm, f32 router %dx%d, %d experts ff %d top-%d + "
+                     "shared expert ff %d, residual; %d token(s)" % (E, H, E, F, k, SF, ntok))
+        self.dominant = self.name
+        self.key = "qwen35_block_q8_0_%d_e%d_t%d" % (H, E, ntok)
+        self.period = self.dominant_period = layers
+
+    def reset(self):
+        for L in self.layers:
+            L["x"].copy_(L["x0"])
+
+    def step_layer(self, L):
+        qg, T = self.qg, self.ntok
+        qg.qg_rmsnorm(L["x"], L["norm"], self.xn, self.H, T, 1e-6, 1.0)
+        qg.qg_gemv(qg.QG_F32, L["router"], self.xn, self.lg, self.E, self.H, T)
+        qg.qg_moe_ffn_shared(L["m"], L["sh"], self.lg, self.k, self.slots, self.xn, L["x"], T, self.ids, self.w,
+                             self.status, self.ws)
+
+    def step(self, i):
+        self.step_layer(self.layers[i % len(self.layers)])
+
+    def output(self):
+        return torch_cat([L["x"] for L in self.layers])
+
+
+class GemmaBlock(Workload):
+    """Gemma4-26B-A4B-style FFN block at Q4_0, T tokens, over L layers: three
+    RMS norms of the residual stream, the dense GELU MLP, the f32 router, the
+    routed experts, and the FFN tail into the residual (qg_rmsnorm, qg_mlp,
+    qg_gemv QG_F32, qg_moe_ffn, qg_post_ffn)."""
+
+    def __init__(self, ntok, layers=16, H=2816, Fd=2112, E=128, F=704, k=8):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        t = gs.Q4_0
+        self.qg, self.ntok, self.k, self.H, self.E, self.Fd = qg, ntok, k, H, E, Fd
+        rb_h, rb_f, rb_d = gs.row_bytes(t, H), gs.row_bytes(t, F), gs.row_bytes(t, Fd)
+        rec = 2 * F * rb_h + H * rb_f
+        g = _gen(900 + ntok)
+        self.layers = []
+        vec = lambda: torch.rand(H, generator=g, device="cuda") + 0.5
+        for _ in range(layers):
+            gu = gs.device_weights(t, E * 2 * F, H, g)
+            dn = gs.device_weights(t, E * H, F, g)
+            ds = torch.rand(E, generator=g, device="cuda") * 1.5 + 0.5
+            L = dict(gu=gu, dn=dn, ds=ds, Wg=gs.device_weights(t, Fd, H, g), Wu=gs.device_weights(t, Fd, H, g),
+                     Wd=gs.device_weights(t, H, Fd, g), router=torch.randn((E, H), generator=g, device="cuda"),
+                     w_ffn=vec(), w_pre2=vec(), w_rs=vec(), w1=vec(), w2=vec(), w=vec(),
+                     os=torch.rand(1, generator=g, device="cuda") * 0.5 + 0.5, x0=gs.device_activations(ntok, H, g))
+            L["x"] = L["x0"].clone()
+            L["m"] = qg.make_moe(t, qg.QG_ACT_GELU_TANH, H, F, E, gu, 2 * F * rb_h, dn, H * rb_f, ds)
+            self.layers.append(L)
+        f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
+        self.xn, self.xm, self.rt, self.md, self.moe = (f32(ntok, H) for _ in range(5))
+        self.lg = f32(ntok, E)
+        self.ids = torch.empty((ntok, k), dtype=torch.int32, device="cuda")
+        self.w = f32(ntok, k)
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
+        self.wsm = f32(qg.qg_mlp_workspace_size(Fd, ntok) // 4)
+        self.ws = f32(qg.qg_moe_workspace_size(self.layers[0]["m"], k, ntok) // 4)
+        self.kr = 1.0 / H ** 0.5
+        uniq = []
+        for L in self.layers:
+            self.step_layer(L)
+            uniq.append(len(set(self.ids.cpu().flatten().tolist())))
+        self.reset()
+        fixed = 2 * Fd * rb_h + H * rb_d + E * H * 4 + 6 * H * 4
+        self.bytes_per_step = int(sum(uniq) / len(uniq) * rec) + fixed
+        self.dominant_bytes = self.bytes_per_step
+        self.name = ("q4_0 Gemma4-style FFN block: 3 rmsnorms, dense GELU MLP %dx%d, f32 router %dx%d, %d experts "
+                     "ff %d top-%d (down scale), FFN tail into the residual; %d token(s)" % (H, Fd, E, H, E, F, k,
+                                                                                            ntok))
+        self.dominant = self.name
+        self.key = "gemma_block_q4_0_%d_e%d_t%d" % (H, E, ntok)
+        self.period = self.dominant_period = layers
+
+    def reset(self):
+        for L in self.layers:
+            L["x"].copy_(L["x0"])
+
+    def step_layer(self, L):
+        qg, T, H = self.qg, self.ntok, self.H
+        qg.qg_rmsnorm(L["x"], L["w_ffn"], self.xn, H, T, 1e-6, 1.0)
+        qg.qg_mlp(qg.QG_Q4_0, qg.QG_ACT_GELU_TANH, L["Wg"], L["Wu"], L["Wd"], H, self.Fd, self.xn, self.md, T,
+                  self.wsm)
+        qg.qg_rmsnorm(L["x"], L["w_pre2"], self.xm, H, T, 1e-6, 1.0)
+        qg.qg_rmsnorm(L["x"], L["w_rs"], self.rt, H, T, 1e-6, self.kr)
+        qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
+        qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
+                      self.ws)
+        qg.qg_post_ffn(self.md, self.moe, L["w1"], L["w2"], L["w"], L["os"], L["x"], H, T, 1e-6)
+
+    def step(self, i):
+        self.step_layer(self.layers[i % len(self.layers)])
+
+    def output(self):
+        return torch_cat([L["x"] for L in self.layers])
+
+
+class HeadPick(Workload):
+    """The decode loop's tail, 1 token: head GEMV, optional logit soft cap,
+    greedy pick, and the picked token's (tied) embedding row gathered for the
+    next step (qg_gemv, qg_argmax, qg_embed), rotating weight copies."""
+
+    def __init__(self, t, V, H, cap, emb_scale, total_bytes, label):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        self.qg, self.t, self.V, self.H, self.cap, self.scale = qg, t, V, H, cap, emb_scale
+        wb = V * gs.row_bytes(t, H)
+        copies = max(2, int(total_bytes // wb))
+        g = _gen(1000 + t)
+        self.W = [gs.device_weights(t, V, H, g) for _ in range(copies)]
+        self.x = gs.device_activations(1, H, g)
+        self.logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+        self.idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.emb = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_argmax_workspace_size(V, 1) // 4, dtype=torch.float32, device="cuda")
+        self.bytes_per_step = wb + gs.row_bytes(t, H)
+        self.dominant_bytes = wb
+        self.name = label
+        self.dominant = "head GEMV %s %dx%d" % (gs.NAMES[t], V, H)
+        self.key = "head_pick_%s_%dx%d" % (gs.NAMES[t].lower(), V, H)
+        self.period = self.dominant_period = copies
+
+    def step(self, i):
+        qg = self.qg
+        W = self.W[i % len(self.W)]
+        qg.qg_gemv(self.t, W, self.x, self.logits, self.V, self.H, 1)
+        qg.qg_argmax(self.logits, self.V, 1, self.cap, self.idx, self.ws)
+        qg.qg_embed(self.t, W, self.V, self.H, self.idx, 1, self.scale, self.emb)
+
+    def dominant_step(self, i):
+        self.qg.qg_gemv(self.t, self.W[i % len(self.W)], self.x, self.logits, self.V, self.H, 1)
+
+    def output(self):
+        return self.emb
+
+
+def torch_cat(ts):
+    import torch
+    return torch.cat([t.flatten() for t in ts])
+
+
 def make_workload(name, copies):
     import gguf_synth as gs
     big = 1.2e9   # bytes of distinct weight copies to rotate through (> 2x the 256 MB cache)
@@ -259,13 +456,23 @@ def make_workload(name, copies):
     if name == "3b":
         return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token")
     if name == "2":
-        return MoeLayers(gs.Q8_0, 0, 2048, 768, 128, 8, 1, 8, False,
+        return MoeLayers(gs.Q8_0, 0, 2048, 768, 128, 8, 1, 16, False,
                          "q8_0 MoE layer 2048, 128 experts ff 768, top-8, 1 token")
     if name in ("4", "4t16"):
         T = 16 if name == "4t16" else 1
-        return MoeLayers(gs.Q4_0, 1, 2816, 704, 128, 8, T, 4, True,
+        return MoeLayers(gs.Q4_0, 1, 2816, 704, 128, 8, T, 16, True,
                          "q4_0 dense GELU MLP 2816x2112 + MoE layer 2816, 128 experts ff 704 (GELU, down scale), "
                          "top-8, %d token(s)" % T, dense_ff=2112)
+    if name in ("q35", "q35t16"):
+        return Qwen35Block(16 if name == "q35t16" else 1)
+    if name in ("gblk", "gblkt16"):
+        return GemmaBlock(16 if name == "gblkt16" else 1)
+    if name == "head8":
+        return HeadPick(gs.Q8_0, 151936, 2560, 0.0, 1.0, big,
+                        "q8_0 head 151936x2560 + argmax + tied embedding row, 1 token")
+    if name == "head6":
+        return HeadPick(gs.Q6_K, 262144, 2816, 30.0, float(2816 ** 0.5), big,
+                        "q6_k head 262144x2816 + soft cap 30 + argmax + scaled tied embedding row, 1 token")
     raise SystemExit("unknown config " + name)
 
 
@@ -296,9 +503,12 @@ def time_workload(wl, steps, warmup):
     rem = steps % per
     tail = _capture(wl.step, range(rem)) if rem else None
     # a replay must reproduce the eager result bit for bit
-    wl.step(per - 1)
+    wl.reset()
+    for i in range(per):
+        wl.step(i)
     torch.cuda.synchronize()
     ref = wl.output().clone()
+    wl.reset()
     full.replay()
     torch.cuda.synchronize()
     if not torch.equal(ref, wl.output()):
@@ -528,7 +738,7 @@ def main():
         cpu = wl.cpu_baseline() if hasattr(wl, "cpu_baseline") else None
     print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu)), flush=True)
     if args.all:
-        for name in ("0", "3a", "3b", "2", "4", "4t16"):
+        for name in ("0", "3a", "3b", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6"):
             if name == args.config:
                 continue
             log("[bench] workload", name)

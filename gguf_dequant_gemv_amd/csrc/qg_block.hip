@@ -25,6 +25,10 @@ QG_DEV float block_sum(float v, float *s_red) {
 
 QG_DEV float rms_factor(float ss, int64_t n, float eps) { return 1.0f / sqrtf(ss / (float)n + eps); }
 
+// Loads go out in batches of LB per thread before any of them is used, so a
+// short vector costs one memory round trip per pass instead of one per element.
+constexpr int LB = 16;
+
 // ------------------------------------------------------------- RMS norm ----
 // One workgroup per token: r = 1/sqrt(mean x^2 + eps), y = ((x r) k) w.  The
 // qwen3_moe_ssd.js rmsnorm kernel (k = 1) and gemma4_moe_ssd.js rmsnormK (the
@@ -36,9 +40,26 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w,
     const float *xt = x + (int64_t)blockIdx.x * n;
     float *yt = y + (int64_t)blockIdx.x * n;
     float ss = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) ss = fmaf(xt[i], xt[i], ss);
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+        float v[LB];
+#pragma unroll
+        for (int b = 0; b < LB; b++) v[b] = i0 + b * 256 < n ? xt[i0 + b * 256] : 0.0f;
+#pragma unroll
+        for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+    }
     const float r = rms_factor(block_sum<4>(ss, s_red), n, eps);
-    for (int64_t i = threadIdx.x; i < n; i += 256) yt[i] = ((xt[i] * r) * k) * w[i];
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+        float v[LB], g[LB];
+#pragma unroll
+        for (int b = 0; b < LB; b++) {
+            const bool in = i0 + b * 256 < n;
+            v[b] = in ? xt[i0 + b * 256] : 0.0f;
+            g[b] = in ? w[i0 + b * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < LB; b++)
+            if (i0 + b * 256 < n) yt[i0 + b * 256] = ((v[b] * r) * k) * g[b];
+    }
 }
 
 // ------------------------------------------------------------ f32 GEMV ----
@@ -50,6 +71,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w,
 template <int NT, bool V4>
 __global__ __launch_bounds__(256) void k_gemv_f32(const float *W, const float *x, float *y, int64_t rows,
                                                   int64_t cols, int ntok) {
+    // weight loads in flight per lane: all of a 2048-wide row for one token,
+    // fewer as the token count (and the x loads per weight) grows
+    constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= rows) return;   // the whole wave leaves; nothing below waits on it
@@ -58,27 +82,42 @@ __global__ __launch_bounds__(256) void k_gemv_f32(const float *W, const float *x
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.0f;
     if constexpr (V4) {
-#pragma unroll 4
-        for (int64_t c = 4 * lane; c < cols; c += 256) {
-            const float4 wv = *(const float4 *)(wr + c);
+        for (int64_t c0 = 4 * lane; c0 < cols; c0 += 256 * B) {
+            float4 wv[B];
+#pragma unroll
+            for (int b = 0; b < B; b++)
+                wv[b] = c0 + 256 * b < cols ? *(const float4 *)(wr + c0 + 256 * b) : make_float4(0, 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 if (t < ntok) {
-                    const float4 xv = *(const float4 *)(x + t * cols + c);
-                    acc[t] = fmaf(wv.x, xv.x, acc[t]);
-                    acc[t] = fmaf(wv.y, xv.y, acc[t]);
-                    acc[t] = fmaf(wv.z, xv.z, acc[t]);
-                    acc[t] = fmaf(wv.w, xv.w, acc[t]);
+                    float4 xv[B];
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        xv[b] = c0 + 256 * b < cols ? *(const float4 *)(x + t * cols + c0 + 256 * b)
+                                                    : make_float4(0, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        acc[t] = fmaf(wv[b].x, xv[b].x, acc[t]);
+                        acc[t] = fmaf(wv[b].y, xv[b].y, acc[t]);
+                        acc[t] = fmaf(wv[b].z, xv[b].z, acc[t]);
+                        acc[t] = fmaf(wv[b].w, xv[b].w, acc[t]);
+                    }
                 }
             }
         }
     } else {
-#pragma unroll 4
-        for (int64_t c = lane; c < cols; c += 64) {
-            const float wv = wr[c];
+        for (int64_t c0 = lane; c0 < cols; c0 += 64 * B) {
+            float wv[B];
 #pragma unroll
-            for (int t = 0; t < NT; t++)
-                if (t < ntok) acc[t] = fmaf(wv, x[t * cols + c], acc[t]);
+            for (int b = 0; b < B; b++) wv[b] = c0 + 64 * b < cols ? wr[c0 + 64 * b] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                if (t < ntok) {
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        if (c0 + 64 * b < cols) acc[t] = fmaf(wv[b], x[t * cols + c0 + 64 * b], acc[t]);
+                }
+            }
         }
     }
 #pragma unroll
@@ -103,25 +142,37 @@ __global__ __launch_bounds__(256) void k_combine_shared(const float *dn, const i
                                                         int64_t H, int k) {
     __shared__ float s_red[4];
     const int t = blockIdx.y;
+    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool mine = h < H;
+    const int64_t o = (int64_t)t * H + (mine ? h : 0);
+    // this thread's operands first, so their loads overlap the gate's
+    const float *q = dn + (int64_t)t * k * H + (mine ? h : 0);
+    float v[QG_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < QG_MAX_TOPK; j++) v[j] = j < k ? q[(int64_t)j * H] : 0.0f;
+    const float s_o = sh[o], r_o = resid[o];
+    const int ok = rt_valid[t];
     const float *xt = x + (int64_t)t * H;
     float p = 0.0f;
-    for (int64_t c = threadIdx.x; c < H; c += 256) p = fmaf(gate_inp[c], xt[c], p);
+    for (int64_t c0 = threadIdx.x; c0 < H; c0 += 256 * LB) {
+        float gv[LB], xv[LB];
+#pragma unroll
+        for (int b = 0; b < LB; b++) {
+            const bool in = c0 + b * 256 < H;
+            gv[b] = in ? gate_inp[c0 + b * 256] : 0.0f;
+            xv[b] = in ? xt[c0 + b * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < LB; b++) p = fmaf(gv[b], xv[b], p);
+    }
     const float sg = block_sum<4>(p, s_red);
     const float gs = 1.0f / (1.0f + expf(-sg));
-    const int64_t h = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (h >= H) return;
-    const float *q = dn + (int64_t)t * k * H + h;
+    if (!mine) return;
     float acc = 0.0f;
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = j0 + j < k ? q[(int64_t)(j0 + j) * H] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; j++)
-            if (j0 + j < k) acc += v[j];
-    }
-    const int64_t o = (int64_t)t * H + h;
-    if (rt_valid[t]) resid[o] = (acc + sh[o] * gs) + resid[o];
+    for (int j = 0; j < QG_MAX_TOPK; j++)
+        if (j < k) acc += v[j];
+    if (ok) resid[o] = (acc + s_o * gs) + r_o;
 }
 
 // ----------------------------------------------------- Gemma's FFN tail ----
@@ -139,22 +190,57 @@ __global__ __launch_bounds__(256) void k_post_ffn(const float *mlp, const float 
     const float *a = mlp + o, *b = moe + o;
     float *xt = x + o;
     float s1 = 0.0f, s2 = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-        s1 = fmaf(a[i], a[i], s1);
-        s2 = fmaf(b[i], b[i], s2);
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+        float va[LB], vb[LB];
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            const bool in = i0 + u * 256 < n;
+            va[u] = in ? a[i0 + u * 256] : 0.0f;
+            vb[u] = in ? b[i0 + u * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            s1 = fmaf(va[u], va[u], s1);
+            s2 = fmaf(vb[u], vb[u], s2);
+        }
     }
     const float r1 = rms_factor(block_sum<4>(s1, s_red), n, eps);
     const float r2 = rms_factor(block_sum<4>(s2, s_red), n, eps);
+    // v = m + e, recomputed from the same f32 operations in both passes below
+    auto vsum = [&](int64_t i0, float (&v)[LB]) {
+        float va[LB], vb[LB], g1[LB], g2[LB];
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            const bool in = i0 + u * 256 < n;
+            va[u] = in ? a[i0 + u * 256] : 0.0f;
+            vb[u] = in ? b[i0 + u * 256] : 0.0f;
+            g1[u] = in ? w1[i0 + u * 256] : 0.0f;
+            g2[u] = in ? w2[i0 + u * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < LB; u++) v[u] = (va[u] * r1) * g1[u] + (vb[u] * r2) * g2[u];
+    };
     float s3 = 0.0f;
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-        const float v = (a[i] * r1) * w1[i] + (b[i] * r2) * w2[i];
-        s3 = fmaf(v, v, s3);
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+        float v[LB];
+        vsum(i0, v);
+#pragma unroll
+        for (int u = 0; u < LB; u++) s3 = fmaf(v[u], v[u], s3);
     }
     const float r3 = rms_factor(block_sum<4>(s3, s_red), n, eps);
     const float ko = os[0];
-    for (int64_t i = threadIdx.x; i < n; i += 256) {
-        const float v = (a[i] * r1) * w1[i] + (b[i] * r2) * w2[i];
-        xt[i] = ((v * r3) * w[i] + xt[i]) * ko;
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+        float v[LB], g[LB], xv[LB];
+        vsum(i0, v);
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            const bool in = i0 + u * 256 < n;
+            g[u] = in ? w[i0 + u * 256] : 0.0f;
+            xv[u] = in ? xt[i0 + u * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < LB; u++)
+            if (i0 + u * 256 < n) xt[i0 + u * 256] = ((v[u] * r3) * g[u] + xv[u]) * ko;
     }
 }
 
@@ -218,6 +304,8 @@ QG_DEV void am_wave(float &bv, int &bi) {
 // l = tanh(clamp(l inv, -10, 10)) cap (gemma4_moe_ssd.js softcap); NaN stays
 // NaN.  Then the first index of the largest value, NaN skipped
 // (qwen3_moe_ssd.js argmax: strict greater-than, lower index on ties).
+constexpr int AB = 8;   // logits per thread per batch of loads
+
 __global__ __launch_bounds__(256) void k_argmax_part(float *l, int64_t n, int64_t span, float cap, float inv,
                                                      float *pv, int32_t *pi) {
     __shared__ float s_v[4];
@@ -227,17 +315,26 @@ __global__ __launch_bounds__(256) void k_argmax_part(float *l, int64_t n, int64_
     const int64_t hi = min(n, lo + span);
     float bv = 0.0f;
     int bi = -1;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-        float v = lt[i];
-        if (cap > 0.0f) {
-            float a = v * inv;
-            a = a < -10.0f ? -10.0f : (a > 10.0f ? 10.0f : a);
-            v = tanhf(a) * cap;
-            lt[i] = v;
-        }
-        if (v == v && (bi < 0 || v > bv)) {
-            bv = v;
-            bi = (int)i;
+    for (int64_t i0 = lo + threadIdx.x; i0 < hi; i0 += 256 * AB) {
+        float v[AB];
+#pragma unroll
+        for (int u = 0; u < AB; u++) v[u] = i0 + u * 256 < hi ? lt[i0 + u * 256] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < AB; u++) {
+            const int64_t i = i0 + u * 256;
+            if (i >= hi) continue;
+            float e = v[u];
+            if (cap > 0.0f) {
+                float z = e * inv;
+                z = z < -10.0f ? -10.0f : (z > 10.0f ? 10.0f : z);
+                e = tanhf(z) * cap;
+                lt[i] = e;
+            }
+            // indices rise within a thread, so strict > keeps the first of equal values
+            if (e == e && (bi < 0 || e > bv)) {
+                bv = e;
+                bi = (int)i;
+            }
         }
     }
     am_wave(bv, bi);
@@ -259,7 +356,16 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float *pv, const int3
     const int t = blockIdx.x, lane = threadIdx.x;
     float bv = 0.0f;
     int bi = -1;
-    for (int g = lane; g < G; g += 64) am_merge(bv, bi, pv[(int64_t)t * G + g], pi[(int64_t)t * G + g]);
+    float v[ARGMAX_MAX_PARTS / 64];
+    int ix[ARGMAX_MAX_PARTS / 64];
+#pragma unroll
+    for (int u = 0; u < ARGMAX_MAX_PARTS / 64; u++) {
+        const int g = lane + 64 * u;
+        v[u] = g < G ? pv[(int64_t)t * G + g] : 0.0f;
+        ix[u] = g < G ? pi[(int64_t)t * G + g] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < ARGMAX_MAX_PARTS / 64; u++) am_merge(bv, bi, v[u], ix[u]);
     am_wave(bv, bi);
     if (lane == 0) idx[t] = bi < 0 ? 0 : bi;
 }
