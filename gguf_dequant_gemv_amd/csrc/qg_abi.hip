@@ -68,6 +68,7 @@ struct Plan {
     int depth;           // UK_LDS: stages in flight per wave
     bool valu_heavy;     // K-quant units: decode-bound rather than HBM-bound
     int ring_off;        // UK_LDS: byte offset of the stage rings in LDS
+    int xchunk;          // UK_LDS: row elements per staged x chunk (0: all of x)
     size_t lds;
 };
 
@@ -110,6 +111,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
         p.valu_heavy = false;
         p.lds = 0;
         p.ntiles = 0;     // set at launch (gated tiles hold half the rows)
+        p.xchunk = 0;
         return p;
     }
     int nt = 1;
@@ -157,6 +159,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
     p.lds = lds_bytes(s.type, cpad, nt);
     p.depth = 0;
     p.ring_off = 0;
+    p.xchunk = 0;
     p.valu_heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
     if (lds_kind(p.kind)) {
         // stage rings after x: two stages per wave when two workgroups still
@@ -171,6 +174,25 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
         p.depth = 1;
         if (tiles_all > 4 * NUM_CU && p.ring_off + 2 * per_depth <= 80 * 1024) p.depth = 2;
         p.lds = p.ring_off + p.depth * per_depth;
+        // x too wide for two workgroups per CU while the tiles need more than
+        // one round at one per CU: stage x in chunks of whole row elements,
+        // the widest that still lets two fit (each chunk is restaged per tile
+        // row from the L2, which costs more than it gains when one round
+        // holds every tile anyway)
+        const int K = (p.nunits + p.lpr - 1) / p.lpr;
+        if (p.lds > 80 * 1024 && K >= 2 && tiles_all > NUM_CU) {
+            for (int jc = K - 1; jc >= 1; jc--) {
+                const int cp = (p.nunits < jc * p.lpr ? p.nunits : jc * p.lpr) * uv;
+                const size_t xl = lds_bytes(s.type, cp, nt);
+                const int roff = (int)((xl + 255) & ~(size_t)255);
+                if (roff + p.depth * per_depth <= 80 * 1024) {
+                    p.xchunk = jc;
+                    p.ring_off = roff;
+                    p.lds = roff + p.depth * per_depth;
+                    break;
+                }
+            }
+        }
     }
     const int64_t tile_rows = 4LL * (64 / p.lpr);
     p.ntiles = (int)((s.rows + tile_rows - 1) / tile_rows);
@@ -276,6 +298,7 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     a.ntiles = p.ntiles;
     a.depth = p.depth;
     a.ring_off = p.ring_off;
+    a.xchunk = p.xchunk;
     gemv_fn f = pick(s.type, p);
     if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
         return QG_EHIP;

@@ -76,6 +76,9 @@ struct GemvArgs {
     int depth;
     int ring_off;
     int ntiles;        // row tiles of 4*RPW rows
+    // k_gemv_lds: x is staged in chunks of this many row elements (units of
+    // L lanes), restaged as each tile row reaches the next chunk; 0 = all of x
+    int xchunk;
 };
 
 // -------------------------------------------------------- unit dot product --
@@ -217,12 +220,14 @@ QG_DEV void x_put(const f32x4 (&v)[XB], int base0, int n4, int c4, float *xt, fl
 }
 
 // Scalar path (unaligned x): element by element, then the sums from LDS.
+// Columns [c0, c0 + cpad) of x land at xs[xpad(0..cpad)], zero past cols.
 template <int NT, int SUMS>
 QG_DEV void stage_x_scalar(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride,
-                           float *ss, int nsum) {
+                           float *ss, int nsum, int c0 = 0) {
     for (int t = 0; t < NT; t++) {
         const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
-        for (int c = threadIdx.x; c < cpad; c += 256) xs[t * xstride + xpad(c)] = c < cols ? src[c] : 0.0f;
+        for (int c = threadIdx.x; c < cpad; c += 256)
+            xs[t * xstride + xpad(c)] = c0 + c < cols ? src[c0 + c] : 0.0f;
     }
     if constexpr (SUMS != 0) {
         __syncthreads();
@@ -617,16 +622,38 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         }
     };
 
-    // ---- x: the first batch goes out before the weights ----
+    // ---- x, staged whole or in chunks of JC row elements (JC*L units) ----
     const int cols = a.cols;
-    const int cpad = a.nunits * UV;
+    const int JC = a.xchunk > 0 ? a.xchunk : K;
+    const int NCH = (K + JC - 1) / JC;
+    const int ccols = JC * L * UV;                      // columns per chunk
+    const int cpad = min(a.nunits, JC * L) * UV;        // staged span (the widest chunk)
     const int xstride = xstride_of(cpad);
     const int nsum = SUMS ? cpad / SUMS : 0;
-    const int n4 = cpad >> 2, c4 = cols >> 2;
     float *xs = lds;
     float *ss = lds + NT * xstride;
     f32x4 xv[XB];
-    if (a.x_vec) x_load(a.x + (int64_t)in_idx[0] * a.x_stride, 0, c4, xv);
+    // chunk ch: columns [ch*ccols, +cw) of the padded row, valid below cols
+    // (the LDS kinds' padded width equals cols, so every chunk has valid x)
+    auto chunk_w = [&](int ch) { return min(ccols, a.nunits * UV - ch * ccols); };
+    auto stage = [&](int ch, bool first_loaded) {
+        const int c0 = ch * ccols, cw = chunk_w(ch);
+        const int n4 = cw >> 2, c4 = min(cols - c0, cw) >> 2;
+        if (a.x_vec) {
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                const float *src = a.x + (int64_t)in_idx[t] * a.x_stride + c0;
+                for (int base0 = 0; base0 < n4; base0 += 256 * XB) {
+                    if (!first_loaded || t != 0 || base0 != 0) x_load(src, base0, c4, xv);
+                    x_put<SUMS>(xv, base0, n4, c4, xs + t * xstride, ss + t * nsum);
+                }
+            }
+        } else {
+            stage_x_scalar<NT, SUMS>(a, in_idx, cols, cw, xs, xstride, ss, nsum, c0);
+        }
+    };
+    // the first batch of x goes out before the weights
+    if (a.x_vec) x_load(a.x + (int64_t)in_idx[0] * a.x_stride, 0, min(cols, chunk_w(0)) >> 2, xv);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- the first `depth` stages ----
@@ -639,19 +666,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- the rest of x, and the group sums ----
-    if (a.x_vec) {
-#pragma unroll
-        for (int t = 0; t < NT; t++) {
-            const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
-            for (int base0 = 0; base0 < n4; base0 += 256 * XB) {
-                if (t != 0 || base0 != 0) x_load(src, base0, c4, xv);
-                x_put<SUMS>(xv, base0, n4, c4, xs + t * xstride, ss + t * nsum);
-            }
-        }
-    } else {
-        stage_x_scalar<NT, SUMS>(a, in_idx, cols, cpad, xs, xstride, ss, nsum);
-    }
+    // ---- the rest of the first chunk, and its group sums ----
+    stage(0, true);
     __syncthreads();
 
     float acc[NT], gate[NT];
@@ -660,6 +676,15 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     int cp = 0, cj = 0;          // element being consumed
     for (int s = 0; s < S; s++) {
         const int slot = s % D;
+        const int jm = cj >= K ? cj - K : cj;      // the element's place in its row
+        if (NCH > 1 && s > 0 && jm % JC == 0) {
+            // every wave has finished with the previous chunk (all waves walk
+            // the same element sequence, so they all meet here)
+            __syncthreads();
+            stage(jm / JC, false);
+            __syncthreads();
+        }
+        const int ub = (jm / JC) * JC * L;         // first unit of the staged chunk
         // stage s has landed once no more than the later issued ones are in flight
         wait_stages<G::NI>(min(D - 1, S - 1 - s));
         u32 wd[U::ND];
@@ -683,18 +708,19 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
         const int64_t r0 = (tile * 4 + wave) * RPW;
-        const int u = sub + (cj >= K ? cj - K : cj) * L;
+        const int u = sub + jm * L;
+        const int ul = u - ub;                     // its place in the staged chunk
         if constexpr (NT == 1 && UV <= 64) {
             // one token, 64-value units: all the unit's x reads go out at once
-            const float *xp = xs + xpad(min(u, a.nunits - 1) * UV);
+            const float *xp = xs + xpad((min(u, a.nunits - 1) - ub) * UV);
             f32x4 xr[UV / 4];
 #pragma unroll
             for (int q = 0; q < UV / 4; q++) xr[q] = *(const f32x4 *)(xp + 4 * q);
-            if (u < a.nunits) unit_dot_x<U>(wd, xr, ss + u * SPU, acc[0]);
+            if (u < a.nunits) unit_dot_x<U>(wd, xr, ss + ul * SPU, acc[0]);
         } else if constexpr (NT == 1 && U::GROUPS > 2) {
-            if (u < a.nunits) unit_dot_pf<U>(wd, xs + xpad(u * UV), ss + u * SPU, acc[0]);
+            if (u < a.nunits) unit_dot_pf<U>(wd, xs + xpad(ul * UV), ss + ul * SPU, acc[0]);
         } else {
-            if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(u * UV), xstride, ss + u * SPU, nsum, acc);
+            if (u < a.nunits) unit_dot<U, NT>(wd, xs + xpad(ul * UV), xstride, ss + ul * SPU, nsum, acc);
         }
         ++cj;
         if (a.glu && cj == K) {   // gate half done: keep its row sums

@@ -97,3 +97,40 @@ def test_kquant_gemv_full(orc, which):
     yr, A = orc.gemv(t, W, x, rows, cols, 1, row_idx=ri)
     check_rows(y[:, ri], yr, A, which)
     assert np.isfinite(y).all()
+
+
+def test_mlp_gate_up_x_chunks(orc):
+    """A gated launch whose x (24576 wide) is staged in chunks and whose row
+    tiles need more than one round: every tile row walks the chunks twice
+    (gate rows, then up rows).  Sampled gate / up rows, every activation, and
+    sampled down rows fed the GPU's activations."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    t, H, F = gs.Q8_0, 24576, 4128
+    g = gs.rng(31)
+    Wg, Wu, Wd = gs.weights(t, g, F, H), gs.weights(t, g, F, H), gs.weights(t, g, H, F)
+    x = gs.activations(g, 1, H)
+    say("mlp x chunks", H, F)
+    tg, tu, td = dev(Wg)[0], dev(Wu)[0], dev(Wd)[0]
+    xt, _ = dev(x)
+    y = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+    qg.qg_mlp(t, qg.QG_ACT_SILU, tg, tu, td, H, F, xt, y, 1, ws)
+    wsh = host(ws)
+    gu = wsh[:2 * F].reshape(1, 2 * F)
+    a0 = _align256(2 * F * 4) // 4
+    act = wsh[a0:a0 + F].reshape(1, F)
+    ri = sample_rows(gs.rng(32), F, 300)
+    yg, Ag = orc.gemv(t, Wg, x, F, H, 1, row_idx=ri)
+    yu, Au = orc.gemv(t, Wu, x, F, H, 1, row_idx=ri)
+    check_rows(gu[:, ri], yg, Ag, "gate rows")
+    check_rows(gu[:, F + ri], yu, Au, "up rows")
+    check_act(orc, 0, gu, act, F, "silu(g)*u")
+    # down rows on the GPU's activation, with the activation's rounding term
+    rd = sample_rows(gs.rng(33), H, 300)
+    yd, Ad = orc.gemv(t, Wd, act, H, F, 1, row_idx=rd)
+    rb = gs.row_bytes(t, F)
+    gabs = np.abs(gu[0, :F].astype(np.float64) * gu[0, F:].astype(np.float64))
+    R = np.array([np.abs(orc.dequant(t, Wd[r * rb:(r + 1) * rb] if Wd.ndim == 1 else Wd[r], F)) @ gabs for r in rd])
+    err = np.abs(host(y)[0, rd] - yd[0])
+    assert np.all(err <= TOL * Ad[0] + 1e-6 * R), "down rows: worst err/A %.3g" % (err / Ad[0]).max()

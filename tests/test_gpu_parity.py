@@ -123,6 +123,36 @@ def test_gemv_parity(orc, t, rows, nbk, ntok, off):
     check_rows(y, y_ref, A, "gemv %s %dx%d T=%d" % (gs.NAMES[t], rows, cols, ntok))
 
 
+# x wider than two workgroups' share of LDS, with more row tiles than one
+# round at one workgroup per CU holds, is staged in chunks of whole row
+# elements (restaged per tile row): T = 1 and 2, aligned and 2-byte-offset
+# weights, ragged last tiles; sampled rows plus the first and last 40
+XCHUNK_CASES = [
+    (gs.Q6_K, 8300, 17408, 1, 0), (gs.Q6_K, 8310, 17408, 2, 2), (gs.Q4_K, 16500, 20480, 1, 0),
+    (gs.Q8_0, 4100, 32768, 1, 0), (gs.Q8_0, 4110, 24576, 2, 2), (gs.Q4_0, 4105, 40960, 1, 2),
+]
+
+
+def _sample(g, rows, n):
+    idx = set(g.choice(rows, size=min(n, rows), replace=False).tolist())
+    idx.update(range(40))
+    idx.update(range(rows - 40, rows))
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("t,rows,cols,ntok,off", XCHUNK_CASES)
+def test_gemv_x_chunks(orc, t, rows, cols, ntok, off):
+    g = gs.rng(2500 + t + rows + ntok)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, ntok, cols)
+    say("gemv x chunks", gs.NAMES[t], rows, cols, "T", ntok, "offset", off)
+    y = gpu_gemv(t, W, x, rows, cols, ntok, off)
+    ri = _sample(g, rows, 400)
+    y_ref, A = orc.gemv(t, W, x, rows, cols, ntok, row_idx=ri)
+    check_rows(y[:, ri], y_ref, A, "gemv x chunks %s %dx%d T=%d" % (gs.NAMES[t], rows, cols, ntok))
+    assert np.isfinite(y).all()
+
+
 @pytest.mark.parametrize("t", TYPES)
 def test_gemv_scaling_property(t):
     """y(2x) = 2 y(x) bitwise: the kernels' arithmetic commutes with an exact
@@ -159,7 +189,9 @@ def test_router_parity(orc, E, k, T):
 # --------------------------------------------------------------- dense MLP --
 @pytest.mark.parametrize("t,act,H,F,T", [(gs.Q8_0, 0, 256, 320, 1), (gs.Q4_0, 1, 320, 224, 3),
                                          (gs.Q4_K, 0, 512, 768, 2), (gs.Q6_K, 1, 768, 512, 16),
-                                         (gs.Q4_0, 1, 2816, 2112, 16), (gs.Q4_0, 1, 2816, 2112, 1)])
+                                         (gs.Q4_0, 1, 2816, 2112, 16), (gs.Q4_0, 1, 2816, 2112, 1),
+                                         # x too wide for LDS beside two workgroups' stages
+                                         (gs.Q6_K, 0, 17408, 256, 1), (gs.Q8_0, 1, 24576, 96, 1)])
 def test_mlp_stagewise(orc, t, act, H, F, T):
     import gguf_dequant_gemv_amd as qg
     torch = _torch()
