@@ -22,6 +22,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix rate, published
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(HERE, "profiles")
 CSRC = os.path.join(HERE, "gguf_dequant_gemv_amd", "csrc")
@@ -37,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="1",
-                    help="0, 1, 2, 3a, 3b, 4, 4t16; whole FFN blocks q35, q35t16, gblk, gblkt16; heads head8, head6")
+                    help="0, 1, 2, 3a, 3b, 4, 4t16; whole FFN blocks q35, q35t16, gblk, gblkt16; heads head8, "
+                         "head6; prefill chunks p64, p256")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
@@ -439,6 +441,45 @@ class HeadPick(Workload):
         return self.emb
 
 
+class PrefillMlp(Workload):
+    """The dense Qwen3-style MLP (hidden 2560, ff 9728, Q8_0) over a prompt
+    chunk of T tokens (qg_mlp: gate||up with SwiGLU, then down), rotating
+    weight copies.  Compute-bound from about 64 tokens: its roofline is the
+    matrix cores' bf16 rate, counted in the contraction's own flops
+    (2 * rows * cols * T per projection; the kernels spend three bf16 MFMAs
+    per product for exactness)."""
+
+    def __init__(self, ntok, H=2560, F=9728, copies=4):
+        import torch
+        import gguf_synth as gs
+        import gguf_dequant_gemv_amd as qg
+        self.qg, self.H, self.F, self.ntok = qg, H, F, ntok
+        g = _gen(1100 + ntok)
+        self.sets = [dict(Wg=gs.device_weights(gs.Q8_0, F, H, g), Wu=gs.device_weights(gs.Q8_0, F, H, g),
+                          Wd=gs.device_weights(gs.Q8_0, H, F, g)) for _ in range(copies)]
+        self.x = gs.device_activations(ntok, H, g)
+        self.y = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_mlp_workspace_size(F, ntok) // 4, dtype=torch.float32, device="cuda")
+        rb = gs.row_bytes(gs.Q8_0, H)
+        self.bytes_per_step = 2 * F * rb + H * gs.row_bytes(gs.Q8_0, F)
+        self.flops_per_step = 2.0 * 3 * H * F * ntok
+        self.dominant_bytes = self.bytes_per_step
+        self.name = "q8_0 dense MLP prefill chunk 2560x9728 (gate||up, SwiGLU, down), %d tokens" % ntok
+        self.dominant = self.name
+        self.key = "prefill_mlp_q8_0_2560x9728_t%d" % ntok
+        self.period = self.dominant_period = copies
+        self.roof = "mfma"
+
+    def step(self, i):
+        s = self.sets[i % len(self.sets)]
+        qg = self.qg
+        qg.qg_mlp(qg.QG_Q8_0, qg.QG_ACT_SILU, s["Wg"], s["Wu"], s["Wd"], self.H, self.F, self.x, self.y, self.ntok,
+                  self.ws)
+
+    def output(self):
+        return self.y
+
+
 def torch_cat(ts):
     import torch
     return torch.cat([t.flatten() for t in ts])
@@ -467,6 +508,8 @@ def make_workload(name, copies):
         return Qwen35Block(16 if name == "q35t16" else 1)
     if name in ("gblk", "gblkt16"):
         return GemmaBlock(16 if name == "gblkt16" else 1)
+    if name in ("p64", "p256"):
+        return PrefillMlp(int(name[1:]))
     if name == "head8":
         return HeadPick(gs.Q8_0, 151936, 2560, 0.0, 1.0, big,
                         "q8_0 head 151936x2560 + argmax + tied embedding row, 1 token")
@@ -686,6 +729,11 @@ def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
                      "kernel": wl.dominant, "bytes_per_launch": wl.dominant_bytes,
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
     }
+    if getattr(wl, "roof", "hbm") == "mfma":
+        tf = wl.flops_per_step / (dom_ms * 1e-3) / 1e12
+        out["roofline"].update(bound="mfma", achieved=round(tf, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                               frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), flops_per_launch=wl.flops_per_step)
+        out["config"]["tokens_per_s"] = round(wl.ntok / (ms * 1e-3), 1)
     if cpu is not None:
         out["cpu_baseline"] = cpu
     return out
@@ -738,7 +786,8 @@ def main():
         cpu = wl.cpu_baseline() if hasattr(wl, "cpu_baseline") else None
     print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu)), flush=True)
     if args.all:
-        for name in ("0", "3a", "3b", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6"):
+        for name in ("0", "3a", "3b", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6",
+                     "p64", "p256"):
             if name == args.config:
                 continue
             log("[bench] workload", name)

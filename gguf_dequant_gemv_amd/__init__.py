@@ -12,13 +12,13 @@ import os
 QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
-QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK = 16, 256, 32
+QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL = 16, 256, 32, 4096
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemv.so")
 
 # Every symbol include/qgemv.h declares.
-EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_dequant",
+EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm", "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_rmsnorm", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
@@ -58,6 +58,7 @@ def lib():
         L.qg_strerror.argtypes = [i32]
         L.qg_strerror.restype = ctypes.c_char_p
         L.qg_gemv.argtypes = [i32, P, P, P, i64, i64, i32, P]
+        L.qg_gemm.argtypes = [i32, P, P, P, i64, i64, i32, P]
         L.qg_dequant.argtypes = [i32, P, P, i64, i64, P]
         L.qg_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
         L.qg_mlp_workspace_size.argtypes = [i64, i32]
@@ -118,6 +119,10 @@ def qg_block_bytes(t):
 
 def qg_gemv(type, W, x, y, rows, cols, ntok=1, stream=None):
     _check("qg_gemv", lib().qg_gemv(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _stream(stream)))
+
+
+def qg_gemm(type, W, x, y, rows, cols, ntok, stream=None):
+    _check("qg_gemm", lib().qg_gemm(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _stream(stream)))
 
 
 def qg_dequant(type, W, out, rows, cols, stream=None):

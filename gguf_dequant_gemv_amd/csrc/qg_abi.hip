@@ -271,6 +271,21 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
     a.nunits = p.nunits;
+    if (!a.grp && a.ntok > QG_MAX_TOKENS && a.x_vec) {
+        // prefill chunk: 64-token tiles, each weight block feeding every token
+        // group of the tile (x read in 16-byte pieces; other x layouts take
+        // the 16-token kernel below, chunk by chunk)
+        const int tt = gemm_token_tile();
+        const int64_t tchunks = (a.ntok + tt - 1) / tt;
+        const int64_t tile_rows = 4 * gemm_rows_per_wave(a.glu);
+        a.ntiles = (int)((a.rows + tile_rows - 1) / tile_rows);
+        gemv_fn f = gemm_kernel_mfma(s.type);
+        int64_t cap = resident_wgs(f, 0) / tchunks;
+        if (cap < 1) cap = 1;
+        grid = dim3((unsigned)(a.ntiles < cap ? a.ntiles : cap), (unsigned)tchunks, 1);
+        hipLaunchKernelGGL(f, grid, dim3(256), 0, st, a);
+        return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+    }
     // four groups of 16 rows per tile, or two when that leaves too few tiles
     // to spread over the CUs
     int groups = 4;
@@ -336,17 +351,28 @@ const char *qg_strerror(int code) {
     }
 }
 
-int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
+}  // extern "C"
+
+namespace {
+// qg_gemv / qg_gemm: the same sum for up to max_tok tokens
+int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
+               void *stream) {
     if (type == QG_F32) {   // plain f32 weights (router, shared-expert gate)
         if (rows <= 0 || cols <= 0) return QG_EINVAL;
-        if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+        if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
         if (!W || !x || !y || !aligned(W, 4) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
-        return launch_gemv_f32((const float *)W, x, y, rows, cols, ntok, (hipStream_t)stream);
+        for (int t0 = 0; t0 < ntok; t0 += QG_MAX_TOKENS) {   // the f32 kernel serves 16 tokens a launch
+            const int nt = ntok - t0 < QG_MAX_TOKENS ? ntok - t0 : QG_MAX_TOKENS;
+            const int rc = launch_gemv_f32((const float *)W, x + (int64_t)t0 * cols, y + (int64_t)t0 * rows, rows,
+                                           cols, nt, (hipStream_t)stream);
+            if (rc) return rc;
+        }
+        return QG_OK;
     }
     Shape s;
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
-    if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+    if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
     // rows in launches of at most MAX_RANGE weight bytes each
     const int64_t chunk = MAX_RANGE / s.row_bytes;
@@ -367,6 +393,17 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
         if (rc) return rc;
     }
     return QG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
+    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_TOKENS, stream);
+}
+
+int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
+    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_PREFILL, stream);
 }
 
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
@@ -395,7 +432,7 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
 
 // Workspace of qg_mlp: gu [ntok][2ff] f32 at offset 0, then act [ntok][ff].
 size_t qg_mlp_workspace_size(int64_t ff, int ntok) {
-    if (ff <= 0 || ntok < 1 || ntok > QG_MAX_TOKENS) return 0;
+    if (ff <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
     return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float));
 }
 
@@ -406,7 +443,7 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     if (rc) return rc;
     rc = make_shape(type, hidden, ff, s_dn);
     if (rc) return rc;
-    if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+    if (ntok < 1 || ntok > QG_MAX_PREFILL) return QG_ELIMIT;
     if (act != QG_ACT_SILU && act != QG_ACT_GELU_TANH) return QG_EINVAL;
     if (!W_gate || !W_up || !W_down || !x || !y || !workspace) return QG_EINVAL;
     if (!aligned(W_gate, 2) || !aligned(W_up, 2) || !aligned(W_down, 2) || !aligned(x, 4) || !aligned(y, 4) ||

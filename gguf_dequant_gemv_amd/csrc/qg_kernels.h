@@ -1057,6 +1057,12 @@ QG_DECL_GEMV(q6_k)
 dequant_fn dequant_kernel(int type);
 // MFMA small-batch kernels (Q8_0 / Q4_0), qg_inst_mfma.hip
 gemv_fn gemv_kernel_mfma(int type, int groups);
+// prefill chunks (qg_gemm.hip): Q8_0 / Q4_0; a tile is 4 waves of
+// gemm_rows_per_wave(glu) rows (gated: that many gate rows and the same up
+// rows) by gemm_token_tile() tokens
+gemv_fn gemm_kernel_mfma(int type);
+int gemm_rows_per_wave(int glu);
+int gemm_token_tile();
 
 // Router / grouping and combine kernels (qg_route.hip).
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,

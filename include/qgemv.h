@@ -68,6 +68,7 @@ enum qg_err {
 };
 
 #define QG_MAX_TOKENS 16    /* small-batch (speculative verify) limit          */
+#define QG_MAX_PREFILL 4096 /* prefill chunk limit of qg_gemm and qg_mlp       */
 #define QG_MAX_EXPERTS 256  /* router width limit ([qwen3] engine: n <= 256)    */
 #define QG_MAX_TOPK 32      /* picks per token limit ([qwen3] engine: k <= 32)  */
 
@@ -93,6 +94,15 @@ const char *qg_strerror(int code);
  * Errors: QG_EINVAL (type, rows<=0, cols<=0 or cols % QK, null pointer, W not
  * 2-byte aligned, x/y not 4-byte aligned), QG_ELIMIT (ntok outside 1..16). */
 int qg_gemv(int type, const void *W, const float *x, float *y,
+            int64_t rows, int64_t cols, int ntok, void *stream);
+
+/* Prefill-size product: the same sum as qg_gemv for a chunk of up to
+ * QG_MAX_PREFILL tokens ([qwen35] / [gemma4] WGSL matmulQ8T / matmulQ4T, the
+ * tiled prompt-chunk GEMMs).  Q8_0 / Q4_0 run on the matrix cores with every
+ * product exact (codes and three bf16 parts of x); the K-quants and f32 run
+ * on the vector kernels in chunks of tokens.  Arguments and errors as
+ * qg_gemv, with QG_ELIMIT for ntok outside 1..QG_MAX_PREFILL. */
+int qg_gemm(int type, const void *W, const float *x, float *y,
             int64_t rows, int64_t cols, int ntok, void *stream);
 
 /* Dequantize a whole tensor: out[r][c] = W[r][c] as f32, bit-exact (each
@@ -123,7 +133,8 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
  * [dense] encodeLayer (gate and up into the two halves of one buffer, siluMul,
  * down); [gemma4] dense GELU MLP (geglu).
  * W_gate, W_up: ff x hidden; W_down: hidden x ff (same block type).
- * x: [ntok][hidden], y: [ntok][hidden].
+ * x: [ntok][hidden], y: [ntok][hidden]; 1 <= ntok <= QG_MAX_PREFILL (a
+ * decode step, a verify batch or a prefill chunk).
  * workspace: device scratch of at least qg_mlp_workspace_size(ff, ntok) bytes,
  * 256-byte aligned.  After the call it holds gu as [ntok][2*ff] f32 at offset 0
  * and a as [ntok][ff] f32 after it (at the next 256-byte boundary):

@@ -166,3 +166,14 @@ def test_moe_shared_rejects_and_sizes():
     assert call(qg.qg_shared_expert(8, 512, FAKE, FAKE, FAKE, None)) == qg.QG_EINVAL   # no gate row
     assert L.qg_moe_ffn_shared(ctypes.byref(m), None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, FAKE, ws,
                                None) == qg.QG_EINVAL
+
+
+def test_gemm_token_limits():
+    L = qg.lib()
+    assert L.qg_gemv(8, FAKE, FAKE, FAKE, 16, 64, 17, None) == qg.QG_ELIMIT
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, qg.QG_MAX_PREFILL + 1, None) == qg.QG_ELIMIT
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, 0, None) == qg.QG_ELIMIT
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 48, 64, None) == qg.QG_EINVAL     # cols % 32
+    assert L.qg_gemm(0, FAKE + 2, FAKE, FAKE, 16, 64, 64, None) == qg.QG_EINVAL  # f32 W misaligned
+    assert qg.qg_mlp_workspace_size(9728, 256) == 256 * 2 * 9728 * 4 + 256 * 9728 * 4
+    assert qg.qg_mlp_workspace_size(9728, qg.QG_MAX_PREFILL + 1) == 0

@@ -1,0 +1,94 @@
+"""GPU parity of prefill-size products (qg_gemm, and qg_mlp over a prompt
+chunk) against the f64 oracle: T = 17..256 tokens, every block type and f32,
+ragged row tiles and token chunks, 2-byte-offset weights; the bar is the same
+|y - y_ref| <= 1e-5 * sum |W x| per row and token."""
+import numpy as np
+import pytest
+
+import gguf_synth as gs
+from test_gpu_parity import TOL, _align256, _torch, check_act, check_rows, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [gs.Q8_0, gs.Q4_0, gs.Q4_K, gs.Q6_K]
+
+
+def gpu_gemm(t, W, x, rows, cols, ntok, w_offset=0):
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    Wt, Wp = dev(W, w_offset)
+    xt, _ = dev(x.astype(np.float32))
+    y = torch.full((ntok, rows), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qg_gemm(t, Wp, xt, y, rows, cols, ntok)
+    return host(y)
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("rows,nbk,ntok,off", [(300, 32, 17, 0), (129, 24, 64, 2), (257, 16, 100, 0),
+                                               (70, 40, 256, 0), (33, 8, 40, 2)])
+def test_gemm_parity(orc, t, rows, nbk, ntok, off):
+    if t in (gs.Q4_K, gs.Q6_K):
+        nbk = max(1, nbk // 8)
+    cols = nbk * gs.QK[t]
+    g = gs.rng(8000 + 31 * t + rows + ntok)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, ntok, cols)
+    say("gemm", gs.NAMES[t], rows, cols, "T", ntok, "offset", off)
+    y = gpu_gemm(t, W, x, rows, cols, ntok, off)
+    y_ref, A = orc.gemv(t, W, x, rows, cols, ntok)
+    check_rows(y, y_ref, A, "gemm %s %dx%d T=%d" % (gs.NAMES[t], rows, cols, ntok))
+
+
+@pytest.mark.parametrize("rows,cols,ntok", [(130, 2048, 40), (256, 2816, 256)])
+def test_gemm_f32(orc, rows, cols, ntok):
+    g = gs.rng(8100 + ntok)
+    W = gs.f32_matrix(g, rows, cols, 0.02)
+    x = gs.activations(g, ntok, cols)
+    say("gemm f32", rows, cols, "T", ntok)
+    y = gpu_gemm(0, W.view(np.uint8), x, rows, cols, ntok)
+    y_ref, A = orc.gemv(orc.F32, W.view(np.uint8), x, rows, cols, ntok)
+    check_rows(y, y_ref, A, "gemm f32")
+
+
+@pytest.mark.parametrize("t,act,H,F,T", [(gs.Q8_0, 0, 512, 768, 64), (gs.Q4_0, 1, 704, 448, 33),
+                                         (gs.Q4_K, 0, 512, 512, 24)])
+def test_mlp_prefill_stagewise(orc, t, act, H, F, T):
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    g = gs.rng(8200 + t + T)
+    Wg, Wu, Wd = gs.weights(t, g, F, H), gs.weights(t, g, F, H), gs.weights(t, g, H, F)
+    x = gs.activations(g, T, H)
+    say("mlp prefill", gs.NAMES[t], H, F, "T", T)
+    tg, tu, td = dev(Wg)[0], dev(Wu)[0], dev(Wd)[0]
+    xt, _ = dev(x)
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(F, T) // 4, dtype=torch.float32, device="cuda")
+    qg.qg_mlp(t, act, tg, tu, td, H, F, xt, y, T, ws)
+    wsh = host(ws)
+    gu = wsh[:T * 2 * F].reshape(T, 2 * F)
+    a0 = _align256(T * 2 * F * 4) // 4
+    check_act(orc, act, gu, wsh[a0:a0 + T * F].reshape(T, F), F, "prefill act")
+    yg, Ag = orc.gemv(t, Wg, x, F, H, T)
+    yu, Au = orc.gemv(t, Wu, x, F, H, T)
+    check_rows(gu, np.concatenate([yg, yu], 1), np.concatenate([Ag, Au], 1), "prefill gate||up")
+    yh = host(y)
+    Wabs = np.abs(orc.dequant(t, Wd, H * F).reshape(H, F))
+    for tt in range(T):
+        yd, Ad = orc.gemv_f64(t, Wd, orc.glu(act, gu[tt], F), H, F)
+        R = Wabs @ np.abs(gu[tt, :F].astype(np.float64) * gu[tt, F:].astype(np.float64))
+        assert np.all(np.abs(yh[tt] - yd) <= TOL * Ad + 1e-6 * R), "prefill down token %d" % tt
+
+
+def test_gemm_full_size_dense_256(orc):
+    """The dense gate projection at a 256-token prefill chunk, Q8_0 9728 x 2560:
+    sampled rows, every token."""
+    t, rows, cols, T = gs.Q8_0, 9728, 2560, 256
+    g = gs.rng(8300)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, T, cols)
+    say("gemm full size", rows, cols, "T", T)
+    y = gpu_gemm(t, W, x, rows, cols, T)
+    ri = np.array(sorted(set(g.choice(rows, 96, replace=False).tolist()) | {0, rows - 1}), np.int64)
+    y_ref, A = orc.gemv(t, W, x, rows, cols, T, row_idx=ri)
+    check_rows(y[:, ri], y_ref, A, "gemm 9728x2560 T=256")
+    assert np.isfinite(y).all()
