@@ -251,8 +251,10 @@ int grid_for(const Plan &p, gemv_fn f) {
 }
 
 #define QG_PICK_NT(NAME) \
-    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.kind, p.lpr) : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.kind, p.lpr) \
-     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.kind, p.lpr) : gemv_kernel_##NAME##_t8(p.kind, p.lpr))
+    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.kind, p.lpr, p.xchunk > 0) \
+     : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.kind, p.lpr, p.xchunk > 0) \
+     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.kind, p.lpr, p.xchunk > 0) \
+     : gemv_kernel_##NAME##_t8(p.kind, p.lpr, p.xchunk > 0))
 
 gemv_fn pick(int type, const Plan &p) {
     switch (type) {

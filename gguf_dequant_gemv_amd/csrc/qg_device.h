@@ -110,6 +110,59 @@ QG_DEV float wave_sum(float v) {
     return (a + b) + (c + d);
 }
 
+// LDS accesses the compiler does not see as memory operations.  Seen, every
+// LDS read or write issued while buffer-to-LDS copies are in flight would
+// wait for all of them (the compiler cannot tell which bytes a copy lands
+// in), which undoes the copies' lead.  The kernel waits itself: QG_WAIT_VM
+// for the copies it is about to read, lds_wait() for these accesses.
+QG_DEV u32 lds_off(const void *p) {
+    return (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+QG_DEV u32 lds_ld32(u32 a) {
+    u32 v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+QG_DEV u32x4 lds_ld128(u32 a) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+QG_DEV void lds_st64(u32 a, u32 lo, u32 hi) {
+    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(u32x2{lo, hi}) : "memory");
+}
+QG_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// after lds_wait(): ties a value read above to the wait, so no use of it is
+// scheduled before the wait
+template <class T>
+QG_DEV void lds_ready(T &v) { asm volatile("" : "+v"(v)); }
+// workgroup barrier without the compiler's fence (which would wait for the
+// copies in flight): this wave's own LDS accesses are complete first
+QG_DEV void lds_barrier() {
+    lds_wait();
+    __builtin_amdgcn_s_barrier();
+}
+
+// N consecutive dwords from LDS byte address a (4-byte aligned), as above
+template <int N>
+QG_DEV void lds_ldn(u32 a, u32 (&t)[N]) {
+#pragma unroll
+    for (int i = 0; i + 1 < N; i += 2) {
+        u32x2 v;
+        asm volatile("ds_read2_b32 %0, %1 offset0:%2 offset1:%3" : "=v"(v) : "v"(a), "i"(i), "i"(i + 1));
+        t[i] = v.x;
+        t[i + 1] = v.y;
+    }
+    if constexpr ((N & 1) != 0) asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(t[N - 1]) : "v"(a), "i"(4 * (N - 1)));
+}
+// 16 bytes at LDS byte address a + O (16-byte aligned)
+template <int O>
+QG_DEV f32x4 lds_ld128f(u32 a) {
+    f32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(O));
+    return v;
+}
+
 // ------------------------------------------------ x staging layout (LDS) ----
 // x values are stored with 4 floats of padding after every 64, so that lanes
 // reading the 64- or 256-value spans of different units hit different banks.

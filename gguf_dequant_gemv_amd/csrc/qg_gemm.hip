@@ -37,39 +37,6 @@ constexpr int GEMM_TT = 16 * GEMM_TG;
 // of its split, neighbouring lanes reading neighbouring 16-byte pieces.  Every chunk issues the same loads (indices clamped to valid
 // memory past the end, results unused), so a fixed wait count retires
 // exactly the loads a chunk needs.
-// LDS accesses the compiler does not see as memory operations.  Seen, every
-// LDS read or write issued while buffer-to-LDS copies are in flight would
-// wait for all of them (the compiler cannot tell which bytes a copy lands
-// in), which undoes the copies' lead.  The kernel waits itself: QG_WAIT_VM
-// for the copies it is about to read, lds_wait() for these accesses.
-QG_DEV u32 lds_off(const void *p) {
-    return (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
-}
-QG_DEV u32 lds_ld32(u32 a) {
-    u32 v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(a));
-    return v;
-}
-QG_DEV u32x4 lds_ld128(u32 a) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-    return v;
-}
-QG_DEV void lds_st64(u32 a, u32 lo, u32 hi) {
-    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(u32x2{lo, hi}) : "memory");
-}
-QG_DEV void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// after lds_wait(): ties a value read above to the wait, so no use of it is
-// scheduled before the wait
-template <class T>
-QG_DEV void lds_ready(T &v) { asm volatile("" : "+v"(v)); }
-// workgroup barrier without the compiler's fence (which would wait for the
-// copies in flight): this wave's own LDS accesses are complete first
-QG_DEV void lds_barrier() {
-    lds_wait();
-    __builtin_amdgcn_s_barrier();
-}
-
 // four values x = h + m + l exactly, each part a bf16 (truncation splits),
 // packed two to a dword, element 2j in the low half
 QG_DEV void split3x4(const f32x4 &x, u32 (&h)[2], u32 (&m)[2], u32 (&l)[2]) {

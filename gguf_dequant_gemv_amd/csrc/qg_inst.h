@@ -18,24 +18,29 @@ gemv_fn pick_lpr(int lpr) {
     }
 }
 
-template <class U, int NT, bool ALN>
+template <class U, int NT, bool ALN, bool XC>
 gemv_fn pick_lpr_lds(int lpr) {
     if constexpr (U::BYTES % 4 != 0) {   // 8 lanes or more make whole 16-byte segments
         switch (lpr) {
-        case 16: return k_gemv_lds<U, 16, NT, ALN>;
-        case 32: return k_gemv_lds<U, 32, NT, ALN>;
-        case 64: return k_gemv_lds<U, 64, NT, ALN>;
-        default: return k_gemv_lds<U, 8, NT, ALN>;
+        case 16: return k_gemv_lds<U, 16, NT, ALN, XC>;
+        case 32: return k_gemv_lds<U, 32, NT, ALN, XC>;
+        case 64: return k_gemv_lds<U, 64, NT, ALN, XC>;
+        default: return k_gemv_lds<U, 8, NT, ALN, XC>;
         }
     } else {
         switch (lpr) {
-        case 4: return k_gemv_lds<U, 4, NT, ALN>;
-        case 8: return k_gemv_lds<U, 8, NT, ALN>;
-        case 16: return k_gemv_lds<U, 16, NT, ALN>;
-        case 32: return k_gemv_lds<U, 32, NT, ALN>;
-        default: return k_gemv_lds<U, 64, NT, ALN>;
+        case 4: return k_gemv_lds<U, 4, NT, ALN, XC>;
+        case 8: return k_gemv_lds<U, 8, NT, ALN, XC>;
+        case 16: return k_gemv_lds<U, 16, NT, ALN, XC>;
+        case 32: return k_gemv_lds<U, 32, NT, ALN, XC>;
+        default: return k_gemv_lds<U, 64, NT, ALN, XC>;
         }
     }
+}
+
+template <class U, int NT, bool ALN>
+gemv_fn pick_lds(int lpr, bool xc) {
+    return xc ? pick_lpr_lds<U, NT, ALN, true>(lpr) : pick_lpr_lds<U, NT, ALN, false>(lpr);
 }
 
 template <int TY> struct Units;
@@ -46,12 +51,12 @@ template <> struct Units<T_Q6_K> { typedef UQ6_K B; typedef UQ6_K P; };
 
 // UK_BLOCK exists for Q8_0 / Q4_0 only (the K-quants always stage in LDS)
 template <int TY, int NT>
-gemv_fn pick(int kind, int lpr) {
+gemv_fn pick(int kind, int lpr, bool xc) {
     if constexpr (TY == T_Q8_0 || TY == T_Q4_0) {
         if (kind == UK_BLOCK) return pick_lpr<typename Units<TY>::B, NT>(lpr);
     }
-    if (kind == UK_LDS) return pick_lpr_lds<typename Units<TY>::P, NT, true>(lpr);
-    return pick_lpr_lds<typename Units<TY>::P, NT, false>(lpr);
+    if (kind == UK_LDS) return pick_lds<typename Units<TY>::P, NT, true>(lpr, xc);
+    return pick_lds<typename Units<TY>::P, NT, false>(lpr, xc);
 }
 
 }  // namespace inst
@@ -59,5 +64,5 @@ gemv_fn pick(int kind, int lpr) {
 
 #define QG_GEMV_INSTANCES(NAME, TY, NT) \
     namespace qg { \
-    gemv_fn gemv_kernel_##NAME##_t##NT(int kind, int lpr) { return inst::pick<TY, NT>(kind, lpr); } \
+    gemv_fn gemv_kernel_##NAME##_t##NT(int kind, int lpr, bool xc) { return inst::pick<TY, NT>(kind, lpr, xc); } \
     }

@@ -169,8 +169,8 @@ QG_DEV void unit_dot_pf(const u32 (&w)[U::ND], const float *xs, const float *ss,
 // The same sums for one token with the unit's x values already in registers
 // (xr[k] = x[4k .. 4k+3] of the unit), so all of a unit's LDS reads can be in
 // flight together before the arithmetic starts.
-template <class U>
-QG_DEV void unit_dot_x(const u32 (&w)[U::ND], const f32x4 (&xr)[U::VALUES / 4], const float *ss, float &acc) {
+template <class U, int NS>
+QG_DEV void unit_dot_x(const u32 (&w)[U::ND], const f32x4 (&xr)[U::VALUES / 4], const float (&ss)[NS], float &acc) {
     float us = 0.0f;
 #pragma unroll
     for (int g = 0; g < U::GROUPS; g++) {
@@ -523,7 +523,19 @@ struct StageGeom {
     static constexpr int STAGE = NI * 1024;               // stage bytes in LDS
 };
 
-template <class U, int L, int NT, bool ALN>
+// Q float4 of x from LDS byte address a, by asm (see lds_ldn)
+template <int Q, int I = 0>
+QG_DEV void load_x16(u32 a, f32x4 (&x)[Q]) {
+    if constexpr (I < Q) {
+        x[I] = lds_ld128f<16 * I>(a);
+        load_x16<Q, I + 1>(a, x);
+    }
+}
+
+// XC: x staged in chunks (restaged inside the element loop).  Kept apart from
+// the whole-x variant: global loads inside the loop make the compiler wait for
+// every load in flight, the stage copies included, at the unit reads.
+template <class U, int L, int NT, bool ALN, bool XC>
 __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     extern __shared__ float lds[];
     constexpr int RPW = 64 / L;
@@ -624,7 +636,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
 
     // ---- x, staged whole or in chunks of JC row elements (JC*L units) ----
     const int cols = a.cols;
-    const int JC = a.xchunk > 0 ? a.xchunk : K;
+    const int JC = XC && a.xchunk > 0 ? a.xchunk : K;
     const int NCH = (K + JC - 1) / JC;
     const int ccols = JC * L * UV;                      // columns per chunk
     const int cpad = min(a.nunits, JC * L) * UV;        // staged span (the widest chunk)
@@ -632,6 +644,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     const int nsum = SUMS ? cpad / SUMS : 0;
     float *xs = lds;
     float *ss = lds + NT * xstride;
+    const u32 xs_l = lds_off(xs), ss_l = lds_off(ss), ring_l = lds_off(ring);
     f32x4 xv[XB];
     // chunk ch: columns [ch*ccols, +cw) of the padded row, valid below cols
     // (the LDS kinds' padded width equals cols, so every chunk has valid x)
@@ -677,7 +690,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     for (int s = 0; s < S; s++) {
         const int slot = s % D;
         const int jm = cj >= K ? cj - K : cj;      // the element's place in its row
-        if (NCH > 1 && s > 0 && jm % JC == 0) {
+        if (XC && NCH > 1 && s > 0 && jm % JC == 0) {
             // every wave has finished with the previous chunk (all waves walk
             // the same element sequence, so they all meet here)
             __syncthreads();
@@ -698,8 +711,43 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
             const u32 phase = ((u32)rr * rb + jj * (u32)(L * U::BYTES) + (hi ? ph1 : ph0)) & 15u;
             uoff = (u32)grp * (SEGP * 16) + phase + (u32)sub * U::BYTES;
         }
-        lds_unit<U, ALN>(ring + slot * G::STAGE, uoff, wd);
-        QG_WAIT_LGKM0();   // the unit is in registers: the stage can be refilled
+        const int u = sub + jm * L;
+        const int ul = u - ub;                     // its place in the staged chunk
+        // one token, 64-value units: the unit's words, its x and its x-sums
+        // are read by asm, so the copies of the later stages stay in flight
+        // (the compiler would wait for every copy before any LDS read)
+        constexpr bool XPF = NT == 1 && UV <= 64 && U::BYTES % 4 == 0;
+        constexpr int NW = U::ND + (ALN ? 0 : 1);   // dwords read for the unit
+        f32x4 xr[XPF ? UV / 4 : 1];
+        float sv[U::GROUPS] = {};                 // x-sums of the unit's groups (SUMS formats)
+        if constexpr (XPF) {
+            u32 t[NW];
+            lds_ldn<NW>(ring_l + slot * G::STAGE + (uoff & ~3u), t);
+            load_x16<UV / 4>(xs_l + 4u * (u32)xpad((min(u, a.nunits - 1) - ub) * UV), xr);
+            u32 sw[SUMS ? U::GROUPS : 1];
+            if constexpr (SUMS != 0) lds_ldn<U::GROUPS>(ss_l + 4u * (u32)((min(u, a.nunits - 1) - ub) * SPU), sw);
+            lds_wait();
+#pragma unroll
+            for (int i = 0; i < NW; i++) lds_ready(t[i]);
+#pragma unroll
+            for (int q = 0; q < UV / 4; q++) lds_ready(xr[q]);
+            if constexpr (SUMS != 0) {
+#pragma unroll
+                for (int g = 0; g < U::GROUPS; g++) {
+                    lds_ready(sw[g]);
+                    sv[g] = __builtin_bit_cast(float, sw[g]);
+                }
+            }
+            if constexpr (ALN) {
+#pragma unroll
+                for (int i = 0; i < U::ND; i++) wd[i] = t[i];
+            } else {
+                realign<U::ND>(t, uoff, wd);
+            }
+        } else {
+            lds_unit<U, ALN>(ring + slot * G::STAGE, uoff, wd);
+            QG_WAIT_LGKM0();   // the unit is in registers: the stage can be refilled
+        }
         __builtin_amdgcn_sched_barrier(0);
         if (ip < P) {
             issue(ip, ij, slot);
@@ -708,15 +756,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
         const int64_t r0 = (tile * 4 + wave) * RPW;
-        const int u = sub + jm * L;
-        const int ul = u - ub;                     // its place in the staged chunk
-        if constexpr (NT == 1 && UV <= 64) {
-            // one token, 64-value units: all the unit's x reads go out at once
-            const float *xp = xs + xpad((min(u, a.nunits - 1) - ub) * UV);
-            f32x4 xr[UV / 4];
-#pragma unroll
-            for (int q = 0; q < UV / 4; q++) xr[q] = *(const f32x4 *)(xp + 4 * q);
-            if (u < a.nunits) unit_dot_x<U>(wd, xr, ss + ul * SPU, acc[0]);
+        if constexpr (XPF) {
+            if (u < a.nunits) unit_dot_x<U>(wd, xr, sv, acc[0]);
         } else if constexpr (NT == 1 && U::GROUPS > 2) {
             if (u < a.nunits) unit_dot_pf<U>(wd, xs + xpad(ul * UV), ss + ul * SPU, acc[0]);
         } else {
@@ -1043,12 +1084,13 @@ typedef void (*dequant_fn)(const uint8_t *, float *, int64_t, int, int64_t);
 enum { UK_BLOCK = 0, UK_LDS = 1, UK_LDS2 = 2, UK_MFMA = 3 };
 // One function per (block type, tokens per workgroup), each instantiated in
 // its own translation unit (qg_inst_<type>_t<NT>.hip); returns the kernel for
-// (kernel kind, lanes per row).  qg_inst_dequant.hip holds the dequantizers.
+// (kernel kind, lanes per row, x staged in chunks).  qg_inst_dequant.hip
+// holds the dequantizers.
 #define QG_DECL_GEMV(NAME) \
-    gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr); \
-    gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr); \
-    gemv_fn gemv_kernel_##NAME##_t4(int kind, int lpr); \
-    gemv_fn gemv_kernel_##NAME##_t8(int kind, int lpr);
+    gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr, bool xc); \
+    gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr, bool xc); \
+    gemv_fn gemv_kernel_##NAME##_t4(int kind, int lpr, bool xc); \
+    gemv_fn gemv_kernel_##NAME##_t8(int kind, int lpr, bool xc);
 QG_DECL_GEMV(q8_0)
 QG_DECL_GEMV(q4_0)
 QG_DECL_GEMV(q4_k)
