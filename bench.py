@@ -104,7 +104,7 @@ class DenseMlpHead(Workload):
         self.x = gs.device_activations(1, H, _gen(7))
         self.h = torch.empty((1, H), dtype=torch.float32, device="cuda")
         self.logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
-        self.ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_mlp_workspace_size(qg.QG_Q8_0, H, F, 1) // 4, dtype=torch.float32, device="cuda")
         rb = gs.row_bytes(gs.Q8_0, H)
         self.mlp_bytes = 2 * F * rb + H * gs.row_bytes(gs.Q8_0, F)
         self.dominant_bytes = V * rb
@@ -232,7 +232,7 @@ class MoeLayers(Workload):
         self.dense_bytes = (2 * dense_ff * rb_gu + H * gs.row_bytes(t, dense_ff)) if dense_ff else 0
         if dense_ff:
             self.ym = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
-            self.wsm = torch.empty(qg.qg_mlp_workspace_size(dense_ff, ntok) // 4, dtype=torch.float32,
+            self.wsm = torch.empty(qg.qg_mlp_workspace_size(t, H, dense_ff, ntok) // 4, dtype=torch.float32,
                                    device="cuda")
         self.bytes_per_step = int(sum(uniq) / len(uniq) * rec) + self.dense_bytes
         self.dominant_bytes = self.bytes_per_step
@@ -360,7 +360,7 @@ class GemmaBlock(Workload):
         self.w = f32(ntok, k)
         self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
-        self.wsm = f32(qg.qg_mlp_workspace_size(Fd, ntok) // 4)
+        self.wsm = f32(qg.qg_mlp_workspace_size(t, H, Fd, ntok) // 4)
         self.ws = f32(qg.qg_moe_workspace_size(self.layers[0]["m"], k, ntok) // 4)
         self.kr = 1.0 / H ** 0.5
         uniq = []
@@ -459,7 +459,7 @@ class PrefillMlp(Workload):
                           Wd=gs.device_weights(gs.Q8_0, H, F, g)) for _ in range(copies)]
         self.x = gs.device_activations(ntok, H, g)
         self.y = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
-        self.ws = torch.empty(qg.qg_mlp_workspace_size(F, ntok) // 4, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_mlp_workspace_size(qg.QG_Q8_0, H, F, ntok) // 4, dtype=torch.float32, device="cuda")
         rb = gs.row_bytes(gs.Q8_0, H)
         self.bytes_per_step = 2 * F * rb + H * gs.row_bytes(gs.Q8_0, F)
         self.flops_per_step = 2.0 * 3 * H * F * ntok

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemv.so")
 
 # Every symbol include/qgemv.h declares.
-EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm", "qg_dequant",
+EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
+           "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_rmsnorm", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
@@ -58,10 +59,12 @@ def lib():
         L.qg_strerror.argtypes = [i32]
         L.qg_strerror.restype = ctypes.c_char_p
         L.qg_gemv.argtypes = [i32, P, P, P, i64, i64, i32, P]
-        L.qg_gemm.argtypes = [i32, P, P, P, i64, i64, i32, P]
+        L.qg_gemm_workspace_size.argtypes = [i32, i64, i64, i32]
+        L.qg_gemm_workspace_size.restype = sz
+        L.qg_gemm.argtypes = [i32, P, P, P, i64, i64, i32, P, sz, P]
         L.qg_dequant.argtypes = [i32, P, P, i64, i64, P]
         L.qg_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
-        L.qg_mlp_workspace_size.argtypes = [i64, i32]
+        L.qg_mlp_workspace_size.argtypes = [i32, i64, i64, i32]
         L.qg_mlp_workspace_size.restype = sz
         L.qg_mlp.argtypes = [i32, i32, P, P, P, i64, i64, P, P, i32, P, sz, P]
         L.qg_moe_workspace_size.argtypes = [ctypes.POINTER(qg_moe), i32, i32]
@@ -121,8 +124,14 @@ def qg_gemv(type, W, x, y, rows, cols, ntok=1, stream=None):
     _check("qg_gemv", lib().qg_gemv(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _stream(stream)))
 
 
-def qg_gemm(type, W, x, y, rows, cols, ntok, stream=None):
-    _check("qg_gemm", lib().qg_gemm(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _stream(stream)))
+def qg_gemm_workspace_size(type, rows, cols, ntok):
+    return lib().qg_gemm_workspace_size(type, rows, cols, ntok)
+
+
+def qg_gemm(type, W, x, y, rows, cols, ntok, workspace=None, workspace_bytes=None, stream=None):
+    nbytes = 0 if workspace is None else _nbytes(workspace, workspace_bytes)
+    _check("qg_gemm", lib().qg_gemm(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _ptr(workspace), nbytes,
+                                    _stream(stream)))
 
 
 def qg_dequant(type, W, out, rows, cols, stream=None):
@@ -134,8 +143,8 @@ def qg_router_topk(logits, n_experts, k, ntok, ids, weights, stream=None):
                                                   _ptr(weights), _stream(stream)))
 
 
-def qg_mlp_workspace_size(ff, ntok):
-    return lib().qg_mlp_workspace_size(ff, ntok)
+def qg_mlp_workspace_size(type, hidden, ff, ntok):
+    return lib().qg_mlp_workspace_size(type, hidden, ff, ntok)
 
 
 def qg_mlp(type, act, W_gate, W_up, W_down, hidden, ff, x, y, ntok, workspace, workspace_bytes=None,

@@ -268,6 +268,48 @@ gemv_fn pick(int type, const Plan &p) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// Prefill launches split along the row when their row and token tiles alone
+// leave CUs idle (the 2560-row down projection of a 64-token chunk is 20
+// tiles): each split sums a run of whole k-chunks into a partial buffer, and
+// a second launch adds the splits in order.  The split count minimises
+// (rounds of resident workgroups) x (chunks per split + pipeline fill), with
+// one workgroup resident per CU (the kernel's register use) and splits of at
+// least four chunks.  The same rule sizes the workspace.
+struct GemmSplit {
+    int n, kchunks;
+};
+GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    const int64_t kv = gemm_chunk_values();
+    const int64_t nch = (cols + kv - 1) / kv;
+    GemmSplit best = {1, (int)nch};
+    if ((type != QG_Q8_0 && type != QG_Q4_0) || ntok <= QG_MAX_TOKENS || ntok > QG_MAX_PREFILL) return best;
+    const int64_t tt = gemm_token_tile();
+    const int64_t tile_rows = 4 * gemm_rows_per_wave(glu);
+    const int64_t wgs = ((rows + tile_rows - 1) / tile_rows) * ((ntok + tt - 1) / tt);
+    if (wgs >= NUM_CU) return best;
+    const int64_t fill = 3;
+    int64_t best_cost = nch + fill;
+    for (int n = 2; n <= 32; n++) {
+        const int64_t kc = (nch + n - 1) / n;
+        if (kc < 4) break;
+        const int64_t ns = (nch + kc - 1) / kc;
+        const int64_t rounds = (wgs * ns + NUM_CU - 1) / NUM_CU;
+        const int64_t cost = rounds * (kc + fill) + fill;   // + the adding launch
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = {(int)ns, (int)kc};
+        }
+    }
+    return best;
+}
+
+// bytes of the partial sums of a split prefill launch (0: no split)
+size_t gemm_part_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    const GemmSplit sp = gemm_split(type, rows, cols, ntok, glu);
+    if (sp.n < 2) return 0;
+    return ((size_t)sp.n * (size_t)ntok * (size_t)(glu ? 2 : 1) * (size_t)rows * 4 + 255) & ~(size_t)255;
+}
+
 // a: weights, x/y, tokens or groups and rows set by the caller.
 int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
@@ -284,9 +326,17 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
         gemv_fn f = gemm_kernel_mfma(s.type);
         int64_t cap = resident_wgs(f, 0) / tchunks;
         if (cap < 1) cap = 1;
-        grid = dim3((unsigned)(a.ntiles < cap ? a.ntiles : cap), (unsigned)tchunks, 1);
+        const GemmSplit sp = gemm_split(s.type, a.rows, s.cols, a.ntok, a.glu);
+        const size_t need = gemm_part_bytes(s.type, a.rows, s.cols, a.ntok, a.glu);
+        const bool split = sp.n > 1 && a.part && need <= a.part_bytes;
+        if (!split) a.part = nullptr;
+        a.kchunks = sp.kchunks;
+        a.ptok = a.ntok;
+        a.prow = (a.glu ? 2 : 1) * a.rows;
+        grid = dim3((unsigned)(a.ntiles < cap ? a.ntiles : cap), (unsigned)tchunks, split ? (unsigned)sp.n : 1u);
         hipLaunchKernelGGL(f, grid, dim3(256), 0, st, a);
-        return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+        if (hipGetLastError() != hipSuccess) return QG_EHIP;
+        return split ? gemm_reduce(a, sp.n, st) : QG_OK;
     }
     // four groups of 16 rows per tile, or two when that leaves too few tiles
     // to spread over the CUs
@@ -358,7 +408,7 @@ const char *qg_strerror(int code) {
 namespace {
 // qg_gemv / qg_gemm: the same sum for up to max_tok tokens
 int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
-               void *stream) {
+               void *ws, size_t ws_bytes, void *stream) {
     if (type == QG_F32) {   // plain f32 weights (router, shared-expert gate)
         if (rows <= 0 || cols <= 0) return QG_EINVAL;
         if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
@@ -376,6 +426,8 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
     if (rc) return rc;
     if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
+    if (ws_bytes < gemm_part_bytes(type, rows, cols, ntok, 0) || (ws_bytes && (!ws || !aligned(ws, 256))))
+        return QG_EINVAL;
     // rows in launches of at most MAX_RANGE weight bytes each
     const int64_t chunk = MAX_RANGE / s.row_bytes;
     for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
@@ -391,6 +443,8 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
         a.y = y + r0;
         a.y_stride = rows;
         a.ntok = ntok;
+        a.part = (float *)ws;
+        a.part_bytes = ws_bytes;
         rc = launch_gemv(sc, p, a, dim3(1, (ntok + p.nt - 1) / p.nt, 1), (hipStream_t)stream);
         if (rc) return rc;
     }
@@ -401,11 +455,17 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
 extern "C" {
 
 int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
-    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_TOKENS, stream);
+    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_TOKENS, nullptr, 0, stream);
 }
 
-int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *stream) {
-    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_PREFILL, stream);
+size_t qg_gemm_workspace_size(int type, int64_t rows, int64_t cols, int ntok) {
+    if (rows <= 0 || cols <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
+    return gemm_part_bytes(type, rows, cols, ntok, 0);
+}
+
+int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *workspace,
+            size_t workspace_bytes, void *stream) {
+    return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_PREFILL, workspace, workspace_bytes, stream);
 }
 
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
@@ -432,10 +492,19 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
-// Workspace of qg_mlp: gu [ntok][2ff] f32 at offset 0, then act [ntok][ff].
-size_t qg_mlp_workspace_size(int64_t ff, int ntok) {
-    if (ff <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
-    return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float));
+// Workspace of qg_mlp: gu [ntok][2ff] f32 at offset 0, then act [ntok][ff],
+// then the partial sums of split prefill launches (gate||up, then down).
+namespace {
+size_t mlp_part_bytes(int type, int64_t hidden, int64_t ff, int ntok) {
+    const size_t a = gemm_part_bytes(type, ff, hidden, ntok, 1), b = gemm_part_bytes(type, hidden, ff, ntok, 0);
+    return a > b ? a : b;
+}
+}  // namespace
+
+size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok) {
+    if (hidden <= 0 || ff <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
+    return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float)) +
+           mlp_part_bytes(type, hidden, ff, ntok);
 }
 
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
@@ -451,10 +520,12 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     if (!aligned(W_gate, 2) || !aligned(W_up, 2) || !aligned(W_down, 2) || !aligned(x, 4) || !aligned(y, 4) ||
         !aligned(workspace, 256))
         return QG_EINVAL;
-    if (workspace_bytes < qg_mlp_workspace_size(ff, ntok)) return QG_EINVAL;
+    if (workspace_bytes < qg_mlp_workspace_size(type, hidden, ff, ntok)) return QG_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     float *gu = (float *)workspace;
     float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
+    float *part = (float *)((uint8_t *)av + align256((size_t)ntok * (size_t)ff * sizeof(float)));
+    const size_t part_bytes = mlp_part_bytes(type, hidden, ff, ntok);
     // gate and up rows together: act(gate) * up per row, raw gate / up kept in gu
     Plan p1 = make_plan(s_g, ntok, 1, aligned(W_gate, 16) && aligned(W_up, 16));
     GemvArgs a = {};
@@ -469,6 +540,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     a.y2 = gu;
     a.y2_stride = 2 * ff;
     a.ntok = ntok;
+    a.part = part;
+    a.part_bytes = part_bytes;
     rc = launch_gemv(s_g, p1, a, dim3(1, (ntok + p1.nt - 1) / p1.nt, 1), st);
     if (rc) return rc;
     // down on the activations
@@ -481,6 +554,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     b.y = y;
     b.y_stride = hidden;
     b.ntok = ntok;
+    b.part = part;
+    b.part_bytes = part_bytes;
     return launch_gemv(s_dn, p2, b, dim3(1, (ntok + p2.nt - 1) / p2.nt, 1), st);
 }
 

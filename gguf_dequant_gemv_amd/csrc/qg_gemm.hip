@@ -14,6 +14,7 @@
 // matmulQ8T, gemma4_moe_ssd.js matmulQ4T) tile 16 rows x 16 tokens through
 // workgroup memory in f32; this keeps their "each weight byte serves many
 // tokens" and moves the contraction to the matrix cores.
+#include "../../include/qgemv.h"
 #include "qg_kernels.h"
 #include "qg_block.h"
 
@@ -83,7 +84,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n16 = lane & 15, q = lane >> 4;
     const int nb = a.cols / 32;
-    const int nch = (nb + BPC - 1) / BPC;
+    // this workgroup's k-chunks [c_lo, nch): the whole row, or one split of it
+    const int nch_all = (nb + BPC - 1) / BPC;
+    const int c_lo = a.part ? (int)blockIdx.z * a.kchunks : 0;
+    const int nch = a.part ? min(nch_all, c_lo + a.kchunks) : nch_all;
     const int64_t rows = a.rows;
     const u32 rb = (u32)a.row_bytes;
     const int t0 = blockIdx.y * GEMM_TT;
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
         return min(tile * tile_rows + sl, rows - 1);
     };
     auto dma = [&](int64_t tile, int chunk) {
-        uint8_t *dst = s_w + (chunk % G::RING) * G::SLOT;
+        uint8_t *dst = s_w + ((chunk - c_lo) % G::RING) * G::SLOT;
         const u32 cbyte = (u32)min(chunk, nch - 1) * (u32)(BPC * BYTES);
 #pragma unroll
         for (int i = 0; i < G::NI; i++) {
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
         // are read from LDS before any of its MFMAs, so the reads of later
         // blocks overlap the arithmetic of earlier ones
         auto consume = [&](int chunk) {
-            const u32 sw = sw0 + (u32)(chunk % G::RING) * G::SLOT;
+            const u32 sw = sw0 + (u32)((chunk - c_lo) % G::RING) * G::SLOT;
             const u32 cbyte = (u32)chunk * (u32)(BPC * BYTES);
             const int nbl = min(BPC, nb - chunk * BPC);
             u32 w[BPC][RG][4];
@@ -279,12 +283,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
             dma(tile, c + 3);
             consume(c);
         };
-        x_fetch(0, 0);
-        dma(tile, 0);
-        x_fetch(1, 1);
-        dma(tile, 1);
-        dma(tile, 2);
-        int c = 0;
+        x_fetch(c_lo, 0);
+        dma(tile, c_lo);
+        x_fetch(c_lo + 1, 1);
+        dma(tile, c_lo + 1);
+        dma(tile, c_lo + 2);
+        int c = c_lo;
         for (; c + 2 <= nch; c += 2) {
             step(c, 0);
             step(c + 1, 1);
@@ -304,7 +308,16 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
                 const int t = 16 * tg + q4 + i;
                 if (t >= nt) continue;
                 const int64_t oi = t0 + t;
-                if (a.glu) {
+                if (a.part) {   // raw sums of this split, gate and up apart
+                    float *pp = a.part + ((int64_t)blockIdx.z * a.ptok + oi) * a.prow;
+#pragma unroll
+                    for (int gi = 0; gi < RG; gi++) {
+                        const bool hi = a.glu && gi >= RG / 2;
+                        const int g = a.glu ? gi % (RG / 2) : gi;
+                        const int64_t r = tile * tile_rows + 16 * (wave * gpw + g) + n16;
+                        if (r < rows) pp[(hi ? rows : 0) + r] = acc[gi][tg][i];
+                    }
+                } else if (a.glu) {
 #pragma unroll
                     for (int gi = 0; gi < RG / 2; gi++) {
                         const int64_t r = tile * tile_rows + 16 * (wave * gpw + gi) + n16;
@@ -337,5 +350,39 @@ gemv_fn gemm_kernel_mfma(int type) { return type == T_Q8_0 ? k_gemm_mfma<T_Q8_0>
 int gemm_rows_per_wave(int glu) { return 16 * (glu ? GemmGeom<T_Q8_0>::RG / 2 : GemmGeom<T_Q8_0>::RG); }
 
 int gemm_token_tile() { return GEMM_TT; }
+
+int gemm_chunk_values() { return GEMM_KC; }
+
+// One thread per output (token blockIdx.y, row r): the splits' raw sums added
+// in split order, so the result does not depend on which split finished first.
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float *part, int nsplit, int64_t ptok, int64_t prow,
+                                                     int64_t rows, int glu, float *y, int64_t y_stride, float *y2,
+                                                     int64_t y2_stride) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = blockIdx.y;
+    if (r >= rows) return;
+    const float *p = part + t * prow + r;
+    const int64_t zs = ptok * prow;
+    float g = 0.0f, u = 0.0f;
+    for (int z = 0; z < nsplit; z++) {
+        g += p[z * zs];
+        if (glu) u += p[z * zs + rows];
+    }
+    if (glu) {
+        y[t * y_stride + r] = qg::glu(glu, g, u);
+        if (y2) {
+            y2[t * y2_stride + r] = g;
+            y2[t * y2_stride + rows + r] = u;
+        }
+    } else {
+        y[t * y_stride + r] = g;
+    }
+}
+
+int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st) {
+    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((a.rows + 255) / 256), (unsigned)a.ntok), dim3(256), 0, st,
+                       a.part, nsplit, a.ptok, a.prow, a.rows, a.glu, a.y, a.y_stride, a.y2, a.y2_stride);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
 
 }  // namespace qg

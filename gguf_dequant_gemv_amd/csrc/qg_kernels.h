@@ -79,6 +79,14 @@ struct GemvArgs {
     // k_gemv_lds: x is staged in chunks of this many row elements (units of
     // L lanes), restaged as each tile row reaches the next chunk; 0 = all of x
     int xchunk;
+    // prefill chunks split along the row (k_gemm_mfma): workgroup z of grid.z
+    // sums k-chunks [z * kchunks, (z + 1) * kchunks) and writes its raw sums
+    // to part + (z * ptok + t) * prow + r (gated: up sums at prow / 2 + r);
+    // part == nullptr: one split, results written to y as usual
+    float *part;
+    size_t part_bytes;
+    int kchunks;
+    int64_t ptok, prow;
 };
 
 // -------------------------------------------------------- unit dot product --
@@ -1105,6 +1113,10 @@ gemv_fn gemv_kernel_mfma(int type, int groups);
 gemv_fn gemm_kernel_mfma(int type);
 int gemm_rows_per_wave(int glu);
 int gemm_token_tile();
+int gemm_chunk_values();   // row values per k-chunk
+// adds the raw sums of a.kchunks-long splits (grid.z = nsplit of them) in
+// split order and writes y (gated: act(g) * u, and g, u to y2 when set)
+int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st);
 
 // Router / grouping and combine kernels (qg_route.hip).
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,

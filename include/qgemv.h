@@ -100,10 +100,17 @@ int qg_gemv(int type, const void *W, const float *x, float *y,
  * QG_MAX_PREFILL tokens ([qwen35] / [gemma4] WGSL matmulQ8T / matmulQ4T, the
  * tiled prompt-chunk GEMMs).  Q8_0 / Q4_0 run on the matrix cores with every
  * product exact (codes and three bf16 parts of x); the K-quants and f32 run
- * on the vector kernels in chunks of tokens.  Arguments and errors as
- * qg_gemv, with QG_ELIMIT for ntok outside 1..QG_MAX_PREFILL. */
+ * on the vector kernels in chunks of tokens.
+ * workspace: device scratch of at least qg_gemm_workspace_size(type, rows,
+ * cols, ntok) bytes, 256-byte aligned (may be NULL when that size is 0).  It
+ * holds partial sums when a launch with few row tiles is split along the row;
+ * its contents after the call are unspecified.
+ * Arguments and errors as qg_gemv, with QG_ELIMIT for ntok outside
+ * 1..QG_MAX_PREFILL and QG_EINVAL for a short or misaligned workspace. */
+size_t qg_gemm_workspace_size(int type, int64_t rows, int64_t cols, int ntok);
 int qg_gemm(int type, const void *W, const float *x, float *y,
-            int64_t rows, int64_t cols, int ntok, void *stream);
+            int64_t rows, int64_t cols, int ntok, void *workspace,
+            size_t workspace_bytes, void *stream);
 
 /* Dequantize a whole tensor: out[r][c] = W[r][c] as f32, bit-exact (each
  * value is the f32 nearest to its exact value; for Q8_0, Q4_0 and Q6_K the
@@ -135,13 +142,14 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
  * W_gate, W_up: ff x hidden; W_down: hidden x ff (same block type).
  * x: [ntok][hidden], y: [ntok][hidden]; 1 <= ntok <= QG_MAX_PREFILL (a
  * decode step, a verify batch or a prefill chunk).
- * workspace: device scratch of at least qg_mlp_workspace_size(ff, ntok) bytes,
- * 256-byte aligned.  After the call it holds gu as [ntok][2*ff] f32 at offset 0
- * and a as [ntok][ff] f32 after it (at the next 256-byte boundary):
- * documented intermediates, useful for staged checking.
+ * workspace: device scratch of at least qg_mlp_workspace_size(type, hidden,
+ * ff, ntok) bytes, 256-byte aligned.  After the call it holds gu as
+ * [ntok][2*ff] f32 at offset 0 and a as [ntok][ff] f32 after it (at the next
+ * 256-byte boundary): documented intermediates, useful for staged checking.
+ * Prefill chunks may use more scratch after a (unspecified contents).
  * Errors: as qg_gemv for both shapes, QG_EINVAL for a short workspace or an
  * unknown act. */
-size_t qg_mlp_workspace_size(int64_t ff, int ntok);
+size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok);
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down,
            int64_t hidden, int64_t ff, const float *x, float *y, int ntok,
            void *workspace, size_t workspace_bytes, void *stream);

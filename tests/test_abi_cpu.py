@@ -76,10 +76,11 @@ def test_router_rejects():
 
 def test_mlp_rejects_and_sizes():
     L = qg.lib()
-    assert qg.qg_mlp_workspace_size(9728, 1) == 2 * 9728 * 4 + 9728 * 4   # gu, then act
-    assert qg.qg_mlp_workspace_size(100, 3) % 256 == 0
-    assert qg.qg_mlp_workspace_size(9728, 0) == 0
-    ws = qg.qg_mlp_workspace_size(64, 1)
+    assert qg.qg_mlp_workspace_size(8, 2560, 9728, 1) == 2 * 9728 * 4 + 9728 * 4   # gu, then act
+    assert qg.qg_mlp_workspace_size(8, 64, 100, 3) % 256 == 0
+    assert qg.qg_mlp_workspace_size(8, 2560, 9728, 0) == 0
+    assert qg.qg_mlp_workspace_size(8, 0, 9728, 1) == 0
+    ws = qg.qg_mlp_workspace_size(8, 64, 64, 1)
     assert L.qg_mlp(8, 0, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 1, FAKE, ws - 4, None) == qg.QG_EINVAL
     assert L.qg_mlp(8, 5, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
     assert L.qg_mlp(8, 0, FAKE, FAKE, FAKE, 64, 48, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
@@ -171,9 +172,30 @@ def test_moe_shared_rejects_and_sizes():
 def test_gemm_token_limits():
     L = qg.lib()
     assert L.qg_gemv(8, FAKE, FAKE, FAKE, 16, 64, 17, None) == qg.QG_ELIMIT
-    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, qg.QG_MAX_PREFILL + 1, None) == qg.QG_ELIMIT
-    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, 0, None) == qg.QG_ELIMIT
-    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 48, 64, None) == qg.QG_EINVAL     # cols % 32
-    assert L.qg_gemm(0, FAKE + 2, FAKE, FAKE, 16, 64, 64, None) == qg.QG_EINVAL  # f32 W misaligned
-    assert qg.qg_mlp_workspace_size(9728, 256) == 256 * 2 * 9728 * 4 + 256 * 9728 * 4
-    assert qg.qg_mlp_workspace_size(9728, qg.QG_MAX_PREFILL + 1) == 0
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, qg.QG_MAX_PREFILL + 1, None, 0, None) == qg.QG_ELIMIT
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 64, 0, None, 0, None) == qg.QG_ELIMIT
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 16, 48, 64, None, 0, None) == qg.QG_EINVAL     # cols % 32
+    assert L.qg_gemm(0, FAKE + 2, FAKE, FAKE, 16, 64, 64, None, 0, None) == qg.QG_EINVAL  # f32 W misaligned
+    gu_act = 256 * 2 * 9728 * 4 + 256 * 9728 * 4
+    assert qg.qg_mlp_workspace_size(qg.QG_Q4_K, 2560, 9728, 256) == gu_act   # no split on the vector kernels
+    assert qg.qg_mlp_workspace_size(8, 2560, 9728, 256) > gu_act             # the 20-tile down splits
+    assert qg.qg_mlp_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0
+
+
+def test_gemm_split_workspace():
+    """Prefill launches with few row tiles split along the row: the workspace
+    holds whole [split][token][row] f32 partial sums; wide launches, the
+    K-quants and decode sizes need none."""
+    L = qg.lib()
+    n = qg.qg_gemm_workspace_size(8, 2560, 9728, 64)
+    assert n > 0 and n % 256 == 0 and n % (64 * 2560 * 4) == 0
+    assert 2 <= n // (64 * 2560 * 4) <= 32
+    assert qg.qg_gemm_workspace_size(2, 2560, 9728, 64) == n                 # Q4_0: the same tiles
+    assert qg.qg_gemm_workspace_size(8, 65536, 2560, 64) == 0                # enough row tiles already
+    assert qg.qg_gemm_workspace_size(8, 2560, 9728, 16) == 0                 # decode-size batches
+    assert qg.qg_gemm_workspace_size(qg.QG_Q6_K, 2560, 9728, 64) == 0
+    assert qg.qg_gemm_workspace_size(8, 2560, 128, 64) == 0                  # too short to split
+    assert qg.qg_gemm_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE, n - 256, None) == qg.QG_EINVAL   # short
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE + 16, n, None) == qg.QG_EINVAL    # misaligned
+    assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, None, n, None) == qg.QG_EINVAL         # null

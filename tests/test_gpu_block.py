@@ -343,7 +343,7 @@ def test_gemma_block_chain(orc):
     check_rel(xnh, orc.rmsnorm(x0, c["w_ffn"], H, T, 1e-6), "ffn_norm")
     tg, tu, td = dev(c["Wg"])[0], dev(c["Wu"])[0], dev(c["Wd"])[0]
     md = _empty((T, H))
-    mws = torch.empty(qg.qg_mlp_workspace_size(Fd, T) // 4, dtype=torch.float32, device="cuda")
+    mws = torch.empty(qg.qg_mlp_workspace_size(t, H, Fd, T) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, qg.QG_ACT_GELU_TANH, tg, tu, td, H, Fd, xn, md, T, mws)
     wsh = host(mws)
     gu = wsh[:T * 2 * Fd].reshape(T, 2 * Fd)

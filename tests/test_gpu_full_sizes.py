@@ -52,7 +52,7 @@ def test_dense_mlp_2560x9728_and_head_151936(orc):
     td, _ = dev(c["Wd"])
     xt, _ = dev(c["x"])
     h = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(t, H, F, 1) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, qg.QG_ACT_SILU, tg, tu, td, H, F, xt, h, 1, ws)
     wsh = host(ws)
     gu = wsh[:2 * F].reshape(1, 2 * F)
@@ -114,7 +114,7 @@ def test_mlp_gate_up_x_chunks(orc):
     tg, tu, td = dev(Wg)[0], dev(Wu)[0], dev(Wd)[0]
     xt, _ = dev(x)
     y = torch.full((1, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qg.qg_mlp_workspace_size(F, 1) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(t, H, F, 1) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, qg.QG_ACT_SILU, tg, tu, td, H, F, xt, y, 1, ws)
     wsh = host(ws)
     gu = wsh[:2 * F].reshape(1, 2 * F)

@@ -204,7 +204,7 @@ def test_mlp_stagewise(orc, t, act, H, F, T):
     td, _ = dev(Wd)
     xt, _ = dev(x)
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qg.qg_mlp_workspace_size(F, T) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(t, H, F, T) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, act, tg, tu, td, H, F, xt, y, T, ws)
     wsh = host(ws)
     gu = wsh[:T * 2 * F].reshape(T, 2 * F)

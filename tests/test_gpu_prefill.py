@@ -19,7 +19,9 @@ def gpu_gemm(t, W, x, rows, cols, ntok, w_offset=0):
     Wt, Wp = dev(W, w_offset)
     xt, _ = dev(x.astype(np.float32))
     y = torch.full((ntok, rows), float("nan"), dtype=torch.float32, device="cuda")
-    qg.qg_gemm(t, Wp, xt, y, rows, cols, ntok)
+    nws = qg.qg_gemm_workspace_size(t, rows, cols, ntok)
+    ws = torch.full((max(nws, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qg_gemm(t, Wp, xt, y, rows, cols, ntok, ws if nws else None)
     return host(y)
 
 
@@ -62,7 +64,7 @@ def test_mlp_prefill_stagewise(orc, t, act, H, F, T):
     tg, tu, td = dev(Wg)[0], dev(Wu)[0], dev(Wd)[0]
     xt, _ = dev(x)
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qg.qg_mlp_workspace_size(F, T) // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(t, H, F, T) // 4, dtype=torch.float32, device="cuda")
     qg.qg_mlp(t, act, tg, tu, td, H, F, xt, y, T, ws)
     wsh = host(ws)
     gu = wsh[:T * 2 * F].reshape(T, 2 * F)
