@@ -284,7 +284,7 @@ GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     GemmSplit best = {1, (int)nch};
     if ((type != QG_Q8_0 && type != QG_Q4_0) || ntok <= QG_MAX_TOKENS || ntok > QG_MAX_PREFILL) return best;
     const int64_t tt = gemm_token_tile();
-    const int64_t tile_rows = 4 * gemm_rows_per_wave(glu);
+    const int64_t tile_rows = gemm_tile_rows(glu);
     const int64_t wgs = ((rows + tile_rows - 1) / tile_rows) * ((ntok + tt - 1) / tt);
     if (wgs >= NUM_CU) return best;
     const int64_t fill = 3;
@@ -303,6 +303,10 @@ GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     return best;
 }
 
+bool prefill_kernel(int type, int ntok) {
+    return (type == QG_Q8_0 || type == QG_Q4_0) && ntok > QG_MAX_TOKENS && ntok <= QG_MAX_PREFILL;
+}
+
 // bytes of the partial sums of a split prefill launch (0: no split)
 size_t gemm_part_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     const GemmSplit sp = gemm_split(type, rows, cols, ntok, glu);
@@ -310,31 +314,39 @@ size_t gemm_part_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) 
     return ((size_t)sp.n * (size_t)ntok * (size_t)(glu ? 2 : 1) * (size_t)rows * 4 + 255) & ~(size_t)255;
 }
 
+// scratch of one prefill launch: the split x, then the partial sums
+size_t gemm_scratch_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    if (!prefill_kernel(type, ntok)) return 0;
+    return ((gemm_xs_bytes(cols, ntok) + 255) & ~(size_t)255) + gemm_part_bytes(type, rows, cols, ntok, glu);
+}
+
 // a: weights, x/y, tokens or groups and rows set by the caller.
 int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
     a.nunits = p.nunits;
-    if (!a.grp && a.ntok > QG_MAX_TOKENS && a.x_vec) {
-        // prefill chunk: 64-token tiles, each weight block feeding every token
-        // group of the tile (x read in 16-byte pieces; other x layouts take
-        // the 16-token kernel below, chunk by chunk)
+    if (!a.grp && a.ntok > QG_MAX_TOKENS) {
+        // prefill chunk: x split once into the scratch, then 64-token tiles,
+        // each weight block feeding every token group of the tile
+        if (!a.ws || a.ws_bytes < gemm_scratch_bytes(s.type, a.rows, s.cols, a.ntok, a.glu)) return QG_EINVAL;
+        int rc = gemm_split_x(a.x, a.x_stride, a.ntok, s.cols, a.ws, st);
+        if (rc) return rc;
+        a.xs = a.ws;
         const int tt = gemm_token_tile();
         const int64_t tchunks = (a.ntok + tt - 1) / tt;
-        const int64_t tile_rows = 4 * gemm_rows_per_wave(a.glu);
+        const int64_t tile_rows = gemm_tile_rows(a.glu);
         a.ntiles = (int)((a.rows + tile_rows - 1) / tile_rows);
         gemv_fn f = gemm_kernel_mfma(s.type);
-        int64_t cap = resident_wgs(f, 0) / tchunks;
+        int64_t cap = NUM_CU / tchunks;   // its LDS ring holds one workgroup per CU
         if (cap < 1) cap = 1;
         const GemmSplit sp = gemm_split(s.type, a.rows, s.cols, a.ntok, a.glu);
-        const size_t need = gemm_part_bytes(s.type, a.rows, s.cols, a.ntok, a.glu);
-        const bool split = sp.n > 1 && a.part && need <= a.part_bytes;
-        if (!split) a.part = nullptr;
+        const bool split = sp.n > 1;
+        a.part = split ? (float *)(a.ws + ((gemm_xs_bytes(s.cols, a.ntok) + 255) & ~(size_t)255)) : nullptr;
         a.kchunks = sp.kchunks;
         a.ptok = a.ntok;
         a.prow = (a.glu ? 2 : 1) * a.rows;
         grid = dim3((unsigned)(a.ntiles < cap ? a.ntiles : cap), (unsigned)tchunks, split ? (unsigned)sp.n : 1u);
-        hipLaunchKernelGGL(f, grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(f, grid, dim3(gemm_threads()), 0, st, a);
         if (hipGetLastError() != hipSuccess) return QG_EHIP;
         return split ? gemm_reduce(a, sp.n, st) : QG_OK;
     }
@@ -426,7 +438,7 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
     if (rc) return rc;
     if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
-    if (ws_bytes < gemm_part_bytes(type, rows, cols, ntok, 0) || (ws_bytes && (!ws || !aligned(ws, 256))))
+    if (ws_bytes < gemm_scratch_bytes(type, rows, cols, ntok, 0) || (ws_bytes && (!ws || !aligned(ws, 256))))
         return QG_EINVAL;
     // rows in launches of at most MAX_RANGE weight bytes each
     const int64_t chunk = MAX_RANGE / s.row_bytes;
@@ -443,8 +455,8 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
         a.y = y + r0;
         a.y_stride = rows;
         a.ntok = ntok;
-        a.part = (float *)ws;
-        a.part_bytes = ws_bytes;
+        a.ws = (uint8_t *)ws;
+        a.ws_bytes = ws_bytes;
         rc = launch_gemv(sc, p, a, dim3(1, (ntok + p.nt - 1) / p.nt, 1), (hipStream_t)stream);
         if (rc) return rc;
     }
@@ -460,7 +472,7 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
 
 size_t qg_gemm_workspace_size(int type, int64_t rows, int64_t cols, int ntok) {
     if (rows <= 0 || cols <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
-    return gemm_part_bytes(type, rows, cols, ntok, 0);
+    return gemm_scratch_bytes(type, rows, cols, ntok, 0);
 }
 
 int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *workspace,
@@ -495,8 +507,8 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
 // Workspace of qg_mlp: gu [ntok][2ff] f32 at offset 0, then act [ntok][ff],
 // then the partial sums of split prefill launches (gate||up, then down).
 namespace {
-size_t mlp_part_bytes(int type, int64_t hidden, int64_t ff, int ntok) {
-    const size_t a = gemm_part_bytes(type, ff, hidden, ntok, 1), b = gemm_part_bytes(type, hidden, ff, ntok, 0);
+size_t mlp_scratch_bytes(int type, int64_t hidden, int64_t ff, int ntok) {
+    const size_t a = gemm_scratch_bytes(type, ff, hidden, ntok, 1), b = gemm_scratch_bytes(type, hidden, ff, ntok, 0);
     return a > b ? a : b;
 }
 }  // namespace
@@ -504,7 +516,7 @@ size_t mlp_part_bytes(int type, int64_t hidden, int64_t ff, int ntok) {
 size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok) {
     if (hidden <= 0 || ff <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
     return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float)) +
-           mlp_part_bytes(type, hidden, ff, ntok);
+           mlp_scratch_bytes(type, hidden, ff, ntok);
 }
 
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
@@ -524,8 +536,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     hipStream_t st = (hipStream_t)stream;
     float *gu = (float *)workspace;
     float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
-    float *part = (float *)((uint8_t *)av + align256((size_t)ntok * (size_t)ff * sizeof(float)));
-    const size_t part_bytes = mlp_part_bytes(type, hidden, ff, ntok);
+    uint8_t *scratch = (uint8_t *)av + align256((size_t)ntok * (size_t)ff * sizeof(float));
+    const size_t scratch_bytes = mlp_scratch_bytes(type, hidden, ff, ntok);
     // gate and up rows together: act(gate) * up per row, raw gate / up kept in gu
     Plan p1 = make_plan(s_g, ntok, 1, aligned(W_gate, 16) && aligned(W_up, 16));
     GemvArgs a = {};
@@ -540,8 +552,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     a.y2 = gu;
     a.y2_stride = 2 * ff;
     a.ntok = ntok;
-    a.part = part;
-    a.part_bytes = part_bytes;
+    a.ws = scratch;
+    a.ws_bytes = scratch_bytes;
     rc = launch_gemv(s_g, p1, a, dim3(1, (ntok + p1.nt - 1) / p1.nt, 1), st);
     if (rc) return rc;
     // down on the activations
@@ -554,8 +566,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
     b.y = y;
     b.y_stride = hidden;
     b.ntok = ntok;
-    b.part = part;
-    b.part_bytes = part_bytes;
+    b.ws = scratch;
+    b.ws_bytes = scratch_bytes;
     return launch_gemv(s_dn, p2, b, dim3(1, (ntok + p2.nt - 1) / p2.nt, 1), st);
 }
 

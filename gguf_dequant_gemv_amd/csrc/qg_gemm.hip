@@ -5,39 +5,40 @@
 // batch kernel: codes are small integers (exact in bf16) and x enters as three
 // bf16 parts whose sum is x exactly, so only the f32 accumulation order
 // differs from an f32 FMA chain.  What changes at prefill size is reuse: a
-// workgroup owns 64 tokens (TG = 4 groups of 16) and 4 waves x RG groups of
+// workgroup owns 64 tokens (TG = 4 groups of 16) and 8 waves x RG groups of
 // 16 rows, and every weight block it loads feeds 3 * TG MFMAs per row group.
-// The tokens' x is staged in LDS a k-chunk (KC values) at a time, already
-// split into its three bf16 parts, so the split is paid once per workgroup
-// rather than once per MFMA, and the weights' row segments go HBM -> LDS by
-// asynchronous 16-byte copies two k-chunks ahead.  The pages' prompt-chunk GEMMs (qwen35_moe_ssd.js
-// matmulQ8T, gemma4_moe_ssd.js matmulQ4T) tile 16 rows x 16 tokens through
-// workgroup memory in f32; this keeps their "each weight byte serves many
-// tokens" and moves the contraction to the matrix cores.
+// Every x chunk it loads feeds all 256 rows (x, in three parts, is as many
+// bytes per chunk as the rows' weights).
+//
+// x is split into its three bf16 parts once per launch (k_split_x), laid out
+// k-chunk by k-chunk: one 64-token tile's KC values of one chunk are a single
+// contiguous block of 3 x 64 x KC bf16.  The GEMM then copies, per k-chunk,
+// that block and the tile's weight row segments HBM -> LDS with 16-byte
+// buffer-to-LDS loads two chunks ahead of use, so its loop holds no x
+// arithmetic, no LDS stores and one barrier per chunk.  The pages' prompt-chunk
+// GEMMs ([qwen35] / [gemma4] WGSL matmulQ8T / matmulQ4T) tile 16 rows x 16
+// tokens through workgroup memory in f32; this keeps their "each weight byte
+// serves many tokens" and moves the contraction to the matrix cores.
 #include "../../include/qgemv.h"
 #include "qg_kernels.h"
 #include "qg_block.h"
 
 namespace qg {
 
-constexpr int GEMM_KC = 64;                     // x values per staged k-chunk (2 blocks)
-constexpr int GEMM_XROW = GEMM_KC * 2 + 16;     // LDS bytes per (part, token) row, padded
+constexpr int GEMM_KC = 64;                     // x values per k-chunk (2 blocks)
 constexpr int GEMM_TG = 4;                      // token groups of 16 per workgroup
 constexpr int GEMM_TT = 16 * GEMM_TG;
+constexpr int GEMM_WAVES = 8;                   // waves per workgroup (two per SIMD)
+constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+constexpr int GEMM_XROW = GEMM_KC * 2;          // bytes of one (part, token) row of a chunk
+constexpr int GEMM_XBLK = 3 * GEMM_TT * GEMM_XROW;   // bytes of one (token tile, chunk) block
 
-// Workgroup tile: 4 waves x RG groups of 16 rows (gated: RG/2 gate groups and
-// the same up groups per wave) x 64 tokens; grid.x row tiles (grid-stride),
-// grid.y 64-token chunks.  Lane l: row / token l%16, k-group l/16 of each
-// 32-value block; D[4(l/16)+i][l%16] = token 4(l/16)+i, row l%16.
-//
-// Per k-chunk (2 blocks) the tile's row segments are copied HBM -> LDS by
-// 16-byte buffer-to-LDS loads, three chunks ahead of use in a ring of four,
-// each from the 16-byte-aligned start below the segment (one more piece than
-// the segment needs); row slots are numbered gate rows first, so every load
-// instruction reads one matrix.  x is loaded into registers two chunks ahead
-// of its split, neighbouring lanes reading neighbouring 16-byte pieces.  Every chunk issues the same loads (indices clamped to valid
-// memory past the end, results unused), so a fixed wait count retires
-// exactly the loads a chunk needs.
+// Position of 16-byte piece p (8 values) of token row t inside its row.  The
+// MFMA operand reads take one piece from each of 16 consecutive token rows
+// (128 bytes apart); permuting the pieces by t spreads those reads over all
+// banks whether the LDS serves 8 lanes from 32 banks or 16 lanes from 64.
+QG_DEV int xs_pos(int p, int t) { return p ^ (t & 7) ^ ((t >> 3) & 1); }
+
 // four values x = h + m + l exactly, each part a bf16 (truncation splits),
 // packed two to a dword, element 2j in the low half
 QG_DEV void split3x4(const f32x4 &x, u32 (&h)[2], u32 (&m)[2], u32 (&l)[2]) {
@@ -58,26 +59,65 @@ QG_DEV void split3x4(const f32x4 &x, u32 (&h)[2], u32 (&m)[2], u32 (&l)[2]) {
     }
 }
 
+// x [ntok][x_stride] f32 -> xs [token tile][chunk][part][64 tokens][KC values]
+// bf16 (pieces permuted by xs_pos).  One thread per 8 values; tokens past
+// ntok and values past cols are zeros.
+__global__ __launch_bounds__(256) void k_split_x(const float *x, int64_t x_stride, int ntok, int cols, int nch,
+                                                 int64_t total, uint8_t *xs) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int p = (int)(i & 7), t = (int)((i >> 3) & (GEMM_TT - 1));
+    const int64_t rest = i >> 9;                       // token tile * nch + chunk
+    const int c = (int)(rest % nch);
+    const int tok = (int)(rest / nch) * GEMM_TT + t;
+    const int k0 = c * GEMM_KC + 8 * p;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        v[j] = tok < ntok && k0 + j < cols ? x[(int64_t)tok * x_stride + k0 + j] : 0.0f;
+    u32 h0[2], m0[2], l0[2], h1[2], m1[2], l1[2];
+    split3x4(f32x4{v[0], v[1], v[2], v[3]}, h0, m0, l0);
+    split3x4(f32x4{v[4], v[5], v[6], v[7]}, h1, m1, l1);
+    uint8_t *d = xs + rest * GEMM_XBLK + (int64_t)t * GEMM_XROW + 16 * xs_pos(p, t);
+    *(u32x4 *)d = u32x4{h0[0], h0[1], h1[0], h1[1]};
+    *(u32x4 *)(d + GEMM_TT * GEMM_XROW) = u32x4{m0[0], m0[1], m1[0], m1[1]};
+    *(u32x4 *)(d + 2 * GEMM_TT * GEMM_XROW) = u32x4{l0[0], l0[1], l1[0], l1[1]};
+}
+
 template <int TY>
 struct GemmGeom {
     static constexpr int BYTES = TY == T_Q8_0 ? 34 : 18;
     static constexpr int RG = 2;                                  // row groups per wave
-    static constexpr int NS = 4 * RG * 16;                        // row slots per tile
+    static constexpr int NS = GEMM_WAVES * RG * 16;               // row slots per tile
     static constexpr int SEGP = (15 + (GEMM_KC / 32) * BYTES + 15) / 16;   // pieces per slot
     static constexpr int PIECES = NS * SEGP;
-    static constexpr int NI = PIECES / 256;                       // loads per thread per chunk
-    static constexpr int RING = 4;
-    static constexpr int SLOT = PIECES * 16;                      // bytes per ring slot
-    static_assert(PIECES % 256 == 0, "whole loads per thread");
+    static constexpr int NI = PIECES / GEMM_THREADS;              // weight loads per thread per chunk
+    static constexpr int XI = GEMM_XBLK / 16 / GEMM_THREADS;      // x loads per thread per chunk
+    static constexpr int AHEAD = 2;                               // chunks requested ahead of use
+    static constexpr int RING = AHEAD + 1;
+    static constexpr int SLOT = PIECES * 16;                      // weight bytes per ring slot
+    static_assert(PIECES % GEMM_THREADS == 0 && XI * GEMM_THREADS * 16 == GEMM_XBLK, "whole loads per thread");
     static_assert((NS / 2) * SEGP % 64 == 0, "a load instruction reads one matrix");
 };
 
+// Workgroup tile: 8 waves x RG groups of 16 rows (gated: RG/2 gate groups and
+// the same up groups per wave) x 64 tokens; grid.x row tiles (grid-stride),
+// grid.y 64-token tiles, grid.z splits of the row.  Lane l: row / token l%16,
+// k-group l/16 of each 32-value block; D[4(l/16)+i][l%16] = token 4(l/16)+i,
+// row l%16.
+//
+// Per k-chunk, the tile's row segments (each from the 16-byte-aligned start
+// below it, one more piece than it needs; row slots numbered gate rows first,
+// so every load instruction reads one matrix) and the chunk's split-x block go
+// HBM -> LDS into ring slot (chunk mod RING), AHEAD chunks before use.  Every
+// chunk issues the same loads (chunks past the split's end clamped to its last
+// one, results unused), so a fixed wait count retires exactly one chunk's.
 template <int TY>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
+__global__ __launch_bounds__(GEMM_THREADS) void k_gemm_mfma(GemvArgs a) {
     typedef GemmGeom<TY> G;
     constexpr int BYTES = G::BYTES, RG = G::RG, SEGP = G::SEGP;
     constexpr int BPC = GEMM_KC / 32;           // blocks per k-chunk
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[3 * GEMM_TT * GEMM_XROW];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[G::RING * GEMM_XBLK];
     __shared__ __attribute__((aligned(16))) uint8_t s_w[G::RING * G::SLOT];
 
     const int tid = threadIdx.x;
@@ -93,13 +133,19 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
     const int t0 = blockIdx.y * GEMM_TT;
     const int nt = min(GEMM_TT, a.ntok - t0);
     const int gpw = a.glu ? RG / 2 : RG;        // distinct row groups per wave
-    const int tile_rows = 4 * 16 * gpw;
+    const int tile_rows = GEMM_WAVES * 16 * gpw;
 
     const u32 ph0 = (u32)((uintptr_t)a.W0 & 15u), ph1 = (u32)((uintptr_t)a.W1 & 15u);
     const rsrc_t rs0 = make_rsrc(a.W0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
     const rsrc_t rs1 = make_rsrc(a.W1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
+    // this token tile's split-x blocks, chunk after chunk
+    const rsrc_t rsx = make_rsrc(a.xs + (int64_t)blockIdx.y * nch_all * GEMM_XBLK, (u32)(nch_all * GEMM_XBLK));
     const u32 cpos = 2u + 8u * (u32)(TY == T_Q8_0 ? q : (q & 1));
     const u32 sx0 = lds_off(s_x), sw0 = lds_off(s_w);
+    // this lane's x piece offset within a (part, token group) row block, per block of the chunk
+    u32 xoff[BPC];
+#pragma unroll
+    for (int bl = 0; bl < BPC; bl++) xoff[bl] = (u32)n16 * GEMM_XROW + 16u * (u32)xs_pos(4 * bl + q, n16);
 
     // row slot -> (matrix, row): gated launches number their gate rows first
     auto slot_row = [&](int64_t tile, int slot, bool &hi) {
@@ -109,57 +155,35 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
         return min(tile * tile_rows + sl, rows - 1);
     };
     auto dma = [&](int64_t tile, int chunk) {
-        uint8_t *dst = s_w + ((chunk - c_lo) % G::RING) * G::SLOT;
-        const u32 cbyte = (u32)min(chunk, nch - 1) * (u32)(BPC * BYTES);
+        const int cc = min(chunk, nch - 1);
+        const int slot = (chunk - c_lo) % G::RING;
+        uint8_t *dst = s_w + slot * G::SLOT;
+        const u32 cbyte = (u32)cc * (u32)(BPC * BYTES);
 #pragma unroll
         for (int i = 0; i < G::NI; i++) {
-            // pieces [i*256 + 64*wave, +64) lie in one matrix
+            // pieces [i*THREADS + 64*wave, +64) lie in one matrix
             const bool hiw = __builtin_amdgcn_readfirstlane(
-                                 (int)(a.glu && (i * 256 + 64 * wave) >= (G::NS / 2) * SEGP)) != 0;
+                                 (int)(a.glu && (i * GEMM_THREADS + 64 * wave) >= (G::NS / 2) * SEGP)) != 0;
             // this thread's piece: a row slot and a piece of its segment
-            const int p = i * 256 + tid;
+            const int p = i * GEMM_THREADS + tid;
             bool hi;
             const int64_t r = slot_row(tile, p / SEGP, hi);
             const u32 off = (((u32)r * rb + cbyte + (hiw ? ph1 : ph0)) & ~15u) + 16u * (u32)(p % SEGP);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(hiw ? rs1 : rs0,
                                                      (__attribute__((address_space(3))) void *)(
                                                          (__attribute__((address_space(3))) uint8_t *)dst +
-                                                         (i * 256 + 64 * wave) * 16),
+                                                         (i * GEMM_THREADS + 64 * wave) * 16),
                                                      16, off, 0, 0, 0);
         }
-    };
-
-    // x staging: a chunk is 64 tokens x KC values = TT * KC/4 pieces of 16
-    // bytes; piece j of thread tid is piece (tid % P4) of token tid / P4 +
-    // j * (256 / P4), so the 16-byte loads of neighbouring lanes are
-    // neighbours in memory
-    constexpr int P4 = GEMM_KC / 4;                    // pieces per token row
-    constexpr int XL = GEMM_TT * P4 / 256;             // pieces (loads) per thread
-    static_assert(256 % P4 == 0 && XL * 256 == GEMM_TT * P4, "x staging map");
-    const int st_p = tid % P4, st_t0 = tid / P4;
-    f32x4 xv[2][XL];
-    auto x_fetch = [&](int chunk, int xb) {
-        const int k = min(chunk, nch - 1) * GEMM_KC + 4 * st_p;
+        uint8_t *xdst = s_x + slot * GEMM_XBLK;
+        const u32 xbyte = (u32)cc * (u32)GEMM_XBLK;
 #pragma unroll
-        for (int j = 0; j < XL; j++) {
-            const int tok = st_t0 + j * (256 / P4);
-            const bool in = tok < nt && chunk < nch && k < a.cols;
-            const f32x4 v = *(const f32x4 *)(a.x + (int64_t)(t0 + (tok < nt ? tok : 0)) * a.x_stride +
-                                             min(k, a.cols - 4));
-            xv[xb][j] = in ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-    };
-    auto x_put3 = [&](int xb) {
-#pragma unroll
-        for (int j = 0; j < XL; j++) {
-            const int tok = st_t0 + j * (256 / P4);
-            u32 h[2], m[2], l[2];
-            split3x4(xv[xb][j], h, m, l);
-            const u32 off = sx0 + (u32)tok * GEMM_XROW + (u32)st_p * 8u;
-            lds_st64(off, h[0], h[1]);
-            lds_st64(off + GEMM_TT * GEMM_XROW, m[0], m[1]);
-            lds_st64(off + 2 * GEMM_TT * GEMM_XROW, l[0], l[1]);
-        }
+        for (int i = 0; i < G::XI; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx,
+                                                     (__attribute__((address_space(3))) void *)(
+                                                         (__attribute__((address_space(3))) uint8_t *)xdst +
+                                                         (i * GEMM_THREADS + 64 * wave) * 16),
+                                                     16, xbyte + 16u * (u32)(i * GEMM_THREADS + tid), 0, 0, 0);
     };
 
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
@@ -189,6 +213,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
         // blocks overlap the arithmetic of earlier ones
         auto consume = [&](int chunk) {
             const u32 sw = sw0 + (u32)((chunk - c_lo) % G::RING) * G::SLOT;
+            const u32 sx = sx0 + (u32)((chunk - c_lo) % G::RING) * GEMM_XBLK;
             const u32 cbyte = (u32)chunk * (u32)(BPC * BYTES);
             const int nbl = min(BPC, nb - chunk * BPC);
             u32 w[BPC][RG][4];
@@ -213,7 +238,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
                 }
 #pragma unroll
                 for (int tg = 0; tg < GEMM_TG; tg++) {
-                    const u32 off = sx0 + (u32)(16 * tg + n16) * GEMM_XROW + (u32)(32 * blc + 8 * q) * 2u;
+                    const u32 off = sx + (u32)(16 * tg) * GEMM_XROW + xoff[blc];
 #pragma unroll
                     for (int pt = 0; pt < 3; pt++) xq[bl][pt][tg] = lds_ld128(off + pt * GEMM_TT * GEMM_XROW);
                 }
@@ -269,31 +294,18 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
             }
         };
 
-        // chunk c: its x (in registers) split into LDS, its segments waited
-        // for, then x two chunks on and segments three chunks on requested,
-        // then c's blocks computed
-        auto step = [&](int c, int xb) {
-            lds_barrier();   // every wave is done with the previous chunk's x and ring slot
-            x_put3(xb);
-            // chunk c's segments have landed: issued before them, or later
-            // than them, are at most 2 * NI + XL loads still outstanding
-            QG_WAIT_VM(2 * G::NI + XL);
+        // chunk c: its copies waited for (this wave's: issued later than
+        // them are at most AHEAD - 1 chunks' loads), then the barrier (every
+        // wave's pieces are in, and every wave is done with chunk c - 1, whose
+        // ring slot chunk c + AHEAD takes), then that request, then c's blocks
+#pragma unroll
+        for (int j = 0; j < G::AHEAD; j++) dma(tile, c_lo + j);
+        for (int c = c_lo; c < nch; c++) {
+            QG_WAIT_VM((G::AHEAD - 1) * (G::NI + G::XI));
             lds_barrier();
-            x_fetch(c + 2, xb);
-            dma(tile, c + 3);
+            dma(tile, c + G::AHEAD);
             consume(c);
-        };
-        x_fetch(c_lo, 0);
-        dma(tile, c_lo);
-        x_fetch(c_lo + 1, 1);
-        dma(tile, c_lo + 1);
-        dma(tile, c_lo + 2);
-        int c = c_lo;
-        for (; c + 2 <= nch; c += 2) {
-            step(c, 0);
-            step(c + 1, 1);
         }
-        if (c < nch) step(c, 0);
         QG_WAIT_VM(0);     // the chunks past the end were requested too
 
         // lane holds tokens 16 tg + 4q + i of row n16 of each group (the
@@ -347,11 +359,26 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemvArgs a) {
 
 gemv_fn gemm_kernel_mfma(int type) { return type == T_Q8_0 ? k_gemm_mfma<T_Q8_0> : k_gemm_mfma<T_Q4_0>; }
 
-int gemm_rows_per_wave(int glu) { return 16 * (glu ? GemmGeom<T_Q8_0>::RG / 2 : GemmGeom<T_Q8_0>::RG); }
+int gemm_tile_rows(int glu) { return GEMM_WAVES * 16 * (glu ? GemmGeom<T_Q8_0>::RG / 2 : GemmGeom<T_Q8_0>::RG); }
+
+int gemm_threads() { return GEMM_THREADS; }
 
 int gemm_token_tile() { return GEMM_TT; }
 
 int gemm_chunk_values() { return GEMM_KC; }
+
+size_t gemm_xs_bytes(int64_t cols, int ntok) {
+    const int64_t nch = (cols + GEMM_KC - 1) / GEMM_KC, tiles = (ntok + GEMM_TT - 1) / GEMM_TT;
+    return (size_t)(tiles * nch * GEMM_XBLK);
+}
+
+int gemm_split_x(const float *x, int64_t x_stride, int ntok, int64_t cols, uint8_t *xs, hipStream_t st) {
+    const int64_t nch = (cols + GEMM_KC - 1) / GEMM_KC, tiles = (ntok + GEMM_TT - 1) / GEMM_TT;
+    const int64_t total = tiles * nch * GEMM_TT * 8;      // threads: 8 values each
+    hipLaunchKernelGGL(k_split_x, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, x, x_stride, ntok,
+                       (int)cols, (int)nch, total, xs);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
 
 // One thread per output (token blockIdx.y, row r): the splits' raw sums added
 // in split order, so the result does not depend on which split finished first.

@@ -84,9 +84,13 @@ struct GemvArgs {
     // to part + (z * ptok + t) * prow + r (gated: up sums at prow / 2 + r);
     // part == nullptr: one split, results written to y as usual
     float *part;
-    size_t part_bytes;
     int kchunks;
     int64_t ptok, prow;
+    // prefill chunks: x split into bf16 parts by k_split_x (device scratch)
+    const uint8_t *xs;
+    // caller scratch for prefill chunks: split x, then partial sums
+    uint8_t *ws;
+    size_t ws_bytes;
 };
 
 // -------------------------------------------------------- unit dot product --
@@ -1107,13 +1111,18 @@ QG_DECL_GEMV(q6_k)
 dequant_fn dequant_kernel(int type);
 // MFMA small-batch kernels (Q8_0 / Q4_0), qg_inst_mfma.hip
 gemv_fn gemv_kernel_mfma(int type, int groups);
-// prefill chunks (qg_gemm.hip): Q8_0 / Q4_0; a tile is 4 waves of
-// gemm_rows_per_wave(glu) rows (gated: that many gate rows and the same up
-// rows) by gemm_token_tile() tokens
+// prefill chunks (qg_gemm.hip): Q8_0 / Q4_0; a workgroup of gemm_threads()
+// threads owns gemm_tile_rows(glu) rows (gated: that many gate rows and the
+// same up rows) by gemm_token_tile() tokens, one workgroup per CU
 gemv_fn gemm_kernel_mfma(int type);
-int gemm_rows_per_wave(int glu);
+int gemm_tile_rows(int glu);
+int gemm_threads();
 int gemm_token_tile();
 int gemm_chunk_values();   // row values per k-chunk
+// bytes of x [ntok][cols] split for the prefill kernel, and the launch that
+// splits it (x rows x_stride floats apart)
+size_t gemm_xs_bytes(int64_t cols, int ntok);
+int gemm_split_x(const float *x, int64_t x_stride, int ntok, int64_t cols, uint8_t *xs, hipStream_t st);
 // adds the raw sums of a.kchunks-long splits (grid.z = nsplit of them) in
 // split order and writes y (gated: act(g) * u, and g, u to y2 when set)
 int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st);

@@ -183,18 +183,20 @@ def test_gemm_token_limits():
 
 
 def test_gemm_split_workspace():
-    """Prefill launches with few row tiles split along the row: the workspace
-    holds whole [split][token][row] f32 partial sums; wide launches, the
-    K-quants and decode sizes need none."""
+    """Prefill-size Q8_0 / Q4_0 launches need scratch: x split into three bf16
+    parts (6 bytes per value of the padded chunk), plus whole [split][token][row]
+    f32 partial sums when few row tiles make the launch split along the row.
+    Decode sizes and the vector kernels need none."""
     L = qg.lib()
     n = qg.qg_gemm_workspace_size(8, 2560, 9728, 64)
-    assert n > 0 and n % 256 == 0 and n % (64 * 2560 * 4) == 0
-    assert 2 <= n // (64 * 2560 * 4) <= 32
+    xs = 64 * 9728 * 6
+    assert n % 256 == 0 and n >= xs + 2 * 64 * 2560 * 4                     # the 20-tile down splits
     assert qg.qg_gemm_workspace_size(2, 2560, 9728, 64) == n                 # Q4_0: the same tiles
-    assert qg.qg_gemm_workspace_size(8, 65536, 2560, 64) == 0                # enough row tiles already
+    wide = qg.qg_gemm_workspace_size(8, 65536, 9728, 64)                     # enough row tiles already
+    assert xs <= wide < xs + 64 * 65536 * 4
     assert qg.qg_gemm_workspace_size(8, 2560, 9728, 16) == 0                 # decode-size batches
     assert qg.qg_gemm_workspace_size(qg.QG_Q6_K, 2560, 9728, 64) == 0
-    assert qg.qg_gemm_workspace_size(8, 2560, 128, 64) == 0                  # too short to split
+    assert 64 * 128 * 6 <= qg.qg_gemm_workspace_size(8, 2560, 128, 64) < 2560 * 64 * 4   # too short to split
     assert qg.qg_gemm_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE, n - 256, None) == qg.QG_EINVAL   # short
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE + 16, n, None) == qg.QG_EINVAL    # misaligned
