@@ -269,12 +269,13 @@ gemv_fn pick(int type, const Plan &p) {
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 // Prefill launches split along the row when their row and token tiles alone
-// leave CUs idle (the 2560-row down projection of a 64-token chunk is 20
+// leave CUs idle (the 2560-row down projection of a 64-token chunk is 10
 // tiles): each split sums a run of whole k-chunks into a partial buffer, and
-// a second launch adds the splits in order.  The split count minimises
-// (rounds of resident workgroups) x (chunks per split + pipeline fill), with
-// one workgroup resident per CU (the kernel's register use) and splits of at
-// least four chunks.  The same rule sizes the workspace.
+// a second launch adds the splits in order.  The split count minimises the
+// estimated time: rounds of resident workgroups (one per CU) x (chunks per
+// split + pipeline fill) at ~2 us a chunk, plus the adding launch (a few us
+// and its bytes at ~2.5 TB/s).  Launches that fill the CUs already are not
+// split.  The same rule sizes the workspace.
 struct GemmSplit {
     int n, kchunks;
 };
@@ -287,16 +288,20 @@ GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     const int64_t tile_rows = gemm_tile_rows(glu);
     const int64_t wgs = ((rows + tile_rows - 1) / tile_rows) * ((ntok + tt - 1) / tt);
     if (wgs >= NUM_CU) return best;
-    const int64_t fill = 3;
-    int64_t best_cost = nch + fill;
+    const double step_us = 2.0, fill = 2.0;
+    // partial sums read, plus the outputs written (gated: y, gate and up)
+    const double out_bytes = (double)ntok * (double)rows * (glu ? 2.0 : 1.0) * 4.0;
+    const double out_written = glu ? 1.5 : 1.0;
+    double best_us = ((double)nch + fill) * step_us;
     for (int n = 2; n <= 32; n++) {
         const int64_t kc = (nch + n - 1) / n;
         if (kc < 4) break;
         const int64_t ns = (nch + kc - 1) / kc;
         const int64_t rounds = (wgs * ns + NUM_CU - 1) / NUM_CU;
-        const int64_t cost = rounds * (kc + fill) + fill;   // + the adding launch
-        if (cost < best_cost) {
-            best_cost = cost;
+        const double us =
+            (double)rounds * ((double)kc + fill) * step_us + 4.0 + ((double)ns + out_written) * out_bytes / 2.5e6;
+        if (us < best_us) {
+            best_us = us;
             best = {(int)ns, (int)kc};
         }
     }
@@ -345,7 +350,10 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
         a.kchunks = sp.kchunks;
         a.ptok = a.ntok;
         a.prow = (a.glu ? 2 : 1) * a.rows;
-        grid = dim3((unsigned)(a.ntiles < cap ? a.ntiles : cap), (unsigned)tchunks, split ? (unsigned)sp.n : 1u);
+        a.wg_x = (int)(a.ntiles < cap ? a.ntiles : cap);
+        a.wg_y = (int)tchunks;
+        a.wg_z = split ? sp.n : 1;
+        grid = dim3((unsigned)a.wg_x * (unsigned)a.wg_y * (unsigned)a.wg_z);
         hipLaunchKernelGGL(f, grid, dim3(gemm_threads()), 0, st, a);
         if (hipGetLastError() != hipSuccess) return QG_EHIP;
         return split ? gemm_reduce(a, sp.n, st) : QG_OK;

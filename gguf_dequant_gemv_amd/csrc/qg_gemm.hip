@@ -30,6 +30,7 @@ constexpr int GEMM_TG = 4;                      // token groups of 16 per workgr
 constexpr int GEMM_TT = 16 * GEMM_TG;
 constexpr int GEMM_WAVES = 8;                   // waves per workgroup (two per SIMD)
 constexpr int GEMM_THREADS = 64 * GEMM_WAVES;
+constexpr int NUM_XCD = 8;                      // accelerator dies, each with its own L2
 constexpr int GEMM_XROW = GEMM_KC * 2;          // bytes of one (part, token) row of a chunk
 constexpr int GEMM_XBLK = 3 * GEMM_TT * GEMM_XROW;   // bytes of one (token tile, chunk) block
 
@@ -101,8 +102,9 @@ struct GemmGeom {
 };
 
 // Workgroup tile: 8 waves x RG groups of 16 rows (gated: RG/2 gate groups and
-// the same up groups per wave) x 64 tokens; grid.x row tiles (grid-stride),
-// grid.y 64-token tiles, grid.z splits of the row.  Lane l: row / token l%16,
+// the same up groups per wave) x 64 tokens; a 1-D launch of wg_x row-tile
+// slots (grid-stride over the row tiles) x wg_y 64-token tiles x wg_z splits
+// of the row.  Lane l: row / token l%16,
 // k-group l/16 of each 32-value block; D[4(l/16)+i][l%16] = token 4(l/16)+i,
 // row l%16.
 //
@@ -124,13 +126,21 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm_mfma(GemvArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n16 = lane & 15, q = lane >> 4;
     const int nb = a.cols / 32;
+    // Workgroups go to the XCDs round-robin by launch index; renumbered so
+    // that each XCD runs one contiguous range of (split, row tile, token
+    // tile), the row tiles of a split (which read the same x chunks) and the
+    // token tiles of a row tile (the same weights) share that XCD's L2.
+    const int nwg = a.wg_x * a.wg_y * a.wg_z;
+    const int xcd = (int)blockIdx.x % NUM_XCD, per = nwg / NUM_XCD;
+    const int lid = xcd * per + min(xcd, nwg % NUM_XCD) + (int)blockIdx.x / NUM_XCD;
+    const int gy = lid % a.wg_y, gx = (lid / a.wg_y) % a.wg_x, gz = lid / (a.wg_y * a.wg_x);
     // this workgroup's k-chunks [c_lo, nch): the whole row, or one split of it
     const int nch_all = (nb + BPC - 1) / BPC;
-    const int c_lo = a.part ? (int)blockIdx.z * a.kchunks : 0;
+    const int c_lo = a.part ? gz * a.kchunks : 0;
     const int nch = a.part ? min(nch_all, c_lo + a.kchunks) : nch_all;
     const int64_t rows = a.rows;
     const u32 rb = (u32)a.row_bytes;
-    const int t0 = blockIdx.y * GEMM_TT;
+    const int t0 = gy * GEMM_TT;
     const int nt = min(GEMM_TT, a.ntok - t0);
     const int gpw = a.glu ? RG / 2 : RG;        // distinct row groups per wave
     const int tile_rows = GEMM_WAVES * 16 * gpw;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm_mfma(GemvArgs a) {
     const rsrc_t rs0 = make_rsrc(a.W0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
     const rsrc_t rs1 = make_rsrc(a.W1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
     // this token tile's split-x blocks, chunk after chunk
-    const rsrc_t rsx = make_rsrc(a.xs + (int64_t)blockIdx.y * nch_all * GEMM_XBLK, (u32)(nch_all * GEMM_XBLK));
+    const rsrc_t rsx = make_rsrc(a.xs + (int64_t)gy * nch_all * GEMM_XBLK, (u32)(nch_all * GEMM_XBLK));
     const u32 cpos = 2u + 8u * (u32)(TY == T_Q8_0 ? q : (q & 1));
     const u32 sx0 = lds_off(s_x), sw0 = lds_off(s_w);
     // this lane's x piece offset within a (part, token group) row block, per block of the chunk
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm_mfma(GemvArgs a) {
                                                      16, xbyte + 16u * (u32)(i * GEMM_THREADS + tid), 0, 0, 0);
     };
 
-    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+    for (int64_t tile = gx; tile < a.ntiles; tile += a.wg_x) {
         // this lane's row slots and rows, one per row group
         int myslot[RG];
         u32 rstart[RG];
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void k_gemm_mfma(GemvArgs a) {
                 if (t >= nt) continue;
                 const int64_t oi = t0 + t;
                 if (a.part) {   // raw sums of this split, gate and up apart
-                    float *pp = a.part + ((int64_t)blockIdx.z * a.ptok + oi) * a.prow;
+                    float *pp = a.part + ((int64_t)gz * a.ptok + oi) * a.prow;
 #pragma unroll
                     for (int gi = 0; gi < RG; gi++) {
                         const bool hi = a.glu && gi >= RG / 2;

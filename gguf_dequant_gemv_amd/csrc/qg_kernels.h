@@ -91,6 +91,9 @@ struct GemvArgs {
     // caller scratch for prefill chunks: split x, then partial sums
     uint8_t *ws;
     size_t ws_bytes;
+    // prefill chunks: the logical grid (row tiles x token tiles x splits)
+    // behind the 1-D launch
+    int wg_x, wg_y, wg_z;
 };
 
 // -------------------------------------------------------- unit dot product --
