@@ -390,35 +390,51 @@ int gemm_split_x(const float *x, int64_t x_stride, int ntok, int64_t cols, uint8
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
-// One thread per output (token blockIdx.y, row r): the splits' raw sums added
-// in split order, so the result does not depend on which split finished first.
+// One thread per V consecutive outputs (token blockIdx.y, rows r..r+V-1): the
+// splits' raw sums added in split order, so the result does not depend on
+// which split finished first.  V = 4 when every row offset is a multiple of 4
+// floats (16-byte loads and stores).
+template <int V>
 __global__ __launch_bounds__(256) void k_gemm_reduce(const float *part, int nsplit, int64_t ptok, int64_t prow,
                                                      int64_t rows, int glu, float *y, int64_t y_stride, float *y2,
                                                      int64_t y2_stride) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    typedef float vec __attribute__((ext_vector_type(V)));
+    const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
     const int64_t t = blockIdx.y;
     if (r >= rows) return;
     const float *p = part + t * prow + r;
     const int64_t zs = ptok * prow;
-    float g = 0.0f, u = 0.0f;
+    vec g = (vec)0.0f, u = (vec)0.0f;
+#pragma unroll 8
     for (int z = 0; z < nsplit; z++) {
-        g += p[z * zs];
-        if (glu) u += p[z * zs + rows];
+        g += *(const vec *)(p + z * zs);
+        if (glu) u += *(const vec *)(p + z * zs + rows);
     }
     if (glu) {
-        y[t * y_stride + r] = qg::glu(glu, g, u);
+        vec o;
+#pragma unroll
+        for (int i = 0; i < V; i++) o[i] = qg::glu(glu, g[i], u[i]);
+        *(vec *)(y + t * y_stride + r) = o;
         if (y2) {
-            y2[t * y2_stride + r] = g;
-            y2[t * y2_stride + rows + r] = u;
+            *(vec *)(y2 + t * y2_stride + r) = g;
+            *(vec *)(y2 + t * y2_stride + rows + r) = u;
         }
     } else {
-        y[t * y_stride + r] = g;
+        *(vec *)(y + t * y_stride + r) = g;
     }
 }
 
 int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st) {
-    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((a.rows + 255) / 256), (unsigned)a.ntok), dim3(256), 0, st,
-                       a.part, nsplit, a.ptok, a.prow, a.rows, a.glu, a.y, a.y_stride, a.y2, a.y2_stride);
+    const bool v4 = a.rows % 4 == 0 && a.prow % 4 == 0 && a.y_stride % 4 == 0 && ((uintptr_t)a.part & 15) == 0 &&
+                    ((uintptr_t)a.y & 15) == 0 && (!a.y2 || (a.y2_stride % 4 == 0 && ((uintptr_t)a.y2 & 15) == 0));
+    const int V = v4 ? 4 : 1;
+    const dim3 grid((unsigned)((a.rows / V + 255) / 256), (unsigned)a.ntok);
+    if (v4)
+        hipLaunchKernelGGL(k_gemm_reduce<4>, grid, dim3(256), 0, st, a.part, nsplit, a.ptok, a.prow, a.rows, a.glu,
+                           a.y, a.y_stride, a.y2, a.y2_stride);
+    else
+        hipLaunchKernelGGL(k_gemm_reduce<1>, grid, dim3(256), 0, st, a.part, nsplit, a.ptok, a.prow, a.rows, a.glu,
+                           a.y, a.y_stride, a.y2, a.y2_stride);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
