@@ -150,6 +150,14 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
             if (score > best + 1e-9) { best = score; p.lpr = lpr; }
         }
     }
+    // Q6_K at one token: per-lane loads (k_gemv) with 8 lanes per row beat the
+    // LDS-staged stream, whose rings of 210-byte units cost the residency the
+    // VALU-heavy decode needs (measured 31.9 vs 33.6 us at 5120 x 17408 and
+    // 134 vs 168 us at 262144 x 2816); x must fit the LDS whole
+    if (s.type == QG_Q6_K && nt == 1 && lds_bytes(s.type, s.nb * s.ti.block_vals, 1) <= 96 * 1024) {
+        p.kind = UK_BLOCK;
+        p.lpr = 8;
+    }
     p.nunits = unit_count(s, p.kind);
     const int uv = (lds_kind(p.kind) && s.ti.pairs) ? 2 * s.ti.qk : s.ti.block_vals;
     const int cpad = p.nunits * uv;

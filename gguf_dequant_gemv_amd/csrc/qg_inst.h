@@ -49,10 +49,11 @@ template <> struct Units<T_Q4_0> { typedef UQ4_0B B; typedef UQ4_0P P; };
 template <> struct Units<T_Q4_K> { typedef UQ4_K B; typedef UQ4_K P; };
 template <> struct Units<T_Q6_K> { typedef UQ6_K B; typedef UQ6_K P; };
 
-// UK_BLOCK exists for Q8_0 / Q4_0 only (the K-quants always stage in LDS)
+// UK_BLOCK exists for Q8_0 / Q4_0, and for Q6_K at one token per workgroup
+// (Q4_K always stages in LDS)
 template <int TY, int NT>
 gemv_fn pick(int kind, int lpr, bool xc) {
-    if constexpr (TY == T_Q8_0 || TY == T_Q4_0) {
+    if constexpr (TY == T_Q8_0 || TY == T_Q4_0 || (TY == T_Q6_K && NT == 1)) {
         if (kind == UK_BLOCK) return pick_lpr<typename Units<TY>::B, NT>(lpr);
     }
     if (kind == UK_LDS) return pick_lds<typename Units<TY>::P, NT, true>(lpr, xc);
