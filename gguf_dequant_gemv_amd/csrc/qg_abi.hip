@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "../../include/qgemv.h"
+#include "qg_moe1.h"
 #include "qg_kernels.h"
 #include "qg_block.h"
 
@@ -625,7 +626,8 @@ namespace {
 // valid the per-token validity, both inside the workspace.
 int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
                const float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
-               size_t workspace_bytes, size_t ws_extra, hipStream_t st, float **dn_out, int32_t **valid_out) {
+               size_t workspace_bytes, size_t ws_extra, hipStream_t st, float **dn_out, int32_t **valid_out,
+               bool down = true) {
     if (!m) return QG_EINVAL;
     const int E = m->n_experts;
     if (E < 1 || E > QG_MAX_EXPERTS || topk < 1 || topk > QG_MAX_TOPK || topk > E || ntok < 1 ||
@@ -692,6 +694,9 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     a.in_by_pair = 0;
     rc = launch_gemv(s_g, p1, a, dim3(1, gmax, (ntok + p1.nt - 1) / p1.nt), st);
     if (rc) return rc;
+    *dn_out = dn;
+    *valid_out = rt_valid;
+    if (!down) return QG_OK;   // the caller runs the down projection itself
 
     // 3. down on each pair's activations
     Plan p2 = make_plan(s_dn, gtok, busy, aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
@@ -737,9 +742,33 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     hipStream_t st = (hipStream_t)stream;
     float *dn = nullptr;
     int32_t *valid = nullptr;
+    // one token: the down projection of every pick and the combine in one launch
+    const bool one = m && ntok == 1 && moe_down1_fits(m->type, m->ff, topk);
     int rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace,
-                        workspace_bytes, 0, st, &dn, &valid);
+                        workspace_bytes, 0, st, &dn, &valid, !one);
     if (rc) return rc;
+    if (one) {
+        const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok);
+        uint8_t *ws = (uint8_t *)workspace;
+        Moe1Args b = {};
+        b.W = (const uint8_t *)m->down;
+        b.stride = m->down_stride;
+        b.rows = m->hidden;
+        b.row_bytes = m->ff / 32 * qg_block_bytes(m->type);
+        b.nb = (int)(m->ff / 32);
+        b.act = (const float *)(ws + L.act);
+        b.act_stride = m->ff;
+        b.ids = (const int32_t *)(ws + L.ids);
+        b.w = (const float *)(ws + L.w);
+        b.slots = expert_slots;
+        b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
+        b.escale = m->down_scale;
+        b.valid = valid;
+        b.dn = dn;
+        b.y = y;
+        b.k = topk;
+        return launch_moe_down1(m->type, b, st);
+    }
     // weighted combine in pick order
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((m->hidden + 255) / 256), ntok), dim3(256), 0, st, dn, valid, y,
                        m->hidden, topk);

@@ -45,7 +45,8 @@ def _bodies(asm):
     return out
 
 
-@pytest.mark.parametrize("tu", ["qg_inst_q8_0_t1.hip", "qg_inst_q4_k_t1.hip", "qg_inst_mfma.hip", "qg_gemm.hip"])
+@pytest.mark.parametrize("tu", ["qg_inst_q8_0_t1.hip", "qg_inst_q4_k_t1.hip", "qg_inst_q6_k_t1.hip", "qg_inst_mfma.hip",
+                                "qg_gemm.hip", "qg_moe1.hip"])
 def test_no_scratch_no_waterfall(tu, tmp_path):
     asm = _asm(tu, tmp_path)
     kern = _kernels(asm)

@@ -275,6 +275,8 @@ MOE_CASES = [
     (gs.Q8_0, 0, 2048, 768, 128, 8, 1, False),      # Qwen3-30B-A3B layer shape
     (gs.Q4_0, 1, 2816, 704, 128, 8, 16, True),      # Gemma-4 26B-A4B expert shape, T = 16
     (gs.Q4_0, 1, 2816, 704, 128, 8, 1, True),       # the same, one token
+    (gs.Q8_0, 0, 256, 1536, 16, 8, 1, True),        # one token, two blocks per lane in the down launch
+    (gs.Q4_0, 1, 320, 96, 12, 1, 1, True),          # one token, one pick
 ]
 
 
@@ -333,3 +335,25 @@ def test_moe_absent_expert_and_slots(orc):
             assert np.all(np.isnan(r["y"][tt]))
         else:
             assert np.array_equal(r["y"][tt], base["y"][tt])
+
+
+def test_moe_one_token_absent_expert_and_slots(orc):
+    """The one-token down + combine launch: a permuted expert residency gives
+    the same y bit for bit, and an absent picked expert leaves y untouched."""
+    t, act, H, F, E, k, T = gs.Q4_0, 1, 320, 192, 10, 3, 1
+    c = _moe_case(t, act, H, F, E, k, T, 6003, True)
+    say("moe-slots one token", E, k)
+    base = run_moe_gpu(c)
+    assert base["status"] == 0 and not np.any(np.isnan(base["y"]))
+    perm = np.array([4, 7, 0, 9, 1, 3, 8, 2, 6, 5], np.int32)
+    pool2 = np.empty_like(c["pool"])
+    rec = c["rec"]
+    for e in range(E):
+        pool2[perm[e] * rec:(perm[e] + 1) * rec] = c["pool"][e * rec:(e + 1) * rec]
+    moved = run_moe_gpu(c, slots=perm, perm_pool=pool2)
+    assert np.array_equal(moved["y"], base["y"])
+    slots = np.arange(E, dtype=np.int32)
+    slots[int(base["ids"][0, 2])] = -1
+    r = run_moe_gpu(c, slots=slots)
+    assert r["status"] == -2
+    assert np.all(np.isnan(r["y"]))
