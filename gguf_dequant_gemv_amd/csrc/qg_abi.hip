@@ -659,17 +659,9 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     int32_t *rt_valid = (int32_t *)(ws + L.valid);
     int32_t *grp = (int32_t *)(ws + L.grp);
 
-    // 1. route: top-k, weights, slot lookup, grouping by expert
-    const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
     const int n_slots = m->n_slots > 0 ? m->n_slots : E;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots, n_slots, ids_out,
-                       w_out, status, rt_ids, rt_w, rt_valid, grp);
-    if (hipGetLastError() != hipSuccess) return QG_EHIP;
     const int pairs = ntok * topk;
     const int gmax = pairs < E ? pairs : E;
-
-    // 2. gate and up rows of every group's expert together: act(gate) * up per
-    //    pair into act, raw gate / up into gu
     // tokens per workgroup for a group: a group holds the pairs that picked one
     // expert, on average about ntok*topk/E of them, so chunks sized for the
     // typical group (a few tokens) keep workgroups from computing copies
@@ -679,7 +671,34 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     // (a group takes the MFMA kernel only when groups typically hold 4+ tokens:
     // smaller groups would leave most of its 16 token columns empty)
     Plan p1 = make_plan(s_g, gtok, busy, aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
+    // one token on the LDS-staged kernel: that launch routes the token itself
+    const bool route_in = ntok == 1 && topk <= ROUTE1_MAXK && lds_kind(p1.kind) && p1.nt == 1;
+
+    // 1. route: top-k, weights, slot lookup, grouping by expert
+    if (!route_in) {
+        const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
+        hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots,
+                           n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp);
+        if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    }
+
+    // 2. gate and up rows of every group's expert together: act(gate) * up per
+    //    pair into act, raw gate / up into gu
     GemvArgs a = {};
+    if (route_in) {
+        a.r_logits = router_logits;
+        a.r_E = E;
+        a.r_k = topk;
+        a.r_nslots = n_slots;
+        a.r_slots = expert_slots;
+        a.r_ids_out = ids_out;
+        a.r_w_out = w_out;
+        a.r_status = status;
+        a.r_ids = rt_ids;
+        a.r_w = rt_w;
+        a.r_valid = rt_valid;
+        a.r_grp = grp;
+    }
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
     a.rows = F;
     a.slot_stride = m->gate_up_stride;

@@ -365,4 +365,28 @@ struct UQ6_K {
     QG_DEV static float value(const u32 (&w)[ND], int i) { return dsc(w, i >> 4) * (code(w, i) - 32.0f); }
 };
 
+// ---------------------------------------------------------- routing ----
+QG_DEV u32 order_key(float f) {  // monotone map f32 -> u32 (-0 folded onto +0)
+    u32 u = __builtin_bit_cast(u32, f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Maximum over the wave, uniform: DPP within each row of 16 lanes, then the
+// four row results through scalar registers.
+template <int CTRL>
+QG_DEV u32 dpp_u(u32 v) {
+    return (u32)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+QG_DEV u32 wave_max_u32(u32 v) {
+    v = max(v, dpp_u<0xB1>(v));    // lane ^ 1
+    v = max(v, dpp_u<0x4E>(v));    // lane ^ 2
+    v = max(v, dpp_u<0x141>(v));   // row_half_mirror
+    v = max(v, dpp_u<0x140>(v));   // row_mirror
+    const u32 a = (u32)__builtin_amdgcn_readlane((int)v, 0), b = (u32)__builtin_amdgcn_readlane((int)v, 16);
+    const u32 c = (u32)__builtin_amdgcn_readlane((int)v, 32), d = (u32)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+
 }  // namespace qg

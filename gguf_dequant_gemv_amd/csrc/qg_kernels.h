@@ -94,7 +94,112 @@ struct GemvArgs {
     // prefill chunks: the logical grid (row tiles x token tiles x splits)
     // behind the 1-D launch
     int wg_x, wg_y, wg_z;
+    // grouped launch routing its one token itself (r_logits set): router
+    // logits [r_E], top r_k, expert -> slot; workgroup (0, 0, 0) writes the
+    // routing outputs (ids, weights, validity, status, the group table)
+    const float *r_logits;
+    int r_E, r_k, r_nslots;
+    const int32_t *r_slots;
+    int32_t *r_ids_out, *r_status, *r_ids, *r_valid, *r_grp;
+    float *r_w_out, *r_w;
 };
+
+// ------------------------------------------- one token's routing in-launch --
+// Every wave selects the top k of the router logits itself (the keys, the
+// lowest index among equal keys and the weights of k_route), so no routing
+// launch precedes the gated expert launch.  Group g is the pick with the g-th
+// smallest expert id, the order k_route's group table lists them in.
+// Workgroup (0, 0, 0) writes what k_route writes for one token.  Returns false
+// when a pick has no pool slot (the token's groups are then empty).
+constexpr int ROUTE1_MAXK = 8;
+
+QG_DEV bool route1_group(const GemvArgs &a, int g, int &e_out, int &slot_out, int &z_out) {
+    const int lane = threadIdx.x & 63;
+    const int E = a.r_E, k = a.r_k;
+    float lv[4];
+    u32 key[4];
+    u32 taken = 0u;   // bit i: value lane + 64 i is picked or absent
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int e = lane + 64 * i;
+        lv[i] = e < E ? a.r_logits[e] : 0.0f;
+        key[i] = order_key(lv[i]);
+        if (e >= E) taken |= 1u << i;
+    }
+    int ids[ROUTE1_MAXK];
+#pragma unroll
+    for (int j = 0; j < ROUTE1_MAXK; j++) {
+        ids[j] = 0;
+        if (j < k) {
+            u32 lm = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                if (!((taken >> i) & 1u)) lm = max(lm, key[i]);
+            const u32 M = wave_max_u32(lm);
+            int e = -1;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
+                if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
+            }
+            e = __builtin_amdgcn_readfirstlane(e);
+            if ((e & 63) == lane) taken |= 1u << (e >> 6);
+            ids[j] = e;
+        }
+    }
+    int slot[ROUTE1_MAXK];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < ROUTE1_MAXK; j++) {
+        slot[j] = j < k ? a.r_slots[ids[j]] : 0;
+        if (j < k) ok = ok && slot[j] >= 0 && slot[j] < a.r_nslots;
+    }
+    // rank of each pick among the picks' expert ids (they are distinct)
+    int rank[ROUTE1_MAXK];
+    e_out = slot_out = z_out = 0;
+#pragma unroll
+    for (int j = 0; j < ROUTE1_MAXK; j++) {
+        rank[j] = 0;
+#pragma unroll
+        for (int i = 0; i < ROUTE1_MAXK; i++) rank[j] += (i < k && ids[i] < ids[j]) ? 1 : 0;
+        if (j < k && rank[j] == g) {
+            e_out = ids[j];
+            slot_out = slot[j];
+            z_out = j;
+        }
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) {
+        int idl = 0, sll = 0, rkl = 0;   // this lane's pick (lane < k)
+#pragma unroll
+        for (int j = 0; j < ROUTE1_MAXK; j++)
+            if (lane == j) { idl = ids[j]; sll = slot[j]; rkl = rank[j]; }
+        // weights over the picks, relative to the top pick
+        const float l0 = a.r_logits[ids[0]];
+        const float ex = lane < k ? expf(a.r_logits[idl] - l0) : 0.0f;
+        const float sum = wave_sum(ex);
+        if (lane < k) {
+            const float wj = ex / sum;
+            a.r_ids[lane] = idl;
+            a.r_w[lane] = wj;
+            if (a.r_ids_out) a.r_ids_out[lane] = idl;
+            if (a.r_w_out) a.r_w_out[lane] = wj;
+            if (ok) {
+                int *rec = a.r_grp + 1 + rkl * GREC;
+                rec[0] = idl;
+                rec[1] = sll;
+                rec[2] = 1;
+                rec[3] = 0;
+                rec[19] = lane;
+            }
+        }
+        if (lane == 0) {
+            a.r_valid[0] = ok ? 1 : 0;
+            if (a.r_status) a.r_status[0] = ok ? 0 : -2;   // QG_OK / QG_EABSENT
+            a.r_grp[0] = ok ? k : 0;
+        }
+    }
+    return ok;
+}
 
 // -------------------------------------------------------- unit dot product --
 // acc[t] += sum over the unit of value(i) * x_t[i], for all NT token slots
@@ -567,7 +672,24 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     int nt;
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
-    if (a.grp) {
+    bool routed = false;
+    if constexpr (NT == 1) {
+        if (a.r_logits) {   // this launch routes its one token itself
+            int e, sl, z;
+            const bool ok = route1_group(a, blockIdx.y, e, sl, z);
+            if (!ok || (int)blockIdx.y >= a.r_k || blockIdx.z > 0) return;
+            nt = 1;
+            Wg0 = a.W0 + (int64_t)sl * a.slot_stride;
+            Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
+            in_idx[0] = a.in_by_pair ? z : 0;
+            out_idx[0] = z;
+            osc_e[0] = a.escale ? a.escale[e] : 1.0f;
+            osc_p[0] = a.pscale ? a.pscale[z] : 1.0f;
+            routed = true;
+        }
+    }
+    if (routed) {
+    } else if (a.grp) {
         const int Gn = a.grp[0];
         const int g = blockIdx.y;
         if (g >= Gn) return;
