@@ -260,12 +260,12 @@ int grid_for(const Plan &p, gemv_fn f) {
 }
 
 #define QG_PICK_NT(NAME) \
-    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.kind, p.lpr, p.xchunk > 0) \
-     : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.kind, p.lpr, p.xchunk > 0) \
-     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.kind, p.lpr, p.xchunk > 0) \
-     : gemv_kernel_##NAME##_t8(p.kind, p.lpr, p.xchunk > 0))
+    (p.nt == 1 ? gemv_kernel_##NAME##_t1(p.kind, p.lpr, p.xchunk > 0, rt) \
+     : p.nt == 2 ? gemv_kernel_##NAME##_t2(p.kind, p.lpr, p.xchunk > 0, false) \
+     : p.nt == 4 ? gemv_kernel_##NAME##_t4(p.kind, p.lpr, p.xchunk > 0, false) \
+     : gemv_kernel_##NAME##_t8(p.kind, p.lpr, p.xchunk > 0, false))
 
-gemv_fn pick(int type, const Plan &p) {
+gemv_fn pick(int type, const Plan &p, bool rt) {
     switch (type) {
     case QG_Q8_0: return QG_PICK_NT(q8_0);
     case QG_Q4_0: return QG_PICK_NT(q4_0);
@@ -387,7 +387,7 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
     if (!a.glu) a.W1 = a.W0;
     if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
-    if (p.kind == UK_MFMA) return launch_mfma(s, p, a, grid, st);
+    if (p.kind == UK_MFMA) return a.r_logits ? QG_EINVAL : launch_mfma(s, p, a, grid, st);
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
     a.cols = s.cols;
     a.nunits = p.nunits;
@@ -395,7 +395,11 @@ int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     a.depth = p.depth;
     a.ring_off = p.ring_off;
     a.xchunk = p.xchunk;
-    gemv_fn f = pick(s.type, p);
+    // a launch that routes its token needs the routing instance (one token,
+    // LDS-staged, x whole); anything else would read a group table that no
+    // routing launch wrote
+    if (a.r_logits && !(p.nt == 1 && p.xchunk == 0)) return QG_EINVAL;
+    gemv_fn f = pick(s.type, p, a.r_logits != nullptr);
     if (p.lds > 64 * 1024 && hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
         return QG_EHIP;
     grid.x = grid_for(p, f);
@@ -672,7 +676,7 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     // smaller groups would leave most of its 16 token columns empty)
     Plan p1 = make_plan(s_g, gtok, busy, aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
     // one token on the LDS-staged kernel: that launch routes the token itself
-    const bool route_in = ntok == 1 && topk <= ROUTE1_MAXK && lds_kind(p1.kind) && p1.nt == 1;
+    const bool route_in = ntok == 1 && topk <= ROUTE1_MAXK && lds_kind(p1.kind) && p1.nt == 1 && p1.xchunk == 0;
 
     // 1. route: top-k, weights, slot lookup, grouping by expert
     if (!route_in) {

@@ -655,8 +655,9 @@ QG_DEV void load_x16(u32 a, f32x4 (&x)[Q]) {
 // XC: x staged in chunks (restaged inside the element loop).  Kept apart from
 // the whole-x variant: global loads inside the loop make the compiler wait for
 // every load in flight, the stage copies included, at the unit reads.
-template <class U, int L, int NT, bool ALN, bool XC>
+template <class U, int L, int NT, bool ALN, bool XC, bool RT>
 __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
+    static_assert(!RT || (NT == 1 && !XC), "a launch that routes its token serves one token, x unchunked");
     extern __shared__ float lds[];
     constexpr int RPW = 64 / L;
     constexpr int UV = U::VALUES;
@@ -673,8 +674,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
     bool routed = false;
-    if constexpr (NT == 1) {
-        if (a.r_logits) {   // this launch routes its one token itself
+    if constexpr (RT) {
+        {   // this launch routes its one token itself
             int e, sl, z;
             const bool ok = route1_group(a, blockIdx.y, e, sl, z);
             if (!ok || (int)blockIdx.y >= a.r_k || blockIdx.z > 0) return;
@@ -1224,10 +1225,10 @@ enum { UK_BLOCK = 0, UK_LDS = 1, UK_LDS2 = 2, UK_MFMA = 3 };
 // (kernel kind, lanes per row, x staged in chunks).  qg_inst_dequant.hip
 // holds the dequantizers.
 #define QG_DECL_GEMV(NAME) \
-    gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr, bool xc); \
-    gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr, bool xc); \
-    gemv_fn gemv_kernel_##NAME##_t4(int kind, int lpr, bool xc); \
-    gemv_fn gemv_kernel_##NAME##_t8(int kind, int lpr, bool xc);
+    gemv_fn gemv_kernel_##NAME##_t1(int kind, int lpr, bool xc, bool rt); \
+    gemv_fn gemv_kernel_##NAME##_t2(int kind, int lpr, bool xc, bool rt); \
+    gemv_fn gemv_kernel_##NAME##_t4(int kind, int lpr, bool xc, bool rt); \
+    gemv_fn gemv_kernel_##NAME##_t8(int kind, int lpr, bool xc, bool rt);
 QG_DECL_GEMV(q8_0)
 QG_DECL_GEMV(q4_0)
 QG_DECL_GEMV(q4_k)
