@@ -575,6 +575,27 @@ def time_workload(wl, steps, warmup):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
     log("[bench] %d steps: %.4f ms/step by events, %.4f ms/step by the host clock" % (steps, ms, wall * 1e3 / steps))
+    # after the timed region: the spread over replays timed one by one, and
+    # one step alone (a graph of a single step: the latency one token sees)
+    def timed(g, n):
+        out = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return sorted(out)
+    reps = timed(full, 20)
+    per_step = [r / per for r in reps]
+    g1 = _capture(wl.step, range(1))
+    one = timed(g1, 20)
+    q = lambda v, f: v[min(len(v) - 1, int(f * len(v)))]
+    spread = {"p10_ms": round(q(per_step, 0.1), 5), "p50_ms": round(q(per_step, 0.5), 5),
+              "p90_ms": round(q(per_step, 0.9), 5), "replays": len(reps), "steps_per_replay": per,
+              "single_step_p50_ms": round(q(one, 0.5), 5)}
+    del g1
     # dominant kernel alone, same rotation
     dper = wl.dominant_period * max(1, 32 // wl.dominant_period)
     dper = max(1, min(dper, 64))
@@ -583,14 +604,14 @@ def time_workload(wl, steps, warmup):
     while time.perf_counter() - t_w < 0.1:
         dg.replay()
         torch.cuda.synchronize()
-    reps = max(1, (steps + dper - 1) // dper)
+    nrep = max(1, (steps + dper - 1) // dper)
     e0.record()
-    for _ in range(reps):
+    for _ in range(nrep):
         dg.replay()
     e1.record()
     torch.cuda.synchronize()
-    dom_ms = e0.elapsed_time(e1) / (reps * dper)
-    return ms, dom_ms
+    dom_ms = e0.elapsed_time(e1) / (nrep * dper)
+    return ms, dom_ms, spread
 
 # ------------------------------------------------------ counter summaries --
 def source_hash():
@@ -707,7 +728,7 @@ def load_traffic(wl_key):
         return None
 
 
-def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
+def result_line(wl, ms, dom_ms, steps, warmup, cpu=None, spread=None):
     gbs = wl.bytes_per_step / (ms * 1e-3) / 1e9
     dom_gbs = wl.dominant_bytes / (dom_ms * 1e-3) / 1e9
     out = {
@@ -736,6 +757,8 @@ def result_line(wl, ms, dom_ms, steps, warmup, cpu=None):
         out["config"]["tokens_per_s"] = round(wl.ntok / (ms * 1e-3), 1)
     if cpu is not None:
         out["cpu_baseline"] = cpu
+    if spread is not None:
+        out["spread"] = spread
     return out
 
 
@@ -778,13 +801,13 @@ def main():
         torch.cuda.synchronize()
         log("[bench] %d dominant launches: %s" % (args.steps, wl.dominant))
         return
-    ms, dom_ms = time_workload(wl, args.steps, args.warmup)
+    ms, dom_ms, spread = time_workload(wl, args.steps, args.warmup)
     log("[bench] %.4f ms/step, dominant %.4f ms" % (ms, dom_ms))
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the oracle on the host cores")
         cpu = wl.cpu_baseline() if hasattr(wl, "cpu_baseline") else None
-    print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu)), flush=True)
+    print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu, spread)), flush=True)
     if args.all:
         for name in ("0", "3a", "3b", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6",
                      "p64", "p256"):
@@ -792,8 +815,8 @@ def main():
                 continue
             log("[bench] workload", name)
             w2 = make_workload(name, 0)
-            ms2, dom2 = time_workload(w2, args.steps, args.warmup)
-            log(json.dumps(result_line(w2, ms2, dom2, args.steps, args.warmup)))
+            ms2, dom2, sp2 = time_workload(w2, args.steps, args.warmup)
+            log(json.dumps(result_line(w2, ms2, dom2, args.steps, args.warmup, None, sp2)))
             del w2
             torch.cuda.empty_cache()
 
