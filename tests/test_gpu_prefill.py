@@ -94,3 +94,41 @@ def test_gemm_full_size_dense_256(orc):
     y_ref, A = orc.gemv(t, W, x, rows, cols, T, row_idx=ri)
     check_rows(y[:, ri], y_ref, A, "gemm 9728x2560 T=256")
     assert np.isfinite(y).all()
+
+
+def test_mlp_full_size_prefill_64(orc):
+    """The dense Qwen3-style MLP (2560 x 9728, Q8_0, SwiGLU) on a 64-token
+    chunk in the launch configuration the prefill bench times: gate||up split
+    along the row 3 ways, down 22 ways, each split's partial sums added by a
+    second launch.  Sampled gate / up rows for every token, every activation,
+    sampled down rows fed the GPU's activations."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    t, act, H, F, T = gs.Q8_0, 0, 2560, 9728, 64
+    g = gs.rng(8400)
+    Wg, Wu, Wd = gs.weights(t, g, F, H), gs.weights(t, g, F, H), gs.weights(t, g, H, F)
+    x = gs.activations(g, T, H)
+    say("mlp full size prefill", H, F, "T", T)
+    tg, tu, td = dev(Wg)[0], dev(Wu)[0], dev(Wd)[0]
+    xt, _ = dev(x)
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qg.qg_mlp_workspace_size(t, H, F, T) // 4, dtype=torch.float32, device="cuda")
+    qg.qg_mlp(t, act, tg, tu, td, H, F, xt, y, T, ws)
+    wsh = host(ws)
+    gu = wsh[:T * 2 * F].reshape(T, 2 * F)
+    a0 = _align256(T * 2 * F * 4) // 4
+    check_act(orc, act, gu, wsh[a0:a0 + T * F].reshape(T, F), F, "full prefill act")
+    ri = np.array(sorted(set(g.choice(F, 96, replace=False).tolist()) | {0, F - 1}), np.int64)
+    yg, Ag = orc.gemv(t, Wg, x, F, H, T, row_idx=ri)
+    yu, Au = orc.gemv(t, Wu, x, F, H, T, row_idx=ri)
+    check_rows(gu[:, ri], yg, Ag, "full prefill gate")
+    check_rows(gu[:, F + ri], yu, Au, "full prefill up")
+    rd = np.array(sorted(set(g.choice(H, 96, replace=False).tolist()) | {0, H - 1}), np.int64)
+    Wsub = np.ascontiguousarray(Wd[rd])   # the sampled rows' blocks ([rows][row bytes])
+    Wabs = np.abs(orc.dequant(t, Wsub, rd.size * F).reshape(rd.size, F))
+    yh = host(y)
+    assert np.isfinite(yh).all()
+    for tt in range(T):
+        yd, Ad = orc.gemv_f64(t, Wsub, orc.glu(act, gu[tt], F), rd.size, F)
+        R = Wabs @ np.abs(gu[tt, :F].astype(np.float64) * gu[tt, F:].astype(np.float64))
+        assert np.all(np.abs(yh[tt, rd] - yd) <= TOL * Ad + 1e-6 * R), "full prefill down token %d" % tt
