@@ -42,6 +42,8 @@ def parse():
                          "head6; prefill chunks p64, p256")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="issue a step's independent branches in order on one stream (default: two streams)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = default)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (calibrates the HBM byte counters)")
@@ -77,6 +79,32 @@ class Workload:
 
     def output(self):
         raise NotImplementedError
+
+
+# Independent branches of a step (the dense MLP beside the routed experts)
+# run on a second stream, forked from and joined back into the current one
+# with events, as a serving engine would issue them; the graph capture takes
+# the fork and join in.  --one-stream issues everything in order instead.
+TWO_STREAMS = True
+
+
+class Branches:
+    def __init__(self):
+        import torch
+        self.side = torch.cuda.Stream() if TWO_STREAMS else None   # default priority
+
+    def run(self, side_fn, main_fn):
+        import torch
+        if self.side is None:
+            side_fn(None)
+            main_fn()
+            return
+        cur = torch.cuda.current_stream()
+        self.side.wait_stream(cur)      # fork: after everything already issued
+        with torch.cuda.stream(self.side):
+            side_fn(self.side)
+        main_fn()
+        cur.wait_stream(self.side)      # join
 
 
 def _gen(seed):
@@ -231,6 +259,7 @@ class MoeLayers(Workload):
         self.rec = rec
         self.dense_bytes = (2 * dense_ff * rb_gu + H * gs.row_bytes(t, dense_ff)) if dense_ff else 0
         if dense_ff:
+            self.branches = Branches()
             self.ym = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
             self.wsm = torch.empty(qg.qg_mlp_workspace_size(t, H, dense_ff, ntok) // 4, dtype=torch.float32,
                                    device="cuda")
@@ -243,11 +272,14 @@ class MoeLayers(Workload):
 
     def step(self, i):
         L = self.layers[i % len(self.layers)]
-        if self.dense_ff:
-            self.qg.qg_mlp(self.t, self.act, L["Wg"], L["Wu"], L["Wd"], self.H, self.dense_ff, L["x"], self.ym,
-                           self.ntok, self.wsm)
-        self.qg.qg_moe_ffn(L["m"], L["lg"], self.k, self.slots, L["x"], self.y, self.ntok, self.ids, self.w,
-                           self.status, self.ws)
+        moe = lambda: self.qg.qg_moe_ffn(L["m"], L["lg"], self.k, self.slots, L["x"], self.y, self.ntok, self.ids,
+                                         self.w, self.status, self.ws)
+        if not self.dense_ff:
+            moe()
+            return
+        dense = lambda st: self.qg.qg_mlp(self.t, self.act, L["Wg"], L["Wu"], L["Wd"], self.H, self.dense_ff,
+                                          L["x"], self.ym, self.ntok, self.wsm, stream=st)
+        self.branches.run(dense, moe)
 
     def output(self):
         return self.y
@@ -337,6 +369,7 @@ class GemmaBlock(Workload):
         import gguf_dequant_gemv_amd as qg
         t = gs.Q4_0
         self.qg, self.ntok, self.k, self.H, self.E, self.Fd = qg, ntok, k, H, E, Fd
+        self.branches = Branches()
         rb_h, rb_f, rb_d = gs.row_bytes(t, H), gs.row_bytes(t, F), gs.row_bytes(t, Fd)
         rec = 2 * F * rb_h + H * rb_f
         g = _gen(900 + ntok)
@@ -384,14 +417,20 @@ class GemmaBlock(Workload):
 
     def step_layer(self, L):
         qg, T, H = self.qg, self.ntok, self.H
-        qg.qg_rmsnorm(L["x"], L["w_ffn"], self.xn, H, T, 1e-6, 1.0)
-        qg.qg_mlp(qg.QG_Q4_0, qg.QG_ACT_GELU_TANH, L["Wg"], L["Wu"], L["Wd"], H, self.Fd, self.xn, self.md, T,
-                  self.wsm)
-        qg.qg_rmsnorm(L["x"], L["w_pre2"], self.xm, H, T, 1e-6, 1.0)
-        qg.qg_rmsnorm(L["x"], L["w_rs"], self.rt, H, T, 1e-6, self.kr)
-        qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
-        qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
-                      self.ws)
+
+        def dense(st):   # ffn_norm, then the dense GELU MLP
+            qg.qg_rmsnorm(L["x"], L["w_ffn"], self.xn, H, T, 1e-6, 1.0, stream=st)
+            qg.qg_mlp(qg.QG_Q4_0, qg.QG_ACT_GELU_TANH, L["Wg"], L["Wu"], L["Wd"], H, self.Fd, self.xn, self.md, T,
+                      self.wsm, stream=st)
+
+        def experts():   # pre_ffw_norm_2 and the router's norm, the router, the experts
+            qg.qg_rmsnorm(L["x"], L["w_pre2"], self.xm, H, T, 1e-6, 1.0)
+            qg.qg_rmsnorm(L["x"], L["w_rs"], self.rt, H, T, 1e-6, self.kr)
+            qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
+            qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
+                          self.ws)
+
+        self.branches.run(dense, experts)
         qg.qg_post_ffn(self.md, self.moe, L["w1"], L["w2"], L["w"], L["os"], L["x"], H, T, 1e-6)
 
     def step(self, i):
@@ -755,6 +794,8 @@ def result_line(wl, ms, dom_ms, steps, warmup, cpu=None, spread=None):
         out["roofline"].update(bound="mfma", achieved=round(tf, 2), peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
                                frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), flops_per_launch=wl.flops_per_step)
         out["config"]["tokens_per_s"] = round(wl.ntok / (ms * 1e-3), 1)
+    if hasattr(wl, "branches"):
+        out["config"]["streams"] = 2 if wl.branches.side is not None else 1
     if cpu is not None:
         out["cpu_baseline"] = cpu
     if spread is not None:
@@ -763,7 +804,9 @@ def result_line(wl, ms, dom_ms, steps, warmup, cpu=None, spread=None):
 
 
 def main():
+    global TWO_STREAMS
     args = parse()
+    TWO_STREAMS = not args.one_stream
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path has no multi-GPU leg); "
               "run with --gpus 1", file=sys.stderr)
