@@ -334,6 +334,21 @@ size_t gemm_scratch_bytes(int type, int64_t rows, int64_t cols, int ntok, int gl
     return ((gemm_xs_bytes(cols, ntok) + 255) & ~(size_t)255) + gemm_part_bytes(type, rows, cols, ntok, glu);
 }
 
+// the same for a qg_gemm call, whose rows go out in launches of at most
+// MAX_RANGE weight bytes: the largest any of those launches needs (a short
+// last launch may split its rows where the full-size ones do not)
+size_t gemm_call_scratch_bytes(int type, int64_t rows, int64_t cols, int ntok) {
+    Shape s;
+    if (make_shape(type, rows, cols, s)) return 0;
+    const int64_t chunk = MAX_RANGE / s.row_bytes;
+    size_t need = gemm_scratch_bytes(type, rows < chunk ? rows : chunk, cols, ntok, 0);
+    if (rows > chunk && rows % chunk) {
+        const size_t last = gemm_scratch_bytes(type, rows % chunk, cols, ntok, 0);
+        if (last > need) need = last;
+    }
+    return need;
+}
+
 // a: weights, x/y, tokens or groups and rows set by the caller.
 int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
     a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
@@ -459,7 +474,7 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
     if (rc) return rc;
     if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
-    if (ws_bytes < gemm_scratch_bytes(type, rows, cols, ntok, 0) || (ws_bytes && (!ws || !aligned(ws, 256))))
+    if (ws_bytes < gemm_call_scratch_bytes(type, rows, cols, ntok) || (ws_bytes && (!ws || !aligned(ws, 256))))
         return QG_EINVAL;
     // rows in launches of at most MAX_RANGE weight bytes each
     const int64_t chunk = MAX_RANGE / s.row_bytes;
@@ -493,7 +508,7 @@ int qg_gemv(int type, const void *W, const float *x, float *y, int64_t rows, int
 
 size_t qg_gemm_workspace_size(int type, int64_t rows, int64_t cols, int ntok) {
     if (rows <= 0 || cols <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
-    return gemm_scratch_bytes(type, rows, cols, ntok, 0);
+    return gemm_call_scratch_bytes(type, rows, cols, ntok);
 }
 
 int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, void *workspace,

@@ -198,6 +198,12 @@ def test_gemm_split_workspace():
     assert qg.qg_gemm_workspace_size(qg.QG_Q6_K, 2560, 9728, 64) == 0
     assert 64 * 128 * 6 <= qg.qg_gemm_workspace_size(8, 2560, 128, 64) < 2560 * 64 * 4   # too short to split
     assert qg.qg_gemm_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0
+    # a tensor past 2 GiB goes out in row launches; its short last launch
+    # splits along the row where the full ones do not, and the size covers it
+    chunk = (1 << 31) // (8192 // 32 * 34)
+    full = qg.qg_gemm_workspace_size(8, chunk, 8192, 64)
+    assert qg.qg_gemm_workspace_size(8, chunk + 100, 8192, 64) >= full + 2 * 64 * 100 * 4
+    assert qg.qg_gemm_workspace_size(8, 2 * chunk, 8192, 64) == full
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE, n - 256, None) == qg.QG_EINVAL   # short
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE + 16, n, None) == qg.QG_EINVAL    # misaligned
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, None, n, None) == qg.QG_EINVAL         # null
