@@ -359,9 +359,9 @@ class Qwen35Block(Workload):
 
 class GemmaBlock(Workload):
     """Gemma4-26B-A4B-style FFN block at Q4_0, T tokens, over L layers: three
-    RMS norms of the residual stream, the dense GELU MLP, the f32 router, the
-    routed experts, and the FFN tail into the residual (qg_rmsnorm, qg_mlp,
-    qg_gemv QG_F32, qg_moe_ffn, qg_post_ffn)."""
+    RMS norms of the residual stream (one launch), the dense GELU MLP, the f32
+    router, the routed experts, and the FFN tail into the residual
+    (qg_rmsnorm_multi, qg_mlp, qg_gemv QG_F32, qg_moe_ffn, qg_post_ffn)."""
 
     def __init__(self, ntok, layers=16, H=2816, Fd=2112, E=128, F=704, k=8):
         import torch
@@ -418,14 +418,15 @@ class GemmaBlock(Workload):
     def step_layer(self, L):
         qg, T, H = self.qg, self.ntok, self.H
 
-        def dense(st):   # ffn_norm, then the dense GELU MLP
-            qg.qg_rmsnorm(L["x"], L["w_ffn"], self.xn, H, T, 1e-6, 1.0, stream=st)
+        # ffn_norm, pre_ffw_norm_2 and the router's scaled norm in one launch
+        qg.qg_rmsnorm_multi(L["x"], H, T, 1e-6, [L["w_ffn"], L["w_pre2"], L["w_rs"]], [1.0, 1.0, self.kr],
+                            [self.xn, self.xm, self.rt])
+
+        def dense(st):   # the dense GELU MLP
             qg.qg_mlp(qg.QG_Q4_0, qg.QG_ACT_GELU_TANH, L["Wg"], L["Wu"], L["Wd"], H, self.Fd, self.xn, self.md, T,
                       self.wsm, stream=st)
 
-        def experts():   # pre_ffw_norm_2 and the router's norm, the router, the experts
-            qg.qg_rmsnorm(L["x"], L["w_pre2"], self.xm, H, T, 1e-6, 1.0)
-            qg.qg_rmsnorm(L["x"], L["w_rs"], self.rt, H, T, 1e-6, self.kr)
+        def experts():   # the router, the experts
             qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
             qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
                           self.ws)

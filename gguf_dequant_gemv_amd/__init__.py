@@ -12,7 +12,7 @@ import os
 QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
-QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL = 16, 256, 32, 4096
+QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL, QG_MAX_NORMS = 16, 256, 32, 4096, 4
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemv.so")
@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
            "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
-           "qg_moe_ffn", "qg_rmsnorm", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
+           "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
 
 _lib = None
@@ -72,6 +72,8 @@ def lib():
         L.qg_moe_ffn.argtypes = [ctypes.POINTER(qg_moe), P, i32, P, P, P, i32, P, P, P, P, sz, P]
         f = ctypes.c_float
         L.qg_rmsnorm.argtypes = [P, P, P, i64, i32, f, f, P]
+        L.qg_rmsnorm_multi.argtypes = [P, i64, i32, f, i32, ctypes.POINTER(P), ctypes.POINTER(f),
+                                       ctypes.POINTER(P), P]
         L.qg_moe_shared_workspace_size.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_shared_expert), i32,
                                                    i32]
         L.qg_moe_shared_workspace_size.restype = sz
@@ -180,6 +182,18 @@ def _nbytes(t, given):
 
 def qg_rmsnorm(x, w, y, n, ntok, eps, k=1.0, stream=None):
     _check("qg_rmsnorm", lib().qg_rmsnorm(_ptr(x), _ptr(w), _ptr(y), n, ntok, eps, k, _stream(stream)))
+
+
+def qg_rmsnorm_multi(x, n, ntok, eps, ws, ks, ys, stream=None):
+    """ws, ys: sequences of device buffers; ks: sequence of floats (host)."""
+    m = len(ws)
+    if len(ks) != m or len(ys) != m:
+        raise ValueError("qg_rmsnorm_multi: ws, ks and ys differ in length")
+    P, f = ctypes.c_void_p, ctypes.c_float
+    wa = (P * max(m, 1))(*[_ptr(t) for t in ws])
+    ya = (P * max(m, 1))(*[_ptr(t) for t in ys])
+    ka = (f * max(m, 1))(*ks)
+    _check("qg_rmsnorm_multi", lib().qg_rmsnorm_multi(_ptr(x), n, ntok, eps, m, wa, ka, ya, _stream(stream)))
 
 
 def make_shared_expert(type, ff, gate, up, down, gate_inp):

@@ -858,6 +858,16 @@ int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, fl
     return launch_rmsnorm(x, w, y, n, ntok, eps, k, (hipStream_t)stream);
 }
 
+int qg_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, const float *const *w,
+                     const float *k, float *const *y, void *stream) {
+    if (n <= 0 || ntok < 1 || !x || !aligned(x, 4) || !(eps >= 0.0f)) return QG_EINVAL;
+    if (nout < 1 || nout > QG_MAX_NORMS) return QG_ELIMIT;
+    if (!w || !k || !y) return QG_EINVAL;
+    for (int j = 0; j < nout; j++)
+        if (!w[j] || !y[j] || !aligned(w[j], 4) || !aligned(y[j], 4)) return QG_EINVAL;
+    return launch_rmsnorm_multi(x, n, ntok, eps, nout, w, k, y, (hipStream_t)stream);
+}
+
 int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2, const float *w,
                 const float *out_scale, float *x, int64_t n, int ntok, float eps, void *stream) {
     if (n <= 0 || ntok < 1 || !(eps >= 0.0f)) return QG_EINVAL;

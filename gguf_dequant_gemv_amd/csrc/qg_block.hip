@@ -34,11 +34,8 @@ constexpr int LB = 16;
 // qwen3_moe_ssd.js rmsnorm kernel (k = 1) and gemma4_moe_ssd.js rmsnormK (the
 // router input: k = 1/sqrt(H), w the router's scale vector).  Every x is read
 // for the sum before any y is written, so y may be x.
-__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w, float *y, int64_t n, float eps,
-                                                 float k) {
+QG_DEV void k_rmsnorm_row(const float *xt, const float *w, float *yt, int64_t n, float eps, float k) {
     __shared__ float s_red[4];
-    const float *xt = x + (int64_t)blockIdx.x * n;
-    float *yt = y + (int64_t)blockIdx.x * n;
     float ss = 0.0f;
     for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
         float v[LB];
@@ -60,6 +57,24 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w,
         for (int b = 0; b < LB; b++)
             if (i0 + b * 256 < n) yt[i0 + b * 256] = ((v[b] * r) * k) * g[b];
     }
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *x, const float *w, float *y, int64_t n, float eps,
+                                                 float k) {
+    k_rmsnorm_row(x + (int64_t)blockIdx.x * n, w, y + (int64_t)blockIdx.x * n, n, eps, k);
+}
+
+// The same norms of one row into several outputs: workgroup (token, o)
+// computes the row's factor as k_rmsnorm does and writes output o.
+struct NormOuts {
+    const float *w[QG_MAX_NORMS];
+    float *y[QG_MAX_NORMS];
+    float k[QG_MAX_NORMS];
+};
+
+__global__ __launch_bounds__(256) void k_rmsnorm_multi(const float *x, int64_t n, float eps, NormOuts o) {
+    const int j = blockIdx.y;
+    k_rmsnorm_row(x + (int64_t)blockIdx.x * n, o.w[j], o.y[j] + (int64_t)blockIdx.x * n, n, eps, o.k[j]);
 }
 
 // ------------------------------------------------------------ f32 GEMV ----
@@ -374,6 +389,18 @@ __global__ __launch_bounds__(64) void k_argmax_final(const float *pv, const int3
 int launch_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k,
                    hipStream_t st) {
     hipLaunchKernelGGL(k_rmsnorm, dim3(ntok), dim3(256), 0, st, x, w, y, n, eps, k);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, const float *const *w,
+                         const float *k, float *const *y, hipStream_t st) {
+    NormOuts o = {};
+    for (int j = 0; j < nout; j++) {
+        o.w[j] = w[j];
+        o.y[j] = y[j];
+        o.k[j] = k[j];
+    }
+    hipLaunchKernelGGL(k_rmsnorm_multi, dim3(ntok, nout), dim3(256), 0, st, x, n, eps, o);
     return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
 }
 

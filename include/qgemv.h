@@ -214,6 +214,19 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk,
 int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k,
                void *stream);
 
+/* Several RMS norms of the same vectors in one launch: output o is
+ *   y_o[t][i] = ((x[t][i] * r_t) * k[o]) * w_o[i]
+ * with r_t as in qg_rmsnorm, bit for bit what nout qg_rmsnorm calls give.
+ * Gemma's FFN block takes three of them from one residual row: ffn_norm (the
+ * dense MLP's input), pre_ffw_norm_2 (the experts' input) and the router's
+ * rmsnormK ([gemma4] encodeLayer's norms before the FFN).
+ * w, y, k: HOST arrays of nout entries (device pointers w[o], y[o]; factors
+ * k[o]); no y[o] may overlap x or another y.  1 <= nout <= QG_MAX_NORMS.
+ * Errors: as qg_rmsnorm, and QG_ELIMIT for nout outside 1..QG_MAX_NORMS. */
+#define QG_MAX_NORMS 4
+int qg_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, const float *const *w,
+                     const float *k, float *const *y, void *stream);
+
 /* The shared expert of a MoE block (a HOST struct; its pointers are device
  * pointers): a dense gated MLP with ff SF beside the routed experts, scaled
  * by the logistic of a scalar gate logit ([qwen35] ffn_gate_shexp,

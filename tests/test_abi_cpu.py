@@ -132,6 +132,15 @@ def test_rmsnorm_post_ffn_rejects():
     assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 64, 1, -1.0, 1.0, None) == qg.QG_EINVAL
     assert L.qg_rmsnorm(FAKE, FAKE, FAKE, 64, 1, float("nan"), 1.0, None) == qg.QG_EINVAL
     assert L.qg_rmsnorm(FAKE + 2, FAKE, FAKE, 64, 1, 1e-6, 1.0, None) == qg.QG_EINVAL
+    P, f = ctypes.c_void_p, ctypes.c_float
+    w3, y3, k3 = (P * 5)(*[FAKE] * 5), (P * 5)(*[FAKE + 4096] * 5), (f * 5)(*[1.0] * 5)
+    multi = lambda n=64, T=1, eps=1e-6, m=3, w=w3, k=k3, y=y3, x=FAKE: L.qg_rmsnorm_multi(x, n, T, eps, m, w, k, y,
+                                                                                         None)
+    assert multi(m=0) == qg.QG_ELIMIT and multi(m=qg.QG_MAX_NORMS + 1) == qg.QG_ELIMIT
+    assert multi(n=0) == qg.QG_EINVAL and multi(T=0) == qg.QG_EINVAL and multi(eps=-1.0) == qg.QG_EINVAL
+    assert multi(x=FAKE + 2) == qg.QG_EINVAL
+    assert multi(w=(P * 3)(FAKE, None, FAKE)) == qg.QG_EINVAL
+    assert multi(y=(P * 3)(FAKE, FAKE + 2, FAKE)) == qg.QG_EINVAL
     assert L.qg_post_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 1, 1e-6, None) == qg.QG_EINVAL
     assert L.qg_post_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1e-6, None) == qg.QG_EINVAL
 

@@ -73,6 +73,27 @@ def test_rmsnorm(orc, n, T, k, inplace):
     check_rel(host(y), orc.rmsnorm(x, w, n, T, 1e-6, k), "rmsnorm")
 
 
+@pytest.mark.parametrize("n,T,nout", [(2816, 1, 3), (2816, 16, 3), (1000, 3, 4), (64, 2, 1)])
+def test_rmsnorm_multi(orc, n, T, nout):
+    """Several norms of one row in a launch: bit for bit the separate
+    qg_rmsnorm calls, and each against the oracle."""
+    import gguf_dequant_gemv_amd as qg
+    g = gs.rng(300 + n + T + nout)
+    x = gs.activations(g, T, n) * np.float32(2.0)
+    ws = [gs.norm_weights(g, n) for _ in range(nout)]
+    ks = [1.0, float(1.0 / np.sqrt(n)), 0.5, 3.0][:nout]
+    say("rmsnorm multi", n, "T", T, "outputs", nout)
+    xt, _ = dev(x)
+    wts = [dev(w)[0] for w in ws]
+    ys = [_empty((T, n)) for _ in range(nout)]
+    qg.qg_rmsnorm_multi(xt, n, T, 1e-6, wts, ks, ys)
+    for j in range(nout):
+        one = _empty((T, n))
+        qg.qg_rmsnorm(xt, wts[j], one, n, T, 1e-6, ks[j])
+        assert np.array_equal(host(ys[j]), host(one)), "output %d differs from qg_rmsnorm" % j
+        check_rel(host(ys[j]), orc.rmsnorm(x, ws[j], n, T, 1e-6, ks[j]), "rmsnorm multi %d" % j)
+
+
 # ------------------------------------------------- shared-expert MoE block --
 def run_shared_gpu(c, lt=None, xt=None, resid=None):
     """qg_moe_ffn_shared on case c; lt / xt / resid: device tensors to use in
