@@ -277,6 +277,8 @@ MOE_CASES = [
     (gs.Q4_0, 1, 2816, 704, 128, 8, 1, True),       # the same, one token
     (gs.Q8_0, 0, 256, 1536, 16, 8, 1, True),        # one token, two blocks per lane in the down launch
     (gs.Q4_0, 1, 320, 96, 12, 1, 1, True),          # one token, one pick
+    (gs.Q8_0, 0, 256, 128, 256, 8, 1, False),       # one token, 256 experts: four logits per lane in the routing
+    (gs.Q4_0, 1, 320, 96, 200, 8, 1, True),         # one token, a ragged expert count
 ]
 
 
