@@ -884,10 +884,8 @@ int qg_embed(int type, const void *W, int64_t rows, int64_t cols, const int32_t 
     if (rc) return rc;
     if (ntok < 1 || ntok > 65535) return QG_ELIMIT;
     if (!W || !tokens || !out || !aligned(W, 2) || !aligned(tokens, 4) || !aligned(out, 4)) return QG_EINVAL;
-    dim3 grid((unsigned)((s.nb + 255) / 256), ntok);
-    hipLaunchKernelGGL(embed_kernel(type), grid, dim3(256), 0, (hipStream_t)stream, (const uint8_t *)W, rows, s.cols,
-                       s.row_bytes, tokens, scale, out);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+    return launch_embed(type, (const uint8_t *)W, rows, (int)s.cols, s.row_bytes, tokens, ntok, scale, out,
+                        (hipStream_t)stream);
 }
 
 size_t qg_argmax_workspace_size(int64_t n, int ntok) {

@@ -6,8 +6,8 @@
 
 namespace qg {
 
-typedef void (*embed_fn)(const uint8_t *, int64_t, int, int64_t, const int32_t *, float, float *);
-embed_fn embed_kernel(int type);
+int launch_embed(int type, const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, const int32_t *tok,
+                 int ntok, float scale, float *out, hipStream_t st);
 
 // argmax: logits per workgroup in the first phase, and at most this many
 // partial results per token

@@ -260,37 +260,73 @@ __global__ __launch_bounds__(256) void k_post_ffn(const float *mlp, const float 
 }
 
 // ------------------------------------------------------ embedding rows ----
-// out[t][c] = value(W[tok[t]][c]) * scale: one thread per block of the row,
-// decoded by the same block units as the GEMV (qwen3_moe_ssd.js embedQ8,
-// gemma4_moe_ssd.js embedQ6K with its scale).  A token outside [0, rows)
-// reads nothing and gets a row of NaN.
+// out[t][c] = value(W[tokens[t]][c]) * scale, decoded by the same block units
+// as the GEMV (qwen3_moe_ssd.js embedQ8, gemma4_moe_ssd.js embedQ6K with its
+// scale).  A lane writes 8 values of one block: wave w of the grid takes part
+// w % P (values 8p .. 8p+7, P = VALUES / 8 parts a block) of 64 consecutive
+// blocks, so the part -- and with it every register index of the decode -- is
+// the same across the wave.  A token outside [0, rows) reads nothing and gets
+// a row of NaN.
+constexpr int EMBED_VALUES = 8;   // values per lane
+
+template <class U, int P>
+QG_DEV void embed8(const u32 (&w)[U::ND], float scale, float *o) {
+#pragma unroll
+    for (int i = 0; i < EMBED_VALUES; i++) o[i] = U::value(w, EMBED_VALUES * P + i) * scale;
+}
+
+// the part p (wave-uniform) as a chain of uniform branches to unrolled code
+template <class U, int P = 0>
+QG_DEV void embed_part(int p, const u32 (&w)[U::ND], float scale, float *o) {
+    if constexpr (P < U::VALUES / EMBED_VALUES) {
+        if (p == P)
+            embed8<U, P>(w, scale, o);
+        else
+            embed_part<U, P + 1>(p, w, scale, o);
+    }
+}
+
 template <class U>
 __global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
                                                const int32_t *tok, float scale, float *out) {
+    constexpr int NP = U::VALUES / EMBED_VALUES;
     const int nbr = cols / U::VALUES;
-    const int b = blockIdx.x * 256 + threadIdx.x;
+    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int p = gw % NP;
+    const int b = (gw / NP) * 64 + (threadIdx.x & 63);
     if (b >= nbr) return;
     const int32_t id = tok[blockIdx.y];
-    float *o = out + (int64_t)blockIdx.y * cols + (int64_t)b * U::VALUES;
+    float *o = out + (int64_t)blockIdx.y * cols + (int64_t)b * U::VALUES + EMBED_VALUES * p;
     if (id < 0 || id >= rows) {
-        for (int i = 0; i < U::VALUES; i++) o[i] = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < EMBED_VALUES; i++) o[i] = __builtin_nanf("");
         return;
     }
-    const uint8_t *p = W + (int64_t)id * row_bytes + (int64_t)b * U::BYTES;
-    const u32 ph = (u32)((uintptr_t)p & 3u);
-    const rsrc_t rs = make_rsrc(p - ph, (u32)(ph + U::BYTES + 3) & ~3u);
+    const uint8_t *q = W + (int64_t)id * row_bytes + (int64_t)b * U::BYTES;
+    const u32 ph = (u32)((uintptr_t)q & 3u);
+    const rsrc_t rs = make_rsrc(q - ph, (u32)(ph + U::BYTES + 3) & ~3u);
     u32 w[U::ND];
     U::load(rs, ph, w);
-#pragma unroll
-    for (int i = 0; i < U::VALUES; i++) o[i] = U::value(w, i) * scale;
+    embed_part<U>(p, w, scale, o);
 }
 
-embed_fn embed_kernel(int type) {
+template <class U>
+static int launch_embed_t(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, const int32_t *tok,
+                          int ntok, float scale, float *out, hipStream_t st) {
+    const int nbr = cols / U::VALUES;
+    const int64_t waves = (int64_t)((nbr + 63) / 64) * (U::VALUES / EMBED_VALUES);
+    const dim3 grid((unsigned)((waves + 3) / 4), ntok);
+    hipLaunchKernelGGL(k_embed<U>, grid, dim3(256), 0, st, W, rows, cols, row_bytes, tok, scale, out);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_embed(int type, const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, const int32_t *tok,
+                 int ntok, float scale, float *out, hipStream_t st) {
     switch (type) {
-    case T_Q8_0: return k_embed<UQ8_0B>;
-    case T_Q4_0: return k_embed<UQ4_0B>;
-    case T_Q4_K: return k_embed<UQ4_K>;
-    default: return k_embed<UQ6_K>;
+    case T_Q8_0: return launch_embed_t<UQ8_0B>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
+    case T_Q4_0: return launch_embed_t<UQ4_0B>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
+    case T_Q4_K: return launch_embed_t<UQ4_K>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
+    default: return launch_embed_t<UQ6_K>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
     }
 }
 

@@ -245,11 +245,12 @@ def test_post_ffn(orc, n, T):
 
 # --------------------------------------------------------- embedding rows --
 @pytest.mark.parametrize("t", [gs.Q8_0, gs.Q4_0, gs.Q4_K, gs.Q6_K])
-@pytest.mark.parametrize("cols_blocks,off", [(64, 0), (3, 2)])
-def test_embed_bit_exact(orc, t, cols_blocks, off):
+@pytest.mark.parametrize("blocks,kblocks,off", [(64, 8, 0), (3, 1, 2), (130, 70, 2), (80, 11, 0)])
+def test_embed_bit_exact(orc, t, blocks, kblocks, off):
+    """A lane per 8 values and a wave per (part, 64 blocks): one and several
+    chunks of 64 blocks, a ragged last chunk, odd 2-byte offsets."""
     import gguf_dequant_gemv_amd as qg
-    if t in (gs.Q4_K, gs.Q6_K):
-        cols_blocks = max(1, cols_blocks // 8)
+    cols_blocks = kblocks if t in (gs.Q4_K, gs.Q6_K) else blocks
     rows, cols = 300, cols_blocks * gs.QK[t]
     W = gs.weights(t, gs.rng(400 + t + cols), rows, cols)
     tokens = np.array([0, 299, 17, 17, 150], np.int32)
