@@ -68,6 +68,7 @@ struct Plan {
     int64_t copies;      // independent problems sharing the GPU in one launch
     int depth;           // UK_LDS: stages in flight per wave
     bool valu_heavy;     // K-quant units: decode-bound rather than HBM-bound
+    bool fill_all;       // grid-stride launches take every resident slot
     int ring_off;        // UK_LDS: byte offset of the stage rings in LDS
     int xchunk;          // UK_LDS: row elements per staged x chunk (0: all of x)
     size_t lds;
@@ -110,6 +111,7 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
         p.depth = 0;
         p.ring_off = 0;
         p.valu_heavy = false;
+        p.fill_all = false;
         p.lds = 0;
         p.ntiles = 0;     // set at launch (gated tiles hold half the rows)
         p.xchunk = 0;
@@ -170,6 +172,13 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
     p.ring_off = 0;
     p.xchunk = 0;
     p.valu_heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
+    // Every resident slot also pays for the grouped expert launches of Q4_0
+    // (twice the values per byte of Q8_0, and one decode shared by at most a
+    // chunk of a few tokens): at 128 experts 704 x 2816, top-8, measured
+    // 91.5 -> 67.6 us at 8 tokens and 150.8 -> 115.8 us at 16 (gate-up plus
+    // down).  Grouped Q8_0 stays on the long streams (256 experts 512 x 2048,
+    // 16 tokens: 89.1 us on them, 98.7 us on every slot).
+    p.fill_all = p.valu_heavy || (s.type == QG_Q4_0 && p.copies > 1);
     if (lds_kind(p.kind)) {
         // stage rings after x: two stages per wave when two workgroups still
         // fit a CU's 160 KiB, else one (a stage is refilled as soon as it has
@@ -240,7 +249,7 @@ int grid_for(const Plan &p, gemv_fn f) {
         // longer HBM streams measured faster than filling every slot)
         if (p.ntiles <= cap) return p.ntiles;
         // the K-quant decode is VALU-heavy: there every resident slot helps
-        int64_t target = p.valu_heavy ? cap : 2 * NUM_CU / p.copies;
+        int64_t target = p.fill_all ? cap : 2 * NUM_CU / p.copies;
         if (target < 1) target = 1;
         if (target > cap) target = cap;
         const int64_t tpw = (p.ntiles + target - 1) / target;
