@@ -545,7 +545,7 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
         return QG_EINVAL;
     hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * ntok), 0, (hipStream_t)stream, logits, n_experts, k, ntok,
                        (const int32_t *)nullptr, 1, ids, weights, (int32_t *)nullptr, ids, weights,
-                       (int32_t *)nullptr, (int32_t *)nullptr);
+                       (int32_t *)nullptr, (int32_t *)nullptr, 0, (int32_t *)nullptr, 0, (int32_t *)nullptr);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
@@ -621,7 +621,7 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
 //   w [T*k] f32 | valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32
 namespace {
 struct MoeWs {
-    size_t gu, act, dn, ids, w, valid, grp, total;
+    size_t gu, act, dn, ids, w, valid, grp, sets, total;
 };
 MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     MoeWs o;
@@ -635,6 +635,7 @@ MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     o.w = off; off += align256(pairs * 4);
     o.valid = off; off += align256((size_t)T * 4);
     o.grp = off; off += align256((1 + groups * GREC) * 4);
+    o.sets = off; off += align256(2 * (size_t)set_list_ints((int)pairs) * 4);   // gate-up and down lists
     o.total = off;
     return o;
 }
@@ -699,14 +700,25 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     // (a group takes the MFMA kernel only when groups typically hold 4+ tokens:
     // smaller groups would leave most of its 16 token columns empty)
     Plan p1 = make_plan(s_g, gtok, busy, aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok);
+    Plan p2 = make_plan(s_dn, gtok, busy, aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
     // one token on the LDS-staged kernel: that launch routes the token itself
     const bool route_in = ntok == 1 && topk <= ROUTE1_MAXK && lds_kind(p1.kind) && p1.nt == 1 && p1.xchunk == 0;
+    // the (group, chunk) sets of each launch, listed by the routing launch:
+    // workgroup y takes set y, so only the last few (past the count) are empty
+    const int ca = p1.kind == UK_MFMA ? 16 : p1.nt, cb = p2.kind == UK_MFMA ? 16 : p2.nt;
+    int32_t *sets_a = route_in ? nullptr : (int32_t *)(ws + L.sets);
+    int32_t *sets_b = route_in ? nullptr : sets_a + set_list_ints(pairs);
+    auto set_grid = [&](int c, const int32_t *sets) {
+        if (!sets) return dim3(1, gmax, (ntok + c - 1) / c);
+        const int64_t most = (int64_t)gmax * ((ntok + c - 1) / c);
+        return dim3(1, (unsigned)(most < pairs ? most : pairs), 1);
+    };
 
     // 1. route: top-k, weights, slot lookup, grouping by expert
     if (!route_in) {
         const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
         hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots,
-                           n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp);
+                           n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp, ca, sets_a, cb, sets_b);
         if (hipGetLastError() != hipSuccess) return QG_EHIP;
     }
 
@@ -738,15 +750,15 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     a.y2 = gu;
     a.y2_stride = 2 * F;
     a.grp = grp;
+    a.sets = sets_a;
     a.in_by_pair = 0;
-    rc = launch_gemv(s_g, p1, a, dim3(1, gmax, (ntok + p1.nt - 1) / p1.nt), st);
+    rc = launch_gemv(s_g, p1, a, set_grid(ca, sets_a), st);
     if (rc) return rc;
     *dn_out = dn;
     *valid_out = rt_valid;
     if (!down) return QG_OK;   // the caller runs the down projection itself
 
     // 3. down on each pair's activations
-    Plan p2 = make_plan(s_dn, gtok, busy, aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
     GemvArgs b = {};
     b.W0 = b.W1 = (const uint8_t *)m->down;
     b.rows = s_dn.rows;
@@ -756,10 +768,11 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     b.y = dn;
     b.y_stride = H;
     b.grp = grp;
+    b.sets = sets_b;
     b.in_by_pair = 1;
     b.escale = m->down_scale;   // (dn * s[e]) * c_z, the combine's terms
     b.pscale = rt_w;
-    rc = launch_gemv(s_dn, p2, b, dim3(1, gmax, (ntok + p2.nt - 1) / p2.nt), st);
+    rc = launch_gemv(s_dn, p2, b, set_grid(cb, sets_b), st);
     if (rc) return rc;
     *dn_out = dn;
     *valid_out = rt_valid;

@@ -40,8 +40,16 @@ QG_DEV float glu(int xmode, float g, float u) { return (xmode == XM_GELU ? gelu_
 //   [1 + g*GREC + 2]        n = number of (token, pick) pairs in the group
 //   [1 + g*GREC + 3 + i]    token of pair i (ascending), i < n
 //   [1 + g*GREC + 19 + i]   pair index z = t*k + j of pair i
+// followed, when the host asked for them, by two set lists (one per chunk
+// size c, for the gate-up and the down launch), each
+//   [0]                     number of sets S
+//   [1 + s]                 (g << 16) | c0: group g, its pairs c0 .. c0+c-1
+// holding every (group, chunk) that carries pairs, groups ascending, so a
+// launch over the list has no empty workgroups before the last set.
 constexpr int GREC = 35;
 constexpr int MAXT = 16;
+// ints of a set list for `pairs` (token, pick) pairs
+constexpr int set_list_ints(int pairs) { return 1 + pairs; }
 
 struct GemvArgs {
     // weights: rows [0, rows) of W0 (grouped: W0 + slot * slot_stride for the
@@ -66,6 +74,9 @@ struct GemvArgs {
     int64_t y2_stride;
     int ntok;          // dense: tokens 0..ntok-1
     const int *grp;    // grouped: the routing table, or nullptr for dense
+    const int *sets;   // grouped: the set list of this launch's chunk size
+                       // (blockIdx.y = set), or nullptr (blockIdx.y = group,
+                       // blockIdx.z = chunk)
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
     // grouped outputs scaled as (y * escale[expert]) * pscale[pair] when set
     // (the MoE combine's per-expert down scale and routing weight)
@@ -397,12 +408,17 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
     if (a.grp) {
-        const int G = a.grp[0];
-        const int g = blockIdx.y;
-        if (g >= G) return;
+        int g = blockIdx.y, c0 = blockIdx.z * NT;
+        if (a.sets) {
+            if ((int)blockIdx.y >= a.sets[0]) return;
+            const int e = a.sets[1 + blockIdx.y];
+            g = e >> 16;
+            c0 = e & 0xffff;
+        } else if (g >= a.grp[0]) {
+            return;
+        }
         const int *rec = a.grp + 1 + g * GREC;
         const int n = rec[2];
-        const int c0 = blockIdx.z * NT;
         if (c0 >= n) return;
         nt = min(NT, n - c0);
         Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
@@ -691,12 +707,17 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     }
     if (routed) {
     } else if (a.grp) {
-        const int Gn = a.grp[0];
-        const int g = blockIdx.y;
-        if (g >= Gn) return;
+        int g = blockIdx.y, c0 = blockIdx.z * NT;
+        if (a.sets) {
+            if ((int)blockIdx.y >= a.sets[0]) return;
+            const int e = a.sets[1 + blockIdx.y];
+            g = e >> 16;
+            c0 = e & 0xffff;
+        } else if (g >= a.grp[0]) {
+            return;
+        }
         const int *rec = a.grp + 1 + g * GREC;
         const int n = rec[2];
-        const int c0 = blockIdx.z * NT;
         if (c0 >= n) return;
         nt = min(NT, n - c0);
         Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
@@ -1017,12 +1038,18 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
     const int *rec = nullptr;
     int c0 = 0;
     if (a.grp) {
-        const int Gn = a.grp[0];
-        const int g = blockIdx.y;
-        if (g >= Gn) return;
+        int g = blockIdx.y;
+        c0 = blockIdx.z * 16;
+        if (a.sets) {
+            if ((int)blockIdx.y >= a.sets[0]) return;
+            const int e = a.sets[1 + blockIdx.y];
+            g = e >> 16;
+            c0 = e & 0xffff;
+        } else if (g >= a.grp[0]) {
+            return;
+        }
         rec = a.grp + 1 + g * GREC;
         const int n = rec[2];
-        c0 = blockIdx.z * 16;
         if (c0 >= n) return;
         nt = min(16, n - c0);
         Wg0 = a.W0 + (int64_t)rec[1] * a.slot_stride;
@@ -1256,7 +1283,7 @@ int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st);
 // Router / grouping and combine kernels (qg_route.hip).
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,
                         float *w_out, int32_t *status, int32_t *rt_ids, float *rt_w, int32_t *rt_valid,
-                        int32_t *grp);
+                        int32_t *grp, int ca, int32_t *sets_a, int cb, int32_t *sets_b);
 __global__ void k_combine(const float *dn, const int32_t *rt_valid, float *y, int64_t H, int k);
 
 }  // namespace qg

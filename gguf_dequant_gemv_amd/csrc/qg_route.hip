@@ -12,7 +12,8 @@ namespace qg {
 __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int k, int T,
                                                 const int32_t *slots, int n_slots, int32_t *ids_out, float *w_out,
                                                 int32_t *status, int32_t *rt_ids, float *rt_w,
-                                                int32_t *rt_valid, int32_t *grp) {
+                                                int32_t *rt_valid, int32_t *grp, int ca, int32_t *sets_a, int cb,
+                                                int32_t *sets_b) {
     __shared__ int s_ids[MAXT * 32];
     __shared__ int s_valid[MAXT];
     __shared__ u32 s_tmask[256];    // expert e: bit t set when valid token t picked e
@@ -20,6 +21,7 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
     __shared__ int s_wcnt[16];
     __shared__ int s_slot[256];     // expert e: its pool slot
     __shared__ float s_val[MAXT * 32];
+    __shared__ int s_na[256], s_nb[256];   // set lists: chunks per group, then their running sums
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int e = tid; e < E; e += blockDim.x) {
         s_tmask[e] = 0u;
@@ -127,6 +129,43 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
         int *rec = grp + 1 + s_gidx[e] * GREC;
         rec[3 + r] = t;
         rec[19 + r] = z;
+    }
+    if (!sets_a && !sets_b) return;
+    // Set lists: group g holds ceil(n_g / c) chunks of c pairs; the chunks go
+    // out in group order at the running sum of the lower groups' counts
+    // (inclusive scan over the experts, whose order is the groups' order).
+    const int n = has ? __popc(s_tmask[tid]) : 0;
+    if (tid < 256) {
+        s_na[tid] = sets_a ? (n + ca - 1) / ca : 0;
+        s_nb[tid] = sets_b ? (n + cb - 1) / cb : 0;
+    }
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        int va = 0, vb = 0;
+        if (tid < 256 && tid >= d) {
+            va = s_na[tid - d];
+            vb = s_nb[tid - d];
+        }
+        __syncthreads();
+        if (tid < 256) {
+            s_na[tid] += va;
+            s_nb[tid] += vb;
+        }
+        __syncthreads();
+    }
+    if (has) {
+        if (sets_a) {
+            const int c1 = s_na[tid], c0 = tid ? s_na[tid - 1] : 0;
+            for (int c = c0; c < c1; c++) sets_a[1 + c] = (gi << 16) | ((c - c0) * ca);
+        }
+        if (sets_b) {
+            const int c1 = s_nb[tid], c0 = tid ? s_nb[tid - 1] : 0;
+            for (int c = c0; c < c1; c++) sets_b[1 + c] = (gi << 16) | ((c - c0) * cb);
+        }
+    }
+    if (tid == 0) {
+        if (sets_a) sets_a[0] = s_na[255];
+        if (sets_b) sets_b[0] = s_nb[255];
     }
 }
 

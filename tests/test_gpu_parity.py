@@ -286,6 +286,25 @@ MOE_CASES = [
 def test_moe_stagewise(orc, t, act, H, F, E, k, T, scale):
     c = _moe_case(t, act, H, F, E, k, T, 5000 + t + H + T, scale)
     say("moe", gs.NAMES[t], "act", act, H, F, E, k, "T", T)
+    _moe_check(orc, c)
+
+
+@pytest.mark.parametrize("t,act", [(gs.Q8_0, 0), (gs.Q4_0, 1), (gs.Q4_K, 0)])
+def test_moe_crowded_experts(orc, t, act):
+    """Every token picks the same four experts (their logits lifted by 20):
+    four groups of 16 pairs, each split into many chunks of the launches'
+    token count, so the routing launch's lists of (group, chunk) sets run
+    long and every chunk of a group must land on the right pairs."""
+    H, F, E, k, T = 256, 256, 64, 4, 16
+    c = _moe_case(t, act, H, F, E, k, T, 6100 + t, act == 1)
+    c["lg"] = c["lg"].copy()
+    c["lg"][:, [5, 17, 40, 63]] += np.float32(20.0)
+    say("moe crowded", gs.NAMES[t], "act", act, H, F, E, k, "T", T)
+    _moe_check(orc, c)
+
+
+def _moe_check(orc, c):
+    t, act, H, F, E, k, T = (c[key] for key in ("t", "act", "H", "F", "E", "k", "T"))
     r = run_moe_gpu(c)
     ref = orc.moe_ffn(t, act, H, F, E, c["pool"][c["gu_off"]:], c["rec"], c["pool"][c["d_off"]:], c["rec"],
                       c["ds"], c["lg"], k, np.arange(E, dtype=np.int32), c["x"], T, want_gu=True)
