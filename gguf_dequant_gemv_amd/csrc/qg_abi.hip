@@ -330,6 +330,39 @@ GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     return best;
 }
 
+// Small-batch MFMA launches (4..16 tokens, dense): row groups of 16 per tile
+// (four, or two when four leave fewer tiles than twice the CUs), and, when
+// the tiles still leave most CUs idle (a few thousand rows of a long row),
+// the blocks of each row split over `n` workgroups of at least 32 blocks
+// (eight per wave) whose raw sums the reduce launch adds in split order.
+// Rows under 192 blocks stay whole: there the reduce launch costs more than
+// the shorter walk saves (2816 x 2112 Q4_0 MLP at 16 tokens: 22.1 us whole,
+// 26.8 us split).  2560 x 9728 Q8_0 at 16 tokens is 80 tiles: 7 splits
+// (the MLP at 4 tokens 69 -> 34 us).
+int small_groups(int64_t rows, int glu, int64_t copies) {
+    return (rows + 16 * (glu ? 2 : 4) - 1) / (16 * (glu ? 2 : 4)) * copies < 2 * NUM_CU ? 2 : 4;
+}
+GemmSplit small_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    const int64_t nb = cols / 32;
+    GemmSplit none = {1, (int)nb};
+    if ((type != QG_Q8_0 && type != QG_Q4_0) || ntok < MFMA_MIN_TOK || ntok > QG_MAX_TOKENS) return none;
+    const int groups = small_groups(rows, glu, 1);
+    const int64_t tile_rows = 16 * (glu ? groups / 2 : groups);
+    const int64_t wgs = (rows + tile_rows - 1) / tile_rows;
+    if (wgs >= NUM_CU || nb < 192) return none;
+    const int64_t want = (2 * NUM_CU + wgs - 1) / wgs;
+    int64_t kb = (nb + want - 1) / want;
+    if (kb < 32) kb = 32;
+    const int64_t n = (nb + kb - 1) / kb;
+    if (n < 2) return none;
+    return {(int)n, (int)kb};
+}
+size_t small_part_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    const GemmSplit sp = small_split(type, rows, cols, ntok, glu);
+    if (sp.n < 2) return 0;
+    return ((size_t)sp.n * (size_t)ntok * (size_t)(glu ? 2 : 1) * (size_t)rows * 4 + 255) & ~(size_t)255;
+}
+
 bool prefill_kernel(int type, int ntok) {
     return (type == QG_Q8_0 || type == QG_Q4_0) && ntok > QG_MAX_TOKENS && ntok <= QG_MAX_PREFILL;
 }
@@ -341,8 +374,10 @@ size_t gemm_part_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) 
     return ((size_t)sp.n * (size_t)ntok * (size_t)(glu ? 2 : 1) * (size_t)rows * 4 + 255) & ~(size_t)255;
 }
 
-// scratch of one prefill launch: the split x, then the partial sums
+// scratch of one prefill launch: the split x, then the partial sums (or of a
+// split small-batch launch: its partial sums)
 size_t gemm_scratch_bytes(int type, int64_t rows, int64_t cols, int ntok, int glu) {
+    if (ntok <= QG_MAX_TOKENS) return small_part_bytes(type, rows, cols, ntok, glu);
     if (!prefill_kernel(type, ntok)) return 0;
     return ((gemm_xs_bytes(cols, ntok) + 255) & ~(size_t)255) + gemm_part_bytes(type, rows, cols, ntok, glu);
 }
@@ -397,16 +432,27 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     }
     // four groups of 16 rows per tile, or two when that leaves too few tiles
     // to spread over the CUs
-    int groups = 4;
-    if ((a.rows + 16 * (a.glu ? 2 : 4) - 1) / (16 * (a.glu ? 2 : 4)) * p.copies < 2 * NUM_CU) groups = 2;
+    const int groups = small_groups(a.rows, a.glu, p.copies);
     const int tile_rows = 16 * (a.glu ? groups / 2 : groups);
     a.ntiles = (int)((a.rows + tile_rows - 1) / tile_rows);
     gemv_fn f = gemv_kernel_mfma(s.type, groups);
     int64_t cap = resident_wgs(f, 0) / p.copies;
     if (cap < 1) cap = 1;
     grid.x = (unsigned)(a.ntiles < cap ? a.ntiles : cap);
+    // dense, with a workspace: split long rows when the tiles leave CUs idle
+    const GemmSplit sp = a.grp ? GemmSplit{1, 0} : small_split(s.type, a.rows, s.cols, a.ntok, a.glu);
+    const bool split = sp.n > 1 && a.ws && a.ws_bytes >= small_part_bytes(s.type, a.rows, s.cols, a.ntok, a.glu);
+    if (split) {
+        a.part = (float *)a.ws;
+        a.kchunks = sp.kchunks;
+        a.ptok = a.ntok;
+        a.prow = (a.glu ? 2 : 1) * a.rows;
+        grid.x = (unsigned)a.ntiles;
+        grid.z = (unsigned)sp.n;
+    }
     hipLaunchKernelGGL(f, grid, dim3(256), 0, st, a);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+    if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    return split ? gemm_reduce(a, sp.n, st) : QG_OK;
 }
 
 int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
@@ -487,7 +533,10 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
     if (rc) return rc;
     if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
     if (!W || !x || !y || !aligned(W, 2) || !aligned(x, 4) || !aligned(y, 4)) return QG_EINVAL;
-    if (ws_bytes < gemm_call_scratch_bytes(type, rows, cols, ntok) || (ws_bytes && (!ws || !aligned(ws, 256))))
+    // (qg_gemv brings no workspace: its small batches run unsplit)
+    const bool takes_ws = max_tok > QG_MAX_TOKENS;
+    if ((takes_ws && ws_bytes < gemm_call_scratch_bytes(type, rows, cols, ntok)) ||
+        (ws_bytes && (!ws || !aligned(ws, 256))))
         return QG_EINVAL;
     // rows in launches of at most MAX_RANGE weight bytes each
     const int64_t chunk = MAX_RANGE / s.row_bytes;

@@ -1077,10 +1077,15 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
     const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
 
     // the four waves split each row's blocks (wave w takes blocks w, w+4, ...)
-    // and their partial sums are added in wave order at the tile's end
+    // and their partial sums are added in wave order at the tile's end.  A
+    // split launch (dense, a.part set) gives workgroup z the blocks
+    // [z kchunks, (z+1) kchunks) and stores the raw sums for the reduce.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n16 = lane & 15, q = lane >> 4;
     const int nb = a.cols / 32;
+    const bool split = a.part != nullptr && !a.grp;
+    const int b_lo = split ? (int)blockIdx.z * a.kchunks : 0;
+    const int b_hi = split ? min(nb, b_lo + a.kchunks) : nb;
     const int64_t rows = a.rows;
     const u32 rb = (u32)a.row_bytes;
     const u32 cpos = 2u + 8u * (u32)(TY == T_Q8_0 ? q : (q & 1));
@@ -1150,23 +1155,24 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
                 for (int i = 0; i < 4; i++) acc[gi][i] = fmaf(d, c[i], acc[gi][i]);
             }
         };
-        // blocks wave, wave+4, ...: PF of them in flight ahead of the one in use
-        const int nmine = nb > wave ? (nb - wave + 3) / 4 : 0;
+        // blocks b_lo + wave, + 4, ...: PF of them in flight ahead of the one in use
+        const int bw = b_lo + wave;
+        const int nmine = b_hi > bw ? (b_hi - bw + 3) / 4 : 0;
 #pragma unroll
-        for (int k = 0; k < PF; k++) fetch(wave + 4 * k, k);
+        for (int k = 0; k < PF; k++) fetch(bw + 4 * k, k);
         int j = 0;
         for (; j + PF + 1 <= nmine; j += PF + 1) {
 #pragma unroll
             for (int k = 0; k <= PF; k++) {
-                fetch(wave + 4 * (j + k + PF), (k + PF) % (PF + 1));
-                consume(wave + 4 * (j + k), k);
+                fetch(bw + 4 * (j + k + PF), (k + PF) % (PF + 1));
+                consume(bw + 4 * (j + k), k);
             }
         }
 #pragma unroll
         for (int k = 0; k <= PF; k++) {
             if (j + k < nmine) {
-                fetch(wave + 4 * (j + k + PF), (k + PF) % (PF + 1));
-                consume(wave + 4 * (j + k), k);
+                fetch(bw + 4 * (j + k + PF), (k + PF) % (PF + 1));
+                consume(bw + 4 * (j + k), k);
             }
         }
         // the four waves' partial sums, added in wave order
@@ -1188,7 +1194,26 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
         {
             const int i = wave;
             const int t = 4 * q + i;
-            if (t < nt) {
+            if (t < nt && split) {
+                // raw sums of this split: [z][token][rows] (gated: gate rows, then up rows)
+                float *pp = a.part + ((int64_t)blockIdx.z * a.ptok + s_out[t]) * a.prow;
+                if (a.glu) {
+#pragma unroll
+                    for (int gi = 0; gi < GR / 2; gi++) {
+                        const int64_t r = tile * tile_rows + 16 * gi + n16;
+                        if (r < rows) {
+                            pp[r] = acc[gi][i];
+                            pp[rows + r] = acc[gi + GR / 2][i];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int gi = 0; gi < GR; gi++) {
+                        const int64_t r = tile * tile_rows + 16 * gi + n16;
+                        if (r < rows) pp[r] = acc[gi][i];
+                    }
+                }
+            } else if (t < nt) {
                 const int64_t oi = s_out[t];
                 const float osc = s_osc[t];
                 if (a.glu) {

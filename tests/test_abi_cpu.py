@@ -189,13 +189,18 @@ def test_gemm_token_limits():
     assert qg.qg_mlp_workspace_size(qg.QG_Q4_K, 2560, 9728, 256) == gu_act   # no split on the vector kernels
     assert qg.qg_mlp_workspace_size(8, 2560, 9728, 256) > gu_act             # the 20-tile down splits
     assert qg.qg_mlp_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0
+    # 16 tokens: the down projection (80 tiles) splits into 7
+    gu_act16 = 16 * 2 * 9728 * 4 + 16 * 9728 * 4
+    assert qg.qg_mlp_workspace_size(8, 2560, 9728, 16) == gu_act16 + 7 * 16 * 2560 * 4
 
 
 def test_gemm_split_workspace():
     """Prefill-size Q8_0 / Q4_0 launches need scratch: x split into three bf16
     parts (6 bytes per value of the padded chunk), plus whole [split][token][row]
     f32 partial sums when few row tiles make the launch split along the row.
-    Decode sizes and the vector kernels need none."""
+    Small batches (4..16 tokens) on the MFMA kernel split long rows the same
+    way when their tiles leave most CUs idle; one to three tokens and the
+    vector kernels need none."""
     L = qg.lib()
     n = qg.qg_gemm_workspace_size(8, 2560, 9728, 64)
     xs = 64 * 9728 * 6
@@ -203,7 +208,15 @@ def test_gemm_split_workspace():
     assert qg.qg_gemm_workspace_size(2, 2560, 9728, 64) == n                 # Q4_0: the same tiles
     wide = qg.qg_gemm_workspace_size(8, 65536, 9728, 64)                     # enough row tiles already
     assert xs <= wide < xs + 64 * 65536 * 4
-    assert qg.qg_gemm_workspace_size(8, 2560, 9728, 16) == 0                 # decode-size batches
+    # 2560 rows are 80 tiles of 32: 304 blocks a row go out in 7 splits of 44
+    assert qg.qg_gemm_workspace_size(8, 2560, 9728, 16) == 7 * 16 * 2560 * 4
+    assert qg.qg_gemm_workspace_size(2, 2560, 9728, 4) == 7 * 4 * 2560 * 4
+    assert qg.qg_gemm_workspace_size(8, 9728, 2560, 16) == 0                 # 304 tiles fill the CUs
+    assert qg.qg_gemm_workspace_size(8, 2560, 9728, 3) == 0                  # the vector kernel
+    assert qg.qg_gemm_workspace_size(qg.QG_Q4_K, 2560, 9728, 16) == 0
+    assert qg.qg_gemm_workspace_size(8, 2560, 512, 16) == 0                  # 16 blocks: too short to split
+    assert qg.qg_gemm_workspace_size(2, 2816, 2112, 16) == 0                 # 66 blocks: whole rows
+    assert qg.qg_gemm_workspace_size(8, 33, 250 * 32, 16) == 8 * 16 * 33 * 4   # 8 splits of 32 blocks
     assert qg.qg_gemm_workspace_size(qg.QG_Q6_K, 2560, 9728, 64) == 0
     assert 64 * 128 * 6 <= qg.qg_gemm_workspace_size(8, 2560, 128, 64) < 2560 * 64 * 4   # too short to split
     assert qg.qg_gemm_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0

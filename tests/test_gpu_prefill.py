@@ -27,7 +27,12 @@ def gpu_gemm(t, W, x, rows, cols, ntok, w_offset=0):
 
 @pytest.mark.parametrize("t", TYPES)
 @pytest.mark.parametrize("rows,nbk,ntok,off", [(300, 32, 17, 0), (129, 24, 64, 2), (257, 16, 100, 0),
-                                               (70, 40, 256, 0), (33, 8, 40, 2)])
+                                               (70, 40, 256, 0), (33, 8, 40, 2),
+                                               # 4..16 tokens (Q8_0 / Q4_0 rows of 192+ blocks
+                                               # split over workgroups): 7 splits of 32 with a
+                                               # short last one, 8 with a short last one, and
+                                               # a short row left whole
+                                               (300, 200, 8, 0), (33, 250, 16, 2), (129, 24, 5, 2)])
 def test_gemm_parity(orc, t, rows, nbk, ntok, off):
     if t in (gs.Q4_K, gs.Q6_K):
         nbk = max(1, nbk // 8)
@@ -79,6 +84,22 @@ def test_mlp_prefill_stagewise(orc, t, act, H, F, T):
         yd, Ad = orc.gemv_f64(t, Wd, orc.glu(act, gu[tt], F), H, F)
         R = Wabs @ np.abs(gu[tt, :F].astype(np.float64) * gu[tt, F:].astype(np.float64))
         assert np.all(np.abs(yh[tt] - yd) <= TOL * Ad + 1e-6 * R), "prefill down token %d" % tt
+
+
+def test_gemm_full_size_small_batch_16(orc):
+    """The dense down projection at 16 tokens, Q8_0 2560 x 9728: 80 row tiles,
+    so each row's 304 blocks go out in 7 splits whose sums a second launch
+    adds.  Sampled rows, every token."""
+    t, rows, cols, T = gs.Q8_0, 2560, 9728, 16
+    g = gs.rng(8310)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, T, cols)
+    say("gemm full size small batch", rows, cols, "T", T)
+    y = gpu_gemm(t, W, x, rows, cols, T)
+    ri = np.array(sorted(set(g.choice(rows, 96, replace=False).tolist()) | {0, rows - 1}), np.int64)
+    y_ref, A = orc.gemv(t, W, x, rows, cols, T, row_idx=ri)
+    check_rows(y[:, ri], y_ref, A, "gemm 2560x9728 T=16")
+    assert np.isfinite(y).all()
 
 
 def test_gemm_full_size_dense_256(orc):
