@@ -103,8 +103,10 @@ int qg_gemv(int type, const void *W, const float *x, float *y,
  * on the vector kernels in chunks of tokens.
  * workspace: device scratch of at least qg_gemm_workspace_size(type, rows,
  * cols, ntok) bytes, 256-byte aligned (may be NULL when that size is 0).  It
- * holds partial sums when a launch with few row tiles is split along the row;
- * its contents after the call are unspecified.
+ * holds partial sums when a launch with few row tiles is split along the row
+ * (prefill chunks, and Q8_0 / Q4_0 batches of 4..16 tokens over rows of 192
+ * or more blocks; qg_gemv runs those batches unsplit); its contents after the
+ * call are unspecified.
  * Arguments and errors as qg_gemv, with QG_ELIMIT for ntok outside
  * 1..QG_MAX_PREFILL and QG_EINVAL for a short or misaligned workspace. */
 size_t qg_gemm_workspace_size(int type, int64_t rows, int64_t cols, int ntok);
@@ -146,7 +148,8 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
  * ff, ntok) bytes, 256-byte aligned.  After the call it holds gu as
  * [ntok][2*ff] f32 at offset 0 and a as [ntok][ff] f32 after it (at the next
  * 256-byte boundary): documented intermediates, useful for staged checking.
- * Prefill chunks may use more scratch after a (unspecified contents).
+ * Prefill chunks and split small batches (as qg_gemm) may use more scratch
+ * after a (unspecified contents).
  * Errors: as qg_gemv for both shapes, QG_EINVAL for a short workspace or an
  * unknown act. */
 size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok);
