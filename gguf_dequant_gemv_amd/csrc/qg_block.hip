@@ -36,6 +36,26 @@ constexpr int LB = 16;
 // for the sum before any y is written, so y may be x.
 QG_DEV void k_rmsnorm_row(const float *xt, const float *w, float *yt, int64_t n, float eps, float k) {
     __shared__ float s_red[4];
+    if (n <= 256 * LB) {
+        // one batch per thread: x and w loaded once, the row's factor and the
+        // outputs from registers (same operations, same order)
+        const int i0 = threadIdx.x;
+        float v[LB], g[LB];
+#pragma unroll
+        for (int b = 0; b < LB; b++) {
+            const bool in = i0 + b * 256 < n;
+            v[b] = in ? xt[i0 + b * 256] : 0.0f;
+            g[b] = in ? w[i0 + b * 256] : 0.0f;
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+        const float r = rms_factor(block_sum<4>(ss, s_red), n, eps);
+#pragma unroll
+        for (int b = 0; b < LB; b++)
+            if (i0 + b * 256 < n) yt[i0 + b * 256] = ((v[b] * r) * k) * g[b];
+        return;
+    }
     float ss = 0.0f;
     for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
         float v[LB];
@@ -204,6 +224,42 @@ __global__ __launch_bounds__(256) void k_post_ffn(const float *mlp, const float 
     const int64_t o = (int64_t)blockIdx.x * n;
     const float *a = mlp + o, *b = moe + o;
     float *xt = x + o;
+    if (n <= 256 * LB) {
+        // one batch per thread: every operand is loaded once, up front, and
+        // the three passes below run on registers (same operations, same order)
+        const int i0 = threadIdx.x;
+        float va[LB], vb[LB], g1[LB], g2[LB], g[LB], xv[LB];
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            const bool in = i0 + u * 256 < n;
+            va[u] = in ? a[i0 + u * 256] : 0.0f;
+            vb[u] = in ? b[i0 + u * 256] : 0.0f;
+            g1[u] = in ? w1[i0 + u * 256] : 0.0f;
+            g2[u] = in ? w2[i0 + u * 256] : 0.0f;
+            g[u] = in ? w[i0 + u * 256] : 0.0f;
+            xv[u] = in ? xt[i0 + u * 256] : 0.0f;
+        }
+        const float ko = os[0];
+        float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            s1 = fmaf(va[u], va[u], s1);
+            s2 = fmaf(vb[u], vb[u], s2);
+        }
+        const float r1 = rms_factor(block_sum<4>(s1, s_red), n, eps);
+        const float r2 = rms_factor(block_sum<4>(s2, s_red), n, eps);
+        float v[LB], s3 = 0.0f;
+#pragma unroll
+        for (int u = 0; u < LB; u++) {
+            v[u] = (va[u] * r1) * g1[u] + (vb[u] * r2) * g2[u];
+            s3 = fmaf(v[u], v[u], s3);
+        }
+        const float r3 = rms_factor(block_sum<4>(s3, s_red), n, eps);
+#pragma unroll
+        for (int u = 0; u < LB; u++)
+            if (i0 + u * 256 < n) xt[i0 + u * 256] = ((v[u] * r3) * g[u] + xv[u]) * ko;
+        return;
+    }
     float s1 = 0.0f, s2 = 0.0f;
     for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
         float va[LB], vb[LB];

@@ -73,7 +73,8 @@ def test_rmsnorm(orc, n, T, k, inplace):
     check_rel(host(y), orc.rmsnorm(x, w, n, T, 1e-6, k), "rmsnorm")
 
 
-@pytest.mark.parametrize("n,T,nout", [(2816, 1, 3), (2816, 16, 3), (1000, 3, 4), (64, 2, 1)])
+@pytest.mark.parametrize("n,T,nout", [(2816, 1, 3), (2816, 16, 3), (1000, 3, 4), (64, 2, 1), (4096, 1, 2),
+                                      (5000, 2, 2)])
 def test_rmsnorm_multi(orc, n, T, nout):
     """Several norms of one row in a launch: bit for bit the separate
     qg_rmsnorm calls, and each against the oracle."""
@@ -227,7 +228,8 @@ def _oracle_ids(c):
 
 
 # ------------------------------------------------------ Gemma's FFN tail ---
-@pytest.mark.parametrize("n,T", [(2816, 1), (2816, 16), (100, 3)])
+# rows of up to 4096 run from registers (one batch per thread), longer ones in passes
+@pytest.mark.parametrize("n,T", [(2816, 1), (2816, 16), (100, 3), (4096, 1), (5000, 2)])
 def test_post_ffn(orc, n, T):
     import gguf_dequant_gemv_amd as qg
     g = gs.rng(300 + n + T)
