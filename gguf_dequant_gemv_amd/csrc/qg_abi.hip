@@ -706,10 +706,16 @@ namespace {
 // Validation, routing, and the two grouped expert launches of a MoE step.  On
 // success dn holds the weighted terms (dn_j s_j) c_j as [ntok][topk][H] and
 // valid the per-token validity, both inside the workspace.
+// a shared expert's gate / up matrices and where its act / gu rows go
+struct SharedGroup {
+    const void *gate, *up;
+    float *act, *gu;
+};
+
 int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
                const float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
                size_t workspace_bytes, size_t ws_extra, hipStream_t st, float **dn_out, int32_t **valid_out,
-               bool down = true) {
+               bool down = true, const SharedGroup *shg = nullptr, bool *sh_done = nullptr) {
     if (!m) return QG_EINVAL;
     const int E = m->n_experts;
     if (E < 1 || E > QG_MAX_EXPERTS || topk < 1 || topk > QG_MAX_TOPK || topk > E || ntok < 1 ||
@@ -805,7 +811,19 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     a.grp = grp;
     a.sets = sets_a;
     a.in_by_pair = 0;
-    rc = launch_gemv(s_g, p1, a, set_grid(ca, sets_a), st);
+    dim3 grid_a = set_grid(ca, sets_a);
+    // a shared expert of the same shape rides along as group k of the
+    // routing launch (the aligned-copy variant needs its ranges aligned too)
+    if (sh_done) *sh_done = false;
+    if (route_in && shg && (p1.kind != UK_LDS || (aligned(shg->gate, 16) && aligned(shg->up, 16)))) {
+        a.sh_W0 = (const uint8_t *)shg->gate;
+        a.sh_W1 = (const uint8_t *)shg->up;
+        a.sh_y = shg->act;
+        a.sh_y2 = shg->gu;
+        grid_a.y += 1;
+        if (sh_done) *sh_done = true;
+    }
+    rc = launch_gemv(s_g, p1, a, grid_a, st);
     if (rc) return rc;
     *dn_out = dn;
     *valid_out = rt_valid;
@@ -913,11 +931,47 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     const SharedWs S = shared_ws(m->hidden, sh->ff, ntok);
     float *dn = nullptr;
     int32_t *valid = nullptr;
-    int rc = moe_routed(m, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status, workspace,
-                        workspace_bytes, S.total, st, &dn, &valid);
-    if (rc) return rc;
-    // the shared expert: a dense gated MLP on the same input, into the workspace
     uint8_t *ws = (uint8_t *)workspace + base;
+    // One token with a shared expert of the routed experts' shape: its gate
+    // and up rows ride in the routing launch, its down row and the whole
+    // combine in the one-token down launch (two launches in all).
+    const bool one = ntok == 1 && sh->type == m->type && sh->ff == m->ff && moe_down1_fits(m->type, m->ff, topk);
+    const SharedGroup shg = {sh->gate, sh->up, (float *)(ws + S.act), (float *)(ws + S.gu)};
+    bool fused = false;
+    int rc = moe_routed(m, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status, workspace,
+                        workspace_bytes, S.total, st, &dn, &valid, !one, one ? &shg : nullptr, &fused);
+    if (rc) return rc;
+    if (one) {
+        const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok);
+        Moe1Args b = {};
+        b.W = (const uint8_t *)m->down;
+        b.stride = m->down_stride;
+        b.rows = m->hidden;
+        b.row_bytes = m->ff / 32 * qg_block_bytes(m->type);
+        b.nb = (int)(m->ff / 32);
+        b.act = (const float *)((uint8_t *)workspace + L.act);
+        b.act_stride = m->ff;
+        b.ids = (const int32_t *)((uint8_t *)workspace + L.ids);
+        b.w = (const float *)((uint8_t *)workspace + L.w);
+        b.slots = expert_slots;
+        b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
+        b.escale = m->down_scale;
+        b.valid = valid;
+        b.dn = dn;
+        b.k = topk;
+        if (fused) {
+            b.shW = (const uint8_t *)sh->down;
+            b.sh_act = (const float *)(ws + S.act);
+            b.gate_inp = sh->gate_inp;
+            b.x = x;
+            b.resid = resid;
+            b.sh_out = (float *)(ws + S.sh);
+            return launch_moe_down1(m->type, b, st);
+        }
+        rc = launch_moe_down1(m->type, b, st);   // the routed terms only (no y)
+        if (rc) return rc;
+    }
+    // the shared expert: a dense gated MLP on the same input, into the workspace
     rc = qg_mlp(sh->type, m->act, sh->gate, sh->up, sh->down, m->hidden, sh->ff, x, (float *)(ws + S.sh), ntok,
                 ws + S.gu, S.sh - S.gu, stream);
     if (rc) return rc;

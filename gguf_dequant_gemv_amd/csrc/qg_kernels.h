@@ -77,6 +77,11 @@ struct GemvArgs {
     const int *sets;   // grouped: the set list of this launch's chunk size
                        // (blockIdx.y = set), or nullptr (blockIdx.y = group,
                        // blockIdx.z = chunk)
+    // a routing launch (RT) may carry a shared expert as group r_k: its gate
+    // rows from sh_W0, up rows from sh_W1 (same shape as a routed expert's),
+    // act(g) * u to sh_y and the raw g, u to sh_y2
+    const uint8_t *sh_W0, *sh_W1;
+    float *sh_y, *sh_y2;
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
     // grouped outputs scaled as (y * escale[expert]) * pscale[pair] when set
     // (the MoE combine's per-expert down scale and routing weight)
@@ -407,6 +412,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     int nt;
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
+    float *yo = a.y, *y2o = a.y2;  // where the rows go
     if (a.grp) {
         int g = blockIdx.y, c0 = blockIdx.z * NT;
         if (a.sets) {
@@ -563,13 +569,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
                 for (int t = 0; t < NT; t++) {
                     if (t < nt) {
                         if (a.glu) {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
-                            if (a.y2) {
-                                a.y2[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
-                                a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
+                            yo[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
+                            if (y2o) {
+                                y2o[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
+                                y2o[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
                             }
                         } else {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
+                            yo[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
                         }
                     }
                 }
@@ -689,9 +695,20 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     int nt;
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
+    float *yo = a.y, *y2o = a.y2;  // where the rows go
     bool routed = false;
     if constexpr (RT) {
-        {   // this launch routes its one token itself
+        if (a.sh_W0 && (int)blockIdx.y == a.r_k) {   // the shared expert's gate and up rows
+            if (blockIdx.z > 0) return;
+            nt = 1;
+            Wg0 = a.sh_W0;
+            Wg1 = a.sh_W1;
+            in_idx[0] = out_idx[0] = 0;
+            osc_e[0] = osc_p[0] = 1.0f;
+            yo = a.sh_y;
+            y2o = a.sh_y2;
+            routed = true;
+        } else {   // this launch routes its one token itself
             int e, sl, z;
             const bool ok = route1_group(a, blockIdx.y, e, sl, z);
             if (!ok || (int)blockIdx.y >= a.r_k || blockIdx.z > 0) return;
@@ -941,13 +958,13 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
                 for (int t = 0; t < NT; t++) {
                     if (t < nt) {
                         if (a.glu) {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
-                            if (a.y2) {
-                                a.y2[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
-                                a.y2[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
+                            yo[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
+                            if (y2o) {
+                                y2o[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
+                                y2o[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
                             }
                         } else {
-                            a.y[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
+                            yo[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
                         }
                     }
                 }

@@ -20,8 +20,18 @@ struct Moe1Args {
     const float *escale;     // per-expert down scale, or nullptr
     const int32_t *valid;    // [1] 0: a pick has no slot, y is left as it is
     float *dn;               // [k][rows] the terms (dn_j * s) * w_j
-    float *y;                // [rows]
+    float *y;                // [rows] the sum of the terms, or nullptr
     int k;
+    // the shared expert, when shW is set: its down matrix (rows x the same
+    // row_bytes), its activation row, and the scalar gate (gate_inp . x);
+    // then resid[r] = (sum of the terms + sh[r] * sigmoid(gate)) + resid[r]
+    // and sh[r] (the raw shared output) goes to sh_out
+    const uint8_t *shW;
+    const float *sh_act;
+    const float *gate_inp;
+    const float *x;
+    float *resid;
+    float *sh_out;
 };
 
 // whether a (block type, F, top-k) the one-token launch serves

@@ -185,6 +185,14 @@ SHARED_CASES = [
     (gs.Q8_0, 2048, 512, 512, 64, 8, 16, None),
     (gs.Q4_0, 352, 96, 160, 16, 4, 3, None),        # small, ragged row tiles
     (gs.Q4_K, 512, 256, 96, 8, 2, 2, gs.Q8_0),      # shared expert in another block type
+    # one token: a shared expert of the routed experts' shape rides in the
+    # routing launch and the one-token down launch (combine included)
+    (gs.Q4_0, 352, 96, 96, 16, 4, 1, None),
+    (gs.Q8_0, 256, 1536, 1536, 16, 8, 1, None),     # two blocks per lane in the down launch
+    # one token, other shapes or types: routed down in one launch, then the
+    # shared expert and the combine as their own launches
+    (gs.Q4_0, 352, 96, 160, 16, 4, 1, None),
+    (gs.Q8_0, 512, 256, 256, 16, 4, 1, gs.Q4_0),
 ]
 
 
@@ -220,6 +228,22 @@ def test_moe_shared_absent_expert(orc):
             assert np.array_equal(r["resid"][tt], r["resid0"][tt])
         else:
             assert not np.array_equal(r["resid"][tt], r["resid0"][tt])
+
+
+def test_moe_shared_absent_expert_one_token(orc):
+    """One token whose first pick has no slot: the fused launches leave its
+    residual row as it was and report QG_EABSENT."""
+    import gguf_dequant_gemv_amd as qg
+    c = gs.qwen35_block(7500, 1, gs.Q8_0, 256, 12, 64, 64, 4)
+    c["logits"] = gs.logits(gs.rng(7501), 1, 12)
+    c["resid"] = gs.activations(gs.rng(7502), 1, 256)
+    ids, _ = _oracle_ids(c)
+    c["slots"] = np.arange(12, dtype=np.int32)
+    c["slots"][int(ids[0, 0])] = -1
+    say("moe shared absent expert, one token", int(ids[0, 0]))
+    r = run_shared_gpu(c)
+    assert r["status"] == qg.QG_EABSENT
+    assert np.array_equal(r["resid"], r["resid0"])
 
 
 def _oracle_ids(c):
