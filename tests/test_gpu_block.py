@@ -96,20 +96,21 @@ def test_rmsnorm_multi(orc, n, T, nout):
 
 
 # ------------------------------------------------- shared-expert MoE block --
-def run_shared_gpu(c, lt=None, xt=None, resid=None):
+def run_shared_gpu(c, lt=None, xt=None, resid=None, pool_off=0, sh_off=0):
     """qg_moe_ffn_shared on case c; lt / xt / resid: device tensors to use in
-    place of c's logits, input and residual.  Returns host copies of every
-    stage and the pieces the checks need."""
+    place of c's logits, input and residual; pool_off / sh_off: byte offsets
+    (even) of the expert pool and of the shared expert's matrices.  Returns
+    host copies of every stage and the pieces the checks need."""
     import gguf_dequant_gemv_amd as qg
     torch = _torch()
     t, H, F, SF, E, k, T = c["type"], c["H"], c["F"], c["SF"], c["E"], c["k"], c["ntok"]
-    pt, pp = dev(c["pool"])
+    pt, pp = dev(c["pool"], pool_off)
     m = qg.make_moe(t, qg.QG_ACT_SILU, H, F, E, pp + c["gu_off"], c["record"], pp + c["d_off"], c["record"])
-    sgt, _ = dev(c["sh_gate"])
-    sut, _ = dev(c["sh_up"])
-    sdt, _ = dev(c["sh_down"])
+    sgt, sgp = dev(c["sh_gate"], sh_off)
+    sut, sup = dev(c["sh_up"], sh_off)
+    sdt, sdp = dev(c["sh_down"], sh_off)
     git, _ = dev(c["sh_gate_inp"])
-    sh = qg.make_shared_expert(c.get("sh_type", t), SF, sgt, sut, sdt, git)
+    sh = qg.make_shared_expert(c.get("sh_type", t), SF, sgp, sup, sdp, git)
     st, _ = dev(c["slots"])
     if lt is None:
         lt, _ = dev(c["logits"])
@@ -228,6 +229,20 @@ def test_moe_shared_absent_expert(orc):
             assert np.array_equal(r["resid"][tt], r["resid0"][tt])
         else:
             assert not np.array_equal(r["resid"][tt], r["resid0"][tt])
+
+
+@pytest.mark.parametrize("pool_off,sh_off", [(0, 2), (2, 2), (2, 0)])
+def test_moe_shared_one_token_offsets(orc, pool_off, sh_off):
+    """One token, shared expert of the routed shape, tensors off 16-byte
+    alignment: with an aligned pool (the aligned-copy routing launch) a
+    misaligned shared expert runs as its own launches; with a misaligned pool
+    it rides in the routing launch at any 2-byte phase."""
+    c = gs.qwen35_block(7600 + pool_off + sh_off, 1, gs.Q8_0, 512, 16, 256, 256, 4)
+    c["logits"] = gs.logits(gs.rng(7601), 1, 16)
+    c["resid"] = gs.activations(gs.rng(7602), 1, 512)
+    say("moe shared one token, pool offset", pool_off, "shared offset", sh_off)
+    r = run_shared_gpu(c, pool_off=pool_off, sh_off=sh_off)
+    check_shared_stages(orc, c, r)
 
 
 def test_moe_shared_absent_expert_one_token(orc):
