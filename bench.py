@@ -291,8 +291,8 @@ class MoeLayers(Workload):
 class Qwen35Block(Workload):
     """A Qwen3.5/3.6-MoE-style FFN block, T tokens, over L independent layers:
     RMS norm of the residual stream, f32 router GEMV, routed experts plus the
-    gated shared expert added into the residual (qg_rmsnorm, qg_gemv QG_F32,
-    qg_moe_ffn_shared)."""
+    gated shared expert added into the residual (qg_rmsnorm_router at one
+    token, else qg_rmsnorm and qg_gemv QG_F32; qg_moe_ffn_shared)."""
 
     def __init__(self, ntok, layers=16, H=2048, E=256, F=512, SF=512, k=8):
         import torch
@@ -348,8 +348,12 @@ class Qwen35Block(Workload):
 
     def step_layer(self, L):
         qg, T = self.qg, self.ntok
-        qg.qg_rmsnorm(L["x"], L["norm"], self.xn, self.H, T, 1e-6, 1.0)
-        qg.qg_gemv(qg.QG_F32, L["router"], self.xn, self.lg, self.E, self.H, T)
+        if T == 1:   # the RMS norm and the router on it, one launch
+            qg.qg_rmsnorm_router(L["x"], self.H, T, 1e-6, L["norm"], 1.0, L["router"], self.E, self.lg,
+                                 [L["norm"]], [1.0], [self.xn])
+        else:        # (each workgroup of the fused launch takes every token's norm: slower at 16)
+            qg.qg_rmsnorm(L["x"], L["norm"], self.xn, self.H, T, 1e-6, 1.0)
+            qg.qg_gemv(qg.QG_F32, L["router"], self.xn, self.lg, self.E, self.H, T)
         qg.qg_moe_ffn_shared(L["m"], L["sh"], self.lg, self.k, self.slots, self.xn, L["x"], T, self.ids, self.w,
                              self.status, self.ws)
 
@@ -362,9 +366,10 @@ class Qwen35Block(Workload):
 
 class GemmaBlock(Workload):
     """Gemma4-26B-A4B-style FFN block at Q4_0, T tokens, over L layers: three
-    RMS norms of the residual stream (one launch), the dense GELU MLP, the f32
-    router, the routed experts, and the FFN tail into the residual
-    (qg_rmsnorm_multi, qg_mlp, qg_gemv QG_F32, qg_moe_ffn, qg_post_ffn)."""
+    RMS norms of the residual stream and the f32 router on one of them (one
+    launch at one token: qg_rmsnorm_router; else qg_rmsnorm_multi and qg_gemv
+    QG_F32), the dense GELU MLP, the routed experts, and the FFN tail into
+    the residual (qg_mlp, qg_moe_ffn, qg_post_ffn)."""
 
     def __init__(self, ntok, layers=16, H=2816, Fd=2112, E=128, F=704, k=8):
         import torch
@@ -421,16 +426,19 @@ class GemmaBlock(Workload):
     def step_layer(self, L):
         qg, T, H = self.qg, self.ntok, self.H
 
-        # ffn_norm, pre_ffw_norm_2 and the router's scaled norm in one launch
-        qg.qg_rmsnorm_multi(L["x"], H, T, 1e-6, [L["w_ffn"], L["w_pre2"], L["w_rs"]], [1.0, 1.0, self.kr],
-                            [self.xn, self.xm, self.rt])
+        if T == 1:   # ffn_norm, pre_ffw_norm_2 and the router on its scaled norm in one launch
+            qg.qg_rmsnorm_router(L["x"], H, T, 1e-6, L["w_rs"], self.kr, L["router"], self.E, self.lg,
+                                 [L["w_ffn"], L["w_pre2"]], [1.0, 1.0], [self.xn, self.xm])
+        else:        # the three norms in one launch, the router on the third
+            qg.qg_rmsnorm_multi(L["x"], H, T, 1e-6, [L["w_ffn"], L["w_pre2"], L["w_rs"]], [1.0, 1.0, self.kr],
+                                [self.xn, self.xm, self.rt])
+            qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
 
         def dense(st):   # the dense GELU MLP
             qg.qg_mlp(qg.QG_Q4_0, qg.QG_ACT_GELU_TANH, L["Wg"], L["Wu"], L["Wd"], H, self.Fd, self.xn, self.md, T,
                       self.wsm, stream=st)
 
-        def experts():   # the router, the experts
-            qg.qg_gemv(qg.QG_F32, L["router"], self.rt, self.lg, self.E, H, T)
+        def experts():   # the routed experts
             qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
                           self.ws)
 

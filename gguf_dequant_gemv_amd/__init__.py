@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
            "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
-           "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
+           "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
 
 _lib = None
@@ -74,6 +74,8 @@ def lib():
         L.qg_rmsnorm.argtypes = [P, P, P, i64, i32, f, f, P]
         L.qg_rmsnorm_multi.argtypes = [P, i64, i32, f, i32, ctypes.POINTER(P), ctypes.POINTER(f),
                                        ctypes.POINTER(P), P]
+        L.qg_rmsnorm_router.argtypes = [P, i64, i32, f, P, f, P, i64, P, i32, ctypes.POINTER(P),
+                                        ctypes.POINTER(f), ctypes.POINTER(P), P]
         L.qg_moe_shared_workspace_size.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_shared_expert), i32,
                                                    i32]
         L.qg_moe_shared_workspace_size.restype = sz
@@ -194,6 +196,20 @@ def qg_rmsnorm_multi(x, n, ntok, eps, ws, ks, ys, stream=None):
     ya = (P * max(m, 1))(*[_ptr(t) for t in ys])
     ka = (f * max(m, 1))(*ks)
     _check("qg_rmsnorm_multi", lib().qg_rmsnorm_multi(_ptr(x), n, ntok, eps, m, wa, ka, ya, _stream(stream)))
+
+
+def qg_rmsnorm_router(x, n, ntok, eps, rw, rk, W, rows, logits, ws=(), ks=(), ys=(), stream=None):
+    """The router's logits of x's norm (rw, rk) and further norms (ws, ks, ys:
+    sequences of device buffers / host floats), one launch."""
+    m = len(ws)
+    if len(ks) != m or len(ys) != m:
+        raise ValueError("qg_rmsnorm_router: ws, ks and ys differ in length")
+    P, f = ctypes.c_void_p, ctypes.c_float
+    wa = (P * max(m, 1))(*[_ptr(t) for t in ws])
+    ya = (P * max(m, 1))(*[_ptr(t) for t in ys])
+    ka = (f * max(m, 1))(*ks)
+    _check("qg_rmsnorm_router", lib().qg_rmsnorm_router(_ptr(x), n, ntok, eps, _ptr(rw), rk, _ptr(W), rows,
+                                                        _ptr(logits), m, wa, ka, ya, _stream(stream)))
 
 
 def make_shared_expert(type, ff, gate, up, down, gate_inp):

@@ -997,6 +997,19 @@ int qg_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, c
     return launch_rmsnorm_multi(x, n, ntok, eps, nout, w, k, y, (hipStream_t)stream);
 }
 
+int qg_rmsnorm_router(const float *x, int64_t n, int ntok, float eps, const float *rw, float rk, const float *W,
+                      int64_t rows, float *logits, int nout, const float *const *w, const float *k, float *const *y,
+                      void *stream) {
+    if (n <= 0 || rows <= 0 || !(eps >= 0.0f)) return QG_EINVAL;
+    if (ntok < 1 || ntok > QG_MAX_TOKENS || nout < 0 || nout > QG_MAX_NORMS) return QG_ELIMIT;
+    if (!x || !rw || !W || !logits || !aligned(x, 4) || !aligned(rw, 4) || !aligned(W, 4) || !aligned(logits, 4))
+        return QG_EINVAL;
+    if (nout > 0 && (!w || !k || !y)) return QG_EINVAL;
+    for (int j = 0; j < nout; j++)
+        if (!w[j] || !y[j] || !aligned(w[j], 4) || !aligned(y[j], 4)) return QG_EINVAL;
+    return launch_norm_gemv_f32(x, n, ntok, eps, rw, rk, W, rows, logits, nout, w, k, y, (hipStream_t)stream);
+}
+
 int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float *w2, const float *w,
                 const float *out_scale, float *x, int64_t n, int ntok, float eps, void *stream) {
     if (n <= 0 || ntok < 1 || !(eps >= 0.0f)) return QG_EINVAL;

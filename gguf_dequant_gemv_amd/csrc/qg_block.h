@@ -17,6 +17,9 @@ int argmax_parts(int64_t n);
 
 int launch_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k,
                    hipStream_t st);
+int launch_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps, const float *rw, float rk, const float *W,
+                         int64_t rows, float *y, int nout, const float *const *w, const float *k, float *const *yo,
+                         hipStream_t st);
 int launch_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, const float *const *w,
                          const float *k, float *const *y, hipStream_t st);
 int launch_gemv_f32(const float *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok,

@@ -97,6 +97,117 @@ __global__ __launch_bounds__(256) void k_rmsnorm_multi(const float *x, int64_t n
     k_rmsnorm_row(x + (int64_t)blockIdx.x * n, o.w[j], o.y[j] + (int64_t)blockIdx.x * n, n, eps, o.k[j]);
 }
 
+// --------------------------------------------- norms + the router GEMV ----
+// One launch for a block's input norms and its f32 router: every workgroup
+// finds the tokens' RMS factors r_t (the sums of squares taken as k_rmsnorm
+// takes them), writes its slice of each output norm y_o = ((x r_t) k_o) w_o,
+// and its waves compute router rows e against the router's input norm
+// ((x r_t) rk) rw, formed on the fly, with k_gemv_f32's loads and order:
+// the logits and norms equal the separate launches' bit for bit.
+template <int NT, bool V4>
+__global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps,
+                                                       const float *rw, float rk, const float *W, int64_t rows,
+                                                       float *y, NormOuts o, int nout) {
+    __shared__ float s_red[4][NT];
+    __shared__ float s_r[NT];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the tokens' sums of squares: thread i's values i, i + 256, ... in order
+    for (int t = 0; t < ntok; t++) {
+        const float *xt = x + (int64_t)t * n;
+        float ss = 0.0f;
+        for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+            float v[LB];
+#pragma unroll
+            for (int b = 0; b < LB; b++) v[b] = i0 + b * 256 < n ? xt[i0 + b * 256] : 0.0f;
+#pragma unroll
+            for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) s_red[wave][t] = ss;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < ntok) {
+        const int t = threadIdx.x;
+        float sum = s_red[0][t];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; w2++) sum += s_red[w2][t];
+        s_r[t] = rms_factor(sum, n, eps);
+    }
+    __syncthreads();
+    // this workgroup's slice of the output norms
+    const int64_t chunk = (n + gridDim.x - 1) / gridDim.x;
+    const int64_t c_lo = (int64_t)blockIdx.x * chunk, c_hi = min(n, c_lo + chunk);
+    for (int j = 0; j < nout; j++)
+        for (int t = 0; t < ntok; t++)
+            for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += 256)
+                o.y[j][(int64_t)t * n + c] = ((x[(int64_t)t * n + c] * s_r[t]) * o.k[j]) * o.w[j][c];
+    // router row r of wave w
+    constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= rows) return;
+    const float *wr = W + r * n;
+    float rt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) rt[t] = t < ntok ? s_r[t] : 0.0f;
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.0f;
+    auto xin = [&](float xv, int t, float g) { return ((xv * rt[t]) * rk) * g; };
+    if constexpr (V4) {
+        for (int64_t c0 = 4 * lane; c0 < n; c0 += 256 * B) {
+            float4 wv[B], gv[B];
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const bool in = c0 + 256 * b < n;
+                wv[b] = in ? *(const float4 *)(wr + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+                gv[b] = in ? *(const float4 *)(rw + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                if (t < ntok) {
+                    float4 xv[B];
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        xv[b] = c0 + 256 * b < n ? *(const float4 *)(x + t * n + c0 + 256 * b)
+                                                 : make_float4(0, 0, 0, 0);
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        acc[t] = fmaf(wv[b].x, xin(xv[b].x, t, gv[b].x), acc[t]);
+                        acc[t] = fmaf(wv[b].y, xin(xv[b].y, t, gv[b].y), acc[t]);
+                        acc[t] = fmaf(wv[b].z, xin(xv[b].z, t, gv[b].z), acc[t]);
+                        acc[t] = fmaf(wv[b].w, xin(xv[b].w, t, gv[b].w), acc[t]);
+                    }
+                }
+            }
+        }
+    } else {
+        for (int64_t c0 = lane; c0 < n; c0 += 64 * B) {
+            float wv[B], gv[B];
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const bool in = c0 + 64 * b < n;
+                wv[b] = in ? wr[c0 + 64 * b] : 0.0f;
+                gv[b] = in ? rw[c0 + 64 * b] : 0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                if (t < ntok) {
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        if (c0 + 64 * b < n) acc[t] = fmaf(wv[b], xin(x[t * n + c0 + 64 * b], t, gv[b]), acc[t]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        if (t < ntok) {
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0) y[t * rows + r] = sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------ f32 GEMV ----
 // y[t][r] = sum_c W[r][c] x[t][c] for f32 weights (the router's logits and the
 // shared expert's gate: qwen3_moe_ssd.js matmulF32).  One wave per row; each
@@ -493,6 +604,25 @@ int launch_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nou
         o.k[j] = k[j];
     }
     hipLaunchKernelGGL(k_rmsnorm_multi, dim3(ntok, nout), dim3(256), 0, st, x, n, eps, o);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps, const float *rw, float rk, const float *W,
+                         int64_t rows, float *y, int nout, const float *const *w, const float *k, float *const *yo,
+                         hipStream_t st) {
+    NormOuts o = {};
+    for (int j = 0; j < nout; j++) {
+        o.w[j] = w[j];
+        o.y[j] = yo[j];
+        o.k[j] = k[j];
+    }
+    const bool v4 = (n % 4) == 0 && ((uintptr_t)W % 16) == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)rw % 16) == 0;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    void (*f)(const float *, int64_t, int, float, const float *, float, const float *, int64_t, float *, NormOuts, int);
+    if (ntok == 1) f = v4 ? k_norm_gemv_f32<1, true> : k_norm_gemv_f32<1, false>;
+    else if (ntok <= 4) f = v4 ? k_norm_gemv_f32<4, true> : k_norm_gemv_f32<4, false>;
+    else f = v4 ? k_norm_gemv_f32<16, true> : k_norm_gemv_f32<16, false>;
+    hipLaunchKernelGGL(f, grid, dim3(256), 0, st, x, n, ntok, eps, rw, rk, W, rows, y, o, nout);
     return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
 }
 

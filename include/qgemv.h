@@ -230,6 +230,26 @@ int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, fl
 int qg_rmsnorm_multi(const float *x, int64_t n, int ntok, float eps, int nout, const float *const *w,
                      const float *k, float *const *y, void *stream);
 
+/* A block's input norms and its f32 router in one launch, per token t:
+ *   logits[t][e] = sum_i W[e][i] * (((x[t][i] * r_t) * rk) * rw[i])
+ *   y_o[t][i]    = ((x[t][i] * r_t) * k[o]) * w_o[i]      (o < nout)
+ * r_t as in qg_rmsnorm: the router's logits of its normed input ([qwen35]
+ * rmsnorm then the router matmulF32; [gemma4] rmsnormK then the router) and
+ * up to QG_MAX_NORMS other norms of the same rows (the experts' and the
+ * dense MLP's inputs), bit for bit what qg_rmsnorm / qg_rmsnorm_multi and
+ * qg_gemv(QG_F32, ...) on the router's norm give when x, rw and W are
+ * 16-byte aligned and n % 4 == 0.  Meant for decode steps: every workgroup
+ * takes every token's sums of squares, so at many tokens the separate
+ * launches are faster.
+ * x: [ntok][n]; rw: [n]; W: [rows][n] f32 (row-major); logits: [ntok][rows];
+ * w, k, y: HOST arrays of nout entries as in qg_rmsnorm_multi (nout may be 0);
+ * no y[o] may overlap x, W or logits.
+ * Errors: QG_EINVAL (n <= 0, rows <= 0, eps < 0 or NaN, null or misaligned
+ * pointer), QG_ELIMIT (ntok outside 1..16, nout outside 0..QG_MAX_NORMS). */
+int qg_rmsnorm_router(const float *x, int64_t n, int ntok, float eps, const float *rw, float rk, const float *W,
+                      int64_t rows, float *logits, int nout, const float *const *w, const float *k,
+                      float *const *y, void *stream);
+
 /* The shared expert of a MoE block (a HOST struct; its pointers are device
  * pointers): a dense gated MLP with ff SF beside the routed experts, scaled
  * by the logistic of a scalar gate logit ([qwen35] ffn_gate_shexp,

@@ -194,6 +194,26 @@ def test_gemm_token_limits():
     assert qg.qg_mlp_workspace_size(8, 2560, 9728, 16) == gu_act16 + 7 * 16 * 2560 * 4
 
 
+def test_rmsnorm_router_rejects():
+    L = qg.lib()
+    ok = (FAKE, 64, 1, 1e-6, FAKE, 1.0, FAKE, 8, FAKE, 0, None, None, None, None)
+    def call(**kw):
+        args = list(ok)
+        names = ["x", "n", "ntok", "eps", "rw", "rk", "W", "rows", "logits", "nout", "w", "k", "y", "stream"]
+        for key, v in kw.items():
+            args[names.index(key)] = v
+        return L.qg_rmsnorm_router(*args)
+    assert call(ntok=17) == qg.QG_ELIMIT
+    assert call(ntok=0) == qg.QG_ELIMIT
+    assert call(nout=qg.QG_MAX_NORMS + 1) == qg.QG_ELIMIT
+    assert call(n=0) == qg.QG_EINVAL
+    assert call(rows=0) == qg.QG_EINVAL
+    assert call(eps=-1.0) == qg.QG_EINVAL
+    assert call(x=None) == qg.QG_EINVAL
+    assert call(W=FAKE + 2) == qg.QG_EINVAL
+    assert call(nout=1) == qg.QG_EINVAL          # nout outputs but no arrays
+
+
 def test_gemm_split_workspace():
     """Prefill-size Q8_0 / Q4_0 launches need scratch: x split into three bf16
     parts (6 bytes per value of the padded chunk), plus whole [split][token][row]

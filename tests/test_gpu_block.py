@@ -95,6 +95,46 @@ def test_rmsnorm_multi(orc, n, T, nout):
         check_rel(host(ys[j]), orc.rmsnorm(x, ws[j], n, T, 1e-6, ks[j]), "rmsnorm multi %d" % j)
 
 
+@pytest.mark.parametrize("n,E,T,nout", [(2048, 256, 1, 1), (2816, 128, 16, 2), (1000, 37, 3, 0), (1001, 9, 2, 1),
+                                         (5000, 8, 2, 3)])
+def test_rmsnorm_router(orc, n, E, T, nout):
+    """Norms + router in one launch: the logits and every norm bit for bit
+    what qg_rmsnorm / qg_gemv(QG_F32) give separately, and both against the
+    oracle."""
+    import gguf_dequant_gemv_amd as qg
+    g = gs.rng(900 + n + E + T)
+    x = gs.activations(g, T, n)
+    rw = gs.norm_weights(g, n)
+    rk = float(np.float32(1.0 / math.sqrt(n)))
+    W = (g.standard_normal((E, n), dtype=np.float32) * np.float32(1.0 / math.sqrt(n))).astype(np.float32)
+    ws = [gs.norm_weights(g, n) for _ in range(nout)]
+    ks = [1.0, 0.5, 2.0][:nout]
+    xt, _ = dev(x)
+    rwt, _ = dev(rw)
+    Wt, _ = dev(W)
+    wts = [dev(w)[0] for w in ws]
+    ys = [_empty((T, n)) for _ in range(nout)]
+    lg = _empty((T, E))
+    say("rmsnorm router", n, E, "T", T, "nout", nout)
+    qg.qg_rmsnorm_router(xt, n, T, 1e-6, rwt, rk, Wt, E, lg, wts, ks, ys)
+    # the separate launches
+    rt = _empty((T, n))
+    qg.qg_rmsnorm(xt, rwt, rt, n, T, 1e-6, rk)
+    lg2 = _empty((T, E))
+    qg.qg_gemv(qg.QG_F32, Wt, rt, lg2, E, n, T)
+    assert np.array_equal(host(lg).view(np.uint32), host(lg2).view(np.uint32))
+    for j in range(nout):
+        one = _empty((T, n))
+        qg.qg_rmsnorm(xt, wts[j], one, n, T, 1e-6, ks[j])
+        assert np.array_equal(host(ys[j]).view(np.uint32), host(one).view(np.uint32)), "norm %d" % j
+        check_rel(host(ys[j]), orc.rmsnorm(x, ws[j], n, T, 1e-6, ks[j]), "norm %d" % j)
+    # logits against the oracle's GEMV of the GPU's router input
+    rth = host(rt)
+    check_rel(rth, orc.rmsnorm(x, rw, n, T, 1e-6, rk), "router input norm")
+    y_ref, A = orc.gemv(orc.F32, W.view(np.uint8), rth, E, n, T)
+    check_rows(host(lg), y_ref, A, "router logits")
+
+
 # ------------------------------------------------- shared-expert MoE block --
 def run_shared_gpu(c, lt=None, xt=None, resid=None, pool_off=0, sh_off=0):
     """qg_moe_ffn_shared on case c; lt / xt / resid: device tensors to use in
