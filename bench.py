@@ -455,7 +455,8 @@ class GemmaBlock(Workload):
 class HeadPick(Workload):
     """The decode loop's tail, 1 token: head GEMV, optional logit soft cap,
     greedy pick, and the picked token's (tied) embedding row gathered for the
-    next step (qg_gemv, qg_argmax, qg_embed), rotating weight copies."""
+    next step (qg_gemv, qg_argmax_embed: the pick and the gather in two
+    launches), rotating weight copies."""
 
     def __init__(self, t, V, H, cap, emb_scale, total_bytes, label):
         import torch
@@ -482,8 +483,8 @@ class HeadPick(Workload):
         qg = self.qg
         W = self.W[i % len(self.W)]
         qg.qg_gemv(self.t, W, self.x, self.logits, self.V, self.H, 1)
-        qg.qg_argmax(self.logits, self.V, 1, self.cap, self.idx, self.ws)
-        qg.qg_embed(self.t, W, self.V, self.H, self.idx, 1, self.scale, self.emb)
+        qg.qg_argmax_embed(self.logits, self.V, 1, self.cap, self.idx, self.ws, self.t, W, self.V, self.H,
+                           self.scale, self.emb)
 
     def dominant_step(self, i):
         self.qg.qg_gemv(self.t, self.W[i % len(self.W)], self.x, self.logits, self.V, self.H, 1)

@@ -22,7 +22,7 @@ EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_ge
            "qg_dequant",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
-           "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax")
+           "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax", "qg_argmax_embed")
 
 _lib = None
 
@@ -86,6 +86,7 @@ def lib():
         L.qg_argmax_workspace_size.argtypes = [i64, i32]
         L.qg_argmax_workspace_size.restype = sz
         L.qg_argmax.argtypes = [P, i64, i32, f, P, P, sz, P]
+        L.qg_argmax_embed.argtypes = [P, i64, i32, f, P, P, sz, i32, P, i64, i64, f, P, P]
         _lib = L
     return _lib
 
@@ -245,3 +246,10 @@ def qg_argmax_workspace_size(n, ntok):
 def qg_argmax(logits, n, ntok, softcap, idx, workspace, workspace_bytes=None, stream=None):
     _check("qg_argmax", lib().qg_argmax(_ptr(logits), n, ntok, softcap, _ptr(idx), _ptr(workspace),
                                         _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def qg_argmax_embed(logits, n, ntok, softcap, idx, workspace, type, W, rows, cols, scale, out,
+                    workspace_bytes=None, stream=None):
+    _check("qg_argmax_embed", lib().qg_argmax_embed(_ptr(logits), n, ntok, softcap, _ptr(idx), _ptr(workspace),
+                                                    _nbytes(workspace, workspace_bytes), type, _ptr(W), rows, cols,
+                                                    scale, _ptr(out), _stream(stream)))

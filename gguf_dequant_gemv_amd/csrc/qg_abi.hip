@@ -1058,4 +1058,23 @@ int qg_argmax(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, v
     return launch_argmax(logits, n, ntok, softcap, pv, pi, idx, (hipStream_t)stream);
 }
 
+int qg_argmax_embed(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, void *workspace,
+                    size_t workspace_bytes, int type, const void *W, int64_t rows, int64_t cols, float scale,
+                    float *out, void *stream) {
+    if (n <= 0 || ntok < 1 || !(softcap >= 0.0f)) return QG_EINVAL;
+    if (n > INT32_MAX || ntok > 65535) return QG_ELIMIT;
+    if (!logits || !idx || !workspace || !aligned(logits, 4) || !aligned(idx, 4) || !aligned(workspace, 256))
+        return QG_EINVAL;
+    const size_t need = qg_argmax_workspace_size(n, ntok);
+    if (workspace_bytes < need) return QG_EINVAL;
+    Shape s;
+    int rc = make_shape(type, rows, cols, s);
+    if (rc) return rc;
+    if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;
+    float *pv = (float *)workspace;
+    int32_t *pi = (int32_t *)((uint8_t *)workspace + need / 2);
+    return launch_argmax_embed(logits, n, ntok, softcap, pv, pi, idx, type, (const uint8_t *)W, rows, (int)s.cols,
+                               s.row_bytes, scale, out, (hipStream_t)stream);
+}
+
 }  // extern "C"

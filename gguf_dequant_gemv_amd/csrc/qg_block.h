@@ -30,5 +30,8 @@ int launch_post_ffn(const float *mlp, const float *moe, const float *w1, const f
                     const float *os, float *x, int64_t n, int ntok, float eps, hipStream_t st);
 int launch_argmax(float *l, int64_t n, int ntok, float cap, float *pv, int32_t *pi, int32_t *idx,
                   hipStream_t st);
+int launch_argmax_embed(float *l, int64_t n, int ntok, float cap, float *pv, int32_t *pi, int32_t *idx, int type,
+                        const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, float scale, float *out,
+                        hipStream_t st);
 
 }  // namespace qg

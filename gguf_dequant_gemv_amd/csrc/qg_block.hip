@@ -453,16 +453,16 @@ QG_DEV void embed_part(int p, const u32 (&w)[U::ND], float scale, float *o) {
     }
 }
 
+// this workgroup's share of row id of token blockIdx.y (the grid as k_embed's)
 template <class U>
-__global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
-                                               const int32_t *tok, float scale, float *out) {
+QG_DEV void embed_row(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, int32_t id, float scale,
+                      float *out) {
     constexpr int NP = U::VALUES / EMBED_VALUES;
     const int nbr = cols / U::VALUES;
     const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const int p = gw % NP;
     const int b = (gw / NP) * 64 + (threadIdx.x & 63);
     if (b >= nbr) return;
-    const int32_t id = tok[blockIdx.y];
     float *o = out + (int64_t)blockIdx.y * cols + (int64_t)b * U::VALUES + EMBED_VALUES * p;
     if (id < 0 || id >= rows) {
 #pragma unroll
@@ -475,6 +475,12 @@ __global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, i
     u32 w[U::ND];
     U::load(rs, ph, w);
     embed_part<U>(p, w, scale, o);
+}
+
+template <class U>
+__global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
+                                               const int32_t *tok, float scale, float *out) {
+    embed_row<U>(W, rows, cols, row_bytes, tok[blockIdx.y], scale, out);
 }
 
 template <class U>
@@ -570,6 +576,43 @@ __global__ __launch_bounds__(256) void k_argmax_part(float *l, int64_t n, int64_
 
 // Phase 2, one wave per token: the winner over the G partials; 0 when the
 // token's logits hold no number at all.
+QG_DEV int argmax_final_wave(const float *pv, const int32_t *pi, int G, int t, int lane) {
+    float bv = 0.0f;
+    int bi = -1;
+    float v[ARGMAX_MAX_PARTS / 64];
+    int ix[ARGMAX_MAX_PARTS / 64];
+#pragma unroll
+    for (int u = 0; u < ARGMAX_MAX_PARTS / 64; u++) {
+        const int g = lane + 64 * u;
+        v[u] = g < G ? pv[(int64_t)t * G + g] : 0.0f;
+        ix[u] = g < G ? pi[(int64_t)t * G + g] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < ARGMAX_MAX_PARTS / 64; u++) am_merge(bv, bi, v[u], ix[u]);
+    am_wave(bv, bi);
+    return bi < 0 ? 0 : bi;
+}
+
+// Phase 2 and the picked token's embedding row in one launch: wave 0 of
+// every workgroup of token t takes the winner as k_argmax_final does (the
+// same merges, so the same index), workgroup (0, t) stores it, and the
+// workgroup then gathers its share of row idx as k_embed does.
+template <class U>
+__global__ __launch_bounds__(256) void k_argmax_embed(const float *pv, const int32_t *pi, int G, int32_t *idx,
+                                                      const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
+                                                      float scale, float *out) {
+    __shared__ int s_id;
+    if (threadIdx.x < 64) {
+        const int id = argmax_final_wave(pv, pi, G, blockIdx.y, threadIdx.x);
+        if (threadIdx.x == 0) {
+            s_id = id;
+            if (blockIdx.x == 0) idx[blockIdx.y] = id;
+        }
+    }
+    __syncthreads();
+    embed_row<U>(W, rows, cols, row_bytes, s_id, scale, out);
+}
+
 __global__ __launch_bounds__(64) void k_argmax_final(const float *pv, const int32_t *pi, int G, int32_t *idx) {
     const int t = blockIdx.x, lane = threadIdx.x;
     float bv = 0.0f;
@@ -654,6 +697,34 @@ int launch_post_ffn(const float *mlp, const float *moe, const float *w1, const f
 int argmax_parts(int64_t n) {
     int64_t g = (n + ARGMAX_SPAN - 1) / ARGMAX_SPAN;
     return (int)(g < ARGMAX_MAX_PARTS ? g : ARGMAX_MAX_PARTS);
+}
+
+template <class U>
+static int launch_argmax_embed_t(int G, const float *pv, const int32_t *pi, int32_t *idx, const uint8_t *W,
+                                 int64_t rows, int cols, int64_t row_bytes, int ntok, float scale, float *out,
+                                 hipStream_t st) {
+    const int nbr = cols / U::VALUES;
+    const int64_t waves = (int64_t)((nbr + 63) / 64) * (U::VALUES / EMBED_VALUES);
+    const dim3 grid((unsigned)((waves + 3) / 4), ntok);
+    hipLaunchKernelGGL(k_argmax_embed<U>, grid, dim3(256), 0, st, pv, pi, G, idx, W, rows, cols, row_bytes, scale,
+                       out);
+    return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+}
+
+int launch_argmax_embed(float *l, int64_t n, int ntok, float cap, float *pv, int32_t *pi, int32_t *idx, int type,
+                        const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, float scale, float *out,
+                        hipStream_t st) {
+    const int G = argmax_parts(n);
+    const int64_t span = (n + G - 1) / G;
+    const float inv = cap > 0.0f ? (float)(1.0 / (double)cap) : 0.0f;
+    hipLaunchKernelGGL(k_argmax_part, dim3(G, ntok), dim3(256), 0, st, l, n, span, cap, inv, pv, pi);
+    if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    switch (type) {
+    case T_Q8_0: return launch_argmax_embed_t<UQ8_0B>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);
+    case T_Q4_0: return launch_argmax_embed_t<UQ4_0B>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);
+    case T_Q4_K: return launch_argmax_embed_t<UQ4_K>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);
+    default: return launch_argmax_embed_t<UQ6_K>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);
+    }
 }
 
 int launch_argmax(float *l, int64_t n, int ntok, float cap, float *pv, int32_t *pi, int32_t *idx,

@@ -318,6 +318,18 @@ size_t qg_argmax_workspace_size(int64_t n, int ntok);
 int qg_argmax(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, void *workspace,
               size_t workspace_bytes, void *stream);
 
+/* The decode loop's tail in two launches: qg_argmax, then the picked
+ * tokens' rows of the (tied) embedding table as qg_embed gathers them,
+ * out[t] = W[idx[t]] * scale ([qwen3] argmax then embedQ8, [gemma4] argmax
+ * then embedQ6K).  The winner over the partial spans is taken inside the
+ * gathering launch; idx and out equal what qg_argmax followed by qg_embed
+ * give, bit for bit.  Arguments as those two calls (logits, idx, workspace
+ * as qg_argmax; type, W, rows, cols, scale, out as qg_embed).
+ * Errors: as qg_argmax and qg_embed (ntok up to 65535). */
+int qg_argmax_embed(float *logits, int64_t n, int ntok, float softcap, int32_t *idx, void *workspace,
+                    size_t workspace_bytes, int type, const void *W, int64_t rows, int64_t cols, float scale,
+                    float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -214,6 +214,25 @@ def test_rmsnorm_router_rejects():
     assert call(nout=1) == qg.QG_EINVAL          # nout outputs but no arrays
 
 
+def test_argmax_embed_rejects():
+    L = qg.lib()
+    n = qg.qg_argmax_workspace_size(1000, 1)
+    good = [FAKE, 1000, 1, 0.0, FAKE, FAKE, n, 8, FAKE, 1000, 64, 1.0, FAKE, None]
+    def call(i, v):
+        args = list(good)
+        args[i] = v
+        return L.qg_argmax_embed(*args)
+    assert call(1, 0) == qg.QG_EINVAL             # n
+    assert call(2, 0) == qg.QG_EINVAL             # ntok
+    assert call(3, -1.0) == qg.QG_EINVAL          # softcap
+    assert call(6, n - 4) == qg.QG_EINVAL         # short workspace
+    assert call(5, FAKE + 16) == qg.QG_EINVAL     # misaligned workspace
+    assert call(7, 99) == qg.QG_EINVAL            # block type
+    assert call(10, 48) == qg.QG_EINVAL           # cols % 32
+    assert call(8, None) == qg.QG_EINVAL          # W
+    assert call(12, FAKE + 2) == qg.QG_EINVAL     # out misaligned
+
+
 def test_gemm_split_workspace():
     """Prefill-size Q8_0 / Q4_0 launches need scratch: x split into three bf16
     parts (6 bytes per value of the padded chunk), plus whole [split][token][row]

@@ -390,6 +390,40 @@ def test_argmax(orc, n, T, cap):
         assert got[0] == n // 3
 
 
+@pytest.mark.parametrize("t,V,cols,cap,T", [(gs.Q8_0, 151936, 2560, 0.0, 1), (gs.Q6_K, 50000, 2816, 30.0, 1),
+                                          (gs.Q4_0, 3000, 96, 0.0, 3), (gs.Q4_K, 700, 512, 30.0, 2)])
+def test_argmax_embed(orc, t, V, cols, cap, T):
+    """The pick and the gather in two launches equal qg_argmax followed by
+    qg_embed bit for bit; the picks against the oracle's."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    g = gs.rng(560 + V + T)
+    l = (g.standard_normal((T, V), dtype=np.float32) * np.float32(8.0)).astype(np.float32)
+    W = gs.weights(t, g, V, cols)
+    Wt, _ = dev(W)
+    scale = float(np.float32(math.sqrt(cols)))
+    say("argmax embed", gs.NAMES[t], V, cols, "cap", cap, "T", T)
+    lt1, _ = dev(l)
+    lt2, _ = dev(l)
+    nws = qg.qg_argmax_workspace_size(V, T)
+    ws1 = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+    ws2 = torch.empty(nws // 4, dtype=torch.float32, device="cuda")
+    idx1 = _empty((T,), "int32", -1)
+    idx2 = _empty((T,), "int32", -1)
+    out1 = _empty((T, cols))
+    out2 = _empty((T, cols))
+    qg.qg_argmax_embed(lt1, V, T, cap, idx1, ws1, t, Wt, V, cols, scale, out1)
+    qg.qg_argmax(lt2, V, T, cap, idx2, ws2)
+    qg.qg_embed(t, Wt, V, cols, idx2, T, scale, out2)
+    assert np.array_equal(host(idx1), host(idx2))
+    assert np.array_equal(host(out1).view(np.uint32), host(out2).view(np.uint32))
+    assert np.array_equal(host(lt1).view(np.uint32), host(lt2).view(np.uint32))   # the capped logits
+    got_l = host(lt1)
+    assert host(idx1).tolist() == orc.argmax(got_l, V, T).tolist()
+    ref = orc.embed(t, W, V, cols, host(idx1).astype(np.int32), scale)
+    assert np.array_equal(host(out1).view(np.uint32), ref.view(np.uint32))
+
+
 def test_argmax_degenerate_rows():
     import gguf_dequant_gemv_amd as qg
     n = 4099
