@@ -337,8 +337,9 @@ GemmSplit gemm_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
 // (eight per wave) whose raw sums the reduce launch adds in split order.
 // Rows under 192 blocks stay whole: there the reduce launch costs more than
 // the shorter walk saves (2816 x 2112 Q4_0 MLP at 16 tokens: 22.1 us whole,
-// 26.8 us split).  2560 x 9728 Q8_0 at 16 tokens is 80 tiles: 7 splits
-// (the MLP at 4 tokens 69 -> 34 us).
+// 26.8 us split) -- unless the tiles fill under a quarter of the CUs, when
+// rows of 64+ blocks split into splits of 16+.  2560 x 9728 Q8_0 at 16
+// tokens is 80 tiles: 7 splits (the MLP at 4 tokens 69 -> 34 us).
 int small_groups(int64_t rows, int glu, int64_t copies) {
     return (rows + 16 * (glu ? 2 : 4) - 1) / (16 * (glu ? 2 : 4)) * copies < 2 * NUM_CU ? 2 : 4;
 }
@@ -349,10 +350,14 @@ GemmSplit small_split(int type, int64_t rows, int64_t cols, int ntok, int glu) {
     const int groups = small_groups(rows, glu, 1);
     const int64_t tile_rows = 16 * (glu ? groups / 2 : groups);
     const int64_t wgs = (rows + tile_rows - 1) / tile_rows;
-    if (wgs >= NUM_CU || nb < 192) return none;
+    // a launch of under a quarter of the CUs' worth of tiles splits rows of
+    // 64+ blocks into splits of 16+ (the shared expert's 512 x 2048 gate and
+    // up at 16 tokens: 32 tiles)
+    const bool sparse = wgs < NUM_CU / 4;
+    if (wgs >= NUM_CU || nb < (sparse ? 64 : 192)) return none;
     const int64_t want = (2 * NUM_CU + wgs - 1) / wgs;
     int64_t kb = (nb + want - 1) / want;
-    if (kb < 32) kb = 32;
+    if (kb < (sparse ? 16 : 32)) kb = sparse ? 16 : 32;
     const int64_t n = (nb + kb - 1) / kb;
     if (n < 2) return none;
     return {(int)n, (int)kb};
@@ -860,15 +865,16 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
 }
 
 // Workspace of a shared expert after the routed part's: gu [ntok][2 SF],
-// act [ntok][SF], sh [ntok][H], each 256-byte aligned.
+// act [ntok][SF] and the scratch of its qg_mlp call (qg_mlp's layout), then
+// sh [ntok][H], each 256-byte aligned.
 struct SharedWs {
     size_t gu, act, sh, total;
 };
-SharedWs shared_ws(int64_t H, int64_t SF, int ntok) {
+SharedWs shared_ws(int type, int64_t H, int64_t SF, int ntok) {
     SharedWs o;
     o.gu = 0;
     o.act = align256((size_t)ntok * 2 * (size_t)SF * 4);
-    o.sh = o.act + align256((size_t)ntok * (size_t)SF * 4);
+    o.sh = o.act + align256((size_t)ntok * (size_t)SF * 4) + mlp_scratch_bytes(type, H, SF, ntok);
     o.total = o.sh + align256((size_t)ntok * (size_t)H * 4);
     return o;
 }
@@ -918,7 +924,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
 size_t qg_moe_shared_workspace_size(const qg_moe *m, const qg_shared_expert *sh, int topk, int ntok) {
     const size_t a = qg_moe_workspace_size(m, topk, ntok);
     if (!a || !sh || sh->ff <= 0) return 0;
-    return a + shared_ws(m->hidden, sh->ff, ntok).total;
+    return a + shared_ws(sh->type, m->hidden, sh->ff, ntok).total;
 }
 
 int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *router_logits, int topk,
@@ -937,7 +943,7 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     hipStream_t st = (hipStream_t)stream;
     const size_t base = qg_moe_workspace_size(m, topk, ntok);
     if (!base) return ntok < 1 || ntok > QG_MAX_TOKENS ? QG_ELIMIT : QG_EINVAL;
-    const SharedWs S = shared_ws(m->hidden, sh->ff, ntok);
+    const SharedWs S = shared_ws(sh->type, m->hidden, sh->ff, ntok);
     float *dn = nullptr;
     int32_t *valid = nullptr;
     uint8_t *ws = (uint8_t *)workspace + base;

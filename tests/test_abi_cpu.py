@@ -255,7 +255,12 @@ def test_gemm_split_workspace():
     assert qg.qg_gemm_workspace_size(qg.QG_Q4_K, 2560, 9728, 16) == 0
     assert qg.qg_gemm_workspace_size(8, 2560, 512, 16) == 0                  # 16 blocks: too short to split
     assert qg.qg_gemm_workspace_size(2, 2816, 2112, 16) == 0                 # 66 blocks: whole rows
-    assert qg.qg_gemm_workspace_size(8, 33, 250 * 32, 16) == 8 * 16 * 33 * 4   # 8 splits of 32 blocks
+    # under a quarter of the CUs' worth of tiles: rows of 64+ blocks split into 16+
+    assert qg.qg_gemm_workspace_size(8, 33, 250 * 32, 16) == 16 * 16 * 33 * 4   # 2 tiles: 16 splits of 16
+    assert qg.qg_gemm_workspace_size(8, 512, 2048, 16) == 4 * 16 * 512 * 4      # 16 tiles: 4 splits
+    assert qg.qg_gemm_workspace_size(8, 512, 63 * 32, 16) == 0                  # 63 blocks: whole rows
+    # the shared expert's 512 x 2048 gate and up (32 gated tiles) split 4 ways
+    assert qg.qg_mlp_workspace_size(8, 2048, 512, 16) == 16 * 2 * 512 * 4 + 16 * 512 * 4 + 4 * 16 * 2 * 512 * 4
     assert qg.qg_gemm_workspace_size(qg.QG_Q6_K, 2560, 9728, 64) == 0
     assert 64 * 128 * 6 <= qg.qg_gemm_workspace_size(8, 2560, 128, 64) < 2560 * 64 * 4   # too short to split
     assert qg.qg_gemm_workspace_size(8, 2560, 9728, qg.QG_MAX_PREFILL + 1) == 0

@@ -171,7 +171,7 @@ def run_shared_gpu(c, lt=None, xt=None, resid=None, pool_off=0, sh_off=0):
     a0 = _align256(P * 2 * F * 4) // 4
     d0 = a0 + _align256(P * F * 4) // 4
     s_a = base + _align256(T * 2 * SF * 4) // 4
-    s_h = s_a + _align256(T * SF * 4) // 4
+    s_h = (nbytes - _align256(T * H * 4)) // 4      # sh is the last region
     out = dict(resid0=r0, resid=host(resid), ids=host(ids), w=host(w), status=int(host(status)[0]),
                x=host(xt), logits=host(lt),
                gu=wsh[:P * 2 * F].reshape(T, k, 2 * F), act=wsh[a0:a0 + P * F].reshape(T, k, F),
