@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 
 # Every symbol include/qgemv.h declares.
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
-           "qg_dequant",
+           "qg_dequant", "qg_gemv_plan",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax", "qg_argmax_embed")
@@ -63,6 +63,7 @@ def lib():
         L.qg_gemm_workspace_size.restype = sz
         L.qg_gemm.argtypes = [i32, P, P, P, i64, i64, i32, P, sz, P]
         L.qg_dequant.argtypes = [i32, P, P, i64, i64, P]
+        L.qg_gemv_plan.argtypes = [i32, i64, i64, i32, i32, i32, P]
         L.qg_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
         L.qg_mlp_workspace_size.argtypes = [i32, i64, i64, i32]
         L.qg_mlp_workspace_size.restype = sz
@@ -137,6 +138,15 @@ def qg_gemm(type, W, x, y, rows, cols, ntok, workspace=None, workspace_bytes=Non
     nbytes = 0 if workspace is None else _nbytes(workspace, workspace_bytes)
     _check("qg_gemm", lib().qg_gemm(type, _ptr(W), _ptr(x), _ptr(y), rows, cols, ntok, _ptr(workspace), nbytes,
                                     _stream(stream)))
+
+
+def qg_gemv_plan(type, rows, cols, ntok=1, w_aligned16=True, query_device=False):
+    """The plan qg_gemv takes for a shape, as a dict (see include/qgemv.h)."""
+    out = (ctypes.c_int32 * 8)()
+    _check("qg_gemv_plan", lib().qg_gemv_plan(type, rows, cols, ntok, int(bool(w_aligned16)),
+                                              int(bool(query_device)), ctypes.addressof(out)))
+    keys = ("kind", "lanes_per_row", "tokens_per_wg", "row_tiles", "workgroups", "lds_bytes", "depth", "xchunk")
+    return dict(zip(keys, list(out)))
 
 
 def qg_dequant(type, W, out, rows, cols, stream=None):

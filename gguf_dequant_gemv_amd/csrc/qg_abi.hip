@@ -583,6 +583,43 @@ int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int
     return gemv_entry(type, W, x, y, rows, cols, ntok, QG_MAX_PREFILL, workspace, workspace_bytes, stream);
 }
 
+int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16, int query_device, int32_t *out) {
+    if (!out) return QG_EINVAL;
+    Shape s;
+    int rc = make_shape(type, rows, cols, s);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+    // the first launch of the call (rows in launches of at most MAX_RANGE bytes)
+    const int64_t chunk = MAX_RANGE / s.row_bytes;
+    if (s.rows > chunk) s.rows = chunk;
+    const Plan p = make_plan(s, ntok, 1, w_aligned16 != 0);
+    for (int i = 0; i < 8; i++) out[i] = 0;
+    out[0] = p.kind;
+    out[2] = p.nt;
+    if (p.kind == UK_MFMA) {
+        const int groups = small_groups(s.rows, 0, 1);
+        out[3] = (int32_t)((s.rows + 16 * groups - 1) / (16 * groups));
+        if (query_device) {
+            const int64_t cap = resident_wgs(gemv_kernel_mfma(type, groups), 0);
+            out[4] = (int32_t)(out[3] < cap ? out[3] : cap);
+        }
+        return QG_OK;
+    }
+    out[1] = p.lpr;
+    out[3] = p.ntiles;
+    if (query_device) {
+        gemv_fn f = pick(type, p, false);
+        if (p.lds > 64 * 1024 &&
+            hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds) != hipSuccess)
+            return QG_EHIP;
+        out[4] = grid_for(p, f);
+    }
+    out[5] = (int32_t)p.lds;
+    out[6] = p.depth;
+    out[7] = p.xchunk;
+    return QG_OK;
+}
+
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
     Shape s;
     int rc = make_shape(type, rows, cols, s);

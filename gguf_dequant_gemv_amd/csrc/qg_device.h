@@ -366,10 +366,14 @@ struct UQ6_K {
 };
 
 // ---------------------------------------------------------- routing ----
-QG_DEV u32 order_key(float f) {  // monotone map f32 -> u32 (-0 folded onto +0)
+// Monotone map f32 -> u32 for the pick order: -0 folded onto +0, and every
+// NaN to 0, below -inf (whose key is 0x007FFFFF), so a NaN logit is picked
+// only after every number, the lowest index first.
+QG_DEV u32 order_key(float f) {
     u32 u = __builtin_bit_cast(u32, f);
     if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const u32 key = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return f != f ? 0u : key;
 }
 
 // Maximum over the wave, uniform: DPP within each row of 16 lanes, then the

@@ -1089,9 +1089,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
     }
     __syncthreads();
 
+    // descriptors from the ranges' 4-byte-aligned starts, up to the dword that
+    // holds the last byte (no load below reads past that dword)
     const u32 ph0 = (u32)((uintptr_t)Wg0 & 3u), ph1 = (u32)((uintptr_t)Wg1 & 3u);
-    const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
-    const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
+    const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 3) & ~(int64_t)3));
+    const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 3) & ~(int64_t)3));
 
     // the four waves split each row's blocks (wave w takes blocks w, w+4, ...)
     // and their partial sums are added in wave order at the tile's end.  A
@@ -1126,18 +1128,24 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; i++) acc[gi][i] = 0.0f;
 
-        // block b's raw data: a 12-byte window holding the lane's 8 code bytes,
-        // the dword holding its row's scale, and its token's 8 x values
+        // block b's raw data: the dwords holding the lane's 8 code bytes (two
+        // when they start on a dword, else three), the dword holding its row's
+        // scale, and its token's 8 x values
         u32 win[PF + 1][GR][3], sd[PF + 1][GR];
         f32x4 xa[PF + 1], xb[PF + 1];
         auto fetch = [&](int b, int k) {
-            b = min(b, nb - 1);   // past the row's end: re-load its last block
+            b = min(b, b_hi - 1);   // past this range's end: re-load its last block
 #pragma unroll
             for (int gi = 0; gi < GR; gi++) {
                 const u32 o = rbase[gi] + (u32)b * BYTES + cpos;
                 const rsrc_t rs = hi[gi] ? rs1 : rs0;
-                const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rs, o & ~3u, 0, 0);
-                win[k][gi][0] = v.x; win[k][gi][1] = v.y; win[k][gi][2] = v.z;
+                const u32 oa = o & ~3u;
+                const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, oa, 0, 0);
+                // a third dword only when the codes straddle three; else the
+                // second again (the shift below then never takes its bytes), so
+                // no load reaches past the dword holding the block's last byte
+                win[k][gi][2] = __builtin_amdgcn_raw_buffer_load_b32(rs, oa + ((o & 3u) ? 8u : 4u), 0, 0);
+                win[k][gi][0] = v.x; win[k][gi][1] = v.y;
                 sd[k][gi] = __builtin_amdgcn_raw_buffer_load_b32(rs, (rbase[gi] + (u32)b * BYTES) & ~3u, 0, 0);
             }
             if (a.x_vec) {

@@ -114,6 +114,21 @@ int qg_gemm(int type, const void *W, const float *x, float *y,
             int64_t rows, int64_t cols, int ntok, void *workspace,
             size_t workspace_bytes, void *stream);
 
+/* The launch plan qg_gemv takes for a shape (host only; for tests and tuning).
+ * out[8] (a HOST array) receives: [0] kernel kind (0 per-lane unit loads, 1
+ * weights staged through LDS from 16-byte-aligned rows, 2 the same for any
+ * 2-byte phase, 3 matrix-core small batch), [1] lanes per row (0 for kind 3),
+ * [2] tokens per workgroup, [3] row tiles, [4] workgroups along the rows
+ * (grid-stride: each walks row tiles wg, wg + [4], ...; needs a device query,
+ * 0 when query_device is 0), [5] dynamic LDS bytes, [6] weight stages in
+ * flight per wave, [7] x chunk (row elements staged at a time, 0 = all of x).
+ * The plan of the first launch of the call (launches cover at most 2 GiB of
+ * weights each).  w_aligned16: W would start 16-byte aligned.
+ * Errors: as qg_gemv, QG_EINVAL for a null out, QG_EHIP when the device query
+ * fails. */
+int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16, int query_device,
+                 int32_t *out);
+
 /* Dequantize a whole tensor: out[r][c] = W[r][c] as f32, bit-exact (each
  * value is the f32 nearest to its exact value; for Q8_0, Q4_0 and Q6_K the
  * exact value is always an f32).  The block-unpack layer's test hook.

@@ -338,6 +338,18 @@ void or_glu_f32(int act, const float *gu, int64_t F, double *out)
  * the lowest index, division by the sum of the picked probabilities).  Ranking
  * the logits is the same order as ranking exact probabilities, and the full
  * softmax denominator cancels in the renormalised weights. */
+/* Logit a ranks above logit b in the pick order: the larger number; a NaN
+ * ranks below every number and two NaNs (or equal numbers, -0 and +0
+ * included) leave the order to the index.  The pages' kernel softmaxes
+ * finite logits only and says nothing about NaN; this reading never prefers
+ * a NaN to a number. */
+static int ranks_above(float a, float b)
+{
+    if (isnan(a)) return 0;
+    if (isnan(b)) return 1;
+    return a > b;
+}
+
 int or_router_topk(const float *logits, int E, int k, int ntok, int32_t *ids, double *w)
 {
     if (E <= 0 || k <= 0 || k > E || ntok <= 0) return -1;
@@ -350,7 +362,7 @@ int or_router_topk(const float *logits, int E, int k, int ntok, int32_t *ids, do
             int best = -1;
             for (int e = 0; e < E; e++) {
                 if (taken[e]) continue;
-                if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep lower index */
+                if (best < 0 || ranks_above(l[e], l[best])) best = e;   /* strict: ties keep lower index */
             }
             taken[best] = 1;
             ids[t * k + j] = best;

@@ -273,3 +273,19 @@ def test_gemm_split_workspace():
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE, n - 256, None) == qg.QG_EINVAL   # short
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, FAKE + 16, n, None) == qg.QG_EINVAL    # misaligned
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, None, n, None) == qg.QG_EINVAL         # null
+
+
+def test_gemv_plan_multi_tile_shapes():
+    """The shapes of the multi-tile parity cases take the per-lane kernel with
+    more row tiles than workgroups can be resident at once (256 CUs, at most
+    8 workgroups of 4 waves each), so some workgroup walks several tiles."""
+    p = qg.qg_gemv_plan(qg.QG_Q6_K, 262144, 2816, 1)
+    assert p["kind"] == 0 and p["lanes_per_row"] == 8 and p["row_tiles"] > 256 * 8
+    p = qg.qg_gemv_plan(qg.QG_Q8_0, 150001, 33 * 32, 1)
+    assert p["kind"] == 0 and p["row_tiles"] > 256 * 8
+    # an even block count takes the LDS-staged kernel instead
+    assert qg.qg_gemv_plan(qg.QG_Q8_0, 151936, 2560, 1)["kind"] == 1
+    assert qg.qg_gemv_plan(qg.QG_Q8_0, 151936, 2560, 1, w_aligned16=False)["kind"] == 2
+    assert qg.qg_gemv_plan(qg.QG_Q8_0, 1024, 2048, 8)["kind"] == 3
+    with pytest.raises(qg.QgError):
+        qg.qg_gemv_plan(qg.QG_Q8_0, 1024, 2047, 1)

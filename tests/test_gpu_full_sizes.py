@@ -99,6 +99,48 @@ def test_kquant_gemv_full(orc, which):
     assert np.isfinite(y).all()
 
 
+def _grid_stride_rows(plan, rows, g, n=400):
+    """Rows to check in a grid-stride launch: the first and last 40, seeded
+    random rows, and rows from the last tile that several workgroups walk
+    (workgroup w takes tiles w, w + grid, ...)."""
+    tile_rows = 4 * (64 // plan["lanes_per_row"])
+    gx, tiles = plan["workgroups"], plan["row_tiles"]
+    assert 0 < gx < tiles, "the launch must give some workgroup more than one tile: %r" % plan
+    idx = set(range(40)) | set(range(rows - 40, rows))
+    idx |= set(g.choice(rows, size=n, replace=False).tolist())
+    for wg in sorted({0, 1, gx // 2, gx - 2, gx - 1}):
+        last = wg + ((tiles - 1 - wg) // gx) * gx
+        assert last > wg, "workgroup %d walks one tile only" % wg
+        r0 = last * tile_rows
+        idx |= {min(r0 + j, rows - 1) for j in (0, 1, tile_rows // 2, tile_rows - 1)}
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+@pytest.mark.parametrize("t,rows,cols", [
+    # the Q6_K head shape on the per-lane kernel (8 lanes a row, 32-row tiles)
+    (gs.Q6_K, 262144, 2816),
+    # odd Q8_0 block count (per-lane kernel, single blocks), ragged last tile
+    (gs.Q8_0, 150001, 33 * 32)])
+def test_gemv_multi_tile_workgroups(orc, t, rows, cols):
+    """The per-lane kernel's loop over several row tiles per workgroup, which
+    runs when the tiles outnumber the workgroups resident at once."""
+    import gguf_dequant_gemv_amd as qg
+    plan = qg.qg_gemv_plan(t, rows, cols, 1, True, True)
+    say("multi-tile gemv", gs.NAMES[t], rows, cols, plan)
+    assert plan["kind"] == 0
+    g = gs.rng(40 + t)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, 1, cols)
+    Wt, _ = dev(W)
+    xt, _ = dev(x)
+    y = gemv_gpu(t, Wt, xt, rows, cols, 1)
+    del Wt
+    ri = _grid_stride_rows(plan, rows, g)
+    yr, A = orc.gemv(t, W, x, rows, cols, 1, row_idx=ri)
+    check_rows(y[:, ri], yr, A, "%s %dx%d multi-tile" % (gs.NAMES[t], rows, cols))
+    assert np.isfinite(y).all()
+
+
 def test_mlp_gate_up_x_chunks(orc):
     """A gated launch whose x (24576 wide) is staged in chunks and whose row
     tiles need more than one round: every tile row walks the chunks twice

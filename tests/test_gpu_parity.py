@@ -186,10 +186,39 @@ def test_router_parity(orc, E, k, T):
     assert np.all(np.abs(host(w) - w_ref) <= 1e-6 * w_ref)
 
 
+@pytest.mark.parametrize("E,k", [(16, 8), (128, 8), (256, 32)])
+def test_router_nan_logits(orc, E, k):
+    """NaN logits rank below every number, lowest index first among NaNs
+    (the oracle's reading); ids exact, weights NaN exactly where the oracle's
+    are (a NaN pick makes the whole token's sum NaN)."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    T = 3
+    g = gs.rng(3500 + E + k)
+    lg = gs.logits(g, T, E)
+    lg[0, g.choice(E, size=E - k // 2, replace=False)] = np.nan   # NaNs get picked
+    lg[1, [0, 3, E - 1]] = np.nan                                  # NaNs never reached
+    lg[2, 0] = np.nan
+    lg[2, 1] = -np.inf
+    say("router nan", E, k, T)
+    lt, _ = dev(lg)
+    ids = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    qg.qg_router_topk(lt, E, k, T, ids, w)
+    ids_ref, w_ref = orc.router_topk(lg, E, k, T)
+    assert np.array_equal(host(ids), ids_ref)
+    wg = host(w)
+    assert np.array_equal(np.isnan(wg), np.isnan(w_ref))
+    fin = ~np.isnan(w_ref)
+    assert np.all(np.abs(wg[fin] - w_ref[fin]) <= 1e-6 * w_ref[fin])
+
+
 # --------------------------------------------------------------- dense MLP --
 @pytest.mark.parametrize("t,act,H,F,T", [(gs.Q8_0, 0, 256, 320, 1), (gs.Q4_0, 1, 320, 224, 3),
                                          (gs.Q4_K, 0, 512, 768, 2), (gs.Q6_K, 1, 768, 512, 16),
                                          (gs.Q4_0, 1, 2816, 2112, 16), (gs.Q4_0, 1, 2816, 2112, 1),
+                                         # gate / up rows of 32 tiles: split 4 ways in 16s
+                                         (gs.Q4_0, 1, 2048, 512, 16),
                                          # x too wide for LDS beside two workgroups' stages
                                          (gs.Q6_K, 0, 17408, 256, 1), (gs.Q8_0, 1, 24576, 96, 1)])
 def test_mlp_stagewise(orc, t, act, H, F, T):

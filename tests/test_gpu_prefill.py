@@ -29,10 +29,14 @@ def gpu_gemm(t, W, x, rows, cols, ntok, w_offset=0):
 @pytest.mark.parametrize("rows,nbk,ntok,off", [(300, 32, 17, 0), (129, 24, 64, 2), (257, 16, 100, 0),
                                                (70, 40, 256, 0), (33, 8, 40, 2),
                                                # 4..16 tokens (Q8_0 / Q4_0 rows split over
-                                               # workgroups): 7 splits of 32 with a short last
-                                               # one; 2 tiles: 16 splits of 16 with a short
-                                               # last one; a short row left whole
-                                               (300, 200, 8, 0), (33, 250, 16, 2), (129, 24, 5, 2)])
+                                               # workgroups).  Under a quarter of the CUs'
+                                               # worth of tiles: 10 tiles, 13 splits of 16
+                                               # with a short last one; 2 tiles, 16 splits of
+                                               # 16 with a short last one.  66 tiles: 7 splits
+                                               # of 32 with a short last one.  A short row
+                                               # left whole.
+                                               (300, 200, 8, 0), (33, 250, 16, 2), (2100, 200, 8, 2),
+                                               (129, 24, 5, 2)])
 def test_gemm_parity(orc, t, rows, nbk, ntok, off):
     if t in (gs.Q4_K, gs.Q6_K):
         nbk = max(1, nbk // 8)

@@ -315,6 +315,28 @@ def test_router_closed_form_two_experts(orc):
     assert abs(w[0, 0] - w0) < 1e-15 and abs(w[0, 1] - (1 - w0)) < 1e-15
 
 
+def test_router_nan_ranks_below_numbers(orc):
+    """Reading of the router on NaN logits (the pages only softmax finite
+    ones): a NaN ranks below every number, -inf included, and NaNs among
+    themselves go lowest index first.  Checked against numpy's stable argsort
+    of the key (NaN -> below -inf)."""
+    lg = np.array([[np.nan, 1.0, -np.inf, np.nan, 0.5, -3.0, np.nan, 0.5]], np.float32)
+    ids, w = orc.router_topk(lg, 8, 8, 1)
+    assert list(ids[0]) == [1, 4, 7, 5, 2, 0, 3, 6]
+    key = np.where(np.isnan(lg[0]), -np.inf, lg[0].astype(np.float64))
+    order = [i for i in np.argsort(-key, kind="stable") if not np.isnan(lg[0, i])]
+    order += [i for i in range(8) if np.isnan(lg[0, i])]
+    assert list(ids[0]) == order
+    # picks that hold no NaN keep the closed-form weights
+    ids3, w3 = orc.router_topk(lg, 8, 3, 1)
+    assert list(ids3[0]) == [1, 4, 7]
+    e = math.exp(-0.5)
+    assert np.allclose(w3[0], np.array([1, e, e]) / (1 + 2 * e), rtol=1e-15, atol=0)
+    # a NaN at index 0 is not kept on top
+    z = np.array([[np.nan, -1.0, 2.0]], np.float32)
+    assert list(orc.router_topk(z, 3, 2, 1)[0][0]) == [2, 1]
+
+
 # ------------------------------------------------------------------ MoE -----
 def _tiny_moe(t, seed, E=6, H=64, F=64, k=2, T=3):
     g = gs.rng(seed)
