@@ -13,6 +13,7 @@ QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
 QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL, QG_MAX_NORMS = 16, 256, 32, 4096, 4
+QG_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqgemv.so")
@@ -21,7 +22,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
            "qg_dequant", "qg_gemv_plan",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
-           "qg_moe_ffn", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
+           "qg_moe_ffn", "qg_moe_ffn_noalloc", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax", "qg_argmax_embed")
 
 _lib = None
@@ -71,6 +72,7 @@ def lib():
         L.qg_moe_workspace_size.argtypes = [ctypes.POINTER(qg_moe), i32, i32]
         L.qg_moe_workspace_size.restype = sz
         L.qg_moe_ffn.argtypes = [ctypes.POINTER(qg_moe), P, i32, P, P, P, i32, P, P, P, P, sz, P]
+        L.qg_moe_ffn_noalloc.argtypes = [ctypes.POINTER(qg_moe), P, i32, P, P, P, i32, P, P, P, P]
         f = ctypes.c_float
         L.qg_rmsnorm.argtypes = [P, P, P, i64, i32, f, f, P]
         L.qg_rmsnorm_multi.argtypes = [P, i64, i32, f, i32, ctypes.POINTER(P), ctypes.POINTER(f),
@@ -187,6 +189,12 @@ def qg_moe_ffn(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out,
     _check("qg_moe_ffn", lib().qg_moe_ffn(ctypes.byref(m), _ptr(router_logits), topk, _ptr(expert_slots),
                                           _ptr(x), _ptr(y), ntok, _ptr(ids_out), _ptr(w_out), _ptr(status),
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qg_moe_ffn_noalloc(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, stream=None):
+    _check("qg_moe_ffn_noalloc",
+           lib().qg_moe_ffn_noalloc(ctypes.byref(m), _ptr(router_logits), topk, _ptr(expert_slots), _ptr(x), _ptr(y),
+                                    ntok, _ptr(ids_out), _ptr(w_out), _ptr(status), _stream(stream)))
 
 
 def _nbytes(t, given):

@@ -958,6 +958,54 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free variant --
+// qg_moe_ffn_noalloc's scratch: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and kept below.
+static __device__ __align__(256) uint8_t scratch[QG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void *noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// the current device's copy of `scratch` (looked up on its first use)
+int noalloc_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return QG_EHIP;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QG_EHIP;
+        noalloc_ptr[dev] = p;
+    }
+    *out = noalloc_ptr[dev];
+    return QG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qg_moe_ffn_noalloc(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots,
+                       const float *x, float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status,
+                       void *stream) {
+    if (!m) return QG_EINVAL;
+    if (ntok < 1 || ntok > QG_MAX_TOKENS || topk < 1 || topk > QG_MAX_TOPK || m->n_experts > QG_MAX_EXPERTS)
+        return QG_ELIMIT;
+    const size_t need = qg_moe_workspace_size(m, topk, ntok);
+    if (!need) return QG_EINVAL;
+    if (need > QG_NOALLOC_SCRATCH_BYTES) return QG_ELIMIT;
+    void *ws = nullptr;
+    const int rc = noalloc_scratch(&ws);
+    if (rc) return rc;
+    return qg_moe_ffn(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, ws,
+                      QG_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 size_t qg_moe_shared_workspace_size(const qg_moe *m, const qg_shared_expert *sh, int topk, int ntok) {
     const size_t a = qg_moe_workspace_size(m, topk, ntok);
     if (!a || !sh || sh->ff <= 0) return 0;

@@ -220,6 +220,23 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk,
                int32_t *ids_out, float *w_out, int32_t *status,
                void *workspace, size_t workspace_bytes, void *stream);
 
+/* qg_moe_ffn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Its scratch is a static device array of
+ * QG_NOALLOC_SCRATCH_BYTES inside the library: one copy per GPU, created with
+ * the library's code object on that GPU and held until the process ends; the
+ * call itself allocates nothing.  The current device must be the stream's.
+ * Every call on a GPU uses that GPU's one copy, so calls that overlap on one
+ * GPU (on different streams, or from different host threads) race and must
+ * not be issued.  After a call the scratch holds what qg_moe_ffn's workspace
+ * would (gu, act, ...); the next call overwrites it.
+ * Arguments, results and errors as qg_moe_ffn, and QG_ELIMIT when
+ * qg_moe_workspace_size(m, topk, ntok) exceeds QG_NOALLOC_SCRATCH_BYTES. */
+#define QG_NOALLOC_SCRATCH_BYTES (8u << 20)
+int qg_moe_ffn_noalloc(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots,
+                       const float *x, float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status,
+                       void *stream);
+
 /* ------------------------------------------------ around the routed experts */
 
 /* RMS norm with a scalar factor, per token of n values:

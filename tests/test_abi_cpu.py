@@ -114,6 +114,23 @@ def test_moe_rejects_and_sizes():
     assert L.qg_moe_ffn(None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, FAKE, ws, None) == qg.QG_EINVAL
 
 
+def test_moe_noalloc_rejects():
+    """The allocation-free variant refuses, before any HIP call, shapes whose
+    workspace would not fit its static scratch, and the limits qg_moe_ffn
+    refuses."""
+    L = qg.lib()
+    call = lambda mm, k=8, T=1: L.qg_moe_ffn_noalloc(ctypes.byref(mm), FAKE, k, FAKE, FAKE, FAKE, T, None, None,
+                                                     FAKE, None)
+    assert qg.qg_moe_workspace_size(_moe(), 8, 16) <= qg.QG_NOALLOC_SCRATCH_BYTES
+    big = _moe(hidden=8192, ff=8192)
+    assert qg.qg_moe_workspace_size(big, 8, 16) > qg.QG_NOALLOC_SCRATCH_BYTES
+    assert call(big, T=16) == qg.QG_ELIMIT
+    assert call(_moe(), T=17) == qg.QG_ELIMIT
+    assert call(_moe(), k=33) == qg.QG_ELIMIT
+    assert call(_moe(n_experts=257)) == qg.QG_ELIMIT
+    assert L.qg_moe_ffn_noalloc(None, FAKE, 8, FAKE, FAKE, FAKE, 1, None, None, FAKE, None) == qg.QG_EINVAL
+
+
 def test_f32_block_and_gemv_rejects():
     L = qg.lib()
     assert qg.qg_block_values(qg.QG_F32) == 1 and qg.qg_block_bytes(qg.QG_F32) == 4
