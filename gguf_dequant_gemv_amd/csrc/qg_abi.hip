@@ -223,8 +223,8 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
 
 // Workgroups that stay resident at once (all CUs), from the kernel's actual
 // register and LDS use; cached per kernel and LDS size.
-int resident_wgs(gemv_fn f, size_t lds) {
-    struct Entry { gemv_fn f; size_t lds; int n; };
+int resident_wgs_of(const void *f, size_t lds) {
+    struct Entry { const void *f; size_t lds; int n; };
     static std::mutex mu;
     static Entry cache[512];
     static int used = 0;
@@ -232,12 +232,13 @@ int resident_wgs(gemv_fn f, size_t lds) {
     for (int i = 0; i < used; i++)
         if (cache[i].f == f && cache[i].lds == lds) return cache[i].n;
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 256, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 256, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const int n = per_cu * NUM_CU;
     if (used < 512) cache[used++] = {f, lds, n};
     return n;
 }
+int resident_wgs(gemv_fn f, size_t lds) { return resident_wgs_of((const void *)f, lds); }
 
 // Grid-stride width.  Workgroups that cannot be resident at once run in
 // later rounds, and fewer workgroups than resident slots leave memory
@@ -460,20 +461,33 @@ int launch_mfma(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_
     return split ? gemm_reduce(a, sp.n, st) : QG_OK;
 }
 
-int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
+// The plan's fields in the kernel arguments of a vector-kernel launch.
+int prep_gemv(const Shape &s, const Plan &p, GemvArgs &a) {
     a.row_bytes = s.row_bytes;
     // gated: gate rows in W0, the same rows of the up matrix in W1
     a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
     if (!a.glu) a.W1 = a.W0;
     if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
-    if (p.kind == UK_MFMA) return a.r_logits ? QG_EINVAL : launch_mfma(s, p, a, grid, st);
-    a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0;
+    a.x_vec = aligned(a.x, 16) && (a.x_stride % 4) == 0 && (!a.xg_x || aligned(a.xg_x, 16));
     a.cols = s.cols;
     a.nunits = p.nunits;
     a.ntiles = p.ntiles;
     a.depth = p.depth;
     a.ring_off = p.ring_off;
     a.xchunk = p.xchunk;
+    return QG_OK;
+}
+
+int launch_gemv(const Shape &s, const Plan &p, GemvArgs a, dim3 grid, hipStream_t st) {
+    if (p.kind == UK_MFMA) {
+        a.row_bytes = s.row_bytes;
+        a.bytes0 = a.bytes1 = a.rows * s.row_bytes;
+        if (!a.glu) a.W1 = a.W0;
+        if (a.bytes0 > MAX_RANGE || a.bytes1 > MAX_RANGE) return QG_ELIMIT;
+        return a.r_logits ? QG_EINVAL : launch_mfma(s, p, a, grid, st);
+    }
+    const int rc = prep_gemv(s, p, a);
+    if (rc) return rc;
     // a launch that routes its token needs the routing instance (one token,
     // LDS-staged, x whole); anything else would read a group table that no
     // routing launch wrote
@@ -713,7 +727,8 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
 
 // Workspace layout for qg_moe_ffn (each part 256-byte aligned, in order):
 //   gu [T*k][2F] f32 | act [T*k][F] f32 | dn [T*k][H] f32 | ids [T*k] i32 |
-//   w [T*k] f32 | valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32
+//   w [T*k] f32 | valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32 |
+//   set lists
 namespace {
 struct MoeWs {
     size_t gu, act, dn, ids, w, valid, grp, sets, total;
@@ -811,7 +826,8 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     const int busy1 = (pairs + gtok1 - 1) / gtok1;
     Plan p1 = make_plan(s_g, gtok1, busy1, aligned(m->gate_up, 16) && (m->gate_up_stride % 16) == 0, gtok1);
     Plan p2 = make_plan(s_dn, gtok, busy, aligned(m->down, 16) && (m->down_stride % 16) == 0, gtok);
-    // one token on the LDS-staged kernel: that launch routes the token itself
+    // one token on the LDS-staged kernel: the gated launch routes the token
+    // itself
     const bool route_in = ntok == 1 && topk <= ROUTE1_MAXK && lds_kind(p1.kind) && p1.nt == 1 && p1.xchunk == 0;
     // the (group, chunk) sets of each launch, listed by the routing launch:
     // workgroup y takes set y, so only the last few (past the count) are empty
@@ -867,10 +883,14 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     // routing launch (the aligned-copy variant needs its ranges aligned too)
     if (sh_done) *sh_done = false;
     if (route_in && shg && (p1.kind != UK_LDS || (aligned(shg->gate, 16) && aligned(shg->up, 16)))) {
-        a.sh_W0 = (const uint8_t *)shg->gate;
-        a.sh_W1 = (const uint8_t *)shg->up;
-        a.sh_y = shg->act;
-        a.sh_y2 = shg->gu;
+        a.xg_W0 = (const uint8_t *)shg->gate;
+        a.xg_W1 = (const uint8_t *)shg->up;
+        a.xg_step = 0;
+        a.xg_up = F;
+        a.xg_x = x;
+        a.xg_y = shg->act;
+        a.xg_y2 = shg->gu;
+        a.xg_n = 1;
         grid_a.y += 1;
         if (sh_done) *sh_done = true;
     }
@@ -907,6 +927,30 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
 struct SharedWs {
     size_t gu, act, sh, total;
 };
+// the one-token down launch's arguments for a pool, its workspace and output
+Moe1Args down1_args(const qg_moe *m, int topk, const int32_t *slots, void *workspace, float *y) {
+    const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, 1);
+    uint8_t *ws = (uint8_t *)workspace;
+    Moe1Args b = {};
+    b.W = (const uint8_t *)m->down;
+    b.stride = m->down_stride;
+    b.rows = m->hidden;
+    b.row_bytes = m->ff / 32 * qg_block_bytes(m->type);
+    b.nb = (int)(m->ff / 32);
+    b.act = (const float *)(ws + L.act);
+    b.act_stride = m->ff;
+    b.ids = (const int32_t *)(ws + L.ids);
+    b.w = (const float *)(ws + L.w);
+    b.slots = slots;
+    b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
+    b.escale = m->down_scale;
+    b.valid = (const int32_t *)(ws + L.valid);
+    b.dn = (float *)(ws + L.dn);
+    b.y = y;
+    b.k = topk;
+    return b;
+}
+
 SharedWs shared_ws(int type, int64_t H, int64_t SF, int ntok) {
     SharedWs o;
     o.gu = 0;
@@ -925,33 +969,13 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     hipStream_t st = (hipStream_t)stream;
     float *dn = nullptr;
     int32_t *valid = nullptr;
-    // one token: the down projection of every pick and the combine in one launch
+    // one token: the down projection of every pick and the combine in one
+    // launch
     const bool one = m && ntok == 1 && moe_down1_fits(m->type, m->ff, topk);
     int rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace,
                         workspace_bytes, 0, st, &dn, &valid, !one);
     if (rc) return rc;
-    if (one) {
-        const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok);
-        uint8_t *ws = (uint8_t *)workspace;
-        Moe1Args b = {};
-        b.W = (const uint8_t *)m->down;
-        b.stride = m->down_stride;
-        b.rows = m->hidden;
-        b.row_bytes = m->ff / 32 * qg_block_bytes(m->type);
-        b.nb = (int)(m->ff / 32);
-        b.act = (const float *)(ws + L.act);
-        b.act_stride = m->ff;
-        b.ids = (const int32_t *)(ws + L.ids);
-        b.w = (const float *)(ws + L.w);
-        b.slots = expert_slots;
-        b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
-        b.escale = m->down_scale;
-        b.valid = valid;
-        b.dn = dn;
-        b.y = y;
-        b.k = topk;
-        return launch_moe_down1(m->type, b, st);
-    }
+    if (one) return launch_moe_down1(m->type, down1_args(m, topk, expert_slots, workspace, y), st);
     // weighted combine in pick order
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((m->hidden + 255) / 256), ntok), dim3(256), 0, st, dn, valid, y,
                        m->hidden, topk);
@@ -1042,33 +1066,16 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
                         workspace_bytes, S.total, st, &dn, &valid, !one, one ? &shg : nullptr, &fused);
     if (rc) return rc;
     if (one) {
-        const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, ntok);
-        Moe1Args b = {};
-        b.W = (const uint8_t *)m->down;
-        b.stride = m->down_stride;
-        b.rows = m->hidden;
-        b.row_bytes = m->ff / 32 * qg_block_bytes(m->type);
-        b.nb = (int)(m->ff / 32);
-        b.act = (const float *)((uint8_t *)workspace + L.act);
-        b.act_stride = m->ff;
-        b.ids = (const int32_t *)((uint8_t *)workspace + L.ids);
-        b.w = (const float *)((uint8_t *)workspace + L.w);
-        b.slots = expert_slots;
-        b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
-        b.escale = m->down_scale;
-        b.valid = valid;
-        b.dn = dn;
-        b.k = topk;
-        if (fused) {
-            b.shW = (const uint8_t *)sh->down;
-            b.sh_act = (const float *)(ws + S.act);
-            b.gate_inp = sh->gate_inp;
-            b.x = x;
-            b.resid = resid;
-            b.sh_out = (float *)(ws + S.sh);
-            return launch_moe_down1(m->type, b, st);
-        }
-        rc = launch_moe_down1(m->type, b, st);   // the routed terms only (no y)
+        Moe1Args b = down1_args(m, topk, expert_slots, workspace, nullptr);
+        b.shW = (const uint8_t *)sh->down;
+        b.sh_act = (const float *)(ws + S.act);
+        b.gate_inp = sh->gate_inp;
+        b.x = x;
+        b.resid = resid;
+        b.sh_out = (float *)(ws + S.sh);
+        if (fused) return launch_moe_down1(m->type, b, st);
+        b.shW = nullptr;   // the routed terms only (no y); the shared expert below
+        rc = launch_moe_down1(m->type, b, st);
         if (rc) return rc;
     }
     // the shared expert: a dense gated MLP on the same input, into the workspace

@@ -52,6 +52,17 @@ QG_DEV u32 opaque(u32 v) {
     return v;
 }
 
+// A wave-uniform pointer, kept in scalar registers: a buffer descriptor built
+// from it then needs no per-lane loop (the compiler cannot always prove a
+// pointer chosen through several paths uniform).
+template <class T>
+QG_DEV T *uniform_ptr(T *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const u32 lo = (u32)__builtin_amdgcn_readfirstlane((int)(u32)v);
+    const u32 hi = (u32)__builtin_amdgcn_readfirstlane((int)(u32)(v >> 32));
+    return (T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ------------------------------------------------------- buffer loads -----
 // Raw buffer descriptor over [base, base + bytes): loads past the end read 0.
 QG_DEV rsrc_t make_rsrc(const void *base, u32 bytes) {

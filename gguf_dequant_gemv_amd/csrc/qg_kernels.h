@@ -77,11 +77,17 @@ struct GemvArgs {
     const int *sets;   // grouped: the set list of this launch's chunk size
                        // (blockIdx.y = set), or nullptr (blockIdx.y = group,
                        // blockIdx.z = chunk)
-    // a routing launch (RT) may carry a shared expert as group r_k: its gate
-    // rows from sh_W0, up rows from sh_W1 (same shape as a routed expert's),
-    // act(g) * u to sh_y and the raw g, u to sh_y2
-    const uint8_t *sh_W0, *sh_W1;
-    float *sh_y, *sh_y2;
+    // a routing launch (RT) may carry xg_n extra groups after its r_k routed
+    // ones (a shared expert, or the row slices of a dense MLP beside the
+    // experts): group r_k + i takes its gate rows from xg_W0 + i * xg_step and
+    // the same up rows from xg_W1 + i * xg_step (a routed expert's shape), its
+    // input from xg_x, and writes act(g) * u to xg_y + i * rows and the raw
+    // g, u to xg_y2 + i * rows and xg_y2 + xg_up + i * rows
+    const uint8_t *xg_W0, *xg_W1;
+    int64_t xg_step, xg_up;
+    const float *xg_x;
+    float *xg_y, *xg_y2;
+    int xg_n;
     int in_by_pair;    // grouped input index: 0 = token, 1 = pair
     // grouped outputs scaled as (y * escale[expert]) * pscale[pair] when set
     // (the MoE combine's per-expert down scale and routing weight)
@@ -123,98 +129,186 @@ struct GemvArgs {
 // ------------------------------------------- one token's routing in-launch --
 // Every wave selects the top k of the router logits itself (the keys, the
 // lowest index among equal keys and the weights of k_route), so no routing
-// launch precedes the gated expert launch.  Group g is the pick with the g-th
-// smallest expert id, the order k_route's group table lists them in.
-// Workgroup (0, 0, 0) writes what k_route writes for one token.  Returns false
-// when a pick has no pool slot (the token's groups are then empty).
+// launch precedes the expert launches.  Group g is the pick with the g-th
+// smallest expert id, the order k_route's group table lists them in.  The
+// lead workgroup writes what k_route writes for one token.
 constexpr int ROUTE1_MAXK = 8;
 
-QG_DEV bool route1_group(const GemvArgs &a, int g, int &e_out, int &slot_out, int &z_out) {
+struct Route1 {        // this lane's share of the router inputs (E <= 256)
+    float lv[4];       // logit of expert lane + 64 i (0 past E)
+    int sl[4];         // its pool slot (-1 past E)
+};
+
+// Issued as early as possible: nothing else in the launch depends on less.
+QG_DEV void route1_load(const GemvArgs &a, Route1 &r) {
     const int lane = threadIdx.x & 63;
-    const int E = a.r_E, k = a.r_k;
-    float lv[4];
-    u32 key[4];
-    u32 taken = 0u;   // bit i: value lane + 64 i is picked or absent
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int e = lane + 64 * i;
-        lv[i] = e < E ? a.r_logits[e] : 0.0f;
-        key[i] = order_key(lv[i]);
-        if (e >= E) taken |= 1u << i;
+        r.lv[i] = e < a.r_E ? a.r_logits[e] : 0.0f;
+        r.sl[i] = e < a.r_E ? a.r_slots[e] : -1;
     }
-    int ids[ROUTE1_MAXK];
+}
+
+// Value of lane `e & 63` of register set (e >> 6), e wave-uniform: each set
+// is read at that lane and the scalar results selected (a select over the
+// sets themselves would become a dynamically indexed register array, which
+// the compiler keeps in scratch memory).
+QG_DEV int pick_lane_i(const int (&v)[4], int e) {
+    const int ln = e & 63, hi = e >> 6;
+    const int r0 = __builtin_amdgcn_readlane(v[0], ln), r1 = __builtin_amdgcn_readlane(v[1], ln);
+    const int r2 = __builtin_amdgcn_readlane(v[2], ln), r3 = __builtin_amdgcn_readlane(v[3], ln);
+    return hi == 0 ? r0 : hi == 1 ? r1 : hi == 2 ? r2 : r3;
+}
+QG_DEV float pick_lane_f(const float (&v)[4], int e) {
+    const int (&vi)[4] = reinterpret_cast<const int (&)[4]>(v);
+    return __builtin_bit_cast(float, pick_lane_i(vi, e));
+}
+
+// The k picks in pick order, held across lanes: lane j < k gets pick j's
+// expert id and pool slot (other lanes keep 0).  One rolled round per pick
+// (the code runs once per wave, so its size, not its count of operations,
+// sets its time: every instruction line it spans is fetched from memory
+// while the weight streams fill the caches).  Returns false when a pick has
+// no pool slot.
+struct Picked {
+    int id, slot;   // this lane's pick (lane < k)
+    bool ok;        // every pick has a slot
+};
+QG_DEV Picked route1_pick(const GemvArgs &a, const Route1 &r) {
+    const int lane = threadIdx.x & 63;
+    const int E = a.r_E, k = a.r_k;
+    u32 key[4];
+    u32 taken = 0u;
 #pragma unroll
-    for (int j = 0; j < ROUTE1_MAXK; j++) {
-        ids[j] = 0;
-        if (j < k) {
-            u32 lm = 0u;
+    for (int i = 0; i < 4; i++) {
+        key[i] = order_key(r.lv[i]);
+        if (lane + 64 * i >= E) taken |= 1u << i;
+    }
+    Picked p = {0, 0, true};
+#pragma unroll 1
+    for (int j = 0; j < k; j++) {
+        u32 lm = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                if (!((taken >> i) & 1u)) lm = max(lm, key[i]);
-            const u32 M = wave_max_u32(lm);
-            int e = -1;
+        for (int i = 0; i < 4; i++)
+            if (!((taken >> i) & 1u)) lm = max(lm, key[i]);
+        const u32 M = wave_max_u32(lm);
+        int e = -1;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
-                if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
-            }
-            e = __builtin_amdgcn_readfirstlane(e);
-            if ((e & 63) == lane) taken |= 1u << (e >> 6);
-            ids[j] = e;
+        for (int i = 0; i < 4; i++) {
+            const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
+            if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if ((e & 63) == lane) taken |= 1u << (e >> 6);
+        const int sl = pick_lane_i(r.sl, e);
+        if (lane == j) { p.id = e; p.slot = sl; }
+        p.ok = p.ok && sl >= 0 && sl < a.r_nslots;
+    }
+    return p;
+}
+
+// Pick j's expert id and slot (j wave-uniform)
+QG_DEV int pick_id(const Picked &p, int j) { return __builtin_amdgcn_readlane(p.id, j); }
+QG_DEV int pick_slot(const Picked &p, int j) { return __builtin_amdgcn_readlane(p.slot, j); }
+
+// Value of expert `e` (per lane) from a per-expert vector held as register
+// sets v[i] = entry lane + 64 i: every set read at lane e & 63, then set
+// e >> 6 selected
+QG_DEV float expert_value(const float (&v)[4], int e) {
+    const int src = (e & 63) << 2, hi = e >> 6;
+    const int c0 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v[0]));
+    const int c1 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v[1]));
+    const int c2 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v[2]));
+    const int c3 = __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v[3]));
+    return __builtin_bit_cast(float, hi == 0 ? c0 : hi == 1 ? c1 : hi == 2 ? c2 : c3);
+}
+
+// Lane j < k gets w_j = exp(l_j - l_0) / sum over the picks (the same
+// operations in every wave, so every wave holds the same bits).
+QG_DEV float route1_weight(const Route1 &r, const Picked &p, int k) {
+    const int lane = threadIdx.x & 63;
+    const float l0 = pick_lane_f(r.lv, pick_id(p, 0));
+    const float lj = expert_value(r.lv, p.id);
+    const float ex = lane < k ? expf(lj - l0) : 0.0f;
+    return ex / wave_sum(ex);
+}
+
+// Lane j < k gets the rank of pick j among the picks' expert ids (distinct)
+QG_DEV int route1_rank(const Picked &p, int k) {
+    int rank = 0;
+#pragma unroll 1
+    for (int i = 0; i < k; i++) rank += pick_id(p, i) < p.id ? 1 : 0;
+    return rank;
+}
+
+// The routing outputs of one token (ids, weights, validity, status, the
+// group table), written by the lead workgroup's first wave.
+QG_DEV void route1_write(const GemvArgs &a, const Route1 &r, const Picked &p, int rank) {
+    const int lane = threadIdx.x & 63;
+    const int k = a.r_k;
+    const float wj = route1_weight(r, p, k);
+    if (lane < k) {
+        a.r_ids[lane] = p.id;
+        a.r_w[lane] = wj;
+        if (a.r_ids_out) a.r_ids_out[lane] = p.id;
+        if (a.r_w_out) a.r_w_out[lane] = wj;
+        if (p.ok) {
+            int *rec = a.r_grp + 1 + rank * GREC;
+            rec[0] = p.id;
+            rec[1] = p.slot;
+            rec[2] = 1;
+            rec[3] = 0;
+            rec[19] = lane;
         }
     }
-    int slot[ROUTE1_MAXK];
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < ROUTE1_MAXK; j++) {
-        slot[j] = j < k ? a.r_slots[ids[j]] : 0;
-        if (j < k) ok = ok && slot[j] >= 0 && slot[j] < a.r_nslots;
+    if (lane == 0) {
+        a.r_valid[0] = p.ok ? 1 : 0;
+        if (a.r_status) a.r_status[0] = p.ok ? 0 : -2;   // QG_OK / QG_EABSENT
+        a.r_grp[0] = p.ok ? k : 0;
     }
-    // rank of each pick among the picks' expert ids (they are distinct)
-    int rank[ROUTE1_MAXK];
-    e_out = slot_out = z_out = 0;
-#pragma unroll
-    for (int j = 0; j < ROUTE1_MAXK; j++) {
-        rank[j] = 0;
-#pragma unroll
-        for (int i = 0; i < ROUTE1_MAXK; i++) rank[j] += (i < k && ids[i] < ids[j]) ? 1 : 0;
-        if (j < k && rank[j] == g) {
-            e_out = ids[j];
-            slot_out = slot[j];
-            z_out = j;
+}
+
+// Group g of a routing launch: its expert, slot and pick index.  Returns
+// false when a pick has no pool slot (the token's groups are then empty).
+QG_DEV bool route1_group(const GemvArgs &a, const Route1 &r, int g, bool lead, int &e_out, int &slot_out,
+                         int &z_out) {
+    const Picked p = route1_pick(a, r);
+    const int lane = threadIdx.x & 63;
+    const int rank = route1_rank(p, a.r_k);
+    // the lane holding the pick of rank g
+    const unsigned long long b = __ballot(lane < a.r_k && rank == g);
+    const int z = b ? (int)__builtin_ctzll(b) : 0;
+    z_out = z;
+    e_out = pick_id(p, z);
+    slot_out = pick_slot(p, z);
+    if (lead && threadIdx.x < 64) route1_write(a, r, p, rank);
+    return p.ok;
+}
+
+// The same for a whole workgroup: its first wave loads the router inputs and
+// selects, the others take the result from LDS (selection is serial work,
+// and every wave of a launch doing it at once would fill the vector units
+// for microseconds).  Call from every thread, before any early return.
+QG_DEV bool route1_group_wg(const GemvArgs &a, int g, bool lead, int &e_out, int &slot_out, int &z_out) {
+    __shared__ int s_r[4];
+    if (threadIdx.x < 64) {
+        Route1 r;
+        route1_load(a, r);
+        int e, sl, z;
+        const bool ok = route1_group(a, r, g, lead, e, sl, z);
+        if (threadIdx.x == 0) {
+            s_r[0] = e;
+            s_r[1] = sl;
+            s_r[2] = z;
+            s_r[3] = ok ? 1 : 0;
         }
     }
-    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 64) {
-        int idl = 0, sll = 0, rkl = 0;   // this lane's pick (lane < k)
-#pragma unroll
-        for (int j = 0; j < ROUTE1_MAXK; j++)
-            if (lane == j) { idl = ids[j]; sll = slot[j]; rkl = rank[j]; }
-        // weights over the picks, relative to the top pick
-        const float l0 = a.r_logits[ids[0]];
-        const float ex = lane < k ? expf(a.r_logits[idl] - l0) : 0.0f;
-        const float sum = wave_sum(ex);
-        if (lane < k) {
-            const float wj = ex / sum;
-            a.r_ids[lane] = idl;
-            a.r_w[lane] = wj;
-            if (a.r_ids_out) a.r_ids_out[lane] = idl;
-            if (a.r_w_out) a.r_w_out[lane] = wj;
-            if (ok) {
-                int *rec = a.r_grp + 1 + rkl * GREC;
-                rec[0] = idl;
-                rec[1] = sll;
-                rec[2] = 1;
-                rec[3] = 0;
-                rec[19] = lane;
-            }
-        }
-        if (lane == 0) {
-            a.r_valid[0] = ok ? 1 : 0;
-            if (a.r_status) a.r_status[0] = ok ? 0 : -2;   // QG_OK / QG_EABSENT
-            a.r_grp[0] = ok ? k : 0;
-        }
-    }
-    return ok;
+    __syncthreads();
+    e_out = __builtin_amdgcn_readfirstlane(s_r[0]);
+    slot_out = __builtin_amdgcn_readfirstlane(s_r[1]);
+    z_out = __builtin_amdgcn_readfirstlane(s_r[2]);
+    return __builtin_amdgcn_readfirstlane(s_r[3]) != 0;
 }
 
 // -------------------------------------------------------- unit dot product --
@@ -358,10 +452,10 @@ QG_DEV void x_put(const f32x4 (&v)[XB], int base0, int n4, int c4, float *xt, fl
 // Scalar path (unaligned x): element by element, then the sums from LDS.
 // Columns [c0, c0 + cpad) of x land at xs[xpad(0..cpad)], zero past cols.
 template <int NT, int SUMS>
-QG_DEV void stage_x_scalar(const GemvArgs &a, const int (&in_idx)[NT], int cols, int cpad, float *xs, int xstride,
-                           float *ss, int nsum, int c0 = 0) {
+QG_DEV void stage_x_scalar(const float *x, int64_t x_stride, const int (&in_idx)[NT], int cols, int cpad, float *xs,
+                           int xstride, float *ss, int nsum, int c0 = 0) {
     for (int t = 0; t < NT; t++) {
-        const float *src = a.x + (int64_t)in_idx[t] * a.x_stride;
+        const float *src = x + (int64_t)in_idx[t] * x_stride;
         for (int c = threadIdx.x; c < cpad; c += 256)
             xs[t * xstride + xpad(c)] = c0 + c < cols ? src[c0 + c] : 0.0f;
     }
@@ -517,7 +611,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
             }
         }
     } else {
-        stage_x_scalar<NT, SUMS>(a, in_idx, cols, cpad, xs, xstride, ss, nsum);
+        stage_x_scalar<NT, SUMS>(a.x, a.x_stride, in_idx, cols, cpad, xs, xstride, ss, nsum);
     }
     __syncthreads();
 
@@ -677,8 +771,12 @@ QG_DEV void load_x16(u32 a, f32x4 (&x)[Q]) {
 // XC: x staged in chunks (restaged inside the element loop).  Kept apart from
 // the whole-x variant: global loads inside the loop make the compiler wait for
 // every load in flight, the stage copies included, at the unit reads.
+// The body runs for workgroup (bx, by, bz) of a grid gdx wide along the
+// rows, so a launch that also holds other work can run it under virtual
+// coordinates; `lead` marks the workgroup that writes a routing launch's
+// outputs (RT).
 template <class U, int L, int NT, bool ALN, bool XC, bool RT>
-__global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
+QG_DEV void gemv_lds_body(const GemvArgs &a, int bx, int by, int bz, int gdx, bool lead) {
     static_assert(!RT || (NT == 1 && !XC), "a launch that routes its token serves one token, x unchunked");
     extern __shared__ float lds[];
     constexpr int RPW = 64 / L;
@@ -696,22 +794,27 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     int in_idx[NT], out_idx[NT];
     float osc_e[NT], osc_p[NT];   // output scales (1 unless a grouped launch sets them)
     float *yo = a.y, *y2o = a.y2;  // where the rows go
+    int64_t y2_up = a.rows;        // the raw up sums' offset after the gate sums
+    const float *xsrc = a.x;       // the input vectors
     bool routed = false;
     if constexpr (RT) {
-        if (a.sh_W0 && (int)blockIdx.y == a.r_k) {   // the shared expert's gate and up rows
-            if (blockIdx.z > 0) return;
+        if (a.xg_n > 0 && by >= a.r_k) {   // an extra group: a shared expert, or a dense MLP's row slice
+            const int i = by - a.r_k;
+            if (i >= a.xg_n || bz > 0) return;
             nt = 1;
-            Wg0 = a.sh_W0;
-            Wg1 = a.sh_W1;
+            Wg0 = a.xg_W0 + (int64_t)i * a.xg_step;
+            Wg1 = a.xg_W1 + (int64_t)i * a.xg_step;
             in_idx[0] = out_idx[0] = 0;
             osc_e[0] = osc_p[0] = 1.0f;
-            yo = a.sh_y;
-            y2o = a.sh_y2;
+            xsrc = a.xg_x;
+            yo = a.xg_y + (int64_t)i * a.rows;
+            y2o = a.xg_y2 ? a.xg_y2 + (int64_t)i * a.rows : nullptr;
+            y2_up = a.xg_up;
             routed = true;
         } else {   // this launch routes its one token itself
             int e, sl, z;
-            const bool ok = route1_group(a, blockIdx.y, e, sl, z);
-            if (!ok || (int)blockIdx.y >= a.r_k || blockIdx.z > 0) return;
+            const bool ok = route1_group_wg(a, by, lead, e, sl, z);
+            if (!ok || by >= a.r_k || bz > 0) return;
             nt = 1;
             Wg0 = a.W0 + (int64_t)sl * a.slot_stride;
             Wg1 = a.glu ? Wg0 + a.rows * a.row_bytes : Wg0;   // up rows follow the gate rows
@@ -724,10 +827,10 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     }
     if (routed) {
     } else if (a.grp) {
-        int g = blockIdx.y, c0 = blockIdx.z * NT;
+        int g = by, c0 = bz * NT;
         if (a.sets) {
-            if ((int)blockIdx.y >= a.sets[0]) return;
-            const int e = a.sets[1 + blockIdx.y];
+            if (by >= a.sets[0]) return;
+            const int e = a.sets[1 + by];
             g = e >> 16;
             c0 = e & 0xffff;
         } else if (g >= a.grp[0]) {
@@ -749,7 +852,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
             osc_p[t] = a.pscale ? a.pscale[out_idx[t]] : 1.0f;
         }
     } else {
-        const int c0 = blockIdx.y * NT;
+        const int c0 = by * NT;
         nt = min(NT, a.ntok - c0);
 #pragma unroll
         for (int t = 0; t < NT; t++) {
@@ -763,6 +866,8 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     // the 16-byte piece holding its last byte (that piece lies in the same
     // page as the byte, so reading it is safe; the bytes past the end are
     // never decoded).
+    Wg0 = uniform_ptr(Wg0);
+    Wg1 = uniform_ptr(Wg1);
     const u32 ph0 = ALN ? 0u : (u32)((uintptr_t)Wg0 & 15u), ph1 = ALN ? 0u : (u32)((uintptr_t)Wg1 & 15u);
     const rsrc_t rs0 = make_rsrc(Wg0 - ph0, (u32)((ph0 + a.bytes0 + 15) & ~(int64_t)15));
     const rsrc_t rs1 = make_rsrc(Wg1 - ph1, (u32)((ph1 + a.bytes1 + 15) & ~(int64_t)15));
@@ -771,7 +876,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     const int grp = lane / L, sub = lane % L;
     const int K = (a.nunits + L - 1) / L;
     const int KT = a.glu ? 2 * K : K;
-    const int P = ((int)a.ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int P = ((int)a.ntiles - bx + gdx - 1) / gdx;
     const int S = P * KT;
     const int D = a.depth;
     const int64_t rows = a.rows;
@@ -789,7 +894,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     }
     // copy element (p, j)'s segments into stage `slot`
     auto issue = [&](int p, int j, int slot) {
-        const int64_t tile = (int64_t)blockIdx.x + (int64_t)p * gridDim.x;
+        const int64_t tile = (int64_t)bx + (int64_t)p * gdx;
         const int64_t r0 = (tile * 4 + wave) * RPW;
         // gated: [K, 2K) are the up rows (uniform; saying so keeps the
         // descriptor choice in scalar registers)
@@ -831,18 +936,18 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         if (a.x_vec) {
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                const float *src = a.x + (int64_t)in_idx[t] * a.x_stride + c0;
+                const float *src = xsrc + (int64_t)in_idx[t] * a.x_stride + c0;
                 for (int base0 = 0; base0 < n4; base0 += 256 * XB) {
                     if (!first_loaded || t != 0 || base0 != 0) x_load(src, base0, c4, xv);
                     x_put<SUMS>(xv, base0, n4, c4, xs + t * xstride, ss + t * nsum);
                 }
             }
         } else {
-            stage_x_scalar<NT, SUMS>(a, in_idx, cols, cw, xs, xstride, ss, nsum, c0);
+            stage_x_scalar<NT, SUMS>(xsrc, a.x_stride, in_idx, cols, cw, xs, xstride, ss, nsum, c0);
         }
     };
     // the first batch of x goes out before the weights
-    if (a.x_vec) x_load(a.x + (int64_t)in_idx[0] * a.x_stride, 0, min(cols, chunk_w(0)) >> 2, xv);
+    if (a.x_vec) x_load(xsrc + (int64_t)in_idx[0] * a.x_stride, 0, min(cols, chunk_w(0)) >> 2, xv);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- the first `depth` stages ----
@@ -879,7 +984,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
         u32 wd[U::ND];
         u32 uoff = (u32)lane * U::BYTES;   // where this lane's unit sits in the stage
         if constexpr (!ALN) {
-            const int64_t tl = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
+            const int64_t tl = (int64_t)bx + (int64_t)cp * gdx;
             const int64_t rw0 = (tl * 4 + wave) * RPW;
             const bool hi = a.glu && cj >= K;
             const int64_t rr = min(rw0 + grp, rows - 1);
@@ -930,7 +1035,7 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
             if (++ij == KT) { ij = 0; ++ip; }
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int64_t tile = (int64_t)blockIdx.x + (int64_t)cp * gridDim.x;
+        const int64_t tile = (int64_t)bx + (int64_t)cp * gdx;
         const int64_t r0 = (tile * 4 + wave) * RPW;
         if constexpr (XPF) {
             if (u < a.nunits) unit_dot_x<U>(wd, xr, sv, acc[0]);
@@ -958,10 +1063,11 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
                 for (int t = 0; t < NT; t++) {
                     if (t < nt) {
                         if (a.glu) {
-                            yo[(int64_t)out_idx[t] * a.y_stride + r] = glu(a.glu, gate[t], acc[t]);
+                            float *py = yo + (int64_t)out_idx[t] * a.y_stride + r;
+                            *py = glu(a.glu, gate[t], acc[t]);
                             if (y2o) {
                                 y2o[(int64_t)out_idx[t] * a.y2_stride + r] = gate[t];
-                                y2o[(int64_t)out_idx[t] * a.y2_stride + rows + r] = acc[t];
+                                y2o[(int64_t)out_idx[t] * a.y2_stride + y2_up + r] = acc[t];
                             }
                         } else {
                             yo[(int64_t)out_idx[t] * a.y_stride + r] = (acc[t] * osc_e[t]) * osc_p[t];
@@ -975,6 +1081,12 @@ __global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
     }
     // no buffer-to-LDS load may still be in flight when the wave ends
     QG_WAIT_VM(0);
+}
+
+template <class U, int L, int NT, bool ALN, bool XC, bool RT>
+__global__ __launch_bounds__(256) void k_gemv_lds(GemvArgs a) {
+    gemv_lds_body<U, L, NT, ALN, XC, RT>(a, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z, (int)gridDim.x,
+                                         blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0);
 }
 
 // ------------------------------------------- small batch on the MFMA units ---
