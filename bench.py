@@ -266,6 +266,10 @@ class MoeLayers(Workload):
             self.ym = torch.empty((ntok, H), dtype=torch.float32, device="cuda")
             self.wsm = torch.empty(qg.qg_mlp_workspace_size(t, H, dense_ff, ntok) // 4, dtype=torch.float32,
                                    device="cuda")
+            for L in self.layers:
+                L["d"] = qg.make_dense_mlp(t, dense_ff, L["Wg"], L["Wu"], L["Wd"])
+            self.wsd = torch.empty(qg.qg_moe_dense_workspace_size(self.layers[0]["m"], self.layers[0]["d"], k, ntok)
+                                   // 4, dtype=torch.float32, device="cuda")
         self.bytes_per_step = int(sum(uniq) / len(uniq) * rec) + self.dense_bytes
         self.dominant_bytes = self.bytes_per_step
         self.name = label
@@ -279,6 +283,10 @@ class MoeLayers(Workload):
                                          self.w, self.status, self.ws)
         if not self.dense_ff:
             moe()
+            return
+        if self.ntok == 1:   # one token: the MLP's rows ride in the experts' two launches
+            self.qg.qg_moe_ffn_dense(L["m"], L["d"], L["lg"], self.k, self.slots, L["x"], self.y, L["x"], self.ym,
+                                     1, self.ids, self.w, self.status, self.wsd)
             return
         dense = lambda st: self.qg.qg_mlp(self.t, self.act, L["Wg"], L["Wu"], L["Wd"], self.H, self.dense_ff,
                                           L["x"], self.ym, self.ntok, self.wsm, stream=st)
@@ -369,7 +377,8 @@ class GemmaBlock(Workload):
     RMS norms of the residual stream and the f32 router on one of them (one
     launch at one token: qg_rmsnorm_router; else qg_rmsnorm_multi and qg_gemv
     QG_F32), the dense GELU MLP, the routed experts, and the FFN tail into
-    the residual (qg_mlp, qg_moe_ffn, qg_post_ffn)."""
+    the residual (one token: qg_moe_ffn_dense, both in two launches; else
+    qg_mlp beside qg_moe_ffn on two streams; then qg_post_ffn)."""
 
     def __init__(self, ntok, layers=16, H=2816, Fd=2112, E=128, F=704, k=8):
         import torch
@@ -393,6 +402,7 @@ class GemmaBlock(Workload):
                      os=torch.rand(1, generator=g, device="cuda") * 0.5 + 0.5, x0=gs.device_activations(ntok, H, g))
             L["x"] = L["x0"].clone()
             L["m"] = qg.make_moe(t, qg.QG_ACT_GELU_TANH, H, F, E, gu, 2 * F * rb_h, dn, H * rb_f, ds)
+            L["d"] = qg.make_dense_mlp(t, Fd, L["Wg"], L["Wu"], L["Wd"])
             self.layers.append(L)
         f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")
         self.xn, self.xm, self.rt, self.md, self.moe = (f32(ntok, H) for _ in range(5))
@@ -403,6 +413,7 @@ class GemmaBlock(Workload):
         self.slots = torch.arange(E, dtype=torch.int32, device="cuda")
         self.wsm = f32(qg.qg_mlp_workspace_size(t, H, Fd, ntok) // 4)
         self.ws = f32(qg.qg_moe_workspace_size(self.layers[0]["m"], k, ntok) // 4)
+        self.wsd = f32(qg.qg_moe_dense_workspace_size(self.layers[0]["m"], self.layers[0]["d"], k, ntok) // 4)
         self.kr = 1.0 / H ** 0.5
         uniq = []
         for L in self.layers:
@@ -442,7 +453,11 @@ class GemmaBlock(Workload):
             qg.qg_moe_ffn(L["m"], self.lg, self.k, self.slots, self.xm, self.moe, T, self.ids, self.w, self.status,
                           self.ws)
 
-        self.branches.run(dense, experts)
+        if T == 1:   # the dense MLP's rows ride in the experts' two launches
+            qg.qg_moe_ffn_dense(L["m"], L["d"], self.lg, self.k, self.slots, self.xm, self.moe, self.xn, self.md, T,
+                                self.ids, self.w, self.status, self.wsd)
+        else:
+            self.branches.run(dense, experts)
         qg.qg_post_ffn(self.md, self.moe, L["w1"], L["w2"], L["w"], L["os"], L["x"], H, T, 1e-6)
 
     def step(self, i):

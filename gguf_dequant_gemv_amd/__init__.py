@@ -23,6 +23,7 @@ EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_ge
            "qg_dequant", "qg_gemv_plan",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_moe_ffn_noalloc", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
+           "qg_moe_dense_workspace_size", "qg_moe_ffn_dense",
            "qg_post_ffn", "qg_embed", "qg_argmax_workspace_size", "qg_argmax", "qg_argmax_embed")
 
 _lib = None
@@ -45,6 +46,11 @@ class qg_moe(ctypes.Structure):
 class qg_shared_expert(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int), ("ff", ctypes.c_int64), ("gate", ctypes.c_void_p),
                 ("up", ctypes.c_void_p), ("down", ctypes.c_void_p), ("gate_inp", ctypes.c_void_p)]
+
+
+class qg_dense_mlp(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int), ("ff", ctypes.c_int64), ("gate", ctypes.c_void_p),
+                ("up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
 
 
 def lib():
@@ -84,6 +90,10 @@ def lib():
         L.qg_moe_shared_workspace_size.restype = sz
         L.qg_moe_ffn_shared.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_shared_expert), P, i32, P, P,
                                         P, i32, P, P, P, P, sz, P]
+        L.qg_moe_dense_workspace_size.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_dense_mlp), i32, i32]
+        L.qg_moe_dense_workspace_size.restype = sz
+        L.qg_moe_ffn_dense.argtypes = [ctypes.POINTER(qg_moe), ctypes.POINTER(qg_dense_mlp), P, i32, P, P, P, P, P,
+                                       i32, P, P, P, P, sz, P]
         L.qg_post_ffn.argtypes = [P, P, P, P, P, P, P, i64, i32, f, P]
         L.qg_embed.argtypes = [i32, P, i64, i64, P, i32, f, P, P]
         L.qg_argmax_workspace_size.argtypes = [i64, i32]
@@ -245,6 +255,23 @@ def qg_moe_ffn_shared(m, sh, router_logits, topk, expert_slots, x, resid, ntok, 
            lib().qg_moe_ffn_shared(ctypes.byref(m), ctypes.byref(sh), _ptr(router_logits), topk, _ptr(expert_slots),
                                    _ptr(x), _ptr(resid), ntok, _ptr(ids_out), _ptr(w_out), _ptr(status),
                                    _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)))
+
+
+def make_dense_mlp(type, ff, gate, up, down):
+    return qg_dense_mlp(type, ff, _ptr(gate), _ptr(up), _ptr(down))
+
+
+def qg_moe_dense_workspace_size(m, d, topk, ntok):
+    return lib().qg_moe_dense_workspace_size(ctypes.byref(m), ctypes.byref(d), topk, ntok)
+
+
+def qg_moe_ffn_dense(m, d, router_logits, topk, expert_slots, x, y, x_mlp, y_mlp, ntok, ids_out, w_out, status,
+                     workspace, workspace_bytes=None, stream=None):
+    _check("qg_moe_ffn_dense",
+           lib().qg_moe_ffn_dense(ctypes.byref(m), ctypes.byref(d), _ptr(router_logits), topk, _ptr(expert_slots),
+                                  _ptr(x), _ptr(y), _ptr(x_mlp), _ptr(y_mlp), ntok, _ptr(ids_out), _ptr(w_out),
+                                  _ptr(status), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                  _stream(stream)))
 
 
 def qg_post_ffn(mlp, moe, w1, w2, w, out_scale, x, n, ntok, eps, stream=None):

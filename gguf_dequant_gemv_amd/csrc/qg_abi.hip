@@ -673,8 +673,12 @@ size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok) {
            mlp_scratch_bytes(type, hidden, ff, ntok);
 }
 
-int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
-           const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+// qg_mlp's argument checks (nothing enqueued)
+int mlp_check(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden,
+              int64_t ff, const float *x, const float *y, int ntok, const void *workspace, size_t workspace_bytes) {
     Shape s_g, s_dn;
     int rc = make_shape(type, ff, hidden, s_g);
     if (rc) return rc;
@@ -687,6 +691,19 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
         !aligned(workspace, 256))
         return QG_EINVAL;
     if (workspace_bytes < qg_mlp_workspace_size(type, hidden, ff, ntok)) return QG_EINVAL;
+    return QG_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
+           const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = mlp_check(type, act, W_gate, W_up, W_down, hidden, ff, x, y, ntok, workspace, workspace_bytes);
+    if (rc) return rc;
+    Shape s_g, s_dn;
+    make_shape(type, ff, hidden, s_g);
+    make_shape(type, hidden, ff, s_dn);
     hipStream_t st = (hipStream_t)stream;
     float *gu = (float *)workspace;
     float *av = (float *)((uint8_t *)workspace + align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)));
@@ -763,16 +780,24 @@ namespace {
 // Validation, routing, and the two grouped expert launches of a MoE step.  On
 // success dn holds the weighted terms (dn_j s_j) c_j as [ntok][topk][H] and
 // valid the per-token validity, both inside the workspace.
-// a shared expert's gate / up matrices and where its act / gu rows go
-struct SharedGroup {
+// Row groups that ride after the routed ones in a one-token gated launch,
+// each of a routed expert's shape (F gate rows and the same up rows): a
+// shared expert (one group), or the F-row slices of a dense MLP's gate / up
+// matrices (n groups, slice i at byte i * step).  Their input x, their
+// act(g) * u rows into act (slice i at act + i F) and raw sums into gu
+// (gate slice i at gu + i F, up slice i at gu + up_off + i F).
+struct ExtraGroups {
     const void *gate, *up;
+    int64_t step, up_off;
+    int n;
+    const float *x;
     float *act, *gu;
 };
 
 int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
                const float *y, int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
                size_t workspace_bytes, size_t ws_extra, hipStream_t st, float **dn_out, int32_t **valid_out,
-               bool down = true, const SharedGroup *shg = nullptr, bool *sh_done = nullptr) {
+               bool down = true, const ExtraGroups *xg = nullptr, bool *xg_done = nullptr) {
     if (!m) return QG_EINVAL;
     const int E = m->n_experts;
     if (E < 1 || E > QG_MAX_EXPERTS || topk < 1 || topk > QG_MAX_TOPK || topk > E || ntok < 1 ||
@@ -879,20 +904,22 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     a.sets = sets_a;
     a.in_by_pair = 0;
     dim3 grid_a = set_grid(ca, sets_a);
-    // a shared expert of the same shape rides along as group k of the
-    // routing launch (the aligned-copy variant needs its ranges aligned too)
-    if (sh_done) *sh_done = false;
-    if (route_in && shg && (p1.kind != UK_LDS || (aligned(shg->gate, 16) && aligned(shg->up, 16)))) {
-        a.xg_W0 = (const uint8_t *)shg->gate;
-        a.xg_W1 = (const uint8_t *)shg->up;
-        a.xg_step = 0;
-        a.xg_up = F;
-        a.xg_x = x;
-        a.xg_y = shg->act;
-        a.xg_y2 = shg->gu;
-        a.xg_n = 1;
-        grid_a.y += 1;
-        if (sh_done) *sh_done = true;
+    // extra groups of the routed experts' shape ride along as groups k, k+1,
+    // ... of the routing launch (the aligned-copy variant needs their ranges
+    // aligned too)
+    if (xg_done) *xg_done = false;
+    if (route_in && xg && xg->n >= 1 &&
+        (p1.kind != UK_LDS || (aligned(xg->gate, 16) && aligned(xg->up, 16) && xg->step % 16 == 0))) {
+        a.xg_W0 = (const uint8_t *)xg->gate;
+        a.xg_W1 = (const uint8_t *)xg->up;
+        a.xg_step = xg->step;
+        a.xg_up = xg->up_off;
+        a.xg_x = xg->x;
+        a.xg_y = xg->act;
+        a.xg_y2 = xg->gu;
+        a.xg_n = xg->n;
+        grid_a.y += xg->n;
+        if (xg_done) *xg_done = true;
     }
     rc = launch_gemv(s_g, p1, a, grid_a, st);
     if (rc) return rc;
@@ -1060,7 +1087,7 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     // and up rows ride in the routing launch, its down row and the whole
     // combine in the one-token down launch (two launches in all).
     const bool one = ntok == 1 && sh->type == m->type && sh->ff == m->ff && moe_down1_fits(m->type, m->ff, topk);
-    const SharedGroup shg = {sh->gate, sh->up, (float *)(ws + S.act), (float *)(ws + S.gu)};
+    const ExtraGroups shg = {sh->gate, sh->up, 0, m->ff, 1, x, (float *)(ws + S.act), (float *)(ws + S.gu)};
     bool fused = false;
     int rc = moe_routed(m, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status, workspace,
                         workspace_bytes, S.total, st, &dn, &valid, !one, one ? &shg : nullptr, &fused);
@@ -1085,6 +1112,67 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     // routed terms + gated shared output + residual
     return launch_combine_shared(dn, valid, (const float *)(ws + S.sh), sh->gate_inp, x, resid, m->hidden, topk,
                                  ntok, st);
+}
+
+size_t qg_moe_dense_workspace_size(const qg_moe *m, const qg_dense_mlp *d, int topk, int ntok) {
+    const size_t a = qg_moe_workspace_size(m, topk, ntok);
+    if (!a || !d || d->ff <= 0) return 0;
+    const size_t b = qg_mlp_workspace_size(d->type, m->hidden, d->ff, ntok);
+    return b ? a + b : 0;
+}
+
+int qg_moe_ffn_dense(const qg_moe *m, const qg_dense_mlp *d, const float *router_logits, int topk,
+                     const int32_t *expert_slots, const float *x, float *y, const float *x_mlp, float *y_mlp,
+                     int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    if (!m || !d) return QG_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t base = qg_moe_workspace_size(m, topk, ntok);
+    if (!base) return ntok < 1 || ntok > QG_MAX_TOKENS || topk < 1 || topk > QG_MAX_TOPK ||
+                          m->n_experts > QG_MAX_EXPERTS ? QG_ELIMIT : QG_EINVAL;
+    if (!workspace || workspace_bytes < base) return QG_EINVAL;
+    uint8_t *wsd = (uint8_t *)workspace + base;   // the MLP's part: qg_mlp's layout
+    const size_t wsd_bytes = workspace_bytes - base;
+    // the dense MLP's arguments, checked before anything is enqueued
+    int rc = mlp_check(d->type, m->act, d->gate, d->up, d->down, m->hidden, d->ff, x_mlp, y_mlp, ntok, wsd,
+                       wsd_bytes);
+    if (rc) return rc;
+    const int64_t H = m->hidden, F = m->ff, FD = d->ff;
+    float *gu = (float *)wsd;
+    float *av = (float *)(wsd + align256((size_t)ntok * 2 * (size_t)FD * 4));
+    // One token, the MLP of the experts' block type and FD a multiple of F:
+    // its gate / up rows as FD / F more groups of the experts' gated launch
+    // and its down row as the extra pick of their down launch (two launches
+    // in all).  Otherwise (or when the gated launch cannot take the groups)
+    // the experts' launches, then qg_mlp's.
+    const bool one = ntok == 1 && d->type == m->type && FD % F == 0 &&
+                     moe_down1_fits_dense(m->type, F, FD, topk);
+    if (!one) {
+        rc = qg_moe_ffn(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace, base,
+                        stream);
+        if (rc) return rc;
+        return qg_mlp(d->type, m->act, d->gate, d->up, d->down, H, FD, x_mlp, y_mlp, ntok, wsd, wsd_bytes, stream);
+    }
+    const int64_t rb = H / 32 * qg_block_bytes(m->type);   // a gate / up row's bytes
+    const ExtraGroups xg = {d->gate, d->up, F * rb, FD, (int)(FD / F), x_mlp, av, gu};
+    float *dn = nullptr;
+    int32_t *valid = nullptr;
+    bool taken = false;
+    rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace, base, 0, st,
+                    &dn, &valid, false, &xg, &taken);
+    if (rc) return rc;
+    Moe1Args b = down1_args(m, topk, expert_slots, workspace, y);
+    if (!taken) {   // the experts' down launch, then the MLP on its own
+        rc = launch_moe_down1(m->type, b, st);
+        if (rc) return rc;
+        return qg_mlp(d->type, m->act, d->gate, d->up, d->down, H, FD, x_mlp, y_mlp, ntok, wsd, wsd_bytes, stream);
+    }
+    b.dW = (const uint8_t *)d->down;
+    b.d_row_bytes = FD / 32 * qg_block_bytes(d->type);
+    b.d_nb = (int)(FD / 32);
+    b.d_act = av;
+    b.y_mlp = y_mlp;
+    return launch_moe_down1(m->type, b, st);
 }
 
 int qg_rmsnorm(const float *x, const float *w, float *y, int64_t n, int ntok, float eps, float k, void *stream) {

@@ -60,6 +60,8 @@ struct Picks {
 
 // whether a (block type, F, top-k) the one-token launch serves
 bool moe_down1_fits(int type, int64_t cols, int k);
+// the same with a dense MLP's down row (dense_cols wide) as the extra pick
+bool moe_down1_fits_dense(int type, int64_t cols, int64_t dense_cols, int k);
 int launch_moe_down1(int type, const Moe1Args &a, hipStream_t st);
 
 }  // namespace qg

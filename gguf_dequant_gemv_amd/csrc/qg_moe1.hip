@@ -11,7 +11,8 @@
 // shared expert its down row is one more pick and the launch ends with the
 // shared-expert combine into the residual ([qwen35] moeAccumShared): the
 // gate logit is reduced in every workgroup in the same order, so all use the
-// same value.
+// same value.  A dense MLP beside the experts ([gemma4] encodeLayer) gives
+// its down row as the extra pick instead, its output kept apart.
 #include "../../include/qgemv.h"
 #include "qg_down1.h"
 
@@ -46,6 +47,11 @@ bool moe_down1_fits(int type, int64_t cols, int k) {
     return (type == T_Q8_0 || type == T_Q4_0) && k >= 1 && k <= MOE1_MAXK && cols / 32 <= 2 * MOE1_L;
 }
 
+bool moe_down1_fits_dense(int type, int64_t cols, int64_t dense_cols, int k) {
+    return moe_down1_fits(type, cols, k) && cols / 32 <= MOE1_L && dense_cols % 32 == 0 &&
+           dense_cols / 32 <= MOE1_L * MOE1_MAXX;
+}
+
 typedef void (*moe1_fn)(Moe1Args);
 
 template <int XP>
@@ -53,13 +59,20 @@ moe1_fn moe1_kernel(int type, bool two) {
     if (type == T_Q8_0) return two ? k_moe_down1<UQ8_0B, 2, XP> : k_moe_down1<UQ8_0B, 1, XP>;
     return two ? k_moe_down1<UQ4_0B, 2, XP> : k_moe_down1<UQ4_0B, 1, XP>;
 }
+// a dense row beside routed rows of one unit per lane (moe_down1_fits_dense)
+moe1_fn moe1_kernel_dense(int type) {
+    return type == T_Q8_0 ? k_moe_down1<UQ8_0B, 1, XP_DENSE> : k_moe_down1<UQ4_0B, 1, XP_DENSE>;
+}
 
 int launch_moe_down1(int type, const Moe1Args &a, hipStream_t st) {
-    const int xp = a.shW ? XP_SHARED : XP_NONE;
-    const size_t lds = down1_lds_bytes(a.nb, type == T_Q8_0 ? 0 : 32, xp, a.nb);
+    const int xp = a.dW ? XP_DENSE : a.shW ? XP_SHARED : XP_NONE;
+    const size_t lds = down1_lds_bytes(a.nb, type == T_Q8_0 ? 0 : 32, xp, xp == XP_DENSE ? a.d_nb : a.nb);
     const bool two = a.nb > MOE1_L;
+    if (xp == XP_DENSE && (two || a.d_nb > MOE1_L * MOE1_MAXX)) return QG_EINVAL;
     const dim3 grid((unsigned)((a.rows + 7) / 8));
-    const moe1_fn f = xp == XP_SHARED ? moe1_kernel<XP_SHARED>(type, two) : moe1_kernel<XP_NONE>(type, two);
+    const moe1_fn f = xp == XP_DENSE    ? moe1_kernel_dense(type)
+                      : xp == XP_SHARED ? moe1_kernel<XP_SHARED>(type, two)
+                                        : moe1_kernel<XP_NONE>(type, two);
     if (lds > 64 * 1024 &&
         hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return QG_EHIP;

@@ -317,6 +317,41 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
                       const int32_t *expert_slots, const float *x, float *resid, int ntok, int32_t *ids_out,
                       float *w_out, int32_t *status, void *workspace, size_t workspace_bytes, void *stream);
 
+/* A dense gated MLP that runs beside the routed experts on an input of its
+ * own (a HOST struct; its pointers are device pointers): [gemma4]
+ * encodeLayer's dense GELU MLP (ffn_gate, ffn_up, ffn_down) next to the
+ * experts, on ffn_norm's output while the experts take pre_ffw_norm_2's. */
+typedef struct qg_dense_mlp {
+    int type;               /* qg_type of gate, up and down (not QG_F32)       */
+    int64_t ff;             /* FD                                              */
+    const void *gate;       /* FD x H blocks                                   */
+    const void *up;         /* FD x H blocks                                   */
+    const void *down;       /* H x FD blocks                                   */
+} qg_dense_mlp;
+
+/* The routed experts and the dense MLP beside them, per token t:
+ *   y[t]     = the routed-expert FFN of x[t]            (as qg_moe_ffn)
+ *   y_mlp[t] = W_down (act(W_gate x_mlp[t]) * (W_up x_mlp[t]))
+ *                                                       (as qg_mlp, act = m->act)
+ * One token, d->type == m->type and FD a multiple of F: two launches in all
+ * instead of four, the MLP's gate / up rows riding in the experts' gated
+ * launch as FD / F more row groups and its down rows in their one-token
+ * down launch (values within the same bound as the separate calls; only the
+ * order of a row's sums may differ).  Otherwise the two calls in turn.
+ * y and y_mlp are separate outputs ([ntok][H] each; Gemma's FFN tail
+ * normalises them apart); neither may overlap x, x_mlp or the other.
+ * workspace: at least qg_moe_dense_workspace_size(m, d, topk, ntok) bytes,
+ * 256-byte aligned: qg_moe_ffn's workspace (same layout), then the MLP's
+ * (qg_mlp's layout: gu [ntok][2 FD], act [ntok][FD], ...) at
+ * qg_moe_workspace_size(m, topk, ntok).
+ * Errors: as qg_moe_ffn, and as qg_mlp for the MLP's shapes and pointers
+ * (all checked before anything is enqueued). */
+size_t qg_moe_dense_workspace_size(const qg_moe *m, const qg_dense_mlp *d, int topk, int ntok);
+int qg_moe_ffn_dense(const qg_moe *m, const qg_dense_mlp *d, const float *router_logits, int topk,
+                     const int32_t *expert_slots, const float *x, float *y, const float *x_mlp, float *y_mlp,
+                     int ntok, int32_t *ids_out, float *w_out, int32_t *status, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Gemma's FFN tail, per token of n values ([gemma4] encodeExperts: the
  * post_ffw_norm_1 / post_ffw_norm_2 rmsnorms, then WGSL postFfn):
  *   m = rmsnorm(mlp) * w1,  e = rmsnorm(moe) * w2,  v = m + e

@@ -195,6 +195,26 @@ def test_moe_shared_rejects_and_sizes():
                                None) == qg.QG_EINVAL
 
 
+def test_moe_dense_rejects_and_sizes():
+    L = qg.lib()
+    m = _moe(n_experts=256, ff=512, gate_up_stride=2 * 512 * 64 * 34, down_stride=2048 * 16 * 34)
+    d = qg.qg_dense_mlp(8, 1536, FAKE, FAKE, FAKE)
+    base = qg.qg_moe_workspace_size(m, 8, 1)
+    ws = qg.qg_moe_dense_workspace_size(m, d, 8, 1)
+    assert ws == base + qg.qg_mlp_workspace_size(8, 2048, 1536, 1)    # qg_mlp's layout after the routed part
+    assert qg.qg_moe_dense_workspace_size(m, qg.qg_dense_mlp(8, 0, FAKE, FAKE, FAKE), 8, 1) == 0
+    call = lambda dd, w=ws, T=1, xm=FAKE, ym=FAKE: L.qg_moe_ffn_dense(
+        ctypes.byref(m), ctypes.byref(dd), FAKE, 8, FAKE, FAKE, FAKE, xm, ym, T, None, None, FAKE, FAKE, w, None)
+    assert call(d, w=ws - 256) == qg.QG_EINVAL                                 # short workspace
+    assert call(d, T=17) == qg.QG_ELIMIT
+    assert call(qg.qg_dense_mlp(8, 100, FAKE, FAKE, FAKE)) == qg.QG_EINVAL     # FD % 32
+    assert call(qg.qg_dense_mlp(8, 1536, FAKE, None, FAKE)) == qg.QG_EINVAL    # no up rows
+    assert call(d, xm=None) == qg.QG_EINVAL
+    assert call(d, ym=FAKE + 2) == qg.QG_EINVAL                                # misaligned output
+    assert L.qg_moe_ffn_dense(ctypes.byref(m), None, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, None, FAKE,
+                              FAKE, ws, None) == qg.QG_EINVAL
+
+
 def test_gemm_token_limits():
     L = qg.lib()
     assert L.qg_gemv(8, FAKE, FAKE, FAKE, 16, 64, 17, None) == qg.QG_ELIMIT
