@@ -10,6 +10,7 @@
 #include "qg_moe1.h"
 #include "qg_kernels.h"
 #include "qg_block.h"
+#include "qg_kq1.h"
 
 using namespace qg;
 
@@ -563,6 +564,20 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
         Shape sc = s;
         sc.rows = rows - r0 < chunk ? rows - r0 : chunk;
         const uint8_t *Wc = (const uint8_t *)W + r0 * s.row_bytes;
+        if (ntok == 1 && (type == QG_Q4_K || type == QG_Q6_K)) {   // quarter-block units (qg_kq1.h)
+            Kq1Args ka = {};
+            ka.W = Wc;
+            ka.rows = sc.rows;
+            ka.row_bytes = (u32)s.row_bytes;
+            ka.range = (u32)(sc.rows * s.row_bytes);
+            ka.nu = (int)(cols / 64);
+            ka.cols = (int)cols;
+            ka.x = x;
+            ka.y = y + r0;
+            rc = launch_kq1(type, ka, (hipStream_t)stream);
+            if (rc == QG_OK) continue;
+            if (rc != QG_EINVAL) return rc;   // else: the block-unit kernels below
+        }
         Plan p = make_plan(sc, ntok, 1, aligned(Wc, 16));
         GemvArgs a = {};
         a.W0 = a.W1 = Wc;
@@ -606,8 +621,28 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
     // the first launch of the call (rows in launches of at most MAX_RANGE bytes)
     const int64_t chunk = MAX_RANGE / s.row_bytes;
     if (s.rows > chunk) s.rows = chunk;
-    const Plan p = make_plan(s, ntok, 1, w_aligned16 != 0);
     for (int i = 0; i < 8; i++) out[i] = 0;
+    if (ntok == 1 && (type == QG_Q4_K || type == QG_Q6_K)) {
+        int L = 0, nw = 0, g = 0;
+        size_t lds = 0;
+        // (a W at the given alignment and an aligned x stand in for the call's)
+        const void *Wq = (const void *)(uintptr_t)(w_aligned16 ? 0x10000 : 0x10002);
+        rc = kq1_plan(type, s.rows, s.cols, Wq, (const float *)(uintptr_t)0x10000, query_device != 0, &L, &nw, &g,
+                      &lds);
+        if (rc == QG_OK) {
+            out[0] = 4;
+            out[1] = L;
+            out[2] = 1;
+            out[3] = g;
+            out[4] = query_device ? g : 0;
+            out[5] = (int32_t)lds;
+            out[6] = 2;
+            out[7] = nw;
+            return QG_OK;
+        }
+        if (rc != QG_EINVAL) return rc;
+    }
+    const Plan p = make_plan(s, ntok, 1, w_aligned16 != 0);
     out[0] = p.kind;
     out[2] = p.nt;
     if (p.kind == UK_MFMA) {

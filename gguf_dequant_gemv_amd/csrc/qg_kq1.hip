@@ -1,0 +1,111 @@
+// qg_kq1.hip -- instances, plan and launch of the one-token K-quant GEMV
+// (k_kq1 in qg_kq1.h).
+#include <mutex>
+
+#include "../../include/qgemv.h"
+#include "qg_kq1.h"
+
+namespace qg {
+
+namespace {
+typedef void (*kq1_fn)(Kq1Args);
+constexpr int KQ1_CU = 256;
+constexpr size_t KQ1_MAX_LDS = 150 * 1024;
+
+template <class U, int NW>
+kq1_fn by_lanes(int L) {
+    return L == 16 ? k_kq1<U, 16, NW> : L == 32 ? k_kq1<U, 32, NW> : k_kq1<U, 64, NW>;
+}
+
+kq1_fn kq1_kernel(int type, bool aln, int L, int nw) {
+    if (type == T_Q6_K) return nw == 8 ? by_lanes<KQ6, 8>(L) : by_lanes<KQ6, 4>(L);
+    if (aln) return nw == 8 ? by_lanes<KQ4<true>, 8>(L) : by_lanes<KQ4<true>, 4>(L);
+    return nw == 8 ? by_lanes<KQ4<false>, 8>(L) : by_lanes<KQ4<false>, 4>(L);
+}
+
+// workgroups resident at once (all CUs): measured for the instance when a
+// device is there to ask, else estimated from LDS and the waves per SIMD
+// its register budget leaves room for
+int kq1_resident(kq1_fn f, int type, int nw, size_t lds, bool query) {
+    int per_cu = 0;
+    if (query) {
+        struct Entry { kq1_fn f; size_t lds; int n; };
+        static std::mutex mu;
+        static Entry cache[64];
+        static int used = 0;
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; i++)
+            if (cache[i].f == f && cache[i].lds == lds) return cache[i].n;
+        // (the limit is set to the largest LDS any plan takes, so a launch
+        // never finds it lowered by a smaller shape's plan)
+        if (hipFuncSetAttribute((const void *)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)KQ1_MAX_LDS) !=
+            hipSuccess)
+            return -1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 64 * nw, lds) != hipSuccess)
+            return -1;
+        if (per_cu < 1) per_cu = 1;
+        if (used < 64) cache[used++] = {f, lds, per_cu * KQ1_CU};
+        return per_cu * KQ1_CU;
+    }
+    const int by_lds = (int)((160 * 1024) / (lds ? lds : 1));
+    const int by_waves = 4 * (type == T_Q4_K ? KQ4<true>::WAVES : KQ6::WAVES) / nw;
+    per_cu = by_lds < by_waves ? by_lds : by_waves;
+    return (per_cu < 1 ? 1 : per_cu) * KQ1_CU;
+}
+}  // namespace
+
+// Whether the one-token K-quant kernel serves (type, rows, cols) with W and
+// x where they are, and its geometry: lanes per row, waves per workgroup,
+// workgroups, LDS bytes.  0: it serves; QG_EINVAL: the caller takes the
+// block-unit kernels; QG_EHIP: a device query failed.
+//
+// The choice of lanes per row weighs the unit slots a lane runs (more lanes,
+// fewer slots) against the waves each SIMD then holds (the decode keeps the
+// vector units busy, so a SIMD's time grows with its waves once it holds two
+// or more; with fewer, latency sets it): the estimate is slots times the sum
+// over the launch's rounds of max(2, the round's waves per SIMD).
+int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,
+             int *wgs, size_t *lds) {
+    if ((type != T_Q4_K && type != T_Q6_K) || rows < 1 || cols < 256 || cols % 256) return QG_EINVAL;
+    if (((uintptr_t)x & 15u) || ((uintptr_t)W & 1u)) return QG_EINVAL;
+    const size_t l = kq1_lds_bytes(type, (int)cols);
+    if (cols > (1 << 20) || l > KQ1_MAX_LDS) return QG_EINVAL;
+    const int bb = type == T_Q4_K ? 144 : 210;
+    if (rows * (cols / 256) * bb >= ((int64_t)1 << 32) - 8) return QG_EINVAL;
+    const bool aln = ((uintptr_t)W & 3u) == 0;
+    const int w = l > 40 * 1024 ? 8 : 4;
+    const int nu = (int)(cols / 64);
+    double best = 0.0;
+    int bl = 0;
+    int64_t bwg = 0;
+    for (int L = 16; L <= 64; L *= 2) {
+        const int K = (nu + L - 1) / L;
+        const int64_t waves = (rows + 64 / L - 1) / (64 / L);
+        const int64_t g = (waves + w - 1) / w;
+        const int cap = kq1_resident(kq1_kernel(type, aln, L, w), type, w, l, query);
+        if (cap < 0) return QG_EHIP;
+        const int64_t full = g / cap, rest = g % cap;
+        const double per_full = (double)cap * w / (4.0 * KQ1_CU), per_rest = (double)rest * w / (4.0 * KQ1_CU);
+        const double est = K * ((double)full * (per_full > 2.0 ? per_full : 2.0) +
+                                (rest ? (per_rest > 2.0 ? per_rest : 2.0) : 0.0));
+        if (bl == 0 || est < best - 1e-9) { best = est; bl = L; bwg = g; }
+    }
+    if (bwg > 0x7fffffff) return QG_EINVAL;
+    *lpr = bl;
+    *nw = w;
+    *wgs = (int)bwg;
+    *lds = l;
+    return QG_OK;
+}
+
+int launch_kq1(int type, const Kq1Args &a, hipStream_t st) {
+    int L = 0, nw = 0, g = 0;
+    size_t lds = 0;
+    const int rc = kq1_plan(type, a.rows, a.cols, a.W, a.x, true, &L, &nw, &g, &lds);
+    if (rc) return rc;
+    const kq1_fn f = kq1_kernel(type, ((uintptr_t)a.W & 3u) == 0, L, nw);
+    hipLaunchKernelGGL(f, dim3((unsigned)g), dim3(64 * nw), lds, st, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+}
+
+}  // namespace qg

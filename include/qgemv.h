@@ -117,11 +117,14 @@ int qg_gemm(int type, const void *W, const float *x, float *y,
 /* The launch plan qg_gemv takes for a shape (host only; for tests and tuning).
  * out[8] (a HOST array) receives: [0] kernel kind (0 per-lane unit loads, 1
  * weights staged through LDS from 16-byte-aligned rows, 2 the same for any
- * 2-byte phase, 3 matrix-core small batch), [1] lanes per row (0 for kind 3),
- * [2] tokens per workgroup, [3] row tiles, [4] workgroups along the rows
- * (grid-stride: each walks row tiles wg, wg + [4], ...; needs a device query,
- * 0 when query_device is 0), [5] dynamic LDS bytes, [6] weight stages in
- * flight per wave, [7] x chunk (row elements staged at a time, 0 = all of x).
+ * 2-byte phase, 3 matrix-core small batch, 4 one token against Q4_K / Q6_K
+ * rows in quarter-block units, taken when x is 16-byte aligned), [1] lanes per
+ * row (0 for kind 3), [2] tokens per workgroup, [3] row tiles, [4] workgroups
+ * along the rows (grid-stride: each walks row tiles wg, wg + [4], ...; needs a
+ * device query, 0 when query_device is 0; kind 4: one tile each), [5] dynamic
+ * LDS bytes, [6] weight stages in flight per wave (kind 4: units in flight per
+ * lane), [7] x chunk (row elements staged at a time, 0 = all of x; kind 4:
+ * waves per workgroup).
  * The plan of the first launch of the call (launches cover at most 2 GiB of
  * weights each).  w_aligned16: W would start 16-byte aligned.
  * Errors: as qg_gemv, QG_EINVAL for a null out, QG_EHIP when the device query

@@ -312,12 +312,26 @@ def test_gemm_split_workspace():
     assert L.qg_gemm(8, FAKE, FAKE, FAKE, 2560, 9728, 64, None, n, None) == qg.QG_EINVAL         # null
 
 
+def test_gemv_plan_kquant_one_token():
+    """One token against K-quant rows takes the quarter-block kernel (kind 4):
+    16 lanes a row for the Q4_K 17408 x 5120 shape (5 units each), 32 for the
+    Q6_K 5120 x 17408 one (8.5 units each, 8-wave workgroups for its 68 KiB of
+    x), and at any 2-byte phase of W; more tokens keep the block kernels."""
+    p = qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 16, 17408 // 16, 4)
+    p = qg.qg_gemv_plan(qg.QG_Q6_K, 5120, 17408, 1)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 32, 5120 // 16, 8)
+    assert p["lds_bytes"] > 64 * 1024
+    assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1, w_aligned16=False)["kind"] == 4
+    assert qg.qg_gemv_plan(qg.QG_Q6_K, 262144, 2816, 1)["lanes_per_row"] == 16
+    assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 2)["kind"] != 4
+    assert qg.qg_gemv_plan(qg.QG_Q8_0, 17408, 5120, 1)["kind"] != 4
+
+
 def test_gemv_plan_multi_tile_shapes():
     """The shapes of the multi-tile parity cases take the per-lane kernel with
     more row tiles than workgroups can be resident at once (256 CUs, at most
     8 workgroups of 4 waves each), so some workgroup walks several tiles."""
-    p = qg.qg_gemv_plan(qg.QG_Q6_K, 262144, 2816, 1)
-    assert p["kind"] == 0 and p["lanes_per_row"] == 8 and p["row_tiles"] > 256 * 8
     p = qg.qg_gemv_plan(qg.QG_Q8_0, 150001, 33 * 32, 1)
     assert p["kind"] == 0 and p["row_tiles"] > 256 * 8
     # an even block count takes the LDS-staged kernel instead

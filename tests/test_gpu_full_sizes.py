@@ -117,8 +117,6 @@ def _grid_stride_rows(plan, rows, g, n=400):
 
 
 @pytest.mark.parametrize("t,rows,cols", [
-    # the Q6_K head shape on the per-lane kernel (8 lanes a row, 32-row tiles)
-    (gs.Q6_K, 262144, 2816),
     # odd Q8_0 block count (per-lane kernel, single blocks), ragged last tile
     (gs.Q8_0, 150001, 33 * 32)])
 def test_gemv_multi_tile_workgroups(orc, t, rows, cols):
@@ -138,6 +136,29 @@ def test_gemv_multi_tile_workgroups(orc, t, rows, cols):
     ri = _grid_stride_rows(plan, rows, g)
     yr, A = orc.gemv(t, W, x, rows, cols, 1, row_idx=ri)
     check_rows(y[:, ri], yr, A, "%s %dx%d multi-tile" % (gs.NAMES[t], rows, cols))
+    assert np.isfinite(y).all()
+
+
+def test_kquant_head_many_rounds(orc):
+    """The Q6_K head shape (262144 x 2816) on the quarter-block kernel: many
+    more workgroups than are resident at once; the first and last 40 rows and
+    seeded random rows against the oracle."""
+    import gguf_dequant_gemv_amd as qg
+    t, rows, cols = gs.Q6_K, 262144, 2816
+    plan = qg.qg_gemv_plan(t, rows, cols, 1, True, True)
+    say("q6_k head one token", rows, cols, plan)
+    assert plan["kind"] == 4 and plan["workgroups"] > 256 * 8
+    g = gs.rng(46)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, 1, cols)
+    Wt, _ = dev(W)
+    xt, _ = dev(x)
+    y = gemv_gpu(t, Wt, xt, rows, cols, 1)
+    del Wt
+    ri = np.array(sorted(set(range(40)) | set(range(rows - 40, rows)) |
+                         set(g.choice(rows, size=600, replace=False).tolist())), dtype=np.int64)
+    yr, A = orc.gemv(t, W, x, rows, cols, 1, row_idx=ri)
+    check_rows(y[:, ri], yr, A, "q6_k head")
     assert np.isfinite(y).all()
 
 

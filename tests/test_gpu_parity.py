@@ -123,6 +123,40 @@ def test_gemv_parity(orc, t, rows, nbk, ntok, off):
     check_rows(y, y_ref, A, "gemv %s %dx%d T=%d" % (gs.NAMES[t], rows, cols, ntok))
 
 
+# One token against K-quant rows: the quarter-block kernel (plan kind 4) for
+# every shape below whose x is 16-byte aligned -- fewer units per row than
+# lanes, units not a multiple of the lanes, odd blocks per row (Q6_K rows then
+# alternate 0 / 2 mod 4), W at a 2-byte phase, x wide enough for 8-wave
+# workgroups; a misaligned x takes the block-unit kernels instead.
+KQ1_CASES = [
+    # type, rows, cols, W offset, x offset
+    (gs.Q4_K, 1, 256, 0, 0), (gs.Q4_K, 37, 768, 0, 0), (gs.Q4_K, 203, 5120, 2, 0), (gs.Q4_K, 130, 20480, 0, 0),
+    (gs.Q4_K, 64, 1280, 0, 4),
+    (gs.Q6_K, 1, 256, 0, 0), (gs.Q6_K, 45, 1280, 0, 0), (gs.Q6_K, 77, 2816, 2, 0), (gs.Q6_K, 33, 17408, 0, 0),
+    (gs.Q6_K, 50, 4352, 0, 4), (gs.Q6_K, 129, 4352, 2, 0),
+]
+
+
+@pytest.mark.parametrize("t,rows,cols,w_off,x_off", KQ1_CASES)
+def test_gemv_kquant_one_token(orc, t, rows, cols, w_off, x_off):
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    plan = qg.qg_gemv_plan(t, rows, cols, 1, w_off == 0)
+    assert plan["kind"] == 4, plan
+    g = gs.rng(2300 + t + rows + cols + w_off + x_off)
+    W = gs.weights(t, g, rows, cols)
+    x = gs.activations(g, 1, cols)
+    say("gemv one token", gs.NAMES[t], rows, cols, "W offset", w_off, "x offset", x_off, plan)
+    Wt, Wp = dev(W, w_off)
+    xt, xp = dev(x, x_off)
+    y = torch.full((1, rows), float("nan"), dtype=torch.float32, device="cuda")
+    qg.qg_gemv(t, Wp, xp, y, rows, cols, 1)
+    yh = host(y)
+    del Wt, xt
+    y_ref, A = orc.gemv(t, W, x, rows, cols, 1)
+    check_rows(yh, y_ref, A, "gemv %s %dx%d one token" % (gs.NAMES[t], rows, cols))
+
+
 # x wider than two workgroups' share of LDS, with more row tiles than one
 # round at one workgroup per CU holds, is staged in chunks of whole row
 # elements (restaged per tile row): T = 1 and 2, aligned and 2-byte-offset
