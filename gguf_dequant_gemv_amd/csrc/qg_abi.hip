@@ -636,7 +636,7 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
             out[3] = g;
             out[4] = query_device ? g : 0;
             out[5] = (int32_t)lds;
-            out[6] = 2;
+            out[6] = type == QG_Q4_K ? KQ4<true>::NF : KQ6::NF;
             out[7] = nw;
             return QG_OK;
         }

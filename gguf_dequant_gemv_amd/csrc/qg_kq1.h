@@ -16,9 +16,12 @@
 //         group of 16 for each p ([ternary-bonsai] dequantQ6K layout).
 // L lanes share a row (lane `sub` takes units sub, sub + L, ...), a wave
 // holds 64/L rows, a workgroup NW waves.  x is staged once per workgroup in
-// LDS (4 floats of padding after every 64, so the lanes of a row read
-// different banks) with its sums over each scale group, which fold the
-// Q4_K mins and the Q6_K offset of 32.  Two units per lane are in flight.
+// LDS (4 floats of padding after every 64 values, so the b128 reads of 8
+// neighbouring lanes spread over the banks) with its sums over each scale
+// group, which fold the Q4_K mins and the Q6_K offset of 32.  (Padding Q6_K's
+// x per 128 values spreads its lanes wider but measured slower, as did a
+// third Q6_K unit in flight.)
+// NF units per lane are in flight (3 for Q4_K, 2 for Q6_K).
 #pragma once
 #include "qg_device.h"
 
@@ -59,15 +62,37 @@ QG_DEV void kq1_fence(float (&s)[4]) {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// x into LDS at xpad positions and the sums of its groups of G values
-template <int NT, int G>
-QG_DEV void kq1_stage_x(const float *x, int cols, float *xs, float *ss) {
+// x in LDS: 4 floats of padding after every PG values (PG = 64 or 128, the
+// span whose offsets spread the lanes of a row over the banks)
+template <int PG>
+QG_DEV int kq1_xpos(int c) { return c + 4 * (c / PG); }
+template <int PG>
+__host__ __device__ inline int kq1_xstride(int cols) { return cols + 4 * (cols / PG) + 4; }
+
+// x into LDS at kq1_xpos positions, with the sums of its groups of G
+// values, in two steps: kq1_x_load puts this thread's share (XN float4, a
+// compile-time bound on cols / 4 / NT) in registers, kq1_x_put stores it.
+// The loads go out before the weight loads, so their wait does not include
+// the weights' (loads retire in order).
+// (every load is issued, past the end at the last float4: a load under a
+// condition would be waited for inside its branch)
+template <int NT, int XN>
+QG_DEV void kq1_x_load(const float *x, int cols, f32x4 (&v)[XN]) {
     const int n4 = cols >> 2;   // a multiple of 64: a wave's lanes are all in range or all out
-    for (int i = threadIdx.x; i < n4; i += NT) {
-        const f32x4 v = ((const f32x4 *)x)[i];
-        *(f32x4 *)(xs + xpad(4 * i)) = v;
-        const float g = group_sum<G / 4>((v.x + v.y) + (v.z + v.w));
-        if ((i & (G / 4 - 1)) == 0) ss[(4 * i) / G] = g;
+#pragma unroll
+    for (int b = 0; b < XN; b++) v[b] = ((const f32x4 *)x)[min((int)threadIdx.x + b * NT, n4 - 1)];
+}
+template <int NT, int XN, int G, int PG>
+QG_DEV void kq1_x_put(const f32x4 (&v)[XN], int cols, float *xs, float *ss) {
+    const int n4 = cols >> 2;
+#pragma unroll
+    for (int b = 0; b < XN; b++) {
+        const int i = (int)threadIdx.x + b * NT;
+        if (i < n4) {
+            *(f32x4 *)(xs + kq1_xpos<PG>(4 * i)) = v[b];
+            const float g = group_sum<G / 4>((v[b].x + v[b].y) + (v[b].z + v[b].w));
+            if ((i & (G / 4 - 1)) == 0) ss[(4 * i) / G] = g;
+        }
     }
 }
 
@@ -76,7 +101,7 @@ template <bool ALN>
 struct KQ4 {
     // WAVES: waves per SIMD its registers leave room for (an estimate for
     // plans made without a device to ask)
-    static constexpr int TYPE = T_Q4_K, BB = 144, G = 32, WAVES = 8;
+    static constexpr int TYPE = T_Q4_K, BB = 144, G = 32, PG = 64, NF = 3, WAVES = 6;
     static constexpr int RAW = ALN ? 12 : 14;   // head, codes (+1 dword each when realigned)
     QG_DEV static void issue(rsrc_t r, u32 rowoff, int u, u32 (&t)[RAW]) {
         const u32 b = rowoff + (u32)(u >> 2) * BB;
@@ -147,7 +172,7 @@ struct KQ4 {
 // Every field of a block sits at the block's own 2-byte phase (the fields
 // start at multiples of 4 within it), so one shift realigns them all.
 struct KQ6 {
-    static constexpr int TYPE = T_Q6_K, BB = 210, G = 16, WAVES = 5;
+    static constexpr int TYPE = T_Q6_K, BB = 210, G = 16, PG = 64, NF = 2, WAVES = 5;
     static constexpr int RAW = 5 + 5 + 5 + 6;   // ql (two pieces), qh, scales + d: each +1 dword
     QG_DEV static void issue(rsrc_t r, u32 rowoff, int u, u32 (&t)[RAW]) {
         const u32 b = rowoff + (u32)(u >> 2) * BB;
@@ -162,10 +187,10 @@ struct KQ6 {
 #pragma unroll
         for (int i = 0; i < 6; i++) t[15 + i] = s[i];
     }
-    // ph: the block's byte phase; xu: x of value 128n + 16h of the block
-    // (with xpad, piece p at xu + {0, 32, 68, 100}); sb: the block's 16
-    // group sums of x
-    QG_DEV static float dot(const u32 (&t)[RAW], u32 ph, int n, int h, const float *xu, const float *sb) {
+    // ph: the block's byte phase; xs: x in LDS, v0: the row index of value
+    // 128n + 16h of the block (piece p: values v0 + 32p ..); sb: the block's
+    // 16 group sums of x
+    QG_DEV static float dot(const u32 (&t)[RAW], u32 ph, int n, int h, const float *xs, int v0, const float *sb) {
         u32 A[4], B[4], H[4], S[5];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -184,7 +209,6 @@ struct KQ6 {
             dsc[p] = d * (float)(int8_t)(w >> (8 * (2 * (p & 1) + h)));
         }
         float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        constexpr int XO[4] = {0, 32, 68, 100};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             kq1_fence(s);
@@ -197,7 +221,7 @@ struct KQ6 {
             cd[3] = opaque(((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
 #pragma unroll
             for (int p = 0; p < 4; p++) {
-                const f32x4 xv = *(const f32x4 *)(xu + XO[p] + 4 * i);
+                const f32x4 xv = *(const f32x4 *)(xs + kq1_xpos<PG>(v0 + 32 * p) + 4 * i);
                 s[p] = fmaf(u8_of(cd[p], 0), xv.x, s[p]);
                 s[p] = fmaf(u8_of(cd[p], 1), xv.y, s[p]);
                 s[p] = fmaf(u8_of(cd[p], 2), xv.z, s[p]);
@@ -216,8 +240,9 @@ struct KQ6 {
 // ---- the kernel ------------------------------------------------------------
 // Workgroup bx: rows (bx * NW + wave) * RPW + grp, RPW = 64 / L.  Lanes past
 // the last row load the last row and store nothing; unit slots past the
-// row's last unit load its last unit and add nothing.
-template <class U, int L, int NW>
+// row's last unit load its last unit and add nothing.  XN: float4 of x per
+// thread (cols <= XN * 4 * 64 * NW).
+template <class U, int L, int NW, int XN>
 __global__ __launch_bounds__(64 * NW) void k_kq1(Kq1Args a) {
     extern __shared__ float lds[];
     constexpr int RPW = 64 / L, NT = 64 * NW;
@@ -235,48 +260,60 @@ __global__ __launch_bounds__(64 * NW) void k_kq1(Kq1Args a) {
     const rsrc_t rs = make_rsrc(a.W - ph0, (a.range + ph0 + 3u) & ~3u);
     const u32 rowoff = ph0 + (u32)rl * a.row_bytes;
 
-    // two units' loads in flight per lane: ta holds slots 0, 2, 4, ...,
-    // tb slots 1, 3, 5, ... (the first two issued before x is staged)
-    u32 ta[U::RAW], tb[U::RAW];
-    U::issue(rs, rowoff, min(sub, nu - 1), ta);
-    U::issue(rs, rowoff, min(sub + L, nu - 1), tb);
-
+    // x's loads, then U::NF units' loads in flight per lane (ring entry f
+    // holds slots f, f + NF, ...), then x into LDS
+    constexpr int NF = U::NF;
+    f32x4 xv[XN];
+    kq1_x_load<NT, XN>(a.x, a.cols, xv);
+    kq1_fence();   // (kept ahead of the weight loads)
+    u32 t[NF][U::RAW];
+#pragma unroll
+    for (int f = 0; f < NF; f++) U::issue(rs, rowoff, min(sub + f * L, nu - 1), t[f]);
     float *xs = lds;
-    float *ss = lds + xstride_of(a.cols);
-    kq1_stage_x<NT, U::G>(a.x, a.cols, xs, ss);
+    float *ss = lds + kq1_xstride<U::PG>(a.cols);
+    kq1_x_put<NT, XN, U::G, U::PG>(xv, a.cols, xs, ss);
     __syncthreads();
 
     // slot k's unit: sub + k L (past the row's end: the last unit, not added)
-    auto unit = [&](const u32 (&t)[U::RAW], int k) {
+    auto unit = [&](const u32 (&tu)[U::RAW], int k) {
         const int u = sub + k * L;
         const int uc = min(u, nu - 1);
         float v;
         kq1_fence();
         if constexpr (U::TYPE == T_Q4_K) {
-            v = U::dot(t, ph0, uc & 3, xs + 68 * uc, ss + 2 * uc);
+            v = U::dot(tu, ph0, uc & 3, xs + kq1_xpos<U::PG>(64 * uc), ss + 2 * uc);
         } else {
             const u32 ph = (rowoff + (u32)(uc >> 2) * U::BB) & 3u;
-            v = U::dot(t, ph, (uc >> 1) & 1, uc & 1, xs + 68 * (uc & ~1) + 16 * (uc & 1), ss + 16 * (uc >> 2));
+            v = U::dot(tu, ph, (uc >> 1) & 1, uc & 1, xs, 64 * (uc & ~1) + 16 * (uc & 1), ss + 16 * (uc >> 2));
         }
         kq1_fence();
         return u < nu ? v : 0.0f;
     };
     float acc = 0.0f;
-    int k = 0;
-    for (; k + 1 < K; k += 2) {
-        acc += unit(ta, k);
-        if (k + 2 < K) U::issue(rs, rowoff, min(sub + (k + 2) * L, nu - 1), ta);
-        acc += unit(tb, k + 1);
-        if (k + 3 < K) U::issue(rs, rowoff, min(sub + (k + 3) * L, nu - 1), tb);
+    kq1_fence();
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += NF) {
+#pragma unroll
+        for (int f = 0; f < NF; f++) {
+            const int k = k0 + f;
+            if (k < K) {
+                acc += unit(t[f], k);
+                if (k + NF < K) U::issue(rs, rowoff, min(sub + (k + NF) * L, nu - 1), t[f]);
+            }
+        }
     }
-    if (k < K) acc += unit(ta, k);
     acc = group_sum<L>(acc);
     if (sub == 0 && r < a.rows) a.y[r] = acc;
 }
 
 // LDS bytes of k_kq1 for a row of `cols` values (x and its group sums)
+// (from the same constants the kernel lays LDS out with)
+template <class U>
+inline size_t kq1_lds_bytes_of(int cols) {
+    return ((size_t)kq1_xstride<U::PG>(cols) + (size_t)cols / U::G) * 4;
+}
 inline size_t kq1_lds_bytes(int type, int cols) {
-    return ((size_t)xstride_of(cols) + (size_t)cols / (type == T_Q4_K ? 32 : 16)) * 4;
+    return type == T_Q4_K ? kq1_lds_bytes_of<KQ4<true>>(cols) : kq1_lds_bytes_of<KQ6>(cols);
 }
 
 int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,

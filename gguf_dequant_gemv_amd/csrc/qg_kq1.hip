@@ -12,15 +12,25 @@ typedef void (*kq1_fn)(Kq1Args);
 constexpr int KQ1_CU = 256;
 constexpr size_t KQ1_MAX_LDS = 150 * 1024;
 
-template <class U, int NW>
+template <class U, int NW, int XN>
 kq1_fn by_lanes(int L) {
-    return L == 16 ? k_kq1<U, 16, NW> : L == 32 ? k_kq1<U, 32, NW> : k_kq1<U, 64, NW>;
+    return L == 16 ? k_kq1<U, 16, NW, XN> : L == 32 ? k_kq1<U, 32, NW, XN> : k_kq1<U, 64, NW, XN>;
 }
 
-kq1_fn kq1_kernel(int type, bool aln, int L, int nw) {
-    if (type == T_Q6_K) return nw == 8 ? by_lanes<KQ6, 8>(L) : by_lanes<KQ6, 4>(L);
-    if (aln) return nw == 8 ? by_lanes<KQ4<true>, 8>(L) : by_lanes<KQ4<true>, 4>(L);
-    return nw == 8 ? by_lanes<KQ4<false>, 8>(L) : by_lanes<KQ4<false>, 4>(L);
+// x's float4 per thread, XN = 4, 9 or 12: the least that holds cols /
+// (4 * 64 NW) (each float4 of the bound is a register set held while the
+// first weight loads go out; other bounds measured to upset the register
+// allocation of the unit ring)
+template <class U, int NW>
+kq1_fn by_x(int L, int cols) {
+    const int n = (cols / 4 + 64 * NW - 1) / (64 * NW);
+    return n <= 4 ? by_lanes<U, NW, 4>(L) : n <= 9 ? by_lanes<U, NW, 9>(L) : by_lanes<U, NW, 12>(L);
+}
+
+kq1_fn kq1_kernel(int type, bool aln, int L, int nw, int cols) {
+    if (type == T_Q6_K) return nw == 8 ? by_x<KQ6, 8>(L, cols) : by_x<KQ6, 4>(L, cols);
+    if (aln) return nw == 8 ? by_x<KQ4<true>, 8>(L, cols) : by_x<KQ4<true>, 4>(L, cols);
+    return nw == 8 ? by_x<KQ4<false>, 8>(L, cols) : by_x<KQ4<false>, 4>(L, cols);
 }
 
 // workgroups resident at once (all CUs): measured for the instance when a
@@ -73,7 +83,10 @@ int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x
     const int bb = type == T_Q4_K ? 144 : 210;
     if (rows * (cols / 256) * bb >= ((int64_t)1 << 32) - 8) return QG_EINVAL;
     const bool aln = ((uintptr_t)W & 3u) == 0;
-    const int w = l > 40 * 1024 ? 8 : 4;
+    // (8-wave workgroups for an x past 4096 values: fewer copies of it, and
+    // a thread's share of its loads within 4 float4 up to 8192 values)
+    const int w = l > 40 * 1024 || cols > 4 * 4 * 64 * 4 ? 8 : 4;
+    if (cols > 12 * 4 * 64 * w) return QG_EINVAL;
     const int nu = (int)(cols / 64);
     double best = 0.0;
     int bl = 0;
@@ -82,7 +95,7 @@ int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x
         const int K = (nu + L - 1) / L;
         const int64_t waves = (rows + 64 / L - 1) / (64 / L);
         const int64_t g = (waves + w - 1) / w;
-        const int cap = kq1_resident(kq1_kernel(type, aln, L, w), type, w, l, query);
+        const int cap = kq1_resident(kq1_kernel(type, aln, L, w, (int)cols), type, w, l, query);
         if (cap < 0) return QG_EHIP;
         const int64_t full = g / cap, rest = g % cap;
         const double per_full = (double)cap * w / (4.0 * KQ1_CU), per_rest = (double)rest * w / (4.0 * KQ1_CU);
@@ -103,7 +116,7 @@ int launch_kq1(int type, const Kq1Args &a, hipStream_t st) {
     size_t lds = 0;
     const int rc = kq1_plan(type, a.rows, a.cols, a.W, a.x, true, &L, &nw, &g, &lds);
     if (rc) return rc;
-    const kq1_fn f = kq1_kernel(type, ((uintptr_t)a.W & 3u) == 0, L, nw);
+    const kq1_fn f = kq1_kernel(type, ((uintptr_t)a.W & 3u) == 0, L, nw, a.cols);
     hipLaunchKernelGGL(f, dim3((unsigned)g), dim3(64 * nw), lds, st, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }

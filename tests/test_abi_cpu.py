@@ -315,13 +315,16 @@ def test_gemm_split_workspace():
 def test_gemv_plan_kquant_one_token():
     """One token against K-quant rows takes the quarter-block kernel (kind 4):
     16 lanes a row for the Q4_K 17408 x 5120 shape (5 units each), 32 for the
-    Q6_K 5120 x 17408 one (8.5 units each, 8-wave workgroups for its 68 KiB of
-    x), and at any 2-byte phase of W; more tokens keep the block kernels."""
+    Q6_K 5120 x 17408 one (8.5 units each), both in 8-wave workgroups (x past
+    4096 values), and at any 2-byte phase of W; more tokens keep the block
+    kernels."""
     p = qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1)
-    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 16, 17408 // 16, 4)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 16, 17408 // 32, 8)
     p = qg.qg_gemv_plan(qg.QG_Q6_K, 5120, 17408, 1)
     assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 32, 5120 // 16, 8)
-    assert p["lds_bytes"] > 64 * 1024
+    # x padded by 4 floats per 64 values (+4), then one sum per 16 (Q6_K) / 32 (Q4_K) values
+    assert p["lds_bytes"] == (17408 + 4 * 272 + 4 + 17408 // 16) * 4
+    assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1)["lds_bytes"] == (5120 + 4 * 80 + 4 + 5120 // 32) * 4
     assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1, w_aligned16=False)["kind"] == 4
     assert qg.qg_gemv_plan(qg.QG_Q6_K, 262144, 2816, 1)["lanes_per_row"] == 16
     assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 2)["kind"] != 4
