@@ -50,8 +50,9 @@ def parse():
     ap.add_argument("--dominant-only", action="store_true",
                     help="only launch the dominant kernel, eagerly, --steps times (for counter runs)")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="no GPU: summarise four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a "
-                         "--dominant-only run and of a --copy-probe run) into the text kept under profiles/")
+                    help="summarise four rocprofv3 --pmc output folders (FETCH_SIZE and WRITE_SIZE of a "
+                         "--dominant-only run of --config with --steps steps, and of a --copy-probe run) into the "
+                         "text kept under profiles/ (builds the workload for its name and bytes: needs the GPU)")
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the --copy-probe run summarised")
     ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "COMMAND"),
                     help="no GPU: summarise the kernel statistics of a rocprofv3 --kernel-trace --stats run "
@@ -695,6 +696,8 @@ def source_hash():
 
 
 def _counter_rows(folder, counter):
+    """(dispatch id, kernel name, value) of every dispatch that recorded
+    `counter`, in dispatch order."""
     import csv
     out = []
     for root, _, files in os.walk(folder):
@@ -703,34 +706,56 @@ def _counter_rows(folder, counter):
                 with open(os.path.join(root, f)) as fh:
                     for r in csv.DictReader(fh):
                         if r["Counter_Name"] == counter:
-                            out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
-    return out
+                            out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
 
 
-def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, wl_key, bytes_per_launch):
-    """Text summary: HBM bytes per launch of the dominant kernel from FETCH_SIZE
-    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter
-    reads for a plain device copy of known size."""
-    def kavg(folder, counter, pick):
-        rows = [r for r in _counter_rows(folder, counter) if pick(r[0])]
+def _step_dispatches(rows):
+    """The library's dispatches of the measured steps: those after the last
+    dispatch of anything else (the inputs' generation and copies come first;
+    the steps launch only this library's kernels)."""
+    last_other = max([d for d, n, _ in rows if "qg::" not in n], default=-1)
+    return [(d, n, v) for d, n, v in rows if d > last_other and "qg::" in n]
+
+
+def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, wl_key, bytes_per_launch, steps):
+    """Text summary: HBM bytes per dominant launch (one step of the dominant
+    part: one kernel, or a step's kernels together) from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) summed over the measured steps' dispatches,
+    each counter scaled by what it reads for a plain device copy of known
+    size."""
+    def per_step(folder, counter):
+        rows = _step_dispatches(_counter_rows(folder, counter))
         if not rows:
-            raise SystemExit("no %s rows in %s" % (counter, folder))
-        names = sorted(set(r[0] for r in rows))
-        return sum(r[2] for r in rows) / len(rows), len(rows), names
-    gem = lambda n: "k_gemv" in n
-    cpy = lambda n: "copyBuffer" in n or "copy" in n.lower()
-    f, nf, names = kavg(fetch_dir, "FETCH_SIZE", gem)
-    w, nw, _ = kavg(write_dir, "WRITE_SIZE", gem)
-    cf, ncf, _ = kavg(cfetch_dir, "FETCH_SIZE", cpy)
-    cw, ncw, _ = kavg(cwrite_dir, "WRITE_SIZE", cpy)
+            raise SystemExit("no %s rows of this library's kernels in %s" % (counter, folder))
+        per_kernel = {}
+        for _, n, v in rows:
+            k = n.replace("void qg::", "").split("(qg::")[0].split("(float")[0]
+            per_kernel.setdefault(k, []).append(v)
+        return sum(v for _, _, v in rows) / steps, len(rows), per_kernel
+
+    def copy_avg(folder, counter):
+        rows = [v for _, n, v in _counter_rows(folder, counter) if "copyBuffer" in n or "copy" in n.lower()]
+        if not rows:
+            raise SystemExit("no %s rows of a copy kernel in %s" % (counter, folder))
+        return sum(rows) / len(rows), len(rows)
+    f, nf, kf = per_step(fetch_dir, "FETCH_SIZE")
+    w, nw, kw = per_step(write_dir, "WRITE_SIZE")
+    cf, ncf = copy_avg(cfetch_dir, "FETCH_SIZE")
+    cw, ncw = copy_avg(cwrite_dir, "WRITE_SIZE")
     kib = copy_mib * 1024.0
     ff, fw = kib / cf, kib / cw
     traffic = (f * ff + w * fw) * 1024.0
     lines = [
         "workload: %s" % wl_key,
-        "kernel: %s" % "; ".join(n.replace("void qg::", "").split("(")[0] for n in names),
-        "fetch_kib_per_dispatch: %.1f (mean of %d dispatches)" % (f, nf),
-        "write_kib_per_dispatch: %.1f (mean of %d dispatches)" % (w, nw),
+        "steps: %d (%d dispatches of this library's kernels counted)" % (steps, nf),
+    ]
+    for k in sorted(kf):
+        lines.append("kernel: %s  dispatches %d  fetch_kib_avg %.1f  write_kib_avg %.1f" % (
+            k, len(kf[k]), sum(kf[k]) / len(kf[k]), sum(kw.get(k, [0.0])) / max(1, len(kw.get(k, [])))))
+    lines += [
+        "fetch_kib_per_step: %.1f" % f,
+        "write_kib_per_step: %.1f" % w,
         "copy_probe_mib: %d (read %d MiB, write %d MiB per copy)" % (copy_mib, copy_mib, copy_mib),
         "copy_fetch_kib: %.1f (%d dispatches) -> fetch factor %.4f" % (cf, ncf, ff),
         "copy_write_kib: %.1f (%d dispatches) -> write factor %.4f" % (cw, ncw, fw),
@@ -842,13 +867,6 @@ def main():
     if args.stats_summary:
         sys.stdout.write(stats_summary(*args.stats_summary))
         return
-    if args.traffic_summary:
-        wl_cls = {"1": ("head_q8_0_151936x2560", 151936 * 80 * 34)}
-        key, nbytes = wl_cls.get(args.config, (None, None))
-        if key is None:
-            raise SystemExit("--traffic-summary: counter summaries are kept for config 1's head GEMV")
-        sys.stdout.write(traffic_summary(*args.traffic_summary, args.copy_mib, key, nbytes))
-        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -866,6 +884,10 @@ def main():
     qg.lib()   # fails loudly if the HIP library is not built
     log("[bench] workload", args.config)
     wl = make_workload(args.config, args.copies)
+    if args.traffic_summary:   # (the workload built only for its name and algorithmic bytes)
+        sys.stdout.write(traffic_summary(*args.traffic_summary, args.copy_mib, wl.key, wl.dominant_bytes,
+                                         args.steps))
+        return
     if args.dominant_only:
         for i in range(args.steps):
             wl.dominant_step(i)
