@@ -160,37 +160,47 @@ class DenseMlpHead(Workload):
     def output(self):
         return self.logits
 
-    def cpu_baseline(self, min_seconds=10.0):
-        """The oracle over the whole step (same shapes, numpy-drawn weights),
-        repeated until at least min_seconds of CPU time have passed."""
+    def cpu_baseline(self):
+        """The oracle over the whole step (same shapes, numpy-drawn weights):
+        one warm-up run, then the median of five, on all the host threads
+        the oracle runs with and on one."""
+        import numpy as np
         import oracle
         import gguf_synth as gs
         c = gs.config1(seed=0)
-        oracle.lib()
-        reps, t0 = 0, time.perf_counter()
-        while True:
+
+        def step():
             yg, _ = oracle.gemv(gs.Q8_0, c["Wg"], c["x"], self.F, self.H)
             yu, _ = oracle.gemv(gs.Q8_0, c["Wu"], c["x"], self.F, self.H)
-            import numpy as np
             a = oracle.glu(oracle.ACT_SILU, np.concatenate([yg[0], yu[0]]), self.F)
             h, _ = oracle.gemv_f64(gs.Q8_0, c["Wd"], a, self.H, self.F)
             oracle.gemv(gs.Q8_0, c["Wh"], h.astype(np.float32), self.V, self.H)
-            reps += 1
-            dt = time.perf_counter() - t0
-            if dt >= min_seconds and reps >= 2:
-                break
-        return dict(value=round(self.bytes_per_step * reps / dt / 1e9, 3), unit="GB/s",
-                    cores=_oracle_threads(), kind="oracle",
-                    sample="the whole step (gate||up, SwiGLU, down, head 151936x2560), %d repetitions in %.1f s"
-                           % (reps, dt))
+
+        many = oracle.set_threads(0)
+        t_many = _median_run(step)
+        oracle.set_threads(1)
+        try:
+            t_one = _median_run(step)
+        finally:
+            oracle.set_threads(many)
+        rate = lambda t: round(self.bytes_per_step / t / 1e9, 3)
+        return dict(value=rate(t_many), unit="GB/s", cores=many, kind="oracle",
+                    sample="the whole step (gate||up, SwiGLU, down, head 151936x2560): median of 5 runs after "
+                           "1 warm-up, %.3f s a run" % t_many,
+                    single_core=dict(value=rate(t_one), unit="GB/s", cores=1,
+                                     sample="the same step on one thread: median of 5 after 1 warm-up, "
+                                            "%.3f s a run" % t_one))
 
 
-def _oracle_threads():
-    n = os.environ.get("OMP_NUM_THREADS")
-    try:
-        return int(n) if n else os.cpu_count()
-    except ValueError:
-        return os.cpu_count()
+def _median_run(fn, runs=5):
+    """Seconds of fn(): one warm-up call, then the median of `runs` timed calls."""
+    fn()
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2]
 
 
 class GemvRot(Workload):

@@ -57,6 +57,7 @@ def lib():
         L.or_embed.argtypes = [i32, P, i64, i64, P, i32, ctypes.c_float, P]
         L.or_softcap.argtypes = [P, i64, ctypes.c_float, P]
         L.or_argmax.argtypes = [P, i64, i32, P]
+        L.or_set_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -264,3 +265,9 @@ def argmax(l, n, ntok):
     if lib().or_argmax(_p(lf), n, ntok, _p(idx)):
         raise ValueError("or_argmax: bad arguments")
     return idx
+
+
+def set_threads(n):
+    """Set the host threads the oracle's loops use (n > 0); returns the count
+    in force afterwards (n = 0 only reads it)."""
+    return lib().or_set_threads(int(n))

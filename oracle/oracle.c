@@ -26,6 +26,7 @@
  * renderings, brute force and library routines.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -639,4 +640,12 @@ int or_argmax(const float *l, int64_t n, int ntok, int32_t *idx)
         idx[t] = (int32_t)(best < 0 ? 0 : best);
     }
     return 0;
+}
+
+/* Host threads the parallel loops above use (n > 0 sets them); returns the
+ * count in force.  Timing only: no result depends on it. */
+int or_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
 }
