@@ -54,6 +54,10 @@ def parse():
                          "--dominant-only run of --config with --steps steps, and of a --copy-probe run) into the "
                          "text kept under profiles/ (builds the workload for its name and bytes: needs the GPU)")
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the --copy-probe run summarised")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="no GPU: per-kernel averages of every counter in rocprofv3 --pmc output folders of "
+                         "--dominant-only runs (the measured steps' dispatches), and per-wave ratios of the SQ "
+                         "instruction and cycle counters, as the text kept under profiles/")
     ap.add_argument("--stats-summary", nargs=2, metavar=("DIR", "COMMAND"),
                     help="no GPU: summarise the kernel statistics of a rocprofv3 --kernel-trace --stats run "
                          "(output folder DIR, made by COMMAND) into the text kept under profiles/")
@@ -777,6 +781,44 @@ def traffic_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, copy_mib, wl_k
     return "\n".join(lines) + "\n"
 
 
+def counter_summary(folders):
+    """Per kernel: the average of each counter over the measured steps'
+    dispatches of this library's kernels (every folder one --pmc pass), and
+    per wave: VALU / LDS / SALU / VMEM instructions and the SQ cycle counts
+    when those counters were taken (SQ cycle counters tick once per 4 cycles
+    on this chip; the ratios are given as counted)."""
+    import csv
+    per = {}
+    for folder in folders:
+        rows = {}
+        for root, _, files in os.walk(folder):
+            for f in files:
+                if f.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, f)) as fh:
+                        for r in csv.DictReader(fh):
+                            rows.setdefault(r["Counter_Name"], []).append(
+                                (int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        for counter, rr in rows.items():
+            for _, n, v in _step_dispatches(sorted(rr)):
+                k = n.replace("void qg::", "").split("(qg::")[0].split("(float")[0]
+                per.setdefault(k, {}).setdefault(counter, []).append(v)
+    lines = ["source_sha256: %s" % source_hash()]
+    for k in sorted(per):
+        avg = {c: sum(v) / len(v) for c, v in per[k].items()}
+        lines.append("kernel: %s" % k)
+        for c in sorted(avg):
+            lines.append("  %-28s %16.1f  (%d dispatches)" % (c, avg[c], len(per[k][c])))
+        w = avg.get("SQ_WAVES")
+        if w:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_WAVE_CYCLES",
+                      "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS"):
+                if c in avg:
+                    lines.append("  per wave %-24s %10.1f" % (c, avg[c] / w))
+            if "SQ_WAVE_CYCLES" in avg and "SQ_ACTIVE_INST_VALU" in avg:
+                lines.append("  VALU issue / wave lifetime: %.3f" % (avg["SQ_ACTIVE_INST_VALU"] / avg["SQ_WAVE_CYCLES"]))
+    return "\n".join(lines) + "\n"
+
+
 def stats_summary(folder, command):
     """Per-kernel table from a rocprofv3 --kernel-trace run: this library's
     kernels by name and grid (one template can serve several shapes), everything
@@ -876,6 +918,9 @@ def main():
         sys.exit(2)
     if args.stats_summary:
         sys.stdout.write(stats_summary(*args.stats_summary))
+        return
+    if args.counter_summary:
+        sys.stdout.write(counter_summary(args.counter_summary))
         return
     import torch
     if not torch.cuda.is_available():
