@@ -689,7 +689,8 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
         return QG_EINVAL;
     hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * ntok), 0, (hipStream_t)stream, logits, n_experts, k, ntok,
                        (const int32_t *)nullptr, 1, ids, weights, (int32_t *)nullptr, ids, weights,
-                       (int32_t *)nullptr, (int32_t *)nullptr, 0, (int32_t *)nullptr, 0, (int32_t *)nullptr);
+                       (int32_t *)nullptr, (int32_t *)nullptr, 0, (int32_t *)nullptr, 0, (int32_t *)nullptr,
+                       (const float *)nullptr, (int32_t *)nullptr, (float *)nullptr);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 
@@ -780,10 +781,10 @@ int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *
 // Workspace layout for qg_moe_ffn (each part 256-byte aligned, in order):
 //   gu [T*k][2F] f32 | act [T*k][F] f32 | dn [T*k][H] f32 | ids [T*k] i32 |
 //   w [T*k] f32 | valid [T] i32 | group table (1 + min(E, T*k) * GREC) i32 |
-//   set lists
+//   set lists | each pair's pool slot [T*k] i32 and down scale [T*k] f32
 namespace {
 struct MoeWs {
-    size_t gu, act, dn, ids, w, valid, grp, sets, total;
+    size_t gu, act, dn, ids, w, valid, grp, sets, pslot, pes, total;
 };
 MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     MoeWs o;
@@ -798,6 +799,8 @@ MoeWs moe_ws(int64_t H, int64_t F, int E, int k, int T) {
     o.valid = off; off += align256((size_t)T * 4);
     o.grp = off; off += align256((1 + groups * GREC) * 4);
     o.sets = off; off += align256(2 * (size_t)set_list_ints((int)pairs) * 4);   // gate-up and down lists
+    o.pslot = off; off += align256(pairs * 4);
+    o.pes = off; off += align256(pairs * 4);
     o.total = off;
     return o;
 }
@@ -904,7 +907,8 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     if (!route_in) {
         const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
         hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots,
-                           n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp, ca, sets_a, cb, sets_b);
+                           n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp, ca, sets_a, cb, sets_b,
+                           m->down_scale, (int32_t *)(ws + L.pslot), (float *)(ws + L.pes));
         if (hipGetLastError() != hipSuccess) return QG_EHIP;
     }
 
@@ -924,6 +928,9 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
         a.r_w = rt_w;
         a.r_valid = rt_valid;
         a.r_grp = grp;
+        a.r_escale = m->down_scale;
+        a.r_pslot = (int32_t *)(ws + L.pslot);
+        a.r_pes = (float *)(ws + L.pes);
     }
     a.W0 = a.W1 = (const uint8_t *)m->gate_up;
     a.rows = F;
@@ -990,7 +997,7 @@ struct SharedWs {
     size_t gu, act, sh, total;
 };
 // the one-token down launch's arguments for a pool, its workspace and output
-Moe1Args down1_args(const qg_moe *m, int topk, const int32_t *slots, void *workspace, float *y) {
+Moe1Args down1_args(const qg_moe *m, int topk, void *workspace, float *y) {
     const MoeWs L = moe_ws(m->hidden, m->ff, m->n_experts, topk, 1);
     uint8_t *ws = (uint8_t *)workspace;
     Moe1Args b = {};
@@ -1001,11 +1008,10 @@ Moe1Args down1_args(const qg_moe *m, int topk, const int32_t *slots, void *works
     b.nb = (int)(m->ff / 32);
     b.act = (const float *)(ws + L.act);
     b.act_stride = m->ff;
-    b.ids = (const int32_t *)(ws + L.ids);
     b.w = (const float *)(ws + L.w);
-    b.slots = slots;
+    b.pslot = (const int32_t *)(ws + L.pslot);
+    b.pes = (const float *)(ws + L.pes);
     b.n_slots = m->n_slots > 0 ? m->n_slots : m->n_experts;
-    b.escale = m->down_scale;
     b.valid = (const int32_t *)(ws + L.valid);
     b.dn = (float *)(ws + L.dn);
     b.y = y;
@@ -1037,7 +1043,7 @@ int qg_moe_ffn(const qg_moe *m, const float *router_logits, int topk, const int3
     int rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace,
                         workspace_bytes, 0, st, &dn, &valid, !one);
     if (rc) return rc;
-    if (one) return launch_moe_down1(m->type, down1_args(m, topk, expert_slots, workspace, y), st);
+    if (one) return launch_moe_down1(m->type, down1_args(m, topk, workspace, y), st);
     // weighted combine in pick order
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((m->hidden + 255) / 256), ntok), dim3(256), 0, st, dn, valid, y,
                        m->hidden, topk);
@@ -1128,7 +1134,7 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
                         workspace_bytes, S.total, st, &dn, &valid, !one, one ? &shg : nullptr, &fused);
     if (rc) return rc;
     if (one) {
-        Moe1Args b = down1_args(m, topk, expert_slots, workspace, nullptr);
+        Moe1Args b = down1_args(m, topk, workspace, nullptr);
         b.shW = (const uint8_t *)sh->down;
         b.sh_act = (const float *)(ws + S.act);
         b.gate_inp = sh->gate_inp;
@@ -1196,7 +1202,7 @@ int qg_moe_ffn_dense(const qg_moe *m, const qg_dense_mlp *d, const float *router
     rc = moe_routed(m, router_logits, topk, expert_slots, x, y, ntok, ids_out, w_out, status, workspace, base, 0, st,
                     &dn, &valid, false, &xg, &taken);
     if (rc) return rc;
-    Moe1Args b = down1_args(m, topk, expert_slots, workspace, y);
+    Moe1Args b = down1_args(m, topk, workspace, y);
     if (!taken) {   // the experts' down launch, then the MLP on its own
         rc = launch_moe_down1(m->type, b, st);
         if (rc) return rc;

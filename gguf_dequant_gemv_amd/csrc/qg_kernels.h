@@ -124,6 +124,11 @@ struct GemvArgs {
     const int32_t *r_slots;
     int32_t *r_ids_out, *r_status, *r_ids, *r_valid, *r_grp;
     float *r_w_out, *r_w;
+    // and, for the one-token down launch, each pick's pool slot and down
+    // scale (r_escale[id], 1 without one) in pick order, when r_pslot is set
+    const float *r_escale;
+    int32_t *r_pslot;
+    float *r_pes;
 };
 
 // ------------------------------------------- one token's routing in-launch --
@@ -137,6 +142,7 @@ constexpr int ROUTE1_MAXK = 8;
 struct Route1 {        // this lane's share of the router inputs (E <= 256)
     float lv[4];       // logit of expert lane + 64 i (0 past E)
     int sl[4];         // its pool slot (-1 past E)
+    float es[4];       // its down scale (1 past E, without one, or unasked)
 };
 
 // Issued as early as possible: nothing else in the launch depends on less.
@@ -147,6 +153,7 @@ QG_DEV void route1_load(const GemvArgs &a, Route1 &r) {
         const int e = lane + 64 * i;
         r.lv[i] = e < a.r_E ? a.r_logits[e] : 0.0f;
         r.sl[i] = e < a.r_E ? a.r_slots[e] : -1;
+        r.es[i] = (a.r_pslot && a.r_escale && e < a.r_E) ? a.r_escale[e] : 1.0f;
     }
 }
 
@@ -248,7 +255,12 @@ QG_DEV void route1_write(const GemvArgs &a, const Route1 &r, const Picked &p, in
     const int lane = threadIdx.x & 63;
     const int k = a.r_k;
     const float wj = route1_weight(r, p, k);
+    const float es = expert_value(r.es, p.id);
     if (lane < k) {
+        if (a.r_pslot) {
+            a.r_pslot[lane] = p.slot;
+            a.r_pes[lane] = es;
+        }
         a.r_ids[lane] = p.id;
         a.r_w[lane] = wj;
         if (a.r_ids_out) a.r_ids_out[lane] = p.id;
@@ -1445,7 +1457,8 @@ int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st);
 // Router / grouping and combine kernels (qg_route.hip).
 __global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,
                         float *w_out, int32_t *status, int32_t *rt_ids, float *rt_w, int32_t *rt_valid,
-                        int32_t *grp, int ca, int32_t *sets_a, int cb, int32_t *sets_b);
+                        int32_t *grp, int ca, int32_t *sets_a, int cb, int32_t *sets_b, const float *escale,
+                        int32_t *rt_pslot, float *rt_pes);
 __global__ void k_combine(const float *dn, const int32_t *rt_valid, float *y, int64_t H, int k);
 
 }  // namespace qg

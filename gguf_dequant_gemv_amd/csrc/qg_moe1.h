@@ -21,11 +21,10 @@ struct Moe1Args {
     int nb;                  // blocks per row (F / 32)
     const float *act;        // [k][act_stride] activations of the picks, pick order
     int64_t act_stride;
-    const int32_t *ids;      // [k] picked experts, pick order
-    const float *w;          // [k] routing weights
-    const int32_t *slots;    // expert -> pool slot
+    const float *w;          // [k] routing weights, pick order
+    const int32_t *pslot;    // [k] the picks' pool slots, pick order
+    const float *pes;        // [k] their down scales (1 without one)
     int n_slots;
-    const float *escale;     // per-expert down scale, or nullptr
     const int32_t *valid;    // [1] 0: a pick has no slot, y is left as it is
     float *dn;               // [k][rows] the terms (dn_j * s) * w_j
     float *y;                // [rows] the sum of the terms, or nullptr

@@ -18,20 +18,17 @@
 
 namespace qg {
 
-// the picks' experts, slots, scales and weights from the routing outputs:
-// each a batch of independent uniform loads (picks past k repeat the last
-// one, unused), so the weight loads wait for two round trips, not two per pick
+// the picks' slots, down scales and weights from the routing outputs (the
+// routing launch wrote them per pick): one batch of independent uniform
+// loads (picks past k repeat the last one, unused), so the weight loads wait
+// for one round trip
 QG_DEV void picks_from_ws(const Moe1Args &a, Picks &pk) {
-    int e[MOE1_MAXK];
 #pragma unroll
     for (int j = 0; j < MOE1_MAXK; j++) {
-        e[j] = a.ids[min(j, a.k - 1)];
-        pk.wj[j] = a.w[min(j, a.k - 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < MOE1_MAXK; j++) {
-        pk.slot[j] = a.slots[e[j]];
-        pk.es[j] = a.escale ? a.escale[e[j]] : 1.0f;
+        const int jj = min(j, a.k - 1);
+        pk.slot[j] = a.pslot[jj];
+        pk.es[j] = a.pes[jj];
+        pk.wj[j] = a.w[jj];
     }
     pk.ok = a.valid[0] != 0;
 }

@@ -13,7 +13,8 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
                                                 const int32_t *slots, int n_slots, int32_t *ids_out, float *w_out,
                                                 int32_t *status, int32_t *rt_ids, float *rt_w,
                                                 int32_t *rt_valid, int32_t *grp, int ca, int32_t *sets_a, int cb,
-                                                int32_t *sets_b) {
+                                                int32_t *sets_b, const float *escale, int32_t *rt_pslot,
+                                                float *rt_pes) {
     __shared__ int s_ids[MAXT * 32];
     __shared__ int s_valid[MAXT];
     __shared__ u32 s_tmask[256];    // expert e: bit t set when valid token t picked e
@@ -73,6 +74,10 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
             ex = expf(s_val[wave * k + lane] - l0);
             const int sl = s_slot[id];
             ok = sl >= 0 && sl < n_slots;
+            if (rt_pslot) {   // each pick's slot and down scale, pick order
+                rt_pslot[wave * k + lane] = sl;
+                rt_pes[wave * k + lane] = escale ? escale[id] : 1.0f;
+            }
         }
         const float sum = wave_sum(ex);
         const int all_ok = __ballot(!ok) == 0ull;
