@@ -142,10 +142,15 @@ Plan make_plan(const Shape &s, int ntok_max, int64_t copies, bool lds_ok, int mf
             // units: segments of 1 KiB or more keep HBM reads in long runs
             // (measured worth more than the idle lanes of a ragged last slot).
             // The K-quant decode is VALU-bound: there idle lanes cost most and
-            // fewer lanes per row (more units each) measured fastest.
+            // fewer lanes per row (more units each) measured fastest.  Grouped
+            // expert launches of several tokens read a few short rows per
+            // expert whatever the lanes, so there the idle lanes alone count
+            // (128 experts, Q4_0 704 x 2816 gate-up and down, 16 tokens: down
+            // 16 -> 4 lanes per row, 126.5 -> 119 us for the layer).
             const bool heavy = s.type == QG_Q4_K || s.type == QG_Q6_K;
+            const bool grouped_tok = p.copies > 1 && ntok_max > 1;
             double seg = 1.0;
-            if (lds_kind(kind) && !heavy) {
+            if (lds_kind(kind) && !heavy && !grouped_tok) {
                 const double sb = (double)lpr * (s.ti.pairs ? 2 * s.ti.bytes : s.ti.bytes);
                 seg = 0.5 + 0.5 * (sb >= 1024.0 ? 1.0 : sb / 1024.0);
             }
