@@ -58,6 +58,8 @@ def lib():
         L.or_softcap.argtypes = [P, i64, ctypes.c_float, P]
         L.or_argmax.argtypes = [P, i64, i32, P]
         L.or_set_threads.argtypes = [i32]
+        L.or_q6k_planes.argtypes = [P, i64, P]
+        L.or_q6k_unplanes.argtypes = [P, i64, P]
         _lib = L
     return _lib
 
@@ -265,6 +267,26 @@ def argmax(l, n, ntok):
     if lib().or_argmax(_p(lf), n, ntok, _p(idx)):
         raise ValueError("or_argmax: bad arguments")
     return idx
+
+
+def q6k_planes(blocks, n):
+    """The Q6_K plane layout of n blocks (uint8 [210 n]): ql, qh, scales, d."""
+    b = _c(blocks, np.uint8).ravel()
+    assert b.size >= 210 * n
+    out = np.empty(210 * n, np.uint8)
+    if lib().or_q6k_planes(_p(b), n, _p(out)):
+        raise ValueError("or_q6k_planes: bad size")
+    return out
+
+
+def q6k_unplanes(planes, n):
+    """Blocks back from the plane layout (the inverse of q6k_planes)."""
+    p = _c(planes, np.uint8).ravel()
+    assert p.size >= 210 * n
+    out = np.empty(210 * n, np.uint8)
+    if lib().or_q6k_unplanes(_p(p), n, _p(out)):
+        raise ValueError("or_q6k_unplanes: bad size")
+    return out
 
 
 def set_threads(n):

@@ -205,6 +205,42 @@ int or_dequant(int type, const uint8_t *blocks, int64_t n, double *out)
     return 0;
 }
 
+/* ----------------------------------------------------- Q6_K planes ---- */
+/* The aligned device layout of Q6_K ([gemma4] q6kPlanes: at load the
+ * 210-byte blocks, which sit at 2-byte alignment, are split into planes of
+ * ql, qh, scales and d).  Here n blocks become four planes, one after another
+ * in one buffer of 210 n bytes:
+ *   ql [n][128] at 0, qh [n][64] at 128 n, scales [n][16] at 192 n,
+ *   d [n] at 208 n as the block's own two f16 bytes
+ * (the page widens d to f32; kept in f16 here, the planes hold the blocks'
+ * bytes and nothing more).  A permutation of the bytes; or_q6k_unplanes is
+ * its inverse. */
+int or_q6k_planes(const uint8_t *blocks, int64_t n, uint8_t *planes)
+{
+    if (n < 0) return -1;
+    for (int64_t b = 0; b < n; b++) {
+        const uint8_t *s = blocks + 210 * b;
+        memcpy(planes + 128 * b, s, 128);
+        memcpy(planes + 128 * n + 64 * b, s + 128, 64);
+        memcpy(planes + 192 * n + 16 * b, s + 192, 16);
+        memcpy(planes + 208 * n + 2 * b, s + 208, 2);
+    }
+    return 0;
+}
+
+int or_q6k_unplanes(const uint8_t *planes, int64_t n, uint8_t *blocks)
+{
+    if (n < 0) return -1;
+    for (int64_t b = 0; b < n; b++) {
+        uint8_t *d = blocks + 210 * b;
+        memcpy(d, planes + 128 * b, 128);
+        memcpy(d + 128, planes + 128 * n + 64 * b, 64);
+        memcpy(d + 192, planes + 192 * n + 16 * b, 16);
+        memcpy(d + 208, planes + 208 * n + 2 * b, 2);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------ GEMV ---- */
 /* y[t][r] = sum_c W[r][c] * x[t][c] and A[t][r] = sum_c |W[r][c] * x[t][c]|,
  * for the rows listed in row_idx (all rows when row_idx is NULL).  W is

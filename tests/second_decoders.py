@@ -101,6 +101,31 @@ def dec_q6_k(blocks):
     return (d[:, None] * s * ((q4 | (h << 4)) - 32)).ravel()
 
 
+def dec_q6_k_planes(planes, n):
+    """n Q6_K blocks in the plane layout, decoded as the [gemma4 page] q6v
+    indexer reads its planes: ql as 32 little-endian words per block (byte
+    qb of the block: word qb >> 2, shift 8 (qb & 3)), qh as 16 words, the
+    scales as 4 words of int8, d from its own plane (f16 here)."""
+    p = np.ascontiguousarray(planes, np.uint8).ravel()
+    ql = p[0:128 * n].view("<u4").reshape(n, 32).astype(np.int64)
+    qh = p[128 * n:192 * n].view("<u4").reshape(n, 16).astype(np.int64)
+    sc = p[192 * n:208 * n].view("<u4").reshape(n, 4).astype(np.int64)
+    dd = p[208 * n:210 * n]
+    d = f16le(dd[0::2], dd[1::2])
+    t = np.arange(256)
+    nh, r = t >> 7, t & 127
+    qd, l = r >> 5, r & 31
+    qb = nh * 64 + l + (qd & 1) * 32
+    lo = (ql[:, qb >> 2] >> ((qb & 3) * 8)) & 0xFF
+    q4 = np.where(qd >= 2, lo >> 4, lo & 15)
+    hb = nh * 32 + l
+    h = (qh[:, hb >> 2] >> ((hb & 3) * 8 + qd * 2)) & 3
+    si = nh * 8 + (l >> 4) + qd * 2
+    s8 = (sc[:, si >> 2] >> ((si & 3) * 8)) & 0xFF
+    s = np.where(s8 >= 128, s8 - 256, s8)
+    return (d[:, None] * s * ((q4 | (h << 4)) - 32)).ravel()
+
+
 DEC = {Q8_0: dec_q8_0, Q4_0: dec_q4_0, Q4_K: dec_q4_k, Q6_K: dec_q6_k}
 
 

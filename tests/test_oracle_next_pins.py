@@ -216,3 +216,39 @@ def test_argmax_ties_nan_and_degenerate(orc):
     assert orc.argmax(l, 4, 5).tolist() == [1, 1, 0, 0, 3]
     l2 = np.array([[-np.inf, -3.4028235e38, -np.inf, -np.inf]], np.float32)
     assert orc.argmax(l2, 4, 1).tolist() == [1]
+
+
+# ------------------------------------------------------------- Q6_K planes --
+from second_decoders import dec_q6_k_planes  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [1, 3, 68])
+def test_q6k_planes_decode_as_the_blocks(orc, n):
+    """The plane layout read by a second decoder written from the page's plane
+    indexer (words of each plane) gives the blocks' values exactly."""
+    W = gs.weights(orc.Q6_K, gs.rng(40 + n), 1, 256 * n)
+    P = orc.q6k_planes(W, n)
+    assert P.size == W.size
+    assert np.array_equal(dec_q6_k_planes(P, n), orc.dequant(orc.Q6_K, W, 256 * n))
+
+
+def test_q6k_planes_worked_offsets(orc):
+    """Two blocks whose bytes name their own place: block b, byte j holds
+    (j + 101 b) mod 256.  Each plane's entries sit where the layout says."""
+    n = 2
+    W = np.array([(j + 101 * b) % 256 for b in range(n) for j in range(210)], np.uint8)
+    P = orc.q6k_planes(W, n)
+    byte = lambda b, j: (j + 101 * b) % 256  # noqa: E731
+    assert P[128 * 1 + 5] == byte(1, 5)                  # ql of block 1
+    assert P[128 * n + 64 * 1 + 0] == byte(1, 128)       # qh of block 1
+    assert P[128 * n + 63] == byte(0, 191)               # last qh byte of block 0
+    assert P[192 * n + 16 * 1 + 15] == byte(1, 207)      # last scale of block 1
+    assert P[208 * n + 0] == byte(0, 208) and P[208 * n + 3] == byte(1, 209)   # d bytes
+    # a permutation of the bytes, undone by the inverse
+    assert np.array_equal(np.sort(P), np.sort(W))
+    assert np.array_equal(orc.q6k_unplanes(P, n), W)
+
+
+def test_q6k_planes_round_trip_random(orc):
+    W = gs.rng(44).integers(0, 256, 210 * 37, dtype=np.uint8)
+    assert np.array_equal(orc.q6k_unplanes(orc.q6k_planes(W, 37), 37), W)
