@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="1",
-                    help="0, 1, 2, 3a, 3b, 4, 4t16; whole FFN blocks q35, q35t16, gblk, gblkt16; heads head8, "
+                    help="0, 1, 2, 3a, 3b (Q6_K in the plane layout), 3bg (Q6_K as GGUF blocks), 4, 4t16; whole FFN blocks q35, q35t16, gblk, gblkt16; heads head8, "
                          "head6; prefill chunks p64, p256")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -210,7 +210,7 @@ def _median_run(fn, runs=5):
 class GemvRot(Workload):
     """One quantized GEMV, T tokens, rotating through distinct weight copies."""
 
-    def __init__(self, t, rows, cols, ntok, total_bytes, label):
+    def __init__(self, t, rows, cols, ntok, total_bytes, label, planes=False):
         import torch
         import gguf_synth as gs
         import gguf_dequant_gemv_amd as qg
@@ -219,13 +219,22 @@ class GemvRot(Workload):
         copies = max(2, int(total_bytes // wb))
         g = _gen(300 + t)
         self.W = [gs.device_weights(t, rows, cols, g) for _ in range(copies)]
+        if planes:
+            # Q6_K in the plane layout, prepared once as at load time (the
+            # same bytes reordered; not part of a step)
+            self.t = qg.QG_Q6_K_PLANES
+            for i, W in enumerate(self.W):
+                P = torch.empty_like(W)
+                qg.qg_prepare(t, W, P, rows, cols)
+                self.W[i] = P
+            torch.cuda.synchronize()
         self.x = gs.device_activations(ntok, cols, g)
         self.y = torch.empty((ntok, rows), dtype=torch.float32, device="cuda")
         self.bytes_per_step = wb
         self.dominant_bytes = wb
         self.name = label
         self.dominant = label
-        self.key = "gemv_%s_%dx%d_t%d" % (gs.NAMES[t].lower(), rows, cols, ntok)
+        self.key = "gemv_%s%s_%dx%d_t%d" % (gs.NAMES[t].lower(), "_planes" if planes else "", rows, cols, ntok)
         self.period = self.dominant_period = copies
 
     def step(self, i):
@@ -577,7 +586,9 @@ def make_workload(name, copies):
     if name == "3a":
         return GemvRot(gs.Q4_K, 17408, 5120, 1, big, "q4_k GEMV 17408x5120, 1 token")
     if name == "3b":
-        return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token")
+        return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token (plane layout)", planes=True)
+    if name == "3bg":
+        return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token (GGUF blocks as stored)")
     if name == "2":
         return MoeLayers(gs.Q8_0, 0, 2048, 768, 128, 8, 1, 16, False,
                          "q8_0 MoE layer 2048, 128 experts ff 768, top-8, 1 token")
@@ -957,7 +968,7 @@ def main():
         cpu = wl.cpu_baseline() if hasattr(wl, "cpu_baseline") else None
     print(json.dumps(result_line(wl, ms, dom_ms, args.steps, args.warmup, cpu, spread)), flush=True)
     if args.all:
-        for name in ("0", "3a", "3b", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6",
+        for name in ("0", "3a", "3b", "3bg", "2", "4", "4t16", "q35", "q35t16", "gblk", "gblkt16", "head8", "head6",
                      "p64", "p256"):
             if name == args.config:
                 continue

@@ -10,6 +10,7 @@ import ctypes
 import os
 
 QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
+QG_Q6_K_PLANES = 270   # Q6_K in the plane layout qg_prepare writes
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
 QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL, QG_MAX_NORMS = 16, 256, 32, 4096, 4
@@ -20,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libqgemv.so")
 
 # Every symbol include/qgemv.h declares.
 EXPORTS = ("qg_block_values", "qg_block_bytes", "qg_strerror", "qg_gemv", "qg_gemm_workspace_size", "qg_gemm",
-           "qg_dequant", "qg_gemv_plan",
+           "qg_dequant", "qg_prepare", "qg_unprepare", "qg_gemv_plan",
            "qg_router_topk", "qg_mlp_workspace_size", "qg_mlp", "qg_moe_workspace_size",
            "qg_moe_ffn", "qg_moe_ffn_noalloc", "qg_rmsnorm", "qg_rmsnorm_multi", "qg_rmsnorm_router", "qg_moe_shared_workspace_size", "qg_moe_ffn_shared",
            "qg_moe_dense_workspace_size", "qg_moe_ffn_dense",
@@ -70,6 +71,8 @@ def lib():
         L.qg_gemm_workspace_size.restype = sz
         L.qg_gemm.argtypes = [i32, P, P, P, i64, i64, i32, P, sz, P]
         L.qg_dequant.argtypes = [i32, P, P, i64, i64, P]
+        L.qg_prepare.argtypes = [i32, P, P, i64, i64, P]
+        L.qg_unprepare.argtypes = [i32, P, P, i64, i64, P]
         L.qg_gemv_plan.argtypes = [i32, i64, i64, i32, i32, i32, P]
         L.qg_router_topk.argtypes = [P, i32, i32, i32, P, P, P]
         L.qg_mlp_workspace_size.argtypes = [i32, i64, i64, i32]
@@ -163,6 +166,16 @@ def qg_gemv_plan(type, rows, cols, ntok=1, w_aligned16=True, query_device=False)
 
 def qg_dequant(type, W, out, rows, cols, stream=None):
     _check("qg_dequant", lib().qg_dequant(type, _ptr(W), _ptr(out), rows, cols, _stream(stream)))
+
+
+def qg_prepare(type, src, dst, rows, cols, stream=None):
+    """GGUF Q6_K blocks -> the plane layout (QG_Q6_K_PLANES), 210 B a block."""
+    _check("qg_prepare", lib().qg_prepare(type, _ptr(src), _ptr(dst), rows, cols, _stream(stream)))
+
+
+def qg_unprepare(type, src, dst, rows, cols, stream=None):
+    """The plane layout -> GGUF Q6_K blocks (the inverse of qg_prepare)."""
+    _check("qg_unprepare", lib().qg_unprepare(type, _ptr(src), _ptr(dst), rows, cols, _stream(stream)))
 
 
 def qg_router_topk(logits, n_experts, k, ntok, ids, weights, stream=None):

@@ -514,12 +514,14 @@ extern "C" {
 
 int qg_block_values(int type) {
     if (type == QG_F32) return 1;
+    if (type == QG_Q6_K_PLANES) type = QG_Q6_K;
     TypeInfo ti;
     return type_info(type, ti) ? ti.qk : 0;
 }
 
 int qg_block_bytes(int type) {
     if (type == QG_F32) return 4;
+    if (type == QG_Q6_K_PLANES) type = QG_Q6_K;
     TypeInfo ti;
     return type_info(type, ti) ? ti.bytes : 0;
 }
@@ -538,6 +540,33 @@ const char *qg_strerror(int code) {
 }  // extern "C"
 
 namespace {
+// One token against a Q6_K tensor in the plane layout: the quarter-block
+// kernel on its planes (one launch: the planes' offsets span the tensor)
+int planes_gemv(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
+                void *stream) {
+    Shape s;
+    int rc = make_shape(QG_Q6_K, rows, cols, s);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
+    if (ntok != 1 || !W || !x || !y || !aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EINVAL;
+    const int64_t n = rows * s.nb;
+    if (n * s.ti.bytes > MAX_RANGE) return QG_ELIMIT;
+    const uint8_t *P = (const uint8_t *)W;
+    Kq1Args ka = {};
+    ka.W = P;
+    ka.Ph = P + 128 * n;
+    ka.Ps = P + 192 * n;
+    ka.Pd = P + 208 * n;
+    ka.rows = rows;
+    ka.row_bytes = (u32)s.row_bytes;
+    ka.range = (u32)(128 * n);
+    ka.nu = (int)(cols / 64);
+    ka.cols = (int)cols;
+    ka.x = x;
+    ka.y = y;
+    return launch_kq1(T_Q6_KP, ka, (hipStream_t)stream);
+}
+
 // qg_gemv / qg_gemm: the same sum for up to max_tok tokens
 int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
                void *ws, size_t ws_bytes, void *stream) {
@@ -553,6 +582,7 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
         }
         return QG_OK;
     }
+    if (type == QG_Q6_K_PLANES) return planes_gemv(W, x, y, rows, cols, ntok, max_tok, stream);
     Shape s;
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
@@ -619,15 +649,21 @@ int qg_gemm(int type, const void *W, const float *x, float *y, int64_t rows, int
 
 int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16, int query_device, int32_t *out) {
     if (!out) return QG_EINVAL;
+    const bool planes = type == QG_Q6_K_PLANES;
     Shape s;
-    int rc = make_shape(type, rows, cols, s);
+    int rc = make_shape(planes ? QG_Q6_K : type, rows, cols, s);
     if (rc) return rc;
+    if (planes) {
+        if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+        if (ntok != 1 || !w_aligned16) return QG_EINVAL;
+        if (rows * s.nb * s.ti.bytes > MAX_RANGE) return QG_ELIMIT;
+    }
     if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
     // the first launch of the call (rows in launches of at most MAX_RANGE bytes)
     const int64_t chunk = MAX_RANGE / s.row_bytes;
     if (s.rows > chunk) s.rows = chunk;
     for (int i = 0; i < 8; i++) out[i] = 0;
-    if (ntok == 1 && (type == QG_Q4_K || type == QG_Q6_K)) {
+    if (ntok == 1 && (type == QG_Q4_K || type == QG_Q6_K || planes)) {
         int L = 0, nw = 0, g = 0;
         size_t lds = 0;
         // (a W at the given alignment and an aligned x stand in for the call's)
@@ -641,11 +677,11 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
             out[3] = g;
             out[4] = query_device ? g : 0;
             out[5] = (int32_t)lds;
-            out[6] = type == QG_Q4_K ? KQ4<true>::NF : KQ6::NF;
+            out[6] = type == QG_Q4_K ? KQ4<true>::NF : planes ? KQ6P::NF : KQ6::NF;
             out[7] = nw;
             return QG_OK;
         }
-        if (rc != QG_EINVAL) return rc;
+        if (rc != QG_EINVAL || planes) return rc;
     }
     const Plan p = make_plan(s, ntok, 1, w_aligned16 != 0);
     out[0] = p.kind;
@@ -676,6 +712,12 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
 
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream) {
     Shape s;
+    if (type == QG_Q6_K_PLANES) {
+        const int rc = make_shape(QG_Q6_K, rows, cols, s);
+        if (rc) return rc;
+        if (!W || !out || !aligned(W, 16) || !aligned(out, 4)) return QG_EINVAL;
+        return launch_q6k_planes_dequant((const uint8_t *)W, out, rows * s.nb, (hipStream_t)stream);
+    }
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
     if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;

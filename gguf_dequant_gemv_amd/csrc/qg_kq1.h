@@ -36,6 +36,9 @@ struct Kq1Args {
     int cols;
     const float *x;     // [cols], 16-byte aligned
     float *y;           // [rows]
+    // Q6_K plane layout only (W: the ql plane, range: its bytes): the qh,
+    // scales and d planes, each 16-byte aligned
+    const uint8_t *Ph, *Ps, *Pd;
 };
 
 // a ? x : y for a per-lane condition, as bit masks (a conditional there
@@ -96,6 +99,11 @@ QG_DEV void kq1_x_put(const f32x4 (&v)[XN], int cols, float *xs, float *ss) {
     }
 }
 
+// The descriptor over a block stream W at byte phase ph0: the range rounded
+// up to whole dwords (a realigned field's last dword may hold the tensor's
+// last bytes, and a dword load reads 0 unless all of it is in range)
+QG_DEV rsrc_t kq1_rsrc(const Kq1Args &a, u32 ph0) { return make_rsrc(a.W - ph0, (a.range + ph0 + 3u) & ~3u); }
+
 // ---- Q4_K: quarter c (= unit & 3) of block unit >> 2 ----------------------
 template <bool ALN>
 struct KQ4 {
@@ -103,6 +111,9 @@ struct KQ4 {
     // plans made without a device to ask)
     static constexpr int TYPE = T_Q4_K, BB = 144, G = 32, PG = 64, NF = 3, WAVES = 6;
     static constexpr int RAW = ALN ? 12 : 14;   // head, codes (+1 dword each when realigned)
+    typedef rsrc_t R;
+    QG_DEV static R rsrc(const Kq1Args &a, u32 ph0) { return kq1_rsrc(a, ph0); }
+    QG_DEV static u32 row_base(const Kq1Args &a, int64_t rl, u32 ph0) { return ph0 + (u32)rl * a.row_bytes; }
     QG_DEV static void issue(rsrc_t r, u32 rowoff, int u, u32 (&t)[RAW]) {
         const u32 b = rowoff + (u32)(u >> 2) * BB;
         const u32 q = b + 16 + 32 * (u32)(u & 3);
@@ -169,12 +180,58 @@ struct KQ4 {
 };
 
 // ---- Q6_K: half n = (unit >> 1) & 1, lane half h = unit & 1 of block unit >> 2
-// Every field of a block sits at the block's own 2-byte phase (the fields
-// start at multiples of 4 within it), so one shift realigns them all.
+// The dot product of one unit from its fields in registers: A, B the two ql
+// pieces (bytes 64n + 16h and 64n + 32 + 16h), H the qh piece (32n + 16h),
+// S the 8 int8 scales of half n, d the super scale.  xs: x in LDS, v0: the
+// row index of value 128n + 16h of the block (piece p: values v0 + 32p ..);
+// sb: the block's 16 group sums of x.
+template <int PG>
+QG_DEV float kq6_dot(const u32 (&A)[4], const u32 (&B)[4], const u32 (&H)[4], const u32 (&S)[2], float d, int h,
+                     int n, const float *xs, int v0, const float *sb) {
+    // group 8n + 2p + h: int8 scale byte 2p + h of the half's scales, times d
+    float dsc[4];
+#pragma unroll
+    for (int p = 0; p < 4; p++) dsc[p] = d * (float)(int8_t)(S[p >> 1] >> (8 * (2 * (p & 1) + h)));
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        kq1_fence(s);
+        // codes of values 32p + 16h + 4i .. +3 of the half, p = 0..3: the
+        // low / high nibbles of the two ql pieces, bit pairs p of qh
+        u32 cd[4];
+        cd[0] = opaque((A[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u));
+        cd[1] = opaque((B[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u));
+        cd[2] = opaque(((A[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u));
+        cd[3] = opaque(((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const f32x4 xv = *(const f32x4 *)(xs + kq1_xpos<PG>(v0 + 32 * p) + 4 * i);
+            s[p] = fmaf(u8_of(cd[p], 0), xv.x, s[p]);
+            s[p] = fmaf(u8_of(cd[p], 1), xv.y, s[p]);
+            s[p] = fmaf(u8_of(cd[p], 2), xv.z, s[p]);
+            s[p] = fmaf(u8_of(cd[p], 3), xv.w, s[p]);
+        }
+    }
+    kq1_fence(s);
+    // (q - 32) folded as sum(q x) - 32 sum(x)
+    float acc = 0.0f;
+#pragma unroll
+    for (int p = 0; p < 4; p++) acc = fmaf(dsc[p], fmaf(-32.0f, sb[8 * n + 2 * p + h], s[p]), acc);
+    return acc;
+}
+
+// GGUF blocks: every field of a block sits at the block's own 2-byte phase
+// (the fields start at multiples of 4 within it), so one shift realigns
+// them all.
 struct KQ6 {
     static constexpr int TYPE = T_Q6_K, BB = 210, G = 16, PG = 64, NF = 2, WAVES = 5;
     static constexpr int RAW = 5 + 5 + 5 + 6;   // ql (two pieces), qh, scales + d: each +1 dword
-    QG_DEV static void issue(rsrc_t r, u32 rowoff, int u, u32 (&t)[RAW]) {
+    typedef rsrc_t R;
+    QG_DEV static R rsrc(const Kq1Args &a, u32 ph0) { return kq1_rsrc(a, ph0); }
+    QG_DEV static u32 row_base(const Kq1Args &a, int64_t rl, u32 ph0) { return ph0 + (u32)rl * a.row_bytes; }
+    // the shift that realigns unit uc's fields
+    QG_DEV static u32 phase(u32 rowoff, int uc) { return (rowoff + (u32)(uc >> 2) * BB) & 3u; }
+    QG_DEV static void issue(const R &r, u32 rowoff, int u, u32 (&t)[RAW]) {
         const u32 b = rowoff + (u32)(u >> 2) * BB;
         const u32 n = (u32)(u >> 1) & 1u, h = (u32)u & 1u;
         u32 a[5], c[5], e[5], s[6];
@@ -187,9 +244,6 @@ struct KQ6 {
 #pragma unroll
         for (int i = 0; i < 6; i++) t[15 + i] = s[i];
     }
-    // ph: the block's byte phase; xs: x in LDS, v0: the row index of value
-    // 128n + 16h of the block (piece p: values v0 + 32p ..); sb: the block's
-    // 16 group sums of x
     QG_DEV static float dot(const u32 (&t)[RAW], u32 ph, int n, int h, const float *xs, int v0, const float *sb) {
         u32 A[4], B[4], H[4], S[5];
 #pragma unroll
@@ -200,40 +254,44 @@ struct KQ6 {
         }
 #pragma unroll
         for (int i = 0; i < 5; i++) S[i] = __builtin_amdgcn_alignbyte(t[16 + i], t[15 + i], ph);
-        // group 8n + 2p + h: int8 scale byte 8n + 2p + h of S[0..3], times d
-        const float d = h2f(S[4]);
-        float dsc[4];
+        const u32 Sn[2] = {kq1_sel(n != 0, S[2], S[0]), kq1_sel(n != 0, S[3], S[1])};
+        return kq6_dot<PG>(A, B, H, Sn, h2f(S[4]), h, n, xs, v0, sb);
+    }
+};
+
+// The plane layout ([gemma4] q6kPlanes, d kept as f16): ql [nb][128], qh
+// [nb][64], scales [nb][16] and d [nb] in planes of their own, each 16-byte
+// aligned, so every field loads whole: the two ql pieces and the qh piece as
+// 16 bytes, the half's scales as 8, d as its 2 bytes (a dword would reach
+// past the last plane's end for an odd block count).  The 4 lanes of a
+// block's units read 128 contiguous bytes of ql, 64 of qh.
+struct KQ6P {
+    static constexpr int TYPE = T_Q6_KP, BB = 210, G = 16, PG = 64, NF = 2, WAVES = 5;
+    static constexpr int RAW = 4 + 4 + 4 + 2 + 1;
+    struct R { rsrc_t q, h, s, d; };
+    QG_DEV static R rsrc(const Kq1Args &a, u32) {
+        const u32 nblk = a.range / 128u;
+        return {make_rsrc(a.W, a.range), make_rsrc(a.Ph, 64u * nblk), make_rsrc(a.Ps, 16u * nblk),
+                make_rsrc(a.Pd, 2u * nblk)};
+    }
+    // the index of the row's first block
+    QG_DEV static u32 row_base(const Kq1Args &a, int64_t rl, u32) { return (u32)rl * (a.row_bytes / BB); }
+    QG_DEV static u32 phase(u32, int) { return 0; }
+    QG_DEV static void issue(const R &r, u32 rowoff, int u, u32 (&t)[RAW]) {
+        const u32 bi = rowoff + (u32)(u >> 2);
+        const u32 n = (u32)(u >> 1) & 1u, h = (u32)u & 1u;
+        ldn<4, 0>(r.q, 128 * bi + 64 * n + 16 * h, t);
+        ldn<4, 4>(r.q, 128 * bi + 64 * n + 32 + 16 * h, t);
+        ldn<4, 8>(r.h, 64 * bi + 32 * n + 16 * h, t);
+        ldn<2, 12>(r.s, 16 * bi + 8 * n, t);
+        t[14] = __builtin_amdgcn_raw_buffer_load_b16(r.d, 2 * bi, 0, 0);
+    }
+    QG_DEV static float dot(const u32 (&t)[RAW], u32, int n, int h, const float *xs, int v0, const float *sb) {
+        u32 A[4], B[4], H[4];
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const u32 w = kq1_sel(n != 0, S[2 + (p >> 1)], S[p >> 1]);
-            dsc[p] = d * (float)(int8_t)(w >> (8 * (2 * (p & 1) + h)));
-        }
-        float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            kq1_fence(s);
-            // codes of values 32p + 16h + 4i .. +3 of the half, p = 0..3: the
-            // low / high nibbles of the two ql pieces, bit pairs p of qh
-            u32 cd[4];
-            cd[0] = opaque((A[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u));
-            cd[1] = opaque((B[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u));
-            cd[2] = opaque(((A[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u));
-            cd[3] = opaque(((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const f32x4 xv = *(const f32x4 *)(xs + kq1_xpos<PG>(v0 + 32 * p) + 4 * i);
-                s[p] = fmaf(u8_of(cd[p], 0), xv.x, s[p]);
-                s[p] = fmaf(u8_of(cd[p], 1), xv.y, s[p]);
-                s[p] = fmaf(u8_of(cd[p], 2), xv.z, s[p]);
-                s[p] = fmaf(u8_of(cd[p], 3), xv.w, s[p]);
-            }
-        }
-        kq1_fence(s);
-        // (q - 32) folded as sum(q x) - 32 sum(x)
-        float acc = 0.0f;
-#pragma unroll
-        for (int p = 0; p < 4; p++) acc = fmaf(dsc[p], fmaf(-32.0f, sb[8 * n + 2 * p + h], s[p]), acc);
-        return acc;
+        for (int i = 0; i < 4; i++) { A[i] = t[i]; B[i] = t[4 + i]; H[i] = t[8 + i]; }
+        const u32 Sn[2] = {t[12], t[13]};
+        return kq6_dot<PG>(A, B, H, Sn, h2f(t[14]), h, n, xs, v0, sb);
     }
 };
 
@@ -254,11 +312,8 @@ __global__ __launch_bounds__(64 * NW) void k_kq1(Kq1Args a) {
     const int nu = a.nu;
     const int K = (nu + L - 1) / L;   // unit slots per lane
     const u32 ph0 = (u32)((uintptr_t)a.W & 3u);
-    // (the range rounded up to whole dwords: a realigned field's last dword
-    // may hold the tensor's last bytes, and a dword load reads 0 unless all
-    // of it is in range)
-    const rsrc_t rs = make_rsrc(a.W - ph0, (a.range + ph0 + 3u) & ~3u);
-    const u32 rowoff = ph0 + (u32)rl * a.row_bytes;
+    const typename U::R rs = U::rsrc(a, ph0);
+    const u32 rowoff = U::row_base(a, rl, ph0);
 
     // x's loads, then U::NF units' loads in flight per lane (ring entry f
     // holds slots f, f + NF, ...), then x into LDS
@@ -283,7 +338,7 @@ __global__ __launch_bounds__(64 * NW) void k_kq1(Kq1Args a) {
         if constexpr (U::TYPE == T_Q4_K) {
             v = U::dot(tu, ph0, uc & 3, xs + kq1_xpos<U::PG>(64 * uc), ss + 2 * uc);
         } else {
-            const u32 ph = (rowoff + (u32)(uc >> 2) * U::BB) & 3u;
+            const u32 ph = U::phase(rowoff, uc);
             v = U::dot(tu, ph, (uc >> 1) & 1, uc & 1, xs, 64 * (uc & ~1) + 16 * (uc & 1), ss + 16 * (uc >> 2));
         }
         kq1_fence();
@@ -313,11 +368,14 @@ inline size_t kq1_lds_bytes_of(int cols) {
     return ((size_t)kq1_xstride<U::PG>(cols) + (size_t)cols / U::G) * 4;
 }
 inline size_t kq1_lds_bytes(int type, int cols) {
-    return type == T_Q4_K ? kq1_lds_bytes_of<KQ4<true>>(cols) : kq1_lds_bytes_of<KQ6>(cols);
+    return type == T_Q4_K ? kq1_lds_bytes_of<KQ4<true>>(cols)
+                          : type == T_Q6_KP ? kq1_lds_bytes_of<KQ6P>(cols) : kq1_lds_bytes_of<KQ6>(cols);
 }
 
 int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,
              int *wgs, size_t *lds);
 int launch_kq1(int type, const Kq1Args &a, hipStream_t st);
+// f32 values of nblk Q6_K blocks held in the plane layout (qg_planes.hip)
+int launch_q6k_planes_dequant(const uint8_t *P, float *out, int64_t nblk, hipStream_t st);
 
 }  // namespace qg

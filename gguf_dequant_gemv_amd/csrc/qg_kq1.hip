@@ -29,6 +29,7 @@ kq1_fn by_x(int L, int cols) {
 
 kq1_fn kq1_kernel(int type, bool aln, int L, int nw, int cols) {
     if (type == T_Q6_K) return nw == 8 ? by_x<KQ6, 8>(L, cols) : by_x<KQ6, 4>(L, cols);
+    if (type == T_Q6_KP) return nw == 8 ? by_x<KQ6P, 8>(L, cols) : by_x<KQ6P, 4>(L, cols);
     if (aln) return nw == 8 ? by_x<KQ4<true>, 8>(L, cols) : by_x<KQ4<true>, 4>(L, cols);
     return nw == 8 ? by_x<KQ4<false>, 8>(L, cols) : by_x<KQ4<false>, 4>(L, cols);
 }
@@ -58,7 +59,7 @@ int kq1_resident(kq1_fn f, int type, int nw, size_t lds, bool query) {
         return per_cu * KQ1_CU;
     }
     const int by_lds = (int)((160 * 1024) / (lds ? lds : 1));
-    const int by_waves = 4 * (type == T_Q4_K ? KQ4<true>::WAVES : KQ6::WAVES) / nw;
+    const int by_waves = 4 * (type == T_Q4_K ? KQ4<true>::WAVES : type == T_Q6_KP ? KQ6P::WAVES : KQ6::WAVES) / nw;
     per_cu = by_lds < by_waves ? by_lds : by_waves;
     return (per_cu < 1 ? 1 : per_cu) * KQ1_CU;
 }
@@ -76,8 +77,9 @@ int kq1_resident(kq1_fn f, int type, int nw, size_t lds, bool query) {
 // over the launch's rounds of max(2, the round's waves per SIMD).
 int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,
              int *wgs, size_t *lds) {
-    if ((type != T_Q4_K && type != T_Q6_K) || rows < 1 || cols < 256 || cols % 256) return QG_EINVAL;
-    if (((uintptr_t)x & 15u) || ((uintptr_t)W & 1u)) return QG_EINVAL;
+    if ((type != T_Q4_K && type != T_Q6_K && type != T_Q6_KP) || rows < 1 || cols < 256 || cols % 256)
+        return QG_EINVAL;
+    if (((uintptr_t)x & 15u) || ((uintptr_t)W & (type == T_Q6_KP ? 15u : 1u))) return QG_EINVAL;
     const size_t l = kq1_lds_bytes(type, (int)cols);
     if (cols > (1 << 20) || l > KQ1_MAX_LDS) return QG_EINVAL;
     const int bb = type == T_Q4_K ? 144 : 210;

@@ -51,7 +51,19 @@ extern "C" {
  *         value = d*sc*(q-32) per 16 values ([bonsai] dequantQ6K)
  *   F32     4 B / 1 value  : IEEE binary32 (GGML's 0), accepted by qg_gemv only:
  *         the router and shared-expert gate weights ([qwen3] matmulF32)     */
-enum qg_type { QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14 };
+enum qg_type { QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14, QG_Q6_K_PLANES = 270 };
+
+/* QG_Q6_K_PLANES: a Q6_K tensor in the device layout qg_prepare writes
+ * ([gemma4] q6kPlanes: the 210-byte blocks, which sit at 2-byte alignment,
+ * split into aligned planes at load).  A tensor of n = rows * cols / 256
+ * blocks is one buffer of 210 n bytes, 16-byte aligned, holding
+ *   ql [n][128] at byte 0, qh [n][64] at 128 n, int8 scales [n][16] at
+ *   192 n, f16 d [n] at 208 n
+ * in the blocks' row-major order: the blocks' bytes, reordered (the page
+ * widens d to f32; here it keeps its two bytes).  Not a GGUF type (GGML's
+ * Q6_K id with bit 8 set).  Accepted by qg_gemv at ntok = 1 with x 16-byte
+ * aligned and 210 n <= 2 GiB, by qg_dequant, qg_gemv_plan, qg_block_values
+ * (256) and qg_block_bytes (210); every other entry point rejects it. */
 
 /* Gated activations: act(gate) * up.
  *   QG_ACT_SILU       gate / (1 + exp(-gate))           ([qwen3] siluMulMoe)
@@ -91,8 +103,13 @@ const char *qg_strerror(int code);
  * type QG_F32: W is a plain row-major f32 matrix (4-byte aligned), the
  * router's logits and the shared expert's gate logit ([qwen3] matmulF32,
  * [qwen35] shgate binding).
+ * type QG_Q6_K_PLANES: W is a Q6_K tensor in the plane layout (16-byte
+ * aligned, 210 * rows * cols / 256 <= 2^31 bytes), one token, x 16-byte
+ * aligned; the same sum as on the blocks.
  * Errors: QG_EINVAL (type, rows<=0, cols<=0 or cols % QK, null pointer, W not
- * 2-byte aligned, x/y not 4-byte aligned), QG_ELIMIT (ntok outside 1..16). */
+ * 2-byte aligned, x/y not 4-byte aligned; for QG_Q6_K_PLANES W or x not
+ * 16-byte aligned or ntok != 1), QG_ELIMIT (ntok outside 1..16; a plane
+ * tensor over 2 GiB). */
 int qg_gemv(int type, const void *W, const float *x, float *y,
             int64_t rows, int64_t cols, int ntok, void *stream);
 
@@ -138,6 +155,22 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
  * Formulas: [bonsai] dequantQ4K / dequantQ6K, [gemma4] q4dot, [qwen3] i8at.
  * Errors: as qg_gemv (no ntok). */
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream);
+
+/* The aligned device layout of a Q6_K tensor, and back ([gemma4] q6kPlanes).
+ * qg_prepare:   src = the GGUF blocks of a rows x cols Q6_K tensor (2-byte
+ *               aligned), dst = 210 * rows * cols / 256 bytes (16-byte
+ *               aligned), written in the QG_Q6_K_PLANES layout.
+ * qg_unprepare: the inverse (src the planes, 16-byte aligned; dst the
+ *               blocks, 2-byte aligned).
+ * A byte permutation: unprepare(prepare(W)) is W byte for byte, and qg_gemv /
+ * qg_dequant give the same sums / values on either layout (up to summation
+ * order for the GEMV).  A load-time step: one launch of one thread per 2
+ * bytes.  type: QG_Q6_K, the only type with a prepared layout.
+ * Errors: QG_EINVAL (another type, rows or cols out of range, cols not a
+ * multiple of 256, a null or misaligned pointer, src and dst overlapping),
+ * QG_ELIMIT (more than 2^31 workgroups). */
+int qg_prepare(int type, const void *src, void *dst, int64_t rows, int64_t cols, void *stream);
+int qg_unprepare(int type, const void *src, void *dst, int64_t rows, int64_t cols, void *stream);
 
 /* Router: per token, the k experts with the largest logits (ties go to the
  * lower expert index), in pick order, and their weights renormalised over the

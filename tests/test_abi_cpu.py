@@ -343,3 +343,45 @@ def test_gemv_plan_multi_tile_shapes():
     assert qg.qg_gemv_plan(qg.QG_Q8_0, 1024, 2048, 8)["kind"] == 3
     with pytest.raises(qg.QgError):
         qg.qg_gemv_plan(qg.QG_Q8_0, 1024, 2047, 1)
+
+
+def test_q6k_planes_type_and_rejects():
+    """The plane layout: block sizes as Q6_K; qg_prepare / qg_unprepare take
+    Q6_K only, 16-byte-aligned planes and non-overlapping buffers; qg_gemv
+    takes it at one token with W and x 16-byte aligned; the entry points
+    that do not serve it reject it."""
+    L, P = qg.lib(), qg.QG_Q6_K_PLANES
+    assert (qg.qg_block_values(P), qg.qg_block_bytes(P)) == (256, 210)
+    n = 4 * 210 * 2   # bytes of 4 rows x 512 values
+    for f in (L.qg_prepare, L.qg_unprepare):
+        assert f(qg.QG_Q8_0, FAKE, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL       # type
+        assert f(P, FAKE, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL               # the layout is not an input type
+        assert f(qg.QG_Q6_K, FAKE, FAKE + 4096, 4, 500, None) == qg.QG_EINVAL       # cols % 256
+        assert f(qg.QG_Q6_K, FAKE, FAKE + 4096, 0, 512, None) == qg.QG_EINVAL       # rows
+        assert f(qg.QG_Q6_K, None, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL       # null
+        assert f(qg.QG_Q6_K, FAKE, FAKE + n - 16, 4, 512, None) == qg.QG_EINVAL     # overlap
+    assert L.qg_prepare(qg.QG_Q6_K, FAKE + 1, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL   # blocks odd
+    assert L.qg_prepare(qg.QG_Q6_K, FAKE + 2, FAKE + 4104, 4, 512, None) == qg.QG_EINVAL   # planes not 16-aligned
+    assert L.qg_unprepare(qg.QG_Q6_K, FAKE + 8, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL  # planes not 16-aligned
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 16, 512, 2, None) == qg.QG_EINVAL        # one token only
+    assert L.qg_gemv(P, FAKE + 2, FAKE, FAKE, 16, 512, 1, None) == qg.QG_EINVAL    # W 16-aligned
+    assert L.qg_gemv(P, FAKE, FAKE + 4, FAKE, 16, 512, 1, None) == qg.QG_EINVAL    # x 16-aligned
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 16, 500, 1, None) == qg.QG_EINVAL        # cols % 256
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 16, 512, 17, None) == qg.QG_ELIMIT
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 5 * 2 ** 20, 4096, 1, None) == qg.QG_ELIMIT   # over 2 GiB
+    assert L.qg_dequant(P, FAKE + 2, FAKE, 4, 512, None) == qg.QG_EINVAL
+    ws = L.qg_mlp_workspace_size(qg.QG_Q6_K, 512, 256, 1)
+    assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_embed(P, FAKE, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
+    assert L.qg_gemm(P, FAKE, FAKE, FAKE, 16, 512, 32, None, 0, None) == qg.QG_EINVAL
+
+
+def test_gemv_plan_q6k_planes():
+    """The plane layout takes the quarter-block kernel with the raw blocks'
+    LDS layout of x; only at one token and from a 16-byte-aligned W."""
+    p = qg.qg_gemv_plan(qg.QG_Q6_K_PLANES, 5120, 17408, 1)
+    assert p["kind"] == 4 and p["lds_bytes"] == (17408 + 4 * 272 + 4 + 17408 // 16) * 4
+    with pytest.raises(qg.QgError):
+        qg.qg_gemv_plan(qg.QG_Q6_K_PLANES, 5120, 17408, 1, w_aligned16=False)
+    with pytest.raises(qg.QgError):
+        qg.qg_gemv_plan(qg.QG_Q6_K_PLANES, 5120, 17408, 2)
