@@ -27,11 +27,17 @@ kq1_fn by_x(int L, int cols) {
     return n <= 4 ? by_lanes<U, NW, 4>(L) : n <= 9 ? by_lanes<U, NW, 9>(L) : by_lanes<U, NW, 12>(L);
 }
 
+// waves per workgroup: 4, 8, 10 or 16
+template <class U>
+kq1_fn by_waves(int L, int nw, int cols) {
+    return nw == 16 ? by_x<U, 16>(L, cols) : nw == 10 ? by_x<U, 10>(L, cols)
+         : nw == 8 ? by_x<U, 8>(L, cols) : by_x<U, 4>(L, cols);
+}
+
 kq1_fn kq1_kernel(int type, bool aln, int L, int nw, int cols) {
-    if (type == T_Q6_K) return nw == 8 ? by_x<KQ6, 8>(L, cols) : by_x<KQ6, 4>(L, cols);
-    if (type == T_Q6_KP) return nw == 8 ? by_x<KQ6P, 8>(L, cols) : by_x<KQ6P, 4>(L, cols);
-    if (aln) return nw == 8 ? by_x<KQ4<true>, 8>(L, cols) : by_x<KQ4<true>, 4>(L, cols);
-    return nw == 8 ? by_x<KQ4<false>, 8>(L, cols) : by_x<KQ4<false>, 4>(L, cols);
+    if (type == T_Q6_K) return by_waves<KQ6>(L, nw, cols);
+    if (type == T_Q6_KP) return by_waves<KQ6P>(L, nw, cols);
+    return aln ? by_waves<KQ4<true>>(L, nw, cols) : by_waves<KQ4<false>>(L, nw, cols);
 }
 
 // workgroups resident at once (all CUs): measured for the instance when a
@@ -70,11 +76,15 @@ int kq1_resident(kq1_fn f, int type, int nw, size_t lds, bool query) {
 // workgroups, LDS bytes.  0: it serves; QG_EINVAL: the caller takes the
 // block-unit kernels; QG_EHIP: a device query failed.
 //
-// The choice of lanes per row weighs the unit slots a lane runs (more lanes,
-// fewer slots) against the waves each SIMD then holds (the decode keeps the
-// vector units busy, so a SIMD's time grows with its waves once it holds two
-// or more; with fewer, latency sets it): the estimate is slots times the sum
-// over the launch's rounds of max(2, the round's waves per SIMD).
+// The choice of lanes per row and waves per workgroup weighs the unit slots
+// a lane runs (more lanes, fewer slots) against the waves the busiest SIMD
+// then holds (the decode keeps the vector units busy, so a SIMD's time grows
+// with its waves once it holds two or more; with fewer, latency sets it):
+// the estimate is slots times the sum over the launch's rounds of max(2,
+// waves on the busiest SIMD), a round's workgroups spread evenly over the
+// CUs and a workgroup's waves over the 4 SIMDs of its CU.  (At Q6_K 5120 x
+// 17408 the busiest CUs held 2 of 320 workgroups of 8 waves: 4 waves per
+// SIMD against 2.5 on average.)
 int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,
              int *wgs, size_t *lds) {
     if ((type != T_Q4_K && type != T_Q6_K && type != T_Q6_KP) || rows < 1 || cols < 256 || cols % 256)
@@ -85,29 +95,40 @@ int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x
     const int bb = type == T_Q4_K ? 144 : 210;
     if (rows * (cols / 256) * bb >= ((int64_t)1 << 32) - 8) return QG_EINVAL;
     const bool aln = ((uintptr_t)W & 3u) == 0;
-    // (8-wave workgroups for an x past 4096 values: fewer copies of it, and
-    // a thread's share of its loads within 4 float4 up to 8192 values)
-    const int w = l > 40 * 1024 || cols > 4 * 4 * 64 * 4 ? 8 : 4;
-    if (cols > 12 * 4 * 64 * w) return QG_EINVAL;
+    // (4-wave workgroups only for an x of up to 4096 values; wider ones
+    // take 8 or more waves: fewer copies of x, and a thread's share of its
+    // loads within the register bound)
+    const bool wide = l > 40 * 1024 || cols > 4 * 4 * 64 * 4;
+    static const int small_w[1] = {4}, wide_w[3] = {8, 10, 16};
+    const int *ws = wide ? wide_w : small_w;
+    const int nws = wide ? 3 : 1;
     const int nu = (int)(cols / 64);
     double best = 0.0;
-    int bl = 0;
+    int bl = 0, bw = 0;
     int64_t bwg = 0;
-    for (int L = 16; L <= 64; L *= 2) {
-        const int K = (nu + L - 1) / L;
-        const int64_t waves = (rows + 64 / L - 1) / (64 / L);
-        const int64_t g = (waves + w - 1) / w;
-        const int cap = kq1_resident(kq1_kernel(type, aln, L, w, (int)cols), type, w, l, query);
-        if (cap < 0) return QG_EHIP;
-        const int64_t full = g / cap, rest = g % cap;
-        const double per_full = (double)cap * w / (4.0 * KQ1_CU), per_rest = (double)rest * w / (4.0 * KQ1_CU);
-        const double est = K * ((double)full * (per_full > 2.0 ? per_full : 2.0) +
-                                (rest ? (per_rest > 2.0 ? per_rest : 2.0) : 0.0));
-        if (bl == 0 || est < best - 1e-9) { best = est; bl = L; bwg = g; }
+    for (int wi = 0; wi < nws; wi++) {
+        const int w = ws[wi];
+        if (cols > 12 * 4 * 64 * w) continue;
+        // the busiest SIMD's waves in a round of n workgroups
+        auto busiest = [w](int64_t n) {
+            const int64_t v = ((n + KQ1_CU - 1) / KQ1_CU * w + 3) / 4;
+            return (double)(v > 2 ? v : 2);
+        };
+        for (int L = 16; L <= 64; L *= 2) {
+            const int K = (nu + L - 1) / L;
+            const int64_t waves = (rows + 64 / L - 1) / (64 / L);
+            const int64_t g = (waves + w - 1) / w;
+            const int cap = kq1_resident(kq1_kernel(type, aln, L, w, (int)cols), type, w, l, query);
+            if (cap < 0) return QG_EHIP;
+            const int64_t full = g / cap, rest = g % cap;
+            const double est = K * ((double)full * busiest(cap) + (rest ? busiest(rest) : 0.0));
+            if (bl == 0 || est < best - 1e-9) { best = est; bl = L; bw = w; bwg = g; }
+        }
     }
+    if (bl == 0) return QG_EINVAL;
     if (bwg > 0x7fffffff) return QG_EINVAL;
     *lpr = bl;
-    *nw = w;
+    *nw = bw;
     *wgs = (int)bwg;
     *lds = l;
     return QG_OK;
