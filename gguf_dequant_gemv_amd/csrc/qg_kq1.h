@@ -185,9 +185,16 @@ struct KQ4 {
 // S the 8 int8 scales of half n, d the super scale.  xs: x in LDS, v0: the
 // row index of value 128n + 16h of the block (piece p: values v0 + 32p ..);
 // sb: the block's 16 group sums of x.
+// (v0 is 16h past a multiple of 128, so piece p's x sits a constant
+// kq6_xoff<PG>(p) floats past v0's: one address per unit, the rest in the
+// LDS reads' offsets)
+template <int PG>
+QG_DEV constexpr int kq6_xoff(int p) { return 32 * p + (PG == 64 ? 4 * (p >> 1) : 0); }
 template <int PG>
 QG_DEV float kq6_dot(const u32 (&A)[4], const u32 (&B)[4], const u32 (&H)[4], const u32 (&S)[2], float d, int h,
                      int n, const float *xs, int v0, const float *sb) {
+    static_assert(PG == 64 || PG == 128, "kq6_dot: x padded per 64 or 128 values");
+    const float *xb = xs + kq1_xpos<PG>(v0);
     // group 8n + 2p + h: int8 scale byte 2p + h of the half's scales, times d
     float dsc[4];
 #pragma unroll
@@ -205,7 +212,7 @@ QG_DEV float kq6_dot(const u32 (&A)[4], const u32 (&B)[4], const u32 (&H)[4], co
         cd[3] = opaque(((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u));
 #pragma unroll
         for (int p = 0; p < 4; p++) {
-            const f32x4 xv = *(const f32x4 *)(xs + kq1_xpos<PG>(v0 + 32 * p) + 4 * i);
+            const f32x4 xv = *(const f32x4 *)(xb + kq6_xoff<PG>(p) + 4 * i);
             s[p] = fmaf(u8_of(cd[p], 0), xv.x, s[p]);
             s[p] = fmaf(u8_of(cd[p], 1), xv.y, s[p]);
             s[p] = fmaf(u8_of(cd[p], 2), xv.z, s[p]);

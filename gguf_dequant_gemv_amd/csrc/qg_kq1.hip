@@ -109,11 +109,16 @@ int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x
     for (int wi = 0; wi < nws; wi++) {
         const int w = ws[wi];
         if (cols > 12 * 4 * 64 * w) continue;
-        // the busiest SIMD's waves in a round of n workgroups
+        // the busiest SIMD's waves in a round of n workgroups, and what the
+        // busiest CU's x staging costs in the same unit (each workgroup
+        // stages all of x: 0.2 slots per 1024 values, measured at Q6_K
+        // 5120 x 17408, where 256 workgroups of 10 waves at 32 lanes per row
+        // ran 19.5 us against 21.6 us for 512 at 64 lanes per row)
         auto busiest = [w](int64_t n) {
             const int64_t v = ((n + KQ1_CU - 1) / KQ1_CU * w + 3) / 4;
             return (double)(v > 2 ? v : 2);
         };
+        auto staging = [cols](int64_t n) { return 0.2 * (double)cols / 1024.0 * (double)((n + KQ1_CU - 1) / KQ1_CU); };
         for (int L = 16; L <= 64; L *= 2) {
             const int K = (nu + L - 1) / L;
             const int64_t waves = (rows + 64 / L - 1) / (64 / L);
@@ -121,7 +126,8 @@ int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x
             const int cap = kq1_resident(kq1_kernel(type, aln, L, w, (int)cols), type, w, l, query);
             if (cap < 0) return QG_EHIP;
             const int64_t full = g / cap, rest = g % cap;
-            const double est = K * ((double)full * busiest(cap) + (rest ? busiest(rest) : 0.0));
+            const double est = K * ((double)full * busiest(cap) + (rest ? busiest(rest) : 0.0)) +
+                               (double)full * staging(cap) + (rest ? staging(rest) : 0.0);
             if (bl == 0 || est < best - 1e-9) { best = est; bl = L; bw = w; bwg = g; }
         }
     }

@@ -316,14 +316,15 @@ def test_gemv_plan_kquant_one_token():
     """One token against K-quant rows takes the quarter-block kernel (kind 4):
     16 lanes a row for the Q4_K 17408 x 5120 shape (5 units each) in
     10-wave workgroups (436: at most 2 on a CU, 5 waves on its busiest SIMD,
-    where 8-wave ones put 3 on some CUs), 64 for the Q6_K 5120 x 17408 one
-    (4.25 units each) in 512 workgroups of 10 waves, two on every CU (x past
+    where 8-wave ones put 3 on some CUs), 32 for the Q6_K 5120 x 17408 one
+    (8.5 units each) in 256 workgroups of 10 waves, one on every CU (64
+    lanes would put two on every CU, each staging all 68 KiB of x; x past
     4096 values takes 8 or more waves a workgroup), and at any 2-byte phase
     of W; more tokens keep the block kernels."""
     p = qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1)
     assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 16, 436, 10)
     p = qg.qg_gemv_plan(qg.QG_Q6_K, 5120, 17408, 1)
-    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 64, 512, 10)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["xchunk"]) == (4, 32, 256, 10)
     # x padded by 4 floats per 64 values (+4), then one sum per 16 (Q6_K) / 32 (Q4_K) values
     assert p["lds_bytes"] == (17408 + 4 * 272 + 4 + 17408 // 16) * 4
     assert qg.qg_gemv_plan(qg.QG_Q4_K, 17408, 5120, 1)["lds_bytes"] == (5120 + 4 * 80 + 4 + 5120 // 32) * 4
