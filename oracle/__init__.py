@@ -59,6 +59,8 @@ def lib():
         L.or_argmax.argtypes = [P, i64, i32, P]
         L.or_set_threads.argtypes = [i32]
         L.or_q6k_planes.argtypes = [P, i64, P]
+        L.or_q8_0_planes.argtypes = [P, i64, P]
+        L.or_q8_0_unplanes.argtypes = [P, i64, P]
         L.or_q6k_unplanes.argtypes = [P, i64, P]
         _lib = L
     return _lib
@@ -286,6 +288,26 @@ def q6k_unplanes(planes, n):
     out = np.empty(210 * n, np.uint8)
     if lib().or_q6k_unplanes(_p(p), n, _p(out)):
         raise ValueError("or_q6k_unplanes: bad size")
+    return out
+
+
+def q8_0_planes(blocks, n):
+    """The Q8_0 plane layout of n blocks (uint8 [34 n]): codes, then scales."""
+    b = _c(blocks, np.uint8).ravel()
+    assert b.size >= 34 * n
+    out = np.empty(34 * n, np.uint8)
+    if lib().or_q8_0_planes(_p(b), n, _p(out)):
+        raise ValueError("or_q8_0_planes: bad size")
+    return out
+
+
+def q8_0_unplanes(planes, n):
+    """Blocks back from the Q8_0 plane layout."""
+    p = _c(planes, np.uint8).ravel()
+    assert p.size >= 34 * n
+    out = np.empty(34 * n, np.uint8)
+    if lib().or_q8_0_unplanes(_p(p), n, _p(out)):
+        raise ValueError("or_q8_0_unplanes: bad size")
     return out
 
 

@@ -241,6 +241,35 @@ int or_q6k_unplanes(const uint8_t *planes, int64_t n, uint8_t *blocks)
     return 0;
 }
 
+/* ----------------------------------------------------- Q8_0 planes ---- */
+/* The Q8_0 device layout the pages' engines use: the codes in a plane of
+ * their own and the scales in another ([qwen3] WGSL i8at reads value e as
+ * byte e & 3 of word e >> 2 of the code plane, scaled by the f16 of group
+ * e >> 5).  n blocks become one buffer of 34 n bytes: the codes [n][32]
+ * (int8) at 0, then the scales d [n] (f16 bytes) at 32 n.  A permutation of
+ * the bytes; or_q8_0_unplanes is its inverse. */
+int or_q8_0_planes(const uint8_t *blocks, int64_t n, uint8_t *planes)
+{
+    if (n < 0) return -1;
+    for (int64_t b = 0; b < n; b++) {
+        const uint8_t *s = blocks + 34 * b;
+        memcpy(planes + 32 * n + 2 * b, s, 2);
+        memcpy(planes + 32 * b, s + 2, 32);
+    }
+    return 0;
+}
+
+int or_q8_0_unplanes(const uint8_t *planes, int64_t n, uint8_t *blocks)
+{
+    if (n < 0) return -1;
+    for (int64_t b = 0; b < n; b++) {
+        uint8_t *d = blocks + 34 * b;
+        memcpy(d, planes + 32 * n + 2 * b, 2);
+        memcpy(d + 2, planes + 32 * b, 32);
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------ GEMV ---- */
 /* y[t][r] = sum_c W[r][c] * x[t][c] and A[t][r] = sum_c |W[r][c] * x[t][c]|,
  * for the rows listed in row_idx (all rows when row_idx is NULL).  W is

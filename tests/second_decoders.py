@@ -126,6 +126,21 @@ def dec_q6_k_planes(planes, n):
     return (d[:, None] * s * ((q4 | (h << 4)) - 32)).ravel()
 
 
+def dec_q8_0_planes(planes, n):
+    """n Q8_0 blocks in the plane layout, decoded as the [qwen3 page] i8at
+    reads its code plane: value e is byte e & 3 of little-endian word e >> 2,
+    sign-extended, times the f16 scale of group e >> 5 (here from the scale
+    plane after the codes)."""
+    p = np.ascontiguousarray(planes, np.uint8).ravel()
+    words = p[:32 * n].view("<u4").astype(np.int64)
+    e = np.arange(32 * n)
+    byte = (words[e >> 2] >> ((e & 3) * 8)) & 0xFF
+    q = np.where(byte >= 128, byte - 256, byte)
+    dd = p[32 * n:34 * n]
+    d = f16le(dd[0::2], dd[1::2])
+    return d[e >> 5] * q
+
+
 DEC = {Q8_0: dec_q8_0, Q4_0: dec_q4_0, Q4_K: dec_q4_k, Q6_K: dec_q6_k}
 
 

@@ -252,3 +252,30 @@ def test_q6k_planes_worked_offsets(orc):
 def test_q6k_planes_round_trip_random(orc):
     W = gs.rng(44).integers(0, 256, 210 * 37, dtype=np.uint8)
     assert np.array_equal(orc.q6k_unplanes(orc.q6k_planes(W, 37), 37), W)
+
+
+# ------------------------------------------------------------- Q8_0 planes --
+from second_decoders import dec_q8_0_planes  # noqa: E402
+
+
+@pytest.mark.parametrize("n", [1, 5, 80])
+def test_q8_0_planes_decode_as_the_blocks(orc, n):
+    """The code and scale planes read by the page's word-wise code-plane
+    indexer give the blocks' values exactly."""
+    W = gs.weights(orc.Q8_0, gs.rng(60 + n), 1, 32 * n)
+    P = orc.q8_0_planes(W, n)
+    assert P.size == W.size
+    assert np.array_equal(dec_q8_0_planes(P, n), orc.dequant(orc.Q8_0, W, 32 * n))
+
+
+def test_q8_0_planes_worked_offsets(orc):
+    """Three blocks whose bytes name their own place (block b, byte j holds
+    (j + 77 b) mod 256): codes row-major at 32 b + j - 2, scales after."""
+    n = 3
+    W = np.array([(j + 77 * b) % 256 for b in range(n) for j in range(34)], np.uint8)
+    P = orc.q8_0_planes(W, n)
+    byte = lambda b, j: (j + 77 * b) % 256  # noqa: E731
+    assert P[0] == byte(0, 2) and P[31] == byte(0, 33) and P[32 * 2 + 5] == byte(2, 7)
+    assert P[32 * n + 0] == byte(0, 0) and P[32 * n + 5] == byte(2, 1)
+    assert np.array_equal(np.sort(P), np.sort(W))
+    assert np.array_equal(orc.q8_0_unplanes(P, n), W)
