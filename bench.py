@@ -125,41 +125,53 @@ def _gen(seed):
 class DenseMlpHead(Workload):
     """gate||up -> SwiGLU -> down (qg_mlp) then head GEMV (qg_gemv), Q8_0, T = 1."""
 
-    def __init__(self, copies=2, H=2560, F=9728, V=151936):
+    def __init__(self, copies=2, H=2560, F=9728, V=151936, planes=True):
         import torch
         import gguf_synth as gs
         import gguf_dequant_gemv_amd as qg
         self.qg = qg
         self.H, self.F, self.V = H, F, V
+        # the tensors in the Q8_0 plane layout, prepared once as at load time
+        # (the same bytes reordered; not part of a step), or GGUF blocks
+        self.t = qg.QG_Q8_0_PLANES if planes else qg.QG_Q8_0
         self.sets = []
         for c in range(copies):
             g = _gen(100 + c)
-            self.sets.append(dict(
-                Wg=gs.device_weights(gs.Q8_0, F, H, g), Wu=gs.device_weights(gs.Q8_0, F, H, g),
-                Wd=gs.device_weights(gs.Q8_0, H, F, g), Wh=gs.device_weights(gs.Q8_0, V, H, g)))
+            W = dict(Wg=(F, H), Wu=(F, H), Wd=(H, F), Wh=(V, H))
+            for k in ("Wg", "Wu", "Wd", "Wh"):
+                W[k] = (gs.device_weights(gs.Q8_0, W[k][0], W[k][1], g), W[k])
+            if planes:
+                for k in W:
+                    src, (r, cc) = W[k]
+                    dst = torch.empty_like(src)
+                    qg.qg_prepare(qg.QG_Q8_0, src, dst, r, cc)
+                    torch.cuda.synchronize()
+                    W[k] = (dst, (r, cc))
+            self.sets.append({k: v[0] for k, v in W.items()})
         self.x = gs.device_activations(1, H, _gen(7))
         self.h = torch.empty((1, H), dtype=torch.float32, device="cuda")
         self.logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
-        self.ws = torch.empty(qg.qg_mlp_workspace_size(qg.QG_Q8_0, H, F, 1) // 4, dtype=torch.float32, device="cuda")
+        self.ws = torch.empty(qg.qg_mlp_workspace_size(self.t, H, F, 1) // 4, dtype=torch.float32, device="cuda")
         rb = gs.row_bytes(gs.Q8_0, H)
         self.mlp_bytes = 2 * F * rb + H * gs.row_bytes(gs.Q8_0, F)
         self.dominant_bytes = V * rb
         self.bytes_per_step = self.mlp_bytes + self.dominant_bytes
-        self.name = "q8_0 dense MLP decode 2560x9728 (gate||up, SwiGLU, down) + tied head 151936x2560, 1 token"
-        self.dominant = "head GEMV Q8_0 151936x2560"
-        self.key = "head_q8_0_151936x2560"
+        lay = "plane layout" if planes else "GGUF blocks"
+        self.name = ("q8_0 dense MLP decode 2560x9728 (gate||up, SwiGLU, down) + tied head 151936x2560, 1 token "
+                     "(%s)" % lay)
+        self.dominant = "head GEMV Q8_0 151936x2560 (%s)" % lay
+        self.key = "head_q8_0_planes_151936x2560" if planes else "head_q8_0_151936x2560"
         self.period = self.dominant_period = copies
 
     def step(self, i):
         qg = self.qg
         s = self.sets[i % len(self.sets)]
-        qg.qg_mlp(qg.QG_Q8_0, qg.QG_ACT_SILU, s["Wg"], s["Wu"], s["Wd"], self.H, self.F, self.x, self.h, 1,
-                  self.ws)
-        qg.qg_gemv(qg.QG_Q8_0, s["Wh"], self.h, self.logits, self.V, self.H, 1)
+        qg.qg_mlp(self.t, qg.QG_ACT_SILU, s["Wg"], s["Wu"], s["Wd"], self.H, self.F, self.x, self.h, 1, self.ws)
+        qg.qg_gemv(self.t, s["Wh"], self.h, self.logits, self.V, self.H, 1)
 
     def dominant_step(self, i):
         s = self.sets[i % len(self.sets)]
-        self.qg.qg_gemv(self.qg.QG_Q8_0, s["Wh"], self.h, self.logits, self.V, self.H, 1)
+        self.qg.qg_gemv(self.t, s["Wh"], self.h, self.logits, self.V, self.H, 1)
 
     def output(self):
         return self.logits
@@ -222,7 +234,7 @@ class GemvRot(Workload):
         if planes:
             # Q6_K in the plane layout, prepared once as at load time (the
             # same bytes reordered; not part of a step)
-            self.t = qg.QG_Q6_K_PLANES
+            self.t = qg.QG_Q6_K_PLANES if t == gs.Q6_K else qg.QG_Q8_0_PLANES
             for i, W in enumerate(self.W):
                 P = torch.empty_like(W)
                 qg.qg_prepare(t, W, P, rows, cols)
@@ -581,12 +593,19 @@ def make_workload(name, copies):
     big = 1.2e9   # bytes of distinct weight copies to rotate through (> 2x the 256 MB cache)
     if name == "1":
         return DenseMlpHead(copies=copies or 2)
+    if name == "1g":
+        return DenseMlpHead(copies=copies or 2, planes=False)
     if name == "0":
         return GemvRot(gs.Q8_0, 1024, 2048, 1, big, "q8_0 GEMV 1024x2048, 1 token")
     if name == "3a":
         return GemvRot(gs.Q4_K, 17408, 5120, 1, big, "q4_k GEMV 17408x5120, 1 token")
     if name == "3b":
         return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token (plane layout)", planes=True)
+    if name == "hq8":
+        return GemvRot(gs.Q8_0, 151936, 2560, 1, big, "q8_0 GEMV 151936x2560 (tied head), 1 token (GGUF blocks)")
+    if name == "hq8p":
+        return GemvRot(gs.Q8_0, 151936, 2560, 1, big, "q8_0 GEMV 151936x2560 (tied head), 1 token (plane layout)",
+                       planes=True)
     if name == "3bg":
         return GemvRot(gs.Q6_K, 5120, 17408, 1, big, "q6_k GEMV 5120x17408, 1 token (GGUF blocks as stored)")
     if name == "2":

@@ -11,6 +11,7 @@ import os
 
 QG_F32, QG_Q4_0, QG_Q8_0, QG_Q4_K, QG_Q6_K = 0, 2, 8, 12, 14
 QG_Q6_K_PLANES = 270   # Q6_K in the plane layout qg_prepare writes
+QG_Q8_0_PLANES = 264   # Q8_0 as a code plane and a scale plane (qg_prepare)
 QG_ACT_SILU, QG_ACT_GELU_TANH = 0, 1
 QG_OK, QG_EINVAL, QG_EABSENT, QG_EHIP, QG_ELIMIT = 0, -1, -2, -3, -4
 QG_MAX_TOKENS, QG_MAX_EXPERTS, QG_MAX_TOPK, QG_MAX_PREFILL, QG_MAX_NORMS = 16, 256, 32, 4096, 4
@@ -169,12 +170,12 @@ def qg_dequant(type, W, out, rows, cols, stream=None):
 
 
 def qg_prepare(type, src, dst, rows, cols, stream=None):
-    """GGUF Q6_K blocks -> the plane layout (QG_Q6_K_PLANES), 210 B a block."""
+    """GGUF Q6_K / Q8_0 blocks -> their plane layout (QG_Q6_K_PLANES / QG_Q8_0_PLANES)."""
     _check("qg_prepare", lib().qg_prepare(type, _ptr(src), _ptr(dst), rows, cols, _stream(stream)))
 
 
 def qg_unprepare(type, src, dst, rows, cols, stream=None):
-    """The plane layout -> GGUF Q6_K blocks (the inverse of qg_prepare)."""
+    """A plane layout -> GGUF blocks (the inverse of qg_prepare)."""
     _check("qg_unprepare", lib().qg_unprepare(type, _ptr(src), _ptr(dst), rows, cols, _stream(stream)))
 
 

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libqgemv.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ["qg_abi.hip", "qg_route.hip", "qg_block.hip", "qg_gemm.hip", "qg_moe1.hip", "qg_kq1.hip", "qg_planes.hip", "qg_inst_dequant.hip", "qg_inst_mfma.hip"] +
            ["qg_inst_%s_t%d.hip" % (t, n) for t in ("q8_0", "q4_0", "q4_k", "q6_k") for n in (1, 2, 4, 8)]]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("qg_device.h", "qg_kernels.h", "qg_inst.h", "qg_block.h", "qg_moe1.h", "qg_down1.h", "qg_kq1.h")] + [
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("qg_device.h", "qg_kernels.h", "qg_inst.h", "qg_block.h", "qg_moe1.h", "qg_down1.h", "qg_kq1.h", "qg_planes.h")] + [
     os.path.join(os.path.dirname(HERE), "include", "qgemv.h")]
 OBJDIR = os.path.join(HERE, "_build")
 

@@ -11,6 +11,7 @@
 #include "qg_kernels.h"
 #include "qg_block.h"
 #include "qg_kq1.h"
+#include "qg_planes.h"
 
 using namespace qg;
 
@@ -515,6 +516,7 @@ extern "C" {
 int qg_block_values(int type) {
     if (type == QG_F32) return 1;
     if (type == QG_Q6_K_PLANES) type = QG_Q6_K;
+    if (type == QG_Q8_0_PLANES) type = QG_Q8_0;
     TypeInfo ti;
     return type_info(type, ti) ? ti.qk : 0;
 }
@@ -522,6 +524,7 @@ int qg_block_values(int type) {
 int qg_block_bytes(int type) {
     if (type == QG_F32) return 4;
     if (type == QG_Q6_K_PLANES) type = QG_Q6_K;
+    if (type == QG_Q8_0_PLANES) type = QG_Q8_0;
     TypeInfo ti;
     return type_info(type, ti) ? ti.bytes : 0;
 }
@@ -567,6 +570,25 @@ int planes_gemv(const void *W, const float *x, float *y, int64_t rows, int64_t c
     return launch_kq1(T_Q6_KP, ka, (hipStream_t)stream);
 }
 
+// One token against a Q8_0 tensor in the plane layout (qg_planes.h)
+int q8_planes_gemv(const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
+                   void *stream) {
+    Shape s;
+    int rc = make_shape(QG_Q8_0, rows, cols, s);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > max_tok) return QG_ELIMIT;
+    if (ntok != 1 || !W || !x || !y || !aligned(W, 16) || !aligned(x, 16) || !aligned(y, 4)) return QG_EINVAL;
+    if (rows * cols >= MAX_RANGE) return QG_ELIMIT;
+    Q8pArgs qa = {};
+    qa.C = (const uint8_t *)W;
+    qa.D = (const uint8_t *)W + rows * cols;
+    qa.rows = rows;
+    qa.cols = (int)cols;
+    qa.x = x;
+    qa.y = y;
+    return launch_q8p1(qa, false, (hipStream_t)stream);
+}
+
 // qg_gemv / qg_gemm: the same sum for up to max_tok tokens
 int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok, int max_tok,
                void *ws, size_t ws_bytes, void *stream) {
@@ -583,6 +605,7 @@ int gemv_entry(int type, const void *W, const float *x, float *y, int64_t rows, 
         return QG_OK;
     }
     if (type == QG_Q6_K_PLANES) return planes_gemv(W, x, y, rows, cols, ntok, max_tok, stream);
+    if (type == QG_Q8_0_PLANES) return q8_planes_gemv(W, x, y, rows, cols, ntok, max_tok, stream);
     Shape s;
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
@@ -651,8 +674,26 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
     if (!out) return QG_EINVAL;
     const bool planes = type == QG_Q6_K_PLANES;
     Shape s;
-    int rc = make_shape(planes ? QG_Q6_K : type, rows, cols, s);
+    int rc = make_shape(planes ? QG_Q6_K : type == QG_Q8_0_PLANES ? QG_Q8_0 : type, rows, cols, s);
     if (rc) return rc;
+    if (type == QG_Q8_0_PLANES) {
+        if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
+        if (ntok != 1 || !w_aligned16) return QG_EINVAL;
+        int g = 0;
+        size_t lds = 0;
+        rc = q8p_plan(rows, cols, false, query_device != 0, &g, &lds);
+        if (rc) return rc;
+        for (int i = 0; i < 8; i++) out[i] = 0;
+        out[0] = 5;
+        out[1] = 64;
+        out[2] = 1;
+        out[3] = (int32_t)((rows + 3) / 4);
+        out[4] = query_device ? g : 0;
+        out[5] = (int32_t)lds;
+        out[6] = 4;
+        out[7] = 4;
+        return QG_OK;
+    }
     if (planes) {
         if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
         if (ntok != 1 || !w_aligned16) return QG_EINVAL;
@@ -718,6 +759,12 @@ int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, 
         if (!W || !out || !aligned(W, 16) || !aligned(out, 4)) return QG_EINVAL;
         return launch_q6k_planes_dequant((const uint8_t *)W, out, rows * s.nb, (hipStream_t)stream);
     }
+    if (type == QG_Q8_0_PLANES) {
+        const int rc = make_shape(QG_Q8_0, rows, cols, s);
+        if (rc) return rc;
+        if (!W || !out || !aligned(W, 16) || !aligned(out, 4)) return QG_EINVAL;
+        return launch_q8_planes_dequant((const uint8_t *)W, out, rows * s.nb, (hipStream_t)stream);
+    }
     int rc = make_shape(type, rows, cols, s);
     if (rc) return rc;
     if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;
@@ -752,6 +799,7 @@ size_t mlp_scratch_bytes(int type, int64_t hidden, int64_t ff, int ntok) {
 
 size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok) {
     if (hidden <= 0 || ff <= 0 || ntok < 1 || ntok > QG_MAX_PREFILL) return 0;
+    if (type == QG_Q8_0_PLANES) type = QG_Q8_0;   // (one token: gu and act only)
     return align256((size_t)ntok * 2 * (size_t)ff * sizeof(float)) + align256((size_t)ntok * (size_t)ff * sizeof(float)) +
            mlp_scratch_bytes(type, hidden, ff, ntok);
 }
@@ -776,12 +824,57 @@ int mlp_check(int type, int act, const void *W_gate, const void *W_up, const voi
     if (workspace_bytes < qg_mlp_workspace_size(type, hidden, ff, ntok)) return QG_EINVAL;
     return QG_OK;
 }
+// One token through a gated MLP whose three tensors are Q8_0 planes: the
+// gated plane launch (gate and up rows, act(g) * u, g and u in gu), then the
+// plane GEMV of down on the activations
+int q8_planes_mlp(int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
+                  const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
+    Shape s_g, s_dn;
+    int rc = make_shape(QG_Q8_0, ff, hidden, s_g);
+    if (rc) return rc;
+    rc = make_shape(QG_Q8_0, hidden, ff, s_dn);
+    if (rc) return rc;
+    if (ntok < 1 || ntok > QG_MAX_PREFILL) return QG_ELIMIT;
+    if (ntok != 1 || (act != QG_ACT_SILU && act != QG_ACT_GELU_TANH)) return QG_EINVAL;
+    if (hidden > Q8P_MAX_COLS || ff > Q8P_MAX_COLS) return QG_EINVAL;
+    if (ff * hidden >= MAX_RANGE) return QG_ELIMIT;
+    if (!W_gate || !W_up || !W_down || !x || !y || !workspace || !aligned(W_gate, 16) || !aligned(W_up, 16) ||
+        !aligned(W_down, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(workspace, 256))
+        return QG_EINVAL;
+    if (workspace_bytes < qg_mlp_workspace_size(QG_Q8_0_PLANES, hidden, ff, 1)) return QG_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    float *gu = (float *)workspace;
+    float *av = (float *)((uint8_t *)workspace + align256((size_t)2 * (size_t)ff * sizeof(float)));
+    Q8pArgs g = {};
+    g.C = (const uint8_t *)W_gate;
+    g.D = (const uint8_t *)W_gate + ff * hidden;
+    g.C2 = (const uint8_t *)W_up;
+    g.D2 = (const uint8_t *)W_up + ff * hidden;
+    g.rows = ff;
+    g.cols = (int)hidden;
+    g.x = x;
+    g.y = av;
+    g.y2 = gu;
+    g.glu = act == QG_ACT_GELU_TANH ? XM_GELU : XM_SILU;
+    rc = launch_q8p1(g, true, st);
+    if (rc) return rc;
+    Q8pArgs d = {};
+    d.C = (const uint8_t *)W_down;
+    d.D = (const uint8_t *)W_down + hidden * ff;
+    d.rows = hidden;
+    d.cols = (int)ff;
+    d.x = av;
+    d.y = y;
+    return launch_q8p1(d, false, st);
+}
 }  // namespace
 
 extern "C" {
 
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down, int64_t hidden, int64_t ff,
            const float *x, float *y, int ntok, void *workspace, size_t workspace_bytes, void *stream) {
+    if (type == QG_Q8_0_PLANES)
+        return q8_planes_mlp(act, W_gate, W_up, W_down, hidden, ff, x, y, ntok, workspace, workspace_bytes, stream);
     int rc = mlp_check(type, act, W_gate, W_up, W_down, hidden, ff, x, y, ntok, workspace, workspace_bytes);
     if (rc) return rc;
     Shape s_g, s_dn;

@@ -382,7 +382,5 @@ inline size_t kq1_lds_bytes(int type, int cols) {
 int kq1_plan(int type, int64_t rows, int64_t cols, const void *W, const float *x, bool query, int *lpr, int *nw,
              int *wgs, size_t *lds);
 int launch_kq1(int type, const Kq1Args &a, hipStream_t st);
-// f32 values of nblk Q6_K blocks held in the plane layout (qg_planes.hip)
-int launch_q6k_planes_dequant(const uint8_t *P, float *out, int64_t nblk, hipStream_t st);
 
 }  // namespace qg

@@ -51,7 +51,10 @@ extern "C" {
  *         value = d*sc*(q-32) per 16 values ([bonsai] dequantQ6K)
  *   F32     4 B / 1 value  : IEEE binary32 (GGML's 0), accepted by qg_gemv only:
  *         the router and shared-expert gate weights ([qwen3] matmulF32)     */
-enum qg_type { QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14, QG_Q6_K_PLANES = 270 };
+enum qg_type {
+    QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14,
+    QG_Q8_0_PLANES = 264, QG_Q6_K_PLANES = 270
+};
 
 /* QG_Q6_K_PLANES: a Q6_K tensor in the device layout qg_prepare writes
  * ([gemma4] q6kPlanes: the 210-byte blocks, which sit at 2-byte alignment,
@@ -63,7 +66,18 @@ enum qg_type { QG_F32 = 0, QG_Q4_0 = 2, QG_Q8_0 = 8, QG_Q4_K = 12, QG_Q6_K = 14,
  * widens d to f32; here it keeps its two bytes).  Not a GGUF type (GGML's
  * Q6_K id with bit 8 set).  Accepted by qg_gemv at ntok = 1 with x 16-byte
  * aligned and 210 n <= 2 GiB, by qg_dequant, qg_gemv_plan, qg_block_values
- * (256) and qg_block_bytes (210); every other entry point rejects it. */
+ * (256) and qg_block_bytes (210); every other entry point rejects it.
+ *
+ * QG_Q8_0_PLANES: a Q8_0 tensor in the layout qg_prepare writes ([qwen3]
+ * WGSL i8at reads Q8_0 from a code plane and per-group scales): for rows x
+ * cols values, one buffer of 34 rows cols / 32 bytes, 16-byte aligned:
+ *   the int8 codes [rows][cols] at byte 0, then the f16 scales
+ *   [rows][cols / 32] at byte rows * cols
+ * (the blocks' bytes, reordered: a row of codes is cols contiguous bytes,
+ * whole 128-byte lines when cols is a multiple of 128).  Accepted by qg_gemv
+ * at ntok = 1 with x 16-byte aligned, rows * cols < 2^31 and cols <= 12288,
+ * by qg_dequant, qg_gemv_plan (kind 5), qg_block_values (32) and
+ * qg_block_bytes (34); every other entry point rejects it. */
 
 /* Gated activations: act(gate) * up.
  *   QG_ACT_SILU       gate / (1 + exp(-gate))           ([qwen3] siluMulMoe)
@@ -105,11 +119,12 @@ const char *qg_strerror(int code);
  * [qwen35] shgate binding).
  * type QG_Q6_K_PLANES: W is a Q6_K tensor in the plane layout (16-byte
  * aligned, 210 * rows * cols / 256 <= 2^31 bytes), one token, x 16-byte
- * aligned; the same sum as on the blocks.
+ * aligned; the same sum as on the blocks.  QG_Q8_0_PLANES likewise (rows *
+ * cols < 2^31, cols <= 12288).
  * Errors: QG_EINVAL (type, rows<=0, cols<=0 or cols % QK, null pointer, W not
- * 2-byte aligned, x/y not 4-byte aligned; for QG_Q6_K_PLANES W or x not
- * 16-byte aligned or ntok != 1), QG_ELIMIT (ntok outside 1..16; a plane
- * tensor over 2 GiB). */
+ * 2-byte aligned, x/y not 4-byte aligned; for the plane layouts W or x not
+ * 16-byte aligned, ntok != 1, or Q8_0 planes with cols > 12288), QG_ELIMIT
+ * (ntok outside 1..16; a plane tensor over 2 GiB). */
 int qg_gemv(int type, const void *W, const float *x, float *y,
             int64_t rows, int64_t cols, int ntok, void *stream);
 
@@ -141,7 +156,10 @@ int qg_gemm(int type, const void *W, const float *x, float *y,
  * device query, 0 when query_device is 0; kind 4: one tile each), [5] dynamic
  * LDS bytes, [6] weight stages in flight per wave (kind 4: units in flight per
  * lane), [7] x chunk (row elements staged at a time, 0 = all of x; kind 4:
- * waves per workgroup).
+ * waves per workgroup).  Kind 5: one token against Q8_0 planes, a wave
+ * walking rows in 16-byte code pieces ([1] 64 lanes a row, [3] row groups
+ * of 4, [4] workgroups, [6] pieces in flight per lane, [7] waves per
+ * workgroup).
  * The plan of the first launch of the call (launches cover at most 2 GiB of
  * weights each).  w_aligned16: W would start 16-byte aligned.
  * Errors: as qg_gemv, QG_EINVAL for a null out, QG_EHIP when the device query
@@ -156,16 +174,17 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
  * Errors: as qg_gemv (no ntok). */
 int qg_dequant(int type, const void *W, float *out, int64_t rows, int64_t cols, void *stream);
 
-/* The aligned device layout of a Q6_K tensor, and back ([gemma4] q6kPlanes).
- * qg_prepare:   src = the GGUF blocks of a rows x cols Q6_K tensor (2-byte
- *               aligned), dst = 210 * rows * cols / 256 bytes (16-byte
- *               aligned), written in the QG_Q6_K_PLANES layout.
+/* The aligned device layouts of Q6_K and Q8_0 tensors, and back ([gemma4]
+ * q6kPlanes, [qwen3] i8at's code plane).
+ * qg_prepare:   src = the GGUF blocks of a rows x cols Q6_K or Q8_0 tensor
+ *               (2-byte aligned), dst = as many bytes (16-byte aligned),
+ *               written in the QG_Q6_K_PLANES / QG_Q8_0_PLANES layout.
  * qg_unprepare: the inverse (src the planes, 16-byte aligned; dst the
  *               blocks, 2-byte aligned).
  * A byte permutation: unprepare(prepare(W)) is W byte for byte, and qg_gemv /
  * qg_dequant give the same sums / values on either layout (up to summation
  * order for the GEMV).  A load-time step: one launch of one thread per 2
- * bytes.  type: QG_Q6_K, the only type with a prepared layout.
+ * bytes.  type: QG_Q6_K or QG_Q8_0, the types with a prepared layout.
  * Errors: QG_EINVAL (another type, rows or cols out of range, cols not a
  * multiple of 256, a null or misaligned pointer, src and dst overlapping),
  * QG_ELIMIT (more than 2^31 workgroups). */

@@ -350,14 +350,14 @@ def test_gemv_plan_multi_tile_shapes():
 
 def test_q6k_planes_type_and_rejects():
     """The plane layout: block sizes as Q6_K; qg_prepare / qg_unprepare take
-    Q6_K only, 16-byte-aligned planes and non-overlapping buffers; qg_gemv
+    Q6_K (and Q8_0) blocks, 16-byte-aligned planes and non-overlapping buffers; qg_gemv
     takes it at one token with W and x 16-byte aligned; the entry points
     that do not serve it reject it."""
     L, P = qg.lib(), qg.QG_Q6_K_PLANES
     assert (qg.qg_block_values(P), qg.qg_block_bytes(P)) == (256, 210)
     n = 4 * 210 * 2   # bytes of 4 rows x 512 values
     for f in (L.qg_prepare, L.qg_unprepare):
-        assert f(qg.QG_Q8_0, FAKE, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL       # type
+        assert f(qg.QG_Q4_K, FAKE, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL       # type
         assert f(P, FAKE, FAKE + 4096, 4, 512, None) == qg.QG_EINVAL               # the layout is not an input type
         assert f(qg.QG_Q6_K, FAKE, FAKE + 4096, 4, 500, None) == qg.QG_EINVAL       # cols % 256
         assert f(qg.QG_Q6_K, FAKE, FAKE + 4096, 0, 512, None) == qg.QG_EINVAL       # rows
@@ -388,3 +388,33 @@ def test_gemv_plan_q6k_planes():
         qg.qg_gemv_plan(qg.QG_Q6_K_PLANES, 5120, 17408, 1, w_aligned16=False)
     with pytest.raises(qg.QgError):
         qg.qg_gemv_plan(qg.QG_Q6_K_PLANES, 5120, 17408, 2)
+
+
+def test_q8_0_planes_type_and_rejects():
+    """The Q8_0 plane layout: block sizes as Q8_0; qg_prepare takes Q8_0; the
+    GEMV and the gated MLP take it at one token with W and x 16-byte aligned
+    and up to 12288 values a row (plan kind 5); the entry points that do not
+    serve it reject it."""
+    L, P = qg.lib(), qg.QG_Q8_0_PLANES
+    assert (qg.qg_block_values(P), qg.qg_block_bytes(P)) == (32, 34)
+    assert L.qg_prepare(qg.QG_Q8_0, FAKE, FAKE + 4096, 4, 48, None) == qg.QG_EINVAL    # cols % 32
+    assert L.qg_prepare(qg.QG_Q8_0, FAKE + 2, FAKE + 4104, 4, 64, None) == qg.QG_EINVAL   # planes not 16-aligned
+    assert L.qg_prepare(qg.QG_Q8_0, FAKE, FAKE + 64, 4, 64, None) == qg.QG_EINVAL      # overlap (272 B)
+    assert L.qg_unprepare(P, FAKE, FAKE + 4096, 4, 64, None) == qg.QG_EINVAL
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 16, 512, 2, None) == qg.QG_EINVAL        # one token only
+    assert L.qg_gemv(P, FAKE + 2, FAKE, FAKE, 16, 512, 1, None) == qg.QG_EINVAL    # W 16-aligned
+    assert L.qg_gemv(P, FAKE, FAKE + 4, FAKE, 16, 512, 1, None) == qg.QG_EINVAL    # x 16-aligned
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 16, 12288 + 32, 1, None) == qg.QG_EINVAL   # row too long
+    assert L.qg_gemv(P, FAKE, FAKE, FAKE, 2 ** 20, 4096, 1, None) == qg.QG_ELIMIT    # 2^32 codes
+    assert L.qg_dequant(P, FAKE + 2, FAKE, 4, 64, None) == qg.QG_EINVAL
+    # qg_mlp takes the layout at one token, all of W, x 16-byte aligned
+    ws = L.qg_mlp_workspace_size(P, 512, 256, 1)
+    assert ws == L.qg_mlp_workspace_size(qg.QG_Q8_0, 512, 256, 1)
+    assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE, FAKE, 2, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_mlp(P, 0, FAKE, FAKE + 2, FAKE, 512, 256, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE + 4, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
+    assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE, FAKE, 1, FAKE, ws - 256, None) == qg.QG_EINVAL
+    assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 12288 + 32, FAKE, FAKE, 1, FAKE, 1 << 30, None) == qg.QG_EINVAL
+    assert L.qg_embed(P, FAKE, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
+    p = qg.qg_gemv_plan(P, 151936, 2560, 1)
+    assert p["kind"] == 5 and p["lds_bytes"] == (2560 + 2560 // 8) * 4
