@@ -509,7 +509,7 @@ class HeadPick(Workload):
     next step (qg_gemv, qg_argmax_embed: the pick and the gather in two
     launches), rotating weight copies."""
 
-    def __init__(self, t, V, H, cap, emb_scale, total_bytes, label):
+    def __init__(self, t, V, H, cap, emb_scale, total_bytes, label, planes=False):
         import torch
         import gguf_synth as gs
         import gguf_dequant_gemv_amd as qg
@@ -518,6 +518,15 @@ class HeadPick(Workload):
         copies = max(2, int(total_bytes // wb))
         g = _gen(1000 + t)
         self.W = [gs.device_weights(t, V, H, g) for _ in range(copies)]
+        if planes:
+            # the table in its plane layout, prepared once as at load time
+            # (head GEMV and embedding gather both read it)
+            for i, W in enumerate(self.W):
+                P = torch.empty_like(W)
+                qg.qg_prepare(t, W, P, V, H)
+                torch.cuda.synchronize()
+                self.W[i] = P
+            self.t = qg.QG_Q8_0_PLANES if t == gs.Q8_0 else qg.QG_Q6_K_PLANES
         self.x = gs.device_activations(1, H, g)
         self.logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
         self.idx = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -526,8 +535,8 @@ class HeadPick(Workload):
         self.bytes_per_step = wb + gs.row_bytes(t, H)
         self.dominant_bytes = wb
         self.name = label
-        self.dominant = "head GEMV %s %dx%d" % (gs.NAMES[t], V, H)
-        self.key = "head_pick_%s_%dx%d" % (gs.NAMES[t].lower(), V, H)
+        self.dominant = "head GEMV %s %dx%d%s" % (gs.NAMES[t], V, H, " (plane layout)" if planes else "")
+        self.key = "head_pick_%s%s_%dx%d" % (gs.NAMES[t].lower(), "_planes" if planes else "", V, H)
         self.period = self.dominant_period = copies
 
     def step(self, i):
@@ -596,7 +605,9 @@ def make_workload(name, copies):
     if name == "1g":
         return DenseMlpHead(copies=copies or 2, planes=False)
     if name == "0":
-        return GemvRot(gs.Q8_0, 1024, 2048, 1, big, "q8_0 GEMV 1024x2048, 1 token")
+        return GemvRot(gs.Q8_0, 1024, 2048, 1, big, "q8_0 GEMV 1024x2048, 1 token (plane layout)", planes=True)
+    if name == "0g":
+        return GemvRot(gs.Q8_0, 1024, 2048, 1, big, "q8_0 GEMV 1024x2048, 1 token (GGUF blocks)")
     if name == "3a":
         return GemvRot(gs.Q4_K, 17408, 5120, 1, big, "q4_k GEMV 17408x5120, 1 token")
     if name == "3b":
@@ -622,12 +633,14 @@ def make_workload(name, copies):
         return GemmaBlock(16 if name == "gblkt16" else 1)
     if name in ("p64", "p256"):
         return PrefillMlp(int(name[1:]))
-    if name == "head8":
+    if name in ("head8", "head8g"):
         return HeadPick(gs.Q8_0, 151936, 2560, 0.0, 1.0, big,
-                        "q8_0 head 151936x2560 + argmax + tied embedding row, 1 token")
-    if name == "head6":
+                        "q8_0 head 151936x2560 + argmax + tied embedding row, 1 token (%s)"
+                        % ("GGUF blocks" if name == "head8g" else "plane layout"), planes=name == "head8")
+    if name in ("head6", "head6g"):
         return HeadPick(gs.Q6_K, 262144, 2816, 30.0, float(2816 ** 0.5), big,
-                        "q6_k head 262144x2816 + soft cap 30 + argmax + scaled tied embedding row, 1 token")
+                        "q6_k head 262144x2816 + soft cap 30 + argmax + scaled tied embedding row, 1 token (%s)"
+                        % ("GGUF blocks" if name == "head6g" else "plane layout"), planes=name == "head6")
     raise SystemExit("unknown config " + name)
 
 

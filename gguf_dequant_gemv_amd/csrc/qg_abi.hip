@@ -1398,10 +1398,12 @@ int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float
 int qg_embed(int type, const void *W, int64_t rows, int64_t cols, const int32_t *tokens, int ntok, float scale,
              float *out, void *stream) {
     Shape s;
-    int rc = make_shape(type, rows, cols, s);
+    const bool planes = type == QG_Q8_0_PLANES || type == QG_Q6_K_PLANES;
+    int rc = make_shape(type == QG_Q8_0_PLANES ? QG_Q8_0 : type == QG_Q6_K_PLANES ? QG_Q6_K : type, rows, cols, s);
     if (rc) return rc;
     if (ntok < 1 || ntok > 65535) return QG_ELIMIT;
-    if (!W || !tokens || !out || !aligned(W, 2) || !aligned(tokens, 4) || !aligned(out, 4)) return QG_EINVAL;
+    if (!W || !tokens || !out || !aligned(W, planes ? 16 : 2) || !aligned(tokens, 4) || !aligned(out, 4))
+        return QG_EINVAL;
     return launch_embed(type, (const uint8_t *)W, rows, (int)s.cols, s.row_bytes, tokens, ntok, scale, out,
                         (hipStream_t)stream);
 }
@@ -1435,9 +1437,10 @@ int qg_argmax_embed(float *logits, int64_t n, int ntok, float softcap, int32_t *
     const size_t need = qg_argmax_workspace_size(n, ntok);
     if (workspace_bytes < need) return QG_EINVAL;
     Shape s;
-    int rc = make_shape(type, rows, cols, s);
+    const bool planes = type == QG_Q8_0_PLANES || type == QG_Q6_K_PLANES;
+    int rc = make_shape(type == QG_Q8_0_PLANES ? QG_Q8_0 : type == QG_Q6_K_PLANES ? QG_Q6_K : type, rows, cols, s);
     if (rc) return rc;
-    if (!W || !out || !aligned(W, 2) || !aligned(out, 4)) return QG_EINVAL;
+    if (!W || !out || !aligned(W, planes ? 16 : 2) || !aligned(out, 4)) return QG_EINVAL;
     float *pv = (float *)workspace;
     int32_t *pi = (int32_t *)((uint8_t *)workspace + need / 2);
     return launch_argmax_embed(logits, n, ntok, softcap, pv, pi, idx, type, (const uint8_t *)W, rows, (int)s.cols,

@@ -477,6 +477,44 @@ QG_DEV void embed_row(const uint8_t *W, int64_t rows, int cols, int64_t row_byte
     embed_part<U>(p, w, scale, o);
 }
 
+// ---- rows of the plane layouts: one thread per value ----------------------
+// value c of row id of a rows x cols tensor held in planes, as qg_dequant
+// gives it: Q8_0 d * code ([qwen3] i8at's code plane), Q6_K (d * scale) *
+// (q - 32) ([bonsai] dequantQ6K's fields in their planes); exact in f32
+template <int TY>
+QG_DEV float plane_value(const uint8_t *W, int64_t rows, int cols, int64_t id, int c) {
+    if constexpr (TY == T_Q8_0P) {
+        const int64_t nb = cols / 32;
+        const uint8_t *D = W + rows * (int64_t)cols;
+        return h2f(*(const uint16_t *)(D + 2 * (id * nb + c / 32))) * (float)(int8_t)W[id * (int64_t)cols + c];
+    } else {
+        const int64_t n = rows * (int64_t)(cols / 256), b = id * (cols / 256) + c / 256;
+        const int t = c & 255, half = t >> 7, r = t & 127, p = r >> 5, l = r & 31;
+        const int lo = W[128 * b + 64 * half + l + 32 * (p & 1)];
+        const int q4 = p >= 2 ? lo >> 4 : lo & 15;
+        const int hb = (W[128 * n + 64 * b + 32 * half + l] >> (2 * p)) & 3;
+        const int sc = (int8_t)W[192 * n + 16 * b + 8 * half + (l >> 4) + 2 * p];
+        const float d = h2f(*(const uint16_t *)(W + 208 * n + 2 * b));
+        return (d * (float)sc) * (float)((q4 | (hb << 4)) - 32);
+    }
+}
+
+// this workgroup's 256 values of row id of token blockIdx.y (an id outside
+// the table gives NaN, as embed_row)
+template <int TY>
+QG_DEV void embed_row_planes(const uint8_t *W, int64_t rows, int cols, int32_t id, float scale, float *out) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= cols) return;
+    float *o = out + (int64_t)blockIdx.y * cols + c;
+    *o = id < 0 || id >= rows ? __builtin_nanf("") : plane_value<TY>(W, rows, cols, id, c) * scale;
+}
+
+template <int TY>
+__global__ __launch_bounds__(256) void k_embed_planes(const uint8_t *W, int64_t rows, int cols, const int32_t *tok,
+                                                      float scale, float *out) {
+    embed_row_planes<TY>(W, rows, cols, tok[blockIdx.y], scale, out);
+}
+
 template <class U>
 __global__ __launch_bounds__(256) void k_embed(const uint8_t *W, int64_t rows, int cols, int64_t row_bytes,
                                                const int32_t *tok, float scale, float *out) {
@@ -495,6 +533,14 @@ static int launch_embed_t(const uint8_t *W, int64_t rows, int cols, int64_t row_
 
 int launch_embed(int type, const uint8_t *W, int64_t rows, int cols, int64_t row_bytes, const int32_t *tok,
                  int ntok, float scale, float *out, hipStream_t st) {
+    if (type == T_Q8_0P || type == T_Q6_KP) {
+        const dim3 grid((unsigned)((cols + 255) / 256), ntok);
+        if (type == T_Q8_0P)
+            hipLaunchKernelGGL(k_embed_planes<T_Q8_0P>, grid, dim3(256), 0, st, W, rows, cols, tok, scale, out);
+        else
+            hipLaunchKernelGGL(k_embed_planes<T_Q6_KP>, grid, dim3(256), 0, st, W, rows, cols, tok, scale, out);
+        return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+    }
     switch (type) {
     case T_Q8_0: return launch_embed_t<UQ8_0B>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
     case T_Q4_0: return launch_embed_t<UQ4_0B>(W, rows, cols, row_bytes, tok, ntok, scale, out, st);
@@ -613,6 +659,23 @@ __global__ __launch_bounds__(256) void k_argmax_embed(const float *pv, const int
     embed_row<U>(W, rows, cols, row_bytes, s_id, scale, out);
 }
 
+// the same with the row gathered from a plane layout
+template <int TY>
+__global__ __launch_bounds__(256) void k_argmax_embed_planes(const float *pv, const int32_t *pi, int G, int32_t *idx,
+                                                             const uint8_t *W, int64_t rows, int cols, float scale,
+                                                             float *out) {
+    __shared__ int s_id;
+    if (threadIdx.x < 64) {
+        const int id = argmax_final_wave(pv, pi, G, blockIdx.y, threadIdx.x);
+        if (threadIdx.x == 0) {
+            s_id = id;
+            if (blockIdx.x == 0) idx[blockIdx.y] = id;
+        }
+    }
+    __syncthreads();
+    embed_row_planes<TY>(W, rows, cols, s_id, scale, out);
+}
+
 __global__ __launch_bounds__(64) void k_argmax_final(const float *pv, const int32_t *pi, int G, int32_t *idx) {
     const int t = blockIdx.x, lane = threadIdx.x;
     float bv = 0.0f;
@@ -719,6 +782,16 @@ int launch_argmax_embed(float *l, int64_t n, int ntok, float cap, float *pv, int
     const float inv = cap > 0.0f ? (float)(1.0 / (double)cap) : 0.0f;
     hipLaunchKernelGGL(k_argmax_part, dim3(G, ntok), dim3(256), 0, st, l, n, span, cap, inv, pv, pi);
     if (hipGetLastError() != hipSuccess) return QG_EHIP;
+    if (type == T_Q8_0P || type == T_Q6_KP) {
+        const dim3 grid((unsigned)((cols + 255) / 256), ntok);
+        if (type == T_Q8_0P)
+            hipLaunchKernelGGL(k_argmax_embed_planes<T_Q8_0P>, grid, dim3(256), 0, st, pv, pi, G, idx, W, rows, cols,
+                               scale, out);
+        else
+            hipLaunchKernelGGL(k_argmax_embed_planes<T_Q6_KP>, grid, dim3(256), 0, st, pv, pi, G, idx, W, rows, cols,
+                               scale, out);
+        return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
+    }
     switch (type) {
     case T_Q8_0: return launch_argmax_embed_t<UQ8_0B>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);
     case T_Q4_0: return launch_argmax_embed_t<UQ4_0B>(G, pv, pi, idx, W, rows, cols, row_bytes, ntok, scale, out, st);

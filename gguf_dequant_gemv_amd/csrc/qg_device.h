@@ -31,7 +31,8 @@ typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-enum { T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14, T_Q6_KP = 270 };   // T_Q6_KP: Q6_K in planes
+// T_Q8_0P / T_Q6_KP: Q8_0 / Q6_K in their plane layouts
+enum { T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14, T_Q8_0P = 264, T_Q6_KP = 270 };
 
 // ---------------------------------------------------------------- scalars --
 QG_DEV float h2f(u32 bits) {  // low 16 bits: IEEE binary16 -> f32 (exact)

@@ -65,8 +65,9 @@ enum qg_type {
  * in the blocks' row-major order: the blocks' bytes, reordered (the page
  * widens d to f32; here it keeps its two bytes).  Not a GGUF type (GGML's
  * Q6_K id with bit 8 set).  Accepted by qg_gemv at ntok = 1 with x 16-byte
- * aligned and 210 n <= 2 GiB, by qg_dequant, qg_gemv_plan, qg_block_values
- * (256) and qg_block_bytes (210); every other entry point rejects it.
+ * aligned and 210 n <= 2 GiB, by qg_dequant, qg_embed, qg_argmax_embed,
+ * qg_gemv_plan, qg_block_values (256) and qg_block_bytes (210); every other
+ * entry point rejects it.
  *
  * QG_Q8_0_PLANES: a Q8_0 tensor in the layout qg_prepare writes ([qwen3]
  * WGSL i8at reads Q8_0 from a code plane and per-group scales): for rows x
@@ -76,8 +77,9 @@ enum qg_type {
  * (the blocks' bytes, reordered: a row of codes is cols contiguous bytes,
  * whole 128-byte lines when cols is a multiple of 128).  Accepted by qg_gemv
  * at ntok = 1 with x 16-byte aligned, rows * cols < 2^31 and cols <= 12288,
- * by qg_dequant, qg_gemv_plan (kind 5), qg_block_values (32) and
- * qg_block_bytes (34); every other entry point rejects it. */
+ * by qg_mlp at ntok = 1 (all three tensors in the layout), by qg_dequant,
+ * qg_embed, qg_argmax_embed, qg_gemv_plan (kind 5), qg_block_values (32)
+ * and qg_block_bytes (34); every other entry point rejects it. */
 
 /* Gated activations: act(gate) * up.
  *   QG_ACT_SILU       gate / (1 + exp(-gate))           ([qwen3] siluMulMoe)
@@ -220,8 +222,12 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok,
  * 256-byte boundary): documented intermediates, useful for staged checking.
  * Prefill chunks and split small batches (as qg_gemm) may use more scratch
  * after a (unspecified contents).
+ * type QG_Q8_0_PLANES (all three tensors in that layout, 16-byte aligned, x
+ * too): one token, the gated plane launch and the plane GEMV of down; the
+ * workspace and its gu / a parts as for QG_Q8_0.
  * Errors: as qg_gemv for both shapes, QG_EINVAL for a short workspace or an
- * unknown act. */
+ * unknown act (for QG_Q8_0_PLANES also ntok != 1, or hidden or ff over
+ * 12288). */
 size_t qg_mlp_workspace_size(int type, int64_t hidden, int64_t ff, int ntok);
 int qg_mlp(int type, int act, const void *W_gate, const void *W_up, const void *W_down,
            int64_t hidden, int64_t ff, const float *x, float *y, int ntok,
@@ -422,7 +428,9 @@ int qg_post_ffn(const float *mlp, const float *moe, const float *w1, const float
  * each value the f32 nearest its exact value (as qg_dequant), multiplied by
  * scale in f32 ([qwen3] WGSL embedQ8 with scale 1, [gemma4] embedQ6K with its
  * scale).  tokens: [ntok] int32 on the device; a token outside [0, rows) reads
- * nothing and gets a row of NaN.  out: [ntok][cols].
+ * nothing and gets a row of NaN.  out: [ntok][cols].  A table in a plane
+ * layout (QG_Q8_0_PLANES, QG_Q6_K_PLANES; 16-byte aligned) gives the same
+ * values, gathered one thread a value.
  * Errors: as qg_dequant; QG_ELIMIT for ntok outside 1..65535. */
 int qg_embed(int type, const void *W, int64_t rows, int64_t cols, const int32_t *tokens, int ntok, float scale,
              float *out, void *stream);

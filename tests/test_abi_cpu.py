@@ -375,7 +375,8 @@ def test_q6k_planes_type_and_rejects():
     assert L.qg_dequant(P, FAKE + 2, FAKE, 4, 512, None) == qg.QG_EINVAL
     ws = L.qg_mlp_workspace_size(qg.QG_Q6_K, 512, 256, 1)
     assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
-    assert L.qg_embed(P, FAKE, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
+    # embedding rows from the planes: 16-byte aligned tables only
+    assert L.qg_embed(P, FAKE + 2, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
     assert L.qg_gemm(P, FAKE, FAKE, FAKE, 16, 512, 32, None, 0, None) == qg.QG_EINVAL
 
 
@@ -415,6 +416,7 @@ def test_q8_0_planes_type_and_rejects():
     assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE + 4, FAKE, 1, FAKE, ws, None) == qg.QG_EINVAL
     assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 256, FAKE, FAKE, 1, FAKE, ws - 256, None) == qg.QG_EINVAL
     assert L.qg_mlp(P, 0, FAKE, FAKE, FAKE, 512, 12288 + 32, FAKE, FAKE, 1, FAKE, 1 << 30, None) == qg.QG_EINVAL
-    assert L.qg_embed(P, FAKE, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
+    # embedding rows from the planes: 16-byte aligned tables only
+    assert L.qg_embed(P, FAKE + 2, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
     p = qg.qg_gemv_plan(P, 151936, 2560, 1)
     assert p["kind"] == 5 and p["lds_bytes"] == (2560 + 2560 // 8) * 4

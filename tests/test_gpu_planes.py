@@ -242,3 +242,44 @@ def test_q8_planes_mlp_stagewise(orc, act, H, F):
         gu[0, :F].astype(np.float64) * gu[0, F:].astype(np.float64))
     err = np.abs(yh[0] - yd)
     assert np.all(err <= TOL * Ad + 1e-6 * R), "planes mlp down: worst err/A %.3g" % (err / Ad).max()
+
+
+@pytest.mark.parametrize("t,rows,cols", [(gs.Q8_0, 300, 2560), (gs.Q8_0, 7, 96), (gs.Q6_K, 300, 2816), (gs.Q6_K, 5, 256)])
+def test_planes_embed_and_argmax_embed(orc, t, rows, cols):
+    """Embedding rows from a plane table equal the GGUF table's bit for bit
+    (ids in range, and one past the end giving NaN), and the fused pick and
+    gather on the planes picks the same token and row as on the blocks."""
+    import gguf_dequant_gemv_amd as qg
+    torch = _torch()
+    P_ = P8 if t == gs.Q8_0 else P
+    g = gs.rng(6600 + t + rows)
+    W = gs.weights(t, g, rows, cols)
+    say("planes embed", gs.NAMES[t], rows, cols)
+    Pt, Wt = (_prepared8 if t == gs.Q8_0 else _prepared)(W, rows, cols)
+    ids = np.array([0, rows - 1, rows // 2, rows], dtype=np.int32)
+    it, _ = dev(ids)
+    a = torch.empty((4, cols), dtype=torch.float32, device="cuda")
+    b = torch.empty((4, cols), dtype=torch.float32, device="cuda")
+    qg.qg_embed(t, Wt, rows, cols, it, 4, 1.5, a)
+    qg.qg_embed(P_, Pt, rows, cols, it, 4, 1.5, b)
+    ah, bh = host(a), host(b)
+    assert np.array_equal(ah[:3].view(np.uint32), bh[:3].view(np.uint32))
+    assert np.isnan(bh[3]).all()
+    ref = orc.embed(t, W, rows, cols, ids[:3], 1.5)
+    assert np.array_equal(bh[:3].astype(np.float64), np.asarray(ref).reshape(3, cols))
+    # the fused pick over the table's logits (a cap of 30, one clear winner)
+    # and the gather of that row
+    n, spike = rows, rows // 3
+    lg = g.standard_normal((1, n)).astype(np.float32) * 3
+    lg[0, spike] = 50.0
+    l1, _ = dev(lg)
+    l2, _ = dev(lg)
+    i1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    i2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(qg.qg_argmax_workspace_size(n, 1) // 4, dtype=torch.float32, device="cuda")
+    e1 = torch.empty((1, cols), dtype=torch.float32, device="cuda")
+    e2 = torch.empty((1, cols), dtype=torch.float32, device="cuda")
+    qg.qg_argmax_embed(l1, n, 1, 30.0, i1, ws, t, Wt, rows, cols, 0.5, e1)
+    qg.qg_argmax_embed(l2, n, 1, 30.0, i2, ws, P_, Pt, rows, cols, 0.5, e2)
+    assert int(host(i1)[0]) == spike and int(host(i2)[0]) == spike
+    assert np.array_equal(host(e1).view(np.uint32), host(e2).view(np.uint32))
