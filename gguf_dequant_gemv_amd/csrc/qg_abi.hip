@@ -687,11 +687,11 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
         out[0] = 5;
         out[1] = 64;
         out[2] = 1;
-        out[3] = (int32_t)((rows + 3) / 4);
+        out[3] = (int32_t)((rows + Q8P_NW - 1) / Q8P_NW);
         out[4] = query_device ? g : 0;
         out[5] = (int32_t)lds;
-        out[6] = 4;
-        out[7] = 4;
+        out[6] = Q8P_NF;
+        out[7] = Q8P_NW;
         return QG_OK;
     }
     if (planes) {

@@ -40,6 +40,9 @@ struct Q8pArgs {
 // banks
 QG_DEV int q8p_xpos(int v) { return v + 4 * (v >> 5); }
 constexpr int Q8P_MAX_COLS = 12288;   // x within the LDS of the largest instance (55 KB)
+// waves per workgroup and pieces in flight per lane (measured best of NW 4 /
+// 8 / 16 and NF 1..8 on the 151936 x 2560 head)
+constexpr int Q8P_NW = 8, Q8P_NF = 2;
 __host__ __device__ inline size_t q8p_lds_bytes(int cols) { return (size_t)(cols + cols / 8) * 4; }
 
 template <int NW, int NF, int XN, bool GATED>

@@ -127,7 +127,7 @@ int launch_q8_planes_dequant(const uint8_t *P, float *out, int64_t nblk, hipStre
 
 namespace {
 typedef void (*q8p_fn)(Q8pArgs);
-constexpr int Q8P_NW = 8, Q8P_NF = 2;   // measured best of NW 4 / 8 / 16, NF 1..8
+
 
 // x's float4 per thread: 4 up to 8192 values, 12 up to 24576
 q8p_fn q8p_kernel(int cols, bool gated) {

@@ -159,9 +159,10 @@ int qg_gemm(int type, const void *W, const float *x, float *y,
  * LDS bytes, [6] weight stages in flight per wave (kind 4: units in flight per
  * lane), [7] x chunk (row elements staged at a time, 0 = all of x; kind 4:
  * waves per workgroup).  Kind 5: one token against Q8_0 planes, a wave
- * walking rows in 16-byte code pieces ([1] 64 lanes a row, [3] row groups
- * of 4, [4] workgroups, [6] pieces in flight per lane, [7] waves per
- * workgroup).
+ * walking rows in 16-byte code pieces ([1] 64 lanes a row, [3] workgroups
+ * for one row a wave, [4] workgroups launched (every one that fits, each
+ * wave walking rows w, w + W, ...), [6] pieces in flight per lane, [7]
+ * waves per workgroup).
  * The plan of the first launch of the call (launches cover at most 2 GiB of
  * weights each).  w_aligned16: W would start 16-byte aligned.
  * Errors: as qg_gemv, QG_EINVAL for a null out, QG_EHIP when the device query

@@ -420,3 +420,10 @@ def test_q8_0_planes_type_and_rejects():
     assert L.qg_embed(P, FAKE + 2, 16, 512, FAKE, 1, ctypes.c_float(1.0), FAKE, None) == qg.QG_EINVAL
     p = qg.qg_gemv_plan(P, 151936, 2560, 1)
     assert p["kind"] == 5 and p["lds_bytes"] == (2560 + 2560 // 8) * 4
+
+
+def test_gemv_plan_q8_0_planes_constants():
+    """The plan reports the plane GEMV's own geometry: 8-wave workgroups,
+    2 pieces in flight per lane, one workgroup per 8 rows before the cap."""
+    p = qg.qg_gemv_plan(qg.QG_Q8_0_PLANES, 1000, 2048, 1)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["depth"], p["xchunk"]) == (5, 64, 125, 2, 8)
