@@ -21,7 +21,13 @@
 // group, which fold the Q4_K mins and the Q6_K offset of 32.  (Padding Q6_K's
 // x per 128 values spreads its lanes wider but measured slower, as did a
 // third Q6_K unit in flight.)
-// NF units per lane are in flight (3 for Q4_K, 2 for Q6_K).
+// NF units per lane are in flight: 1 for Q4_K and Q6_K planes, 2 for Q6_K
+// blocks.  Each wave holds only a few units a lane, so with more in flight
+// most of the matrix is requested at once and a wave's decode waits on
+// whichever of its units the memory delivers last: one in flight measured
+// 15.2 -> 13.0 us at Q4_K 17408 x 5120 and 19.3 -> 18.3 us on Q6_K planes
+// 5120 x 17408 (3 to 5 in flight: 15.2 to 17.3 us); Q6_K blocks measured
+// alike at 1 and 2.
 #pragma once
 #include "qg_device.h"
 
@@ -109,7 +115,7 @@ template <bool ALN>
 struct KQ4 {
     // WAVES: waves per SIMD its registers leave room for (an estimate for
     // plans made without a device to ask)
-    static constexpr int TYPE = T_Q4_K, BB = 144, G = 32, PG = 64, NF = 3, WAVES = 6;
+    static constexpr int TYPE = T_Q4_K, BB = 144, G = 32, PG = 64, NF = 1, WAVES = 6;
     static constexpr int RAW = ALN ? 12 : 14;   // head, codes (+1 dword each when realigned)
     typedef rsrc_t R;
     QG_DEV static R rsrc(const Kq1Args &a, u32 ph0) { return kq1_rsrc(a, ph0); }
@@ -273,7 +279,7 @@ struct KQ6 {
 // past the last plane's end for an odd block count).  The 4 lanes of a
 // block's units read 128 contiguous bytes of ql, 64 of qh.
 struct KQ6P {
-    static constexpr int TYPE = T_Q6_KP, BB = 210, G = 16, PG = 64, NF = 2, WAVES = 5;
+    static constexpr int TYPE = T_Q6_KP, BB = 210, G = 16, PG = 64, NF = 1, WAVES = 5;
     static constexpr int RAW = 4 + 4 + 4 + 2 + 1;
     struct R { rsrc_t q, h, s, d; };
     QG_DEV static R rsrc(const Kq1Args &a, u32) {
