@@ -14,6 +14,35 @@
 
 namespace qg {
 
+// The shared expert's gate logit (gate_inp . x over the H values), one
+// thread's part: its products in the order the shared-expert combine takes
+// them (16 columns 256 apart per batch), for a workgroup of 256 threads.
+QG_DEV float gate_part(const Moe1Args &a, int tid) {
+    float gp = 0.0f;
+    for (int64_t c0 = tid; c0 < a.rows; c0 += 256 * 16) {
+        float gv[16], xv[16];
+#pragma unroll
+        for (int b = 0; b < 16; b++) {
+            const bool in = c0 + b * 256 < a.rows;
+            gv[b] = in ? a.gate_inp[c0 + b * 256] : 0.0f;
+            xv[b] = in ? a.x[c0 + b * 256] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < 16; b++) gp = fmaf(gv[b], xv[b], gp);
+    }
+    return gp;
+}
+// the workgroup's sum of the parts (wave sums, then the 4 waves in order),
+// through the sigmoid; every workgroup takes the same steps, so all get the
+// same value
+QG_DEV float gate_finish(float gp, int wave, int lane, float *s_red) {
+    gp = wave_sum(gp);
+    if (lane == 0) s_red[wave] = gp;
+    __syncthreads();
+    const float sg = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+    return 1.0f / (1.0f + expf(-sg));
+}
+
 // Workgroup bx: rows bx*8 .. +7 (lane (grp, sub) of wave w: row (bx*4 + w)*2
 // + grp, units sub, sub + 32, ... of that row).  KMAX routed picks at most
 // (k of them), UPL units per lane of a routed row; XP the extra pick (its
@@ -68,22 +97,8 @@ QG_DEV void down1_body(const Moe1Args &a, int bx, const Picks &pk) {
             if (XP == XP_SHARED || sub + i * L < nbx) U::issue(rs, offx[i], tx[i]);
         }
     }
-    // the shared expert's gate logit: this thread's products in the order
-    // the shared-expert combine takes them (16 columns 256 apart per batch)
     [[maybe_unused]] float gp = 0.0f;
-    if constexpr (XP == XP_SHARED) {
-        for (int64_t c0 = tid; c0 < a.rows; c0 += 256 * 16) {
-            float gv[16], xv[16];
-#pragma unroll
-            for (int b = 0; b < 16; b++) {
-                const bool in = c0 + b * 256 < a.rows;
-                gv[b] = in ? a.gate_inp[c0 + b * 256] : 0.0f;
-                xv[b] = in ? a.x[c0 + b * 256] : 0.0f;
-            }
-#pragma unroll
-            for (int b = 0; b < 16; b++) gp = fmaf(gv[b], xv[b], gp);
-        }
-    }
+    if constexpr (XP == XP_SHARED) gp = gate_part(a, tid);
 
     // the activation rows (and their 32-value sums) into LDS, as one flat
     // batch over (row, float4): every thread's loads are issued before any
@@ -129,13 +144,7 @@ QG_DEV void down1_body(const Moe1Args &a, int bx, const Picks &pk) {
     }
     __syncthreads();
     [[maybe_unused]] float gs = 0.0f;
-    if constexpr (XP == XP_SHARED) {   // the block's sum: wave sums, then the waves in order
-        gp = wave_sum(gp);
-        if (lane == 0) s_red[wave] = gp;
-        __syncthreads();
-        const float sg = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
-        gs = 1.0f / (1.0f + expf(-sg));
-    }
+    if constexpr (XP == XP_SHARED) gs = gate_finish(gp, wave, lane, s_red);
 
     float yacc = 0.0f;
 #pragma unroll
@@ -177,6 +186,167 @@ QG_DEV void down1_body(const Moe1Args &a, int bx, const Picks &pk) {
         }
         if constexpr (XP == XP_DENSE) a.y_mlp[r] = xv;
         if (KMAX && a.y && pk.ok) a.y[r] = yacc;
+    }
+}
+
+// ---- column layout -------------------------------------------------------
+// The (pick, block) columns of one output row: routed pick j's block b is
+// column j*nb + b, the extra pick's blocks follow (k*nb + nbx columns, at
+// most D1C_NT).  Thread c of the workgroup takes column c for the
+// workgroup's R consecutive rows: it loads the column's 32 activation values
+// into registers once (their sum too, for the folding formats), then that
+// block of each of the R rows, and leaves each block's dot in LDS.  Every
+// lane has work whatever nb is, and a workgroup stages nothing.  Then one
+// thread per (row, pick) adds the pick's block dots in block order and forms
+// the term (dn_j * s[e_j]) * w_j, and one thread per row adds the terms in
+// pick order.  The routed blocks are read through one descriptor over the
+// whole expert pool (the launcher checks that its bytes fit 32 bits).
+constexpr int D1C_NT = 256, D1C_RMAX = 12;
+
+// one block against 32 activation values held in registers: the two halves'
+// sums as unit_dot forms them, folded with the block's scale
+template <class U>
+QG_DEV float reg_dot(const u32 (&w)[U::ND], const f32x4 (&x)[8], float xs) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        float &s = q >= 4 ? s1 : s0;
+        s = fmaf(U::dcode(w, 4 * q), x[q].x, s);
+        s = fmaf(U::dcode(w, 4 * q + 1), x[q].y, s);
+        s = fmaf(U::dcode(w, 4 * q + 2), x[q].z, s);
+        s = fmaf(U::dcode(w, 4 * q + 3), x[q].w, s);
+    }
+    return U::fold(w, 0, fmaf(s1, U::dfix(0, 1), s0 * U::dfix(0, 0)), xs);
+}
+
+// the routed pool's descriptor range: through the last slot's last row
+__host__ __device__ inline int64_t down1c_pool_bytes(int64_t ph, int64_t n_slots, int64_t stride, int64_t rows,
+                                                     int64_t row_bytes) {
+    return (ph + (n_slots - 1) * stride + rows * row_bytes + 3) & ~(int64_t)3;
+}
+
+// Workgroup bx: rows bx*R .. bx*R + R - 1 (R <= D1C_RMAX)
+template <class U, int XP>
+QG_DEV void down1c_body(const Moe1Args &a, int bx, int R) {
+    static_assert(U::VALUES == 32 && U::GROUPS == 1, "down1c_body: one 32-value block per unit");
+    __shared__ float s_dot[D1C_RMAX][D1C_NT];
+    __shared__ float s_term[D1C_RMAX][MOE1_MAXK + 1];
+    __shared__ float s_red[4];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int k = a.k, nb = a.nb, kn = k * nb;
+    const int nbx = XP == XP_DENSE ? a.d_nb : XP == XP_SHARED ? nb : 0;
+    const int C = kn + nbx;
+    const int c = min(tid, C - 1);   // threads past the columns repeat the last one and store nothing
+    const bool routed = c < kn;
+    const int j = routed ? c / nb : 0;
+    const int b = routed ? c - j * nb : c - kn;
+    const int64_t r0 = (int64_t)bx * R;
+    // the phase-two role of this thread: (row i2, pick s2) while tid < R * S
+    const int S = k + (XP != XP_NONE ? 1 : 0);
+    const int i2 = tid / S, s2 = tid - i2 * S;
+    const bool ok = a.valid[0] != 0;
+
+    // the column's activation values first: they depend on the column only,
+    // so their loads go out while the picks' slots are still on their way
+    const float *xsrc = routed ? a.act + (int64_t)j * a.act_stride : (XP == XP_SHARED ? a.sh_act : a.d_act);
+    f32x4 xr[8];
+#pragma unroll
+    for (int q = 0; q < 8; q++) xr[q] = ((const f32x4 *)(xsrc + 32 * b))[q];
+
+    // the column's block of each row: the routed pool or the extra matrix
+    const uint8_t *pool = uniform_ptr(a.W);
+    const u32 ph = (u32)((uintptr_t)pool & 3u);
+    const rsrc_t rp = make_rsrc(pool - ph, (u32)down1c_pool_bytes(ph, a.n_slots, a.stride, a.rows, a.row_bytes));
+    [[maybe_unused]] rsrc_t rx = rp;
+    u32 coff = 0, rb = 0;
+    if constexpr (XP != XP_NONE) {
+        const uint8_t *xb = uniform_ptr(XP == XP_SHARED ? a.shW : a.dW);
+        const int64_t rbx = XP == XP_SHARED ? a.row_bytes : a.d_row_bytes;
+        const u32 phx = (u32)((uintptr_t)xb & 3u);
+        rx = make_rsrc(xb - phx, (u32)((phx + a.rows * rbx + 3) & ~(int64_t)3));
+        coff = phx + (u32)b * U::BYTES;
+        rb = (u32)rbx;
+    }
+    // this lane's pick: its slot (read per lane, so no per-pick array is
+    // indexed by lane), and for phase two the down scale and weight of s2
+    const int s0 = a.pslot[j];
+    const int s2c = min(s2, k - 1);
+    const float es2 = a.pes[s2c], w2 = a.w[s2c];
+    if (routed) {
+        const int sl = s0 < 0 ? 0 : (s0 >= a.n_slots ? a.n_slots - 1 : s0);
+        coff = ph + (u32)sl * (u32)a.stride + (u32)b * U::BYTES;
+        rb = (u32)a.row_bytes;
+    }
+    u32 t[D1C_RMAX][U::NR], off[D1C_RMAX];
+#pragma unroll
+    for (int i = 0; i < D1C_RMAX; i++) {
+        const int64_t r = r0 + i < a.rows ? r0 + i : a.rows - 1;   // past the last row: a valid row, unused
+        off[i] = coff + (u32)r * rb;
+    }
+    // the routed lanes' loads, then the extra lanes' (two one-sided blocks
+    // apart, so that each load keeps its own uniform descriptor rather than
+    // one chosen per lane)
+    if (XP == XP_NONE || routed) {
+#pragma unroll
+        for (int i = 0; i < D1C_RMAX; i++)
+            if (i < R) U::issue(rp, off[i], t[i]);
+    }
+    if constexpr (XP != XP_NONE) {
+        asm volatile("" ::: "memory");
+        if (!routed) {
+#pragma unroll
+            for (int i = 0; i < D1C_RMAX; i++)
+                if (i < R) U::issue(rx, off[i], t[i]);
+        }
+    }
+    [[maybe_unused]] float gp = 0.0f;
+    if constexpr (XP == XP_SHARED) gp = gate_part(a, tid);
+    float xs = 0.0f;
+    if constexpr (U::SUMS != 0) {
+        float h[8];
+#pragma unroll
+        for (int q = 0; q < 8; q++) h[q] = (xr[q].x + xr[q].y) + (xr[q].z + xr[q].w);
+        xs = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+    }
+#pragma unroll
+    for (int i = 0; i < D1C_RMAX; i++) {
+        if (i < R) {
+            u32 wd[U::ND];
+            U::prep(t[i], off[i], wd);
+            s_dot[i][tid] = reg_dot<U>(wd, xr, xs);
+        }
+    }
+    [[maybe_unused]] float gs = 0.0f;
+    if constexpr (XP == XP_SHARED) gs = gate_finish(gp, wave, lane, s_red);   // holds a barrier
+    __syncthreads();
+
+    // one thread per (row, pick): the pick's block dots in block order
+    if (tid < R * S) {
+        const int i = i2, s = s2;
+        const bool ex = s >= k;
+        const int c0 = ex ? kn : s * nb, n = ex ? nbx : nb;
+        float sum = 0.0f;
+        for (int q = 0; q < n; q++) sum += s_dot[i][c0 + q];
+        if (!ex) {
+            sum = (sum * es2) * w2;
+            if (r0 + i < a.rows) a.dn[(int64_t)s * a.rows + r0 + i] = sum;
+        }
+        s_term[i][s] = sum;
+    }
+    __syncthreads();
+    // one thread per row: the terms in pick order
+    if (tid < R && r0 + tid < a.rows) {
+        const int64_t r = r0 + tid;
+        float yacc = 0.0f;
+        for (int s = 0; s < k; s++) yacc += s_term[tid][s];
+        [[maybe_unused]] const float xv = s_term[tid][k];
+        if constexpr (XP == XP_SHARED) {
+            a.sh_out[r] = xv;
+            if (ok) a.resid[r] = (yacc + xv * gs) + a.resid[r];
+        }
+        if constexpr (XP == XP_DENSE) a.y_mlp[r] = xv;
+        if (a.y && ok) a.y[r] = yacc;
     }
 }
 

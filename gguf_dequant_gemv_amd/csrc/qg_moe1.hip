@@ -14,6 +14,8 @@
 // same value.  A dense MLP beside the experts ([gemma4] encodeLayer) gives
 // its down row as the extra pick instead, its output kept apart.
 #include "../../include/qgemv.h"
+#include <algorithm>
+
 #include "qg_down1.h"
 
 namespace qg {
@@ -40,6 +42,11 @@ __global__ __launch_bounds__(256) void k_moe_down1(Moe1Args a) {
     down1_body<U, MOE1_MAXK, UPL, XP>(a, (int)blockIdx.x, pk);
 }
 
+template <class U, int XP>
+__global__ __launch_bounds__(D1C_NT) void k_moe_down1c(Moe1Args a, int R) {
+    down1c_body<U, XP>(a, (int)blockIdx.x, R);
+}
+
 bool moe_down1_fits(int type, int64_t cols, int k) {
     return (type == T_Q8_0 || type == T_Q4_0) && k >= 1 && k <= MOE1_MAXK && cols / 32 <= 2 * MOE1_L;
 }
@@ -61,8 +68,42 @@ moe1_fn moe1_kernel_dense(int type) {
     return type == T_Q8_0 ? k_moe_down1<UQ8_0B, 1, XP_DENSE> : k_moe_down1<UQ4_0B, 1, XP_DENSE>;
 }
 
+typedef void (*moe1c_fn)(Moe1Args, int);
+
+template <int XP>
+moe1c_fn moe1c_kernel(int type) {
+    return type == T_Q8_0 ? k_moe_down1c<UQ8_0B, XP> : k_moe_down1c<UQ4_0B, XP>;
+}
+
+// The column layout (down1c_body) where the (pick, block) columns fit one
+// workgroup and the pool's bytes fit a 32-bit descriptor.  R rows a
+// workgroup: about two workgroups a CU (a SIMD then holds two waves, one
+// computing while the other waits; measured 7.9 us against 8.5 at one a CU
+// and 9.1 at three for the 2816-row Q4_0 layer with its dense row), but one
+// a CU with the shared expert, whose gate logit every workgroup reduces
+// again (7.7 us against 10.4 at two a CU, 2048 rows of Q8_0).
+bool down1c_plan(const Moe1Args &a, int xp, int *rows_per_wg, int *wgs) {
+    const int nbx = xp == XP_DENSE ? a.d_nb : xp == XP_SHARED ? a.nb : 0;
+    if ((int64_t)a.k * a.nb + nbx > D1C_NT || a.n_slots < 1) return false;
+    const int64_t ph = (int64_t)((uintptr_t)a.W & 3u);
+    if (down1c_pool_bytes(ph, a.n_slots, a.stride, a.rows, a.row_bytes) > (int64_t)0xFFFFFFF0) return false;
+    const int64_t per = xp == XP_SHARED ? 256 : 512;
+    const int64_t R = std::min<int64_t>(D1C_RMAX, (a.rows + per - 1) / per);
+    *rows_per_wg = (int)R;
+    *wgs = (int)((a.rows + R - 1) / R);
+    return true;
+}
+
 int launch_moe_down1(int type, const Moe1Args &a, hipStream_t st) {
     const int xp = a.dW ? XP_DENSE : a.shW ? XP_SHARED : XP_NONE;
+    int R = 0, g = 0;
+    if (down1c_plan(a, xp, &R, &g)) {
+        const moe1c_fn f = xp == XP_DENSE    ? moe1c_kernel<XP_DENSE>(type)
+                           : xp == XP_SHARED ? moe1c_kernel<XP_SHARED>(type)
+                                             : moe1c_kernel<XP_NONE>(type);
+        hipLaunchKernelGGL(f, dim3((unsigned)g), dim3(D1C_NT), 0, st, a, R);
+        return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
+    }
     const size_t lds = down1_lds_bytes(a.nb, type == T_Q8_0 ? 0 : 32, xp, xp == XP_DENSE ? a.d_nb : a.nb);
     const bool two = a.nb > MOE1_L;
     if (xp == XP_DENSE && (two || a.d_nb > MOE1_L * MOE1_MAXX)) return QG_EINVAL;

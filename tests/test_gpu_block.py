@@ -230,6 +230,7 @@ SHARED_CASES = [
     # routing launch and the one-token down launch (combine included)
     (gs.Q4_0, 352, 96, 96, 16, 4, 1, None),
     (gs.Q8_0, 256, 1536, 1536, 16, 8, 1, None),     # two blocks per lane in the down launch
+    (gs.Q8_0, 2336, 512, 512, 16, 8, 1, None),      # 10 rows a down workgroup, the last one ragged
     # one token, other shapes or types: routed down in one launch, then the
     # shared expert and the combine as their own launches
     (gs.Q4_0, 352, 96, 160, 16, 4, 1, None),

@@ -105,6 +105,7 @@ DENSE_CASES = [
     (gs.Q8_0, 512, 256, 512, 16, 4, 1, None, 0),      # two groups, Q8_0 units
     (gs.Q4_0, 352, 96, 288, 16, 4, 1, None, 1),       # small, ragged row tiles
     (gs.Q8_0, 256, 256, 4096, 8, 2, 1, None, 0),      # the widest dense row the down launch takes (4 units/lane)
+    (gs.Q8_0, 256, 1024, 1024, 16, 8, 1, None, 0),    # 288 (pick, block) columns: the row-walking down launch
     # the separate calls
     (gs.Q8_0, 512, 256, 384, 16, 4, 1, None, 0),      # FD not a multiple of F
     (gs.Q4_0, 352, 96, 288, 16, 4, 3, None, 1),       # several tokens

@@ -342,6 +342,7 @@ MOE_CASES = [
     (gs.Q4_0, 1, 320, 96, 12, 1, 1, True),          # one token, one pick
     (gs.Q8_0, 0, 256, 128, 256, 8, 1, False),       # one token, 256 experts: four logits per lane in the routing
     (gs.Q4_0, 1, 320, 96, 200, 8, 1, True),         # one token, a ragged expert count
+    (gs.Q8_0, 0, 1088, 256, 32, 8, 1, True),        # one token, 3 rows a down workgroup, the last one ragged
 ]
 
 
