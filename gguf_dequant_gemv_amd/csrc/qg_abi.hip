@@ -679,19 +679,19 @@ int qg_gemv_plan(int type, int64_t rows, int64_t cols, int ntok, int w_aligned16
     if (type == QG_Q8_0_PLANES) {
         if (ntok < 1 || ntok > QG_MAX_TOKENS) return QG_ELIMIT;
         if (ntok != 1 || !w_aligned16) return QG_EINVAL;
-        int g = 0;
+        int g = 0, nw = 0;
         size_t lds = 0;
-        rc = q8p_plan(rows, cols, false, query_device != 0, &g, &lds);
+        rc = q8p_plan(rows, cols, false, query_device != 0, &g, &lds, &nw);
         if (rc) return rc;
         for (int i = 0; i < 8; i++) out[i] = 0;
         out[0] = 5;
         out[1] = 64;
         out[2] = 1;
-        out[3] = (int32_t)((rows + Q8P_NW - 1) / Q8P_NW);
+        out[3] = (int32_t)((rows + nw - 1) / nw);
         out[4] = query_device ? g : 0;
         out[5] = (int32_t)lds;
         out[6] = Q8P_NF;
-        out[7] = Q8P_NW;
+        out[7] = nw;
         return QG_OK;
     }
     if (planes) {

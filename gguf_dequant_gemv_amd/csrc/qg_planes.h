@@ -43,6 +43,16 @@ constexpr int Q8P_MAX_COLS = 12288;   // x within the LDS of the largest instanc
 // waves per workgroup and pieces in flight per lane (measured best of NW 4 /
 // 8 / 16 and NF 1..8 on the 151936 x 2560 head)
 constexpr int Q8P_NW = 8, Q8P_NF = 2;
+// Waves per workgroup of the plain (not gated) launch: up to 4096 rows, the
+// fewest of 4, 8, 10, 12, 14, 16 that put every row on its own wave within
+// 256 workgroups (one a CU: a CU holding two workgroups of a launch ends its
+// waves last, measured 8.6 against 6.3 us on 2560 rows); beyond that Q8P_NW,
+// every wave walking several rows.
+__host__ __device__ inline int q8p_waves(int64_t rows, bool gated) {
+    if (gated || rows > 16 * 256) return Q8P_NW;
+    const int per = (int)((rows + 255) / 256);
+    return per <= 4 ? 4 : per <= 8 ? 8 : per <= 10 ? 10 : per <= 12 ? 12 : per <= 14 ? 14 : 16;
+}
 __host__ __device__ inline size_t q8p_lds_bytes(int cols) { return (size_t)(cols + cols / 8) * 4; }
 
 template <int NW, int NF, int XN, bool GATED>
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(64 * NW) void k_q8p1(Q8pArgs a) {
     }
 }
 
-int q8p_plan(int64_t rows, int64_t cols, bool gated, bool query, int *wgs, size_t *lds);
+int q8p_plan(int64_t rows, int64_t cols, bool gated, bool query, int *wgs, size_t *lds, int *nw);
 int launch_q8p1(const Q8pArgs &a, bool gated, hipStream_t st);
 // f32 values of nblk Q6_K / Q8_0 blocks held in their plane layouts
 int launch_q6k_planes_dequant(const uint8_t *P, float *out, int64_t nblk, hipStream_t st);

@@ -129,16 +129,27 @@ namespace {
 typedef void (*q8p_fn)(Q8pArgs);
 
 
-// x's float4 per thread: 4 up to 8192 values, 12 up to 24576
-q8p_fn q8p_kernel(int cols, bool gated) {
+// x's float4 per thread: 4 up to 1024 NW values, 12 up to 3072 NW
+template <int NW>
+q8p_fn q8p_plain(int cols) {
+    return cols <= 4 * 4 * 64 * NW ? k_q8p1<NW, Q8P_NF, 4, false> : k_q8p1<NW, Q8P_NF, 12, false>;
+}
+q8p_fn q8p_kernel(int cols, bool gated, int nw) {
     if (gated)
         return cols <= 4 * 4 * 64 * Q8P_NW ? k_q8p1<Q8P_NW, Q8P_NF, 4, true> : k_q8p1<Q8P_NW, Q8P_NF, 12, true>;
-    return cols <= 4 * 4 * 64 * Q8P_NW ? k_q8p1<Q8P_NW, Q8P_NF, 4, false> : k_q8p1<Q8P_NW, Q8P_NF, 12, false>;
+    switch (nw) {
+    case 4: return q8p_plain<4>(cols);
+    case 10: return q8p_plain<10>(cols);
+    case 12: return q8p_plain<12>(cols);
+    case 14: return q8p_plain<14>(cols);
+    case 16: return q8p_plain<16>(cols);
+    default: return q8p_plain<8>(cols);
+    }
 }
 
 // workgroups resident at once on all CUs (measured when a device is there to
 // ask, else 8 a CU)
-int q8p_resident(q8p_fn f, size_t lds, bool query) {
+int q8p_resident(q8p_fn f, int nw, size_t lds, bool query) {
     if (!query) return 8 * 256;
     static std::mutex mu;
     static q8p_fn cf[8];
@@ -148,7 +159,7 @@ int q8p_resident(q8p_fn f, size_t lds, bool query) {
     for (int i = 0; i < used; i++)
         if (cf[i] == f && cl[i] == lds) return cn[i];
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 64 * Q8P_NW, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)f, 64 * nw, lds) != hipSuccess)
         return -1;
     if (per_cu < 1) per_cu = 1;
     if (used < 8) { cf[used] = f; cl[used] = lds; cn[used] = per_cu * 256; used++; }
@@ -156,26 +167,29 @@ int q8p_resident(q8p_fn f, size_t lds, bool query) {
 }
 }  // namespace
 
-// One token against a Q8_0 tensor in the plane layout: every workgroup that
-// fits at once (each wave walks rows w, w + W, ...), at most one per 4 rows.
-int q8p_plan(int64_t rows, int64_t cols, bool gated, bool query, int *wgs, size_t *lds) {
+// One token against a Q8_0 tensor in the plane layout: nw waves a workgroup
+// (q8p_waves), every workgroup that fits at once (each wave walks rows w,
+// w + W, ...), at most one per nw rows.
+int q8p_plan(int64_t rows, int64_t cols, bool gated, bool query, int *wgs, size_t *lds, int *nw) {
     if (rows < 1 || cols < 32 || cols % 32 || cols > Q8P_MAX_COLS) return QG_EINVAL;
     if (rows * cols >= ((int64_t)1 << 31)) return QG_ELIMIT;
     const size_t l = q8p_lds_bytes((int)cols);
-    const int cap = q8p_resident(q8p_kernel((int)cols, gated), l, query);
+    const int w = q8p_waves(rows, gated);
+    const int cap = q8p_resident(q8p_kernel((int)cols, gated, w), w, l, query);
     if (cap < 0) return QG_EHIP;
-    const int64_t need = (rows + Q8P_NW - 1) / Q8P_NW;
+    const int64_t need = (rows + w - 1) / w;
     *wgs = (int)(need < cap ? need : cap);
     *lds = l;
+    *nw = w;
     return QG_OK;
 }
 
 int launch_q8p1(const Q8pArgs &a, bool gated, hipStream_t st) {
-    int g = 0;
+    int g = 0, w = 0;
     size_t l = 0;
-    const int rc = q8p_plan(a.rows, a.cols, gated, true, &g, &l);
+    const int rc = q8p_plan(a.rows, a.cols, gated, true, &g, &l, &w);
     if (rc) return rc;
-    hipLaunchKernelGGL(q8p_kernel(a.cols, gated), dim3((unsigned)g), dim3(64 * Q8P_NW), l, st, a);
+    hipLaunchKernelGGL(q8p_kernel(a.cols, gated, w), dim3((unsigned)g), dim3(64 * w), l, st, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_EHIP;
 }
 

@@ -423,7 +423,13 @@ def test_q8_0_planes_type_and_rejects():
 
 
 def test_gemv_plan_q8_0_planes_constants():
-    """The plan reports the plane GEMV's own geometry: 8-wave workgroups,
-    2 pieces in flight per lane, one workgroup per 8 rows before the cap."""
+    """The plan reports the plane GEMV's own geometry: 2 pieces in flight
+    per lane; up to 4096 rows the fewest waves a workgroup (4, 8, 10, 12,
+    14, 16) that give every row its own wave within 256 workgroups, beyond
+    that 8-wave workgroups walking several rows each."""
     p = qg.qg_gemv_plan(qg.QG_Q8_0_PLANES, 1000, 2048, 1)
-    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["depth"], p["xchunk"]) == (5, 64, 125, 2, 8)
+    assert (p["kind"], p["lanes_per_row"], p["row_tiles"], p["depth"], p["xchunk"]) == (5, 64, 250, 2, 4)
+    for rows, nw in ((1, 4), (1024, 4), (1025, 8), (2048, 8), (2049, 10), (2560, 10), (2816, 12), (3500, 14),
+                     (4096, 16), (4097, 8), (151936, 8)):
+        p = qg.qg_gemv_plan(qg.QG_Q8_0_PLANES, rows, 256, 1)
+        assert p["xchunk"] == nw and p["row_tiles"] == (rows + nw - 1) // nw, (rows, p)

@@ -117,7 +117,9 @@ def test_planes_gemv_full_size(orc, rows, cols):
 # (rows, cols): a 16-byte piece count per row below, at and past 64 lanes, a
 # ragged last slot (cols / 16 not a multiple of 64), odd blocks per row, rows
 # below one per wave and far past the resident waves
-Q8_SHAPES = [(1, 32), (3, 96), (45, 1024), (77, 2560), (129, 1056), (1000, 2048), (33, 9728), (20000, 2560)]
+Q8_SHAPES = [(1, 32), (3, 96), (45, 1024), (77, 2560), (129, 1056), (1000, 2048), (33, 9728), (20000, 2560),
+             # 8, 10, 12 (x in 12 float4 a thread), 14 and 16 waves a workgroup, last workgroups ragged
+             (1500, 64), (2100, 512), (2500, 12288), (3300, 256), (4096, 320)]
 
 
 def _prepared8(W, rows, cols):
