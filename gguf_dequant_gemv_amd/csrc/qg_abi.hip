@@ -781,7 +781,7 @@ int qg_router_topk(const float *logits, int n_experts, int k, int ntok, int32_t 
         return QG_ELIMIT;
     if (!logits || !ids || !weights || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4))
         return QG_EINVAL;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(64 * ntok), 0, (hipStream_t)stream, logits, n_experts, k, ntok,
+    hipLaunchKernelGGL(route_kernel(n_experts), dim3(1), dim3(64 * ntok), 0, (hipStream_t)stream, logits, n_experts, k, ntok,
                        (const int32_t *)nullptr, 1, ids, weights, (int32_t *)nullptr, ids, weights,
                        (int32_t *)nullptr, (int32_t *)nullptr, 0, (int32_t *)nullptr, 0, (int32_t *)nullptr,
                        (const float *)nullptr, (int32_t *)nullptr, (float *)nullptr);
@@ -1046,7 +1046,7 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
     // 1. route: top-k, weights, slot lookup, grouping by expert
     if (!route_in) {
         const int nthreads = 64 * ntok < 256 ? 256 : 64 * ntok;
-        hipLaunchKernelGGL(k_route, dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots,
+        hipLaunchKernelGGL(route_kernel(E), dim3(1), dim3(nthreads), 0, st, router_logits, E, topk, ntok, expert_slots,
                            n_slots, ids_out, w_out, status, rt_ids, rt_w, rt_valid, grp, ca, sets_a, cb, sets_b,
                            m->down_scale, (int32_t *)(ws + L.pslot), (float *)(ws + L.pes));
         if (hipGetLastError() != hipSuccess) return QG_EHIP;

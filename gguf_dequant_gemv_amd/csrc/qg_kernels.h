@@ -1455,10 +1455,12 @@ int gemm_split_x(const float *x, int64_t x_stride, int ntok, int64_t cols, uint8
 int gemm_reduce(const GemvArgs &a, int nsplit, hipStream_t st);
 
 // Router / grouping and combine kernels (qg_route.hip).
-__global__ void k_route(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots, int32_t *ids_out,
-                        float *w_out, int32_t *status, int32_t *rt_ids, float *rt_w, int32_t *rt_valid,
-                        int32_t *grp, int ca, int32_t *sets_a, int cb, int32_t *sets_b, const float *escale,
-                        int32_t *rt_pslot, float *rt_pes);
+typedef void (*route_fn)(const float *logits, int E, int k, int T, const int32_t *slots, int n_slots,
+                         int32_t *ids_out, float *w_out, int32_t *status, int32_t *rt_ids, float *rt_w,
+                         int32_t *rt_valid, int32_t *grp, int ca, int32_t *sets_a, int cb, int32_t *sets_b,
+                         const float *escale, int32_t *rt_pslot, float *rt_pes);
+// k_route for E experts (E <= 256): the instance with the fewest register sets
+route_fn route_kernel(int E);
 __global__ void k_combine(const float *dn, const int32_t *rt_valid, float *y, int64_t H, int k);
 
 }  // namespace qg

@@ -9,6 +9,11 @@ namespace qg {
 // kernel's selection and renormalisation; ranking logits orders as ranking
 // the probabilities does.  With `grp` set it also groups the (token, pick)
 // pairs by expert for the expert GEMVs (slot lookup, absent-expert status).
+// NS register sets of 64 experts per lane (E <= 64 NS).  Every global input
+// goes out in one batch (the wave's logits, then the experts' slots and down
+// scales into LDS), so the launch pays one memory round trip before the
+// selection.
+template <int NS>
 __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int k, int T,
                                                 const int32_t *slots, int n_slots, int32_t *ids_out, float *w_out,
                                                 int32_t *status, int32_t *rt_ids, float *rt_w,
@@ -21,35 +26,45 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
     __shared__ int s_gidx[256];     // expert e: its group index
     __shared__ int s_wcnt[16];
     __shared__ int s_slot[256];     // expert e: its pool slot
+    __shared__ float s_es[256];     // expert e: its down scale (1 without one)
     __shared__ float s_val[MAXT * 32];
     __shared__ int s_na[256], s_nb[256];   // set lists: chunks per group, then their running sums
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int e = tid; e < E; e += blockDim.x) {
-        s_tmask[e] = 0u;
-        s_slot[e] = slots ? slots[e] : 0;
-    }
+    float lv[NS] = {};
     if (wave < T) {
         const float *l = logits + (int64_t)wave * E;
-        float lv[4];
-        u32 key[4];
-        u32 taken = 0u;  // bit i: value lane + 64 i is picked or absent
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < NS; i++) {
             const int e = lane + 64 * i;
             lv[i] = e < E ? l[e] : 0.0f;
+        }
+    }
+    const bool want_es = rt_pslot && escale;
+    for (int e = tid; e < E; e += blockDim.x) {
+        const int sv = slots ? slots[e] : 0;
+        const float ev = want_es ? escale[e] : 1.0f;
+        s_tmask[e] = 0u;
+        s_slot[e] = sv;
+        s_es[e] = ev;
+    }
+    if (wave < T) {
+        u32 key[NS];
+        u32 taken = 0u;  // bit i: value lane + 64 i is picked or absent
+#pragma unroll
+        for (int i = 0; i < NS; i++) {
             key[i] = order_key(lv[i]);
-            if (e >= E) taken |= 1u << i;
+            if (lane + 64 * i >= E) taken |= 1u << i;
         }
         for (int j = 0; j < k; j++) {
             // the largest key still free; among equal keys the lowest index
             u32 lm = 0u;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+            for (int i = 0; i < NS; i++)
                 if (!((taken >> i) & 1u)) lm = max(lm, key[i]);
             const u32 M = wave_max_u32(lm);
             int e = -1;
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
+            for (int i = 0; i < NS; i++) {
                 const unsigned long long b = __ballot(!((taken >> i) & 1u) && key[i] == M);
                 if (e < 0 && b) e = 64 * i + (int)__builtin_ctzll(b);
             }
@@ -57,7 +72,7 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
                 taken |= 1u << (e >> 6);
                 float v = lv[0];
 #pragma unroll
-                for (int i = 1; i < 4; i++) v = (e >> 6) == i ? lv[i] : v;
+                for (int i = 1; i < NS; i++) v = (e >> 6) == i ? lv[i] : v;
                 s_ids[wave * k + j] = e;
                 s_val[wave * k + j] = v;
             }
@@ -76,7 +91,7 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
             ok = sl >= 0 && sl < n_slots;
             if (rt_pslot) {   // each pick's slot and down scale, pick order
                 rt_pslot[wave * k + lane] = sl;
-                rt_pes[wave * k + lane] = escale ? escale[id] : 1.0f;
+                rt_pes[wave * k + lane] = s_es[id];
             }
         }
         const float sum = wave_sum(ex);
@@ -145,19 +160,34 @@ __global__ __launch_bounds__(1024) void k_route(const float *logits, int E, int 
         s_nb[tid] = sets_b ? (n + cb - 1) / cb : 0;
     }
     __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        int va = 0, vb = 0;
-        if (tid < 256 && tid >= d) {
-            va = s_na[tid - d];
-            vb = s_nb[tid - d];
+    if (wave == 0) {   // inclusive scans of both, by one wave: 4 experts a lane, then across the lanes
+        int a4[4], b4[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            a4[i] = s_na[4 * lane + i];
+            b4[i] = s_nb[4 * lane + i];
         }
-        __syncthreads();
-        if (tid < 256) {
-            s_na[tid] += va;
-            s_nb[tid] += vb;
+#pragma unroll
+        for (int i = 1; i < 4; i++) {
+            a4[i] += a4[i - 1];
+            b4[i] += b4[i - 1];
         }
-        __syncthreads();
+        int ta = a4[3], tb = b4[3];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int ua = __shfl_up(ta, d), ub = __shfl_up(tb, d);
+            if (lane >= d) {
+                ta += ua;
+                tb += ub;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            s_na[4 * lane + i] = ta - a4[3] + a4[i];
+            s_nb[4 * lane + i] = tb - b4[3] + b4[i];
+        }
     }
+    __syncthreads();
     if (has) {
         if (sets_a) {
             const int c1 = s_na[tid], c0 = tid ? s_na[tid - 1] : 0;
@@ -198,5 +228,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *dn, const int32_t 
     }
     if (ok) y[(int64_t)t * H + h] = acc;
 }
+
+route_fn route_kernel(int E) { return E <= 64 ? k_route<1> : E <= 128 ? k_route<2> : k_route<4>; }
 
 }  // namespace qg
