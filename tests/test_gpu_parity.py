@@ -301,14 +301,19 @@ def _moe_case(t, act, H, F, E, k, T, seed, with_scale):
                 lg=lg, x=x, ds=ds)
 
 
-def run_moe_gpu(c, slots=None, perm_pool=None):
+def run_moe_gpu(c, slots=None, perm_pool=None, pool_dev=None, n_slots=0):
+    """pool_dev: a device pool (tensor) to read instead of c["pool"], with
+    n_slots slots of c["rec"] bytes."""
     import gguf_dequant_gemv_amd as qg
     torch = _torch()
-    pool = c["pool"] if perm_pool is None else perm_pool
-    pt, pp = dev(pool)
+    if pool_dev is not None:
+        pt, pp = pool_dev, pool_dev.data_ptr()
+    else:
+        pool = c["pool"] if perm_pool is None else perm_pool
+        pt, pp = dev(pool)
     dst = dev(c["ds"])[0] if c["ds"] is not None else None
     m = qg.make_moe(c["t"], c["act"], c["H"], c["F"], c["E"], pp + c["gu_off"], c["rec"], pp + c["d_off"],
-                    c["rec"], dst)
+                    c["rec"], dst, n_slots)
     slots = np.arange(c["E"], dtype=np.int32) if slots is None else slots
     st, _ = dev(slots.astype(np.int32))
     lt, _ = dev(c["lg"])
@@ -367,9 +372,9 @@ def test_moe_crowded_experts(orc, t, act):
     _moe_check(orc, c)
 
 
-def _moe_check(orc, c):
+def _moe_check(orc, c, **run_kw):
     t, act, H, F, E, k, T = (c[key] for key in ("t", "act", "H", "F", "E", "k", "T"))
-    r = run_moe_gpu(c)
+    r = run_moe_gpu(c, **run_kw)
     ref = orc.moe_ffn(t, act, H, F, E, c["pool"][c["gu_off"]:], c["rec"], c["pool"][c["d_off"]:], c["rec"],
                       c["ds"], c["lg"], k, np.arange(E, dtype=np.int32), c["x"], T, want_gu=True)
     assert r["status"] == 0
@@ -420,6 +425,29 @@ def test_moe_absent_expert_and_slots(orc):
             assert np.all(np.isnan(r["y"][tt]))
         else:
             assert np.array_equal(r["y"][tt], base["y"][tt])
+
+
+@pytest.mark.parametrize("t,act", [(gs.Q8_0, 0), (gs.Q4_0, 1)])
+def test_moe_one_token_pool_past_4gib(orc, t, act):
+    """One token against an expert pool of a little over 4 GiB whose experts
+    sit in its last slots: the column down launch addresses the pool with
+    32-bit offsets, so this pool takes the row-walking down launch, and the
+    gated launch reaches slots past 4 GiB; the same stage-wise checks as any
+    other case."""
+    torch = _torch()
+    H, F, E, k, T = 256, 128, 6, 3, 1
+    c = _moe_case(t, act, H, F, E, k, T, 6004 + t, act == 1)
+    rec = c["rec"]
+    n_slots = (4 * 2 ** 30 + 64 * 2 ** 20) // rec + E
+    slots = np.array([n_slots - 1 - e for e in range(E)], np.int32)
+    say("moe pool past 4 GiB", gs.NAMES[t], "slots", n_slots, "record", rec)
+    big = torch.empty(n_slots * rec, dtype=torch.uint8, device="cuda")
+    src = torch.from_numpy(c["pool"]).cuda()
+    for e in range(E):
+        s0 = int(slots[e]) * rec
+        big[s0:s0 + rec] = src[e * rec:(e + 1) * rec]
+    _moe_check(orc, c, slots=slots, pool_dev=big, n_slots=n_slots)
+    del big
 
 
 def test_moe_one_token_absent_expert_and_slots(orc):
