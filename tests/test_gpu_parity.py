@@ -427,6 +427,26 @@ def test_moe_absent_expert_and_slots(orc):
             assert np.array_equal(r["y"][tt], base["y"][tt])
 
 
+@pytest.mark.parametrize("t,act,E,k", [(gs.Q8_0, 0, 128, 8), (gs.Q4_0, 1, 200, 8), (gs.Q8_0, 0, 40, 3),
+                                      (gs.Q4_0, 1, 256, 5)])
+def test_moe_one_token_tied_logits(orc, t, act, E, k):
+    """One token, routed inside the gated launch: exact ties among the router
+    logits, six at the top and more just below, so the k-th place falls
+    inside a run of equal logits (the lowest indices win); the picks, their
+    order and the weights equal the oracle's router, then the stage-wise
+    checks."""
+    H, F, T = 256, 128, 1
+    c = _moe_case(t, act, H, F, E, k, T, 6200 + E + k, act == 1)
+    lg = c["lg"].copy()
+    top = [E - 1, 3, 17, E // 2, 9, 1]
+    lg[0, top] = np.float32(6.0)
+    nxt = [e for e in ((7 * i + 5) % E for i in range(k + 3)) if e not in top]
+    lg[0, nxt] = np.float32(5.5)
+    c["lg"] = lg
+    say("moe one token tied logits", gs.NAMES[t], "E", E, "k", k)
+    _moe_check(orc, c)
+
+
 @pytest.mark.parametrize("t,act", [(gs.Q8_0, 0), (gs.Q4_0, 1)])
 def test_moe_one_token_pool_past_4gib(orc, t, act):
     """One token against an expert pool of a little over 4 GiB whose experts
