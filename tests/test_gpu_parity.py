@@ -348,6 +348,9 @@ MOE_CASES = [
     (gs.Q8_0, 0, 256, 128, 256, 8, 1, False),       # one token, 256 experts: four logits per lane in the routing
     (gs.Q4_0, 1, 320, 96, 200, 8, 1, True),         # one token, a ragged expert count
     (gs.Q8_0, 0, 1088, 256, 32, 8, 1, True),        # one token, 3 rows a down workgroup, the last one ragged
+    (gs.Q8_0, 0, 512, 1024, 16, 8, 1, True),        # one token, exactly 256 (pick, block) columns
+    (gs.Q8_0, 0, 256, 128, 256, 8, 16, False),      # 16 tokens, 256 experts: the routing launch's four register sets
+    (gs.Q4_0, 1, 320, 96, 200, 6, 5, True),         # 5 tokens, 200 experts: four sets, the last one partly empty
 ]
 
 
