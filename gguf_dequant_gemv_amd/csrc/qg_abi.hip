@@ -970,6 +970,10 @@ struct ExtraGroups {
     int n;
     const float *x;
     float *act, *gu;
+    // a shared expert's gate logit (gate_inp . x), reduced in the routing
+    // launch into gate_out[0] when both are set
+    const float *gate_inp;
+    float *gate_out;
 };
 
 int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int32_t *expert_slots, const float *x,
@@ -1100,6 +1104,8 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
         a.xg_y = xg->act;
         a.xg_y2 = xg->gu;
         a.xg_n = xg->n;
+        a.r_gate_inp = xg->gate_inp;
+        a.r_gate_out = xg->gate_inp ? xg->gate_out : nullptr;
         grid_a.y += xg->n;
         if (xg_done) *xg_done = true;
     }
@@ -1134,7 +1140,7 @@ int moe_routed(const qg_moe *m, const float *router_logits, int topk, const int3
 // act [ntok][SF] and the scratch of its qg_mlp call (qg_mlp's layout), then
 // sh [ntok][H], each 256-byte aligned.
 struct SharedWs {
-    size_t gu, act, sh, total;
+    size_t gu, act, sh, glog, total;
 };
 // the one-token down launch's arguments for a pool, its workspace and output
 Moe1Args down1_args(const qg_moe *m, int topk, void *workspace, float *y) {
@@ -1163,7 +1169,8 @@ SharedWs shared_ws(int type, int64_t H, int64_t SF, int ntok) {
     SharedWs o;
     o.gu = 0;
     o.act = align256((size_t)ntok * 2 * (size_t)SF * 4);
-    o.sh = o.act + align256((size_t)ntok * (size_t)SF * 4) + mlp_scratch_bytes(type, H, SF, ntok);
+    o.glog = o.act + align256((size_t)ntok * (size_t)SF * 4) + mlp_scratch_bytes(type, H, SF, ntok);
+    o.sh = o.glog + 256;   // after the gate logit (one token), the output sh last
     o.total = o.sh + align256((size_t)ntok * (size_t)H * 4);
     return o;
 }
@@ -1268,7 +1275,8 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     // and up rows ride in the routing launch, its down row and the whole
     // combine in the one-token down launch (two launches in all).
     const bool one = ntok == 1 && sh->type == m->type && sh->ff == m->ff && moe_down1_fits(m->type, m->ff, topk);
-    const ExtraGroups shg = {sh->gate, sh->up, 0, m->ff, 1, x, (float *)(ws + S.act), (float *)(ws + S.gu)};
+    const ExtraGroups shg = {sh->gate, sh->up, 0, m->ff, 1, x, (float *)(ws + S.act), (float *)(ws + S.gu),
+                             sh->gate_inp, (float *)(ws + S.glog)};
     bool fused = false;
     int rc = moe_routed(m, router_logits, topk, expert_slots, x, resid, ntok, ids_out, w_out, status, workspace,
                         workspace_bytes, S.total, st, &dn, &valid, !one, one ? &shg : nullptr, &fused);
@@ -1281,6 +1289,7 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
         b.x = x;
         b.resid = resid;
         b.sh_out = (float *)(ws + S.sh);
+        b.gate_logit = (const float *)(ws + S.glog);   // reduced by the routing launch
         if (fused) return launch_moe_down1(m->type, b, st);
         b.shW = nullptr;   // the routed terms only (no y); the shared expert below
         rc = launch_moe_down1(m->type, b, st);
@@ -1288,7 +1297,7 @@ int qg_moe_ffn_shared(const qg_moe *m, const qg_shared_expert *sh, const float *
     }
     // the shared expert: a dense gated MLP on the same input, into the workspace
     rc = qg_mlp(sh->type, m->act, sh->gate, sh->up, sh->down, m->hidden, sh->ff, x, (float *)(ws + S.sh), ntok,
-                ws + S.gu, S.sh - S.gu, stream);
+                ws + S.gu, S.glog - S.gu, stream);
     if (rc) return rc;
     // routed terms + gated shared output + residual
     return launch_combine_shared(dn, valid, (const float *)(ws + S.sh), sh->gate_inp, x, resid, m->hidden, topk,
@@ -1335,7 +1344,7 @@ int qg_moe_ffn_dense(const qg_moe *m, const qg_dense_mlp *d, const float *router
         return qg_mlp(d->type, m->act, d->gate, d->up, d->down, H, FD, x_mlp, y_mlp, ntok, wsd, wsd_bytes, stream);
     }
     const int64_t rb = H / 32 * qg_block_bytes(m->type);   // a gate / up row's bytes
-    const ExtraGroups xg = {d->gate, d->up, F * rb, FD, (int)(FD / F), x_mlp, av, gu};
+    const ExtraGroups xg = {d->gate, d->up, F * rb, FD, (int)(FD / F), x_mlp, av, gu, nullptr, nullptr};
     float *dn = nullptr;
     int32_t *valid = nullptr;
     bool taken = false;

@@ -98,7 +98,9 @@ QG_DEV void down1_body(const Moe1Args &a, int bx, const Picks &pk) {
         }
     }
     [[maybe_unused]] float gp = 0.0f;
-    if constexpr (XP == XP_SHARED) gp = gate_part(a, tid);
+    if constexpr (XP == XP_SHARED) {
+        if (!a.gate_logit) gp = gate_part(a, tid);
+    }
 
     // the activation rows (and their 32-value sums) into LDS, as one flat
     // batch over (row, float4): every thread's loads are issued before any
@@ -144,7 +146,8 @@ QG_DEV void down1_body(const Moe1Args &a, int bx, const Picks &pk) {
     }
     __syncthreads();
     [[maybe_unused]] float gs = 0.0f;
-    if constexpr (XP == XP_SHARED) gs = gate_finish(gp, wave, lane, s_red);
+    if constexpr (XP == XP_SHARED)
+        gs = a.gate_logit ? 1.0f / (1.0f + expf(-a.gate_logit[0])) : gate_finish(gp, wave, lane, s_red);
 
     float yacc = 0.0f;
 #pragma unroll
@@ -301,7 +304,9 @@ QG_DEV void down1c_body(const Moe1Args &a, int bx, int R) {
         }
     }
     [[maybe_unused]] float gp = 0.0f;
-    if constexpr (XP == XP_SHARED) gp = gate_part(a, tid);
+    if constexpr (XP == XP_SHARED) {
+        if (!a.gate_logit) gp = gate_part(a, tid);
+    }
     float xs = 0.0f;
     if constexpr (U::SUMS != 0) {
         float h[8];
@@ -318,7 +323,8 @@ QG_DEV void down1c_body(const Moe1Args &a, int bx, int R) {
         }
     }
     [[maybe_unused]] float gs = 0.0f;
-    if constexpr (XP == XP_SHARED) gs = gate_finish(gp, wave, lane, s_red);   // holds a barrier
+    if constexpr (XP == XP_SHARED)   // (gate_finish holds a barrier; gate_logit is the same for all threads)
+        gs = a.gate_logit ? 1.0f / (1.0f + expf(-a.gate_logit[0])) : gate_finish(gp, wave, lane, s_red);
     __syncthreads();
 
     // one thread per (row, pick): the pick's block dots in block order

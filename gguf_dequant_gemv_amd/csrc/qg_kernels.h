@@ -129,6 +129,10 @@ struct GemvArgs {
     const float *r_escale;
     int32_t *r_pslot;
     float *r_pes;
+    // and, with a shared expert riding in the launch, its gate logit
+    // r_gate_inp . x (cols values), written to r_gate_out[0] when set
+    const float *r_gate_inp;
+    float *r_gate_out;
 };
 
 // ------------------------------------------- one token's routing in-launch --
@@ -301,9 +305,30 @@ QG_DEV bool route1_group(const GemvArgs &a, const Route1 &r, int g, bool lead, i
 // The same for a whole workgroup: its first wave loads the router inputs and
 // selects, the others take the result from LDS (selection is serial work,
 // and every wave of a launch doing it at once would fill the vector units
-// for microseconds).  Call from every thread, before any early return.
+// for microseconds).  In the lead workgroup the other three waves meanwhile
+// reduce the shared expert's gate logit (when asked), in three parts added
+// in a fixed order, so the down launch reads one value.  Call from every
+// thread of a 256-thread workgroup, before any early return.
 QG_DEV bool route1_group_wg(const GemvArgs &a, int g, bool lead, int &e_out, int &slot_out, int &z_out) {
     __shared__ int s_r[4];
+    __shared__ float s_g[4];
+    if (threadIdx.x >= 64 && lead && a.r_gate_out) {
+        const int w = (int)(threadIdx.x >> 6) - 1, l = (int)threadIdx.x & 63;
+        float gp = 0.0f;
+        for (int c0 = 64 * w + l; c0 < a.cols; c0 += 192 * 8) {
+            float gv[8], xv[8];
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                const bool in = c0 + 192 * b < a.cols;
+                gv[b] = in ? a.r_gate_inp[c0 + 192 * b] : 0.0f;
+                xv[b] = in ? a.x[c0 + 192 * b] : 0.0f;
+            }
+#pragma unroll
+            for (int b = 0; b < 8; b++) gp = fmaf(gv[b], xv[b], gp);
+        }
+        gp = wave_sum(gp);
+        if (l == 0) s_g[w] = gp;
+    }
     if (threadIdx.x < 64) {
         Route1 r;
         route1_load(a, r);
@@ -317,6 +342,7 @@ QG_DEV bool route1_group_wg(const GemvArgs &a, int g, bool lead, int &e_out, int
         }
     }
     __syncthreads();
+    if (lead && a.r_gate_out && threadIdx.x == 0) a.r_gate_out[0] = (s_g[0] + s_g[1]) + s_g[2];
     e_out = __builtin_amdgcn_readfirstlane(s_r[0]);
     slot_out = __builtin_amdgcn_readfirstlane(s_r[1]);
     z_out = __builtin_amdgcn_readfirstlane(s_r[2]);

@@ -39,6 +39,7 @@ struct Moe1Args {
     const float *x;
     float *resid;
     float *sh_out;
+    const float *gate_logit;   // when set: the gate logit, already reduced (the routing launch's)
     // XP_DENSE (dW set): a dense MLP's down matrix beside the experts (rows x
     // d_row_bytes, d_nb blocks a row), its activation row [d_nb * 32] and its
     // output y_mlp [rows], kept apart from the experts' sum

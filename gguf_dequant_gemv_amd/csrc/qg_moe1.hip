@@ -80,14 +80,15 @@ moe1c_fn moe1c_kernel(int type) {
 // workgroup: about two workgroups a CU (a SIMD then holds two waves, one
 // computing while the other waits; measured 7.9 us against 8.5 at one a CU
 // and 9.1 at three for the 2816-row Q4_0 layer with its dense row), but one
-// a CU with the shared expert, whose gate logit every workgroup reduces
-// again (7.7 us against 10.4 at two a CU, 2048 rows of Q8_0).
+// a CU with a shared expert whose gate logit every workgroup reduces again
+// (7.7 us against 10.4 at two a CU, 2048 rows of Q8_0); two when the
+// routing launch has reduced it.
 bool down1c_plan(const Moe1Args &a, int xp, int *rows_per_wg, int *wgs) {
     const int nbx = xp == XP_DENSE ? a.d_nb : xp == XP_SHARED ? a.nb : 0;
     if ((int64_t)a.k * a.nb + nbx > D1C_NT || a.n_slots < 1) return false;
     const int64_t ph = (int64_t)((uintptr_t)a.W & 3u);
     if (down1c_pool_bytes(ph, a.n_slots, a.stride, a.rows, a.row_bytes) > (int64_t)0xFFFFFFF0) return false;
-    const int64_t per = xp == XP_SHARED ? 256 : 512;
+    const int64_t per = xp == XP_SHARED && !a.gate_logit ? 256 : 512;
     const int64_t R = std::min<int64_t>(D1C_RMAX, (a.rows + per - 1) / per);
     *rows_per_wg = (int)R;
     *wgs = (int)((a.rows + R - 1) / R);

@@ -370,8 +370,9 @@ typedef struct qg_shared_expert {
  * workspace: at least qg_moe_shared_workspace_size(m, sh, topk, ntok) bytes,
  * 256-byte aligned: qg_moe_ffn's workspace (same layout), then the shared
  * expert's gu [ntok][2 SF] and act [ntok][SF] (qg_mlp's layout, with its
- * scratch after act when it needs one) and its output sh [ntok][H] last,
- * each at a 256-byte boundary.
+ * scratch after act when it needs one), 256 bytes for the gate logit
+ * gate_inp . x (one token: reduced by the routing launch) and its output
+ * sh [ntok][H] last, each at a 256-byte boundary.
  * Errors: as qg_moe_ffn, and as qg_mlp for the shared expert's shapes (all
  * checked before anything is enqueued). */
 size_t qg_moe_shared_workspace_size(const qg_moe *m, const qg_shared_expert *sh, int topk, int ntok);

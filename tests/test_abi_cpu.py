@@ -183,7 +183,7 @@ def test_moe_shared_rejects_and_sizes():
     sh = qg.qg_shared_expert(8, 512, FAKE, FAKE, FAKE, FAKE)
     base = qg.qg_moe_workspace_size(m, 8, 1)
     ws = qg.qg_moe_shared_workspace_size(m, sh, 8, 1)
-    assert ws == base + 2 * 512 * 4 + 512 * 4 + 2048 * 4     # gu, act, sh after the routed part
+    assert ws == base + 2 * 512 * 4 + 512 * 4 + 2048 * 4 + 256   # gu, act, sh, gate logit after the routed part
     call = lambda s, w=ws, T=1: L.qg_moe_ffn_shared(ctypes.byref(m), ctypes.byref(s), FAKE, 8, FAKE, FAKE, FAKE, T,
                                                    None, None, FAKE, FAKE, w, None)
     assert call(sh, w=ws - 256) == qg.QG_EINVAL
