@@ -111,19 +111,52 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
     __shared__ float s_red[4][NT];
     __shared__ float s_r[NT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // the tokens' sums of squares: thread i's values i, i + 256, ... in order
-    for (int t = 0; t < ntok; t++) {
-        const float *xt = x + (int64_t)t * n;
-        float ss = 0.0f;
-        for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
-            float v[LB];
+    constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;   // this wave's router row
+    const float *wr = W + (r < rows ? r : 0) * n;
+    // One token whose x is one batch: x's loads, then the first batch of the
+    // router row and its norm gains, then the sums, which wait for x alone
+    // (loads return in order), so the row's round trip overlaps the norm.
+    // Every load here is unconditional (clamped addresses, values selected
+    // after), so the count of loads in flight is exact.
+    const bool early = NT == 1 && V4 && n <= 256 * LB;
+    [[maybe_unused]] float4 wv0[B], gv0[B];
+    if (early) {
+        float v[LB];
 #pragma unroll
-            for (int b = 0; b < LB; b++) v[b] = i0 + b * 256 < n ? xt[i0 + b * 256] : 0.0f;
-#pragma unroll
-            for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+        for (int b = 0; b < LB; b++) {
+            const int64_t i = (int64_t)threadIdx.x + b * 256;
+            const float xv = x[i < n ? i : n - 1];
+            v[b] = i < n ? xv : 0.0f;
         }
+        if constexpr (V4) {
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                const int64_t c = min((int64_t)(4 * lane + 256 * b), n - 4);
+                wv0[b] = *(const float4 *)(wr + c);
+                gv0[b] = *(const float4 *)(rw + c);
+            }
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
         ss = wave_sum(ss);
-        if (lane == 0) s_red[wave][t] = ss;
+        if (lane == 0) s_red[wave][0] = ss;
+    } else {
+        // the tokens' sums of squares: thread i's values i, i + 256, ... in order
+        for (int t = 0; t < ntok; t++) {
+            const float *xt = x + (int64_t)t * n;
+            float ss = 0.0f;
+            for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
+                float v[LB];
+#pragma unroll
+                for (int b = 0; b < LB; b++) v[b] = i0 + b * 256 < n ? xt[i0 + b * 256] : 0.0f;
+#pragma unroll
+                for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+            }
+            ss = wave_sum(ss);
+            if (lane == 0) s_red[wave][t] = ss;
+        }
     }
     __syncthreads();
     if ((int)threadIdx.x < ntok) {
@@ -142,10 +175,7 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
             for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += 256)
                 o.y[j][(int64_t)t * n + c] = ((x[(int64_t)t * n + c] * s_r[t]) * o.k[j]) * o.w[j][c];
     // router row r of wave w
-    constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
     if (r >= rows) return;
-    const float *wr = W + r * n;
     float rt[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) rt[t] = t < ntok ? s_r[t] : 0.0f;
@@ -156,11 +186,20 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
     if constexpr (V4) {
         for (int64_t c0 = 4 * lane; c0 < n; c0 += 256 * B) {
             float4 wv[B], gv[B];
+            if (early && c0 == 4 * lane) {   // the first batch, loaded before the norm
 #pragma unroll
-            for (int b = 0; b < B; b++) {
-                const bool in = c0 + 256 * b < n;
-                wv[b] = in ? *(const float4 *)(wr + c0 + 256 * b) : make_float4(0, 0, 0, 0);
-                gv[b] = in ? *(const float4 *)(rw + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+                for (int b = 0; b < B; b++) {
+                    const bool in = c0 + 256 * b < n;
+                    wv[b] = in ? wv0[b] : make_float4(0, 0, 0, 0);
+                    gv[b] = in ? gv0[b] : make_float4(0, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const bool in = c0 + 256 * b < n;
+                    wv[b] = in ? *(const float4 *)(wr + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+                    gv[b] = in ? *(const float4 *)(rw + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int t = 0; t < NT; t++) {
