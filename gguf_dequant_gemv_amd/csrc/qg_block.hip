@@ -102,17 +102,21 @@ __global__ __launch_bounds__(256) void k_rmsnorm_multi(const float *x, int64_t n
 // finds the tokens' RMS factors r_t (the sums of squares taken as k_rmsnorm
 // takes them), writes its slice of each output norm y_o = ((x r_t) k_o) w_o,
 // and its waves compute router rows e against the router's input norm
-// ((x r_t) rk) rw, formed on the fly, with k_gemv_f32's loads and order:
-// the logits and norms equal the separate launches' bit for bit.
-template <int NT, bool V4>
+// ((x r_t) rk) rw, formed on the fly, with k_gemv_f32's loads and order
+// (WPR waves to a row as there): the logits and norms equal the separate
+// launches' bit for bit.
+template <int NT, bool V4, int WPR>
 __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps,
                                                        const float *rw, float rk, const float *W, int64_t rows,
                                                        float *y, NormOuts o, int nout) {
+    static_assert(WPR == 1 || (WPR == 4 && V4 && NT > 1), "rows shared by the 4 waves only on the float4 path");
     __shared__ float s_red[4][NT];
     __shared__ float s_r[NT];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;   // this wave's router row
+    // this wave's router row, and its share of the row's column passes
+    const int64_t r = WPR == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+    const int part = WPR == 1 ? 0 : wave;
     const float *wr = W + (r < rows ? r : 0) * n;
     // One token whose x is one batch: x's loads, then the first batch of the
     // router row and its norm gains, then the sums, which wait for x alone
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.0f;
     auto xin = [&](float xv, int t, float g) { return ((xv * rt[t]) * rk) * g; };
-    if constexpr (V4) {
+    if constexpr (V4 && NT == 1) {
         for (int64_t c0 = 4 * lane; c0 < n; c0 += 256 * B) {
             float4 wv[B], gv[B];
             if (early && c0 == 4 * lane) {   // the first batch, loaded before the norm
@@ -201,21 +205,53 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
                     gv[b] = in ? *(const float4 *)(rw + c0 + 256 * b) : make_float4(0, 0, 0, 0);
                 }
             }
+            float4 xv[B];
+#pragma unroll
+            for (int b = 0; b < B; b++)
+                xv[b] = c0 + 256 * b < n ? *(const float4 *)(x + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                acc[0] = fmaf(wv[b].x, xin(xv[b].x, 0, gv[b].x), acc[0]);
+                acc[0] = fmaf(wv[b].y, xin(xv[b].y, 0, gv[b].y), acc[0]);
+                acc[0] = fmaf(wv[b].z, xin(xv[b].z, 0, gv[b].z), acc[0]);
+                acc[0] = fmaf(wv[b].w, xin(xv[b].w, 0, gv[b].w), acc[0]);
+            }
+        }
+    } else if constexpr (V4) {
+        // several tokens: loads unconditional as in k_gemv_f32 (clamped token
+        // and column, values selected after), so a pass's x loads go out together
+        const float4 z4 = make_float4(0, 0, 0, 0);
+        for (int64_t c0 = 4 * lane + (int64_t)part * 256 * B; c0 < n; c0 += 256 * B * WPR) {
+            float4 wv[B], gv[B];
+            {
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    const int64_t c = c0 + 256 * b;
+                    const float4 w4 = *(const float4 *)(wr + (c < n ? c : n - 4));
+                    const float4 g4 = *(const float4 *)(rw + (c < n ? c : n - 4));
+                    wv[b] = c < n ? w4 : z4;
+                    gv[b] = c < n ? g4 : z4;
+                }
+            }
+            float4 xv[NT][B];
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                if (t < ntok) {
-                    float4 xv[B];
+                const int64_t tt = t < ntok ? t : ntok - 1;
 #pragma unroll
-                    for (int b = 0; b < B; b++)
-                        xv[b] = c0 + 256 * b < n ? *(const float4 *)(x + t * n + c0 + 256 * b)
-                                                 : make_float4(0, 0, 0, 0);
+                for (int b = 0; b < B; b++) {
+                    const int64_t c = c0 + 256 * b;
+                    const float4 v = *(const float4 *)(x + tt * n + (c < n ? c : n - 4));
+                    xv[t][b] = c < n ? v : z4;
+                }
+            }
 #pragma unroll
-                    for (int b = 0; b < B; b++) {
-                        acc[t] = fmaf(wv[b].x, xin(xv[b].x, t, gv[b].x), acc[t]);
-                        acc[t] = fmaf(wv[b].y, xin(xv[b].y, t, gv[b].y), acc[t]);
-                        acc[t] = fmaf(wv[b].z, xin(xv[b].z, t, gv[b].z), acc[t]);
-                        acc[t] = fmaf(wv[b].w, xin(xv[b].w, t, gv[b].w), acc[t]);
-                    }
+            for (int t = 0; t < NT; t++) {
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    acc[t] = fmaf(wv[b].x, xin(xv[t][b].x, t, gv[b].x), acc[t]);
+                    acc[t] = fmaf(wv[b].y, xin(xv[t][b].y, t, gv[b].y), acc[t]);
+                    acc[t] = fmaf(wv[b].z, xin(xv[t][b].z, t, gv[b].z), acc[t]);
+                    acc[t] = fmaf(wv[b].w, xin(xv[t][b].w, t, gv[b].w), acc[t]);
                 }
             }
         }
@@ -238,11 +274,27 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
             }
         }
     }
+    if constexpr (WPR == 1) {
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-        if (t < ntok) {
-            const float sum = wave_sum(acc[t]);
-            if (lane == 0) y[t * rows + r] = sum;
+        for (int t = 0; t < NT; t++) {
+            if (t < ntok) {
+                const float sum = wave_sum(acc[t]);
+                if (lane == 0) y[t * rows + r] = sum;
+            }
+        }
+    } else {   // the waves' sums in wave order, as k_gemv_f32 adds them (s_red is free again)
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+            const float s = wave_sum(acc[t]);
+            if (lane == 0) s_red[wave][t] = s;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < ntok) {
+            const int t = threadIdx.x;
+            float s = s_red[0][t];
+#pragma unroll
+            for (int w = 1; w < WPR; w++) s += s_red[w][t];
+            y[t * rows + r] = s;
         }
     }
 }
@@ -252,41 +304,58 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
 // shared expert's gate: qwen3_moe_ssd.js matmulF32).  One wave per row; each
 // lane takes 4 consecutive columns per step (V4: 16-byte loads), the row's
 // values are loaded once and used for all NT tokens, and the lane partials are
-// summed across the wave.
-template <int NT, bool V4>
+// summed across the wave.  With WPR = 4 the four waves of a workgroup share
+// one row (wave w takes the column passes w, w + 4, ...), which puts four
+// times the workgroups on the chip when the rows are few and each pass is
+// long (16 tokens' x loads); their sums are added in wave order through LDS.
+template <int NT, bool V4, int WPR>
 __global__ __launch_bounds__(256) void k_gemv_f32(const float *W, const float *x, float *y, int64_t rows,
                                                   int64_t cols, int ntok) {
+    static_assert(WPR == 1 || (WPR == 4 && V4), "rows shared by the 4 waves only on the float4 path");
     // weight loads in flight per lane: all of a 2048-wide row for one token,
     // fewer as the token count (and the x loads per weight) grows
     constexpr int B = NT == 1 ? 8 : (NT <= 4 ? 4 : 2);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-    if (r >= rows) return;   // the whole wave leaves; nothing below waits on it
+    const int64_t r = WPR == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+    const int part = WPR == 1 ? 0 : wave;
+    if (r >= rows) return;   // the whole wave (WPR 4: workgroup) leaves; nothing below waits on it
     const float *wr = W + r * cols;
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) acc[t] = 0.0f;
     if constexpr (V4) {
-        for (int64_t c0 = 4 * lane; c0 < cols; c0 += 256 * B) {
+        // every load unconditional (token slots past ntok read the last
+        // token, columns past the row its last float4; their values are
+        // replaced by zeros or dropped), so the tokens' x loads of a pass go
+        // out together instead of one token's round trip after another
+        const float4 z4 = make_float4(0, 0, 0, 0);
+        for (int64_t c0 = 4 * lane + (int64_t)part * 256 * B; c0 < cols; c0 += 256 * B * WPR) {
             float4 wv[B];
 #pragma unroll
-            for (int b = 0; b < B; b++)
-                wv[b] = c0 + 256 * b < cols ? *(const float4 *)(wr + c0 + 256 * b) : make_float4(0, 0, 0, 0);
+            for (int b = 0; b < B; b++) {
+                const int64_t c = c0 + 256 * b;
+                const float4 v = *(const float4 *)(wr + (c < cols ? c : cols - 4));
+                wv[b] = c < cols ? v : z4;
+            }
+            float4 xv[NT][B];
 #pragma unroll
             for (int t = 0; t < NT; t++) {
-                if (t < ntok) {
-                    float4 xv[B];
+                const int64_t tt = t < ntok ? t : ntok - 1;
 #pragma unroll
-                    for (int b = 0; b < B; b++)
-                        xv[b] = c0 + 256 * b < cols ? *(const float4 *)(x + t * cols + c0 + 256 * b)
-                                                    : make_float4(0, 0, 0, 0);
+                for (int b = 0; b < B; b++) {
+                    const int64_t c = c0 + 256 * b;
+                    const float4 v = *(const float4 *)(x + tt * cols + (c < cols ? c : cols - 4));
+                    xv[t][b] = c < cols ? v : z4;
+                }
+            }
 #pragma unroll
-                    for (int b = 0; b < B; b++) {
-                        acc[t] = fmaf(wv[b].x, xv[b].x, acc[t]);
-                        acc[t] = fmaf(wv[b].y, xv[b].y, acc[t]);
-                        acc[t] = fmaf(wv[b].z, xv[b].z, acc[t]);
-                        acc[t] = fmaf(wv[b].w, xv[b].w, acc[t]);
-                    }
+            for (int t = 0; t < NT; t++) {
+#pragma unroll
+                for (int b = 0; b < B; b++) {
+                    acc[t] = fmaf(wv[b].x, xv[t][b].x, acc[t]);
+                    acc[t] = fmaf(wv[b].y, xv[t][b].y, acc[t]);
+                    acc[t] = fmaf(wv[b].z, xv[t][b].z, acc[t]);
+                    acc[t] = fmaf(wv[b].w, xv[t][b].w, acc[t]);
                 }
             }
         }
@@ -305,11 +374,28 @@ __global__ __launch_bounds__(256) void k_gemv_f32(const float *W, const float *x
             }
         }
     }
+    if constexpr (WPR == 1) {
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-        if (t < ntok) {
+        for (int t = 0; t < NT; t++) {
+            if (t < ntok) {
+                const float s = wave_sum(acc[t]);
+                if (lane == 0) y[t * rows + r] = s;
+            }
+        }
+    } else {
+        __shared__ float s_part[WPR][NT];
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
             const float s = wave_sum(acc[t]);
-            if (lane == 0) y[t * rows + r] = s;
+            if (lane == 0) s_part[wave][t] = s;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < ntok) {
+            const int t = threadIdx.x;
+            float s = s_part[0][t];
+#pragma unroll
+            for (int w = 1; w < WPR; w++) s += s_part[w][t];
+            y[t * rows + r] = s;
         }
     }
 }
@@ -762,11 +848,14 @@ int launch_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps, const f
         o.k[j] = k[j];
     }
     const bool v4 = (n % 4) == 0 && ((uintptr_t)W % 16) == 0 && ((uintptr_t)x % 16) == 0 && ((uintptr_t)rw % 16) == 0;
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    // the same row split as launch_gemv_f32 takes for these sizes, so the
+    // logits keep its summation order
+    const bool split = v4 && ntok > 4 && rows <= 65536;
+    const dim3 grid((unsigned)(split ? rows : (rows + 3) / 4));
     void (*f)(const float *, int64_t, int, float, const float *, float, const float *, int64_t, float *, NormOuts, int);
-    if (ntok == 1) f = v4 ? k_norm_gemv_f32<1, true> : k_norm_gemv_f32<1, false>;
-    else if (ntok <= 4) f = v4 ? k_norm_gemv_f32<4, true> : k_norm_gemv_f32<4, false>;
-    else f = v4 ? k_norm_gemv_f32<16, true> : k_norm_gemv_f32<16, false>;
+    if (ntok == 1) f = v4 ? k_norm_gemv_f32<1, true, 1> : k_norm_gemv_f32<1, false, 1>;
+    else if (ntok <= 4) f = v4 ? k_norm_gemv_f32<4, true, 1> : k_norm_gemv_f32<4, false, 1>;
+    else f = split ? k_norm_gemv_f32<16, true, 4> : v4 ? k_norm_gemv_f32<16, true, 1> : k_norm_gemv_f32<16, false, 1>;
     hipLaunchKernelGGL(f, grid, dim3(256), 0, st, x, n, ntok, eps, rw, rk, W, rows, y, o, nout);
     return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
 }
@@ -774,11 +863,14 @@ int launch_norm_gemv_f32(const float *x, int64_t n, int ntok, float eps, const f
 int launch_gemv_f32(const float *W, const float *x, float *y, int64_t rows, int64_t cols, int ntok,
                     hipStream_t st) {
     const bool v4 = (cols % 4) == 0 && ((uintptr_t)W % 16) == 0 && ((uintptr_t)x % 16) == 0;
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    // 5 to 16 tokens over at most 64K rows (the routers and gates): one row a
+    // workgroup, its column passes spread over the 4 waves
+    const bool split = v4 && ntok > 4 && rows <= 65536;
+    const dim3 grid((unsigned)(split ? rows : (rows + 3) / 4));
     void (*f)(const float *, const float *, float *, int64_t, int64_t, int);
-    if (ntok == 1) f = v4 ? k_gemv_f32<1, true> : k_gemv_f32<1, false>;
-    else if (ntok <= 4) f = v4 ? k_gemv_f32<4, true> : k_gemv_f32<4, false>;
-    else f = v4 ? k_gemv_f32<16, true> : k_gemv_f32<16, false>;
+    if (ntok == 1) f = v4 ? k_gemv_f32<1, true, 1> : k_gemv_f32<1, false, 1>;
+    else if (ntok <= 4) f = v4 ? k_gemv_f32<4, true, 1> : k_gemv_f32<4, false, 1>;
+    else f = split ? k_gemv_f32<16, true, 4> : v4 ? k_gemv_f32<16, true, 1> : k_gemv_f32<16, false, 1>;
     hipLaunchKernelGGL(f, grid, dim3(256), 0, st, W, x, y, rows, cols, ntok);
     return hipGetLastError() == hipSuccess ? 0 : QG_EHIP;
 }

@@ -33,6 +33,9 @@ def _empty(shape, dtype="float32", fill=float("nan")):
 # ------------------------------------------------------------ f32 GEMV ------
 @pytest.mark.parametrize("rows,cols,T,off", [
     (128, 2048, 1, 0), (128, 2048, 3, 0), (256, 2048, 16, 0), (1, 2816, 1, 0),
+    (128, 2816, 16, 0),    # 5.5 column passes shared by a row's 4 waves
+    (300, 1000, 5, 0),     # 5 tokens, ragged last pass
+    (3, 44, 7, 0),         # one short pass: three of a row's waves add nothing
     (37, 70, 5, 0),        # cols not a multiple of 4: the scalar path
     (9, 256, 2, 4),        # W 4 bytes past a 16-byte boundary: the scalar path
 ])
@@ -96,7 +99,7 @@ def test_rmsnorm_multi(orc, n, T, nout):
 
 
 @pytest.mark.parametrize("n,E,T,nout", [(2048, 256, 1, 1), (2816, 128, 16, 2), (1000, 37, 3, 0), (1001, 9, 2, 1),
-                                         (5000, 8, 2, 3)])
+                                         (5000, 8, 2, 3), (1000, 300, 5, 1), (44, 3, 7, 1)])
 def test_rmsnorm_router(orc, n, E, T, nout):
     """Norms + router in one launch: the logits and every norm bit for bit
     what qg_rmsnorm / qg_gemv(QG_F32) give separately, and both against the
