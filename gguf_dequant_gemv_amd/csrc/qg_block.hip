@@ -147,19 +147,36 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
         ss = wave_sum(ss);
         if (lane == 0) s_red[wave][0] = ss;
     } else {
-        // the tokens' sums of squares: thread i's values i, i + 256, ... in order
-        for (int t = 0; t < ntok; t++) {
-            const float *xt = x + (int64_t)t * n;
-            float ss = 0.0f;
+        // the tokens' sums of squares: thread i's values i, i + 256, ... in
+        // order, TB tokens' loads out together (clamped token and index,
+        // values selected after)
+        constexpr int TB = NT < 8 ? NT : 8;
+        for (int t0 = 0; t0 < ntok; t0 += TB) {
+            float ss[TB];
+#pragma unroll
+            for (int u = 0; u < TB; u++) ss[u] = 0.0f;
             for (int64_t i0 = threadIdx.x; i0 < n; i0 += 256 * LB) {
-                float v[LB];
+                float v[TB][LB];
 #pragma unroll
-                for (int b = 0; b < LB; b++) v[b] = i0 + b * 256 < n ? xt[i0 + b * 256] : 0.0f;
+                for (int u = 0; u < TB; u++) {
+                    const int64_t tt = t0 + u < ntok ? t0 + u : ntok - 1;
 #pragma unroll
-                for (int b = 0; b < LB; b++) ss = fmaf(v[b], v[b], ss);
+                    for (int b = 0; b < LB; b++) {
+                        const int64_t i = i0 + b * 256;
+                        const float xv = x[tt * n + (i < n ? i : n - 1)];
+                        v[u][b] = i < n ? xv : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < TB; u++)
+#pragma unroll
+                    for (int b = 0; b < LB; b++) ss[u] = fmaf(v[u][b], v[u][b], ss[u]);
             }
-            ss = wave_sum(ss);
-            if (lane == 0) s_red[wave][t] = ss;
+#pragma unroll
+            for (int u = 0; u < TB; u++) {
+                const float s = wave_sum(ss[u]);
+                if (lane == 0 && t0 + u < ntok) s_red[wave][t0 + u] = s;
+            }
         }
     }
     __syncthreads();
@@ -174,10 +191,24 @@ __global__ __launch_bounds__(256) void k_norm_gemv_f32(const float *x, int64_t n
     // this workgroup's slice of the output norms
     const int64_t chunk = (n + gridDim.x - 1) / gridDim.x;
     const int64_t c_lo = (int64_t)blockIdx.x * chunk, c_hi = min(n, c_lo + chunk);
-    for (int j = 0; j < nout; j++)
-        for (int t = 0; t < ntok; t++)
+    if constexpr (NT == 1) {
+        for (int j = 0; j < nout; j++)
             for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += 256)
-                o.y[j][(int64_t)t * n + c] = ((x[(int64_t)t * n + c] * s_r[t]) * o.k[j]) * o.w[j][c];
+                o.y[j][c] = ((x[c] * s_r[0]) * o.k[j]) * o.w[j][c];
+    } else if (nout > 0) {   // a column's loads (every token's x, every output's gain) before its stores
+        for (int64_t c = c_lo + threadIdx.x; c < c_hi; c += 256) {
+            float xc[NT], wc[QG_MAX_NORMS];
+#pragma unroll
+            for (int t = 0; t < NT; t++) xc[t] = x[(int64_t)(t < ntok ? t : ntok - 1) * n + c];
+#pragma unroll
+            for (int j = 0; j < QG_MAX_NORMS; j++) wc[j] = o.w[j < nout ? j : 0][c];
+#pragma unroll
+            for (int j = 0; j < QG_MAX_NORMS; j++)
+#pragma unroll
+                for (int t = 0; t < NT; t++)
+                    if (j < nout && t < ntok) o.y[j][(int64_t)t * n + c] = ((xc[t] * s_r[t]) * o.k[j]) * wc[j];
+        }
+    }
     // router row r of wave w
     if (r >= rows) return;
     float rt[NT];
